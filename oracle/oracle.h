@@ -1,0 +1,82 @@
+/*
+ * Plain CPU oracle for the fused dequantise-and-multiply of GGUF block-quantised
+ * weights against Q8_0-quantised activations.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The HIP library shares
+ * no code, header, table or helper with it, and neither includes the other.
+ *
+ * What it computes (llamay "Architecture", section "The package map": pkg/quant
+ * holds the block layouts, dequantisation and the fused W4A8 kernels;
+ * pkg/tensor holds MatVec for decode and MatMul for prefill):
+ *
+ *   y[m][n] = sum_k  w^[n][k] * x^[m][k]
+ *
+ * where w^ is the dequantised weight (per the GGUF block layout) and x^ is the
+ * dequantised Q8_0 activation.  Everything is plain scalar C: activation
+ * quantisation in f32 (it decides integer codes, so it takes the kernel's
+ * precision), integer partials in int64, and results in f64.
+ *
+ * Type ids are the GGUF ones: Q4_0 = 2, Q8_0 = 8, Q4_K = 12, Q6_K = 14.
+ * All functions return 0 on success and a negative value on a bad argument
+ * (-1 unknown type, -2 bad shape, -3 a partial does not fit in int32).
+ */
+#ifndef GQMV_ORACLE_H
+#define GQMV_ORACLE_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* fp16 bits -> exact double; f32 -> fp16 bits, round to nearest even,
+ * subnormals kept, overflow to infinity. */
+double   oracle_half_to_double(uint16_t h);
+uint16_t oracle_float_to_half(float f);
+
+/* Q8_0 activation quantisation of x[rows][K] (K % 32 == 0) into
+ * rows*(K/32) blocks of 34 bytes: fp16 d (LE) then 32 int8 codes. */
+int oracle_quantize_act(const float* x, int64_t rows, int64_t K, uint8_t* out);
+
+/* Field-by-field unpack of an N x K weight blob.  Per element: the stored code
+ * q[N*K] (Q8_0 signed, Q4_0/Q4_K 0..15, Q6_K 0..63), its sub-block scale
+ * sub_scale[N*K] (Q4_K sc_j, Q6_K s_j, else 1) and min sub_min[N*K] (Q4_K m_j,
+ * else 0).  Per block of QK elements: d[N*K/QK] and dmin[N*K/QK] (Q4_K only,
+ * else 0).  Any output pointer may be NULL. */
+int oracle_unpack(int type, const uint8_t* w, int64_t N, int64_t K, int32_t* q,
+                  int32_t* sub_scale, int32_t* sub_min, double* d, double* dmin);
+
+/* Dequantised weights, f64 [N][K]. */
+int oracle_dequant(int type, const uint8_t* w, int64_t N, int64_t K, double* out);
+
+/* Dequantised Q8_0 activations, f64 [rows][K]. */
+int oracle_dequant_act(const uint8_t* xq, int64_t rows, int64_t K, double* out);
+
+/* Exact integer partial per (m, n, 32-element block b), layout [B][N][K/32]:
+ *   Q8_0: sum w*a     Q4_0: sum (q-8)*a     Q6_K: sum s_j*(q-32)*a
+ *   Q4_K: two integers per block, layout [B][N][K/32][2]:
+ *         P = sum sc_j*q*a  and  Q = sum m_j*a                              */
+int oracle_partials(int type, const uint8_t* w, int64_t N, int64_t K,
+                    const uint8_t* xq, int64_t B, int32_t* P);
+
+/* y[B][N] in f64 from the per-block partials and fp16 scales, blocks in
+ * ascending order; A[B][N] = sum_k |w^ * x^| (either may be NULL). */
+int oracle_matmul_f64(int type, const uint8_t* w, int64_t N, int64_t K,
+                      const uint8_t* xq, int64_t B, double* y, double* A);
+
+/* y[B][N] in f64 straight from the dequantised matrices, element by element. */
+int oracle_dense_f64(int type, const uint8_t* w, int64_t N, int64_t K,
+                     const uint8_t* xq, int64_t B, double* y);
+
+/* y[B][N] in f32 following the documented f32 reduction order: blocks are
+ * grouped into chunks of 8 (256 elements; the last chunk may be short); each
+ * chunk starts at +0 and adds its block terms in ascending order, each term
+ * added with one rounding (fmaf of the exact partial and the exact product of
+ * the two fp16 scales; Q4_K adds +P*(d*da) then -Q*(dmin*da)); y is the
+ * chunk sums added in ascending order starting from +0. */
+int oracle_matmul_canon_f32(int type, const uint8_t* w, int64_t N, int64_t K,
+                            const uint8_t* xq, int64_t B, float* y);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
