@@ -1,0 +1,179 @@
+"""Python binding of libqmv.so (include/qmv.h): the same entry points, argument
+marshalling only.  Every step of the multiply runs in the HIP kernels.
+
+Raw pointers and sizes go straight through; the torch-tensor helpers below
+only turn tensors into (pointer, stream) and check shapes/dtypes.  There is no
+CPU fallback: if the library is missing or the device is not gfx950 the calls
+raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqmv.so")
+
+Q4_0, Q8_0, Q4_K, Q6_K = 2, 8, 12, 14
+TYPES = {"Q4_0": Q4_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
+BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210)}
+EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmm_launch",
+           "qmv_partials_launch", "qmv_strerror")
+MAX_BATCH = 16
+
+
+class QmvError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {strerror(code)} (status {code})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqmv.so (built in-tree by build.py); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m gguf_quantized_matvec_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.qmv_act_bytes.argtypes = [I64, I64]
+        L.qmv_act_bytes.restype = ctypes.c_size_t
+        L.quantize_act_q8_0.argtypes = [P, P, I64, I64, P]
+        L.qmv_launch.argtypes = [I, P, I64, I64, P, I64, P, P, P]
+        L.qmm_launch.argtypes = [I, P, I64, I64, P, I64, P, P, P]
+        L.qmv_partials_launch.argtypes = [I, P, I64, I64, P, I64, P, P]
+        for f in ("quantize_act_q8_0", "qmv_launch", "qmm_launch", "qmv_partials_launch"):
+            getattr(L, f).restype = I
+        L.qmv_strerror.argtypes = [I]
+        L.qmv_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().qmv_strerror(int(code)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise QmvError(rc, what)
+
+
+# ---------------------------------------------------------------- raw C-ABI --
+
+def qmv_act_bytes(rows: int, K: int) -> int:
+    return int(lib().qmv_act_bytes(rows, K))
+
+
+def quantize_act_q8_0(x: int, xq: int, rows: int, K: int, stream: int = 0) -> None:
+    _check(lib().quantize_act_q8_0(x, xq, rows, K, stream), "quantize_act_q8_0")
+
+
+def qmv_launch(type: int, w: int, N: int, K: int, x, B: int, xq: int, y: int,
+               stream: int = 0) -> None:
+    _check(lib().qmv_launch(type, w, N, K, x, B, xq, y, stream), "qmv_launch")
+
+
+def qmm_launch(type: int, w: int, N: int, K: int, x, M: int, xq: int, y: int,
+               stream: int = 0) -> None:
+    _check(lib().qmm_launch(type, w, N, K, x, M, xq, y, stream), "qmm_launch")
+
+
+def qmv_partials_launch(type: int, w: int, N: int, K: int, xq: int, B: int, P: int,
+                        stream: int = 0) -> None:
+    _check(lib().qmv_partials_launch(type, w, N, K, xq, B, P, stream), "qmv_partials_launch")
+
+
+def qmv_strerror(code: int) -> str:
+    return strerror(code)
+
+
+# ------------------------------------------------------------ torch helpers --
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t, dtype, what):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def row_bytes(type: int, K: int) -> int:
+    qk, nbytes = BLOCK[type]
+    return (K // qk) * nbytes
+
+
+def act_buffer(rows: int, K: int, device="cuda"):
+    """Allocate an activation scratch tensor of qmv_act_bytes(rows, K) bytes."""
+    import torch
+    n = qmv_act_bytes(rows, K)
+    if n == 0:
+        raise ValueError(f"bad activation shape rows={rows} K={K}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def quantize(x, xq=None, stream=None):
+    """x: f32 [rows, K] device tensor -> xq scratch (Q8_0 blocks first)."""
+    import torch
+    rows, K = x.shape
+    if xq is None:
+        xq = act_buffer(rows, K, x.device)
+    quantize_act_q8_0(_dev(x, torch.float32, "x"), _dev(xq, torch.uint8, "xq"), rows, K,
+                      _stream(stream))
+    return xq
+
+
+def matvec(type: int, w, N: int, K: int, x=None, xq=None, B=None, y=None, stream=None):
+    """Decode GEMV: y [B, N] f32 = x [B, K] @ W^T, B <= 16 (x None: reuse xq)."""
+    import torch
+    if x is not None:
+        B = x.shape[0]
+    if xq is None:
+        xq = act_buffer(B, K, w.device)
+    if y is None:
+        y = torch.empty(B, N, dtype=torch.float32, device=w.device)
+    xp = _dev(x, torch.float32, "x") if x is not None else None
+    qmv_launch(type, _dev(w, torch.uint8, "w"), N, K, xp, B, _dev(xq, torch.uint8, "xq"),
+               _dev(y, torch.float32, "y"), _stream(stream))
+    return y
+
+
+def matmul(type: int, w, N: int, K: int, x=None, xq=None, M=None, y=None, stream=None):
+    """Prefill GEMM: y [M, N] f32 = x [M, K] @ W^T."""
+    import torch
+    if x is not None:
+        M = x.shape[0]
+    if xq is None:
+        xq = act_buffer(M, K, w.device)
+    if y is None:
+        y = torch.empty(M, N, dtype=torch.float32, device=w.device)
+    xp = _dev(x, torch.float32, "x") if x is not None else None
+    qmm_launch(type, _dev(w, torch.uint8, "w"), N, K, xp, M, _dev(xq, torch.uint8, "xq"),
+               _dev(y, torch.float32, "y"), _stream(stream))
+    return y
+
+
+def partials(type: int, w, N: int, K: int, xq, B: int, P=None, stream=None):
+    """Test hook: int32 per-block partials [B, N, K/32] (Q4_K [B, N, K/32, 2])."""
+    import torch
+    shape = (B, N, K // 32, 2) if type == Q4_K else (B, N, K // 32)
+    if P is None:
+        P = torch.empty(shape, dtype=torch.int32, device=w.device)
+    qmv_partials_launch(type, _dev(w, torch.uint8, "w"), N, K, _dev(xq, torch.uint8, "xq"), B,
+                        _dev(P, torch.int32, "P"), _stream(stream))
+    return P

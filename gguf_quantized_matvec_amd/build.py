@@ -1,0 +1,39 @@
+"""Build libqmv.so in-tree with hipcc for gfx950.
+
+    python -m gguf_quantized_matvec_amd.build
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libqmv.so")
+SOURCES = [os.path.join(CSRC, "qmv_kernels.hip"), os.path.join(CSRC, "qmv_api.cpp")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # exact f32 arithmetic: no contraction of a*b+c, correctly rounded divide
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # no packed-fp32 VALU instructions anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def build() -> str:
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-x", "hip", SOURCES[0], "-x", "hip", SOURCES[1], "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libqmv.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,131 @@
+// C-ABI of libqmv.so (declared in include/qmv.h): argument checks on the host,
+// a device check, and dispatch to the kernels.  Nothing is allocated and
+// nothing is synchronised; every check runs before any HIP call, so a refused
+// call has no effect at all.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/qmv.h"
+#include "qmv_internal.h"
+
+namespace {
+
+int elems_per_block(int type) {
+    switch (type) {
+    case QMV_Q8_0:
+    case QMV_Q4_0: return 32;
+    case QMV_Q4_K:
+    case QMV_Q6_K: return 256;
+    }
+    return 0;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_weights(int type, const void* w, int64_t N, int64_t K) {
+    const int qk = elems_per_block(type);
+    if (!qk) return QMV_EINVAL_TYPE;
+    if (N < 1 || N > INT32_MAX || K < 32 || K > QMV_MAX_K || K % qk) return QMV_EINVAL_SHAPE;
+    if (!w || !aligned(w, 16)) return QMV_EINVAL_PTR;
+    return QMV_OK;
+}
+
+// Cached per device: 1 = gfx950, 2 = something else.
+std::atomic<int> g_dev_ok[64];
+
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return QMV_EUNSUPPORTED_DEVICE;
+    if (dev < 64) {
+        const int v = g_dev_ok[dev].load(std::memory_order_relaxed);
+        if (v) return v == 1 ? QMV_OK : QMV_EUNSUPPORTED_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QMV_EUNSUPPORTED_DEVICE;
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? QMV_OK : QMV_EUNSUPPORTED_DEVICE;
+}
+
+int launched(int hip_rc) { return hip_rc == 0 ? QMV_OK : QMV_ELAUNCH; }
+
+// Shared front half of qmv_launch / qmm_launch.
+int matmul_common(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t rows,
+                  int64_t max_rows, void* xq, float* y, void* stream, bool gemm) {
+    int rc = check_weights(type, w, N, K);
+    if (rc) return rc;
+    if (rows < 1 || rows > max_rows) return QMV_EINVAL_SHAPE;
+    if (!xq || !y || !aligned(xq, 16) || !aligned(y, 4)) return QMV_EINVAL_PTR;
+    if (x && !aligned(x, 16)) return QMV_EINVAL_PTR;
+    if ((rc = check_device())) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* q = static_cast<uint8_t*>(xq);
+    rc = x ? qmv::launch_quantize(x, q, rows, K, s) : qmv::launch_rebuild(q, rows, K, s);
+    if (rc) return QMV_ELAUNCH;
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    return launched(gemm ? qmv::launch_qmm(type, wb, N, K, q, rows, y, s)
+                         : qmv::launch_qmv(type, wb, N, K, q, rows, y, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qmv_act_bytes(int64_t rows, int64_t K) {
+    if (rows < 1 || rows > QMV_MAX_M || K < 32 || K > QMV_MAX_K || K % 32) return 0;
+    return (size_t)qmv::act_layout(rows, K).total;
+}
+
+int quantize_act_q8_0(const float* x, void* xq, int64_t rows, int64_t K, void* stream) {
+    if (rows < 1 || rows > QMV_MAX_M || K < 32 || K > QMV_MAX_K || K % 32) return QMV_EINVAL_SHAPE;
+    if (!x || !xq || !aligned(x, 16) || !aligned(xq, 16)) return QMV_EINVAL_PTR;
+    const int rc = check_device();
+    if (rc) return rc;
+    return launched(qmv::launch_quantize(x, static_cast<uint8_t*>(xq), rows, K,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int qmv_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
+               void* xq, float* y, void* stream) {
+    return matmul_common(type, w, N, K, x, B, QMV_MAX_BATCH, xq, y, stream, false);
+}
+
+int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t M,
+               void* xq, float* y, void* stream) {
+    return matmul_common(type, w, N, K, x, M, QMV_MAX_M, xq, y, stream, true);
+}
+
+int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, const void* xq,
+                        int64_t B, int32_t* P, void* stream) {
+    int rc = check_weights(type, w, N, K);
+    if (rc) return rc;
+    if (B < 1 || B > QMV_MAX_BATCH) return QMV_EINVAL_SHAPE;
+    if (!xq || !P || !aligned(xq, 16) || !aligned(P, 4)) return QMV_EINVAL_PTR;
+    if ((rc = check_device())) return rc;
+    return launched(qmv::launch_partials(type, static_cast<const uint8_t*>(w), N, K,
+                                         static_cast<const uint8_t*>(xq), B, P,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+const char* qmv_strerror(int code) {
+    switch (code) {
+    case QMV_OK: return "ok";
+    case QMV_EINVAL_TYPE:
+        return "unsupported weight type: accepted are Q4_0 (2), Q8_0 (8), Q4_K (12), Q6_K (14)";
+    case QMV_EINVAL_SHAPE:
+        return "bad shape: need 1 <= N <= 2^31-1, 32 <= K <= 2^20 with K % 32 == 0 "
+               "(K % 256 == 0 for Q4_K/Q6_K), 1 <= B <= 16 for qmv_launch (use qmm_launch "
+               "for more rows), 1 <= M <= 2^24 for qmm_launch";
+    case QMV_EINVAL_PTR:
+        return "bad pointer: w, x and xq must be non-NULL (x may be NULL to reuse xq) and "
+               "16-byte aligned; y and P 4-byte aligned";
+    case QMV_ELAUNCH: return "HIP kernel launch failed";
+    case QMV_EUNSUPPORTED_DEVICE: return "current device is not an MI355X (gfx950)";
+    }
+    return "unknown status code";
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+/*
+ * qmv.h — C-ABI of the MI355X (gfx950) fused dequantise-and-multiply library
+ * for GGUF block-quantised weights (libqmv.so).
+ *
+ * What it computes.  The llamay pages ("Architecture", section "The package
+ * map") place the block layouts, dequantisation and fused W4A8 kernels in
+ * pkg/quant and "MatVec for decode, MatMul for prefill" in pkg/tensor; the
+ * same page's bench transcript notes that prefill is arithmetic-bound and
+ * decode memory-bound.  Here that is, for a weight matrix W (N rows of K
+ * elements, GGUF block layout) and f32 activations X (rows of K elements):
+ *
+ *     xq      = Q8_0(X)                           (per 32-element block:
+ *               d = amax/127 in f32, codes = round-half-away(x * (1/d)),
+ *               stored scale fp16(d))
+ *     Y[m][n] = sum over 32-blocks b of  d_w(n,b) * d_a(m,b) * I(m,n,b)
+ *
+ * with I the exact integer dot product of the block's weight codes and
+ * activation codes (Q4_0 codes offset by -8, Q6_K codes by -32 and weighted by
+ * the 16-element sub-scale; Q4_K contributes d*sc_j*sum(q*a) - dmin*m_j*sum(a)).
+ *
+ * Floating-point order (fixed, identical for every entry point, batch size
+ * and launch shape, so that every row of a batched or prefill call is
+ * bit-identical to the batch-1 call on that row — the pages' claim that
+ * output does not depend on batch composition, "llamay" docs, "The three
+ * claims", and that batched prefill equals sequential decode, "Architecture",
+ * "The forward pass"):
+ *   the K/32 blocks of a row are cut into chunks of 8 blocks (256 elements;
+ *   the last chunk may be shorter).  Each chunk sum starts at +0 and adds its
+ *   blocks in ascending order, each block term added with ONE rounding to f32
+ *   (an fma of the exact integer partial with the exact product of the two
+ *   fp16 scales; Q4_K adds its +d and then its -dmin term).  Y is the chunk
+ *   sums added in ascending order starting from +0.
+ *
+ * Weight layout.  Row n of W occupies bytes [n*R, (n+1)*R) of w, R =
+ * (K/QK)*block_bytes: Q8_0 (type 8) 32 elements / 34 bytes, Q4_0 (type 2)
+ * 32 / 18, Q4_K (type 12) 256 / 144, Q6_K (type 14) 256 / 210 — a GGUF 2-D
+ * tensor with K (ne0) contiguous.  Blocks need not be aligned; w itself must
+ * be 16-byte aligned.  X and Y are dense row-major f32.
+ *
+ * Ownership.  The caller owns and allocates every buffer (device memory).
+ * The library allocates nothing, keeps no per-call state, never synchronises,
+ * and enqueues all work asynchronously on `stream` (a hipStream_t; NULL = the
+ * null stream).  Calls are thread-safe.  x, xq and y must not overlap w or
+ * each other.
+ *
+ * Errors.  Every argument is checked on the host before anything is enqueued;
+ * a failed check returns a negative code and enqueues nothing.  A failed
+ * launch returns QMV_ELAUNCH.  qmv_strerror() names what is accepted.
+ *
+ * Preconditions not checked (data lives on the device): activations finite,
+ * and each 32-block's amax either 0 or in [127 * 2^-126, 127 * 65504].
+ */
+#ifndef QMV_H
+#define QMV_H
+#include <stddef.h>
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* GGUF tensor type ids. */
+enum qmv_type { QMV_Q4_0 = 2, QMV_Q8_0 = 8, QMV_Q4_K = 12, QMV_Q6_K = 14 };
+
+enum qmv_status {
+    QMV_OK = 0,
+    QMV_EINVAL_TYPE = -1,        /* type is not Q4_0, Q8_0, Q4_K or Q6_K */
+    QMV_EINVAL_SHAPE = -2,       /* N, K, rows or batch out of range */
+    QMV_EINVAL_PTR = -3,         /* NULL or misaligned pointer */
+    QMV_ELAUNCH = -4,            /* the HIP launch failed */
+    QMV_EUNSUPPORTED_DEVICE = -5 /* the current device is not gfx950 */
+};
+
+/* Limits: 1 <= N <= 2^31-1; 32 <= K <= 2^20, K % 32 == 0 (K % 256 == 0 for
+ * Q4_K and Q6_K, whose rows must be whole 256-element superblocks — the pages
+ * fall back from Q4_K to Q4_0 for exactly that reason, "Models and formats",
+ * quantize transcript); 1 <= B <= 16 for qmv_launch; 1 <= M <= 2^24 for
+ * qmm_launch. */
+#define QMV_MAX_K (1 << 20)
+#define QMV_MAX_BATCH 16
+#define QMV_MAX_M (1 << 24)
+
+/* Bytes of activation scratch `xq` for `rows` rows of K elements.  The first
+ * rows*(K/32)*34 bytes are the Q8_0 blocks (fp16 d little-endian, then 32
+ * int8 codes, blocks in row-major order); the rest is a private staging copy
+ * the kernels read.  Returns 0 for an invalid shape. */
+size_t qmv_act_bytes(int64_t rows, int64_t K);
+
+/* Quantise x [rows][K] (f32, 16-byte aligned) to Q8_0 into xq (16-byte
+ * aligned, qmv_act_bytes(rows, K) bytes).  Work for the Q8_0 activation
+ * format of the W4A8 path ("Architecture", "The package map"). */
+int quantize_act_q8_0(const float* x, void* xq, int64_t rows, int64_t K, void* stream);
+
+/* Decode GEMV (MatVec): y[B][N] = x[B][K] * W^T for 1 <= B <= 16.
+ * If x is non-NULL it is quantised into xq first (xq then holds its Q8_0
+ * blocks); if x is NULL, xq must hold valid Q8_0 blocks for B rows (its
+ * first B*(K/32)*34 bytes) and the library rebuilds its private part from
+ * them.  xq: qmv_act_bytes(B, K) bytes, 16-byte aligned.  Decode is
+ * memory-bound ("Architecture", bench transcript), so every weight byte is
+ * read once per call whatever B is ("A request, end to end": a batch reads
+ * the weights once rather than once per sequence). */
+int qmv_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
+               void* xq, float* y, void* stream);
+
+/* Prefill GEMM (MatMul): y[M][N] = x[M][K] * W^T for any M >= 1, on int8
+ * MFMA.  Same x / xq contract as qmv_launch with qmv_act_bytes(M, K) bytes.
+ * Each row of y is bit-identical to qmv_launch with B = 1 on that row. */
+int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t M,
+               void* xq, float* y, void* stream);
+
+/* Test hook: the exact int32 per-block partials that the kernels scale and
+ * accumulate, from the same decode and integer-dot path as qmv_launch.
+ * xq must come from quantize_act_q8_0 (or a qmv/qmm call with x != NULL) for
+ * B rows, 1 <= B <= 16.  P layout [B][N][K/32] int32; for Q4_K
+ * [B][N][K/32][2] = (sc_j * sum q*a, m_j * sum a). */
+int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, const void* xq,
+                        int64_t B, int32_t* P, void* stream);
+
+/* Static text for a status code. */
+const char* qmv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

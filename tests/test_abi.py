@@ -1,0 +1,81 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared entry
+point, and refuses bad arguments on the host before touching the GPU."""
+import os
+import re
+
+import pytest
+
+import gguf_quantized_matvec_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(g.LIB_PATH), reason="libqmv.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(g.EXPORTS), names
+    L = g.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_act_bytes():
+    # 1 row, K = 896: 28 blocks * 34 = 952 public bytes -> private at 1024;
+    # private = 1 group * 28 * (512 + 3*64)
+    assert g.qmv_act_bytes(1, 896) == 1024 + 28 * 704
+    assert g.qmv_act_bytes(17, 64) == ((17 * 2 * 34 + 255) // 256) * 256 + 2 * 2 * 704
+    for rows, K in [(0, 32), (1, 31), (1, 0), (1, 48), (-1, 32), (1, (1 << 20) + 32)]:
+        assert g.qmv_act_bytes(rows, K) == 0
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-NULL address; never dereferenced
+
+
+@pytest.mark.parametrize("args,code", [
+    ((3, FAKE, 16, 32, FAKE, 1, FAKE, FAKE), -1),            # unknown type
+    ((g.Q8_0, FAKE, 16, 48, FAKE, 1, FAKE, FAKE), -2),       # K % 32
+    ((g.Q4_K, FAKE, 16, 896, FAKE, 1, FAKE, FAKE), -2),      # K-quant K % 256
+    ((g.Q6_K, FAKE, 16, 4864 + 32, FAKE, 1, FAKE, FAKE), -2),
+    ((g.Q8_0, FAKE, 0, 32, FAKE, 1, FAKE, FAKE), -2),        # N
+    ((g.Q8_0, FAKE, 16, 32, FAKE, 0, FAKE, FAKE), -2),       # B = 0
+    ((g.Q8_0, FAKE, 16, 32, FAKE, 17, FAKE, FAKE), -2),      # B > 16: use qmm
+    ((g.Q8_0, FAKE, 16, (1 << 20) + 32, FAKE, 1, FAKE, FAKE), -2),
+    ((g.Q8_0, None, 16, 32, FAKE, 1, FAKE, FAKE), -3),       # w NULL
+    ((g.Q8_0, FAKE + 8, 16, 32, FAKE, 1, FAKE, FAKE), -3),   # w misaligned
+    ((g.Q8_0, FAKE, 16, 32, FAKE + 4, 1, FAKE, FAKE), -3),   # x misaligned
+    ((g.Q8_0, FAKE, 16, 32, FAKE, 1, None, FAKE), -3),       # xq NULL
+    ((g.Q8_0, FAKE, 16, 32, FAKE, 1, FAKE + 8, FAKE), -3),   # xq misaligned
+    ((g.Q8_0, FAKE, 16, 32, FAKE, 1, FAKE, FAKE + 2), -3),   # y misaligned
+])
+def test_qmv_refusals(args, code):
+    assert g.lib().qmv_launch(*args, None) == code
+
+
+def test_qmm_and_partials_refusals():
+    L = g.lib()
+    assert L.qmm_launch(g.Q4_0, FAKE, 16, 32, FAKE, 0, FAKE, FAKE, None) == -2
+    assert L.qmm_launch(g.Q4_0, FAKE, 16, 32, FAKE, (1 << 24) + 1, FAKE, FAKE, None) == -2
+    assert L.qmm_launch(g.Q4_K, FAKE, 16, 512 + 32, FAKE, 4, FAKE, FAKE, None) == -2
+    assert L.qmv_partials_launch(g.Q8_0, FAKE, 16, 32, FAKE, 17, FAKE, None) == -2
+    assert L.qmv_partials_launch(g.Q8_0, FAKE, 16, 32, None, 1, FAKE, None) == -3
+    assert L.qmv_partials_launch(7, FAKE, 16, 32, FAKE, 1, FAKE, None) == -1
+    assert L.quantize_act_q8_0(FAKE, FAKE, 1, 40, None) == -2
+    assert L.quantize_act_q8_0(FAKE + 4, FAKE, 1, 32, None) == -3
+
+
+def test_strerror_names_what_works():
+    assert "Q4_0" in g.strerror(-1) and "Q6_K" in g.strerror(-1)
+    assert "K % 256" in g.strerror(-2) and "qmm_launch" in g.strerror(-2)
+    assert "gfx950" in g.strerror(-5)
+    assert g.strerror(0) == "ok" and "unknown" in g.strerror(-99)
+    with pytest.raises(g.QmvError) as e:
+        g.qmv_launch(3, FAKE, 16, 32, FAKE, 1, FAKE, FAKE, 0)
+    assert e.value.code == -1

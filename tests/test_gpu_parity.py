@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+* Q8_0 activation blocks and int32 block partials: bit-exact.
+* f32 outputs: within 1e-4 * sum|w^ x^| of the oracle's f64 result, and
+  bit-identical to the oracle's emulation of the documented f32 order.
+* Every row of a batched (B <= 16) or prefill call is bit-identical to the
+  batch-1 call on that row.
+Shapes span several 16-row tiles, ragged row tiles, ragged last chunks, every
+weight-row alignment the layouts allow, and the blob's unaligned end.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from checks import assert_bitwise, assert_tol
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gguf_quantized_matvec_amd as g
+    g.lib()  # raises if the library is missing: no fallback
+    return g
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def pub(xq, rows, K):
+    return host(xq)[: rows * (K // 32) * 34]
+
+
+# (fmt, N, K): K=896 ragged chunk; K=416 13 blocks; K=32 single block;
+# Q6_K K=768 -> 630-byte rows (2-byte aligned spans), odd N -> unaligned end.
+SMALL = [
+    (synth.Q8_0, 100, 896), (synth.Q8_0, 16, 32), (synth.Q8_0, 33, 4096 + 96),
+    (synth.Q4_0, 37, 416), (synth.Q4_0, 50, 4864), (synth.Q4_0, 17, 32),
+    (synth.Q4_K, 45, 1024), (synth.Q4_K, 16, 256), (synth.Q4_K, 7, 4864),
+    (synth.Q6_K, 33, 768), (synth.Q6_K, 16, 256), (synth.Q6_K, 19, 1024),
+]
+
+
+def _inputs(fmt, N, K, B, seed):
+    blob, _ = synth.weights(fmt, N, K, seed, s_range=(-128, 127))
+    x = synth.activations(B, K, seed + 7)
+    return blob, x
+
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (3, 896), (16, 4096), (21, 1024), (40, 4864)])
+def test_quantize_bit_exact(g, rows, K):
+    x = synth.activations(rows, K, 5) * np.float32(4.0)
+    x[0, :32] = 0.0                        # an all-zero block
+    x[-1, 32:64] = np.float32(1e-3)        # a tiny block (subnormal fp16 scale)
+    want = oracle.quantize_act(x)
+    xq = g.quantize(dev(x))
+    assert_bitwise(pub(xq, rows, K), want, "Q8_0 blocks")
+
+
+@pytest.mark.parametrize("fmt,N,K", SMALL)
+@pytest.mark.parametrize("B", [1, 3, 16])
+def test_partials_bit_exact(g, fmt, N, K, B):
+    blob, x = _inputs(fmt, N, K, B, 100 + N)
+    xq = g.quantize(dev(x))
+    P = g.partials(fmt, dev(blob), N, K, xq, B)
+    want = oracle.partials(fmt, blob, N, K, oracle.quantize_act(x), B)
+    assert_bitwise(host(P), want, "partials")
+
+
+@pytest.mark.parametrize("fmt,N,K", SMALL)
+@pytest.mark.parametrize("B", [1, 2, 5, 16])
+def test_qmv_against_oracle(g, fmt, N, K, B):
+    blob, x = _inputs(fmt, N, K, B, 200 + N)
+    y = host(g.matvec(fmt, dev(blob), N, K, x=dev(x)))
+    xq = oracle.quantize_act(x)
+    y64, A = oracle.matmul_f64(fmt, blob, N, K, xq, B)
+    assert_tol(y, y64, A, what="qmv vs f64")
+    assert_bitwise(y, oracle.matmul_canon_f32(fmt, blob, N, K, xq, B), "qmv vs f32 order")
+
+
+@pytest.mark.parametrize("fmt,N,K", SMALL)
+def test_batch_rows_equal_batch1(g, fmt, N, K):
+    blob, x = _inputs(fmt, N, K, 16, 300 + N)
+    w = dev(blob)
+    y16 = host(g.matvec(fmt, w, N, K, x=dev(x)))
+    for B in (2, 7, 16):
+        yB = host(g.matvec(fmt, w, N, K, x=dev(x[:B])))
+        assert_bitwise(yB, y16[:B], f"B={B} vs B=16")
+    for m in (0, 5, 15):
+        y1 = host(g.matvec(fmt, w, N, K, x=dev(x[m:m + 1])))
+        assert_bitwise(y1[0], y16[m], f"row {m} vs batch-1")
+    # permuting the batch permutes the rows
+    perm = np.random.default_rng(1).permutation(16)
+    yp = host(g.matvec(fmt, w, N, K, x=dev(x[perm])))
+    assert_bitwise(yp, y16[perm], "permuted batch")
+
+
+@pytest.mark.parametrize("fmt,N,K", [SMALL[0], SMALL[4], SMALL[6], SMALL[9]])
+@pytest.mark.parametrize("M", [17, 40])
+def test_qmm_rows_equal_qmv(g, fmt, N, K, M):
+    blob, x = _inputs(fmt, N, K, M, 400 + N)
+    w = dev(blob)
+    y = host(g.matmul(fmt, w, N, K, x=dev(x)))
+    xq = oracle.quantize_act(x)
+    assert_bitwise(y, oracle.matmul_canon_f32(fmt, blob, N, K, xq, M), "qmm vs f32 order")
+    for m in (0, 16, M - 1):
+        y1 = host(g.matvec(fmt, w, N, K, x=dev(x[m:m + 1])))
+        assert_bitwise(y[m], y1[0], f"qmm row {m} vs qmv")
+
+
+@pytest.mark.parametrize("fmt,N,K", [SMALL[1], SMALL[5], SMALL[7], SMALL[10]])
+def test_reuse_xq_without_x(g, fmt, N, K):
+    """x = NULL: the Q8_0 blocks in xq are the input; the staging part is rebuilt."""
+    B = 4
+    blob, x = _inputs(fmt, N, K, B, 500)
+    w = dev(blob)
+    y_ref = host(g.matvec(fmt, w, N, K, x=dev(x)))
+    xq = g.act_buffer(B, K)
+    xq.fill_(0xAB)
+    xq[: B * (K // 32) * 34] = dev(oracle.quantize_act(x))
+    y = host(g.matvec(fmt, w, N, K, xq=xq, B=B))
+    assert_bitwise(y, y_ref, "x=NULL vs x")
+    ym = host(g.matmul(fmt, w, N, K, xq=xq, M=B))
+    assert_bitwise(ym, y_ref, "qmm x=NULL vs qmv")
+
+
+def test_repeat_runs_are_identical(g):
+    fmt, N, K = synth.Q4_K, 300, 4096
+    blob, x = _inputs(fmt, N, K, 5, 600)
+    w, xd = dev(blob), dev(x)
+    ys = [host(g.matvec(fmt, w, N, K, x=xd)) for _ in range(3)]
+    assert_bitwise(ys[0], ys[1], "run 1 vs 2")
+    assert_bitwise(ys[0], ys[2], "run 1 vs 3")
+
+
+def test_scaling_and_negation(g):
+    fmt, N, K = synth.Q6_K, 40, 1024
+    blob, x = _inputs(fmt, N, K, 3, 700)
+    w = dev(blob)
+    y = host(g.matvec(fmt, w, N, K, x=dev(x)))
+    yn = host(g.matvec(fmt, w, N, K, x=dev(-x)))
+    assert_bitwise(yn, -y, "negated x")
+    y4 = host(g.matvec(fmt, w, N, K, x=dev(x * np.float32(4.0))))
+    assert_bitwise(y4, y * np.float32(4.0), "x * 4")
+
+
+def test_zero_activations_give_zero(g):
+    fmt, N, K = synth.Q4_K, 20, 512
+    blob, _ = _inputs(fmt, N, K, 1, 800)
+    y = host(g.matvec(fmt, dev(blob), N, K, x=dev(np.zeros((2, K), np.float32))))
+    assert np.all(y == 0) and not np.any(np.signbit(y))
+
+
+def test_largest_k(g):
+    fmt, N, K, B = synth.Q4_0, 3, 1 << 20, 2
+    blob, x = _inputs(fmt, N, K, B, 900)
+    y = host(g.matvec(fmt, dev(blob), N, K, x=dev(x)))
+    xq = oracle.quantize_act(x)
+    y64, A = oracle.matmul_f64(fmt, blob, N, K, xq, B)
+    assert_tol(y, y64, A, what="K=2^20")
+    assert_bitwise(y, oracle.matmul_canon_f32(fmt, blob, N, K, xq, B), "K=2^20 f32 order")
+
+
+def test_byte_coverage(g):
+    """Changing any single weight byte of a small blob changes some output."""
+    fmt, N, K = synth.Q4_K, 2, 256
+    f = synth.draw_fields(fmt, N, K, 950)
+    f["sc"] = np.maximum(f["sc"], 1)                # every code and min matters
+    f["m"] = np.maximum(f["m"], 1)
+    f["d"] = np.maximum(f["d"], np.float16(1e-2))
+    f["dmin"] = np.maximum(f["dmin"], np.float16(1e-2))
+    blob = synth.encode(f)
+    x = np.abs(synth.activations(1, K, 951)) + np.float32(0.5)   # codes all >= 1
+    xd = dev(x)
+    base = host(g.matvec(fmt, dev(blob), N, K, x=xd))
+    unchanged = []
+    for i in range(blob.size):
+        b2 = blob.copy()
+        b2[i] ^= 0x11
+        if np.array_equal(host(g.matvec(fmt, dev(b2), N, K, x=xd)), base):
+            unchanged.append(i)
+    assert not unchanged, f"bytes with no effect: {unchanged[:10]}"
