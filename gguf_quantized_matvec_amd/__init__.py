@@ -68,7 +68,7 @@ def qmv_act_bytes(rows: int, K: int) -> int:
     return int(lib().qmv_act_bytes(rows, K))
 
 
-def quantize_act_q8_0(x: int, xq: int, rows: int, K: int, stream: int = 0) -> None:
+def quantize_act_q8_0(x, xq: int, rows: int, K: int, stream: int = 0) -> None:
     _check(lib().quantize_act_q8_0(x, xq, rows, K, stream), "quantize_act_q8_0")
 
 
@@ -127,14 +127,16 @@ def act_buffer(rows: int, K: int, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def quantize(x, xq=None, stream=None):
-    """x: f32 [rows, K] device tensor -> xq scratch (Q8_0 blocks first)."""
+def quantize(x, xq=None, stream=None, rows=None, K=None):
+    """x: f32 [rows, K] device tensor -> xq scratch (Q8_0 blocks first).
+    x None: re-stage the Q8_0 blocks already in xq (rows, K given)."""
     import torch
-    rows, K = x.shape
+    if x is not None:
+        rows, K = x.shape
     if xq is None:
         xq = act_buffer(rows, K, x.device)
-    quantize_act_q8_0(_dev(x, torch.float32, "x"), _dev(xq, torch.uint8, "xq"), rows, K,
-                      _stream(stream))
+    xp = _dev(x, torch.float32, "x") if x is not None else None
+    quantize_act_q8_0(xp, _dev(xq, torch.uint8, "xq"), rows, K, _stream(stream))
     return xq
 
 

@@ -63,8 +63,7 @@ int matmul_common(int type, const void* w, int64_t N, int64_t K, const float* x,
     if ((rc = check_device())) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* q = static_cast<uint8_t*>(xq);
-    rc = x ? qmv::launch_quantize(x, q, rows, K, s) : qmv::launch_rebuild(q, rows, K, s);
-    if (rc) return QMV_ELAUNCH;
+    if (x && qmv::launch_quantize(x, q, rows, K, s)) return QMV_ELAUNCH;
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     return launched(gemm ? qmv::launch_qmm(type, wb, N, K, q, rows, y, s)
                          : qmv::launch_qmv(type, wb, N, K, q, rows, y, s));
@@ -81,11 +80,12 @@ size_t qmv_act_bytes(int64_t rows, int64_t K) {
 
 int quantize_act_q8_0(const float* x, void* xq, int64_t rows, int64_t K, void* stream) {
     if (rows < 1 || rows > QMV_MAX_M || K < 32 || K > QMV_MAX_K || K % 32) return QMV_EINVAL_SHAPE;
-    if (!x || !xq || !aligned(x, 16) || !aligned(xq, 16)) return QMV_EINVAL_PTR;
+    if (!xq || !aligned(xq, 16) || (x && !aligned(x, 16))) return QMV_EINVAL_PTR;
     const int rc = check_device();
     if (rc) return rc;
-    return launched(qmv::launch_quantize(x, static_cast<uint8_t*>(xq), rows, K,
-                                         static_cast<hipStream_t>(stream)));
+    uint8_t* q = static_cast<uint8_t*>(xq);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(x ? qmv::launch_quantize(x, q, rows, K, s) : qmv::launch_rebuild(q, rows, K, s));
 }
 
 int qmv_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
@@ -120,8 +120,8 @@ const char* qmv_strerror(int code) {
                "(K % 256 == 0 for Q4_K/Q6_K), 1 <= B <= 16 for qmv_launch (use qmm_launch "
                "for more rows), 1 <= M <= 2^24 for qmm_launch";
     case QMV_EINVAL_PTR:
-        return "bad pointer: w, x and xq must be non-NULL (x may be NULL to reuse xq) and "
-               "16-byte aligned; y and P 4-byte aligned";
+        return "bad pointer: w and xq must be non-NULL, w, x and xq 16-byte aligned (x may "
+               "be NULL to use xq as staged), y and P 4-byte aligned";
     case QMV_ELAUNCH: return "HIP kernel launch failed";
     case QMV_EUNSUPPORTED_DEVICE: return "current device is not an MI355X (gfx950)";
     }

@@ -86,15 +86,18 @@ enum qmv_status {
 size_t qmv_act_bytes(int64_t rows, int64_t K);
 
 /* Quantise x [rows][K] (f32, 16-byte aligned) to Q8_0 into xq (16-byte
- * aligned, qmv_act_bytes(rows, K) bytes).  Work for the Q8_0 activation
- * format of the W4A8 path ("Architecture", "The package map"). */
+ * aligned, qmv_act_bytes(rows, K) bytes): the Q8_0 blocks and the staging
+ * copy.  With x == NULL, the Q8_0 blocks already in xq (first rows*(K/32)*34
+ * bytes, e.g. produced elsewhere) are taken as the input and only the staging
+ * copy is rebuilt from them.  The 8-bit activation format of the W4A8 path
+ * ("Architecture", "The package map"). */
 int quantize_act_q8_0(const float* x, void* xq, int64_t rows, int64_t K, void* stream);
 
 /* Decode GEMV (MatVec): y[B][N] = x[B][K] * W^T for 1 <= B <= 16.
- * If x is non-NULL it is quantised into xq first (xq then holds its Q8_0
- * blocks); if x is NULL, xq must hold valid Q8_0 blocks for B rows (its
- * first B*(K/32)*34 bytes) and the library rebuilds its private part from
- * them.  xq: qmv_act_bytes(B, K) bytes, 16-byte aligned.  Decode is
+ * If x is non-NULL it is quantised into xq first (as quantize_act_q8_0); if x
+ * is NULL, xq must already hold a complete quantize_act_q8_0 result for these
+ * B rows and K, which is used as is (so several matrices can share one
+ * quantisation).  xq: qmv_act_bytes(B, K) bytes, 16-byte aligned.  Decode is
  * memory-bound ("Architecture", bench transcript), so every weight byte is
  * read once per call whatever B is ("A request, end to end": a batch reads
  * the weights once rather than once per sequence). */

@@ -120,19 +120,22 @@ def test_qmm_rows_equal_qmv(g, fmt, N, K, M):
 
 
 @pytest.mark.parametrize("fmt,N,K", [SMALL[1], SMALL[5], SMALL[7], SMALL[10]])
-def test_reuse_xq_without_x(g, fmt, N, K):
-    """x = NULL: the Q8_0 blocks in xq are the input; the staging part is rebuilt."""
+def test_staged_xq_paths(g, fmt, N, K):
+    """x = NULL uses xq as staged; quantize with x = NULL re-stages Q8_0 blocks
+    written by someone else (here the oracle) over a scribbled staging area."""
     B = 4
     blob, x = _inputs(fmt, N, K, B, 500)
     w = dev(blob)
     y_ref = host(g.matvec(fmt, w, N, K, x=dev(x)))
-    xq = g.act_buffer(B, K)
-    xq.fill_(0xAB)
-    xq[: B * (K // 32) * 34] = dev(oracle.quantize_act(x))
-    y = host(g.matvec(fmt, w, N, K, xq=xq, B=B))
-    assert_bitwise(y, y_ref, "x=NULL vs x")
-    ym = host(g.matmul(fmt, w, N, K, xq=xq, M=B))
-    assert_bitwise(ym, y_ref, "qmm x=NULL vs qmv")
+    xq = g.quantize(dev(x))
+    assert_bitwise(host(g.matvec(fmt, w, N, K, xq=xq, B=B)), y_ref, "staged xq")
+    xq2 = g.act_buffer(B, K)
+    xq2.fill_(0xAB)
+    xq2[: B * (K // 32) * 34] = dev(oracle.quantize_act(x))
+    g.quantize(None, xq2, rows=B, K=K)
+    assert_bitwise(host(xq2), host(xq), "re-staged xq")
+    assert_bitwise(host(g.matvec(fmt, w, N, K, xq=xq2, B=B)), y_ref, "x=NULL vs x")
+    assert_bitwise(host(g.matmul(fmt, w, N, K, xq=xq2, M=B)), y_ref, "qmm x=NULL vs qmv")
 
 
 def test_repeat_runs_are_identical(g):
