@@ -1,0 +1,397 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused dequantise-and-multiply on one MI355X.
+
+One step = one decode token through a Q4_0 SwiGLU FFN at batch 1 (the
+Qwen2.5-0.5B FFN shape of the llamay pages: gate and up 4864x896, down
+896x4864): quantise the 896-wide activation once, GEMV gate and up on it,
+quantise the 4864-wide activation, GEMV down.  Inputs are seeded synthetic
+weights/activations already resident in HBM; the weights are rotated over
+copies totalling >= --rotate-mib so every step streams them from HBM rather
+than from the 256 MB last-level cache.  Steps are replayed from a captured
+HIP graph (the path is launch-bound at this size).
+
+Prints ONE JSON line: metric/value (weight GB/s of the timed steps, wall
+clock), the roofline of the dominant kernel (the GEMV; per-launch durations
+from HIP timing events recorded inside the graph, on the launch stream), the
+CPU oracle timed on a bounded sample of the same step, and (unless
+--no-suite) per-matrix GEMV/GEMM figures for every workload shape.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
+KERNEL_SRC = os.path.join(ROOT, "gguf_quantized_matvec_amd", "csrc", "qmv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_src_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def gemv_alg_bytes(fmt, N, K, B, g) -> int:
+    """Algorithmic bytes of one GEMV launch: weight blob + Q8_0 activation
+    blocks + f32 output."""
+    return N * g.row_bytes(fmt, K) + B * (K // 32) * 34 + B * N * 4
+
+
+class GraphSteps:
+    """Capture `nsteps` calls of step(i) into one HIP graph, optionally with
+    external timing events around the launches that step() marks."""
+
+    def __init__(self, torch, step, nsteps, timed):
+        self.torch = torch
+        self.events = []
+        self.graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(self.graph, stream=s):
+                for i in range(nsteps):
+                    step(i, self._mark if timed else None)
+        torch.cuda.current_stream().wait_stream(s)
+        self.nsteps = nsteps
+
+    def _mark(self, tag):
+        ev = self.torch.cuda.Event(enable_timing=True, external=True)
+        ev.record()
+        self.events.append((tag, ev))
+
+    def replay(self):
+        self.graph.replay()
+
+    def durations_ms(self):
+        """(tag, ms) for each start/end pair recorded in the last replay."""
+        out = []
+        for k in range(0, len(self.events), 2):
+            (tag, e0), (_, e1) = self.events[k], self.events[k + 1]
+            out.append((tag, e0.elapsed_time(e1)))
+        return out
+
+
+def eager_durations(torch, step, nsteps):
+    """Per-launch durations with ordinary timing events around eager launches.
+    A spin kernel queued first lets the host enqueue everything before the GPU
+    starts, so each event pair brackets GPU execution only."""
+    evs = []
+
+    def mark(tag):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        evs.append((tag, ev))
+
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)
+    for i in range(nsteps):
+        step(i, mark)
+    torch.cuda.synchronize()
+    return [(evs[k][0], evs[k][1].elapsed_time(evs[k + 1][1])) for k in range(0, len(evs), 2)]
+
+
+def run_steps(graphs, make, n):
+    """Replay graphs to run exactly n steps (graph sizes created on demand)."""
+    full = graphs["full"]
+    for _ in range(n // full.nsteps):
+        full.replay()
+    r = n % full.nsteps
+    if r:
+        if r not in graphs:
+            graphs[r] = make(r, False)
+        graphs[r].replay()
+
+
+def ffn_workload(torch, g, synth, rotate_bytes):
+    """The headline step's buffers: rotated weight copies, activations, outputs."""
+    fmt = synth.Q4_0
+    shapes = [("gate", 4864, 896), ("up", 4864, 896), ("down", 896, 4864)]
+    blobs = {}
+    for i, (name, N, K) in enumerate(shapes):
+        blob, _ = synth.weights(fmt, N, K, synth.seed_for(1, i), dscale=0.02)
+        blobs[name] = torch.from_numpy(blob).cuda()
+    step_bytes = sum(int(b.numel()) for b in blobs.values())
+    R = max(1, math.ceil(rotate_bytes / step_bytes))
+    copies = {k: [v] + [v.clone() for _ in range(R - 1)] for k, v in blobs.items()}
+    x1 = torch.from_numpy(synth.activations(1, 896, synth.act_seed_for(1, 1))).cuda()
+    x2 = torch.from_numpy(synth.activations(1, 4864, synth.act_seed_for(1, 1) + 1)).cuda()
+    xq1, xq2 = g.act_buffer(1, 896), g.act_buffer(1, 4864)
+    ys = {n: torch.empty(1, N, dtype=torch.float32, device="cuda") for n, N, _ in shapes}
+    return dict(fmt=fmt, shapes=shapes, copies=copies, R=R, x1=x1, x2=x2, xq1=xq1, xq2=xq2,
+                ys=ys, step_bytes=step_bytes)
+
+
+def make_ffn_step(torch, g, W):
+    L = g.lib()
+    fmt = W["fmt"]
+    ptr = {k: [t.data_ptr() for t in v] for k, v in W["copies"].items()}
+    x1, x2 = W["x1"].data_ptr(), W["x2"].data_ptr()
+    q1, q2 = W["xq1"].data_ptr(), W["xq2"].data_ptr()
+    y = {k: v.data_ptr() for k, v in W["ys"].items()}
+    R = W["R"]
+
+    def check(rc, what):
+        if rc:
+            raise g.QmvError(rc, what)
+
+    def step(i, mark):
+        s = torch.cuda.current_stream().cuda_stream
+        c = i % R
+        check(L.quantize_act_q8_0(x1, q1, 1, 896, s), "quantize")
+        for name, N, K, q in (("gate", 4864, 896, q1), ("up", 4864, 896, q1)):
+            if mark: mark(name)
+            check(L.qmv_launch(fmt, ptr[name][c], N, K, None, 1, q, y[name], s), name)
+            if mark: mark(name)
+        check(L.quantize_act_q8_0(x2, q2, 1, 4864, s), "quantize")
+        if mark: mark("down")
+        check(L.qmv_launch(fmt, ptr["down"][c], 896, 4864, None, 1, q2, y["down"], s), "down")
+        if mark: mark("down")
+    return step
+
+
+def cpu_baseline(W, seconds):
+    """The CPU oracle on the same step (both quantisations and the three
+    products in f64), rows split over host threads, for ~`seconds`."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+    import synth
+    blobs = {k: v[0].cpu().numpy() for k, v in W["copies"].items()}
+    x1, x2 = W["x1"].cpu().numpy(), W["x2"].cpu().numpy()
+    fmt = W["fmt"]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    rb = {n: synth.row_bytes(fmt, K) for n, _, K in W["shapes"]}
+
+    def rows_job(name, N, K, xq, r0, r1):
+        b = blobs[name][r0 * rb[name]: r1 * rb[name]]
+        oracle.matmul_f64(fmt, b, r1 - r0, K, xq, 1, want_abs=False)
+
+    oracle.lib()
+    steps = 0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(cores) as ex:
+        while True:
+            xq1 = oracle.quantize_act(x1)
+            xq2 = oracle.quantize_act(x2)
+            futs = []
+            for name, N, K in W["shapes"]:
+                xq = xq1 if K == 896 else xq2
+                per = math.ceil(N / cores)
+                for r0 in range(0, N, per):
+                    futs.append(ex.submit(rows_job, name, N, K, xq, r0, min(N, r0 + per)))
+            for f in futs:
+                f.result()
+            steps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(W["step_bytes"] * steps / dt / 1e9, 4), "unit": "GB/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{steps} steps of the Q4_0 FFN decode step (quantise both activations, "
+                      f"gate/up/down products in f64), rows split over {cores} threads, "
+                      f"{dt:.1f} s; tok/s {steps / dt:.2f}"}
+
+
+def suite(torch, g, synth, rotate_bytes, reps=3):
+    """Per-matrix figures for every workload shape: GEMV at each decode batch
+    (weight GB/s) and GEMM at each prefill size (int8 TOPS), from timing events
+    inside captured graphs over rotated weight copies."""
+    res = []
+    for wl, spec in synth.WORKLOADS.items():
+        ci = list(synth.WORKLOADS).index(wl)
+        for mi, (fmt, N, K, ds) in enumerate(spec["mats"]):
+            blob, _ = synth.weights(fmt, N, K, synth.seed_for(ci, mi), dscale=ds)
+            wt = torch.from_numpy(blob).cuda()
+            nbytes = int(wt.numel())
+            R = max(1, min(64, math.ceil(rotate_bytes / nbytes)))
+            copies = [wt] + [wt.clone() for _ in range(R - 1)]
+            for B in spec["batches"]:
+                x = torch.from_numpy(synth.activations(B, K, synth.act_seed_for(ci, B))).cuda()
+                xq = g.quantize(x)
+                y = torch.empty(B, N, dtype=torch.float32, device="cuda")
+                L = g.lib()
+                fn = L.qmv_launch if B <= 16 else L.qmm_launch
+
+                def step(i, mark, fn=fn, B=B, xq=xq, y=y):
+                    s = torch.cuda.current_stream().cuda_stream
+                    if mark: mark("k")
+                    rc = fn(fmt, copies[i % R].data_ptr(), N, K, None, B, xq.data_ptr(),
+                            y.data_ptr(), s)
+                    if mark: mark("k")
+                    if rc:
+                        raise g.QmvError(rc, "suite")
+                step(0, None)
+                torch.cuda.synchronize()
+                try:
+                    G = GraphSteps(torch, step, R, True)
+                    for _ in range(reps):
+                        G.replay()
+                    torch.cuda.synchronize()
+                    d = sorted(ms for _, ms in G.durations_ms())
+                except Exception:
+                    G = None
+                    d = sorted(ms for _, ms in eager_durations(torch, step, R))
+                med = d[len(d) // 2] * 1e-3
+                row = {"workload": wl, "fmt": synth.NAMES[fmt], "N": N, "K": K, "rows": B,
+                       "us": round(med * 1e6, 2), "weight_MB": round(nbytes / 1e6, 2)}
+                if B <= 16:
+                    gbs = nbytes / med / 1e9
+                    row.update(weight_GBs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                               tok_s=round(B / med, 1))
+                else:
+                    tops = 2.0 * B * N * K / med / 1e12
+                    row.update(int8_TOPS=round(tops, 1), mfma_frac=round(tops / INT8_PEAK_TOPS, 4))
+                res.append(row)
+                del G, x, xq, y
+            del copies, wt
+            torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--rotate-mib", type=int, default=1024)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-suite", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a 256 MiB device copy 10 times (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the multiply shards by weight rows with no cross-GPU "
+              f"reduction, so per-GPU throughput is the single-GPU figure", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gguf_quantized_matvec_amd as g
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    g.lib()
+
+    if args.copy_calib:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": a.numel(), "launches": 10}))
+        return
+
+    W = ffn_workload(torch, g, synth, args.rotate_mib << 20)
+    step = make_ffn_step(torch, g, W)
+    step(0, None)                       # eager run: device check, lazy init
+    torch.cuda.synchronize()
+
+    graphs = {}
+
+    def make(n, timed):
+        return GraphSteps(torch, step, n, timed)
+
+    try:
+        graphs["full"] = make(W["R"], True)
+        event_mode = "events recorded inside the replayed graph"
+    except Exception as e:  # timing events as graph nodes unsupported: time eagerly
+        print(f"bench.py: graph timing events unavailable ({e}); timing launches eagerly",
+              file=sys.stderr)
+        graphs["full"] = make(W["R"], False)
+        event_mode = None
+    run_steps(graphs, make, args.warmup)
+    torch.cuda.synchronize()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(graphs, make, args.steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    if args.steps < graphs["full"].nsteps:   # make sure the event graph ran at least once
+        graphs["full"].replay()
+        torch.cuda.synchronize()
+
+    if event_mode:
+        durs = graphs["full"].durations_ms()
+    else:
+        durs = eager_durations(torch, step, W["R"])
+        event_mode = "events around eager launches queued behind a spin kernel"
+    alg = {"gate": gemv_alg_bytes(W["fmt"], 4864, 896, 1, g),
+           "up": gemv_alg_bytes(W["fmt"], 4864, 896, 1, g),
+           "down": gemv_alg_bytes(W["fmt"], 896, 4864, 1, g)}
+    tot_ms = sum(ms for _, ms in durs)
+    tot_bytes = sum(alg[t] for t, _ in durs)
+    achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
+    avg_us = tot_ms * 1e3 / len(durs)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tf = json.load(open(TRAFFIC_FILE))
+        if tf.get("kernel_src_sha") == kernel_src_sha():
+            traffic = tf.get("bytes_per_launch")
+
+    value = W["step_bytes"] * args.steps / wall / 1e9
+    out = {
+        "metric": "decode GEMV weight-GB/s (% HBM peak); prefill int8 GEMM TOPS (% MFMA peak)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8 x i8 -> i32 (MFMA), f32 scale-accumulate",
+        "data": "synthetic (seeded GGUF Q4_0 blocks and N(0,1) activations)",
+        "config": {"workload": "Q4_0 SwiGLU FFN decode, batch 1: gate+up 4864x896, down 896x4864 "
+                               "(llamay Qwen2.5-0.5B shapes)",
+                   "global_batch": 1, "weights_per_step_bytes": W["step_bytes"],
+                   "rotated_copies": W["R"], "graph_replay": True,
+                   "tok_s": round(args.steps / wall, 1),
+                   "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "k_qmv<Q4_0> (GEMV)", "avg_launch_us": round(avg_us, 3),
+                     "launches_timed": len(durs), "timing": event_mode,
+                     "alg_bytes_per_launch": {"4864x896": alg["gate"], "896x4864": alg["down"]}},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
+    if not args.no_suite:
+        del graphs
+        W.clear()
+        torch.cuda.empty_cache()
+        out["suite"] = suite(torch, g, synth, 512 << 20)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

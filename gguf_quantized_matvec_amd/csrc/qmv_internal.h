@@ -8,29 +8,42 @@ namespace qmv {
 
 // Activation scratch `xq` for `rows` rows of K elements:
 //   [0, pub)            Q8_0 blocks, row-major: fp16 d (LE) + 32 int8 codes
-//   [priv0, ...)        private staging copy, in groups of 16 rows
-//                       (G = ceil(rows/16); rows past `rows` are zero):
+//   [priv0, ...)        private staging copies (every offset 256-aligned):
+//   for the MFMA kernels, in groups of 16 rows (G = ceil(rows/16); rows past
+//   `rows` are zero):
 //     codes  [G][nb][64][8] int8   the 16x16x32 MFMA A-operand of block b:
 //                                  lane l = m + 16*kg holds codes
 //                                  a[16g+m][32b + 8kg .. 32b + 8kg + 7]
 //     da     [G][nb][16] f32       f32 value of the fp16 block scale
 //     ca     [G][nb][16] f32       da * S (exact in f32)
 //     S      [G][nb][16] int32     sum of the block's 32 codes
+//   for the lane-per-chunk dot kernels, row-major over the `rows` rows:
+//     rcodes [rows][K] int8        codes in element order
+//     rda    [rows][nb] f32        as da
+//     rca    [rows][nb] f32        as ca
+//     rs16   [rows][nb] int32      sums of the two 16-element halves as two
+//                                  int16: low half = elements 0..15
 struct ActLayout {
-    int64_t nb, G, pub, priv0, codes, da, ca, S, total;
+    int64_t nb, G, pub, priv0, codes, da, ca, S, rcodes, rda, rca, rs16, total;
 };
+
+inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
 inline ActLayout act_layout(int64_t rows, int64_t K) {
     ActLayout L;
     L.nb = K / 32;
     L.G = (rows + 15) / 16;
     L.pub = rows * L.nb * 34;
-    L.priv0 = (L.pub + 255) & ~int64_t(255);
+    L.priv0 = align256(L.pub);
     L.codes = L.priv0;
-    L.da = L.codes + L.G * L.nb * 512;
-    L.ca = L.da + L.G * L.nb * 64;
-    L.S = L.ca + L.G * L.nb * 64;
-    L.total = L.S + L.G * L.nb * 64;
+    L.da = align256(L.codes + L.G * L.nb * 512);
+    L.ca = align256(L.da + L.G * L.nb * 64);
+    L.S = align256(L.ca + L.G * L.nb * 64);
+    L.rcodes = align256(L.S + L.G * L.nb * 64);
+    L.rda = align256(L.rcodes + rows * K);
+    L.rca = align256(L.rda + rows * L.nb * 4);
+    L.rs16 = align256(L.rca + rows * L.nb * 4);
+    L.total = align256(L.rs16 + rows * L.nb * 4);
     return L;
 }
 

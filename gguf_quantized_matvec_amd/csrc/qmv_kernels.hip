@@ -24,12 +24,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "qmv_internal.h"
 
 namespace qmv {
 namespace {
 
 constexpr int T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14;
+
+// Batch sizes up to this run on the lane-per-chunk v_dot4 kernel, larger ones on MFMA.
+constexpr int DOT_MAX_ROWS = 4;
+// ... as long as their activation rows fit in a workgroup's LDS.
+constexpr int DOT_MAX_LDS = 96 * 1024;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -123,6 +130,22 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x,
     reinterpret_cast<float*>(xq + L.da)[gb * 16 + m] = dval;
     reinterpret_cast<float*>(xq + L.ca)[gb * 16 + m] = dval * (float)S;
     reinterpret_cast<int32_t*>(xq + L.S)[gb * 16 + m] = S;
+    if (r < rows) {
+        // row-major copy for the lane-per-chunk kernels
+        uint4* rc = reinterpret_cast<uint4*>(xq + L.rcodes + r * K + 32 * b);
+        uint32_t wv[8];
+        __builtin_memcpy(wv, q, 32);
+        rc[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        rc[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+        int s_lo = 0;
+#pragma unroll
+        for (int i = 0; i < 16; i++) s_lo += (int8_t)q[i];
+        const int s_hi = S - s_lo;
+        reinterpret_cast<float*>(xq + L.rda)[r * nb + b] = dval;
+        reinterpret_cast<float*>(xq + L.rca)[r * nb + b] = dval * (float)S;
+        reinterpret_cast<int32_t*>(xq + L.rs16)[r * nb + b] =
+            (int32_t)(((uint32_t)s_lo & 0xFFFFu) | ((uint32_t)s_hi << 16));
+    }
 }
 
 // ------------------------------------------------------------- formats ----
@@ -137,41 +160,63 @@ template <> struct Fmt<T_Q4_K> { static constexpr int QK = 256, BB = 144, CB = 1
 template <> struct Fmt<T_Q6_K> { static constexpr int QK = 256, BB = 210, CB = 210, PPS = 14; };
 
 template <int FMT> constexpr int span_stride() { return 16 * Fmt<FMT>::PPS + 16; }
+template <int FMT> constexpr int F_QK() { return Fmt<FMT>::QK; }
 template <int FMT> constexpr int pieces_per_lane() { return (16 * Fmt<FMT>::PPS + 63) / 64; }
 
-// The final piece of the whole blob may run past its end: read it bytewise.
-__device__ __attribute__((noinline)) uint4 tail_piece(const uint8_t* w, int64_t off,
-                                                      int64_t wbytes) {
-    uint32_t v[4] = {0, 0, 0, 0};
-    for (int i = 0; i < 16; i++)
-        if (off + i < wbytes) v[i >> 2] |= (uint32_t)w[off + i] << (8 * (i & 3));
-    return make_uint4(v[0], v[1], v[2], v[3]);
+// ------------------------------------------------------- weight stream ----
+// A tile is 16 consecutive weight rows; its bytes are one contiguous range
+// [n0*R, (n0+16)*R) of the blob.  Offsets inside a tile fit in 32 bits
+// (16 * R <= 16 * (2^20/32) * 34 bytes).
+struct TileRef {
+    const uint8_t* base;  // w + n0*R
+    int nrows;            // rows of the tile that exist (1..16)
+    uint32_t left;        // blob bytes from base to the end of the blob
+    bool fast;            // whole tile present and >= 16 bytes of blob after it
+};
+
+__device__ __forceinline__ TileRef make_tile(const uint8_t* w, int64_t wbytes, int64_t N,
+                                             int64_t R, int64_t tile) {
+    TileRef t;
+    const int64_t n0 = tile * 16;
+    t.base = w + n0 * R;
+    t.nrows = (int)(N - n0 < 16 ? N - n0 : 16);
+    const int64_t left = wbytes - n0 * R;
+    t.left = (uint32_t)(left < 0x7fffffff ? left : 0x7fffffff);
+    t.fast = t.nrows == 16 && 16 * R + 16 <= left;
+    return t;
 }
 
-// Global -> registers: the 16 row spans of chunk c (rows n0..n0+15), as
-// 16-byte pieces aligned down from each span start.  Piece p of the wave is
-// lane p%64 of step p/64; it belongs to span p/PPS, offset 16*(p%PPS).
+// Global -> registers: the 16 row spans of chunk c, as 16-byte pieces aligned
+// down from each span start.  Piece p of the wave is lane p%64 of step p/64;
+// it belongs to span p/PPS at offset 16*(p%PPS).  Pieces past a span's end
+// are not loaded.  Only the last tile of a blob takes the guarded path, which
+// reads its final partial piece bytewise instead of running past the blob.
 template <int FMT>
-__device__ __forceinline__ void fetch_chunk(const uint8_t* __restrict__ w, int64_t wbytes,
-                                            int64_t n0, int64_t N, int64_t R, int c, int nbc,
+__device__ __forceinline__ void fetch_chunk(const TileRef& t, uint32_t R, int c, int nbc,
                                             int lane, uint4 (&reg)[pieces_per_lane<FMT>()]) {
     using F = Fmt<FMT>;
-    const int len = F::QK == 32 ? nbc * F::BB : F::BB;
+    const uint32_t len = F::QK == 32 ? nbc * F::BB : F::BB;
 #pragma unroll
-    for (int t = 0; t < pieces_per_lane<FMT>(); t++) {
-        const int p = t * 64 + lane;
+    for (int k = 0; k < pieces_per_lane<FMT>(); k++) {
+        const int p = k * 64 + lane;
         const int n = p / F::PPS, j = p - n * F::PPS;
-        reg[t] = make_uint4(0, 0, 0, 0);
-        if (n < 16 && n0 + n < N) {
-            const int64_t s = (n0 + n) * R + (int64_t)c * F::CB;
-            const int64_t off = (s & ~int64_t(15)) + 16 * j;
-            if (off < s + len) {
-                if (off + 16 <= wbytes)
-                    reg[t] = *reinterpret_cast<const uint4*>(w + off);
-                else
-                    reg[t] = tail_piece(w, off, wbytes);
+        const uint32_t s = n * R + c * F::CB;
+        const uint32_t off = (s & ~15u) + 16 * j;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t.fast) {
+            if (n < 16 && off < s + len) v = *reinterpret_cast<const uint4*>(t.base + off);
+        } else if (n < t.nrows && off < s + len) {
+            if (off + 16 <= t.left) {
+                v = *reinterpret_cast<const uint4*>(t.base + off);
+            } else {
+                uint32_t b[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < 16; i++)
+                    if (off + i < t.left) b[i >> 2] |= (uint32_t)t.base[off + i] << (8 * (i & 3));
+                v = make_uint4(b[0], b[1], b[2], b[3]);
             }
         }
+        reg[k] = v;
     }
 }
 
@@ -180,10 +225,10 @@ __device__ __forceinline__ void stage_chunk(uint8_t* wl, int lane,
                                             const uint4 (&reg)[pieces_per_lane<FMT>()]) {
     using F = Fmt<FMT>;
 #pragma unroll
-    for (int t = 0; t < pieces_per_lane<FMT>(); t++) {
-        const int p = t * 64 + lane;
+    for (int k = 0; k < pieces_per_lane<FMT>(); k++) {
+        const int p = k * 64 + lane;
         const int n = p / F::PPS, j = p - n * F::PPS;
-        if (n < 16) *reinterpret_cast<uint4*>(wl + n * span_stride<FMT>() + 16 * j) = reg[t];
+        if (n < 16) *reinterpret_cast<uint4*>(wl + n * span_stride<FMT>() + 16 * j) = reg[k];
     }
 }
 
@@ -200,211 +245,816 @@ __device__ __forceinline__ uint64_t bytes_minus(uint64_t x, uint64_t bias8) {
     return ((x | hi) - bias8) ^ hi;
 }
 
-// --------------------------------------------------------------- GEMV -----
-// Grid: one workgroup per (16 activation rows g, 16 weight rows); KS waves per
-// workgroup split the chunks of those rows round-robin (chunk r0 + wave).
-// After every round the chunk sums are combined in chunk order through LDS,
-// so the f32 order is the documented one whatever KS is.
-// PARTIALS: write the int32 block partials instead (test hook).
-template <int FMT, bool PARTIALS>
-__global__ __launch_bounds__(512) void k_qmv(const uint8_t* __restrict__ w, int64_t wbytes,
-                                             int64_t N, int64_t K, const uint8_t* __restrict__ xq,
-                                             ActLayout L, int64_t rows, int64_t tiles,
-                                             float* __restrict__ y, int32_t* __restrict__ P) {
-    using F = Fmt<FMT>;
-    constexpr int STRIDE = span_stride<FMT>();
-    constexpr int NP = pieces_per_lane<FMT>();
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, KS = blockDim.x >> 6;
-    uint8_t* wl = smem + wv * (16 * STRIDE);
-    float* pbuf = reinterpret_cast<float*>(smem + KS * 16 * STRIDE);
-    const int64_t tile = blockIdx.x % tiles, g = blockIdx.x / tiles;
-    const int64_t n0 = tile * 16;
-    const int Bg = (int)(rows - 16 * g < 16 ? rows - 16 * g : 16);
-    const int nb = (int)(K >> 5), C = (nb + 7) >> 3;
-    const int64_t R = (K / F::QK) * F::BB;
-    const int nn = lane & 15, kg = lane >> 4;
-    const uint8_t* acodes = xq + L.codes + g * nb * 512 + lane * 8;
-    const float* ada = reinterpret_cast<const float*>(xq + L.da) + g * nb * 16 + 4 * kg;
-    const float* aca = reinterpret_cast<const float*>(xq + L.ca) + g * nb * 16 + 4 * kg;
-    const int32_t* aS = reinterpret_cast<const int32_t*>(xq + L.S) + g * nb * 16 + 4 * kg;
-    const bool a_ok = nn < Bg;          // this lane's A-operand row exists
-    const bool s_ok = 4 * kg < Bg;      // some of this lane's 4 output rows exist
+// ---------------------------------------------------- activation stream ----
+// Activation side of one chunk: the lane's A operand of each of the 8 blocks,
+// and 2 of the chunk's 8 x 16 scale values (da, and ca for Q4_K).  The
+// staging copy always holds 16 rows per group (padding rows are zero), so
+// the loads need no row guard.
+struct ActRef {
+    const uint8_t* codes;  // group's codes + lane*8
+    const float* da;       // group's da
+    const float* ca;       // group's ca
+};
 
-    float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    uint4 reg[NP];
-    if (wv < C) {
-        const int nbc0 = F::QK == 32 ? min(8, nb - 8 * wv) : 8;
-        fetch_chunk<FMT>(w, wbytes, n0, N, R, wv, nbc0, lane, reg);
+__device__ __forceinline__ ActRef make_act(const uint8_t* xq, const ActLayout& L, int64_t g,
+                                           int lane) {
+    ActRef a;
+    a.codes = xq + L.codes + g * L.nb * 512 + lane * 8;
+    a.da = reinterpret_cast<const float*>(xq + L.da) + g * L.nb * 16;
+    a.ca = reinterpret_cast<const float*>(xq + L.ca) + g * L.nb * 16;
+    return a;
+}
+
+struct ActRegs {
+    long a[8];
+    float2 da, ca;
+};
+
+template <int FMT>
+__device__ __forceinline__ void fetch_act(const ActRef& A, int c, int nbc, int lane,
+                                          ActRegs& r) {
+#pragma unroll
+    for (int bb = 0; bb < 8; bb++)
+        r.a[bb] = bb < nbc ? *reinterpret_cast<const long*>(A.codes + (8 * c + bb) * 512) : 0;
+    const int sb = lane >> 3;   // scale block: 8 blocks x 16 rows, two per lane
+    const int sbc = sb < nbc ? sb : nbc - 1;
+    const uint32_t o = (8 * c + sbc) * 16 + 2 * (lane & 7);
+    float2 da = *reinterpret_cast<const float2*>(A.da + o);
+    float2 ca = make_float2(0.f, 0.f);
+    if (FMT == T_Q4_K) ca = *reinterpret_cast<const float2*>(A.ca + o);
+    const bool ok = sb < nbc;
+    r.da = ok ? da : make_float2(0.f, 0.f);
+    r.ca = ok ? ca : make_float2(0.f, 0.f);
+}
+
+// ------------------------------------------------------------ one chunk ----
+// The 8 (or fewer) blocks of chunk c for the 16 rows staged at wl and the
+// activation rows of the A operand.  Lane (nn = l%16, kg = l/16) decodes its
+// row's 8 codes of each block; the MFMA result of lane l, element i, is
+// (activation row 4*kg + i, weight row nn).  Non-PARTIALS: p[i] is the chunk
+// sum of rows 4*kg + i for i < NI (NI = 1, 2 or 4 rows per lane are needed).
+// PARTIALS: the exact integer partials are written to P instead.
+struct PartialsOut {
+    int32_t* P;
+    const int32_t* S;  // group's S + 4*kg
+    int64_t N, row0, n;
+    int nb, Bg, nrows;
+};
+
+template <int FMT, int NI, bool PARTIALS>
+__device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, const long (&acur)[8],
+                                           int c, int nbc, int kg, float (&p)[NI],
+                                           const PartialsOut& po) {
+    // per-chunk fields of the K-quant superblock
+    float dw = 0.0f, dmw = 0.0f;
+    uint32_t s12[3] = {0, 0, 0};
+    if (FMT == T_Q4_K) {
+        dw = half_bits_to_float(ld<uint16_t>(rb));
+        dmw = half_bits_to_float(ld<uint16_t>(rb + 2));
+        s12[0] = ld<uint32_t>(rb + 4);
+        s12[1] = ld<uint32_t>(rb + 8);
+        s12[2] = ld<uint32_t>(rb + 12);
     }
-    for (int r0 = 0; r0 < C; r0 += KS) {
-        const int c = r0 + wv;
-        float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (c < C) {
-            stage_chunk<FMT>(wl, lane, reg);
-            wave_sync();
-            const int nbc = F::QK == 32 ? min(8, nb - 8 * c) : 8;
-            const int cn = c + KS;
-            if (cn < C) {
-                const int nbcn = F::QK == 32 ? min(8, nb - 8 * cn) : 8;
-                fetch_chunk<FMT>(w, wbytes, n0, N, R, cn, nbcn, lane, reg);
-            }
-            const int delta = (int)(((n0 + nn) * R + (int64_t)c * F::CB) & 15);
-            const uint8_t* rb = wl + nn * STRIDE + delta;
-
-            // per-chunk fields of the K-quant superblock
-            float dw = 0.0f, dmw = 0.0f;
-            uint32_t s12[3] = {0, 0, 0};
-            if (FMT == T_Q4_K) {
-                dw = half_bits_to_float(ld<uint16_t>(rb));
-                dmw = half_bits_to_float(ld<uint16_t>(rb + 2));
-                s12[0] = ld<uint32_t>(rb + 4);
-                s12[1] = ld<uint32_t>(rb + 8);
-                s12[2] = ld<uint32_t>(rb + 12);
-            }
-            if (FMT == T_Q6_K) dw = half_bits_to_float(ld<uint16_t>(rb + 208));
+    if (FMT == T_Q6_K) dw = half_bits_to_float(ld<uint16_t>(rb + 208));
+#pragma unroll
+    for (int i = 0; i < NI; i++) p[i] = 0.0f;
 
 #pragma unroll
-            for (int bb = 0; bb < 8; bb++) {
-                if (F::QK == 32 && bb >= nbc) break;
-                const int64_t b = (int64_t)8 * c + bb;
-                const long a = a_ok ? *reinterpret_cast<const long*>(acodes + b * 512) : 0;
-                const v4i zero = {0, 0, 0, 0};
-                v4i acc, acc1 = zero;
-                int sc = 0, mn = 0, s0 = 0, s1 = 0;
-                if (FMT == T_Q8_0) {
-                    const uint8_t* blk = rb + 34 * bb;
-                    dw = half_bits_to_float(ld<uint16_t>(blk));
-                    const long wc = ld<long>(blk + 2 + 8 * kg);
-                    acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, wc, zero, 0, 0, 0);
-                } else if (FMT == T_Q4_0) {
-                    const uint8_t* blk = rb + 18 * bb;
-                    dw = half_bits_to_float(ld<uint16_t>(blk));
-                    uint64_t raw = ld<uint64_t>(blk + 2 + 8 * (kg & 1));
-                    if (kg & 2) raw >>= 4;
-                    const uint64_t wc =
-                        bytes_minus(raw & 0x0F0F0F0F0F0F0F0Full, 0x0808080808080808ull);
-                    acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, (long)wc, zero, 0, 0, 0);
-                } else if (FMT == T_Q4_K) {
-                    // 6-bit scale and min of sub-block bb (two per 12 bytes)
-                    const uint8_t* sb = reinterpret_cast<const uint8_t*>(s12);
-                    if (bb < 4) {
-                        sc = sb[bb] & 63;
-                        mn = sb[bb + 4] & 63;
+    for (int bb = 0; bb < 8; bb++) {
+        if (F_QK<FMT>() == 32 && bb >= nbc) break;
+        const long a = acur[bb];
+        const v4i zero = {0, 0, 0, 0};
+        v4i I;  // exact integer partial of (row 4kg+i, this lane's weight row)
+        int mn = 0;
+        if (FMT == T_Q8_0) {
+            const uint8_t* blk = rb + 34 * bb;
+            dw = half_bits_to_float(ld<uint16_t>(blk));
+            I = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, ld<long>(blk + 2 + 8 * kg), zero, 0, 0, 0);
+        } else if (FMT == T_Q4_0) {
+            const uint8_t* blk = rb + 18 * bb;
+            dw = half_bits_to_float(ld<uint16_t>(blk));
+            uint64_t raw = ld<uint64_t>(blk + 2 + 8 * (kg & 1));
+            if (kg & 2) raw >>= 4;
+            const uint64_t wc = bytes_minus(raw & 0x0F0F0F0F0F0F0F0Full, 0x0808080808080808ull);
+            I = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, (long)wc, zero, 0, 0, 0);
+        } else if (FMT == T_Q4_K) {
+            // 6-bit scale and min of sub-block bb (two per 12 bytes)
+            const uint8_t* sb = reinterpret_cast<const uint8_t*>(s12);
+            int sc;
+            if (bb < 4) {
+                sc = sb[bb] & 63;
+                mn = sb[bb + 4] & 63;
+            } else {
+                sc = (sb[bb + 4] & 15) | ((sb[bb - 4] >> 6) << 4);
+                mn = (sb[bb + 4] >> 4) | ((sb[bb] >> 6) << 4);
+            }
+            uint64_t raw = ld<uint64_t>(rb + 16 + 32 * (bb >> 1) + 8 * kg);
+            if (bb & 1) raw >>= 4;
+            const v4i acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                a, (long)(raw & 0x0F0F0F0F0F0F0F0Full), zero, 0, 0, 0);
+            I = sc * acc;
+        } else {  // Q6_K
+            const int h = bb >> 2, kq = bb & 3;
+            uint64_t ql = ld<uint64_t>(rb + 64 * h + 32 * (kq & 1) + 8 * kg);
+            const uint64_t qh = ld<uint64_t>(rb + 128 + 32 * h + 8 * kg);
+            if (kq & 2) ql >>= 4;
+            const uint64_t q6 = (ql & 0x0F0F0F0F0F0F0F0Full) |
+                                (((qh >> (2 * kq)) & 0x0303030303030303ull) << 4);
+            const uint64_t wc = bytes_minus(q6, 0x2020202020202020ull);
+            const int s0 = (int8_t)rb[192 + 2 * bb], s1 = (int8_t)rb[192 + 2 * bb + 1];
+            // the two 16-element halves carry different sub-scales: one MFMA
+            // per half, the other half's codes zeroed
+            const long lo = kg < 2 ? (long)wc : 0, hi = kg < 2 ? 0 : (long)wc;
+            const v4i acc0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, lo, zero, 0, 0, 0);
+            const v4i acc1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, hi, zero, 0, 0, 0);
+            I = s0 * acc0 + s1 * acc1;
+        }
+
+        if (PARTIALS) {
+            const int b = 8 * c + bb;
+            int4 S4 = make_int4(0, 0, 0, 0);
+            if (FMT == T_Q4_K) S4 = *reinterpret_cast<const int4*>(po.S + b * 16);
+            const int Sv[4] = {S4.x, S4.y, S4.z, S4.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int m = 4 * kg + i;
+                if (m < po.Bg && po.n < po.nrows) {
+                    const int64_t o = ((po.row0 + m) * po.N + po.n) * po.nb + b;
+                    if (FMT == T_Q4_K) {
+                        po.P[2 * o] = I[i];
+                        po.P[2 * o + 1] = mn * Sv[i];
                     } else {
-                        sc = (sb[bb + 4] & 15) | ((sb[bb - 4] >> 6) << 4);
-                        mn = (sb[bb + 4] >> 4) | ((sb[bb] >> 6) << 4);
-                    }
-                    uint64_t raw = ld<uint64_t>(rb + 16 + 32 * (bb >> 1) + 8 * kg);
-                    if (bb & 1) raw >>= 4;
-                    const uint64_t wc = raw & 0x0F0F0F0F0F0F0F0Full;
-                    acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, (long)wc, zero, 0, 0, 0);
-                } else {  // Q6_K
-                    const int h = bb >> 2, kq = bb & 3;
-                    uint64_t ql = ld<uint64_t>(rb + 64 * h + 32 * (kq & 1) + 8 * kg);
-                    const uint64_t qh = ld<uint64_t>(rb + 128 + 32 * h + 8 * kg);
-                    if (kq & 2) ql >>= 4;
-                    const uint64_t q6 = (ql & 0x0F0F0F0F0F0F0F0Full) |
-                                        (((qh >> (2 * kq)) & 0x0303030303030303ull) << 4);
-                    const uint64_t wc = bytes_minus(q6, 0x2020202020202020ull);
-                    s0 = (int8_t)rb[192 + 2 * bb];
-                    s1 = (int8_t)rb[192 + 2 * bb + 1];
-                    // the two 16-element halves carry different sub-scales:
-                    // one MFMA per half, the other half's codes zeroed
-                    const long lo = kg < 2 ? (long)wc : 0, hi = kg < 2 ? 0 : (long)wc;
-                    acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, lo, zero, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, hi, zero, 0, 0, 0);
-                }
-
-                if (PARTIALS) {
-                    int4 S4 = make_int4(0, 0, 0, 0);
-                    if (FMT == T_Q4_K && s_ok) S4 = *reinterpret_cast<const int4*>(aS + b * 16);
-                    const int Sv[4] = {S4.x, S4.y, S4.z, S4.w};
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int m = 4 * kg + i;
-                        if (m < Bg && n0 + nn < N) {
-                            const int64_t o = ((16 * g + m) * N + n0 + nn) * nb + b;
-                            if (FMT == T_Q4_K) {
-                                P[2 * o] = sc * acc[i];
-                                P[2 * o + 1] = mn * Sv[i];
-                            } else if (FMT == T_Q6_K) {
-                                P[o] = s0 * acc[i] + s1 * acc1[i];
-                            } else {
-                                P[o] = acc[i];
-                            }
-                        }
-                    }
-                } else {
-                    float4 da4 = make_float4(0.f, 0.f, 0.f, 0.f), ca4 = da4;
-                    if (s_ok) {
-                        da4 = *reinterpret_cast<const float4*>(ada + b * 16);
-                        if (FMT == T_Q4_K) ca4 = *reinterpret_cast<const float4*>(aca + b * 16);
-                    }
-                    const float dav[4] = {da4.x, da4.y, da4.z, da4.w};
-                    const float cav[4] = {ca4.x, ca4.y, ca4.z, ca4.w};
-                    const float cw = FMT == T_Q4_K ? dmw * (float)mn : 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        if (4 * kg + i < Bg) {
-                            if (FMT == T_Q4_K) {
-                                p[i] = fmaf((float)(sc * acc[i]), dw * dav[i], p[i]);
-                                p[i] = fmaf(-cw, cav[i], p[i]);
-                            } else if (FMT == T_Q6_K) {
-                                p[i] = fmaf((float)(s0 * acc[i] + s1 * acc1[i]), dw * dav[i], p[i]);
-                            } else {
-                                p[i] = fmaf((float)acc[i], dw * dav[i], p[i]);
-                            }
-                        }
+                        po.P[o] = I[i];
                     }
                 }
             }
-            wave_sync();
-        }
-        if (!PARTIALS) {
-            if (c < C) {
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    if (4 * kg + i < Bg) pbuf[wv * 256 + (4 * kg + i) * 16 + nn] = p[i];
+        } else {
+            float dav[4], cav[4] = {0.f, 0.f, 0.f, 0.f};
+            const float* sp = sl + bb * 16 + 4 * kg;
+            if (NI == 1) {
+                dav[0] = sp[0];
+                if (FMT == T_Q4_K) cav[0] = sp[128];
+            } else if (NI == 2) {
+                const float2 d2 = *reinterpret_cast<const float2*>(sp);
+                dav[0] = d2.x; dav[1] = d2.y;
+                if (FMT == T_Q4_K) {
+                    const float2 c2 = *reinterpret_cast<const float2*>(sp + 128);
+                    cav[0] = c2.x; cav[1] = c2.y;
+                }
+            } else {
+                const float4 d4 = *reinterpret_cast<const float4*>(sp);
+                dav[0] = d4.x; dav[1] = d4.y; dav[2] = d4.z; dav[3] = d4.w;
+                if (FMT == T_Q4_K) {
+                    const float4 c4 = *reinterpret_cast<const float4*>(sp + 128);
+                    cav[0] = c4.x; cav[1] = c4.y; cav[2] = c4.z; cav[3] = c4.w;
+                }
             }
-            __syncthreads();
-            const int nact = min(KS, C - r0);
+            const float cw = FMT == T_Q4_K ? dmw * (float)mn : 0.0f;
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const int e = threadIdx.x + k * blockDim.x;
-                if (e < 16 * Bg)
-                    for (int w2 = 0; w2 < nact; w2++) yacc[k] = yacc[k] + pbuf[w2 * 256 + e];
-            }
-            __syncthreads();
-        }
-    }
-    if (!PARTIALS) {
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const int e = threadIdx.x + k * blockDim.x;
-            if (e < 16 * Bg) {
-                const int m = e >> 4, n = e & 15;
-                if (n0 + n < N) y[(16 * g + m) * N + n0 + n] = yacc[k];
+            for (int i = 0; i < NI; i++) {
+                p[i] = fmaf((float)I[i], dw * dav[i], p[i]);
+                if (FMT == T_Q4_K) p[i] = fmaf(-cw, cav[i], p[i]);
             }
         }
     }
 }
 
-template <int FMT, bool PARTIALS>
-int launch_qmv_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t rows,
-                 float* y, int32_t* P, hipStream_t s) {
+// ------------------------------------------------------------- kernels ----
+// Each wave's LDS slice: the 16 row spans of its chunk, then the chunk's
+// activation scales [2][8][16] f32 (da, ca).
+template <int FMT> constexpr int wave_lds() { return 16 * span_stride<FMT>() + 1024; }
+
+template <int FMT>
+__device__ __forceinline__ void stage_all(uint8_t* wl, float* sl, int lane,
+                                          const uint4 (&reg)[pieces_per_lane<FMT>()],
+                                          const ActRegs& nxt, long (&acur)[8]) {
+    stage_chunk<FMT>(wl, lane, reg);
+    *reinterpret_cast<float2*>(sl + 2 * lane) = nxt.da;
+    if (FMT == T_Q4_K) *reinterpret_cast<float2*>(sl + 128 + 2 * lane) = nxt.ca;
+#pragma unroll
+    for (int bb = 0; bb < 8; bb++) acur[bb] = nxt.a[bb];
+    wave_sync();
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Tall matrices: every wave is independent and walks whole tiles, chunk after
+// chunk, keeping one chunk of prefetch in flight across tile boundaries.
+template <int FMT, int NI>
+__global__ __launch_bounds__(256) void k_qmv_rows(const uint8_t* __restrict__ w, int64_t wbytes,
+                                                  int64_t N, int64_t K,
+                                                  const uint8_t* __restrict__ xq, ActLayout L,
+                                                  int64_t rows, int64_t tiles,
+                                                  float* __restrict__ y) {
+    using F = Fmt<FMT>;
+    constexpr int NP = pieces_per_lane<FMT>();
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
+    uint8_t* wl = smem + wv * wave_lds<FMT>();
+    float* sl = reinterpret_cast<float*>(wl + 16 * span_stride<FMT>());
+    const int nb = (int)(K >> 5), C = (nb + 7) >> 3;
+    const int64_t Rl = (K / F::QK) * F::BB;
+    const uint32_t R = (uint32_t)Rl;
+    const int nn = lane & 15, kg = lane >> 4;
+    const int64_t TG = tiles * L.G;
+    const int64_t TW = (int64_t)gridDim.x * (blockDim.x >> 6);
+    int64_t tg = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
+    if (tg >= TG) return;
+
+    uint4 reg[NP];
+    ActRegs nxt;
+    long acur[8];
+    int c = 0;
+    TileRef t = make_tile(w, wbytes, N, Rl, tg % tiles);
+    ActRef A = make_act(xq, L, tg / tiles, lane);
+    {
+        const int nbc = F::QK == 32 ? min(8, nb) : 8;
+        fetch_chunk<FMT>(t, R, 0, nbc, lane, reg);
+        fetch_act<FMT>(A, 0, nbc, lane, nxt);
+    }
+    float yacc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) yacc[i] = 0.0f;
+    const PartialsOut none{};
+    while (true) {
+        const int nbc = F::QK == 32 ? min(8, nb - 8 * c) : 8;
+        stage_all<FMT>(wl, sl, lane, reg, nxt, acur);
+        const TileRef tc = t;
+        const int64_t tgc = tg;
+        const int cc = c;
+        // advance to the next item and prefetch it
+        if (++c == C) {
+            c = 0;
+            tg += TW;
+            if (tg < TG) {
+                t = make_tile(w, wbytes, N, Rl, tg % tiles);
+                A = make_act(xq, L, tg / tiles, lane);
+            }
+        }
+        if (tg < TG) {
+            const int nbcn = F::QK == 32 ? min(8, nb - 8 * c) : 8;
+            fetch_chunk<FMT>(t, R, c, nbcn, lane, reg);
+            fetch_act<FMT>(A, c, nbcn, lane, nxt);
+        }
+        const uint8_t* rb = wl + nn * span_stride<FMT>() + ((nn * R + cc * F::CB) & 15);
+        float p[NI];
+        chunk_math<FMT, NI, false>(rb, sl, acur, cc, nbc, kg, p, none);
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < NI; i++) yacc[i] = yacc[i] + p[i];
+        if (cc == C - 1) {
+            const int64_t g = tgc / tiles, n0 = (tgc % tiles) * 16;
+            const int Bg = (int)(rows - 16 * g < 16 ? rows - 16 * g : 16);
+#pragma unroll
+            for (int i = 0; i < NI; i++) {
+                const int m = 4 * kg + i;
+                if (m < Bg && nn < tc.nrows) y[(16 * g + m) * N + n0 + nn] = yacc[i];
+                yacc[i] = 0.0f;
+            }
+            if (tg >= TG) break;
+        }
+    }
+}
+
+// Short matrices: KS waves of one workgroup share a tile and take its chunks
+// round-robin; after every round the chunk sums are combined in chunk order
+// through LDS.  PARTIALS: write the int32 partials instead (test hook).
+template <int FMT, int NI, bool PARTIALS>
+__global__ __launch_bounds__(512) void k_qmv_split(const uint8_t* __restrict__ w, int64_t wbytes,
+                                                   int64_t N, int64_t K,
+                                                   const uint8_t* __restrict__ xq, ActLayout L,
+                                                   int64_t rows, int64_t tiles,
+                                                   float* __restrict__ y, int32_t* __restrict__ P) {
+    using F = Fmt<FMT>;
+    constexpr int NP = pieces_per_lane<FMT>();
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6), KS = blockDim.x >> 6;
+    uint8_t* wl = smem + wv * wave_lds<FMT>();
+    float* sl = reinterpret_cast<float*>(wl + 16 * span_stride<FMT>());
+    float* pbuf = reinterpret_cast<float*>(smem + KS * wave_lds<FMT>());
+    const int64_t tile = blockIdx.x % tiles, g = blockIdx.x / tiles;
+    const int64_t n0 = tile * 16;
+    const int Bg = (int)(rows - 16 * g < 16 ? rows - 16 * g : 16);
+    const int nb = (int)(K >> 5), C = (nb + 7) >> 3;
+    const int64_t Rl = (K / F::QK) * F::BB;
+    const uint32_t R = (uint32_t)Rl;
+    const int nn = lane & 15, kg = lane >> 4;
+    const TileRef t = make_tile(w, wbytes, N, Rl, tile);
+    const ActRef A = make_act(xq, L, g, lane);
+    PartialsOut po{};
+    if (PARTIALS) {
+        po.P = P;
+        po.S = reinterpret_cast<const int32_t*>(xq + L.S) + g * nb * 16 + 4 * kg;
+        po.N = N; po.row0 = 16 * g; po.n = n0 + nn; po.nb = nb; po.Bg = Bg; po.nrows = (int)N;
+    }
+
+    float yacc = 0.0f;
+    uint4 reg[NP];
+    ActRegs nxt;
+    long acur[8];
+    if (wv < C) {
+        const int nbc0 = F::QK == 32 ? min(8, nb - 8 * wv) : 8;
+        fetch_chunk<FMT>(t, R, wv, nbc0, lane, reg);
+        fetch_act<FMT>(A, wv, nbc0, lane, nxt);
+    }
+    for (int r0 = 0; r0 < C; r0 += KS) {
+        const int c = r0 + wv;
+        float p[NI];
+        if (c < C) {
+            stage_all<FMT>(wl, sl, lane, reg, nxt, acur);
+            const int nbc = F::QK == 32 ? min(8, nb - 8 * c) : 8;
+            const int cn = c + KS;
+            if (cn < C) {
+                const int nbcn = F::QK == 32 ? min(8, nb - 8 * cn) : 8;
+                fetch_chunk<FMT>(t, R, cn, nbcn, lane, reg);
+                fetch_act<FMT>(A, cn, nbcn, lane, nxt);
+            }
+            const uint8_t* rb = wl + nn * span_stride<FMT>() + ((nn * R + c * F::CB) & 15);
+            chunk_math<FMT, NI, PARTIALS>(rb, sl, acur, c, nbc, kg, p, po);
+            wave_sync();
+            if (!PARTIALS) {
+#pragma unroll
+                for (int i = 0; i < NI; i++)
+                    if (4 * kg + i < Bg) pbuf[wv * 256 + (4 * kg + i) * 16 + nn] = p[i];
+            }
+        }
+        if (!PARTIALS) {
+            __syncthreads();
+            const int nact = min(KS, C - r0);
+            if (threadIdx.x < 16 * Bg)
+                for (int w2 = 0; w2 < nact; w2++) yacc = yacc + pbuf[w2 * 256 + threadIdx.x];
+            __syncthreads();
+        }
+    }
+    if (!PARTIALS && threadIdx.x < 16 * Bg) {
+        const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
+        if (n < t.nrows) y[(16 * g + m) * N + n0 + n] = yacc;
+    }
+}
+
+// ------------------------------------------------- lane-per-chunk GEMV ----
+// For a few activation rows (B <= 4) the MFMA tile would be mostly empty and
+// the per-lane decode overhead of 8 codes per block dominates.  Here every
+// lane owns one 256-element chunk of one weight row: it streams the chunk's
+// bytes straight into registers (16-byte loads at the chunk's own, possibly
+// 2-byte, alignment), decodes all of them in-lane, and takes the block dots
+// with v_dot4_i32_i8 against the row-major staging copy of the activations.
+// Field offsets inside a chunk are compile-time constants, so unaligned fields
+// cost one v_alignbyte each.  The integer partials are exact and the f32
+// sequence per block is the documented one, so results are bit-identical to
+// the MFMA kernels.
+
+template <int N, class Fn, int... Is>
+__device__ __forceinline__ void static_for_impl(Fn&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// dword at compile-time byte offset O of a register array holding bytes in order
+template <int O, int NW>
+__device__ __forceinline__ uint32_t dw_at(const uint32_t (&r)[NW]) {
+    static_assert(O >= 0 && O + 4 <= 4 * NW, "field outside the chunk registers");
+    if constexpr (O % 4 == 0)
+        return r[O / 4];
+    else
+        return __builtin_amdgcn_alignbyte(r[O / 4 + 1], r[O / 4], O % 4);
+}
+template <int O, int NW>
+__device__ __forceinline__ uint32_t half_at(const uint32_t (&r)[NW]) {
+    return (r[O / 4] >> (8 * (O % 4))) & 0xFFFFu;
+}
+template <int O, int NW>
+__device__ __forceinline__ int sbyte_at(const uint32_t (&r)[NW]) {
+    return __builtin_amdgcn_sbfe((int)r[O / 4], 8 * (O % 4), 8);
+}
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// bytes of one chunk, loaded from the chunk start
+template <int FMT> struct DotFmt;
+template <> struct DotFmt<T_Q8_0> { static constexpr int NPC = 17; };  // 272 B
+template <> struct DotFmt<T_Q4_0> { static constexpr int NPC = 9; };   // 144 B
+template <> struct DotFmt<T_Q4_K> { static constexpr int NPC = 9; };   // 144 B
+template <> struct DotFmt<T_Q6_K> { static constexpr int NPC = 14; };  // 210 B (+14)
+
+template <int FMT>
+__device__ __forceinline__ void load_chunk_regs(const uint8_t* cs, bool guarded, int64_t room,
+                                                uint32_t (&r)[4 * DotFmt<FMT>::NPC]) {
+    constexpr int NPC = DotFmt<FMT>::NPC;
+    const uint8_t* p = static_cast<const uint8_t*>(__builtin_assume_aligned(cs, 2));
+    if (!guarded) {
+#pragma unroll
+        for (int i = 0; i < NPC; i++) __builtin_memcpy(&r[4 * i], p + 16 * i, 16);
+    } else {
+        // blob end inside the loaded range: full pieces, then bytes
+#pragma unroll
+        for (int i = 0; i < NPC; i++) {
+            if (16 * i + 16 <= room) {
+                __builtin_memcpy(&r[4 * i], p + 16 * i, 16);
+            } else {
+                uint32_t b[4] = {0, 0, 0, 0};
+                for (int j = 0; j < 16; j++)
+                    if (16 * i + j < room) b[j >> 2] |= (uint32_t)p[16 * i + j] << (8 * (j & 3));
+                r[4 * i] = b[0]; r[4 * i + 1] = b[1]; r[4 * i + 2] = b[2]; r[4 * i + 3] = b[3];
+            }
+        }
+    }
+}
+
+// Activation rows staged in LDS by the workgroup: codes of chunk c of row m
+// at codes + c*272 (256 bytes + 16 of padding, so lanes on different chunks
+// hit different banks); per-block scale words da, ca and s16 (two int16
+// half-block sums) at [b].
+struct ActRow {
+    const uint8_t* codes;
+    const float* da;
+    const float* ca;
+    const int32_t* s16;
+};
+constexpr int ACT_CHUNK_STRIDE = 272;
+
+__device__ __forceinline__ void act_block(const ActRow& A, int b, uint32_t (&a)[8]) {
+    const uint4* q = reinterpret_cast<const uint4*>(A.codes + (b >> 3) * ACT_CHUNK_STRIDE +
+                                                    (b & 7) * 32);
+    const uint4 lo = q[0], hi = q[1];
+    a[0] = lo.x; a[1] = lo.y; a[2] = lo.z; a[3] = lo.w;
+    a[4] = hi.x; a[5] = hi.y; a[6] = hi.z; a[7] = hi.w;
+}
+
+// LDS bytes of B staged activation rows of K elements.
+__host__ __device__ inline int act_lds_row_bytes(int64_t K) {
+    const int64_t nb = K / 32, C = (nb + 7) / 8;
+    return (int)((C * ACT_CHUNK_STRIDE + 3 * nb * 4 + 15) & ~int64_t(15));
+}
+
+// p[m] = sum over the chunk's blocks in order (documented f32 order).
+template <int FMT, int B>
+__device__ __forceinline__ void dot_chunk(const uint32_t (&r)[4 * DotFmt<FMT>::NPC],
+                                          const ActRow (&A)[B], int c, int nbc, float (&p)[B]) {
+#pragma unroll
+    for (int m = 0; m < B; m++) p[m] = 0.0f;
+    if constexpr (FMT == T_Q8_0) {
+        static_for<8>([&](auto BB) {
+            constexpr int bb = BB;
+            if (bb < nbc) {
+                const int b = 8 * c + bb;
+                const float dw = half_bits_to_float(half_at<34 * bb>(r));
+                uint32_t w[8];
+                static_for<8>([&](auto I) { w[I] = dw_at<34 * bb + 2 + 4 * I>(r); });
+#pragma unroll
+                for (int m = 0; m < B; m++) {
+                    uint32_t a[8];
+                    act_block(A[m], b, a);
+                    int D = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; i++) D = dot4(w[i], a[i], D);
+                    p[m] = fmaf((float)D, dw * A[m].da[b], p[m]);
+                }
+            }
+        });
+    } else if constexpr (FMT == T_Q4_0) {
+        static_for<8>([&](auto BB) {
+            constexpr int bb = BB;
+            if (bb < nbc) {
+                const int b = 8 * c + bb;
+                const float dw = half_bits_to_float(half_at<18 * bb>(r));
+                uint32_t lo[4], hi[4];
+                static_for<4>([&](auto I) {
+                    const uint32_t q = dw_at<18 * bb + 2 + 4 * I>(r);
+                    lo[I] = q & 0x0F0F0F0Fu;
+                    hi[I] = (q >> 4) & 0x0F0F0F0Fu;
+                });
+#pragma unroll
+                for (int m = 0; m < B; m++) {
+                    uint32_t a[8];
+                    act_block(A[m], b, a);
+                    int D = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) D = dot4(lo[i], a[i], D);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) D = dot4(hi[i], a[4 + i], D);
+                    const int s16 = A[m].s16[b];
+                    const int S = (int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16);
+                    p[m] = fmaf((float)(D - 8 * S), dw * A[m].da[b], p[m]);
+                }
+            }
+        });
+    } else if constexpr (FMT == T_Q4_K) {
+        const float d = half_bits_to_float(half_at<0>(r));
+        const float dmin = half_bits_to_float(half_at<2>(r));
+        static_for<8>([&](auto BB) {
+            constexpr int j = BB;
+            const int b = 8 * c + j;
+            // 6-bit scale and min of sub-block j (bytes 4..15 of the superblock)
+            int sc, mn;
+            if constexpr (j < 4) {
+                sc = (int)((dw_at<4 + (j & ~3)>(r) >> (8 * (j & 3))) & 63);
+                mn = (int)((dw_at<8>(r) >> (8 * j)) & 63);
+            } else {
+                const uint32_t s_hi = dw_at<12>(r) >> (8 * (j - 4));   // byte j+4
+                const uint32_t s_lo = dw_at<4>(r) >> (8 * (j - 4));    // byte j-4
+                const uint32_t s_mid = dw_at<8>(r) >> (8 * (j - 4));   // byte j
+                sc = (int)((s_hi & 15) | (((s_lo >> 6) & 3) << 4));
+                mn = (int)(((s_hi >> 4) & 15) | (((s_mid >> 6) & 3) << 4));
+            }
+            const float cw = dmin * (float)mn;
+            uint32_t q[8];
+            static_for<8>([&](auto I) {
+                q[I] = (dw_at<16 + 32 * (j >> 1) + 4 * I>(r) >> (4 * (j & 1))) & 0x0F0F0F0Fu;
+            });
+#pragma unroll
+            for (int m = 0; m < B; m++) {
+                uint32_t a[8];
+                act_block(A[m], b, a);
+                int D = 0;
+#pragma unroll
+                for (int i = 0; i < 8; i++) D = dot4(q[i], a[i], D);
+                p[m] = fmaf((float)(sc * D), d * A[m].da[b], p[m]);
+                p[m] = fmaf(-cw, A[m].ca[b], p[m]);
+            }
+        });
+    } else {  // Q6_K
+        const float d = half_bits_to_float(half_at<208>(r));
+        static_for<8>([&](auto BB) {
+            constexpr int bb = BB, h = bb >> 2, kq = bb & 3;
+            const int b = 8 * c + bb;
+            const int s0 = sbyte_at<192 + 2 * bb>(r), s1 = sbyte_at<193 + 2 * bb>(r);
+            uint32_t q[8];
+            static_for<8>([&](auto I) {
+                const uint32_t ql = dw_at<64 * h + 32 * (kq & 1) + 4 * I>(r);
+                const uint32_t qh = dw_at<128 + 32 * h + 4 * I>(r);
+                q[I] = ((ql >> (4 * (kq >> 1))) & 0x0F0F0F0Fu) |
+                       (((qh >> (2 * kq)) & 0x03030303u) << 4);
+            });
+#pragma unroll
+            for (int m = 0; m < B; m++) {
+                uint32_t a[8];
+                act_block(A[m], b, a);
+                int D0 = 0, D1 = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) D0 = dot4(q[i], a[i], D0);
+#pragma unroll
+                for (int i = 4; i < 8; i++) D1 = dot4(q[i], a[i], D1);
+                const int s16 = A[m].s16[b];
+                const int S0 = (int)(int16_t)(s16 & 0xFFFF), S1 = s16 >> 16;
+                const int I = s0 * (D0 - 32 * S0) + s1 * (D1 - 32 * S1);
+                p[m] = fmaf((float)I, d * A[m].da[b], p[m]);
+            }
+        });
+    }
+}
+
+// Persistent waves over work units.  C <= 64 chunks per row: a unit is G =
+// 64/LPR rows (LPR = lanes per row, a power of two >= C) in one pass.
+// C > 64: a unit is one row, in passes of 64 chunks.  Chunk sums are added
+// in chunk order per row through a small LDS buffer.
+template <int FMT, int B>
+__global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int64_t wbytes,
+                                             int64_t N, int64_t K,
+                                             const uint8_t* __restrict__ xq, ActLayout L,
+                                             float* __restrict__ y) {
+    using F = Fmt<FMT>;
+    constexpr int NPC = DotFmt<FMT>::NPC;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
+    const int nb = (int)(K >> 5), C = (nb + 7) >> 3;
+    const int rowb = act_lds_row_bytes(K);
+    float (*pbuf)[64] = reinterpret_cast<float (*)[64]>(smem + B * rowb + wv * B * 256);
+
+    const int64_t R = (K / F::QK) * F::BB;
+    int LPR = 1;
+    while (LPR < C && LPR < 64) LPR <<= 1;
+    const int G = 64 / LPR;
+    const int PR = (C + 63) >> 6;  // passes per unit (1 unless C > 64)
+    const int64_t units = C <= 64 ? (N + G - 1) / G : N;
+    const int64_t TW = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int64_t first = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
+    // items of this wave: (unit first + k*TW, pass q), k-major
+    const int64_t nit = ((units - first + TW - 1) / TW) * PR;
+
+    // issue the loads of item `it` into r (zeros for lanes without a chunk)
+    auto issue = [&](int64_t it, uint32_t (&r)[4 * NPC]) {
+        const int64_t u = first + (it / PR) * TW;
+        const int q = (int)(it % PR);
+        const int64_t row = C <= 64 ? u * G + lane / LPR : u;
+        const int c = C <= 64 ? (lane & (LPR - 1)) : 64 * q + lane;
+        const bool valid = row < N && c < C;
+        const int64_t off = row * R + (int64_t)c * F::CB;
+        const int64_t room = wbytes - off;
+        const bool near_end = valid && room < 16 * NPC;
+#pragma unroll
+        for (int i = 0; i < 4 * NPC; i++) r[i] = 0;
+        if (valid)
+            load_chunk_regs<FMT>(w + off, __builtin_amdgcn_ballot_w64(near_end) != 0, room, r);
+    };
+
+
+    // first chunk in flight while the activations are staged
+    uint32_t ra[4 * NPC], rb[4 * NPC];
+    if (first < units) issue(0, ra);
+
+    // stage the B activation rows: codes (per-chunk padded), da, ca, s16
+    ActRow A[B];
+#pragma unroll
+    for (int m = 0; m < B; m++) {
+        uint8_t* base = smem + m * rowb;
+        A[m].codes = base;
+        A[m].da = reinterpret_cast<const float*>(base + C * ACT_CHUNK_STRIDE);
+        A[m].ca = A[m].da + nb;
+        A[m].s16 = reinterpret_cast<const int32_t*>(A[m].ca + nb);
+        const uint4* src = reinterpret_cast<const uint4*>(xq + L.rcodes + m * K);
+        for (int i = threadIdx.x; i < nb * 2; i += blockDim.x)  // 16-byte pieces
+            *reinterpret_cast<uint4*>(base + (i >> 4) * ACT_CHUNK_STRIDE + (i & 15) * 16) = src[i];
+        const float* sda = reinterpret_cast<const float*>(xq + L.rda) + m * nb;
+        const float* sca = reinterpret_cast<const float*>(xq + L.rca) + m * nb;
+        const int32_t* ss = reinterpret_cast<const int32_t*>(xq + L.rs16) + m * nb;
+        float* dda = const_cast<float*>(A[m].da);
+        for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+            dda[i] = sda[i];
+            dda[nb + i] = sca[i];
+            reinterpret_cast<int32_t*>(dda + 2 * nb)[i] = ss[i];
+        }
+    }
+    __syncthreads();
+
+    float yacc[B];
+#pragma unroll
+    for (int j = 0; j < B; j++) yacc[j] = 0.0f;
+    // reduce and (at a unit's last pass) write item `it`, whose chunk is in r
+    auto work = [&](int64_t it, const uint32_t (&r)[4 * NPC]) {
+        const int64_t u = first + (it / PR) * TW;
+        const int q = (int)(it % PR);
+        const int64_t row = C <= 64 ? u * G + lane / LPR : u;
+        const int c = C <= 64 ? (lane & (LPR - 1)) : 64 * q + lane;
+        const bool valid = row < N && c < C;
+        const int nbc = F::QK == 32 ? min(8, nb - 8 * c) : 8;
+        float p[B];
+        if (valid) {
+            dot_chunk<FMT, B>(r, A, c, nbc, p);
+        } else {
+#pragma unroll
+            for (int m = 0; m < B; m++) p[m] = 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < B; m++) pbuf[m][lane] = p[m];
+        wave_sync();
+        // lane t < G*B (in steps of 64) adds row t%G's chunks for row m = t/G
+        const int cnt = C <= 64 ? C : min(64, C - 64 * q);
+#pragma unroll
+        for (int j = 0; j < B; j++) {
+            const int t = lane + 64 * j;
+            if (t < G * B) {
+                const int m = t / G, rl = t - m * G;
+                for (int k = 0; k < cnt; k++) yacc[j] = yacc[j] + pbuf[m][rl * LPR + k];
+            }
+        }
+        wave_sync();
+        if (q == PR - 1) {
+#pragma unroll
+            for (int j = 0; j < B; j++) {
+                const int t = lane + 64 * j;
+                if (t < G * B) {
+                    const int m = t / G, rl = t - m * G;
+                    const int64_t orow = C <= 64 ? u * G + rl : u;
+                    if (orow < N) y[m * N + orow] = yacc[j];
+                }
+                yacc[j] = 0.0f;
+            }
+        }
+    };
+
+    // two register sets: the next item's chunk is in flight while this one
+    // is decoded and multiplied
+    if (first >= units) return;
+    int64_t it = 0;
+    while (true) {
+        if (it + 1 < nit) issue(it + 1, rb);
+        work(it, ra);
+        if (++it >= nit) break;
+        if (it + 1 < nit) issue(it + 1, ra);
+        work(it, rb);
+        if (++it >= nit) break;
+    }
+}
+
+// Workgroups of `threads` threads and `shmem` bytes of LDS that the whole
+// device holds at once (occupancy of the kernel times the CU count), cached
+// per call site and device.
+struct ResidentCache {
+    int64_t v[16] = {0};
+};
+inline int64_t resident_blocks(ResidentCache& cache, const void* kernel, int threads,
+                               size_t shmem) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    const int slot = dev & 15;
+    if (cache.v[slot] > 0) return cache.v[slot];
+    int per_cu = 0, cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, shmem) !=
+            hipSuccess || per_cu < 1)
+        per_cu = 1;
+    cache.v[slot] = (int64_t)per_cu * cus;
+    return cache.v[slot];
+}
+
+template <int FMT, int B>
+int launch_dot_b(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, float* y,
+                 hipStream_t s) {
+    using F = Fmt<FMT>;
+    const ActLayout L = act_layout(B, K);
+    const int nb = (int)(K / 32), C = (nb + 7) / 8;
+    int LPR = 1;
+    while (LPR < C && LPR < 64) LPR <<= 1;
+    const int64_t G = 64 / LPR;
+    const int64_t units = C <= 64 ? (N + G - 1) / G : N;
+    const int64_t wbytes = N * (K / F::QK) * F::BB;
+    const size_t shmem = (size_t)B * act_lds_row_bytes(K) + 4 * B * 256;
+    static bool attr_set = false;  // allow up to the full 160 KB of LDS
+    if (!attr_set) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dot<FMT, B>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr_set = true;
+    }
+    // one resident generation of waves, each walking units with stride
+    static ResidentCache cache;  // occupancy depends on K only through shmem: key on it
+    static size_t cache_shmem = 0;
+    if (cache_shmem != shmem) { cache = ResidentCache(); cache_shmem = shmem; }
+    const int64_t resident =
+        4 * resident_blocks(cache, reinterpret_cast<const void*>(&k_dot<FMT, B>), 256, shmem);
+    const int64_t per = (units + resident - 1) / resident;
+    const int64_t waves = (units + per - 1) / per;
+    const int64_t blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((k_dot<FMT, B>), dim3((unsigned)blocks), dim3(256), shmem, s, w, wbytes,
+                       N, K, xq, L, y);
+    return (int)hipGetLastError();
+}
+
+template <int FMT>
+int launch_dot_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t rows,
+                 float* y, hipStream_t s) {
+    switch (rows) {
+    case 1: return launch_dot_b<FMT, 1>(w, N, K, xq, y, s);
+    case 2: return launch_dot_b<FMT, 2>(w, N, K, xq, y, s);
+    case 3: return launch_dot_b<FMT, 3>(w, N, K, xq, y, s);
+    default: return launch_dot_b<FMT, 4>(w, N, K, xq, y, s);
+    }
+}
+
+// Rows of the 16-row activation group each lane needs (see chunk_math).
+inline int ni_for(int64_t rows) { return rows == 1 ? 1 : rows == 2 ? 2 : 4; }
+
+template <int FMT, int NI>
+int launch_qmv_ni(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t rows,
+                  float* y, int32_t* P, hipStream_t s, bool partials) {
     using F = Fmt<FMT>;
     const ActLayout L = act_layout(rows, K);
     const int64_t tiles = (N + 15) / 16;
     const int nb = (int)(K / 32), C = (nb + 7) / 8;
-    const int64_t wgs = tiles * L.G;
-    int KS = 1;
-    while (KS < 8 && wgs * KS < 2048 && KS * 2 <= C) KS *= 2;
-    const size_t shmem = (size_t)KS * 16 * span_stride<FMT>() + (PARTIALS ? 0 : (size_t)KS * 1024);
+    const int64_t TG = tiles * L.G;
     const int64_t wbytes = N * (K / F::QK) * F::BB;
-    hipLaunchKernelGGL((k_qmv<FMT, PARTIALS>), dim3((unsigned)wgs), dim3(64 * KS), shmem, s, w,
-                       wbytes, N, K, xq, L, rows, tiles, y, P);
+    // Enough tiles to fill the chip with independent waves: persistent waves
+    // walking whole tiles.  Otherwise split each tile's chunks over the waves
+    // of a workgroup (<= 8 waves keeps its LDS under 64 KB).
+    const int64_t CHIP_WAVES = 256 * 16;
+    if (!partials && TG >= 2048) {
+        const int64_t per = (TG + CHIP_WAVES - 1) / CHIP_WAVES;  // tiles per wave
+        const int64_t waves = (TG + per - 1) / per;
+        const int64_t blocks = (waves + 3) / 4;
+        hipLaunchKernelGGL((k_qmv_rows<FMT, NI>), dim3((unsigned)blocks), dim3(256),
+                           4 * wave_lds<FMT>(), s, w, wbytes, N, K, xq, L, rows, tiles, y);
+        return (int)hipGetLastError();
+    }
+    int KS = 1;
+    while (KS < 8 && TG * KS < 4096 && KS * 2 <= C) KS *= 2;
+    // the in-order combine gives one thread to each of the 16*rows outputs
+    const int need = (int)((16 * (rows < 16 ? rows : 16) + 63) / 64);
+    if (!partials && KS < need) KS = need;
+    const size_t shmem = (size_t)KS * wave_lds<FMT>() + (partials ? 0 : (size_t)KS * 1024);
+    if (partials)
+        hipLaunchKernelGGL((k_qmv_split<FMT, 4, true>), dim3((unsigned)TG), dim3(64 * KS), shmem, s,
+                           w, wbytes, N, K, xq, L, rows, tiles, y, P);
+    else
+        hipLaunchKernelGGL((k_qmv_split<FMT, NI, false>), dim3((unsigned)TG), dim3(64 * KS), shmem,
+                           s, w, wbytes, N, K, xq, L, rows, tiles, y, P);
     return (int)hipGetLastError();
+}
+
+template <int FMT>
+int launch_qmv_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t rows,
+                 float* y, int32_t* P, hipStream_t s, bool partials) {
+    switch (ni_for(rows)) {
+    case 1: return launch_qmv_ni<FMT, 1>(w, N, K, xq, rows, y, P, s, partials);
+    case 2: return launch_qmv_ni<FMT, 2>(w, N, K, xq, rows, y, P, s, partials);
+    default: return launch_qmv_ni<FMT, 4>(w, N, K, xq, rows, y, P, s, partials);
+    }
 }
 
 }  // namespace
@@ -427,11 +1077,19 @@ int launch_rebuild(uint8_t* xq, int64_t rows, int64_t K, hipStream_t s) {
 
 int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
                int64_t rows, float* y, hipStream_t s) {
+    if (rows <= DOT_MAX_ROWS && rows * act_lds_row_bytes(K) + 4 * rows * 256 <= DOT_MAX_LDS) {
+        switch (type) {
+        case T_Q8_0: return launch_dot_t<T_Q8_0>(w, N, K, xq, rows, y, s);
+        case T_Q4_0: return launch_dot_t<T_Q4_0>(w, N, K, xq, rows, y, s);
+        case T_Q4_K: return launch_dot_t<T_Q4_K>(w, N, K, xq, rows, y, s);
+        case T_Q6_K: return launch_dot_t<T_Q6_K>(w, N, K, xq, rows, y, s);
+        }
+    }
     switch (type) {
-    case T_Q8_0: return launch_qmv_t<T_Q8_0, false>(w, N, K, xq, rows, y, nullptr, s);
-    case T_Q4_0: return launch_qmv_t<T_Q4_0, false>(w, N, K, xq, rows, y, nullptr, s);
-    case T_Q4_K: return launch_qmv_t<T_Q4_K, false>(w, N, K, xq, rows, y, nullptr, s);
-    case T_Q6_K: return launch_qmv_t<T_Q6_K, false>(w, N, K, xq, rows, y, nullptr, s);
+    case T_Q8_0: return launch_qmv_t<T_Q8_0>(w, N, K, xq, rows, y, nullptr, s, false);
+    case T_Q4_0: return launch_qmv_t<T_Q4_0>(w, N, K, xq, rows, y, nullptr, s, false);
+    case T_Q4_K: return launch_qmv_t<T_Q4_K>(w, N, K, xq, rows, y, nullptr, s, false);
+    case T_Q6_K: return launch_qmv_t<T_Q6_K>(w, N, K, xq, rows, y, nullptr, s, false);
     }
     return (int)hipErrorInvalidValue;
 }
@@ -439,10 +1097,10 @@ int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* 
 int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
                     int64_t rows, int32_t* P, hipStream_t s) {
     switch (type) {
-    case T_Q8_0: return launch_qmv_t<T_Q8_0, true>(w, N, K, xq, rows, nullptr, P, s);
-    case T_Q4_0: return launch_qmv_t<T_Q4_0, true>(w, N, K, xq, rows, nullptr, P, s);
-    case T_Q4_K: return launch_qmv_t<T_Q4_K, true>(w, N, K, xq, rows, nullptr, P, s);
-    case T_Q6_K: return launch_qmv_t<T_Q6_K, true>(w, N, K, xq, rows, nullptr, P, s);
+    case T_Q8_0: return launch_qmv_ni<T_Q8_0, 4>(w, N, K, xq, rows, nullptr, P, s, true);
+    case T_Q4_0: return launch_qmv_ni<T_Q4_0, 4>(w, N, K, xq, rows, nullptr, P, s, true);
+    case T_Q4_K: return launch_qmv_ni<T_Q4_K, 4>(w, N, K, xq, rows, nullptr, P, s, true);
+    case T_Q6_K: return launch_qmv_ni<T_Q6_K, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     }
     return (int)hipErrorInvalidValue;
 }

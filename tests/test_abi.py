@@ -28,10 +28,12 @@ def test_exports_every_declared_symbol():
 
 
 def test_act_bytes():
-    # 1 row, K = 896: 28 blocks * 34 = 952 public bytes -> private at 1024;
-    # private = 1 group * 28 * (512 + 3*64)
-    assert g.qmv_act_bytes(1, 896) == 1024 + 28 * 704
-    assert g.qmv_act_bytes(17, 64) == ((17 * 2 * 34 + 255) // 256) * 256 + 2 * 2 * 704
+    # worked by hand from the layout in qmv_internal.h (every part 256-aligned):
+    # 1 row, K = 896 (28 blocks): Q8_0 blocks 952 B; MFMA staging 14336 + 3*1792;
+    # row-major staging 896 + 3*112 -> 22528 bytes
+    assert g.qmv_act_bytes(1, 896) == 22528
+    # 17 rows, K = 64: blocks 1156 B; 2 groups -> 2048 + 3*256; rows 1088 + 3*136
+    assert g.qmv_act_bytes(17, 64) == 6144
     for rows, K in [(0, 32), (1, 31), (1, 0), (1, 48), (-1, 32), (1, (1 << 20) + 32)]:
         assert g.qmv_act_bytes(rows, K) == 0
 

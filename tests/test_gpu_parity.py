@@ -79,7 +79,7 @@ def test_partials_bit_exact(g, fmt, N, K, B):
 
 
 @pytest.mark.parametrize("fmt,N,K", SMALL)
-@pytest.mark.parametrize("B", [1, 2, 5, 16])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 16])
 def test_qmv_against_oracle(g, fmt, N, K, B):
     blob, x = _inputs(fmt, N, K, B, 200 + N)
     y = host(g.matvec(fmt, dev(blob), N, K, x=dev(x)))
@@ -133,7 +133,11 @@ def test_staged_xq_paths(g, fmt, N, K):
     xq2.fill_(0xAB)
     xq2[: B * (K // 32) * 34] = dev(oracle.quantize_act(x))
     g.quantize(None, xq2, rows=B, K=K)
-    assert_bitwise(host(xq2), host(xq), "re-staged xq")
+    pub_end = B * (K // 32) * 34
+    assert_bitwise(host(xq2)[:pub_end], host(xq)[:pub_end], "re-staged xq: Q8_0 blocks")
+    # both staging copies: the MFMA one (partials hook) and the row-major one (B <= 4 GEMV)
+    assert_bitwise(host(g.partials(fmt, w, N, K, xq2, B)), host(g.partials(fmt, w, N, K, xq, B)),
+                   "re-staged xq: MFMA staging")
     assert_bitwise(host(g.matvec(fmt, w, N, K, xq=xq2, B=B)), y_ref, "x=NULL vs x")
     assert_bitwise(host(g.matmul(fmt, w, N, K, xq=xq2, M=B)), y_ref, "qmm x=NULL vs qmv")
 
