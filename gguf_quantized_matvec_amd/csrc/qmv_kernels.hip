@@ -36,7 +36,7 @@ constexpr int T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14;
 // Batch sizes up to this run on the lane-per-chunk v_dot4 kernel, larger ones on MFMA.
 constexpr int DOT_MAX_ROWS = 4;
 // ... as long as their activation rows fit in a workgroup's LDS.
-constexpr int DOT_MAX_LDS = 96 * 1024;
+constexpr int DOT_MAX_ACT_LDS = 96 * 1024;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -635,34 +635,38 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-// bytes of one chunk, loaded from the chunk start
+// Dwords of one chunk as loaded from the 4-byte-aligned address at or below
+// the chunk start (chunks start 2-byte aligned; 16-byte loads at 2-byte
+// alignment lose a quarter of the bandwidth, at 4-byte alignment nothing),
+// then shifted down by 0 or 2 bytes so that r[] holds the chunk from byte 0.
 template <int FMT> struct DotFmt;
-template <> struct DotFmt<T_Q8_0> { static constexpr int NPC = 17; };  // 272 B
-template <> struct DotFmt<T_Q4_0> { static constexpr int NPC = 9; };   // 144 B
-template <> struct DotFmt<T_Q4_K> { static constexpr int NPC = 9; };   // 144 B
-template <> struct DotFmt<T_Q6_K> { static constexpr int NPC = 14; };  // 210 B (+14)
+// NWD = ceil(CB/4) dwords after the shift, plus the one the shift reads from.
+template <> struct DotFmt<T_Q8_0> { static constexpr int NWD = 69; };  // 272 B: 68 + 1
+template <> struct DotFmt<T_Q4_0> { static constexpr int NWD = 37; };  // 144 B: 36 + 1
+template <> struct DotFmt<T_Q4_K> { static constexpr int NWD = 36; };  // 144 B, aligned
+template <> struct DotFmt<T_Q6_K> { static constexpr int NWD = 54; };  // 210 B: 53 + 1
 
 template <int FMT>
-__device__ __forceinline__ void load_chunk_regs(const uint8_t* cs, bool guarded, int64_t room,
-                                                uint32_t (&r)[4 * DotFmt<FMT>::NPC]) {
-    constexpr int NPC = DotFmt<FMT>::NPC;
-    const uint8_t* p = static_cast<const uint8_t*>(__builtin_assume_aligned(cs, 2));
+__device__ __forceinline__ void load_chunk_regs(const uint8_t* w, int64_t off, int64_t wbytes,
+                                                bool guarded, uint32_t (&r)[DotFmt<FMT>::NWD]) {
+    constexpr int NWD = DotFmt<FMT>::NWD;
+    const int64_t off4 = off & ~int64_t(3);
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(w + off4);
     if (!guarded) {
-#pragma unroll
-        for (int i = 0; i < NPC; i++) __builtin_memcpy(&r[4 * i], p + 16 * i, 16);
+        __builtin_memcpy(r, p, 4 * NWD);
     } else {
-        // blob end inside the loaded range: full pieces, then bytes
+        // blob end inside the loaded range: dwords, then the final half dword
 #pragma unroll
-        for (int i = 0; i < NPC; i++) {
-            if (16 * i + 16 <= room) {
-                __builtin_memcpy(&r[4 * i], p + 16 * i, 16);
-            } else {
-                uint32_t b[4] = {0, 0, 0, 0};
-                for (int j = 0; j < 16; j++)
-                    if (16 * i + j < room) b[j >> 2] |= (uint32_t)p[16 * i + j] << (8 * (j & 3));
-                r[4 * i] = b[0]; r[4 * i + 1] = b[1]; r[4 * i + 2] = b[2]; r[4 * i + 3] = b[3];
-            }
+        for (int j = 0; j < NWD; j++) {
+            const int64_t g = off4 + 4 * j;
+            r[j] = g + 4 <= wbytes ? p[j]
+                 : g + 2 <= wbytes ? (uint32_t)*reinterpret_cast<const uint16_t*>(w + g) : 0u;
         }
+    }
+    if (FMT != T_Q4_K) {
+        const uint32_t sh = (uint32_t)(off & 3);  // 0 or 2
+#pragma unroll
+        for (int j = 0; j < NWD - 1; j++) r[j] = __builtin_amdgcn_alignbyte(r[j + 1], r[j], sh);
     }
 }
 
@@ -694,7 +698,7 @@ __host__ __device__ inline int act_lds_row_bytes(int64_t K) {
 
 // p[m] = sum over the chunk's blocks in order (documented f32 order).
 template <int FMT, int B>
-__device__ __forceinline__ void dot_chunk(const uint32_t (&r)[4 * DotFmt<FMT>::NPC],
+__device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                                           const ActRow (&A)[B], int c, int nbc, float (&p)[B]) {
 #pragma unroll
     for (int m = 0; m < B; m++) p[m] = 0.0f;
@@ -813,13 +817,19 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[4 * DotFmt<FMT>::N
 // 64/LPR rows (LPR = lanes per row, a power of two >= C) in one pass.
 // C > 64: a unit is one row, in passes of 64 chunks.  Chunk sums are added
 // in chunk order per row through a small LDS buffer.
+// Persistent waves over work units.  C <= 64 chunks per row: a unit is G =
+// 64/LPR rows (LPR = lanes per row, a power of two >= C) in one pass.
+// C > 64: a unit is one row, in passes of 64 chunks.  Every lane streams its
+// chunk straight into registers; at this register count many waves stay
+// resident, which keeps enough bytes in flight to cover HBM latency.  Chunk
+// sums are added in chunk order per row through a small LDS buffer.
 template <int FMT, int B>
 __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int64_t wbytes,
                                              int64_t N, int64_t K,
                                              const uint8_t* __restrict__ xq, ActLayout L,
                                              float* __restrict__ y) {
     using F = Fmt<FMT>;
-    constexpr int NPC = DotFmt<FMT>::NPC;
+    constexpr int NWD = DotFmt<FMT>::NWD;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int nb = (int)(K >> 5), C = (nb + 7) >> 3;
@@ -835,28 +845,32 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
     const int64_t TW = (int64_t)gridDim.x * (blockDim.x >> 6);
     const int64_t first = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
     // items of this wave: (unit first + k*TW, pass q), k-major
-    const int64_t nit = ((units - first + TW - 1) / TW) * PR;
+    const int64_t nit = first < units ? ((units - first + TW - 1) / TW) * PR : 0;
 
-    // issue the loads of item `it` into r (zeros for lanes without a chunk)
-    auto issue = [&](int64_t it, uint32_t (&r)[4 * NPC]) {
-        const int64_t u = first + (it / PR) * TW;
-        const int q = (int)(it % PR);
-        const int64_t row = C <= 64 ? u * G + lane / LPR : u;
-        const int c = C <= 64 ? (lane & (LPR - 1)) : 64 * q + lane;
+    auto slot = [&](int64_t it, int64_t& u, int& q, int64_t& row, int& c) {
+        u = first + (it / PR) * TW;
+        q = (int)(it % PR);
+        row = C <= 64 ? u * G + lane / LPR : u;
+        c = C <= 64 ? (lane & (LPR - 1)) : 64 * q + lane;
+    };
+    auto issue = [&](int64_t it, uint32_t (&r)[NWD]) {
+        int64_t u, row;
+        int q, c;
+        slot(it, u, q, row, c);
         const bool valid = row < N && c < C;
         const int64_t off = row * R + (int64_t)c * F::CB;
-        const int64_t room = wbytes - off;
-        const bool near_end = valid && room < 16 * NPC;
+        const bool near_end = valid && off + 4 * NWD > wbytes;
+        if (valid) {
+            load_chunk_regs<FMT>(w, off, wbytes, __builtin_amdgcn_ballot_w64(near_end) != 0, r);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4 * NPC; i++) r[i] = 0;
-        if (valid)
-            load_chunk_regs<FMT>(w + off, __builtin_amdgcn_ballot_w64(near_end) != 0, room, r);
+            for (int i = 0; i < NWD; i++) r[i] = 0;
+        }
     };
 
-
     // first chunk in flight while the activations are staged
-    uint32_t ra[4 * NPC], rb[4 * NPC];
-    if (first < units) issue(0, ra);
+    uint32_t r[NWD];
+    if (nit > 0) issue(0, r);
 
     // stage the B activation rows: codes (per-chunk padded), da, ca, s16
     ActRow A[B];
@@ -881,16 +895,15 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
         }
     }
     __syncthreads();
+    if (nit == 0) return;
 
     float yacc[B];
 #pragma unroll
     for (int j = 0; j < B; j++) yacc[j] = 0.0f;
-    // reduce and (at a unit's last pass) write item `it`, whose chunk is in r
-    auto work = [&](int64_t it, const uint32_t (&r)[4 * NPC]) {
-        const int64_t u = first + (it / PR) * TW;
-        const int q = (int)(it % PR);
-        const int64_t row = C <= 64 ? u * G + lane / LPR : u;
-        const int c = C <= 64 ? (lane & (LPR - 1)) : 64 * q + lane;
+    for (int64_t it = 0; it < nit; it++) {
+        int64_t u, row;
+        int q, c;
+        slot(it, u, q, row, c);
         const bool valid = row < N && c < C;
         const int nbc = F::QK == 32 ? min(8, nb - 8 * c) : 8;
         float p[B];
@@ -900,6 +913,7 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
 #pragma unroll
             for (int m = 0; m < B; m++) p[m] = 0.0f;
         }
+        if (it + 1 < nit) issue(it + 1, r);  // registers are free again
 #pragma unroll
         for (int m = 0; m < B; m++) pbuf[m][lane] = p[m];
         wave_sync();
@@ -926,19 +940,6 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
                 yacc[j] = 0.0f;
             }
         }
-    };
-
-    // two register sets: the next item's chunk is in flight while this one
-    // is decoded and multiplied
-    if (first >= units) return;
-    int64_t it = 0;
-    while (true) {
-        if (it + 1 < nit) issue(it + 1, rb);
-        work(it, ra);
-        if (++it >= nit) break;
-        if (it + 1 < nit) issue(it + 1, ra);
-        work(it, rb);
-        if (++it >= nit) break;
     }
 }
 
@@ -1077,7 +1078,7 @@ int launch_rebuild(uint8_t* xq, int64_t rows, int64_t K, hipStream_t s) {
 
 int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
                int64_t rows, float* y, hipStream_t s) {
-    if (rows <= DOT_MAX_ROWS && rows * act_lds_row_bytes(K) + 4 * rows * 256 <= DOT_MAX_LDS) {
+    if (rows <= DOT_MAX_ROWS && rows * act_lds_row_bytes(K) + 4 * rows * 256 <= DOT_MAX_ACT_LDS) {
         switch (type) {
         case T_Q8_0: return launch_dot_t<T_Q8_0>(w, N, K, xq, rows, y, s);
         case T_Q4_0: return launch_dot_t<T_Q4_0>(w, N, K, xq, rows, y, s);
