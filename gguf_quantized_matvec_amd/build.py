@@ -11,7 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmv.so")
-SOURCES = [os.path.join(CSRC, "qmv_kernels.hip"), os.path.join(CSRC, "qmv_api.cpp")]
+SOURCES = [os.path.join(CSRC, "qmv_kernels.hip"), os.path.join(CSRC, "qmm_kernels.hip"),
+           os.path.join(CSRC, "qmv_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -26,7 +27,7 @@ FLAGS = [
 
 def build() -> str:
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-x", "hip", SOURCES[0], "-x", "hip", SOURCES[1], "-o", tmp]
+    cmd = [HIPCC, *FLAGS, "-x", "hip", *SOURCES, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

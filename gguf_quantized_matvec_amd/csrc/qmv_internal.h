@@ -23,8 +23,11 @@ namespace qmv {
 //     rca    [rows][nb] f32        as ca
 //     rs16   [rows][nb] int32      sums of the two 16-element halves as two
 //                                  int16: low half = elements 0..15
+//   for the prefill GEMM (f16 MFMA; small integers are exact in f16):
+//     hcodes [rows][K] f16         codes as f16 values
+//     hda    [rows][nb] u16        fp16 bits of the block scale
 struct ActLayout {
-    int64_t nb, G, pub, priv0, codes, da, ca, S, rcodes, rda, rca, rs16, total;
+    int64_t nb, G, pub, priv0, codes, da, ca, S, rcodes, rda, rca, rs16, hcodes, hda, total;
 };
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
@@ -43,7 +46,9 @@ inline ActLayout act_layout(int64_t rows, int64_t K) {
     L.rda = align256(L.rcodes + rows * K);
     L.rca = align256(L.rda + rows * L.nb * 4);
     L.rs16 = align256(L.rca + rows * L.nb * 4);
-    L.total = align256(L.rs16 + rows * L.nb * 4);
+    L.hcodes = align256(L.rs16 + rows * L.nb * 4);
+    L.hda = align256(L.hcodes + rows * K * 2);
+    L.total = align256(L.hda + rows * L.nb * 2);
     return L;
 }
 
@@ -57,5 +62,8 @@ int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, const uint
                     int64_t rows, int32_t* P, hipStream_t s);
 int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
                int64_t rows, float* y, hipStream_t s);
+// Prefill GEMM on f16 MFMA (qmm_kernels.hip), for rows > 16.
+int launch_gemm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
+                float* y, hipStream_t s);
 
 }  // namespace qmv

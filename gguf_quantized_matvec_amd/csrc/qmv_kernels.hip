@@ -145,6 +145,28 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x,
         reinterpret_cast<float*>(xq + L.rca)[r * nb + b] = dval * (float)S;
         reinterpret_cast<int32_t*>(xq + L.rs16)[r * nb + b] =
             (int32_t)(((uint32_t)s_lo & 0xFFFFu) | ((uint32_t)s_hi << 16));
+        // f16 copy for the GEMM: code values are exact in f16
+        uint4* hc = reinterpret_cast<uint4*>(xq + L.hcodes + (r * K + 32 * b) * 2);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            uint32_t hw[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const _Float16 lo = (_Float16)(float)(int8_t)q[8 * j + 2 * t];
+                const _Float16 hi = (_Float16)(float)(int8_t)q[8 * j + 2 * t + 1];
+                uint16_t ul, uh;
+                __builtin_memcpy(&ul, &lo, 2);
+                __builtin_memcpy(&uh, &hi, 2);
+                hw[t] = (uint32_t)ul | ((uint32_t)uh << 16);
+            }
+            hc[j] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        }
+        uint16_t dbits = 0;
+        {
+            const _Float16 dh = (_Float16)dval;  // exact: dval came from fp16
+            __builtin_memcpy(&dbits, &dh, 2);
+        }
+        reinterpret_cast<uint16_t*>(xq + L.hda)[r * nb + b] = dbits;
     }
 }
 
@@ -1108,7 +1130,8 @@ int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, const uint
 
 int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
                int64_t rows, float* y, hipStream_t s) {
-    return launch_qmv(type, w, N, K, xq, rows, y, s);
+    if (rows <= 16) return launch_qmv(type, w, N, K, xq, rows, y, s);
+    return launch_gemm(type, w, N, K, xq, rows, y, s);
 }
 
 }  // namespace qmv

@@ -30,10 +30,11 @@ def test_exports_every_declared_symbol():
 def test_act_bytes():
     # worked by hand from the layout in qmv_internal.h (every part 256-aligned):
     # 1 row, K = 896 (28 blocks): Q8_0 blocks 952 B; MFMA staging 14336 + 3*1792;
-    # row-major staging 896 + 3*112 -> 22528 bytes
-    assert g.qmv_act_bytes(1, 896) == 22528
-    # 17 rows, K = 64: blocks 1156 B; 2 groups -> 2048 + 3*256; rows 1088 + 3*136
-    assert g.qmv_act_bytes(17, 64) == 6144
+    # row-major staging 896 + 3*112; f16 staging 1792 + 56 -> 24576 bytes
+    assert g.qmv_act_bytes(1, 896) == 24576
+    # 17 rows, K = 64: blocks 1156 B; 2 groups -> 2048 + 3*256; rows 1088 + 3*136;
+    # f16 rows 2176 + 68 -> 8704 bytes
+    assert g.qmv_act_bytes(17, 64) == 8704
     for rows, K in [(0, 32), (1, 31), (1, 0), (1, 48), (-1, 32), (1, (1 << 20) + 32)]:
         assert g.qmv_act_bytes(rows, K) == 0
 
