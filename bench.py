@@ -11,12 +11,17 @@ than from the 256 MB last-level cache.  Steps are replayed from a captured
 HIP graph (the path is launch-bound at this size).
 
 Prints ONE JSON line: metric/value (weight GB/s of the timed steps, wall
-clock), the roofline of the dominant kernel (the GEMV; per-launch durations
-from HIP timing events recorded inside the graph, on the launch stream), the
-CPU oracle timed on a bounded sample of the same step, and (unless
---no-suite) per-matrix GEMV/GEMM figures for every workload shape.
+clock), the roofline of the dominant kernel (the GEMV; execution times from
+HIP events that each kernel records at its own start and end on the stream it
+runs on), the CPU oracle timed on a bounded sample of the same step, and
+(with --suite) per-matrix GEMV/GEMM figures for every workload shape.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--suite]
+
+Counter collection helpers: --profile-steps N (eager steps only),
+--copy-calib (a 256 MiB copy, the counters' byte calibration) and
+--traffic-from DIR (turns their rocprofv3 --pmc output into
+profiles/traffic.json).
 """
 from __future__ import annotations
 
@@ -49,56 +54,42 @@ def gemv_alg_bytes(fmt, N, K, B, g) -> int:
 
 
 class GraphSteps:
-    """Capture `nsteps` calls of step(i) into one HIP graph, optionally with
-    external timing events around the launches that step() marks."""
+    """`nsteps` calls of step(i) captured into one HIP graph."""
 
-    def __init__(self, torch, step, nsteps, timed):
-        self.torch = torch
-        self.events = []
+    def __init__(self, torch, step, nsteps):
         self.graph = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             with torch.cuda.graph(self.graph, stream=s):
                 for i in range(nsteps):
-                    step(i, self._mark if timed else None)
+                    step(i, None)
         torch.cuda.current_stream().wait_stream(s)
         self.nsteps = nsteps
-
-    def _mark(self, tag):
-        ev = self.torch.cuda.Event(enable_timing=True, external=True)
-        ev.record()
-        self.events.append((tag, ev))
 
     def replay(self):
         self.graph.replay()
 
-    def durations_ms(self):
-        """(tag, ms) for each start/end pair recorded in the last replay."""
-        out = []
-        for k in range(0, len(self.events), 2):
-            (tag, e0), (_, e1) = self.events[k], self.events[k + 1]
-            out.append((tag, e0.elapsed_time(e1)))
-        return out
 
-
-def eager_durations(torch, step, nsteps):
-    """Per-launch durations with ordinary timing events around eager launches.
-    A spin kernel queued first lets the host enqueue everything before the GPU
-    starts, so each event pair brackets GPU execution only."""
-    evs = []
-
-    def mark(tag):
-        ev = torch.cuda.Event(enable_timing=True)
-        ev.record()
-        evs.append((tag, ev))
-
+def graph_launch_us(torch, launch, n, reps=3):
+    """Average time per launch of `n` back-to-back launches of one kernel
+    (launch(i) enqueues launch i), captured into a HIP graph and replayed
+    between two HIP events on the stream the kernels run on.  The figure is
+    the kernel's execution time plus the short dispatch gap between
+    consecutive graph nodes; the median over `reps` replays is returned."""
+    G = GraphSteps(torch, lambda i, _: launch(i), n)
+    G.replay()                               # warm
     torch.cuda.synchronize()
-    torch.cuda._sleep(200_000_000)
-    for i in range(nsteps):
-        step(i, mark)
-    torch.cuda.synchronize()
-    return [(evs[k][0], evs[k][1].elapsed_time(evs[k + 1][1])) for k in range(0, len(evs), 2)]
+    s = torch.cuda.current_stream()
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        G.replay()
+        e1.record(s)
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / n)
+    return sorted(out)[len(out) // 2]
 
 
 def run_steps(graphs, make, n):
@@ -109,7 +100,7 @@ def run_steps(graphs, make, n):
     r = n % full.nsteps
     if r:
         if r not in graphs:
-            graphs[r] = make(r, False)
+            graphs[r] = make(r)
         graphs[r].replay()
 
 
@@ -145,18 +136,20 @@ def make_ffn_step(torch, g, W):
         if rc:
             raise g.QmvError(rc, what)
 
-    def step(i, mark):
+    def gemv(name, c):
+        N, K, q = (896, 4864, q2) if name == "down" else (4864, 896, q1)
+        s = torch.cuda.current_stream().cuda_stream
+        check(L.qmv_launch(fmt, ptr[name][c], N, K, None, 1, q, y[name], s), name)
+
+    def step(i, _unused=None):
         s = torch.cuda.current_stream().cuda_stream
         c = i % R
         check(L.quantize_act_q8_0(x1, q1, 1, 896, s), "quantize")
-        for name, N, K, q in (("gate", 4864, 896, q1), ("up", 4864, 896, q1)):
-            if mark: mark(name)
-            check(L.qmv_launch(fmt, ptr[name][c], N, K, None, 1, q, y[name], s), name)
-            if mark: mark(name)
+        gemv("gate", c)
+        gemv("up", c)
         check(L.quantize_act_q8_0(x2, q2, 1, 4864, s), "quantize")
-        if mark: mark("down")
-        check(L.qmv_launch(fmt, ptr["down"][c], 896, 4864, None, 1, q2, y["down"], s), "down")
-        if mark: mark("down")
+        gemv("down", c)
+    step.gemv = gemv
     return step
 
 
@@ -209,11 +202,12 @@ def cpu_baseline(W, seconds):
                       f"{dt:.1f} s; tok/s {steps / dt:.2f}"}
 
 
-def suite(torch, g, synth, rotate_bytes, reps=3):
+def suite(torch, g, synth, rotate_bytes):
     """Per-matrix figures for every workload shape: GEMV at each decode batch
-    (weight GB/s) and GEMM at each prefill size (int8 TOPS), from timing events
-    inside captured graphs over rotated weight copies."""
+    (weight GB/s) and GEMM at each prefill size (int8-equivalent TOPS), from
+    the time per launch of back-to-back graph launches over rotated copies."""
     res = []
+    L = g.lib()
     for wl, spec in synth.WORKLOADS.items():
         ci = list(synth.WORKLOADS).index(wl)
         for mi, (fmt, N, K, ds) in enumerate(spec["mats"]):
@@ -226,29 +220,16 @@ def suite(torch, g, synth, rotate_bytes, reps=3):
                 x = torch.from_numpy(synth.activations(B, K, synth.act_seed_for(ci, B))).cuda()
                 xq = g.quantize(x)
                 y = torch.empty(B, N, dtype=torch.float32, device="cuda")
-                L = g.lib()
                 fn = L.qmv_launch if B <= 16 else L.qmm_launch
 
-                def step(i, mark, fn=fn, B=B, xq=xq, y=y):
-                    s = torch.cuda.current_stream().cuda_stream
-                    if mark: mark("k")
+                def launch(i, fn=fn, B=B, xq=xq, y=y):
                     rc = fn(fmt, copies[i % R].data_ptr(), N, K, None, B, xq.data_ptr(),
-                            y.data_ptr(), s)
-                    if mark: mark("k")
+                            y.data_ptr(), torch.cuda.current_stream().cuda_stream)
                     if rc:
                         raise g.QmvError(rc, "suite")
-                step(0, None)
-                torch.cuda.synchronize()
-                try:
-                    G = GraphSteps(torch, step, R, True)
-                    for _ in range(reps):
-                        G.replay()
-                    torch.cuda.synchronize()
-                    d = sorted(ms for _, ms in G.durations_ms())
-                except Exception:
-                    G = None
-                    d = sorted(ms for _, ms in eager_durations(torch, step, R))
-                med = d[len(d) // 2] * 1e-3
+                launch(0)
+                n = max(R, 20) if B <= 16 else max(min(R, 10), 5)
+                med = graph_launch_us(torch, launch, n) * 1e-6
                 row = {"workload": wl, "fmt": synth.NAMES[fmt], "N": N, "K": K, "rows": B,
                        "us": round(med * 1e6, 2), "weight_MB": round(nbytes / 1e6, 2)}
                 if B <= 16:
@@ -259,10 +240,50 @@ def suite(torch, g, synth, rotate_bytes, reps=3):
                     tops = 2.0 * B * N * K / med / 1e12
                     row.update(int8_TOPS=round(tops, 1), mfma_frac=round(tops / INT8_PEAK_TOPS, 4))
                 res.append(row)
-                del G, x, xq, y
+                print(json.dumps({"suite_row": row}), file=sys.stderr, flush=True)
+                del x, xq, y
             del copies, wt
             torch.cuda.empty_cache()
     return res
+
+
+def traffic_from(pmc_dir):
+    """profiles/traffic.json from four rocprofv3 --pmc runs under pmc_dir:
+    fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of `bench.py --profile-steps`),
+    calib_fetch/ and calib_write/ (the same counters of `bench.py --copy-calib`).
+    Each counter is scaled by true bytes / counted bytes of the plain copy."""
+    import csv
+    import glob
+
+    def rows(sub, counter):
+        out = []
+        for f in glob.glob(os.path.join(pmc_dir, sub, "**", "*counter_collection.csv"),
+                           recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Counter_Name") == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        if not out:
+            raise SystemExit(f"no {counter} rows under {os.path.join(pmc_dir, sub)}")
+        return out
+
+    def copy_kib(sub, counter):
+        # the largest dispatch of the calibration run is the 256 MiB copy
+        return max(v for _, v in rows(sub, counter))
+
+    copy_bytes = 256 << 20
+    f_scale = copy_bytes / (copy_kib("calib_fetch", "FETCH_SIZE") * 1024)
+    w_scale = copy_bytes / (copy_kib("calib_write", "WRITE_SIZE") * 1024)
+    fk = [v for k, v in rows("fetch", "FETCH_SIZE") if "k_dot" in k]
+    wk = [v for k, v in rows("write", "WRITE_SIZE") if "k_dot" in k]
+    fetch = sum(fk) / len(fk) * 1024 * f_scale
+    write = sum(wk) / len(wk) * 1024 * w_scale
+    out = {"kernel": "k_dot (GEMV, Q4_0, batch 1)", "kernel_src_sha": kernel_src_sha(),
+           "dispatches": [len(fk), len(wk)],
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+           "bytes_per_launch": round(fetch + write)}
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out))
 
 
 def main():
@@ -273,14 +294,23 @@ def main():
     ap.add_argument("--rotate-mib", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-suite", action="store_true")
+    ap.add_argument("--suite", action="store_true",
+                    help="also report every workload matrix (GEMV and GEMM) separately")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run this many eager steps (for counter collection)")
+    ap.add_argument("--traffic-from", default=None,
+                    help="write profiles/traffic.json from rocprofv3 --pmc output under DIR")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 256 MiB device copy 10 times (counter calibration)")
     args = ap.parse_args()
 
+    if args.traffic_from:
+        traffic_from(args.traffic_from)
+        return
+
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the multiply shards by weight rows with no cross-GPU "
               f"reduction, so per-GPU throughput is the single-GPU figure", file=sys.stderr)
         sys.exit(2)
@@ -310,45 +340,38 @@ def main():
     step = make_ffn_step(torch, g, W)
     step(0, None)                       # eager run: device check, lazy init
     torch.cuda.synchronize()
+    if args.profile_steps:
+        for i in range(args.profile_steps):
+            step(i, None)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps}))
+        return
 
     graphs = {}
 
-    def make(n, timed):
-        return GraphSteps(torch, step, n, timed)
+    def make(n):
+        return GraphSteps(torch, step, n)
 
-    try:
-        graphs["full"] = make(W["R"], True)
-        event_mode = "events recorded inside the replayed graph"
-    except Exception as e:  # timing events as graph nodes unsupported: time eagerly
-        print(f"bench.py: graph timing events unavailable ({e}); timing launches eagerly",
-              file=sys.stderr)
-        graphs["full"] = make(W["R"], False)
-        event_mode = None
+    graphs["full"] = make(W["R"])
     run_steps(graphs, make, args.warmup)
     torch.cuda.synchronize()
 
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     run_steps(graphs, make, args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    if args.steps < graphs["full"].nsteps:   # make sure the event graph ran at least once
-        graphs["full"].replay()
-        torch.cuda.synchronize()
 
-    if event_mode:
-        durs = graphs["full"].durations_ms()
-    else:
-        durs = eager_durations(torch, step, W["R"])
-        event_mode = "events around eager launches queued behind a spin kernel"
+    # the dominant kernel, the GEMV: time per launch of the step's three GEMVs
+    # back to back over every rotated copy (the activations stay staged)
+    order = ("gate", "up", "down")
+    per_launch_us = graph_launch_us(
+        torch, lambda i: step.gemv(order[i % 3], (i // 3) % W["R"]), 3 * W["R"])
     alg = {"gate": gemv_alg_bytes(W["fmt"], 4864, 896, 1, g),
            "up": gemv_alg_bytes(W["fmt"], 4864, 896, 1, g),
            "down": gemv_alg_bytes(W["fmt"], 896, 4864, 1, g)}
-    tot_ms = sum(ms for _, ms in durs)
-    tot_bytes = sum(alg[t] for t, _ in durs)
-    achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
-    avg_us = tot_ms * 1e3 / len(durs)
+    alg_per_launch = sum(alg.values()) / 3
+    achieved = alg_per_launch / (per_launch_us * 1e-6) / 1e9
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -368,7 +391,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8 x i8 -> i32 (MFMA), f32 scale-accumulate",
+        "dtype": "i8",
         "data": "synthetic (seeded GGUF Q4_0 blocks and N(0,1) activations)",
         "config": {"workload": "Q4_0 SwiGLU FFN decode, batch 1: gate+up 4864x896, down 896x4864 "
                                "(llamay Qwen2.5-0.5B shapes)",
@@ -379,13 +402,16 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "k_qmv<Q4_0> (GEMV)", "avg_launch_us": round(avg_us, 3),
-                     "launches_timed": len(durs), "timing": event_mode,
+                     "kernel": "k_dot<Q4_0, 1> (GEMV)", "avg_launch_us": round(per_launch_us, 3),
+                     "launches_timed": 3 * W["R"],
+                     "timing": "HIP events on the launch stream around a graph replay of the "
+                               "step's GEMVs (gate, up, down) back to back over every rotated "
+                               "copy; time per launch includes the inter-node dispatch gap",
                      "alg_bytes_per_launch": {"4864x896": alg["gate"], "896x4864": alg["down"]}},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
-    if not args.no_suite:
+    if args.suite:
         del graphs
         W.clear()
         torch.cuda.empty_cache()

@@ -104,9 +104,12 @@ int quantize_act_q8_0(const float* x, void* xq, int64_t rows, int64_t K, void* s
 int qmv_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
                void* xq, float* y, void* stream);
 
-/* Prefill GEMM (MatMul): y[M][N] = x[M][K] * W^T for any M >= 1, on int8
- * MFMA.  Same x / xq contract as qmv_launch with qmv_act_bytes(M, K) bytes.
- * Each row of y is bit-identical to qmv_launch with B = 1 on that row. */
+/* Prefill GEMM (MatMul): y[M][N] = x[M][K] * W^T for any M >= 1.  Prefill
+ * is the arithmetic-bound phase ("Architecture", bench transcript): for
+ * M > 16 the integer block dots run on the matrix cores (f16 MFMA, which is
+ * exact on these small integers); M <= 16 runs the GEMV.  Same x / xq
+ * contract as qmv_launch with qmv_act_bytes(M, K) bytes.  Each row of y is
+ * bit-identical to qmv_launch with B = 1 on that row. */
 int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t M,
                void* xq, float* y, void* stream);
 
