@@ -6,27 +6,36 @@
 // cost is not the integer dot but the per-block scaling: every (row, column,
 // 32-block) needs its own f32 term added in the documented order.  Two facts
 // measured on the hardware keep that to one VALU fma per output and block:
-//   * f16 MFMA on small integers is exact: codes (|a| <= 127; weights |w| <=
-//     945 after folding Q4_K's 6-bit sub-scale in) are exact in f16, their
-//     products and sums (< 2^24) are exact in the f32 accumulator, so
-//     v_mfma_f32_32x32x16_f16 returns the exact integer block partial;
+//   * f16 MFMA on small integers is exact: codes (|a| <= 127; weights with
+//     the sub-scale folded in, |w| <= 945 for Q4_K and <= 4096 and even or
+//     <= 2048 for Q6_K) are exact in f16, their products and sums (< 2^24)
+//     are exact in the f32 accumulator, so v_mfma_f32_32x32x16_f16 returns
+//     the exact integer block partial;
 //   * the product of two fp16 values is exact in f32 (subnormals included),
 //     so a rank-1 MFMA (one nonzero k) gives every d_w * d_a of a 32x32 tile.
 // Then p = fma(I, d_w*d_a, p) is exactly the term the GEMV adds, and rows are
-// bit-identical to the batch-1 GEMV.
+// bit-identical to the batch-1 GEMV.  Q4_K's min term is fma(-(dmin*m_j),
+// d_a*S, p) with both products exact (S: the block's activation code sum),
+// which is the same real product as the documented (m_j*S)*(dmin*d_a).
 //
-// Tiling: a workgroup owns 128 x 128 outputs (4 waves of 64 x 64, each 2 x 2
-// MFMA tiles of 32 x 32) and walks K one 256-element chunk (8 blocks) at a
-// time.  Each thread fetches half a chunk of one activation row and one weight
-// row into registers; after the chunk in LDS has been consumed it decodes the
-// weights to f16 and stores both, then issues the loads of the next chunk,
-// which stay in flight while the 8 blocks are multiplied.  LDS rows are XOR
-// swizzled in 16-byte pieces so that MFMA fragment reads spread over all
-// banks.  Workgroups are ordered in groups of 8 M-tiles and mapped so that
-// each XCD runs a contiguous range of them: concurrently resident workgroups
-// on one XCD share activation and weight tiles through its L2.
+// Tiling: a workgroup of 8 waves owns 128 x 128 outputs; wave w computes rows
+// 64*(w&1) .. +63 and columns 32*(w>>1) .. +31 (2 x 1 MFMA tiles of 32 x 32),
+// two waves per SIMD.  K is walked 128 elements (4 blocks) per step.  The
+// activation tile (f16 codes) goes global -> LDS directly with
+// global_load_lds into a double buffer; each thread fetches one weight block
+// into registers, decodes it to f16 into LDS after the previous step is
+// consumed, and then issues the next step's loads, which stay in flight
+// while the 4 blocks are multiplied.  Per block and wave the multiply is 6
+// MFMAs (2 x (2 integer + 1 rank-1 scale)) against 32 VALU fmas (64 for
+// Q4_K), read from ready-made LDS operands.  LDS rows are XOR swizzled in 16-byte
+// pieces so that MFMA fragment reads hit all banks.  Workgroups are ordered
+// in groups of 8 M-tiles and mapped so that each XCD runs a contiguous range
+// of them: concurrently resident workgroups on one XCD share activation and
+// weight tiles through its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "qmv_internal.h"
 
@@ -36,9 +45,14 @@ namespace {
 constexpr int T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14;
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int TM = 128, TN = 128;
+constexpr int TM = 128, TN = 128;   // workgroup tile
+constexpr int SB = 4;               // 32-element blocks per K step
+constexpr int PR = 4 * SB;          // 16-byte pieces per tile row per step
+constexpr int NA = 2;               // activation steps resident in LDS (1 in flight)
 
 template <int FMT> struct GFmt;
 template <> struct GFmt<T_Q8_0> { static constexpr int QK = 32, BB = 34; };
@@ -46,67 +60,47 @@ template <> struct GFmt<T_Q4_0> { static constexpr int QK = 32, BB = 18; };
 template <> struct GFmt<T_Q4_K> { static constexpr int QK = 256, BB = 144; };
 template <> struct GFmt<T_Q6_K> { static constexpr int QK = 256, BB = 210; };
 
-__device__ __forceinline__ uint32_t ldu16(const uint8_t* p) {
-    return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
-}
 __device__ __forceinline__ _Float16 h_of_bits(uint32_t b) {
     const uint16_t u = (uint16_t)b;
     _Float16 h;
     __builtin_memcpy(&h, &u, 2);
     return h;
 }
-__device__ __forceinline__ float f_of_hbits(uint32_t b) { return (float)h_of_bits(b); }
 
-// Scale fields of one weight row and 32-block.
-struct WRow {
-    uint32_t d;     // fp16 bits: block / superblock d
-    uint32_t dmin;  // Q4_K: fp16 bits of dmin
-    int sc, mn;     // Q4_K: 6-bit scale and min of the sub-block
-    int s0, s1;     // Q6_K: int8 sub-scales of the two 16-element halves
-};
-
-// Weight bytes one staging thread fetches per chunk: the four 32-blocks
-// 4*half .. 4*half+3 of its row's chunk (K-quants: the superblock's header
-// and the quarter of codes those sub-blocks use).
+// Weight bytes one staging thread fetches per step: one 32-element block of
+// one row (K-quants: the fields of the superblock that block uses).
 template <int FMT> struct WRaw;
-template <> struct WRaw<T_Q8_0> { uint32_t v[34]; };   // 4 x 34 B
-template <> struct WRaw<T_Q4_0> { uint32_t v[18]; };   // 4 x 18 B
-template <> struct WRaw<T_Q4_K> { uint32_t hdr[4]; uint32_t q[16]; };   // 16 B + 64 B of qs
-template <> struct WRaw<T_Q6_K> { uint32_t ql[16]; uint32_t qh[8]; uint32_t s[2]; uint32_t d; };
+template <> struct WRaw<T_Q8_0> { uint32_t v[9]; };    // 34 B
+template <> struct WRaw<T_Q4_0> { uint32_t v[5]; };    // 18 B
+template <> struct WRaw<T_Q4_K> { uint32_t hdr[4]; uint32_t q[8]; };   // d, dmin, sc12; 32 B of qs
+template <> struct WRaw<T_Q6_K> { uint32_t ql[8]; uint32_t qh[8]; uint32_t sd; };  // s pair | d << 16
 
-// Fetch chunk c, half `half` of a weight row (blocks are 2-byte aligned).
+// Block b (< nb) of a weight row.
 template <int FMT>
-__device__ __forceinline__ void fetch_w(const uint8_t* row, int c, int half, int nbc,
-                                        WRaw<FMT>& r) {
+__device__ __forceinline__ void fetch_w(const uint8_t* row, int b, WRaw<FMT>& r) {
     if constexpr (FMT == T_Q8_0 || FMT == T_Q4_0) {
-        constexpr int BB = FMT == T_Q8_0 ? 34 : 18;
-        const uint8_t* p = row + (int64_t)(8 * c + 4 * half) * BB;
-        const int nblk = nbc - 4 * half;  // blocks of this half that exist (ragged last chunk)
-        if (nblk >= 4) {
-            __builtin_memcpy(r.v, p, 4 * BB);
-        } else {
-#pragma unroll
-            for (int i = 0; i < BB; i++) r.v[i] = 0;
-            for (int k = 0; k < nblk; k++) __builtin_memcpy(reinterpret_cast<uint8_t*>(r.v) + k * BB, p + k * BB, BB);
-        }
+        __builtin_memcpy(r.v, row + (int64_t)b * GFmt<FMT>::BB, GFmt<FMT>::BB);
     } else if constexpr (FMT == T_Q4_K) {
-        const uint8_t* sb = row + (int64_t)144 * c;
+        const uint8_t* sb = row + (int64_t)144 * (b >> 3);
+        const int j = b & 7;
         __builtin_memcpy(r.hdr, sb, 16);
-        __builtin_memcpy(r.q, sb + 16 + 64 * half, 64);
+        __builtin_memcpy(r.q, sb + 16 + 32 * (j >> 1), 32);
     } else {
-        const uint8_t* sb = row + (int64_t)210 * c;
-        __builtin_memcpy(r.ql, sb + 64 * half, 64);
-        __builtin_memcpy(r.qh, sb + 128 + 32 * half, 32);
-        __builtin_memcpy(r.s, sb + 192 + 8 * half, 8);
-        r.d = ldu16(sb + 208);
+        const uint8_t* sb = row + (int64_t)210 * (b >> 3);
+        const int bb = b & 7, h = bb >> 2, kk = bb & 3;
+        __builtin_memcpy(r.ql, sb + 64 * h + 32 * (kk & 1), 32);
+        __builtin_memcpy(r.qh, sb + 128 + 32 * h, 32);
+        uint16_t sp, d;
+        __builtin_memcpy(&sp, sb + 192 + 2 * bb, 2);
+        __builtin_memcpy(&d, sb + 208, 2);
+        r.sd = (uint32_t)sp | ((uint32_t)d << 16);
     }
 }
 
-// f16 pair (lo, hi) from 16-bit integers in the low bits of each half: the
-// bits 0x6400 | v are the f16 value 1024 + v (v < 1024), so subtracting
-// 1024 + bias exactly gives v - bias.
+// f16 pair from 16-bit integers v < 1024 in the low bits of each half: the
+// bits 0x6400 | v are the f16 value 1024 + v, so subtracting 1024 + bias
+// exactly gives v - bias.
 __device__ __forceinline__ uint32_t pk_ints_to_f16(uint32_t two, float bias) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const uint32_t bits = two | 0x64006400u;
     h2 v;
     __builtin_memcpy(&v, &bits, 4);
@@ -124,18 +118,30 @@ __device__ __forceinline__ void bytes_to_f16(uint32_t q, float bias, uint32_t& o
     o1 = pk_ints_to_f16(__builtin_amdgcn_perm(0u, q, 0x0c030c02u), bias);
 }
 
-template <typename T>
-__device__ __forceinline__ T byte_at(const uint32_t* v, int o) {
-    return (T)reinterpret_cast<const uint8_t*>(v)[o];
+__device__ __forceinline__ uint32_t pk_mul(uint32_t a, _Float16 s) {
+    h2 v;
+    __builtin_memcpy(&v, &a, 4);
+    const h2 ss = {s, s};
+    v = v * ss;
+    uint32_t out;
+    __builtin_memcpy(&out, &v, 4);
+    return out;
 }
 
-// Decode block k (0..3) of the fetched half-chunk: 32 f16 codes (16 dwords,
-// element order) and the block's scale fields.
-template <int FMT>
-__device__ __forceinline__ void decode_blk(const WRaw<FMT>& r, int k, int half, uint32_t (&o)[16],
-                                           WRow& s) {
+// Scale words of a decoded block, as the multiply reads them.
+struct WScale {
+    uint32_t d;    // fp16 bits of the block / superblock d
+    uint32_t x1;   // Q4_K: f32 bits of dmin * m_j;  Q6_K (unscaled codes): s0 | s1 << 16
+};
+
+// Decode block b of the fetched bytes into 32 f16 values (16 dwords, element
+// order).  Q4_K folds the 6-bit sub-scale into the codes (sc*q <= 945);
+// Q6_K folds the int8 sub-scales in when FOLD (|s*(q-32)| <= 2048, or even
+// and <= 4096: exact in f16), else leaves q - 32 and returns s0, s1.
+template <int FMT, bool FOLD>
+__device__ __forceinline__ void decode_w(const WRaw<FMT>& r, int b, uint32_t (&o)[16], WScale& s) {
     if constexpr (FMT == T_Q8_0) {
-        const uint8_t* blk = reinterpret_cast<const uint8_t*>(r.v) + 34 * k;
+        const uint8_t* blk = reinterpret_cast<const uint8_t*>(r.v);
         s.d = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8);
 #pragma unroll
         for (int i = 0; i < 8; i++) {
@@ -145,7 +151,7 @@ __device__ __forceinline__ void decode_blk(const WRaw<FMT>& r, int k, int half, 
             bytes_to_f16(q ^ 0x80808080u, 128.0f, o[2 * i], o[2 * i + 1]);
         }
     } else if constexpr (FMT == T_Q4_0) {
-        const uint8_t* blk = reinterpret_cast<const uint8_t*>(r.v) + 18 * k;
+        const uint8_t* blk = reinterpret_cast<const uint8_t*>(r.v);
         s.d = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -155,46 +161,50 @@ __device__ __forceinline__ void decode_blk(const WRaw<FMT>& r, int k, int half, 
             bytes_to_f16((q >> 4) & 0x0F0F0F0Fu, 8.0f, o[8 + 2 * i], o[8 + 2 * i + 1]);  // 16..31
         }
     } else if constexpr (FMT == T_Q4_K) {
-        const int j = 4 * half + k;  // sub-block
+        const int j = b & 7;  // sub-block
         s.d = r.hdr[0] & 0xFFFFu;
-        s.dmin = r.hdr[0] >> 16;
-        const uint8_t* s12 = reinterpret_cast<const uint8_t*>(r.hdr) + 4;
+        // byte i of the 12 packed scale bytes (selects, not a dynamic index)
+        auto s12 = [&r](int i) -> int {
+            const uint32_t d = i < 4 ? r.hdr[1] : (i < 8 ? r.hdr[2] : r.hdr[3]);
+            return (int)((d >> (8 * (i & 3))) & 0xFFu);
+        };
+        int sc, mn;
         if (j < 4) {
-            s.sc = s12[j] & 63;
-            s.mn = s12[j + 4] & 63;
+            sc = s12(j) & 63;
+            mn = s12(j + 4) & 63;
         } else {
-            s.sc = (s12[j + 4] & 15) | ((s12[j - 4] >> 6) << 4);
-            s.mn = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
+            sc = (s12(j + 4) & 15) | ((s12(j - 4) >> 6) << 4);
+            mn = (s12(j + 4) >> 4) | ((s12(j) >> 6) << 4);
         }
-        // codes q (0..15) times the sub-scale: sc*q <= 945 is exact in f16
-        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-        const _Float16 sch = (_Float16)(float)s.sc;
-        const h2 sc2 = {sch, sch};
-        const int base = 8 * (k >> 1);  // dword of qs[32*(j>>1)] inside this half's 64 bytes
+        const float dmin = (float)h_of_bits(r.hdr[0] >> 16);
+        s.x1 = __float_as_uint(dmin * (float)mn);  // exact: 11-bit x 6-bit
+        const _Float16 sch = (_Float16)(float)sc;
+        const int sh = 4 * (j & 1);
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const uint32_t nib = ((k & 1) ? (r.q[base + i] >> 4) : r.q[base + i]) & 0x0F0F0F0Fu;
             uint32_t f0, f1;
-            bytes_to_f16(nib, 0.0f, f0, f1);
-            h2 v0, v1;
-            __builtin_memcpy(&v0, &f0, 4);
-            __builtin_memcpy(&v1, &f1, 4);
-            v0 = v0 * sc2;
-            v1 = v1 * sc2;
-            __builtin_memcpy(&o[2 * i], &v0, 4);
-            __builtin_memcpy(&o[2 * i + 1], &v1, 4);
+            bytes_to_f16((r.q[i] >> sh) & 0x0F0F0F0Fu, 0.0f, f0, f1);
+            o[2 * i] = pk_mul(f0, sch);
+            o[2 * i + 1] = pk_mul(f1, sch);
         }
     } else {
-        const int kq = k;  // block 4*half + k of the superblock: h = half, kq = k
-        s.d = r.d;
-        s.s0 = byte_at<int8_t>(r.s, 2 * k);
-        s.s1 = byte_at<int8_t>(r.s, 2 * k + 1);
-        const int lbase = 8 * (kq & 1);  // dword of ql[32*(kq&1)] inside this half's 64 bytes
+        const int bb = b & 7, kk = bb & 3;
+        s.d = r.sd >> 16;
+        const int s0 = (int8_t)(r.sd & 0xFF), s1 = (int8_t)((r.sd >> 8) & 0xFF);
+        s.x1 = (uint32_t)(s0 & 0xFFFF) | ((uint32_t)s1 << 16);
+        const int lsh = 4 * (kk >> 1);
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const uint32_t lo = ((kq & 2) ? (r.ql[lbase + i] >> 4) : r.ql[lbase + i]) & 0x0F0F0F0Fu;
-            const uint32_t hi = ((r.qh[i] >> (2 * kq)) & 0x03030303u) << 4;
+            const uint32_t lo = (r.ql[i] >> lsh) & 0x0F0F0F0Fu;
+            const uint32_t hi = ((r.qh[i] >> (2 * kk)) & 0x03030303u) << 4;
             bytes_to_f16(lo | hi, 32.0f, o[2 * i], o[2 * i + 1]);
+        }
+        if constexpr (FOLD) {
+            const _Float16 f0 = (_Float16)(float)s0, f1 = (_Float16)(float)s1;
+#pragma unroll
+            for (int i = 0; i < 8; i++) o[i] = pk_mul(o[i], f0);
+#pragma unroll
+            for (int i = 8; i < 16; i++) o[i] = pk_mul(o[i], f1);
         }
     }
 }
@@ -218,190 +228,235 @@ __device__ __forceinline__ void tile_of(int64_t wg, int64_t tilesM, int64_t tile
     tn = r / gm;
 }
 
-// LDS of one chunk (8 blocks) of a 128 x 128 tile.  Tile rows hold 8 blocks x
-// 32 f16 = 512 bytes as 32 pieces of 16 bytes; piece q of row r is stored at
-// slot q ^ (r & 31) so the 32 rows a fragment read touches hit different banks.
-struct Chunk {
-    uint4 a[TM * 32];     // activation codes (f16)
-    uint4 w[TN * 32];     // decoded weights (f16)
-    uint32_t da[8][TM];   // fp16 bits of the activation block scales
-    uint32_t dw[8][TN];   // fp16 bits of the weight d
-    uint32_t x1[8][TN];   // Q4_K: dmin bits | m_j << 16;  Q6_K: s0 | s1 << 16
+// LDS of the workgroup.  Tile rows hold SB blocks x 32 f16 = 256 bytes as 16
+// pieces of 16 bytes; piece q of row r sits in slot r*16 + (q ^ (r & 15)), so
+// the 8 lanes of each ds_read_b128 pass (consecutive rows) hit different banks.
+// The scale products run as rank-1 MFMAs whose operands are read ready-made:
+// ra[b][r] = (d_a, 0, ..., 0) for activation row r (row TM is all zero, for
+// the lanes that hold k = 8..15), rw[b][r] = d_w in all 8 halves.
+struct Smem {
+    uint4 a[NA][TM * PR];  // activation codes (f16), a ring of NA steps
+    uint4 w[TN * PR];      // decoded weights (f16)
+    uint4 ra[SB][TM + 1];  // rank-1 A operands (fp16 d_a at k = 0)
+    uint4 rw[SB][TN];      // rank-1 B operands (fp16 d_w broadcast)
+    float ca[SB][TM];      // Q4_K: d_a * S (S = the block's code sum)
+    uint32_t x1[SB][TN];   // see WScale::x1
 };
-__device__ __forceinline__ int slot(int row, int q) { return row * 32 + (q ^ (row & 31)); }
+__device__ __forceinline__ int slot(int row, int q) { return row * PR + (q ^ (row & 15)); }
 
 template <int FMT>
-__global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ w, int64_t N, int64_t K,
+__global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int64_t N, int64_t K,
                                               const uint8_t* __restrict__ xq, ActLayout L,
                                               int64_t M, int64_t tilesM, int64_t tilesN,
                                               float* __restrict__ y) {
     using F = GFmt<FMT>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    Chunk& cs = *reinterpret_cast<Chunk*>(smem);
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+    Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv >> 1, wn = wv & 1;
+    const int wm = wv & 1, wn = wv >> 1;
     int64_t tm, tn;
     tile_of(blockIdx.x, tilesM, tilesN, tm, tn);
     const int64_t m0 = tm * TM, n0 = tn * TN;
-    const int nb = (int)(K >> 5), C = (nb + 7) >> 3;
+    const int nb = (int)(K >> 5);
+    const int H = (nb + SB - 1) / SB;   // K steps
     const int64_t R = (K / F::QK) * F::BB;
 
-    // staging role: row srow, half shalf (blocks 4*shalf .. 4*shalf+3 of a chunk)
-    const int srow = tid >> 1, shalf = tid & 1;
-    const int64_t am = m0 + srow < M ? m0 + srow : M - 1;  // clamp: rows past M are discarded
-    const int64_t wr = n0 + srow < N ? n0 + srow : N - 1;
-    const uint8_t* arow = xq + L.hcodes + am * K * 2;
+    // staging role: tile row sr (activation row m0 + sr, weight row n0 + sr),
+    // block sk of the step
+    const int sr = tid >> 2, sk = tid & 3;
+    const int64_t am = m0 + sr < M ? m0 + sr : M - 1;  // clamp: rows past M are discarded
+    const int64_t wr = n0 + sr < N ? n0 + sr : N - 1;
     const uint16_t* ahda = reinterpret_cast<const uint16_t*>(xq + L.hda) + am * nb;
+    const float* arca = reinterpret_cast<const float*>(xq + L.rca) + am * nb;
     const uint8_t* wrow = w + wr * R;
+    if (tid < SB) sm.ra[tid][TM] = make_uint4(0, 0, 0, 0);
 
-    // next chunk, in registers
-    uint4 ra[16];
-    uint32_t rda[4];
-    WRaw<FMT> rw;
-    auto fetch = [&](int c) {
-        const int nbc = min(8, nb - 8 * c);
+    // activation tile by global_load_lds: each wave instruction fills 64
+    // consecutive slots = 4 tile rows; wave wv fills rows 16wv .. 16wv + 15;
+    // lane l: row 16wv + 4i + l/16, slot l%16, which holds piece
+    // (l%16) ^ (row & 15).  Source pointers advance 256 bytes per step.
+    const uint8_t* asrc[4];
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const int b = 8 * c + 4 * shalf + k;
-            const bool ok = 4 * shalf + k < nbc;
-            const uint4* src = reinterpret_cast<const uint4*>(arow + (int64_t)(ok ? b : 0) * 64);
+    for (int i = 0; i < 4; i++) {
+        const int row = 16 * wv + 4 * i + (lane >> 4);
+        const int piece = (lane & 15) ^ (row & 15);
+        const int64_t arow = m0 + row < M ? m0 + row : M - 1;
+        asrc[i] = xq + L.hcodes + (arow * K + 8 * piece) * 2;
+    }
+    auto issue_a = [&](int h, int buf) {
+        const bool ragged = SB * h + SB > nb;  // uniform: only the last step of a ragged K
 #pragma unroll
-            for (int q = 0; q < 4; q++) ra[4 * k + q] = ok ? src[q] : make_uint4(0, 0, 0, 0);
-            rda[k] = ok ? ahda[b] : 0u;
-        }
-        fetch_w<FMT>(wrow, c, shalf, nbc, rw);
-    };
-    auto stage = [&](int c) {
-        const int nbc = min(8, nb - 8 * c);
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const int bk = 4 * shalf + k;  // block inside the chunk
-#pragma unroll
-            for (int q = 0; q < 4; q++) cs.a[slot(srow, 4 * bk + q)] = ra[4 * k + q];
-            cs.da[bk][srow] = rda[k];
-            uint32_t o[16];
-            WRow f;
-            decode_blk<FMT>(rw, k, shalf, o, f);
-            if (bk >= nbc) f.d = 0;  // ragged last chunk: the missing blocks add nothing
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-                cs.w[slot(srow, 4 * bk + q)] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-            cs.dw[bk][srow] = f.d;
-            if (FMT == T_Q4_K) cs.x1[bk][srow] = f.dmin | ((uint32_t)f.mn << 16);
-            if (FMT == T_Q6_K) cs.x1[bk][srow] = (uint32_t)(f.s0 & 0xFFFF) | ((uint32_t)f.s1 << 16);
+        for (int i = 0; i < 4; i++) {
+            const uint8_t* src = asrc[i] + (int64_t)h * (SB * 64);
+            if (ragged) {
+                // blocks past the row end: fetch any in-row bytes, never read
+                const int row = 16 * wv + 4 * i + (lane >> 4);
+                const int piece = (lane & 15) ^ (row & 15);
+                const int blk = SB * h + (piece >> 2);
+                if (blk >= nb) src -= (int64_t)(blk - (nb - 1)) * 64;
+            }
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)&sm.a[buf][(16 * wv + 4 * i) * PR], 16, 0, 0);
         }
     };
 
-    // accumulators: chunk sum p and running sum yv, per 32x32 tile (i, j)
-    v16f p[2][2], yv[2][2];
+    // weight bytes and activation scales of the next step, in registers;
+    // every thread always loads (a clamped block past the end of K), so that
+    // consuming them also waits for the earlier activation loads of the same
+    // step (vector memory loads complete in order)
+    struct Raw {
+        WRaw<FMT> w;
+        uint32_t da;
+        float ca;
+        bool have;
+    };
+    auto fetch = [&](int h, Raw& r) {
+        const int b = SB * h + sk;
+        r.have = b < nb;
+        const int bc = r.have ? b : nb - 1;
+        fetch_w<FMT>(wrow, bc, r.w);
+        r.da = ahda[bc];
+        if (FMT == T_Q4_K) r.ca = arca[bc];
+    };
+
+    // accumulators of tile i: chunk sum p and running sum yv
+    v16f p[2], yv[2];
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) p[i][j][e] = yv[i][j][e] = 0.0f;
+        for (int e = 0; e < 16; e++) p[i][e] = yv[i][e] = 0.0f;
 
     const int lr = lane & 31, kq = lane >> 5;  // MFMA lane roles
     const v16f zero16 = {};
-    fetch(0);
-    for (int c = 0; c < C; c++) {
-        __syncthreads();  // the previous chunk is fully consumed
-        stage(c);
+    // fragment slots: A rows 64wm + 32i + lr, B rows 32wn + lr; piece
+    // 4*bk + 2hh + kq holds k = 16hh + 8kq .. +8 of block bk
+    const int arow0 = 64 * wm + lr, brow = 32 * wn + lr;
+
+    auto step = [&](int h, Raw& r) {
+        const int nbh = min(SB, nb - SB * h);
+        bool odd_big = false;
+        if constexpr (FMT == T_Q6_K) {
+            const int s0 = (int8_t)(r.w.sd & 0xFF), s1 = (int8_t)((r.w.sd >> 8) & 0xFF);
+            odd_big = r.have && (((s0 & 1) && (s0 > 64 || s0 < -64)) ||
+                                 ((s1 & 1) && (s1 > 64 || s1 < -64)));
+        }
+        // B1: step h-1 is consumed (its W tile and activation slot are free)
+        const bool unfolded = __syncthreads_or(odd_big) != 0;
+        {
+            uint32_t o[16];
+            WScale f{};
+            if (FMT == T_Q6_K && unfolded)
+                decode_w<FMT, false>(r.w, SB * h + sk, o, f);
+            else
+                decode_w<FMT, true>(r.w, SB * h + sk, o, f);
+            if (!r.have) f.d = 0;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                sm.w[slot(sr, 4 * sk + q)] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+            const uint32_t dd = f.d | (f.d << 16);
+            sm.rw[sk][sr] = make_uint4(dd, dd, dd, dd);
+            sm.ra[sk][sr] = make_uint4(r.da, 0, 0, 0);
+            if (FMT == T_Q4_K) sm.ca[sk][sr] = r.ca;
+            if (FMT == T_Q4_K || FMT == T_Q6_K) sm.x1[sk][sr] = f.x1;
+        }
+        // B2: the W tile is staged; this wave's activation loads of step h
+        // completed before its weight loads of step h were consumed above
         __syncthreads();
-        if (c + 1 < C) fetch(c + 1);  // streams while this chunk is multiplied
-        const int nbc = min(8, nb - 8 * c);
-        for (int bk = 0; bk < nbc; bk++) {
-            // fragments: A rows 64wm + 32i + lr, B rows 64wn + 32j + lr; piece
-            // 4*bk + 2h + kq holds k = 16h + 8kq .. +8 of block bk
-            v8h A[2][2], Bf[2][2];
+        if (h + 1 < H) {
+            issue_a(h + 1, (h + 1) % NA);  // in flight while step h is multiplied
+            fetch(h + 1, r);
+        }
+        const uint4* A = sm.a[h % NA];
+        // the multiply of one step; UNF: Q6_K codes were staged without their
+        // sub-scales (a scale that cannot be folded exactly occurs in the step)
+        auto multiply = [&](auto unf_tag) {
+            constexpr bool UNF = decltype(unf_tag)::value;
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int bk = 0; bk < SB; bk++) {
+                if (bk < nbh) {
+                    v8h Af[2][2], Bf[2], Ra[2], Rw;
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const int ra_ = 64 * wm + 32 * i + lr, rb_ = 64 * wn + 32 * i + lr;
-                    const uint4 va = cs.a[slot(ra_, 4 * bk + 2 * h + kq)];
-                    const uint4 vb = cs.w[slot(rb_, 4 * bk + 2 * h + kq)];
-                    __builtin_memcpy(&A[i][h], &va, 16);
-                    __builtin_memcpy(&Bf[i][h], &vb, 16);
-                }
-            // rank-1 operands of the scale products: only k = 0 is nonzero
-            v8h Ra[2], Rw[2], Rm[2];
+                    for (int hh = 0; hh < 2; hh++) {
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const v8h za = {};
-                Ra[i] = za;
-                Rw[i] = za;
-                Rm[i] = za;
-                if (kq == 0) {
-                    Ra[i][0] = h_of_bits(cs.da[bk][64 * wm + 32 * i + lr]);
-                    Rw[i][0] = h_of_bits(cs.dw[bk][64 * wn + 32 * i + lr]);
-                    if (FMT == T_Q4_K) Rm[i][0] = h_of_bits(cs.x1[bk][64 * wn + 32 * i + lr] & 0xFFFFu);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const v16f S =
-                        __builtin_amdgcn_mfma_f32_32x32x16_f16(Ra[i], Rw[j], zero16, 0, 0, 0);
-                    if constexpr (FMT == T_Q6_K) {
-                        const v16f I0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i][0], Bf[j][0], zero16, 0, 0, 0);
-                        const v16f I1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i][1], Bf[j][1], zero16, 0, 0, 0);
-                        const uint32_t s01 = cs.x1[bk][64 * wn + 32 * j + lr];
-                        const float s0 = (float)(int16_t)(s01 & 0xFFFF), s1 = (float)((int)s01 >> 16);
-#pragma unroll
-                        for (int e = 0; e < 16; e++) {
-                            const float I = fmaf(s0, I0[e], s1 * I1[e]);  // exact integer
-                            p[i][j][e] = fmaf(I, S[e], p[i][j][e]);
+                        for (int i = 0; i < 2; i++) {
+                            const uint4 va = A[slot(arow0 + 32 * i, 4 * bk + 2 * hh + kq)];
+                            __builtin_memcpy(&Af[i][hh], &va, 16);
                         }
-                    } else {
-                        v16f I = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i][0], Bf[j][0], zero16, 0, 0, 0);
-                        I = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i][1], Bf[j][1], I, 0, 0, 0);
-                        if constexpr (FMT == T_Q4_K) {
-                            // Q = m_j * sum(a): B operand is m_j at every k
-                            const _Float16 mh = (_Float16)(float)(cs.x1[bk][64 * wn + 32 * j + lr] >> 16);
-                            v8h Mb;
+                        const uint4 vb = sm.w[slot(brow, 4 * bk + 2 * hh + kq)];
+                        __builtin_memcpy(&Bf[hh], &vb, 16);
+                    }
+                    {
+                        const uint4 r0 = sm.ra[bk][kq ? TM : arow0];
+                        const uint4 r1 = sm.ra[bk][kq ? TM : arow0 + 32];
+                        const uint4 rb = sm.rw[bk][brow];
+                        __builtin_memcpy(&Ra[0], &r0, 16);
+                        __builtin_memcpy(&Ra[1], &r1, 16);
+                        __builtin_memcpy(&Rw, &rb, 16);
+                    }
+                    const uint32_t x1 = (FMT == T_Q4_K || FMT == T_Q6_K) ? sm.x1[bk][brow] : 0u;
 #pragma unroll
-                            for (int t = 0; t < 8; t++) Mb[t] = mh;
-                            v16f Q = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i][0], Mb, zero16, 0, 0, 0);
-                            Q = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i][1], Mb, Q, 0, 0, 0);
-                            const v16f S2 =
-                                __builtin_amdgcn_mfma_f32_32x32x16_f16(Ra[i], Rm[j], zero16, 0, 0, 0);
+                    for (int i = 0; i < 2; i++) {
+                        const v16f S = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ra[i], Rw, zero16, 0, 0, 0);
+                        if constexpr (FMT == T_Q6_K && UNF) {
+                            const v16f I0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i][0], Bf[0], zero16, 0, 0, 0);
+                            const v16f I1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i][1], Bf[1], zero16, 0, 0, 0);
+                            const float s0 = (float)(int16_t)(x1 & 0xFFFF), s1 = (float)((int)x1 >> 16);
 #pragma unroll
                             for (int e = 0; e < 16; e++) {
-                                p[i][j][e] = fmaf(I[e], S[e], p[i][j][e]);
-                                p[i][j][e] = fmaf(-Q[e], S2[e], p[i][j][e]);
+                                const float I = fmaf(s0, I0[e], s1 * I1[e]);  // exact integer
+                                p[i][e] = fmaf(I, S[e], p[i][e]);
                             }
                         } else {
+                            v16f I = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i][0], Bf[0], zero16, 0, 0, 0);
+                            I = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i][1], Bf[1], I, 0, 0, 0);
 #pragma unroll
-                            for (int e = 0; e < 16; e++) p[i][j][e] = fmaf(I[e], S[e], p[i][j][e]);
+                            for (int e = 0; e < 16; e++) p[i][e] = fmaf(I[e], S[e], p[i][e]);
+                            if constexpr (FMT == T_Q4_K) {
+                                // element e of the lane is row 8(e/4) + 4kq + e%4 of the tile
+                                const float nX = -__uint_as_float(x1);
+                                const float* cr = &sm.ca[bk][64 * wm + 32 * i + 4 * kq];
+#pragma unroll
+                                for (int g = 0; g < 4; g++) {
+                                    const float4 c4 = *reinterpret_cast<const float4*>(cr + 8 * g);
+                                    p[i][4 * g + 0] = fmaf(nX, c4.x, p[i][4 * g + 0]);
+                                    p[i][4 * g + 1] = fmaf(nX, c4.y, p[i][4 * g + 1]);
+                                    p[i][4 * g + 2] = fmaf(nX, c4.z, p[i][4 * g + 2]);
+                                    p[i][4 * g + 3] = fmaf(nX, c4.w, p[i][4 * g + 3]);
+                                }
+                            }
                         }
                     }
                 }
-        }
-        // end of the chunk: add it, in chunk order
+            }
+        };
+        if (FMT == T_Q6_K && unfolded)
+            multiply(std::true_type{});
+        else
+            multiply(std::false_type{});
+        // end of a 256-element chunk (two steps) or of K: add it, in chunk order
+        if ((h & 1) || h + 1 == H) {
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int j = 0; j < 2; j++)
+            for (int i = 0; i < 2; i++)
 #pragma unroll
                 for (int e = 0; e < 16; e++) {
-                    yv[i][j][e] = yv[i][j][e] + p[i][j][e];
-                    p[i][j][e] = 0.0f;
+                    yv[i][e] = yv[i][e] + p[i][e];
+                    p[i][e] = 0.0f;
                 }
-    }
+        }
+    };
 
-    // lane l, element e of tile (i, j): row 8(e/4) + 4kq + e%4, column lr
+    Raw r;
+    issue_a(0, 0);
+    fetch(0, r);
+    for (int h = 0; h < H; h++) step(h, r);
+
+    // lane l, element e of tile i: row 8(e/4) + 4kq + e%4, column lr
+    const int64_t n = n0 + 32 * wn + lr;
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t n = n0 + 64 * wn + 32 * j + lr;
-#pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int64_t m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * kq + (e & 3);
-                if (m < M && n < N) y[m * N + n] = yv[i][j][e];
-            }
+        for (int e = 0; e < 16; e++) {
+            const int64_t m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * kq + (e & 3);
+            if (m < M && n < N) y[m * N + n] = yv[i][e];
         }
 }
 
@@ -410,15 +465,15 @@ int launch_gemm_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int
                   float* y, hipStream_t s) {
     const ActLayout L = act_layout(M, K);
     const int64_t tilesM = (M + TM - 1) / TM, tilesN = (N + TN - 1) / TN;
-    static bool attr_set = false;  // the chunk tiles need more than the default 64 KB of LDS
+    static bool attr_set = false;  // more than the default 64 KB of LDS
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<FMT>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)sizeof(Chunk));
+                                                 (int)sizeof(Smem));
         if (e != hipSuccess) return (int)e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_gemm<FMT>), dim3((unsigned)(tilesM * tilesN)), dim3(256), sizeof(Chunk),
+    hipLaunchKernelGGL((k_gemm<FMT>), dim3((unsigned)(tilesM * tilesN)), dim3(512), sizeof(Smem),
                        s, w, N, K, xq, L, M, tilesM, tilesN, y);
     return (int)hipGetLastError();
 }

@@ -119,6 +119,40 @@ def test_qmm_rows_equal_qmv(g, fmt, N, K, M):
         assert_bitwise(y[m], y1[0], f"qmm row {m} vs qmv")
 
 
+# Prefill GEMM over several 128 x 128 workgroup tiles with ragged edges in M
+# and N, and a ragged last K step (K = 416: 13 blocks).  Q6_K also with the
+# sub-scale range of the workloads ([-32, 31], folded into f16 codes) and with
+# a few rows whose odd sub-scales beyond +-64 force the unfolded path in
+# their steps only.
+GEMM = [
+    (synth.Q8_0, 129, 416, 129, None), (synth.Q4_0, 300, 896, 130, None),
+    (synth.Q4_K, 200, 1024, 150, None), (synth.Q6_K, 140, 768, 131, (-128, 127)),
+    (synth.Q6_K, 140, 768, 131, (-32, 31)), (synth.Q6_K, 260, 1024, 257, "mixed"),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,M,srange", GEMM)
+def test_gemm_tiles_against_oracle(g, fmt, N, K, M, srange):
+    seed = 900 + N + M
+    if srange == "mixed":
+        f = synth.draw_fields(fmt, N, K, seed, s_range=(-32, 31))
+        f["s"][7, 0, 5] = 101     # odd, beyond +-64: row 7, superblock 0, block 2
+        f["s"][200, 1, 14] = -77  # row 200, superblock 1, block 15
+        blob = synth.encode(f)
+    else:
+        blob, _ = synth.weights(fmt, N, K, seed, s_range=srange or (-32, 31))
+    x = synth.activations(M, K, seed + 7)
+    w = dev(blob)
+    y = host(g.matmul(fmt, w, N, K, x=dev(x)))
+    xq = oracle.quantize_act(x)
+    y64, A = oracle.matmul_f64(fmt, blob, N, K, xq, M)
+    assert_tol(y, y64, A, what="gemm vs f64")
+    assert_bitwise(y, oracle.matmul_canon_f32(fmt, blob, N, K, xq, M), "gemm vs f32 order")
+    for m in (0, 127, 128, M - 1):
+        y1 = host(g.matvec(fmt, w, N, K, x=dev(x[m:m + 1])))
+        assert_bitwise(y[m], y1[0], f"gemm row {m} vs qmv")
+
+
 @pytest.mark.parametrize("fmt,N,K", [SMALL[1], SMALL[5], SMALL[7], SMALL[10]])
 def test_staged_xq_paths(g, fmt, N, K):
     """x = NULL uses xq as staged; quantize with x = NULL re-stages Q8_0 blocks
