@@ -63,10 +63,9 @@ int matmul_common(int type, const void* w, int64_t N, int64_t K, const float* x,
     if ((rc = check_device())) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* q = static_cast<uint8_t*>(xq);
-    if (x && qmv::launch_quantize(x, q, rows, K, s)) return QMV_ELAUNCH;
     const uint8_t* wb = static_cast<const uint8_t*>(w);
-    return launched(gemm ? qmv::launch_qmm(type, wb, N, K, q, rows, y, s)
-                         : qmv::launch_qmv(type, wb, N, K, q, rows, y, s));
+    return launched(gemm ? qmv::launch_qmm(type, wb, N, K, x, q, rows, y, s)
+                         : qmv::launch_qmv(type, wb, N, K, x, q, rows, y, s));
 }
 
 }  // namespace
@@ -85,7 +84,9 @@ int quantize_act_q8_0(const float* x, void* xq, int64_t rows, int64_t K, void* s
     if (rc) return rc;
     uint8_t* q = static_cast<uint8_t*>(xq);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return launched(x ? qmv::launch_quantize(x, q, rows, K, s) : qmv::launch_rebuild(q, rows, K, s));
+    const int st = qmv::staging_for(rows, K);
+    return launched(x ? qmv::launch_quantize(x, q, rows, K, st, s)
+                      : qmv::launch_rebuild(q, rows, K, st, s));
 }
 
 int qmv_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
@@ -98,7 +99,7 @@ int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, in
     return matmul_common(type, w, N, K, x, M, QMV_MAX_M, xq, y, stream, true);
 }
 
-int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, const void* xq,
+int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                         int64_t B, int32_t* P, void* stream) {
     int rc = check_weights(type, w, N, K);
     if (rc) return rc;
@@ -106,7 +107,7 @@ int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, const voi
     if (!xq || !P || !aligned(xq, 16) || !aligned(P, 4)) return QMV_EINVAL_PTR;
     if ((rc = check_device())) return rc;
     return launched(qmv::launch_partials(type, static_cast<const uint8_t*>(w), N, K,
-                                         static_cast<const uint8_t*>(xq), B, P,
+                                         static_cast<uint8_t*>(xq), B, P,
                                          static_cast<hipStream_t>(stream)));
 }
 

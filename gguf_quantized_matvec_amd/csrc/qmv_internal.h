@@ -52,15 +52,26 @@ inline ActLayout act_layout(int64_t rows, int64_t K) {
     return L;
 }
 
+// Which private staging copies a quantisation writes: only those that the
+// multiply for that many rows reads.
+enum Staging : int {
+    ST_ROW = 1,   // rcodes, rda, rca, rs16 (lane-per-chunk GEMV)
+    ST_MFMA = 2,  // codes, da, ca, S (MFMA GEMV and the partials hook)
+    ST_F16 = 4,   // hcodes, hda and rca (prefill GEMM)
+};
+int staging_for(int64_t rows, int64_t K);
+
 // Kernel launchers (qmv_kernels.hip).  Arguments are already validated.
-// Each returns 0 or a hipError_t value.
-int launch_quantize(const float* x, uint8_t* xq, int64_t rows, int64_t K, hipStream_t s);
-int launch_rebuild(uint8_t* xq, int64_t rows, int64_t K, hipStream_t s);
-int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
+// Each returns 0 or a hipError_t value.  x != NULL: the launch quantises x
+// into xq first (fused into the multiply where that kernel can).
+int launch_quantize(const float* x, uint8_t* xq, int64_t rows, int64_t K, int staging,
+                    hipStream_t s);
+int launch_rebuild(uint8_t* xq, int64_t rows, int64_t K, int staging, hipStream_t s);
+int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                int64_t rows, float* y, hipStream_t s);
-int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
+int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* xq,
                     int64_t rows, int32_t* P, hipStream_t s);
-int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
+int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                int64_t rows, float* y, hipStream_t s);
 // Prefill GEMM on f16 MFMA (qmm_kernels.hip), for rows > 16.
 int launch_gemm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t M,

@@ -61,46 +61,85 @@ __device__ __forceinline__ T ld(const uint8_t* p) {
 }
 
 // ------------------------------------------------------------ quantise ----
-// Q8_0 per 32-element block: amax, d = amax/127 (correctly rounded f32
+// Q8_0 of one 32-element block: amax, d = amax/127 (correctly rounded f32
 // divide), id = 1/d (0 for an all-zero block), codes = round-half-away(x*id),
-// stored scale fp16(d).  One thread per (row, block) of the 16-row-padded
-// range; padding rows get zero codes and scales in the staging copy.
-// FROM_PUBLIC: take codes and d from the Q8_0 blocks already in xq instead.
+// stored scale fp16(d); dval = f32 value of the stored scale.
+__device__ __forceinline__ void quant_block(const float* __restrict__ xb, uint8_t (&q)[32],
+                                            uint16_t& h, float& dval) {
+    float v[32];
+    const float4* x4 = reinterpret_cast<const float4*>(xb);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const float4 f = x4[j];
+        v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
+    const float d = amax / 127.0f;
+    const float id = d != 0.0f ? 1.0f / d : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) q[i] = (uint8_t)(int8_t)(int)roundf(v[i] * id);
+    h = float_to_half_bits(d);
+    dval = half_bits_to_float(h);
+}
+
+__device__ __forceinline__ void store_public(uint8_t* pub, const uint8_t (&q)[32], uint16_t h) {
+    uint8_t blk[34];
+    blk[0] = (uint8_t)(h & 255);
+    blk[1] = (uint8_t)(h >> 8);
+#pragma unroll
+    for (int i = 0; i < 32; i++) blk[2 + i] = q[i];
+    __builtin_memcpy(pub, blk, 34);
+}
+
+// Sum of the block's codes, and the two int16 half sums packed (low = 0..15).
+__device__ __forceinline__ void code_sums(const uint8_t (&q)[32], int& S, int32_t& s16) {
+    int lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) lo += (int8_t)q[i];
+#pragma unroll
+    for (int i = 16; i < 32; i++) hi += (int8_t)q[i];
+    S = lo + hi;
+    s16 = (int32_t)(((uint32_t)lo & 0xFFFFu) | ((uint32_t)hi << 16));
+}
+
+// The row-major staging of block b of row r (the lane-per-chunk kernels).
+__device__ __forceinline__ void store_row_staging(uint8_t* xq, const ActLayout& L, int64_t r,
+                                                  int64_t K, int64_t b, const uint8_t (&q)[32],
+                                                  float dval, int S, int32_t s16) {
+    const int64_t nb = L.nb;
+    uint4* rc = reinterpret_cast<uint4*>(xq + L.rcodes + r * K + 32 * b);
+    uint32_t wv[8];
+    __builtin_memcpy(wv, q, 32);
+    rc[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    rc[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+    reinterpret_cast<float*>(xq + L.rda)[r * nb + b] = dval;
+    reinterpret_cast<float*>(xq + L.rca)[r * nb + b] = dval * (float)S;
+    reinterpret_cast<int32_t*>(xq + L.rs16)[r * nb + b] = s16;
+}
+
+// Quantise x (or, FROM_PUBLIC, take codes and d from the Q8_0 blocks already
+// in xq) and write the staging copies selected by `staging`.  One thread per
+// (row, block); with ST_MFMA over the 16-row-padded range, whose padding
+// rows get zero codes and scales in that copy.
 template <bool FROM_PUBLIC>
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x,
                                                   uint8_t* __restrict__ xq, int64_t rows,
-                                                  int64_t K, ActLayout L) {
+                                                  int64_t K, ActLayout L, int staging) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t nb = L.nb;
-    if (t >= 16 * L.G * nb) return;
+    const int64_t span = (staging & ST_MFMA) ? 16 * L.G : rows;
+    if (t >= span * nb) return;
     const int64_t r = t / nb, b = t - r * nb;
     uint8_t q[32];
     float dval = 0.0f;
     if (r < rows) {
         uint8_t* pub = xq + (r * nb + b) * 34;
         if (!FROM_PUBLIC) {
-            float v[32];
-            const float4* xb = reinterpret_cast<const float4*>(x + r * K + 32 * b);
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                float4 f = xb[j];
-                v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
-            }
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
-            const float d = amax / 127.0f;
-            const float id = d != 0.0f ? 1.0f / d : 0.0f;
-#pragma unroll
-            for (int i = 0; i < 32; i++) q[i] = (uint8_t)(int8_t)(int)roundf(v[i] * id);
-            const uint16_t h = float_to_half_bits(d);
-            uint8_t blk[34];
-            blk[0] = (uint8_t)(h & 255);
-            blk[1] = (uint8_t)(h >> 8);
-#pragma unroll
-            for (int i = 0; i < 32; i++) blk[2 + i] = q[i];
-            __builtin_memcpy(pub, blk, 34);
-            dval = half_bits_to_float(h);
+            uint16_t h;
+            quant_block(x + r * K + 32 * b, q, h, dval);
+            store_public(pub, q, h);
         } else {
             uint8_t blk[34];
             __builtin_memcpy(blk, pub, 34);
@@ -112,52 +151,41 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x,
 #pragma unroll
         for (int i = 0; i < 32; i++) q[i] = 0;
     }
-    const int64_t g = r >> 4;
-    const int m = (int)(r & 15);
-    const int64_t gb = g * nb + b;
-    uint8_t* codes = xq + L.codes + gb * 512;
-    int S = 0;
+    int S;
+    int32_t s16;
+    code_sums(q, S, s16);
+    if (staging & ST_MFMA) {
+        const int64_t g = r >> 4;
+        const int m = (int)(r & 15);
+        const int64_t gb = g * nb + b;
+        uint8_t* codes = xq + L.codes + gb * 512;
 #pragma unroll
-    for (int kg = 0; kg < 4; kg++) {
-        uint64_t v = 0;
+        for (int kg = 0; kg < 4; kg++) {
+            uint64_t v = 0;
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            v |= (uint64_t)q[8 * kg + j] << (8 * j);
-            S += (int8_t)q[8 * kg + j];
+            for (int j = 0; j < 8; j++) v |= (uint64_t)q[8 * kg + j] << (8 * j);
+            *reinterpret_cast<uint64_t*>(codes + (m + 16 * kg) * 8) = v;
         }
-        *reinterpret_cast<uint64_t*>(codes + (m + 16 * kg) * 8) = v;
+        reinterpret_cast<float*>(xq + L.da)[gb * 16 + m] = dval;
+        reinterpret_cast<float*>(xq + L.ca)[gb * 16 + m] = dval * (float)S;
+        reinterpret_cast<int32_t*>(xq + L.S)[gb * 16 + m] = S;
     }
-    reinterpret_cast<float*>(xq + L.da)[gb * 16 + m] = dval;
-    reinterpret_cast<float*>(xq + L.ca)[gb * 16 + m] = dval * (float)S;
-    reinterpret_cast<int32_t*>(xq + L.S)[gb * 16 + m] = S;
-    if (r < rows) {
-        // row-major copy for the lane-per-chunk kernels
-        uint4* rc = reinterpret_cast<uint4*>(xq + L.rcodes + r * K + 32 * b);
-        uint32_t wv[8];
-        __builtin_memcpy(wv, q, 32);
-        rc[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-        rc[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
-        int s_lo = 0;
-#pragma unroll
-        for (int i = 0; i < 16; i++) s_lo += (int8_t)q[i];
-        const int s_hi = S - s_lo;
-        reinterpret_cast<float*>(xq + L.rda)[r * nb + b] = dval;
-        reinterpret_cast<float*>(xq + L.rca)[r * nb + b] = dval * (float)S;
-        reinterpret_cast<int32_t*>(xq + L.rs16)[r * nb + b] =
-            (int32_t)(((uint32_t)s_lo & 0xFFFFu) | ((uint32_t)s_hi << 16));
-        // f16 copy for the GEMM: code values are exact in f16
+    if (r >= rows) return;
+    if (staging & ST_ROW) store_row_staging(xq, L, r, K, b, q, dval, S, s16);
+    if (staging & ST_F16) {
+        // f16 copy for the GEMM (code values are exact in f16), and d_a * S
         uint4* hc = reinterpret_cast<uint4*>(xq + L.hcodes + (r * K + 32 * b) * 2);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             uint32_t hw[4];
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const _Float16 lo = (_Float16)(float)(int8_t)q[8 * j + 2 * t];
-                const _Float16 hi = (_Float16)(float)(int8_t)q[8 * j + 2 * t + 1];
+            for (int t2 = 0; t2 < 4; t2++) {
+                const _Float16 lo = (_Float16)(float)(int8_t)q[8 * j + 2 * t2];
+                const _Float16 hi = (_Float16)(float)(int8_t)q[8 * j + 2 * t2 + 1];
                 uint16_t ul, uh;
                 __builtin_memcpy(&ul, &lo, 2);
                 __builtin_memcpy(&uh, &hi, 2);
-                hw[t] = (uint32_t)ul | ((uint32_t)uh << 16);
+                hw[t2] = (uint32_t)ul | ((uint32_t)uh << 16);
             }
             hc[j] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         }
@@ -167,6 +195,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x,
             __builtin_memcpy(&dbits, &dh, 2);
         }
         reinterpret_cast<uint16_t*>(xq + L.hda)[r * nb + b] = dbits;
+        reinterpret_cast<float*>(xq + L.rca)[r * nb + b] = dval * (float)S;
     }
 }
 
@@ -845,10 +874,13 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
 // chunk straight into registers; at this register count many waves stay
 // resident, which keeps enough bytes in flight to cover HBM latency.  Chunk
 // sums are added in chunk order per row through a small LDS buffer.
+// x != NULL: every workgroup quantises the B activation rows from x straight
+// into its LDS (the same arithmetic as k_quantize), and workgroup 0 also
+// writes them to xq (Q8_0 blocks and the row-major staging) for later calls.
 template <int FMT, int B>
 __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int64_t wbytes,
-                                             int64_t N, int64_t K,
-                                             const uint8_t* __restrict__ xq, ActLayout L,
+                                             int64_t N, int64_t K, const float* __restrict__ x,
+                                             uint8_t* __restrict__ xq, ActLayout L,
                                              float* __restrict__ y) {
     using F = Fmt<FMT>;
     constexpr int NWD = DotFmt<FMT>::NWD;
@@ -903,17 +935,49 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
         A[m].da = reinterpret_cast<const float*>(base + C * ACT_CHUNK_STRIDE);
         A[m].ca = A[m].da + nb;
         A[m].s16 = reinterpret_cast<const int32_t*>(A[m].ca + nb);
-        const uint4* src = reinterpret_cast<const uint4*>(xq + L.rcodes + m * K);
-        for (int i = threadIdx.x; i < nb * 2; i += blockDim.x)  // 16-byte pieces
-            *reinterpret_cast<uint4*>(base + (i >> 4) * ACT_CHUNK_STRIDE + (i & 15) * 16) = src[i];
-        const float* sda = reinterpret_cast<const float*>(xq + L.rda) + m * nb;
-        const float* sca = reinterpret_cast<const float*>(xq + L.rca) + m * nb;
-        const int32_t* ss = reinterpret_cast<const int32_t*>(xq + L.rs16) + m * nb;
-        float* dda = const_cast<float*>(A[m].da);
-        for (int i = threadIdx.x; i < nb; i += blockDim.x) {
-            dda[i] = sda[i];
-            dda[nb + i] = sca[i];
-            reinterpret_cast<int32_t*>(dda + 2 * nb)[i] = ss[i];
+    }
+    if (x) {
+        const bool writer = blockIdx.x == 0;
+        for (int i = threadIdx.x; i < B * nb; i += blockDim.x) {
+            const int m = i / nb, b = i - m * nb;
+            uint8_t q[32];
+            uint16_t h;
+            float dval;
+            quant_block(x + (int64_t)m * K + 32 * b, q, h, dval);
+            int S;
+            int32_t s16;
+            code_sums(q, S, s16);
+            uint8_t* base = smem + m * rowb;
+            uint32_t wq[8];
+            __builtin_memcpy(wq, q, 32);
+            uint4* dst = reinterpret_cast<uint4*>(base + (b >> 3) * ACT_CHUNK_STRIDE + (b & 7) * 32);
+            dst[0] = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+            dst[1] = make_uint4(wq[4], wq[5], wq[6], wq[7]);
+            float* dda = const_cast<float*>(A[m].da);
+            dda[b] = dval;
+            dda[nb + b] = dval * (float)S;
+            reinterpret_cast<int32_t*>(dda + 2 * nb)[b] = s16;
+            if (writer) {
+                store_public(xq + ((int64_t)m * nb + b) * 34, q, h);
+                store_row_staging(xq, L, m, K, b, q, dval, S, s16);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < B; m++) {
+            uint8_t* base = smem + m * rowb;
+            const uint4* src = reinterpret_cast<const uint4*>(xq + L.rcodes + m * K);
+            for (int i = threadIdx.x; i < nb * 2; i += blockDim.x)  // 16-byte pieces
+                *reinterpret_cast<uint4*>(base + (i >> 4) * ACT_CHUNK_STRIDE + (i & 15) * 16) = src[i];
+            const float* sda = reinterpret_cast<const float*>(xq + L.rda) + m * nb;
+            const float* sca = reinterpret_cast<const float*>(xq + L.rca) + m * nb;
+            const int32_t* ss = reinterpret_cast<const int32_t*>(xq + L.rs16) + m * nb;
+            float* dda = const_cast<float*>(A[m].da);
+            for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+                dda[i] = sda[i];
+                dda[nb + i] = sca[i];
+                reinterpret_cast<int32_t*>(dda + 2 * nb)[i] = ss[i];
+            }
         }
     }
     __syncthreads();
@@ -989,7 +1053,7 @@ inline int64_t resident_blocks(ResidentCache& cache, const void* kernel, int thr
 }
 
 template <int FMT, int B>
-int launch_dot_b(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, float* y,
+int launch_dot_b(const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq, float* y,
                  hipStream_t s) {
     using F = Fmt<FMT>;
     const ActLayout L = act_layout(B, K);
@@ -1016,18 +1080,18 @@ int launch_dot_b(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, floa
     const int64_t waves = (units + per - 1) / per;
     const int64_t blocks = (waves + 3) / 4;
     hipLaunchKernelGGL((k_dot<FMT, B>), dim3((unsigned)blocks), dim3(256), shmem, s, w, wbytes,
-                       N, K, xq, L, y);
+                       N, K, x, xq, L, y);
     return (int)hipGetLastError();
 }
 
 template <int FMT>
-int launch_dot_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t rows,
-                 float* y, hipStream_t s) {
+int launch_dot_t(const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
+                 int64_t rows, float* y, hipStream_t s) {
     switch (rows) {
-    case 1: return launch_dot_b<FMT, 1>(w, N, K, xq, y, s);
-    case 2: return launch_dot_b<FMT, 2>(w, N, K, xq, y, s);
-    case 3: return launch_dot_b<FMT, 3>(w, N, K, xq, y, s);
-    default: return launch_dot_b<FMT, 4>(w, N, K, xq, y, s);
+    case 1: return launch_dot_b<FMT, 1>(w, N, K, x, xq, y, s);
+    case 2: return launch_dot_b<FMT, 2>(w, N, K, x, xq, y, s);
+    case 3: return launch_dot_b<FMT, 3>(w, N, K, x, xq, y, s);
+    default: return launch_dot_b<FMT, 4>(w, N, K, x, xq, y, s);
     }
 }
 
@@ -1080,33 +1144,50 @@ int launch_qmv_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int6
     }
 }
 
+// The lane-per-chunk kernel takes up to DOT_MAX_ROWS rows whose activations fit
+// in a workgroup's LDS; everything else up to 16 rows runs on MFMA.
+bool use_dot(int64_t rows, int64_t K) {
+    return rows <= DOT_MAX_ROWS && rows * act_lds_row_bytes(K) + 4 * rows * 256 <= DOT_MAX_ACT_LDS;
+}
+
 }  // namespace
 
-int launch_quantize(const float* x, uint8_t* xq, int64_t rows, int64_t K, hipStream_t s) {
+int staging_for(int64_t rows, int64_t K) {
+    if (rows > 16) return ST_F16;
+    return use_dot(rows, K) ? ST_ROW : ST_MFMA;
+}
+
+int launch_quantize(const float* x, uint8_t* xq, int64_t rows, int64_t K, int staging,
+                    hipStream_t s) {
     const ActLayout L = act_layout(rows, K);
-    const int64_t threads = 16 * L.G * L.nb;
+    const int64_t threads = ((staging & ST_MFMA) ? 16 * L.G : rows) * L.nb;
     hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       s, x, xq, rows, K, L);
+                       s, x, xq, rows, K, L, staging);
     return (int)hipGetLastError();
 }
 
-int launch_rebuild(uint8_t* xq, int64_t rows, int64_t K, hipStream_t s) {
+int launch_rebuild(uint8_t* xq, int64_t rows, int64_t K, int staging, hipStream_t s) {
     const ActLayout L = act_layout(rows, K);
-    const int64_t threads = 16 * L.G * L.nb;
+    const int64_t threads = ((staging & ST_MFMA) ? 16 * L.G : rows) * L.nb;
     hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       s, nullptr, xq, rows, K, L);
+                       s, nullptr, xq, rows, K, L, staging);
     return (int)hipGetLastError();
 }
 
-int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
+int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                int64_t rows, float* y, hipStream_t s) {
-    if (rows <= DOT_MAX_ROWS && rows * act_lds_row_bytes(K) + 4 * rows * 256 <= DOT_MAX_ACT_LDS) {
+    if (use_dot(rows, K)) {  // quantisation fused into the kernel when x is given
         switch (type) {
-        case T_Q8_0: return launch_dot_t<T_Q8_0>(w, N, K, xq, rows, y, s);
-        case T_Q4_0: return launch_dot_t<T_Q4_0>(w, N, K, xq, rows, y, s);
-        case T_Q4_K: return launch_dot_t<T_Q4_K>(w, N, K, xq, rows, y, s);
-        case T_Q6_K: return launch_dot_t<T_Q6_K>(w, N, K, xq, rows, y, s);
+        case T_Q8_0: return launch_dot_t<T_Q8_0>(w, N, K, x, xq, rows, y, s);
+        case T_Q4_0: return launch_dot_t<T_Q4_0>(w, N, K, x, xq, rows, y, s);
+        case T_Q4_K: return launch_dot_t<T_Q4_K>(w, N, K, x, xq, rows, y, s);
+        case T_Q6_K: return launch_dot_t<T_Q6_K>(w, N, K, x, xq, rows, y, s);
         }
+        return (int)hipErrorInvalidValue;
+    }
+    if (x) {
+        const int rc = launch_quantize(x, xq, rows, K, ST_MFMA, s);
+        if (rc) return rc;
     }
     switch (type) {
     case T_Q8_0: return launch_qmv_t<T_Q8_0>(w, N, K, xq, rows, y, nullptr, s, false);
@@ -1117,8 +1198,11 @@ int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* 
     return (int)hipErrorInvalidValue;
 }
 
-int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
+int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* xq,
                     int64_t rows, int32_t* P, hipStream_t s) {
+    // the partials come from the MFMA path: stage its copy from the Q8_0 blocks
+    const int rc = launch_rebuild(xq, rows, K, ST_MFMA, s);
+    if (rc) return rc;
     switch (type) {
     case T_Q8_0: return launch_qmv_ni<T_Q8_0, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     case T_Q4_0: return launch_qmv_ni<T_Q4_0, 4>(w, N, K, xq, rows, nullptr, P, s, true);
@@ -1128,9 +1212,13 @@ int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, const uint
     return (int)hipErrorInvalidValue;
 }
 
-int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
+int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                int64_t rows, float* y, hipStream_t s) {
-    if (rows <= 16) return launch_qmv(type, w, N, K, xq, rows, y, s);
+    if (rows <= 16) return launch_qmv(type, w, N, K, x, xq, rows, y, s);
+    if (x) {
+        const int rc = launch_quantize(x, xq, rows, K, ST_F16, s);
+        if (rc) return rc;
+    }
     return launch_gemm(type, w, N, K, xq, rows, y, s);
 }
 

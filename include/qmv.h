@@ -81,8 +81,9 @@ enum qmv_status {
 
 /* Bytes of activation scratch `xq` for `rows` rows of K elements.  The first
  * rows*(K/32)*34 bytes are the Q8_0 blocks (fp16 d little-endian, then 32
- * int8 codes, blocks in row-major order); the rest is a private staging copy
- * the kernels read.  Returns 0 for an invalid shape. */
+ * int8 codes, blocks in row-major order); the rest holds private staging
+ * copies in the layouts the kernels for that many rows read (only those are
+ * written).  Returns 0 for an invalid shape. */
 size_t qmv_act_bytes(int64_t rows, int64_t K);
 
 /* Quantise x [rows][K] (f32, 16-byte aligned) to Q8_0 into xq (16-byte
@@ -94,10 +95,11 @@ size_t qmv_act_bytes(int64_t rows, int64_t K);
 int quantize_act_q8_0(const float* x, void* xq, int64_t rows, int64_t K, void* stream);
 
 /* Decode GEMV (MatVec): y[B][N] = x[B][K] * W^T for 1 <= B <= 16.
- * If x is non-NULL it is quantised into xq first (as quantize_act_q8_0); if x
- * is NULL, xq must already hold a complete quantize_act_q8_0 result for these
- * B rows and K, which is used as is (so several matrices can share one
- * quantisation).  xq: qmv_act_bytes(B, K) bytes, 16-byte aligned.  Decode is
+ * If x is non-NULL it is quantised into xq first, leaving xq exactly as
+ * quantize_act_q8_0 would (for B <= 4 the quantisation runs inside the GEMV
+ * kernel, one launch); if x is NULL, xq must already hold a complete
+ * quantize_act_q8_0 result for these B rows and K, which is used as is (so
+ * several matrices can share one quantisation).  xq: qmv_act_bytes(B, K) bytes, 16-byte aligned.  Decode is
  * memory-bound ("Architecture", bench transcript), so every weight byte is
  * read once per call whatever B is ("A request, end to end": a batch reads
  * the weights once rather than once per sequence). */
@@ -114,11 +116,12 @@ int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, in
                void* xq, float* y, void* stream);
 
 /* Test hook: the exact int32 per-block partials that the kernels scale and
- * accumulate, from the same decode and integer-dot path as qmv_launch.
- * xq must come from quantize_act_q8_0 (or a qmv/qmm call with x != NULL) for
- * B rows, 1 <= B <= 16.  P layout [B][N][K/32] int32; for Q4_K
+ * accumulate, from the weight decode and integer dot of the batched-decode
+ * (MFMA) path.  xq must hold quantize_act_q8_0's Q8_0 blocks for B rows,
+ * 1 <= B <= 16; the hook first rebuilds the private part of xq from them
+ * (the Q8_0 blocks are not changed).  P layout [B][N][K/32] int32; for Q4_K
  * [B][N][K/32][2] = (sc_j * sum q*a, m_j * sum a). */
-int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, const void* xq,
+int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                         int64_t B, int32_t* P, void* stream);
 
 /* Static text for a status code. */

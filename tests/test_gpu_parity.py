@@ -176,6 +176,26 @@ def test_staged_xq_paths(g, fmt, N, K):
     assert_bitwise(host(g.matmul(fmt, w, N, K, xq=xq2, M=B)), y_ref, "qmm x=NULL vs qmv")
 
 
+@pytest.mark.parametrize("fmt,N,K", [SMALL[0], SMALL[4], SMALL[8], SMALL[11]])
+@pytest.mark.parametrize("B", [1, 3, 4, 5])
+def test_fused_quantisation_leaves_xq_as_quantize(g, fmt, N, K, B):
+    """qmv with x quantises inside the GEMV for B <= 4: xq must then hold the
+    same Q8_0 blocks as quantize_act_q8_0 and serve a later x = NULL call."""
+    blob, x = _inputs(fmt, N, K, B, 700 + B)
+    w = dev(blob)
+    xq = g.act_buffer(B, K)
+    xq.fill_(0x5A)
+    y = host(g.matvec(fmt, w, N, K, x=dev(x), xq=xq))
+    pub_end = B * (K // 32) * 34
+    assert_bitwise(host(xq)[:pub_end], oracle.quantize_act(x).reshape(-1), "fused xq blocks")
+    assert_bitwise(y, oracle.matmul_canon_f32(fmt, blob, N, K, oracle.quantize_act(x), B),
+                   "fused vs f32 order")
+    y2 = torch.empty(B, N, dtype=torch.float32, device="cuda")
+    assert_bitwise(host(g.matvec(fmt, w, N, K, xq=xq, B=B, y=y2)), y, "reuse of fused xq")
+    xq3 = g.quantize(dev(x))
+    assert_bitwise(host(g.matvec(fmt, w, N, K, xq=xq3, B=B)), y, "quantize + x=NULL vs fused")
+
+
 def test_repeat_runs_are_identical(g):
     fmt, N, K = synth.Q4_K, 300, 4096
     blob, x = _inputs(fmt, N, K, 5, 600)
