@@ -874,10 +874,10 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
 // chunk straight into registers; at this register count many waves stay
 // resident, which keeps enough bytes in flight to cover HBM latency.  Chunk
 // sums are added in chunk order per row through a small LDS buffer.
-// x != NULL: every workgroup quantises the B activation rows from x straight
-// into its LDS (the same arithmetic as k_quantize), and workgroup 0 also
-// writes them to xq (Q8_0 blocks and the row-major staging) for later calls.
-template <int FMT, int B>
+// FUSED: every workgroup quantises the B activation rows from x straight into
+// its LDS (the same arithmetic as k_quantize), and workgroup 0 also writes
+// them to xq (Q8_0 blocks and the row-major staging) for later calls.
+template <int FMT, int B, bool FUSED>
 __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int64_t wbytes,
                                              int64_t N, int64_t K, const float* __restrict__ x,
                                              uint8_t* __restrict__ xq, ActLayout L,
@@ -936,30 +936,58 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
         A[m].ca = A[m].da + nb;
         A[m].s16 = reinterpret_cast<const int32_t*>(A[m].ca + nb);
     }
-    if (x) {
+    if constexpr (FUSED) {
+        // four lanes per block, 8 elements each: the block's amax and code
+        // sums by lane shuffles, then the same d, id and codes as k_quantize
         const bool writer = blockIdx.x == 0;
-        for (int i = threadIdx.x; i < B * nb; i += blockDim.x) {
-            const int m = i / nb, b = i - m * nb;
-            uint8_t q[32];
-            uint16_t h;
-            float dval;
-            quant_block(x + (int64_t)m * K + 32 * b, q, h, dval);
-            int S;
-            int32_t s16;
-            code_sums(q, S, s16);
+        for (int i = threadIdx.x; i < 4 * B * nb; i += blockDim.x) {
+            const int blk = i >> 2, part = i & 3;
+            const int m = blk / nb, b = blk - m * nb;
+            const float4* xb = reinterpret_cast<const float4*>(x + (int64_t)m * K + 32 * b + 8 * part);
+            const float4 f0 = xb[0], f1 = xb[1];
+            const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+            float amax = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; k++) amax = fmaxf(amax, fabsf(v[k]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            const float d = amax / 127.0f;
+            const float id = d != 0.0f ? 1.0f / d : 0.0f;
+            uint32_t c2[2] = {0u, 0u};
+            int sp = 0;
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                const int qv = (int)roundf(v[k] * id);
+                sp += qv;
+                c2[k >> 2] |= ((uint32_t)qv & 0xFFu) << (8 * (k & 3));
+            }
+            const uint16_t h = float_to_half_bits(d);
+            const float dval = half_bits_to_float(h);
+            const int s01 = sp + __shfl_xor(sp, 1);     // parts 0+1 (lanes 0, 1), 2+3 (lanes 2, 3)
+            const int s23 = __shfl_xor(s01, 2);
             uint8_t* base = smem + m * rowb;
-            uint32_t wq[8];
-            __builtin_memcpy(wq, q, 32);
-            uint4* dst = reinterpret_cast<uint4*>(base + (b >> 3) * ACT_CHUNK_STRIDE + (b & 7) * 32);
-            dst[0] = make_uint4(wq[0], wq[1], wq[2], wq[3]);
-            dst[1] = make_uint4(wq[4], wq[5], wq[6], wq[7]);
-            float* dda = const_cast<float*>(A[m].da);
-            dda[b] = dval;
-            dda[nb + b] = dval * (float)S;
-            reinterpret_cast<int32_t*>(dda + 2 * nb)[b] = s16;
+            *reinterpret_cast<uint2*>(base + (b >> 3) * ACT_CHUNK_STRIDE + (b & 7) * 32 + 8 * part) =
+                make_uint2(c2[0], c2[1]);
+            float* dda = reinterpret_cast<float*>(base + C * ACT_CHUNK_STRIDE);
+            const int S = s01 + s23;
+            const int32_t s16 = (int32_t)(((uint32_t)s01 & 0xFFFFu) | ((uint32_t)s23 << 16));
+            if (part == 0) {
+                dda[b] = dval;
+                dda[nb + b] = dval * (float)S;
+                reinterpret_cast<int32_t*>(dda + 2 * nb)[b] = s16;
+            }
             if (writer) {
-                store_public(xq + ((int64_t)m * nb + b) * 34, q, h);
-                store_row_staging(xq, L, m, K, b, q, dval, S, s16);
+                uint8_t* pub = xq + ((int64_t)m * nb + b) * 34;
+                __builtin_memcpy(pub + 2 + 8 * part, c2, 8);
+                *reinterpret_cast<uint2*>(xq + L.rcodes + (int64_t)m * K + 32 * b + 8 * part) =
+                    make_uint2(c2[0], c2[1]);
+                if (part == 0) {
+                    const uint8_t hb[2] = {(uint8_t)(h & 255), (uint8_t)(h >> 8)};
+                    __builtin_memcpy(pub, hb, 2);
+                    reinterpret_cast<float*>(xq + L.rda)[m * nb + b] = dval;
+                    reinterpret_cast<float*>(xq + L.rca)[m * nb + b] = dval * (float)S;
+                    reinterpret_cast<int32_t*>(xq + L.rs16)[m * nb + b] = s16;
+                }
             }
         }
     } else {
@@ -1052,8 +1080,8 @@ inline int64_t resident_blocks(ResidentCache& cache, const void* kernel, int thr
     return cache.v[slot];
 }
 
-template <int FMT, int B>
-int launch_dot_b(const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq, float* y,
+template <int FMT, int B, bool FUSED>
+int launch_dot_f(const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq, float* y,
                  hipStream_t s) {
     using F = Fmt<FMT>;
     const ActLayout L = act_layout(B, K);
@@ -1066,7 +1094,7 @@ int launch_dot_b(const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t
     const size_t shmem = (size_t)B * act_lds_row_bytes(K) + 4 * B * 256;
     static bool attr_set = false;  // allow up to the full 160 KB of LDS
     if (!attr_set) {
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dot<FMT, B>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr_set = true;
     }
@@ -1075,13 +1103,21 @@ int launch_dot_b(const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t
     static size_t cache_shmem = 0;
     if (cache_shmem != shmem) { cache = ResidentCache(); cache_shmem = shmem; }
     const int64_t resident =
-        4 * resident_blocks(cache, reinterpret_cast<const void*>(&k_dot<FMT, B>), 256, shmem);
+        4 * resident_blocks(cache, reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED>), 256, shmem);
     const int64_t per = (units + resident - 1) / resident;
     const int64_t waves = (units + per - 1) / per;
     const int64_t blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((k_dot<FMT, B>), dim3((unsigned)blocks), dim3(256), shmem, s, w, wbytes,
-                       N, K, x, xq, L, y);
+    hipLaunchKernelGGL((k_dot<FMT, B, FUSED>), dim3((unsigned)blocks), dim3(256), shmem, s, w,
+                       wbytes, N, K, x, xq, L, y);
     return (int)hipGetLastError();
+}
+
+// x != NULL: the kernel quantises x itself
+template <int FMT, int B>
+int launch_dot_b(const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq, float* y,
+                 hipStream_t s) {
+    return x ? launch_dot_f<FMT, B, true>(w, N, K, x, xq, y, s)
+             : launch_dot_f<FMT, B, false>(w, N, K, x, xq, y, s);
 }
 
 template <int FMT>
