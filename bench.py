@@ -4,9 +4,10 @@
 One step = one decode token through a Q4_0 SwiGLU FFN at batch 1 (the
 Qwen2.5-0.5B FFN shape of the llamay pages: gate and up 4864x896, down
 896x4864): quantise the 896-wide activation once, GEMV gate and up on it,
-quantise the 4864-wide activation, GEMV down.  At batch 1 the library runs
-each quantisation inside the GEMV that first needs it, so a step is three
-launches.  Inputs are seeded synthetic
+quantise the 4864-wide activation, GEMV down.  The three GEMVs are
+independent here (down takes its own synthetic activation), so a step is one
+grouped launch (qmv_launch_group) in which each GEMV quantises its activation
+inside the kernel.  Inputs are seeded synthetic
 weights/activations already resident in HBM; the weights are rotated over
 copies totalling >= --rotate-mib so every step streams them from HBM rather
 than from the 256 MB last-level cache.  Steps are replayed from a captured
@@ -127,34 +128,26 @@ def ffn_workload(torch, g, synth, rotate_bytes):
 
 
 def make_ffn_step(torch, g, W):
+    """One decode step = one grouped launch (qmv_launch_group) of the three
+    GEMVs, each quantising its own activation inside the kernel; gate's and
+    down's Q8_0 blocks are also written to their xq buffers."""
     L = g.lib()
     fmt = W["fmt"]
-    ptr = {k: [t.data_ptr() for t in v] for k, v in W["copies"].items()}
+    R = W["R"]
     x1, x2 = W["x1"].data_ptr(), W["x2"].data_ptr()
     q1, q2 = W["xq1"].data_ptr(), W["xq2"].data_ptr()
     y = {k: v.data_ptr() for k, v in W["ys"].items()}
-    R = W["R"]
-
-    def check(rc, what):
-        if rc:
-            raise g.QmvError(rc, what)
-
-    def gemv(name, c):
-        # gate quantises x1 inside its GEMV, up reuses that quantisation,
-        # down quantises x2 inside its GEMV
-        s = torch.cuda.current_stream().cuda_stream
-        if name == "down":
-            check(L.qmv_launch(fmt, ptr[name][c], 896, 4864, x2, 1, q2, y[name], s), name)
-        else:
-            xin = x1 if name == "gate" else None
-            check(L.qmv_launch(fmt, ptr[name][c], 4864, 896, xin, 1, q1, y[name], s), name)
+    groups = []
+    for c in range(R):
+        wp = {k: v[c].data_ptr() for k, v in W["copies"].items()}
+        groups.append((g.Gemv * 3)(g.Gemv(wp["gate"], 4864, 896, x1, q1, y["gate"]),
+                                   g.Gemv(wp["up"], 4864, 896, x1, None, y["up"]),
+                                   g.Gemv(wp["down"], 896, 4864, x2, q2, y["down"])))
 
     def step(i, _unused=None):
-        c = i % R
-        gemv("gate", c)
-        gemv("up", c)
-        gemv("down", c)
-    step.gemv = gemv
+        rc = L.qmv_launch_group(fmt, 1, groups[i % R], 3, torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise g.QmvError(rc, "qmv_launch_group")
     return step
 
 
@@ -282,7 +275,7 @@ def traffic_from(pmc_dir):
     wk = [v for k, v in rows("write", "WRITE_SIZE") if "k_dot" in k]
     fetch = sum(fk) / len(fk) * 1024 * f_scale
     write = sum(wk) / len(wk) * 1024 * w_scale
-    out = {"kernel": "k_dot (GEMV, Q4_0, batch 1)", "kernel_src_sha": kernel_src_sha(),
+    out = {"kernel": "k_dot (grouped GEMV gate+up+down, Q4_0, batch 1)", "kernel_src_sha": kernel_src_sha(),
            "dispatches": [len(fk), len(wk)],
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
@@ -367,15 +360,14 @@ def main():
     t1 = time.perf_counter()
     wall = t1 - t0
 
-    # the dominant kernel, the GEMV: time per launch of the step's three GEMVs
-    # back to back over every rotated copy
-    order = ("gate", "up", "down")
-    per_launch_us = graph_launch_us(
-        torch, lambda i: step.gemv(order[i % 3], (i // 3) % W["R"]), 3 * W["R"])
+    # the dominant (only) kernel: time per launch of the grouped GEMV, back to
+    # back over every rotated copy
+    per_launch_us = graph_launch_us(torch, lambda i: step(i), W["R"])
+    # every GEMV reads its x; gate and down write their Q8_0 blocks, up does not
     alg = {"gate": gemv_alg_bytes(W["fmt"], 4864, 896, 1, g, fused=True),
-           "up": gemv_alg_bytes(W["fmt"], 4864, 896, 1, g),
+           "up": gemv_alg_bytes(W["fmt"], 4864, 896, 1, g, fused=True) - (896 // 32) * 34,
            "down": gemv_alg_bytes(W["fmt"], 896, 4864, 1, g, fused=True)}
-    alg_per_launch = sum(alg.values()) / 3
+    alg_per_launch = alg["gate"] + alg["up"] + alg["down"]
     achieved = alg_per_launch / (per_launch_us * 1e-6) / 1e9
 
     traffic = None
@@ -407,11 +399,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "k_dot<Q4_0, 1> (GEMV)", "avg_launch_us": round(per_launch_us, 3),
-                     "launches_timed": 3 * W["R"],
+                     "kernel": "k_dot<Q4_0, 1, fused> (grouped GEMV: gate, up, down)",
+                     "avg_launch_us": round(per_launch_us, 3),
+                     "launches_timed": W["R"],
                      "timing": "HIP events on the launch stream around a graph replay of the "
-                               "step's GEMVs (gate, up, down) back to back over every rotated "
-                               "copy; time per launch includes the inter-node dispatch gap",
+                               "step's grouped launch back to back over every rotated copy; "
+                               "time per launch includes the inter-node dispatch gap",
                      "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu:

@@ -17,9 +17,16 @@ LIB_PATH = os.path.join(HERE, "libqmv.so")
 Q4_0, Q8_0, Q4_K, Q6_K = 2, 8, 12, 14
 TYPES = {"Q4_0": Q4_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
 BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210)}
-EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmm_launch",
+EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
            "qmv_partials_launch", "qmv_strerror")
 MAX_BATCH = 16
+MAX_GROUP = 8
+
+
+class Gemv(ctypes.Structure):
+    """struct qmv_gemv: one GEMV of qmv_launch_group (pointers as integers)."""
+    _fields_ = [("w", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("x", ctypes.c_void_p), ("xq", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 class QmvError(RuntimeError):
@@ -44,8 +51,10 @@ def lib() -> ctypes.CDLL:
         L.quantize_act_q8_0.argtypes = [P, P, I64, I64, P]
         L.qmv_launch.argtypes = [I, P, I64, I64, P, I64, P, P, P]
         L.qmm_launch.argtypes = [I, P, I64, I64, P, I64, P, P, P]
+        L.qmv_launch_group.argtypes = [I, I64, ctypes.POINTER(Gemv), I, P]
         L.qmv_partials_launch.argtypes = [I, P, I64, I64, P, I64, P, P]
-        for f in ("quantize_act_q8_0", "qmv_launch", "qmm_launch", "qmv_partials_launch"):
+        for f in ("quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
+                  "qmv_partials_launch"):
             getattr(L, f).restype = I
         L.qmv_strerror.argtypes = [I]
         L.qmv_strerror.restype = ctypes.c_char_p
@@ -75,6 +84,12 @@ def quantize_act_q8_0(x, xq: int, rows: int, K: int, stream: int = 0) -> None:
 def qmv_launch(type: int, w: int, N: int, K: int, x, B: int, xq: int, y: int,
                stream: int = 0) -> None:
     _check(lib().qmv_launch(type, w, N, K, x, B, xq, y, stream), "qmv_launch")
+
+
+def qmv_launch_group(type: int, B: int, gemvs, stream: int = 0) -> None:
+    """gemvs: a sequence of Gemv (or of (w, N, K, x, xq, y) tuples)."""
+    arr = (Gemv * len(gemvs))(*[gv if isinstance(gv, Gemv) else Gemv(*gv) for gv in gemvs])
+    _check(lib().qmv_launch_group(type, B, arr, len(gemvs), stream), "qmv_launch_group")
 
 
 def qmm_launch(type: int, w: int, N: int, K: int, x, M: int, xq: int, y: int,
@@ -153,6 +168,32 @@ def matvec(type: int, w, N: int, K: int, x=None, xq=None, B=None, y=None, stream
     qmv_launch(type, _dev(w, torch.uint8, "w"), N, K, xp, B, _dev(xq, torch.uint8, "xq"),
                _dev(y, torch.float32, "y"), _stream(stream))
     return y
+
+
+def matvec_group(type: int, items, stream=None):
+    """Grouped decode GEMVs: items are dicts with w, N, K and x (f32 [B, K])
+    or xq (staged), optional xq / y.  Returns the list of y [B, N]."""
+    import torch
+    B = None
+    descs, ys = [], []
+    for it in items:
+        x, xq = it.get("x"), it.get("xq")
+        b = x.shape[0] if x is not None else it["B"]
+        if B is None:
+            B = b
+        elif b != B:
+            raise ValueError("all GEMVs of a group take the same number of rows")
+        w = it["w"]
+        y = it.get("y")
+        if y is None:
+            y = torch.empty(B, it["N"], dtype=torch.float32, device=w.device)
+        xp = _dev(x, torch.float32, "x") if x is not None else None
+        qp = _dev(xq, torch.uint8, "xq") if xq is not None else None
+        descs.append(Gemv(_dev(w, torch.uint8, "w"), it["N"], it["K"], xp, qp,
+                          _dev(y, torch.float32, "y")))
+        ys.append(y)
+    qmv_launch_group(type, B, descs, _stream(stream))
+    return ys
 
 
 def matmul(type: int, w, N: int, K: int, x=None, xq=None, M=None, y=None, stream=None):

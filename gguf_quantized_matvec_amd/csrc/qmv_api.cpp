@@ -94,6 +94,31 @@ int qmv_launch(int type, const void* w, int64_t N, int64_t K, const float* x, in
     return matmul_common(type, w, N, K, x, B, QMV_MAX_BATCH, xq, y, stream, false);
 }
 
+int qmv_launch_group(int type, int64_t B, const qmv_gemv* g, int count, void* stream) {
+    if (!g) return QMV_EINVAL_PTR;
+    if (count < 1 || count > QMV_MAX_GROUP || B < 1 || B > QMV_MAX_BATCH) return QMV_EINVAL_SHAPE;
+    const bool quantise = g[0].x != nullptr;
+    qmv::GemvDesc d[QMV_MAX_GROUP];
+    for (int k = 0; k < count; k++) {
+        const int rc = check_weights(type, g[k].w, g[k].N, g[k].K);
+        if (rc) return rc;
+        if ((g[k].x != nullptr) != quantise) return QMV_EINVAL_PTR;
+        if (!g[k].y || !aligned(g[k].y, 4)) return QMV_EINVAL_PTR;
+        if (g[k].x && !aligned(g[k].x, 16)) return QMV_EINVAL_PTR;
+        if (!g[k].x && !g[k].xq) return QMV_EINVAL_PTR;
+        if (g[k].xq && !aligned(g[k].xq, 16)) return QMV_EINVAL_PTR;
+        d[k] = qmv::GemvDesc{static_cast<const uint8_t*>(g[k].w), g[k].N, g[k].K, g[k].x,
+                             static_cast<uint8_t*>(g[k].xq), g[k].y};
+    }
+    // xq may be left NULL only when the whole group runs as one fused launch;
+    // every other path quantises into xq first
+    for (int k = 0; k < count; k++)
+        if (!g[k].xq && qmv::staging_for(B, g[k].K) != qmv::ST_ROW) return QMV_EINVAL_PTR;
+    const int rc = check_device();
+    if (rc) return rc;
+    return launched(qmv::launch_qmv_group(type, d, count, B, static_cast<hipStream_t>(stream)));
+}
+
 int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t M,
                void* xq, float* y, void* stream) {
     return matmul_common(type, w, N, K, x, M, QMV_MAX_M, xq, y, stream, true);

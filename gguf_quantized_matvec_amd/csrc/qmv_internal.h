@@ -52,6 +52,26 @@ inline ActLayout act_layout(int64_t rows, int64_t K) {
     return L;
 }
 
+// One GEMV of a (possibly grouped) decode launch.
+struct GemvDesc {
+    const uint8_t* w;
+    int64_t N, K;
+    const float* x;   // non-NULL: quantised by the launch
+    uint8_t* xq;      // staged quantisation (x NULL), or where to write it (may be NULL if x given)
+    float* y;
+};
+
+// Bytes of one weight row.
+inline int64_t row_bytes(int type, int64_t K) {
+    switch (type) {
+    case 2: return K / 32 * 18;     // Q4_0
+    case 8: return K / 32 * 34;     // Q8_0
+    case 12: return K / 256 * 144;  // Q4_K
+    case 14: return K / 256 * 210;  // Q6_K
+    }
+    return 0;
+}
+
 // Which private staging copies a quantisation writes: only those that the
 // multiply for that many rows reads.
 enum Staging : int {
@@ -69,6 +89,9 @@ int launch_quantize(const float* x, uint8_t* xq, int64_t rows, int64_t K, int st
 int launch_rebuild(uint8_t* xq, int64_t rows, int64_t K, int staging, hipStream_t s);
 int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                int64_t rows, float* y, hipStream_t s);
+// count GEMVs of one type and row count: one launch if the lane-per-chunk
+// kernel takes them all (and all or none quantise x), else one after another.
+int launch_qmv_group(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s);
 int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* xq,
                     int64_t rows, int32_t* P, hipStream_t s);
 int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,

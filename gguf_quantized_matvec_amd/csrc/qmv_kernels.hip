@@ -864,28 +864,43 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
     }
 }
 
-// Persistent waves over work units.  C <= 64 chunks per row: a unit is G =
-// 64/LPR rows (LPR = lanes per row, a power of two >= C) in one pass.
-// C > 64: a unit is one row, in passes of 64 chunks.  Chunk sums are added
-// in chunk order per row through a small LDS buffer.
-// Persistent waves over work units.  C <= 64 chunks per row: a unit is G =
-// 64/LPR rows (LPR = lanes per row, a power of two >= C) in one pass.
-// C > 64: a unit is one row, in passes of 64 chunks.  Every lane streams its
-// chunk straight into registers; at this register count many waves stay
-// resident, which keeps enough bytes in flight to cover HBM latency.  Chunk
-// sums are added in chunk order per row through a small LDS buffer.
-// FUSED: every workgroup quantises the B activation rows from x straight into
-// its LDS (the same arithmetic as k_quantize), and workgroup 0 also writes
-// them to xq (Q8_0 blocks and the row-major staging) for later calls.
+// One GEMV of a launch (a launch may carry several, of one format and one
+// row count B): weights, shape, output, and the activations: x to quantise
+// in the kernel (FUSED), or the staged quantisation in xq.
+struct DotJob {
+    const uint8_t* w;
+    float* y;
+    const float* x;   // FUSED: f32 activations [B][K]
+    uint8_t* xq;      // staged quantisation; FUSED: written by the job's first workgroup (may be NULL)
+    int64_t N, K, wbytes;
+    int64_t rcodes, rda, rca, rs16;  // offsets of the row-major staging in xq
+    int first_block;                 // the job's first workgroup in the grid
+};
+constexpr int MAX_JOBS = 8;
+struct DotJobs {
+    DotJob j[MAX_JOBS];
+    int count;
+};
+
+// Work units: C <= 64 chunks per row: a unit is G = 64/LPR rows (LPR = lanes
+// per row, a power of two >= C), one chunk per lane; C > 64: a unit is one
+// row, in passes of 64 chunks.  Every wave takes one unit; a workgroup is 4
+// waves sharing the activation rows staged in LDS.  Each lane streams its
+// chunk straight into registers, issued before the activations are staged.
+// Chunk sums are added in chunk order per row through a small LDS buffer,
+// and each row's result is stored once, at the end.
 template <int FMT, int B, bool FUSED>
-__global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int64_t wbytes,
-                                             int64_t N, int64_t K, const float* __restrict__ x,
-                                             uint8_t* __restrict__ xq, ActLayout L,
-                                             float* __restrict__ y) {
+__global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
     using F = Fmt<FMT>;
     constexpr int NWD = DotFmt<FMT>::NWD;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    // this workgroup's job (compile-time indices: the table stays in scalar registers)
+    DotJob J = jobs.j[0];
+#pragma unroll
+    for (int k = 1; k < MAX_JOBS; k++)
+        if (k < jobs.count && (int)blockIdx.x >= jobs.j[k].first_block) J = jobs.j[k];
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
+    const int64_t N = J.N, K = J.K;
     const int nb = (int)(K >> 5), C = (nb + 7) >> 3;
     const int rowb = act_lds_row_bytes(K);
     float (*pbuf)[64] = reinterpret_cast<float (*)[64]>(smem + B * rowb + wv * B * 256);
@@ -894,28 +909,24 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
     int LPR = 1;
     while (LPR < C && LPR < 64) LPR <<= 1;
     const int G = 64 / LPR;
-    const int PR = (C + 63) >> 6;  // passes per unit (1 unless C > 64)
+    const int PR = (C + 63) >> 6;  // passes (1 unless C > 64)
     const int64_t units = C <= 64 ? (N + G - 1) / G : N;
-    const int64_t TW = (int64_t)gridDim.x * (blockDim.x >> 6);
-    const int64_t first = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
-    // items of this wave: (unit first + k*TW, pass q), k-major
-    const int64_t nit = first < units ? ((units - first + TW - 1) / TW) * PR : 0;
+    const int64_t u = (int64_t)((int)blockIdx.x - J.first_block) * 4 + wv;
+    const bool active = u < units;
 
-    auto slot = [&](int64_t it, int64_t& u, int& q, int64_t& row, int& c) {
-        u = first + (it / PR) * TW;
-        q = (int)(it % PR);
+    auto chunk_of = [&](int q, int64_t& row, int& c) {
         row = C <= 64 ? u * G + lane / LPR : u;
         c = C <= 64 ? (lane & (LPR - 1)) : 64 * q + lane;
     };
-    auto issue = [&](int64_t it, uint32_t (&r)[NWD]) {
-        int64_t u, row;
-        int q, c;
-        slot(it, u, q, row, c);
-        const bool valid = row < N && c < C;
+    auto issue = [&](int q, uint32_t (&r)[NWD]) {
+        int64_t row;
+        int c;
+        chunk_of(q, row, c);
+        const bool valid = active && row < N && c < C;
         const int64_t off = row * R + (int64_t)c * F::CB;
-        const bool near_end = valid && off + 4 * NWD > wbytes;
+        const bool near_end = valid && off + 4 * NWD > J.wbytes;
         if (valid) {
-            load_chunk_regs<FMT>(w, off, wbytes, __builtin_amdgcn_ballot_w64(near_end) != 0, r);
+            load_chunk_regs<FMT>(J.w, off, J.wbytes, __builtin_amdgcn_ballot_w64(near_end) != 0, r);
         } else {
 #pragma unroll
             for (int i = 0; i < NWD; i++) r[i] = 0;
@@ -924,7 +935,7 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
 
     // first chunk in flight while the activations are staged
     uint32_t r[NWD];
-    if (nit > 0) issue(0, r);
+    issue(0, r);
 
     // stage the B activation rows: codes (per-chunk padded), da, ca, s16
     ActRow A[B];
@@ -939,7 +950,9 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
     if constexpr (FUSED) {
         // four lanes per block, 8 elements each: the block's amax and code
         // sums by lane shuffles, then the same d, id and codes as k_quantize
-        const bool writer = blockIdx.x == 0;
+        const bool writer = (int)blockIdx.x == J.first_block && J.xq != nullptr;
+        const float* x = J.x;
+        uint8_t* xq = J.xq;
         for (int i = threadIdx.x; i < 4 * B * nb; i += blockDim.x) {
             const int blk = i >> 2, part = i & 3;
             const int m = blk / nb, b = blk - m * nb;
@@ -979,27 +992,28 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
             if (writer) {
                 uint8_t* pub = xq + ((int64_t)m * nb + b) * 34;
                 __builtin_memcpy(pub + 2 + 8 * part, c2, 8);
-                *reinterpret_cast<uint2*>(xq + L.rcodes + (int64_t)m * K + 32 * b + 8 * part) =
+                *reinterpret_cast<uint2*>(xq + J.rcodes + (int64_t)m * K + 32 * b + 8 * part) =
                     make_uint2(c2[0], c2[1]);
                 if (part == 0) {
                     const uint8_t hb[2] = {(uint8_t)(h & 255), (uint8_t)(h >> 8)};
                     __builtin_memcpy(pub, hb, 2);
-                    reinterpret_cast<float*>(xq + L.rda)[m * nb + b] = dval;
-                    reinterpret_cast<float*>(xq + L.rca)[m * nb + b] = dval * (float)S;
-                    reinterpret_cast<int32_t*>(xq + L.rs16)[m * nb + b] = s16;
+                    reinterpret_cast<float*>(xq + J.rda)[m * nb + b] = dval;
+                    reinterpret_cast<float*>(xq + J.rca)[m * nb + b] = dval * (float)S;
+                    reinterpret_cast<int32_t*>(xq + J.rs16)[m * nb + b] = s16;
                 }
             }
         }
     } else {
+        const uint8_t* xq = J.xq;
 #pragma unroll
         for (int m = 0; m < B; m++) {
             uint8_t* base = smem + m * rowb;
-            const uint4* src = reinterpret_cast<const uint4*>(xq + L.rcodes + m * K);
+            const uint4* src = reinterpret_cast<const uint4*>(xq + J.rcodes + m * K);
             for (int i = threadIdx.x; i < nb * 2; i += blockDim.x)  // 16-byte pieces
                 *reinterpret_cast<uint4*>(base + (i >> 4) * ACT_CHUNK_STRIDE + (i & 15) * 16) = src[i];
-            const float* sda = reinterpret_cast<const float*>(xq + L.rda) + m * nb;
-            const float* sca = reinterpret_cast<const float*>(xq + L.rca) + m * nb;
-            const int32_t* ss = reinterpret_cast<const int32_t*>(xq + L.rs16) + m * nb;
+            const float* sda = reinterpret_cast<const float*>(xq + J.rda) + m * nb;
+            const float* sca = reinterpret_cast<const float*>(xq + J.rca) + m * nb;
+            const int32_t* ss = reinterpret_cast<const int32_t*>(xq + J.rs16) + m * nb;
             float* dda = const_cast<float*>(A[m].da);
             for (int i = threadIdx.x; i < nb; i += blockDim.x) {
                 dda[i] = sda[i];
@@ -1009,15 +1023,15 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
         }
     }
     __syncthreads();
-    if (nit == 0) return;
+    if (!active) return;
 
     float yacc[B];
 #pragma unroll
     for (int j = 0; j < B; j++) yacc[j] = 0.0f;
-    for (int64_t it = 0; it < nit; it++) {
-        int64_t u, row;
-        int q, c;
-        slot(it, u, q, row, c);
+    for (int q = 0; q < PR; q++) {
+        int64_t row;
+        int c;
+        chunk_of(q, row, c);
         const bool valid = row < N && c < C;
         const int nbc = F::QK == 32 ? min(8, nb - 8 * c) : 8;
         float p[B];
@@ -1027,7 +1041,7 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
 #pragma unroll
             for (int m = 0; m < B; m++) p[m] = 0.0f;
         }
-        if (it + 1 < nit) issue(it + 1, r);  // registers are free again
+        if (q + 1 < PR) issue(q + 1, r);  // registers are free again
 #pragma unroll
         for (int m = 0; m < B; m++) pbuf[m][lane] = p[m];
         wave_sync();
@@ -1042,93 +1056,93 @@ __global__ __launch_bounds__(256) void k_dot(const uint8_t* __restrict__ w, int6
             }
         }
         wave_sync();
-        if (q == PR - 1) {
+    }
 #pragma unroll
-            for (int j = 0; j < B; j++) {
-                const int t = lane + 64 * j;
-                if (t < G * B) {
-                    const int m = t / G, rl = t - m * G;
-                    const int64_t orow = C <= 64 ? u * G + rl : u;
-                    if (orow < N) y[m * N + orow] = yacc[j];
-                }
-                yacc[j] = 0.0f;
-            }
+    for (int j = 0; j < B; j++) {
+        const int t = lane + 64 * j;
+        if (t < G * B) {
+            const int m = t / G, rl = t - m * G;
+            const int64_t orow = C <= 64 ? u * G + rl : u;
+            if (orow < N) J.y[m * N + orow] = yacc[j];
         }
     }
 }
 
-// Workgroups of `threads` threads and `shmem` bytes of LDS that the whole
-// device holds at once (occupancy of the kernel times the CU count), cached
-// per call site and device.
-struct ResidentCache {
-    int64_t v[16] = {0};
-};
-inline int64_t resident_blocks(ResidentCache& cache, const void* kernel, int threads,
-                               size_t shmem) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    const int slot = dev & 15;
-    if (cache.v[slot] > 0) return cache.v[slot];
-    int per_cu = 0, cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1)
-        cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, shmem) !=
-            hipSuccess || per_cu < 1)
-        per_cu = 1;
-    cache.v[slot] = (int64_t)per_cu * cus;
-    return cache.v[slot];
-}
-
-template <int FMT, int B, bool FUSED>
-int launch_dot_f(const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq, float* y,
-                 hipStream_t s) {
-    using F = Fmt<FMT>;
-    const ActLayout L = act_layout(B, K);
+// Workgroups of the dot kernel for one GEMV: one wave per unit, 4 per group.
+inline int64_t dot_blocks(int type, int64_t N, int64_t K) {
     const int nb = (int)(K / 32), C = (nb + 7) / 8;
     int LPR = 1;
     while (LPR < C && LPR < 64) LPR <<= 1;
     const int64_t G = 64 / LPR;
+    (void)type;
     const int64_t units = C <= 64 ? (N + G - 1) / G : N;
-    const int64_t wbytes = N * (K / F::QK) * F::BB;
-    const size_t shmem = (size_t)B * act_lds_row_bytes(K) + 4 * B * 256;
+    return (units + 3) / 4;
+}
+
+inline size_t dot_shmem(int B, int64_t K) { return (size_t)B * act_lds_row_bytes(K) + 4 * B * 256; }
+
+template <int FMT, int B, bool FUSED>
+int launch_dot_jobs(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
     static bool attr_set = false;  // allow up to the full 160 KB of LDS
     if (!attr_set) {
         hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr_set = true;
     }
-    // one resident generation of waves, each walking units with stride
-    static ResidentCache cache;  // occupancy depends on K only through shmem: key on it
-    static size_t cache_shmem = 0;
-    if (cache_shmem != shmem) { cache = ResidentCache(); cache_shmem = shmem; }
-    const int64_t resident =
-        4 * resident_blocks(cache, reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED>), 256, shmem);
-    const int64_t per = (units + resident - 1) / resident;
-    const int64_t waves = (units + per - 1) / per;
-    const int64_t blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((k_dot<FMT, B, FUSED>), dim3((unsigned)blocks), dim3(256), shmem, s, w,
-                       wbytes, N, K, x, xq, L, y);
+    hipLaunchKernelGGL((k_dot<FMT, B, FUSED>), dim3((unsigned)blocks), dim3(256), shmem, s, jobs);
     return (int)hipGetLastError();
 }
 
-// x != NULL: the kernel quantises x itself
-template <int FMT, int B>
-int launch_dot_b(const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq, float* y,
-                 hipStream_t s) {
-    return x ? launch_dot_f<FMT, B, true>(w, N, K, x, xq, y, s)
-             : launch_dot_f<FMT, B, false>(w, N, K, x, xq, y, s);
+template <int FMT>
+int launch_dot_rows(const DotJobs& jobs, int64_t rows, bool fused, int64_t blocks, size_t shmem,
+                    hipStream_t s) {
+    switch (rows) {
+    case 1: return fused ? launch_dot_jobs<FMT, 1, true>(jobs, blocks, shmem, s)
+                         : launch_dot_jobs<FMT, 1, false>(jobs, blocks, shmem, s);
+    case 2: return fused ? launch_dot_jobs<FMT, 2, true>(jobs, blocks, shmem, s)
+                         : launch_dot_jobs<FMT, 2, false>(jobs, blocks, shmem, s);
+    case 3: return fused ? launch_dot_jobs<FMT, 3, true>(jobs, blocks, shmem, s)
+                         : launch_dot_jobs<FMT, 3, false>(jobs, blocks, shmem, s);
+    default: return fused ? launch_dot_jobs<FMT, 4, true>(jobs, blocks, shmem, s)
+                          : launch_dot_jobs<FMT, 4, false>(jobs, blocks, shmem, s);
+    }
 }
 
-template <int FMT>
-int launch_dot_t(const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
-                 int64_t rows, float* y, hipStream_t s) {
-    switch (rows) {
-    case 1: return launch_dot_b<FMT, 1>(w, N, K, x, xq, y, s);
-    case 2: return launch_dot_b<FMT, 2>(w, N, K, x, xq, y, s);
-    case 3: return launch_dot_b<FMT, 3>(w, N, K, x, xq, y, s);
-    default: return launch_dot_b<FMT, 4>(w, N, K, x, xq, y, s);
+// One launch of the dot kernel over `count` GEMVs of one type and row count.
+int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s) {
+    if (count < 1 || count > MAX_JOBS) return (int)hipErrorInvalidValue;
+    DotJobs jobs{};
+    jobs.count = count;
+    int64_t blocks = 0;
+    size_t shmem = 0;
+    const bool fused = d[0].x != nullptr;
+    for (int k = 0; k < count; k++) {
+        const ActLayout L = act_layout(rows, d[k].K);
+        DotJob& J = jobs.j[k];
+        J.w = d[k].w;
+        J.y = d[k].y;
+        J.x = d[k].x;
+        J.xq = d[k].xq;
+        J.N = d[k].N;
+        J.K = d[k].K;
+        J.wbytes = d[k].N * row_bytes(type, d[k].K);
+        J.rcodes = L.rcodes;
+        J.rda = L.rda;
+        J.rca = L.rca;
+        J.rs16 = L.rs16;
+        J.first_block = (int)blocks;
+        blocks += dot_blocks(type, d[k].N, d[k].K);
+        const size_t sh = dot_shmem((int)rows, d[k].K);
+        shmem = sh > shmem ? sh : shmem;
     }
+    if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
+    switch (type) {
+    case T_Q8_0: return launch_dot_rows<T_Q8_0>(jobs, rows, fused, blocks, shmem, s);
+    case T_Q4_0: return launch_dot_rows<T_Q4_0>(jobs, rows, fused, blocks, shmem, s);
+    case T_Q4_K: return launch_dot_rows<T_Q4_K>(jobs, rows, fused, blocks, shmem, s);
+    case T_Q6_K: return launch_dot_rows<T_Q6_K>(jobs, rows, fused, blocks, shmem, s);
+    }
+    return (int)hipErrorInvalidValue;
 }
 
 // Rows of the 16-row activation group each lane needs (see chunk_math).
@@ -1213,14 +1227,10 @@ int launch_rebuild(uint8_t* xq, int64_t rows, int64_t K, int staging, hipStream_
 int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                int64_t rows, float* y, hipStream_t s) {
     if (use_dot(rows, K)) {  // quantisation fused into the kernel when x is given
-        switch (type) {
-        case T_Q8_0: return launch_dot_t<T_Q8_0>(w, N, K, x, xq, rows, y, s);
-        case T_Q4_0: return launch_dot_t<T_Q4_0>(w, N, K, x, xq, rows, y, s);
-        case T_Q4_K: return launch_dot_t<T_Q4_K>(w, N, K, x, xq, rows, y, s);
-        case T_Q6_K: return launch_dot_t<T_Q6_K>(w, N, K, x, xq, rows, y, s);
-        }
-        return (int)hipErrorInvalidValue;
+        const GemvDesc d{w, N, K, x, xq, y};
+        return launch_dot(type, &d, 1, rows, s);
     }
+    if (!xq) return (int)hipErrorInvalidValue;  // the MFMA path reads a staged xq
     if (x) {
         const int rc = launch_quantize(x, xq, rows, K, ST_MFMA, s);
         if (rc) return rc;
@@ -1232,6 +1242,20 @@ int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
     case T_Q6_K: return launch_qmv_t<T_Q6_K>(w, N, K, xq, rows, y, nullptr, s, false);
     }
     return (int)hipErrorInvalidValue;
+}
+
+int launch_qmv_group(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s) {
+    bool one = count <= MAX_JOBS;
+    for (int k = 0; k < count && one; k++)
+        one = use_dot(rows, d[k].K) && ((d[k].x != nullptr) == (d[0].x != nullptr));
+    if (one) return launch_dot(type, d, count, rows, s);
+    for (int k = 0; k < count; k++)  // one after another: each needs its xq
+        if (!d[k].xq) return (int)hipErrorInvalidValue;
+    for (int k = 0; k < count; k++) {
+        const int rc = launch_qmv(type, d[k].w, d[k].N, d[k].K, d[k].x, d[k].xq, rows, d[k].y, s);
+        if (rc) return rc;
+    }
+    return 0;
 }
 
 int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* xq,

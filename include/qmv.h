@@ -78,6 +78,7 @@ enum qmv_status {
 #define QMV_MAX_K (1 << 20)
 #define QMV_MAX_BATCH 16
 #define QMV_MAX_M (1 << 24)
+#define QMV_MAX_GROUP 8
 
 /* Bytes of activation scratch `xq` for `rows` rows of K elements.  The first
  * rows*(K/32)*34 bytes are the Q8_0 blocks (fp16 d little-endian, then 32
@@ -105,6 +106,29 @@ int quantize_act_q8_0(const float* x, void* xq, int64_t rows, int64_t K, void* s
  * the weights once rather than once per sequence). */
 int qmv_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
                void* xq, float* y, void* stream);
+
+/* One GEMV of a grouped decode launch (qmv_launch_group). */
+typedef struct qmv_gemv {
+    const void* w;   /* weight blob as for qmv_launch */
+    int64_t N, K;
+    const float* x;  /* [B][K] f32 activations, or NULL for all entries (xq staged) */
+    void* xq;        /* qmv_act_bytes(B, K) bytes: receives the quantisation when x is given,
+                        or holds it when x is NULL.  May be NULL only with x given and
+                        B <= 4 (the group then runs as one launch that needs no scratch);
+                        otherwise a NULL xq is refused with QMV_EINVAL_PTR */
+    float* y;        /* [B][N] */
+} qmv_gemv;
+
+/* Several independent decode GEMVs of one weight type and one batch B, such
+ * as the gate, up and down projections of a decode step, in one launch when
+ * the lane-per-chunk kernel takes them all (B <= 4), so that they share the
+ * launch latency and the chip instead of running one after another; larger B
+ * runs them one after another.  Either every entry quantises its own x, or
+ * every entry reads a staged xq (x NULL).  1 <= count <= QMV_MAX_GROUP.
+ * Entry k gives bit-identical y (and xq, when written) to qmv_launch(type,
+ * w, N, K, x, B, xq, y) on its own.  Entries must not write to memory that
+ * another entry reads or writes. */
+int qmv_launch_group(int type, int64_t B, const qmv_gemv* g, int count, void* stream);
 
 /* Prefill GEMM (MatMul): y[M][N] = x[M][K] * W^T for any M >= 1.  Prefill
  * is the arithmetic-bound phase ("Architecture", bench transcript): for

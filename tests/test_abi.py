@@ -74,6 +74,24 @@ def test_qmm_and_partials_refusals():
     assert L.quantize_act_q8_0(FAKE + 4, FAKE, 1, 32, None) == -3
 
 
+def test_group_refusals():
+    L = g.lib()
+    G = g.Gemv
+    ok = G(16, 1, 32, 16, None, 16)
+    arr = (G * 1)(ok)
+    assert L.qmv_launch_group(3, 1, arr, 1, None) == -1                    # type
+    assert L.qmv_launch_group(8, 1, arr, 0, None) == -2                    # count
+    assert L.qmv_launch_group(8, 1, arr, 9, None) == -2
+    assert L.qmv_launch_group(8, 17, arr, 1, None) == -2                   # batch
+    assert L.qmv_launch_group(8, 1, None, 1, None) == -3
+    two = (G * 2)(ok, G(16, 1, 32, None, 16, 16))                          # x given for one only
+    assert L.qmv_launch_group(8, 1, two, 2, None) == -3
+    assert L.qmv_launch_group(8, 1, (G * 1)(G(16, 1, 32, None, None, 16)), 1, None) == -3
+    assert L.qmv_launch_group(12, 1, (G * 1)(G(16, 1, 96, 16, None, 16)), 1, None) == -2
+    # xq may be NULL only for a single fused launch (B <= 4); B = 5 quantises into xq
+    assert L.qmv_launch_group(8, 5, (G * 1)(G(16, 1, 32, 16, None, 16)), 1, None) == -3
+
+
 def test_strerror_names_what_works():
     assert "Q4_0" in g.strerror(-1) and "Q6_K" in g.strerror(-1)
     assert "K % 256" in g.strerror(-2) and "qmm_launch" in g.strerror(-2)

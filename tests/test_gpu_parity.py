@@ -252,3 +252,37 @@ def test_byte_coverage(g):
         if np.array_equal(host(g.matvec(fmt, dev(b2), N, K, x=xd)), base):
             unchanged.append(i)
     assert not unchanged, f"bytes with no effect: {unchanged[:10]}"
+
+
+@pytest.mark.parametrize("fmt,shapes", [
+    (synth.Q4_0, [(4864, 896), (4864, 896), (896, 4864)]),
+    (synth.Q4_K, [(300, 1024), (45, 4864), (7, 256)]),
+    (synth.Q6_K, [(33, 768), (19, 1024)]),
+    (synth.Q8_0, [(100, 896), (16, 32), (33, 4192), (17, 64), (5, 32), (70, 416), (9, 96), (40, 4096)]),
+])
+@pytest.mark.parametrize("B", [1, 3, 5])
+def test_group_equals_single_launches(g, fmt, shapes, B):
+    """qmv_launch_group: every entry bit-identical to its own qmv_launch, with
+    quantisation in the launch (xq written for the first entry only) and with
+    staged xq."""
+    items, ref, xs, blobs = [], [], [], []
+    for k, (N, K) in enumerate(shapes):
+        blob, x = _inputs(fmt, N, K, B, 800 + 10 * k + B)
+        w = dev(blob)
+        blobs.append(w)
+        xs.append(x)
+        ref.append(host(g.matvec(fmt, w, N, K, x=dev(x))))
+        # xq may be left out only when the group runs as one launch (B <= 4)
+        items.append({"w": w, "N": N, "K": K, "x": dev(x),
+                      "xq": g.act_buffer(B, K) if k == 0 or B > 4 else None})
+    ys = g.matvec_group(fmt, items)
+    for k, (N, K) in enumerate(shapes):
+        assert_bitwise(host(ys[k]), ref[k], f"group entry {k} ({N}x{K})")
+    pub_end = B * (shapes[0][1] // 32) * 34
+    assert_bitwise(host(items[0]["xq"])[:pub_end], oracle.quantize_act(xs[0]).reshape(-1),
+                   "group xq")
+    staged = [{"w": blobs[k], "N": N, "K": K, "B": B, "xq": g.quantize(dev(xs[k]))}
+              for k, (N, K) in enumerate(shapes)]
+    ys2 = g.matvec_group(fmt, staged)
+    for k in range(len(shapes)):
+        assert_bitwise(host(ys2[k]), ref[k], f"staged group entry {k}")
