@@ -688,8 +688,8 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
 
 // Dwords of one chunk as loaded from the 4-byte-aligned address at or below
 // the chunk start (chunks start 2-byte aligned; 16-byte loads at 2-byte
-// alignment lose a quarter of the bandwidth, at 4-byte alignment nothing),
-// then shifted down by 0 or 2 bytes so that r[] holds the chunk from byte 0.
+// alignment lose a quarter of the bandwidth, at 4-byte alignment nothing);
+// realign_chunk then shifts them down by 0 or 2 bytes.
 template <int FMT> struct DotFmt;
 // NWD = ceil(CB/4) dwords after the shift, plus the one the shift reads from.
 template <> struct DotFmt<T_Q8_0> { static constexpr int NWD = 69; };  // 272 B: 68 + 1
@@ -714,7 +714,15 @@ __device__ __forceinline__ void load_chunk_regs(const uint8_t* w, int64_t off, i
                  : g + 2 <= wbytes ? (uint32_t)*reinterpret_cast<const uint16_t*>(w + g) : 0u;
         }
     }
-    if (FMT != T_Q4_K) {
+}
+
+// Shift the loaded dwords down by the chunk's offset inside its first dword
+// (0 or 2 bytes), so that r[] holds the chunk from byte 0.  Separate from the
+// loads so that the wait for them falls just before the chunk is used.
+template <int FMT>
+__device__ __forceinline__ void realign_chunk(int64_t off, uint32_t (&r)[DotFmt<FMT>::NWD]) {
+    constexpr int NWD = DotFmt<FMT>::NWD;
+    if constexpr (FMT != T_Q4_K) {
         const uint32_t sh = (uint32_t)(off & 3);  // 0 or 2
 #pragma unroll
         for (int j = 0; j < NWD - 1; j++) r[j] = __builtin_amdgcn_alignbyte(r[j + 1], r[j], sh);
@@ -933,9 +941,11 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
         }
     };
 
-    // first chunk in flight while the activations are staged
+    // first chunk in flight while the activations are staged (FUSED: issued
+    // right after the first activation loads, so that those, which complete
+    // in issue order, need not wait for the weights)
     uint32_t r[NWD];
-    issue(0, r);
+    if constexpr (!FUSED) issue(0, r);
 
     // stage the B activation rows: codes (per-chunk padded), da, ca, s16
     ActRow A[B];
@@ -953,11 +963,30 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
         const bool writer = (int)blockIdx.x == J.first_block && J.xq != nullptr;
         const float* x = J.x;
         uint8_t* xq = J.xq;
-        for (int i = threadIdx.x; i < 4 * B * nb; i += blockDim.x) {
+        const int total = 4 * B * nb;  // (block, quarter) tasks; whole blocks stay in one pass
+        constexpr int UNR = 2;         // passes whose x loads are issued together
+        for (int pass = 0; pass == 0 || (int)threadIdx.x + pass * UNR * (int)blockDim.x < total; pass++) {
+          const int i0 = threadIdx.x + pass * UNR * blockDim.x;
+          float4 xf[UNR][2];
+#pragma unroll
+          for (int uu = 0; uu < UNR; uu++) {
+            const int i = i0 + uu * blockDim.x;
+            if (i < total) {
+              const int blk = i >> 2, part = i & 3;
+              const int m = blk / nb, b = blk - m * nb;
+              const float4* xb = reinterpret_cast<const float4*>(x + (int64_t)m * K + 32 * b + 8 * part);
+              xf[uu][0] = xb[0];
+              xf[uu][1] = xb[1];
+            }
+          }
+          if (pass == 0) issue(0, r);  // every lane takes pass 0
+#pragma unroll
+          for (int uu = 0; uu < UNR; uu++) {
+            const int i = i0 + uu * blockDim.x;
+            if (i >= total) break;
             const int blk = i >> 2, part = i & 3;
             const int m = blk / nb, b = blk - m * nb;
-            const float4* xb = reinterpret_cast<const float4*>(x + (int64_t)m * K + 32 * b + 8 * part);
-            const float4 f0 = xb[0], f1 = xb[1];
+            const float4 f0 = xf[uu][0], f1 = xf[uu][1];
             const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
             float amax = 0.0f;
 #pragma unroll
@@ -1002,6 +1031,7 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
                     reinterpret_cast<int32_t*>(xq + J.rs16)[m * nb + b] = s16;
                 }
             }
+          }
         }
     } else {
         const uint8_t* xq = J.xq;
@@ -1036,6 +1066,7 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
         const int nbc = F::QK == 32 ? min(8, nb - 8 * c) : 8;
         float p[B];
         if (valid) {
+            realign_chunk<FMT>(row * R + (int64_t)c * F::CB, r);
             dot_chunk<FMT, B>(r, A, c, nbc, p);
         } else {
 #pragma unroll
