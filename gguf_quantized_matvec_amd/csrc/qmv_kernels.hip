@@ -945,7 +945,37 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
     // right after the first activation loads, so that those, which complete
     // in issue order, need not wait for the weights)
     uint32_t r[NWD];
-    if constexpr (!FUSED) issue(0, r);
+    // non-fused: the first pass of the activation copy is loaded into
+    // registers and stored to LDS after the weights are issued.  A long copy
+    // (>= 256 pieces) is loaded before the weights, so that it is not queued
+    // behind them (loads complete in issue order); a short one after them.
+    constexpr int SP = 4, SW = 2;  // 16-byte code pieces / scale words per thread in that pass
+    uint4 pc[SP];
+    uint32_t pw[SW][3];
+    const int npc = B * nb * 2, nwd = B * nb;
+    const bool copy_first = npc >= 256;
+    if constexpr (!FUSED) {
+        const uint8_t* xq = J.xq;
+        if (!copy_first) issue(0, r);
+#pragma unroll
+        for (int uu = 0; uu < SP; uu++) {
+            const int i = threadIdx.x + uu * blockDim.x;  // piece i: row i / (2nb), piece i % (2nb)
+            if (i < npc) {
+                const int m = i / (2 * nb), k = i - m * 2 * nb;
+                pc[uu] = reinterpret_cast<const uint4*>(xq + J.rcodes + (int64_t)m * K)[k];
+            }
+        }
+#pragma unroll
+        for (int uu = 0; uu < SW; uu++) {
+            const int i = threadIdx.x + uu * blockDim.x;  // word i: row i / nb, block i % nb
+            if (i < nwd) {
+                pw[uu][0] = reinterpret_cast<const uint32_t*>(xq + J.rda)[i];
+                pw[uu][1] = reinterpret_cast<const uint32_t*>(xq + J.rca)[i];
+                pw[uu][2] = reinterpret_cast<const uint32_t*>(xq + J.rs16)[i];
+            }
+        }
+        if (copy_first) issue(0, r);
+    }
 
     // stage the B activation rows: codes (per-chunk padded), da, ca, s16
     ActRow A[B];
@@ -1035,22 +1065,37 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
         }
     } else {
         const uint8_t* xq = J.xq;
+        // piece k of row m goes to chunk k/16, offset (k%16)*16 of the padded row
+        auto put_piece = [&](int i, uint4 v) {
+            const int m = i / (2 * nb), k = i - m * 2 * nb;
+            *reinterpret_cast<uint4*>(smem + m * rowb + (k >> 4) * ACT_CHUNK_STRIDE + (k & 15) * 16) = v;
+        };
+        auto put_words = [&](int i, uint32_t da, uint32_t ca, uint32_t s16) {
+            const int m = i / nb, b = i - m * nb;
+            uint32_t* dd = reinterpret_cast<uint32_t*>(smem + m * rowb + C * ACT_CHUNK_STRIDE);
+            dd[b] = da;
+            dd[nb + b] = ca;
+            dd[2 * nb + b] = s16;
+        };
 #pragma unroll
-        for (int m = 0; m < B; m++) {
-            uint8_t* base = smem + m * rowb;
-            const uint4* src = reinterpret_cast<const uint4*>(xq + J.rcodes + m * K);
-            for (int i = threadIdx.x; i < nb * 2; i += blockDim.x)  // 16-byte pieces
-                *reinterpret_cast<uint4*>(base + (i >> 4) * ACT_CHUNK_STRIDE + (i & 15) * 16) = src[i];
-            const float* sda = reinterpret_cast<const float*>(xq + J.rda) + m * nb;
-            const float* sca = reinterpret_cast<const float*>(xq + J.rca) + m * nb;
-            const int32_t* ss = reinterpret_cast<const int32_t*>(xq + J.rs16) + m * nb;
-            float* dda = const_cast<float*>(A[m].da);
-            for (int i = threadIdx.x; i < nb; i += blockDim.x) {
-                dda[i] = sda[i];
-                dda[nb + i] = sca[i];
-                reinterpret_cast<int32_t*>(dda + 2 * nb)[i] = ss[i];
-            }
+        for (int uu = 0; uu < SP; uu++) {
+            const int i = threadIdx.x + uu * blockDim.x;
+            if (i < npc) put_piece(i, pc[uu]);
         }
+#pragma unroll
+        for (int uu = 0; uu < SW; uu++) {
+            const int i = threadIdx.x + uu * blockDim.x;
+            if (i < nwd) put_words(i, pw[uu][0], pw[uu][1], pw[uu][2]);
+        }
+        // the rest (long rows): load and store
+        for (int i = threadIdx.x + SP * blockDim.x; i < npc; i += blockDim.x) {
+            const int m = i / (2 * nb), k = i - m * 2 * nb;
+            put_piece(i, reinterpret_cast<const uint4*>(xq + J.rcodes + (int64_t)m * K)[k]);
+        }
+        for (int i = threadIdx.x + SW * blockDim.x; i < nwd; i += blockDim.x)
+            put_words(i, reinterpret_cast<const uint32_t*>(xq + J.rda)[i],
+                      reinterpret_cast<const uint32_t*>(xq + J.rca)[i],
+                      reinterpret_cast<const uint32_t*>(xq + J.rs16)[i]);
     }
     __syncthreads();
     if (!active) return;
