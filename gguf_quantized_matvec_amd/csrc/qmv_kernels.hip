@@ -941,9 +941,7 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
         }
     };
 
-    // first chunk in flight while the activations are staged (FUSED: issued
-    // right after the first activation loads, so that those, which complete
-    // in issue order, need not wait for the weights)
+    // first chunk in flight while the activations are staged
     uint32_t r[NWD];
     // non-fused: the first pass of the activation copy is loaded into
     // registers and stored to LDS after the weights are issued.  A long copy
@@ -995,6 +993,12 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
         uint8_t* xq = J.xq;
         const int total = 4 * B * nb;  // (block, quarter) tasks; whole blocks stay in one pass
         constexpr int UNR = 2;         // passes whose x loads are issued together
+        // a long activation is loaded ahead of the weights (loads complete in
+        // issue order), a short one behind them; formats with long chunks
+        // (Q8_0, Q6_K) always load the weights first, which keeps the chunk
+        // registers free during the quantisation
+        const bool x_first = NWD <= 40 && total > 256;
+        if (!x_first) issue(0, r);
         for (int pass = 0; pass == 0 || (int)threadIdx.x + pass * UNR * (int)blockDim.x < total; pass++) {
           const int i0 = threadIdx.x + pass * UNR * blockDim.x;
           float4 xf[UNR][2];
@@ -1009,7 +1013,7 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
               xf[uu][1] = xb[1];
             }
           }
-          if (pass == 0) issue(0, r);  // every lane takes pass 0
+          if (pass == 0 && x_first) issue(0, r);  // every lane takes pass 0
 #pragma unroll
           for (int uu = 0; uu < UNR; uu++) {
             const int i = i0 + uu * blockDim.x;
@@ -1302,7 +1306,15 @@ int launch_rebuild(uint8_t* xq, int64_t rows, int64_t K, int staging, hipStream_
 
 int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                int64_t rows, float* y, hipStream_t s) {
-    if (use_dot(rows, K)) {  // quantisation fused into the kernel when x is given
+    if (use_dot(rows, K)) {
+        // quantisation fused into the kernel when x is given, unless the
+        // workgroups' re-reads of x would exceed the weight bytes: then one
+        // quantise launch first
+        if (x && dot_blocks(type, N, K) * rows * K * 4 > N * row_bytes(type, K)) {
+            const int rc = launch_quantize(x, xq, rows, K, ST_ROW, s);
+            if (rc) return rc;
+            x = nullptr;
+        }
         const GemvDesc d{w, N, K, x, xq, y};
         return launch_dot(type, &d, 1, rows, s);
     }

@@ -98,9 +98,11 @@ int quantize_act_q8_0(const float* x, void* xq, int64_t rows, int64_t K, void* s
 /* Decode GEMV (MatVec): y[B][N] = x[B][K] * W^T for 1 <= B <= 16.
  * If x is non-NULL it is quantised into xq first, leaving xq exactly as
  * quantize_act_q8_0 would (for B <= 4 the quantisation runs inside the GEMV
- * kernel, one launch); if x is NULL, xq must already hold a complete
- * quantize_act_q8_0 result for these B rows and K, which is used as is (so
- * several matrices can share one quantisation).  xq: qmv_act_bytes(B, K) bytes, 16-byte aligned.  Decode is
+ * kernel, one launch, unless the kernel's workgroups would between them read
+ * x more bytes than the weights hold; then it is a launch of its own); if x
+ * is NULL, xq must already hold a complete quantize_act_q8_0 result for
+ * these B rows and K, which is used as is (so several matrices can share one
+ * quantisation).  xq: qmv_act_bytes(B, K) bytes, 16-byte aligned.  Decode is
  * memory-bound ("Architecture", bench transcript), so every weight byte is
  * read once per call whatever B is ("A request, end to end": a batch reads
  * the weights once rather than once per sequence). */

@@ -286,3 +286,20 @@ def test_group_equals_single_launches(g, fmt, shapes, B):
     ys2 = g.matvec_group(fmt, staged)
     for k in range(len(shapes)):
         assert_bitwise(host(ys2[k]), ref[k], f"staged group entry {k}")
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0, synth.Q4_K, synth.Q6_K])
+@pytest.mark.parametrize("fused", [False, True])
+def test_large_gemv_persistent(g, fmt, fused):
+    """Batch 1 over 24613 rows (more than 6144 work units of 4 rows: the
+    persistent, double-buffered schedule), ragged last unit, against the
+    documented f32 order."""
+    N, K = 24613, 4096
+    blob, x = _inputs(fmt, N, K, 1, 950 + fmt)
+    w = dev(blob)
+    xq = oracle.quantize_act(x)
+    if fused:
+        y = host(g.matvec(fmt, w, N, K, x=dev(x)))
+    else:
+        y = host(g.matvec(fmt, w, N, K, xq=g.quantize(dev(x)), B=1))
+    assert_bitwise(y, oracle.matmul_canon_f32(fmt, blob, N, K, xq, 1), "large gemv vs f32 order")
