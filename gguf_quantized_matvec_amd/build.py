@@ -11,12 +11,15 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmv.so")
-SOURCES = [os.path.join(CSRC, "qmv_kernels.hip"), os.path.join(CSRC, "qmm_kernels.hip"),
-           os.path.join(CSRC, "qmv_api.cpp")]
+# (source, extra flags): the GEMV kernels take MFMA results straight into
+# VGPRs (no accumulation-register copies); the GEMM keeps the default choice
+SOURCES = [(os.path.join(CSRC, "qmv_kernels.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+           (os.path.join(CSRC, "qmm_kernels.hip"), []),
+           (os.path.join(CSRC, "qmv_api.cpp"), [])]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # exact f32 arithmetic: no contraction of a*b+c, correctly rounded divide
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     # no packed-fp32 VALU instructions anywhere in the device code
@@ -25,13 +28,23 @@ FLAGS = [
 ]
 
 
-def build() -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-x", "hip", *SOURCES, "-o", tmp]
+def _run(cmd: list) -> None:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libqmv.so")
+
+
+def build() -> str:
+    objs = []
+    for src, extra in SOURCES:
+        obj = os.path.join(CSRC, os.path.basename(src) + ".o")
+        _run([HIPCC, *FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj])
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", *objs, "-o", tmp])
+    for obj in objs:
+        os.remove(obj)
     os.replace(tmp, LIB)
     return LIB
 

@@ -235,7 +235,6 @@ __device__ __forceinline__ void tile_of(int64_t wg, int64_t tilesM, int64_t tile
 // ra[b][r] = (d_a, 0, ..., 0) for activation row r (row TM is all zero, for
 // the lanes that hold k = 8..15), rw[b][r] = d_w in all 8 halves.
 struct Smem {
-    uint4 a[NA][TM * PR];  // activation codes (f16), a ring of NA steps
     uint4 w[TN * PR];      // decoded weights (f16)
     uint4 ra[SB][TM + 1];  // rank-1 A operands (fp16 d_a at k = 0)
     uint4 rw[SB][TN];      // rank-1 B operands (fp16 d_w broadcast)
@@ -244,14 +243,27 @@ struct Smem {
 };
 __device__ __forceinline__ int slot(int row, int q) { return row * PR + (q ^ (row & 15)); }
 
+// The activation ring (f16 codes of NA = 2 steps) lives in two separate LDS
+// objects: while the next step is copied into one by global_load_lds, the
+// multiply reads the other, and the compiler, seeing two objects, does not
+// make those reads wait for the copy in flight (with one object it must).
+__shared__ uint4 lds_a0[TM * PR];
+__shared__ uint4 lds_a1[TM * PR];
+__shared__ Smem lds_rest;
+template <int P> __device__ __forceinline__ uint4* a_buf() {
+    if constexpr (P == 0) return lds_a0;
+    else return lds_a1;
+}
+using Even = std::integral_constant<int, 0>;
+using Odd = std::integral_constant<int, 1>;
+
 template <int FMT>
 __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int64_t N, int64_t K,
                                               const uint8_t* __restrict__ xq, ActLayout L,
                                               int64_t M, int64_t tilesM, int64_t tilesN,
                                               float* __restrict__ y) {
     using F = GFmt<FMT>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
-    Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+    Smem* const sm = &lds_rest;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wm = wv & 1, wn = wv >> 1;
     int64_t tm, tn;
@@ -269,7 +281,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
     const uint16_t* ahda = reinterpret_cast<const uint16_t*>(xq + L.hda) + am * nb;
     const float* arca = reinterpret_cast<const float*>(xq + L.rca) + am * nb;
     const uint8_t* wrow = w + wr * R;
-    if (tid < SB) sm.ra[tid][TM] = make_uint4(0, 0, 0, 0);
+    if (tid < SB) sm->ra[tid][TM] = make_uint4(0, 0, 0, 0);
 
     // activation tile by global_load_lds: each wave instruction fills 64
     // consecutive slots = 4 tile rows; wave wv fills rows 16wv .. 16wv + 15;
@@ -283,7 +295,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
         const int64_t arow = m0 + row < M ? m0 + row : M - 1;
         asrc[i] = xq + L.hcodes + (arow * K + 8 * piece) * 2;
     }
-    auto issue_a = [&](int h, int buf) {
+    auto issue_a = [&](int h, auto par) {
         const bool ragged = SB * h + SB > nb;  // uniform: only the last step of a ragged K
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -295,7 +307,8 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
                 const int blk = SB * h + (piece >> 2);
                 if (blk >= nb) src -= (int64_t)(blk - (nb - 1)) * 64;
             }
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)&sm.a[buf][(16 * wv + 4 * i) * PR], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                src, (lds_void*)(a_buf<decltype(par)::value>() + (16 * wv + 4 * i) * PR), 16, 0, 0);
         }
     };
 
@@ -331,7 +344,9 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
     // 4*bk + 2hh + kq holds k = 16hh + 8kq .. +8 of block bk
     const int arow0 = 64 * wm + lr, brow = 32 * wn + lr;
 
-    auto step = [&](int h, Raw& r) {
+    // step h reads activation buffer P = h % 2 and fills the other
+    auto step = [&](int h, Raw& r, auto par) {
+        constexpr int P = decltype(par)::value;
         const int nbh = min(SB, nb - SB * h);
         bool odd_big = false;
         if constexpr (FMT == T_Q6_K) {
@@ -351,21 +366,21 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
             if (!r.have) f.d = 0;
 #pragma unroll
             for (int q = 0; q < 4; q++)
-                sm.w[slot(sr, 4 * sk + q)] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+                sm->w[slot(sr, 4 * sk + q)] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
             const uint32_t dd = f.d | (f.d << 16);
-            sm.rw[sk][sr] = make_uint4(dd, dd, dd, dd);
-            sm.ra[sk][sr] = make_uint4(r.da, 0, 0, 0);
-            if (FMT == T_Q4_K) sm.ca[sk][sr] = r.ca;
-            if (FMT == T_Q4_K || FMT == T_Q6_K) sm.x1[sk][sr] = f.x1;
+            sm->rw[sk][sr] = make_uint4(dd, dd, dd, dd);
+            sm->ra[sk][sr] = make_uint4(r.da, 0, 0, 0);
+            if (FMT == T_Q4_K) sm->ca[sk][sr] = r.ca;
+            if (FMT == T_Q4_K || FMT == T_Q6_K) sm->x1[sk][sr] = f.x1;
         }
         // B2: the W tile is staged; this wave's activation loads of step h
         // completed before its weight loads of step h were consumed above
         __syncthreads();
         if (h + 1 < H) {
-            issue_a(h + 1, (h + 1) % NA);  // in flight while step h is multiplied
+            issue_a(h + 1, std::integral_constant<int, 1 - P>{});  // in flight while step h is multiplied
             fetch(h + 1, r);
         }
-        const uint4* A = sm.a[h % NA];
+        const uint4* A = a_buf<P>();
         // the multiply of one step; UNF: Q6_K codes were staged without their
         // sub-scales (a scale that cannot be folded exactly occurs in the step)
         auto multiply = [&](auto unf_tag) {
@@ -381,18 +396,18 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
                             const uint4 va = A[slot(arow0 + 32 * i, 4 * bk + 2 * hh + kq)];
                             __builtin_memcpy(&Af[i][hh], &va, 16);
                         }
-                        const uint4 vb = sm.w[slot(brow, 4 * bk + 2 * hh + kq)];
+                        const uint4 vb = sm->w[slot(brow, 4 * bk + 2 * hh + kq)];
                         __builtin_memcpy(&Bf[hh], &vb, 16);
                     }
                     {
-                        const uint4 r0 = sm.ra[bk][kq ? TM : arow0];
-                        const uint4 r1 = sm.ra[bk][kq ? TM : arow0 + 32];
-                        const uint4 rb = sm.rw[bk][brow];
+                        const uint4 r0 = sm->ra[bk][kq ? TM : arow0];
+                        const uint4 r1 = sm->ra[bk][kq ? TM : arow0 + 32];
+                        const uint4 rb = sm->rw[bk][brow];
                         __builtin_memcpy(&Ra[0], &r0, 16);
                         __builtin_memcpy(&Ra[1], &r1, 16);
                         __builtin_memcpy(&Rw, &rb, 16);
                     }
-                    const uint32_t x1 = (FMT == T_Q4_K || FMT == T_Q6_K) ? sm.x1[bk][brow] : 0u;
+                    const uint32_t x1 = (FMT == T_Q4_K || FMT == T_Q6_K) ? sm->x1[bk][brow] : 0u;
 #pragma unroll
                     for (int i = 0; i < 2; i++) {
                         const v16f S = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ra[i], Rw, zero16, 0, 0, 0);
@@ -413,7 +428,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
                             if constexpr (FMT == T_Q4_K) {
                                 // element e of the lane is row 8(e/4) + 4kq + e%4 of the tile
                                 const float nX = -__uint_as_float(x1);
-                                const float* cr = &sm.ca[bk][64 * wm + 32 * i + 4 * kq];
+                                const float* cr = &sm->ca[bk][64 * wm + 32 * i + 4 * kq];
 #pragma unroll
                                 for (int g = 0; g < 4; g++) {
                                     const float4 c4 = *reinterpret_cast<const float4*>(cr + 8 * g);
@@ -445,9 +460,12 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
     };
 
     Raw r;
-    issue_a(0, 0);
+    issue_a(0, Even{});
     fetch(0, r);
-    for (int h = 0; h < H; h++) step(h, r);
+    for (int h = 0; h < H; h += 2) {
+        step(h, r, Even{});
+        if (h + 1 < H) step(h + 1, r, Odd{});
+    }
 
     // lane l, element e of tile i: row 8(e/4) + 4kq + e%4, column lr
     const int64_t n = n0 + 32 * wn + lr;
@@ -465,15 +483,7 @@ int launch_gemm_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int
                   float* y, hipStream_t s) {
     const ActLayout L = act_layout(M, K);
     const int64_t tilesM = (M + TM - 1) / TM, tilesN = (N + TN - 1) / TN;
-    static bool attr_set = false;  // more than the default 64 KB of LDS
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<FMT>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)sizeof(Smem));
-        if (e != hipSuccess) return (int)e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL((k_gemm<FMT>), dim3((unsigned)(tilesM * tilesN)), dim3(512), sizeof(Smem),
+    hipLaunchKernelGGL((k_gemm<FMT>), dim3((unsigned)(tilesM * tilesN)), dim3(512), 0,
                        s, w, N, K, xq, L, M, tilesM, tilesN, y);
     return (int)hipGetLastError();
 }

@@ -212,6 +212,7 @@ template <> struct Fmt<T_Q6_K> { static constexpr int QK = 256, BB = 210, CB = 2
 
 template <int FMT> constexpr int span_stride() { return 16 * Fmt<FMT>::PPS + 16; }
 template <int FMT> constexpr int F_QK() { return Fmt<FMT>::QK; }
+template <int FMT> constexpr int F_BB() { return Fmt<FMT>::BB; }
 template <int FMT> constexpr int pieces_per_lane() { return (16 * Fmt<FMT>::PPS + 63) / 64; }
 
 // ------------------------------------------------------- weight stream ----
@@ -242,11 +243,27 @@ __device__ __forceinline__ TileRef make_tile(const uint8_t* w, int64_t wbytes, i
 // it belongs to span p/PPS at offset 16*(p%PPS).  Pieces past a span's end
 // are not loaded.  Only the last tile of a blob takes the guarded path, which
 // reads its final partial piece bytewise instead of running past the blob.
+// The two paths are separate loops: interleaved per piece, the merge after
+// each piece makes the compiler wait for every load already issued before it
+// may write the next piece's register, leaving one piece in flight per lane.
 template <int FMT>
 __device__ __forceinline__ void fetch_chunk(const TileRef& t, uint32_t R, int c, int nbc,
                                             int lane, uint4 (&reg)[pieces_per_lane<FMT>()]) {
     using F = Fmt<FMT>;
     const uint32_t len = F::QK == 32 ? nbc * F::BB : F::BB;
+    if (t.fast) {
+#pragma unroll
+        for (int k = 0; k < pieces_per_lane<FMT>(); k++) {
+            const int p = k * 64 + lane;
+            const int n = p / F::PPS, j = p - n * F::PPS;
+            const uint32_t s = n * R + c * F::CB;
+            const uint32_t off = (s & ~15u) + 16 * j;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (n < 16 && off < s + len) v = *reinterpret_cast<const uint4*>(t.base + off);
+            reg[k] = v;
+        }
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < pieces_per_lane<FMT>(); k++) {
         const int p = k * 64 + lane;
@@ -254,9 +271,7 @@ __device__ __forceinline__ void fetch_chunk(const TileRef& t, uint32_t R, int c,
         const uint32_t s = n * R + c * F::CB;
         const uint32_t off = (s & ~15u) + 16 * j;
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (t.fast) {
-            if (n < 16 && off < s + len) v = *reinterpret_cast<const uint4*>(t.base + off);
-        } else if (n < t.nrows && off < s + len) {
+        if (n < t.nrows && off < s + len) {
             if (off + 16 <= t.left) {
                 v = *reinterpret_cast<const uint4*>(t.base + off);
             } else {
@@ -356,17 +371,73 @@ template <int FMT, int NI, bool PARTIALS>
 __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, const long (&acur)[8],
                                            int c, int nbc, int kg, float (&p)[NI],
                                            const PartialsOut& po) {
+    // All LDS reads of the chunk are issued first (the lane's weight bytes of
+    // every block and its rows' activation scales), so the wave pays one LDS
+    // round trip per chunk rather than one per block.  Blocks past nbc read
+    // bytes inside the wave's slice that are never used.
+    uint64_t q[8];       // per block (Q8_0, Q4_0); per 32-byte quarter (Q4_K, Q6_K ql)
+    uint16_t dq[8];      // per-block fp16 d (Q8_0, Q4_0)
+    uint64_t qh[2];      // Q6_K high bits, per 128-element half
+    uint4 hdr;           // Q4_K: d, dmin, 12 scale bytes; Q6_K: the 16 sub-scales
+    uint16_t d6 = 0;     // Q6_K d
+    if (FMT == T_Q8_0 || FMT == T_Q4_0) {
+#pragma unroll
+        for (int bb = 0; bb < 8; bb++) {
+            const uint8_t* blk = rb + F_BB<FMT>() * bb;
+            dq[bb] = ld<uint16_t>(blk);
+            q[bb] = FMT == T_Q8_0 ? ld<uint64_t>(blk + 2 + 8 * kg)
+                                  : ld<uint64_t>(blk + 2 + 8 * (kg & 1)) >> (2 * (kg & 2));
+        }
+    } else if (FMT == T_Q4_K) {
+        hdr = ld<uint4>(rb);
+#pragma unroll
+        for (int j = 0; j < 4; j++) q[j] = ld<uint64_t>(rb + 16 + 32 * j + 8 * kg);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) q[j] = ld<uint64_t>(rb + 32 * j + 8 * kg);
+        qh[0] = ld<uint64_t>(rb + 128 + 8 * kg);
+        qh[1] = ld<uint64_t>(rb + 160 + 8 * kg);
+        hdr = ld<uint4>(rb + 192);
+        d6 = ld<uint16_t>(rb + 208);
+    }
+    float dav[8][4], cav[8][4];
+    if (!PARTIALS) {
+#pragma unroll
+        for (int bb = 0; bb < 8; bb++) {
+            const float* sp = sl + bb * 16 + 4 * kg;
+#pragma unroll
+            for (int i = 0; i < 4; i++) dav[bb][i] = cav[bb][i] = 0.0f;
+            if (NI == 1) {
+                dav[bb][0] = sp[0];
+                if (FMT == T_Q4_K) cav[bb][0] = sp[128];
+            } else if (NI == 2) {
+                const float2 d2 = *reinterpret_cast<const float2*>(sp);
+                dav[bb][0] = d2.x; dav[bb][1] = d2.y;
+                if (FMT == T_Q4_K) {
+                    const float2 c2 = *reinterpret_cast<const float2*>(sp + 128);
+                    cav[bb][0] = c2.x; cav[bb][1] = c2.y;
+                }
+            } else {
+                const float4 d4 = *reinterpret_cast<const float4*>(sp);
+                dav[bb][0] = d4.x; dav[bb][1] = d4.y; dav[bb][2] = d4.z; dav[bb][3] = d4.w;
+                if (FMT == T_Q4_K) {
+                    const float4 c4 = *reinterpret_cast<const float4*>(sp + 128);
+                    cav[bb][0] = c4.x; cav[bb][1] = c4.y; cav[bb][2] = c4.z; cav[bb][3] = c4.w;
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     // per-chunk fields of the K-quant superblock
     float dw = 0.0f, dmw = 0.0f;
-    uint32_t s12[3] = {0, 0, 0};
+    uint32_t s12[3] = {hdr.y, hdr.z, hdr.w};
     if (FMT == T_Q4_K) {
-        dw = half_bits_to_float(ld<uint16_t>(rb));
-        dmw = half_bits_to_float(ld<uint16_t>(rb + 2));
-        s12[0] = ld<uint32_t>(rb + 4);
-        s12[1] = ld<uint32_t>(rb + 8);
-        s12[2] = ld<uint32_t>(rb + 12);
+        dw = half_bits_to_float((uint16_t)(hdr.x & 0xFFFF));
+        dmw = half_bits_to_float((uint16_t)(hdr.x >> 16));
     }
-    if (FMT == T_Q6_K) dw = half_bits_to_float(ld<uint16_t>(rb + 208));
+    if (FMT == T_Q6_K) dw = half_bits_to_float(d6);
+    const uint32_t sc6[4] = {hdr.x, hdr.y, hdr.z, hdr.w};
 #pragma unroll
     for (int i = 0; i < NI; i++) p[i] = 0.0f;
 
@@ -375,18 +446,18 @@ __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, c
         if (F_QK<FMT>() == 32 && bb >= nbc) break;
         const long a = acur[bb];
         const v4i zero = {0, 0, 0, 0};
-        v4i I;  // exact integer partial of (row 4kg+i, this lane's weight row)
+        // Exact integer partial of (row 4kg+i, this lane's weight row).  The
+        // K-quant sub-scale products use the full-rate 24-bit multiply: the
+        // MFMA sums (|.| < 2^16) and the 6- or 8-bit scales fit its operands.
+        v4i I;
         int mn = 0;
         if (FMT == T_Q8_0) {
-            const uint8_t* blk = rb + 34 * bb;
-            dw = half_bits_to_float(ld<uint16_t>(blk));
-            I = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, ld<long>(blk + 2 + 8 * kg), zero, 0, 0, 0);
+            dw = half_bits_to_float(dq[bb]);
+            I = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, (long)q[bb], zero, 0, 0, 0);
         } else if (FMT == T_Q4_0) {
-            const uint8_t* blk = rb + 18 * bb;
-            dw = half_bits_to_float(ld<uint16_t>(blk));
-            uint64_t raw = ld<uint64_t>(blk + 2 + 8 * (kg & 1));
-            if (kg & 2) raw >>= 4;
-            const uint64_t wc = bytes_minus(raw & 0x0F0F0F0F0F0F0F0Full, 0x0808080808080808ull);
+            dw = half_bits_to_float(dq[bb]);
+            // lanes kg = 2, 3 took the high nibbles (one per-lane shift above)
+            const uint64_t wc = bytes_minus(q[bb] & 0x0F0F0F0F0F0F0F0Full, 0x0808080808080808ull);
             I = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, (long)wc, zero, 0, 0, 0);
         } else if (FMT == T_Q4_K) {
             // 6-bit scale and min of sub-block bb (two per 12 bytes)
@@ -399,26 +470,28 @@ __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, c
                 sc = (sb[bb + 4] & 15) | ((sb[bb - 4] >> 6) << 4);
                 mn = (sb[bb + 4] >> 4) | ((sb[bb] >> 6) << 4);
             }
-            uint64_t raw = ld<uint64_t>(rb + 16 + 32 * (bb >> 1) + 8 * kg);
+            uint64_t raw = q[bb >> 1];
             if (bb & 1) raw >>= 4;
             const v4i acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(
                 a, (long)(raw & 0x0F0F0F0F0F0F0F0Full), zero, 0, 0, 0);
-            I = sc * acc;
+#pragma unroll
+            for (int i = 0; i < 4; i++) I[i] = __mul24(sc, acc[i]);
         } else {  // Q6_K
             const int h = bb >> 2, kq = bb & 3;
-            uint64_t ql = ld<uint64_t>(rb + 64 * h + 32 * (kq & 1) + 8 * kg);
-            const uint64_t qh = ld<uint64_t>(rb + 128 + 32 * h + 8 * kg);
+            uint64_t ql = q[2 * h + (kq & 1)];
             if (kq & 2) ql >>= 4;
             const uint64_t q6 = (ql & 0x0F0F0F0F0F0F0F0Full) |
-                                (((qh >> (2 * kq)) & 0x0303030303030303ull) << 4);
+                                (((qh[h] >> (2 * kq)) & 0x0303030303030303ull) << 4);
             const uint64_t wc = bytes_minus(q6, 0x2020202020202020ull);
-            const int s0 = (int8_t)rb[192 + 2 * bb], s1 = (int8_t)rb[192 + 2 * bb + 1];
+            const uint32_t sw = sc6[bb >> 1] >> (16 * (bb & 1));
+            const int s0 = (int8_t)(sw & 0xFF), s1 = (int8_t)((sw >> 8) & 0xFF);
             // the two 16-element halves carry different sub-scales: one MFMA
             // per half, the other half's codes zeroed
             const long lo = kg < 2 ? (long)wc : 0, hi = kg < 2 ? 0 : (long)wc;
             const v4i acc0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, lo, zero, 0, 0, 0);
             const v4i acc1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, hi, zero, 0, 0, 0);
-            I = s0 * acc0 + s1 * acc1;
+#pragma unroll
+            for (int i = 0; i < 4; i++) I[i] = __mul24(s0, acc0[i]) + __mul24(s1, acc1[i]);
         }
 
         if (PARTIALS) {
@@ -440,31 +513,11 @@ __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, c
                 }
             }
         } else {
-            float dav[4], cav[4] = {0.f, 0.f, 0.f, 0.f};
-            const float* sp = sl + bb * 16 + 4 * kg;
-            if (NI == 1) {
-                dav[0] = sp[0];
-                if (FMT == T_Q4_K) cav[0] = sp[128];
-            } else if (NI == 2) {
-                const float2 d2 = *reinterpret_cast<const float2*>(sp);
-                dav[0] = d2.x; dav[1] = d2.y;
-                if (FMT == T_Q4_K) {
-                    const float2 c2 = *reinterpret_cast<const float2*>(sp + 128);
-                    cav[0] = c2.x; cav[1] = c2.y;
-                }
-            } else {
-                const float4 d4 = *reinterpret_cast<const float4*>(sp);
-                dav[0] = d4.x; dav[1] = d4.y; dav[2] = d4.z; dav[3] = d4.w;
-                if (FMT == T_Q4_K) {
-                    const float4 c4 = *reinterpret_cast<const float4*>(sp + 128);
-                    cav[0] = c4.x; cav[1] = c4.y; cav[2] = c4.z; cav[3] = c4.w;
-                }
-            }
             const float cw = FMT == T_Q4_K ? dmw * (float)mn : 0.0f;
 #pragma unroll
             for (int i = 0; i < NI; i++) {
-                p[i] = fmaf((float)I[i], dw * dav[i], p[i]);
-                if (FMT == T_Q4_K) p[i] = fmaf(-cw, cav[i], p[i]);
+                p[i] = fmaf((float)I[i], dw * dav[bb][i], p[i]);
+                if (FMT == T_Q4_K) p[i] = fmaf(-cw, cav[bb][i], p[i]);
             }
         }
     }
