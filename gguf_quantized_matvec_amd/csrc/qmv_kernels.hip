@@ -814,50 +814,55 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                                           const ActRow (&A)[B], int c, int nbc, float (&p)[B]) {
 #pragma unroll
     for (int m = 0; m < B; m++) p[m] = 0.0f;
+    // 32-element formats: the blocks of a short last chunk (bb >= nbc) are
+    // computed too and their terms dropped by a select, so that the block
+    // loop has no branch (nbc differs between lanes) and the LDS reads of
+    // later blocks can be issued ahead.  Their activation bytes lie in the
+    // chunk's padding and the following row fields, inside the staged copy.
     if constexpr (FMT == T_Q8_0) {
         static_for<8>([&](auto BB) {
             constexpr int bb = BB;
-            if (bb < nbc) {
-                const int b = 8 * c + bb;
-                const float dw = half_bits_to_float(half_at<34 * bb>(r));
-                uint32_t w[8];
-                static_for<8>([&](auto I) { w[I] = dw_at<34 * bb + 2 + 4 * I>(r); });
+            const bool on = bb < nbc;
+            const int b = 8 * c + bb;
+            const float dw = half_bits_to_float(half_at<34 * bb>(r));
+            uint32_t w[8];
+            static_for<8>([&](auto I) { w[I] = dw_at<34 * bb + 2 + 4 * I>(r); });
 #pragma unroll
-                for (int m = 0; m < B; m++) {
-                    uint32_t a[8];
-                    act_block(A[m], b, a);
-                    int D = 0;
+            for (int m = 0; m < B; m++) {
+                uint32_t a[8];
+                act_block(A[m], b, a);
+                int D = 0;
 #pragma unroll
-                    for (int i = 0; i < 8; i++) D = dot4(w[i], a[i], D);
-                    p[m] = fmaf((float)D, dw * A[m].da[b], p[m]);
-                }
+                for (int i = 0; i < 8; i++) D = dot4(w[i], a[i], D);
+                const float t = fmaf((float)D, dw * A[m].da[b], p[m]);
+                p[m] = on ? t : p[m];
             }
         });
     } else if constexpr (FMT == T_Q4_0) {
         static_for<8>([&](auto BB) {
             constexpr int bb = BB;
-            if (bb < nbc) {
-                const int b = 8 * c + bb;
-                const float dw = half_bits_to_float(half_at<18 * bb>(r));
-                uint32_t lo[4], hi[4];
-                static_for<4>([&](auto I) {
-                    const uint32_t q = dw_at<18 * bb + 2 + 4 * I>(r);
-                    lo[I] = q & 0x0F0F0F0Fu;
-                    hi[I] = (q >> 4) & 0x0F0F0F0Fu;
-                });
+            const bool on = bb < nbc;
+            const int b = 8 * c + bb;
+            const float dw = half_bits_to_float(half_at<18 * bb>(r));
+            uint32_t lo[4], hi[4];
+            static_for<4>([&](auto I) {
+                const uint32_t q = dw_at<18 * bb + 2 + 4 * I>(r);
+                lo[I] = q & 0x0F0F0F0Fu;
+                hi[I] = (q >> 4) & 0x0F0F0F0Fu;
+            });
 #pragma unroll
-                for (int m = 0; m < B; m++) {
-                    uint32_t a[8];
-                    act_block(A[m], b, a);
-                    int D = 0;
+            for (int m = 0; m < B; m++) {
+                uint32_t a[8];
+                act_block(A[m], b, a);
+                int D = 0;
 #pragma unroll
-                    for (int i = 0; i < 4; i++) D = dot4(lo[i], a[i], D);
+                for (int i = 0; i < 4; i++) D = dot4(lo[i], a[i], D);
 #pragma unroll
-                    for (int i = 0; i < 4; i++) D = dot4(hi[i], a[4 + i], D);
-                    const int s16 = A[m].s16[b];
-                    const int S = (int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16);
-                    p[m] = fmaf((float)(D - 8 * S), dw * A[m].da[b], p[m]);
-                }
+                for (int i = 0; i < 4; i++) D = dot4(hi[i], a[4 + i], D);
+                const int s16 = A[m].s16[b];
+                const int S = (int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16);
+                const float t = fmaf((float)(D - 8 * S), dw * A[m].da[b], p[m]);
+                p[m] = on ? t : p[m];
             }
         });
     } else if constexpr (FMT == T_Q4_K) {
