@@ -14,9 +14,9 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqmv.so")
 
-Q4_0, Q8_0, Q4_K, Q6_K = 2, 8, 12, 14
-TYPES = {"Q4_0": Q4_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
-BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210)}
+Q4_0, Q5_0, Q8_0, Q4_K, Q6_K = 2, 6, 8, 12, 14
+TYPES = {"Q4_0": Q4_0, "Q5_0": Q5_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
+BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_K: (256, 144), Q6_K: (256, 210)}
 EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
            "qmv_partials_launch", "qmv_strerror")
 MAX_BATCH = 16

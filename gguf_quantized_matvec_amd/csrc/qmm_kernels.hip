@@ -42,7 +42,7 @@
 namespace qmv {
 namespace {
 
-constexpr int T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14;
+constexpr int T_Q4_0 = 2, T_Q5_0 = 6, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14;
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -57,6 +57,7 @@ constexpr int NA = 2;               // activation steps resident in LDS (1 in fl
 template <int FMT> struct GFmt;
 template <> struct GFmt<T_Q8_0> { static constexpr int QK = 32, BB = 34; };
 template <> struct GFmt<T_Q4_0> { static constexpr int QK = 32, BB = 18; };
+template <> struct GFmt<T_Q5_0> { static constexpr int QK = 32, BB = 22; };
 template <> struct GFmt<T_Q4_K> { static constexpr int QK = 256, BB = 144; };
 template <> struct GFmt<T_Q6_K> { static constexpr int QK = 256, BB = 210; };
 
@@ -72,13 +73,14 @@ __device__ __forceinline__ _Float16 h_of_bits(uint32_t b) {
 template <int FMT> struct WRaw;
 template <> struct WRaw<T_Q8_0> { uint32_t v[9]; };    // 34 B
 template <> struct WRaw<T_Q4_0> { uint32_t v[5]; };    // 18 B
+template <> struct WRaw<T_Q5_0> { uint32_t v[6]; };    // 22 B
 template <> struct WRaw<T_Q4_K> { uint32_t hdr[4]; uint32_t q[8]; };   // d, dmin, sc12; 32 B of qs
 template <> struct WRaw<T_Q6_K> { uint32_t ql[8]; uint32_t qh[8]; uint32_t sd; };  // s pair | d << 16
 
 // Block b (< nb) of a weight row.
 template <int FMT>
 __device__ __forceinline__ void fetch_w(const uint8_t* row, int b, WRaw<FMT>& r) {
-    if constexpr (FMT == T_Q8_0 || FMT == T_Q4_0) {
+    if constexpr (FMT == T_Q8_0 || FMT == T_Q4_0 || FMT == T_Q5_0) {
         __builtin_memcpy(r.v, row + (int64_t)b * GFmt<FMT>::BB, GFmt<FMT>::BB);
     } else if constexpr (FMT == T_Q4_K) {
         const uint8_t* sb = row + (int64_t)144 * (b >> 3);
@@ -159,6 +161,22 @@ __device__ __forceinline__ void decode_w(const WRaw<FMT>& r, int b, uint32_t (&o
             __builtin_memcpy(&q, blk + 2 + 4 * i, 4);
             bytes_to_f16(q & 0x0F0F0F0Fu, 8.0f, o[2 * i], o[2 * i + 1]);                // 0..15
             bytes_to_f16((q >> 4) & 0x0F0F0F0Fu, 8.0f, o[8 + 2 * i], o[8 + 2 * i + 1]);  // 16..31
+        }
+    } else if constexpr (FMT == T_Q5_0) {
+        const uint8_t* blk = reinterpret_cast<const uint8_t*>(r.v);
+        s.d = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8);
+        uint32_t h;
+        __builtin_memcpy(&h, blk + 2, 4);
+        // fifth bit j of the block -> bit 4 of code j (see spread4)
+        auto spread4 = [](uint32_t v) { return (__umul24(v, 0x204081u) & 0x01010101u) << 4; };
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint32_t q;
+            __builtin_memcpy(&q, blk + 6 + 4 * i, 4);
+            const uint32_t lo = (q & 0x0F0F0F0Fu) | spread4((h >> (4 * i)) & 15u);
+            const uint32_t hi = ((q >> 4) & 0x0F0F0F0Fu) | spread4((h >> (16 + 4 * i)) & 15u);
+            bytes_to_f16(lo, 16.0f, o[2 * i], o[2 * i + 1]);            // 0..15
+            bytes_to_f16(hi, 16.0f, o[8 + 2 * i], o[8 + 2 * i + 1]);    // 16..31
         }
     } else if constexpr (FMT == T_Q4_K) {
         const int j = b & 7;  // sub-block
@@ -495,6 +513,7 @@ int launch_gemm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t*
     switch (type) {
     case T_Q8_0: return launch_gemm_t<T_Q8_0>(w, N, K, xq, M, y, s);
     case T_Q4_0: return launch_gemm_t<T_Q4_0>(w, N, K, xq, M, y, s);
+    case T_Q5_0: return launch_gemm_t<T_Q5_0>(w, N, K, xq, M, y, s);
     case T_Q4_K: return launch_gemm_t<T_Q4_K>(w, N, K, xq, M, y, s);
     case T_Q6_K: return launch_gemm_t<T_Q6_K>(w, N, K, xq, M, y, s);
     }

@@ -65,6 +65,7 @@ struct GemvDesc {
 inline int64_t row_bytes(int type, int64_t K) {
     switch (type) {
     case 2: return K / 32 * 18;     // Q4_0
+    case 6: return K / 32 * 22;     // Q5_0
     case 8: return K / 32 * 34;     // Q8_0
     case 12: return K / 256 * 144;  // Q4_K
     case 14: return K / 256 * 210;  // Q6_K

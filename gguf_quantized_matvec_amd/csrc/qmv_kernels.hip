@@ -31,7 +31,7 @@
 namespace qmv {
 namespace {
 
-constexpr int T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14;
+constexpr int T_Q4_0 = 2, T_Q5_0 = 6, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14;
 
 // Batch sizes up to this run on the lane-per-chunk v_dot4 kernel, larger ones on MFMA.
 constexpr int DOT_MAX_ROWS = 4;
@@ -207,6 +207,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x,
 template <int FMT> struct Fmt;
 template <> struct Fmt<T_Q8_0> { static constexpr int QK = 32, BB = 34, CB = 272, PPS = 18; };
 template <> struct Fmt<T_Q4_0> { static constexpr int QK = 32, BB = 18, CB = 144, PPS = 10; };
+template <> struct Fmt<T_Q5_0> { static constexpr int QK = 32, BB = 22, CB = 176, PPS = 12; };
 template <> struct Fmt<T_Q4_K> { static constexpr int QK = 256, BB = 144, CB = 144, PPS = 9; };
 template <> struct Fmt<T_Q6_K> { static constexpr int QK = 256, BB = 210, CB = 210, PPS = 14; };
 
@@ -304,6 +305,13 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Q5_0 fifth bits: the 4 bits of h (0..15) moved to bit 4 of bytes 0..3.
+// h * 0x204081 places copies of h at bits 0, 7, 14 and 21 with no carries,
+// so bit 8j of the product is bit j of h.
+__device__ __forceinline__ uint32_t spread4(uint32_t h) {
+    return (__umul24(h, 0x204081u) & 0x01010101u) << 4;
+}
+
 // Bytewise x - bias for bytes x in [0, 2*bias): add 128, subtract, flip bit 7
 // (no borrow crosses a byte because every byte of x|0x80.. is >= 128).
 __device__ __forceinline__ uint64_t bytes_minus(uint64_t x, uint64_t bias8) {
@@ -378,15 +386,22 @@ __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, c
     uint64_t q[8];       // per block (Q8_0, Q4_0); per 32-byte quarter (Q4_K, Q6_K ql)
     uint16_t dq[8];      // per-block fp16 d (Q8_0, Q4_0)
     uint64_t qh[2];      // Q6_K high bits, per 128-element half
+    uint32_t h5[8];      // Q5_0: the block's fifth bits, the lane's 8 in the low byte
     uint4 hdr;           // Q4_K: d, dmin, 12 scale bytes; Q6_K: the 16 sub-scales
     uint16_t d6 = 0;     // Q6_K d
-    if (FMT == T_Q8_0 || FMT == T_Q4_0) {
+    if (FMT == T_Q8_0 || FMT == T_Q4_0 || FMT == T_Q5_0) {
 #pragma unroll
         for (int bb = 0; bb < 8; bb++) {
             const uint8_t* blk = rb + F_BB<FMT>() * bb;
             dq[bb] = ld<uint16_t>(blk);
-            q[bb] = FMT == T_Q8_0 ? ld<uint64_t>(blk + 2 + 8 * kg)
-                                  : ld<uint64_t>(blk + 2 + 8 * (kg & 1)) >> (2 * (kg & 2));
+            if (FMT == T_Q8_0) {
+                q[bb] = ld<uint64_t>(blk + 2 + 8 * kg);
+            } else {
+                // lanes kg = 2, 3 take the high nibbles: one per-lane shift
+                const int qs = FMT == T_Q5_0 ? 6 : 2;
+                q[bb] = ld<uint64_t>(blk + qs + 8 * (kg & 1)) >> (2 * (kg & 2));
+            }
+            if (FMT == T_Q5_0) h5[bb] = ld<uint32_t>(blk + 2) >> (8 * kg);
         }
     } else if (FMT == T_Q4_K) {
         hdr = ld<uint4>(rb);
@@ -456,8 +471,12 @@ __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, c
             I = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, (long)q[bb], zero, 0, 0, 0);
         } else if (FMT == T_Q4_0) {
             dw = half_bits_to_float(dq[bb]);
-            // lanes kg = 2, 3 took the high nibbles (one per-lane shift above)
             const uint64_t wc = bytes_minus(q[bb] & 0x0F0F0F0F0F0F0F0Full, 0x0808080808080808ull);
+            I = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, (long)wc, zero, 0, 0, 0);
+        } else if (FMT == T_Q5_0) {
+            dw = half_bits_to_float(dq[bb]);
+            const uint64_t b5 = ((uint64_t)spread4((h5[bb] >> 4) & 15u) << 32) | spread4(h5[bb] & 15u);
+            const uint64_t wc = bytes_minus((q[bb] & 0x0F0F0F0F0F0F0F0Full) | b5, 0x1010101010101010ull);
             I = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, (long)wc, zero, 0, 0, 0);
         } else if (FMT == T_Q4_K) {
             // 6-bit scale and min of sub-block bb (two per 12 bytes)
@@ -747,6 +766,7 @@ template <int FMT> struct DotFmt;
 // NWD = ceil(CB/4) dwords after the shift, plus the one the shift reads from.
 template <> struct DotFmt<T_Q8_0> { static constexpr int NWD = 69; };  // 272 B: 68 + 1
 template <> struct DotFmt<T_Q4_0> { static constexpr int NWD = 37; };  // 144 B: 36 + 1
+template <> struct DotFmt<T_Q5_0> { static constexpr int NWD = 45; };  // 176 B: 44 + 1
 template <> struct DotFmt<T_Q4_K> { static constexpr int NWD = 36; };  // 144 B, aligned
 template <> struct DotFmt<T_Q6_K> { static constexpr int NWD = 54; };  // 210 B: 53 + 1
 
@@ -862,6 +882,34 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                 const int s16 = A[m].s16[b];
                 const int S = (int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16);
                 const float t = fmaf((float)(D - 8 * S), dw * A[m].da[b], p[m]);
+                p[m] = on ? t : p[m];
+            }
+        });
+    } else if constexpr (FMT == T_Q5_0) {
+        static_for<8>([&](auto BB) {
+            constexpr int bb = BB;
+            const bool on = bb < nbc;
+            const int b = 8 * c + bb;
+            const float dw = half_bits_to_float(half_at<22 * bb>(r));
+            const uint32_t h = dw_at<22 * bb + 2>(r);
+            uint32_t lo[4], hi[4];
+            static_for<4>([&](auto I) {
+                const uint32_t q = dw_at<22 * bb + 6 + 4 * I>(r);
+                lo[I] = (q & 0x0F0F0F0Fu) | spread4((h >> (4 * I)) & 15u);
+                hi[I] = ((q >> 4) & 0x0F0F0F0Fu) | spread4((h >> (16 + 4 * I)) & 15u);
+            });
+#pragma unroll
+            for (int m = 0; m < B; m++) {
+                uint32_t a[8];
+                act_block(A[m], b, a);
+                int D = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) D = dot4(lo[i], a[i], D);
+#pragma unroll
+                for (int i = 0; i < 4; i++) D = dot4(hi[i], a[4 + i], D);
+                const int s16 = A[m].s16[b];
+                const int S = (int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16);
+                const float t = fmaf((float)(D - 16 * S), dw * A[m].da[b], p[m]);
                 p[m] = on ? t : p[m];
             }
         });
@@ -1277,6 +1325,7 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
     switch (type) {
     case T_Q8_0: return launch_dot_rows<T_Q8_0>(jobs, rows, fused, blocks, shmem, s);
     case T_Q4_0: return launch_dot_rows<T_Q4_0>(jobs, rows, fused, blocks, shmem, s);
+    case T_Q5_0: return launch_dot_rows<T_Q5_0>(jobs, rows, fused, blocks, shmem, s);
     case T_Q4_K: return launch_dot_rows<T_Q4_K>(jobs, rows, fused, blocks, shmem, s);
     case T_Q6_K: return launch_dot_rows<T_Q6_K>(jobs, rows, fused, blocks, shmem, s);
     }
@@ -1384,6 +1433,7 @@ int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
     switch (type) {
     case T_Q8_0: return launch_qmv_t<T_Q8_0>(w, N, K, xq, rows, y, nullptr, s, false);
     case T_Q4_0: return launch_qmv_t<T_Q4_0>(w, N, K, xq, rows, y, nullptr, s, false);
+    case T_Q5_0: return launch_qmv_t<T_Q5_0>(w, N, K, xq, rows, y, nullptr, s, false);
     case T_Q4_K: return launch_qmv_t<T_Q4_K>(w, N, K, xq, rows, y, nullptr, s, false);
     case T_Q6_K: return launch_qmv_t<T_Q6_K>(w, N, K, xq, rows, y, nullptr, s, false);
     }
@@ -1412,6 +1462,7 @@ int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* x
     switch (type) {
     case T_Q8_0: return launch_qmv_ni<T_Q8_0, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     case T_Q4_0: return launch_qmv_ni<T_Q4_0, 4>(w, N, K, xq, rows, nullptr, P, s, true);
+    case T_Q5_0: return launch_qmv_ni<T_Q5_0, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     case T_Q4_K: return launch_qmv_ni<T_Q4_K, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     case T_Q6_K: return launch_qmv_ni<T_Q6_K, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     }

@@ -15,8 +15,9 @@
  *     Y[m][n] = sum over 32-blocks b of  d_w(n,b) * d_a(m,b) * I(m,n,b)
  *
  * with I the exact integer dot product of the block's weight codes and
- * activation codes (Q4_0 codes offset by -8, Q6_K codes by -32 and weighted by
- * the 16-element sub-scale; Q4_K contributes d*sc_j*sum(q*a) - dmin*m_j*sum(a)).
+ * activation codes (Q4_0 codes offset by -8, Q5_0 codes by -16, Q6_K codes by
+ * -32 and weighted by the 16-element sub-scale; Q4_K contributes
+ * d*sc_j*sum(q*a) - dmin*m_j*sum(a)).
  *
  * Floating-point order (fixed, identical for every entry point, batch size
  * and launch shape, so that every row of a batched or prefill call is
@@ -33,8 +34,12 @@
  *
  * Weight layout.  Row n of W occupies bytes [n*R, (n+1)*R) of w, R =
  * (K/QK)*block_bytes: Q8_0 (type 8) 32 elements / 34 bytes, Q4_0 (type 2)
- * 32 / 18, Q4_K (type 12) 256 / 144, Q6_K (type 14) 256 / 210 — a GGUF 2-D
- * tensor with K (ne0) contiguous.  Blocks need not be aligned; w itself must
+ * 32 / 18, Q5_0 (type 6) 32 / 22, Q4_K (type 12) 256 / 144, Q6_K (type 14)
+ * 256 / 210 — a GGUF 2-D tensor with K (ne0) contiguous.  The formats are
+ * the ones the pages list ("Models and formats", section "Tensor formats");
+ * the byte layouts are the GGUF block structures, which the pages do not
+ * print.  Q5_0 is the format of most matrices in the pages' own Qwen2.5-0.5B
+ * file (the tensor histogram of its info transcript).  Blocks need not be aligned; w itself must
  * be 16-byte aligned.  X and Y are dense row-major f32.
  *
  * Ownership.  The caller owns and allocates every buffer (device memory).
@@ -59,11 +64,11 @@ extern "C" {
 #endif
 
 /* GGUF tensor type ids. */
-enum qmv_type { QMV_Q4_0 = 2, QMV_Q8_0 = 8, QMV_Q4_K = 12, QMV_Q6_K = 14 };
+enum qmv_type { QMV_Q4_0 = 2, QMV_Q5_0 = 6, QMV_Q8_0 = 8, QMV_Q4_K = 12, QMV_Q6_K = 14 };
 
 enum qmv_status {
     QMV_OK = 0,
-    QMV_EINVAL_TYPE = -1,        /* type is not Q4_0, Q8_0, Q4_K or Q6_K */
+    QMV_EINVAL_TYPE = -1,        /* type is not Q4_0, Q5_0, Q8_0, Q4_K or Q6_K */
     QMV_EINVAL_SHAPE = -2,       /* N, K, rows or batch out of range */
     QMV_EINVAL_PTR = -3,         /* NULL or misaligned pointer */
     QMV_ELAUNCH = -4,            /* the HIP launch failed */

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-Q4_0, Q8_0, Q4_K, Q6_K = 2, 8, 12, 14
+Q4_0, Q5_0, Q8_0, Q4_K, Q6_K = 2, 6, 8, 12, 14
 
 
 def build(force: bool = True) -> str:
@@ -68,7 +68,7 @@ def _ok(rc, what):
         raise ValueError(f"{what} failed with code {rc}")
 
 
-QK = {Q8_0: 32, Q4_0: 32, Q4_K: 256, Q6_K: 256}
+QK = {Q8_0: 32, Q4_0: 32, Q5_0: 32, Q4_K: 256, Q6_K: 256}
 
 
 def half_to_double(h: int) -> float:

@@ -17,7 +17,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14 };
+enum { T_Q4_0 = 2, T_Q5_0 = 6, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14 };
 
 /* ---------------------------------------------------------------- fp16 -- */
 
@@ -54,6 +54,9 @@ uint16_t oracle_float_to_half(float f) {
 }
 
 static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static uint32_t rd32(const uint8_t* p) {
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
 
 /* ------------------------------------------------------- layouts ------- */
 
@@ -61,6 +64,7 @@ static int block_shape(int type, int* qk, int* nbytes) {
     switch (type) {
     case T_Q8_0: *qk = 32;  *nbytes = 34;  return 0;
     case T_Q4_0: *qk = 32;  *nbytes = 18;  return 0;
+    case T_Q5_0: *qk = 32;  *nbytes = 22;  return 0;
     case T_Q4_K: *qk = 256; *nbytes = 144; return 0;
     case T_Q6_K: *qk = 256; *nbytes = 210; return 0;
     default: return -1;
@@ -100,6 +104,15 @@ static void decode_elem(int type, const uint8_t* blk, int e, int* q, int* sc, in
         *q = e < 16 ? (byte & 15) : (byte >> 4);
         break;
     }
+    case T_Q5_0: {
+        /* d (2 bytes), then the 32 fifth bits as one LE u32, then the low
+         * nibbles packed as in Q4_0 */
+        uint8_t byte = blk[6 + (e & 15)];
+        int low4 = e < 16 ? (byte & 15) : (byte >> 4);
+        int bit5 = (int)((rd32(blk + 2) >> e) & 1u);
+        *q = low4 | (bit5 << 4);
+        break;
+    }
     case T_Q4_K: {
         int c = e / 64, r = e % 64;
         uint8_t byte = blk[16 + 32 * c + (r & 31)];
@@ -131,12 +144,14 @@ static void block_scales(int type, const uint8_t* blk, double* d, double* dmin) 
 /* The integer weight factor that multiplies the activation code, and the
  * integer that multiplies dmin (Q4_K only):
  *   value = d * wint  (Q8_0, Q4_0, Q6_K)      value = d*wint - dmin*mint (Q4_K)
- * Q8_0: wint = q;  Q4_0: q-8;  Q6_K: s_j*(q-32);  Q4_K: wint = sc_j*q, mint = m_j. */
+ * Q8_0: wint = q;  Q4_0: q-8;  Q5_0: q-16;  Q6_K: s_j*(q-32);
+ * Q4_K: wint = sc_j*q, mint = m_j. */
 static void elem_ints(int type, int q, int sc, int mn, int64_t* wint, int64_t* mint) {
     *mint = 0;
     switch (type) {
     case T_Q8_0: *wint = q; break;
     case T_Q4_0: *wint = q - 8; break;
+    case T_Q5_0: *wint = q - 16; break;
     case T_Q6_K: *wint = (int64_t)sc * (q - 32); break;
     case T_Q4_K: *wint = (int64_t)sc * q; *mint = mn; break;
     }
@@ -171,6 +186,7 @@ static double elem_value(int type, int q, int sc, int mn, double d, double dmin)
     switch (type) {
     case T_Q8_0: return d * q;
     case T_Q4_0: return d * (q - 8);
+    case T_Q5_0: return d * (q - 16);
     case T_Q4_K: return d * sc * q - dmin * mn;
     case T_Q6_K: return d * sc * (q - 32);
     }

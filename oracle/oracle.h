@@ -17,7 +17,7 @@
  * quantisation in f32 (it decides integer codes, so it takes the kernel's
  * precision), integer partials in int64, and results in f64.
  *
- * Type ids are the GGUF ones: Q4_0 = 2, Q8_0 = 8, Q4_K = 12, Q6_K = 14.
+ * Type ids are the GGUF ones: Q4_0 = 2, Q5_0 = 6, Q8_0 = 8, Q4_K = 12, Q6_K = 14.
  * All functions return 0 on success and a negative value on a bad argument
  * (-1 unknown type, -2 bad shape, -3 a partial does not fit in int32).
  */
@@ -38,7 +38,7 @@ uint16_t oracle_float_to_half(float f);
 int oracle_quantize_act(const float* x, int64_t rows, int64_t K, uint8_t* out);
 
 /* Field-by-field unpack of an N x K weight blob.  Per element: the stored code
- * q[N*K] (Q8_0 signed, Q4_0/Q4_K 0..15, Q6_K 0..63), its sub-block scale
+ * q[N*K] (Q8_0 signed, Q4_0/Q4_K 0..15, Q5_0 0..31, Q6_K 0..63), its sub-block scale
  * sub_scale[N*K] (Q4_K sc_j, Q6_K s_j, else 1) and min sub_min[N*K] (Q4_K m_j,
  * else 0).  Per block of QK elements: d[N*K/QK] and dmin[N*K/QK] (Q4_K only,
  * else 0).  Any output pointer may be NULL. */
@@ -52,7 +52,8 @@ int oracle_dequant(int type, const uint8_t* w, int64_t N, int64_t K, double* out
 int oracle_dequant_act(const uint8_t* xq, int64_t rows, int64_t K, double* out);
 
 /* Exact integer partial per (m, n, 32-element block b), layout [B][N][K/32]:
- *   Q8_0: sum w*a     Q4_0: sum (q-8)*a     Q6_K: sum s_j*(q-32)*a
+ *   Q8_0: sum w*a     Q4_0: sum (q-8)*a     Q5_0: sum (q-16)*a
+ *   Q6_K: sum s_j*(q-32)*a
  *   Q4_K: two integers per block, layout [B][N][K/32][2]:
  *         P = sum sc_j*q*a  and  Q = sum m_j*a                              */
 int oracle_partials(int type, const uint8_t* w, int64_t N, int64_t K,

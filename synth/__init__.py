@@ -14,6 +14,9 @@ the byte layouts below are the published GGUF ones:
   Q4_0  32 elems, 18 B : d f16 | qs u8[16]                e<16: lo nibble of qs[e];
                                                           e>=16: hi nibble of qs[e-16];
                                                           value d*(q-8)
+  Q5_0  32 elems, 22 B : d f16 | qh u32 | qs u8[16]       low 4 bits as Q4_0; bit 4 of
+                                                          q is bit e of qh (LE u32);
+                                                          value d*(q-16)
   Q4_K 256 elems, 144 B: d f16 | dmin f16 | sc12 u8[12] | qs u8[128]
                          element e: c=e//64, r=e%64, byte qs[32c + r%32],
                          lo nibble if r<32 else hi nibble; sub-block j=e//32;
@@ -29,11 +32,11 @@ from __future__ import annotations
 import numpy as np
 
 # GGUF tensor type ids (public GGUF enumeration).
-Q4_0, Q8_0, Q4_K, Q6_K = 2, 8, 12, 14
-FORMATS = {"Q4_0": Q4_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
+Q4_0, Q5_0, Q8_0, Q4_K, Q6_K = 2, 6, 8, 12, 14
+FORMATS = {"Q4_0": Q4_0, "Q5_0": Q5_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
 NAMES = {v: k for k, v in FORMATS.items()}
 # (elements per block, bytes per block)
-BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210)}
+BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_K: (256, 144), Q6_K: (256, 210)}
 
 
 def row_bytes(fmt: int, K: int) -> int:
@@ -70,6 +73,9 @@ def draw_fields(fmt: int, N: int, K: int, seed: int, dscale: float = 0.01,
     elif fmt == Q4_0:
         f["d"] = _f16_scales(rng, (N, nb), dscale)
         f["q"] = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    elif fmt == Q5_0:
+        f["d"] = _f16_scales(rng, (N, nb), dscale)
+        f["q"] = rng.integers(0, 32, size=(N, K), dtype=np.uint8)
     elif fmt == Q4_K:
         f["d"] = _f16_scales(rng, (N, nb), dscale)
         f["dmin"] = _f16_scales(rng, (N, nb), dscale)
@@ -104,6 +110,14 @@ def encode(f: dict) -> np.ndarray:
         q = f["q"].reshape(N, nb, 32)
         out[:, :, 0:2] = _f16_bytes(f["d"])
         out[:, :, 2:18] = q[:, :, :16] | (q[:, :, 16:] << 4)
+    elif fmt == Q5_0:
+        q = f["q"].reshape(N, nb, 32)
+        out[:, :, 0:2] = _f16_bytes(f["d"])
+        bits = (q >> 4).astype(np.uint32) << np.arange(32, dtype=np.uint32)
+        qh = np.bitwise_or.reduce(bits, axis=2)
+        out[:, :, 2:6] = qh.astype("<u4").view(np.uint8).reshape(N, nb, 4)
+        lo = q & 15
+        out[:, :, 6:22] = lo[:, :, :16] | (lo[:, :, 16:] << 4)
     elif fmt == Q4_K:
         sc, m = f["sc"], f["m"]
         out[:, :, 0:2] = _f16_bytes(f["d"])
@@ -159,6 +173,11 @@ WORKLOADS = {
     "8b_class": dict(mats=[(Q4_K, 4096, 4096, 0.02), (Q4_K, 1024, 4096, 0.02),
                            (Q4_K, 14336, 4096, 0.02), (Q6_K, 4096, 14336, 0.02)],
                      batches=[1, 16, 2048]),
+    # the pages' Qwen2.5-0.5B file holds 132 Q5_0 tensors (histogram only);
+    # taken here as its 2-D shapes other than ffn_down: gate/up 4864x896,
+    # attention q/o 896x896, k/v 128x896 (an inference)
+    "q5_0_qwen": dict(mats=[(Q5_0, 4864, 896, 0.02), (Q5_0, 896, 896, 0.02),
+                            (Q5_0, 128, 896, 0.02)], batches=[1, 16, 512]),
 }
 
 

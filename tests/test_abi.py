@@ -44,6 +44,9 @@ FAKE = 1 << 20  # a 16-byte aligned non-NULL address; never dereferenced
 
 @pytest.mark.parametrize("args,code", [
     ((3, FAKE, 16, 32, FAKE, 1, FAKE, FAKE), -1),            # unknown type
+    ((7, FAKE, 16, 32, FAKE, 1, FAKE, FAKE), -1),            # Q5_1: not (yet) accepted
+    ((g.Q5_0, FAKE, 16, 48, FAKE, 1, FAKE, FAKE), -2),       # Q5_0 accepted: K % 32
+    ((g.Q5_0, FAKE + 8, 16, 32, FAKE, 1, FAKE, FAKE), -3),   # Q5_0 accepted: w misaligned
     ((g.Q8_0, FAKE, 16, 48, FAKE, 1, FAKE, FAKE), -2),       # K % 32
     ((g.Q4_K, FAKE, 16, 896, FAKE, 1, FAKE, FAKE), -2),      # K-quant K % 256
     ((g.Q6_K, FAKE, 16, 4864 + 32, FAKE, 1, FAKE, FAKE), -2),
@@ -93,7 +96,7 @@ def test_group_refusals():
 
 
 def test_strerror_names_what_works():
-    assert "Q4_0" in g.strerror(-1) and "Q6_K" in g.strerror(-1)
+    assert "Q4_0" in g.strerror(-1) and "Q6_K" in g.strerror(-1) and "Q5_0" in g.strerror(-1)
     assert "K % 256" in g.strerror(-2) and "qmm_launch" in g.strerror(-2)
     assert "gfx950" in g.strerror(-5)
     assert g.strerror(0) == "ok" and "unknown" in g.strerror(-99)

@@ -16,14 +16,14 @@ import oracle
 import synth
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden", "weight_blocks.json")
-FMTS = [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K]
+FMTS = [synth.Q8_0, synth.Q4_0, synth.Q5_0, synth.Q4_K, synth.Q6_K]
 
 
 def _golden():
     return json.load(open(GOLD))["blocks"]
 
 
-@pytest.mark.parametrize("name", ["Q8_0", "Q4_0", "Q4_K", "Q6_K"])
+@pytest.mark.parametrize("name", ["Q8_0", "Q4_0", "Q5_0", "Q4_K", "Q6_K"])
 def test_hand_assembled_block(name):
     g = _golden()[name]
     blk = np.zeros(g["nbytes"], np.uint8)
@@ -92,7 +92,8 @@ def test_roundtrip_exhaustive_codes_and_subscales(fmt):
     qk = synth.BLOCK[fmt][0]
     K = qk * 2
     f = synth.draw_fields(fmt, 1, K, 0)
-    rng_codes = {synth.Q8_0: 256, synth.Q4_0: 16, synth.Q4_K: 16, synth.Q6_K: 64}[fmt]
+    rng_codes = {synth.Q8_0: 256, synth.Q4_0: 16, synth.Q5_0: 32, synth.Q4_K: 16,
+                 synth.Q6_K: 64}[fmt]
     N = max(rng_codes, 64 if fmt == synth.Q4_K else 1, 256 if fmt == synth.Q6_K else 1)
     f = synth.draw_fields(fmt, N, K, 3)
     n = np.arange(N)[:, None]
@@ -118,7 +119,7 @@ def test_roundtrip_exhaustive_codes_and_subscales(fmt):
 def test_one_hot_element_position(fmt):
     """A single non-neutral code lands on exactly its own element."""
     qk = synth.BLOCK[fmt][0]
-    neutral = {synth.Q8_0: 0, synth.Q4_0: 8, synth.Q4_K: 0, synth.Q6_K: 32}[fmt]
+    neutral = {synth.Q8_0: 0, synth.Q4_0: 8, synth.Q5_0: 16, synth.Q4_K: 0, synth.Q6_K: 32}[fmt]
     for e in [0, 1, 15, 16, 31, qk - 1] + ([32, 63, 64, 127, 128, 200] if qk == 256 else []):
         f = synth.draw_fields(fmt, 1, qk, 5)
         f["q"][:] = neutral
@@ -145,6 +146,8 @@ def test_dequant_matches_element_formulas(fmt):
         want = d * q
     elif fmt == synth.Q4_0:
         want = d * (q - 8)
+    elif fmt == synth.Q5_0:
+        want = d * (q - 16)
     elif fmt == synth.Q4_K:
         sc = np.repeat(f["sc"].reshape(N, -1), 32, axis=1)
         mm = np.repeat(f["m"].reshape(N, -1), 32, axis=1)

@@ -21,7 +21,7 @@ import oracle
 import synth
 from checks import assert_bitwise, assert_tol, tol_violations
 
-FMTS = [synth.Q8_0, synth.Q4_0, synth.Q4_K, synth.Q6_K]
+FMTS = [synth.Q8_0, synth.Q4_0, synth.Q5_0, synth.Q4_K, synth.Q6_K]
 
 
 def _acts(xq, B, K):
@@ -49,6 +49,8 @@ def _wint_mint(f):
         wint = q
     elif fmt == synth.Q4_0:
         wint = q - 8
+    elif fmt == synth.Q5_0:
+        wint = q - 16
     elif fmt == synth.Q4_K:
         wint = np.repeat(f["sc"].reshape(N, -1), 32, axis=1).astype(np.int64) * q
         mint = np.repeat(f["m"].reshape(N, -1), 32, axis=1).astype(np.int64)
@@ -130,11 +132,13 @@ def test_hand_worked_q8_0_product():
     assert oracle.partials(synth.Q8_0, blk, 1, 32, xq, 1)[0, 0, 0] == -32260
 
 
-@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q4_K, synth.Q6_K])
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q5_0, synth.Q4_K, synth.Q6_K])
 def test_zero_point_rows_give_exact_zero(fmt):
     blob, f, x, xq, N, K, B = _case(fmt, N=2, nblk=2, B=2, seed=8)
     if fmt == synth.Q4_0:
         f["q"][:] = 8
+    elif fmt == synth.Q5_0:
+        f["q"][:] = 16
     elif fmt == synth.Q6_K:
         f["q"][:] = 32
     else:
@@ -218,8 +222,8 @@ def _canon_exact(fmt, blob, N, K, xq, B):
     return y
 
 
-@pytest.mark.parametrize("fmt,nblk", [(synth.Q8_0, 20), (synth.Q4_0, 9), (synth.Q4_K, 2),
-                                      (synth.Q6_K, 2)])
+@pytest.mark.parametrize("fmt,nblk", [(synth.Q8_0, 20), (synth.Q4_0, 9), (synth.Q5_0, 11),
+                                      (synth.Q4_K, 2), (synth.Q6_K, 2)])
 def test_canon_f32_against_exact_rational_emulation(fmt, nblk):
     blob, f, x, xq, N, K, B = _case(fmt, N=3, nblk=nblk, B=2, seed=31)
     got = oracle.matmul_canon_f32(fmt, blob, N, K, xq, B)
