@@ -988,12 +988,16 @@ struct DotJob {
     uint8_t* xq;      // staged quantisation; FUSED: written by the job's first workgroup (may be NULL)
     int64_t N, K, wbytes;
     int64_t rcodes, rda, rca, rs16;  // offsets of the row-major staging in xq
-    int first_block;                 // the job's first workgroup in the grid
 };
 constexpr int MAX_JOBS = 8;
+// The first workgroups of all jobs come first, so that a workgroup of a group
+// finds its job with one scalar load and compares, then loads that job's
+// fields once: every dependent kernel-argument load (about half a
+// microsecond each, measured) sits at the head of every wave's critical path.
 struct DotJobs {
-    DotJob j[MAX_JOBS];
+    int first[MAX_JOBS];  // job k owns workgroups [first[k], first[k+1])
     int count;
+    DotJob j[MAX_JOBS];
 };
 
 // Work units: C <= 64 chunks per row: a unit is G = 64/LPR rows (LPR = lanes
@@ -1003,16 +1007,27 @@ struct DotJobs {
 // chunk straight into registers, issued before the activations are staged.
 // Chunk sums are added in chunk order per row through a small LDS buffer,
 // and each row's result is stored once, at the end.
-template <int FMT, int B, bool FUSED>
+template <int FMT, int B, bool FUSED, bool SINGLE>
 __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
     using F = Fmt<FMT>;
     constexpr int NWD = DotFmt<FMT>::NWD;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    // this workgroup's job (compile-time indices: the table stays in scalar registers)
-    DotJob J = jobs.j[0];
+    // this workgroup's job: a single GEMV reads its fields directly (one
+    // round trip); a group finds its job in the table head, then loads it
+    DotJob J;
+    int first_block = 0;
+    if constexpr (SINGLE) {
+        J = jobs.j[0];
+    } else {
+        int job = 0;
 #pragma unroll
-    for (int k = 1; k < MAX_JOBS; k++)
-        if (k < jobs.count && (int)blockIdx.x >= jobs.j[k].first_block) J = jobs.j[k];
+        for (int k = 1; k < MAX_JOBS; k++) {
+            const bool mine = k < jobs.count && (int)blockIdx.x >= jobs.first[k];
+            job = mine ? k : job;
+            first_block = mine ? jobs.first[k] : first_block;
+        }
+        J = jobs.j[job];
+    }
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int64_t N = J.N, K = J.K;
     const int nb = (int)(K >> 5), C = (nb + 7) >> 3;
@@ -1020,16 +1035,16 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
     float (*pbuf)[64] = reinterpret_cast<float (*)[64]>(smem + B * rowb + wv * B * 256);
 
     const int64_t R = (K / F::QK) * F::BB;
-    int LPR = 1;
-    while (LPR < C && LPR < 64) LPR <<= 1;
-    const int G = 64 / LPR;
+    int lg = 0;  // LPR = 2^lg lanes per row, G = 64 / LPR rows per unit
+    while ((1 << lg) < C && lg < 6) lg++;
+    const int LPR = 1 << lg, G = 64 >> lg;
     const int PR = (C + 63) >> 6;  // passes (1 unless C > 64)
-    const int64_t units = C <= 64 ? (N + G - 1) / G : N;
-    const int64_t u = (int64_t)((int)blockIdx.x - J.first_block) * 4 + wv;
+    const int64_t units = C <= 64 ? (N + G - 1) >> (6 - lg) : N;
+    const int64_t u = (int64_t)((int)blockIdx.x - first_block) * 4 + wv;
     const bool active = u < units;
 
     auto chunk_of = [&](int q, int64_t& row, int& c) {
-        row = C <= 64 ? u * G + lane / LPR : u;
+        row = C <= 64 ? u * G + (lane >> lg) : u;
         c = C <= 64 ? (lane & (LPR - 1)) : 64 * q + lane;
     };
     auto issue = [&](int q, uint32_t (&r)[NWD]) {
@@ -1094,7 +1109,7 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
     if constexpr (FUSED) {
         // four lanes per block, 8 elements each: the block's amax and code
         // sums by lane shuffles, then the same d, id and codes as k_quantize
-        const bool writer = (int)blockIdx.x == J.first_block && J.xq != nullptr;
+        const bool writer = (int)blockIdx.x == first_block && J.xq != nullptr;
         const float* x = J.x;
         uint8_t* xq = J.xq;
         const int total = 4 * B * nb;  // (block, quarter) tasks; whole blocks stay in one pass
@@ -1237,7 +1252,7 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
         for (int j = 0; j < B; j++) {
             const int t = lane + 64 * j;
             if (t < G * B) {
-                const int m = t / G, rl = t - m * G;
+                const int m = t >> (6 - lg), rl = t & (G - 1);
                 for (int k = 0; k < cnt; k++) yacc[j] = yacc[j] + pbuf[m][rl * LPR + k];
             }
         }
@@ -1247,7 +1262,7 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
     for (int j = 0; j < B; j++) {
         const int t = lane + 64 * j;
         if (t < G * B) {
-            const int m = t / G, rl = t - m * G;
+            const int m = t >> (6 - lg), rl = t & (G - 1);
             const int64_t orow = C <= 64 ? u * G + rl : u;
             if (orow < N) J.y[m * N + orow] = yacc[j];
         }
@@ -1267,16 +1282,23 @@ inline int64_t dot_blocks(int type, int64_t N, int64_t K) {
 
 inline size_t dot_shmem(int B, int64_t K) { return (size_t)B * act_lds_row_bytes(K) + 4 * B * 256; }
 
-template <int FMT, int B, bool FUSED>
-int launch_dot_jobs(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
+template <int FMT, int B, bool FUSED, bool SINGLE>
+int launch_dot_kernel(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
     static bool attr_set = false;  // allow up to the full 160 KB of LDS
     if (!attr_set) {
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED, SINGLE>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_dot<FMT, B, FUSED>), dim3((unsigned)blocks), dim3(256), shmem, s, jobs);
+    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, SINGLE>), dim3((unsigned)blocks), dim3(256), shmem,
+                       s, jobs);
     return (int)hipGetLastError();
+}
+
+template <int FMT, int B, bool FUSED>
+int launch_dot_jobs(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
+    return jobs.count == 1 ? launch_dot_kernel<FMT, B, FUSED, true>(jobs, blocks, shmem, s)
+                           : launch_dot_kernel<FMT, B, FUSED, false>(jobs, blocks, shmem, s);
 }
 
 template <int FMT>
@@ -1316,7 +1338,7 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
         J.rda = L.rda;
         J.rca = L.rca;
         J.rs16 = L.rs16;
-        J.first_block = (int)blocks;
+        jobs.first[k] = (int)blocks;
         blocks += dot_blocks(type, d[k].N, d[k].K);
         const size_t sh = dot_shmem((int)rows, d[k].K);
         shmem = sh > shmem ? sh : shmem;
