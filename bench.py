@@ -351,6 +351,11 @@ def main():
         return GraphSteps(torch, step, n)
 
     graphs["full"] = make(W["R"])
+    # capture the partial-replay graphs too before anything is timed
+    for n in (args.warmup, args.steps):
+        r = n % W["R"]
+        if r and r not in graphs:
+            graphs[r] = make(r)
     run_steps(graphs, make, args.warmup)
     torch.cuda.synchronize()
 
