@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-Q4_0, Q5_0, Q8_0, Q4_K, Q6_K = 2, 6, 8, 12, 14
+Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q8_1, Q4_K, Q6_K = 2, 3, 6, 7, 8, 9, 12, 14
 
 
 def build(force: bool = True) -> str:
@@ -68,7 +68,7 @@ def _ok(rc, what):
         raise ValueError(f"{what} failed with code {rc}")
 
 
-QK = {Q8_0: 32, Q4_0: 32, Q5_0: 32, Q4_K: 256, Q6_K: 256}
+QK = {Q8_0: 32, Q4_0: 32, Q5_0: 32, Q4_1: 32, Q5_1: 32, Q8_1: 32, Q4_K: 256, Q6_K: 256}
 
 
 def half_to_double(h: int) -> float:
@@ -117,10 +117,10 @@ def dequant_act(xq: np.ndarray, rows: int, K: int) -> np.ndarray:
 
 
 def partials(fmt: int, blob, N: int, K: int, xq, B: int) -> np.ndarray:
-    """[B, N, K/32] int32 (Q4_K: [B, N, K/32, 2])."""
+    """[B, N, K/32] int32 (Q4_K, Q4_1, Q5_1: [B, N, K/32, 2])."""
     blob = np.ascontiguousarray(blob, dtype=np.uint8)
     xq = np.ascontiguousarray(xq, dtype=np.uint8)
-    per = 2 if fmt == Q4_K else 1
+    per = 2 if fmt in (Q4_K, Q4_1, Q5_1) else 1
     P = np.zeros(B * N * (K // 32) * per, np.int32)
     _ok(lib().oracle_partials(fmt, _p(blob), N, K, _p(xq), B, _p(P)), "partials")
     return P.reshape((B, N, K // 32, 2) if per == 2 else (B, N, K // 32))

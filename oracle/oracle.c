@@ -17,7 +17,11 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { T_Q4_0 = 2, T_Q5_0 = 6, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14 };
+enum { T_Q4_0 = 2, T_Q4_1 = 3, T_Q5_0 = 6, T_Q5_1 = 7, T_Q8_0 = 8, T_Q8_1 = 9, T_Q4_K = 12,
+       T_Q6_K = 14 };
+
+/* formats whose value adds a per-block minimum: d*q + m */
+static int has_min(int type) { return type == T_Q4_1 || type == T_Q5_1; }
 
 /* ---------------------------------------------------------------- fp16 -- */
 
@@ -65,6 +69,9 @@ static int block_shape(int type, int* qk, int* nbytes) {
     case T_Q8_0: *qk = 32;  *nbytes = 34;  return 0;
     case T_Q4_0: *qk = 32;  *nbytes = 18;  return 0;
     case T_Q5_0: *qk = 32;  *nbytes = 22;  return 0;
+    case T_Q4_1: *qk = 32;  *nbytes = 20;  return 0;
+    case T_Q5_1: *qk = 32;  *nbytes = 24;  return 0;
+    case T_Q8_1: *qk = 32;  *nbytes = 36;  return 0;
     case T_Q4_K: *qk = 256; *nbytes = 144; return 0;
     case T_Q6_K: *qk = 256; *nbytes = 210; return 0;
     default: return -1;
@@ -99,6 +106,23 @@ static void decode_elem(int type, const uint8_t* blk, int e, int* q, int* sc, in
     case T_Q8_0:
         *q = (int8_t)blk[2 + e];
         break;
+    case T_Q8_1:  /* d, then s = d*sum(q) (not part of the value), then the codes */
+        *q = (int8_t)blk[4 + e];
+        break;
+    case T_Q4_1: {  /* d, m, then the nibbles as in Q4_0; m enters once per element */
+        uint8_t byte = blk[4 + (e & 15)];
+        *q = e < 16 ? (byte & 15) : (byte >> 4);
+        *mn = 1;
+        break;
+    }
+    case T_Q5_1: {  /* d, m, the fifth bits (LE u32), the nibbles */
+        uint8_t byte = blk[8 + (e & 15)];
+        int low4 = e < 16 ? (byte & 15) : (byte >> 4);
+        int bit5 = (int)((rd32(blk + 4) >> e) & 1u);
+        *q = low4 | (bit5 << 4);
+        *mn = 1;
+        break;
+    }
     case T_Q4_0: {
         uint8_t byte = blk[2 + (e & 15)];
         *q = e < 16 ? (byte & 15) : (byte >> 4);
@@ -138,7 +162,7 @@ static void block_scales(int type, const uint8_t* blk, double* d, double* dmin) 
         *d = oracle_half_to_double(rd16(blk + 208));
     else
         *d = oracle_half_to_double(rd16(blk));
-    if (type == T_Q4_K) *dmin = oracle_half_to_double(rd16(blk + 2));
+    if (type == T_Q4_K || has_min(type)) *dmin = oracle_half_to_double(rd16(blk + 2));
 }
 
 /* The integer weight factor that multiplies the activation code, and the
@@ -152,6 +176,9 @@ static void elem_ints(int type, int q, int sc, int mn, int64_t* wint, int64_t* m
     case T_Q8_0: *wint = q; break;
     case T_Q4_0: *wint = q - 8; break;
     case T_Q5_0: *wint = q - 16; break;
+    case T_Q8_1: *wint = q; break;
+    case T_Q4_1:
+    case T_Q5_1: *wint = q; *mint = mn; break;
     case T_Q6_K: *wint = (int64_t)sc * (q - 32); break;
     case T_Q4_K: *wint = (int64_t)sc * q; *mint = mn; break;
     }
@@ -187,6 +214,9 @@ static double elem_value(int type, int q, int sc, int mn, double d, double dmin)
     case T_Q8_0: return d * q;
     case T_Q4_0: return d * (q - 8);
     case T_Q5_0: return d * (q - 16);
+    case T_Q8_1: return d * q;
+    case T_Q4_1:
+    case T_Q5_1: return d * q + dmin;   /* dmin holds the block's m */
     case T_Q4_K: return d * sc * q - dmin * mn;
     case T_Q6_K: return d * sc * (q - 32);
     }
@@ -283,7 +313,8 @@ static void row_decode(int type, const uint8_t* wrow, int64_t K, int qk, int nby
             int64_t k = b * qk + e;
             elem_ints(type, cq, csc, cmn, &r->wint[k], &r->mint[k]);
             r->d[k] = bd;
-            r->dmin[k] = bdmin;
+            /* the factor of the subtracted min term: Q4_K dmin; Q4_1/Q5_1 add m */
+            r->dmin[k] = has_min(type) ? -bdmin : bdmin;
         }
     }
 }
@@ -308,7 +339,7 @@ int oracle_partials(int type, const uint8_t* w, int64_t N, int64_t K,
     if (rc) return rc;
     if (B < 0) return -2;
     int64_t nb = K / 32, rb = (K / qk) * nbytes;
-    int per = type == T_Q4_K ? 2 : 1;
+    int per = (type == T_Q4_K || has_min(type)) ? 2 : 1;
     row_t r;
     if (row_alloc(&r, K)) { row_free(&r); return -4; }
     for (int64_t n = 0; n < N; n++) {
@@ -404,7 +435,7 @@ int oracle_matmul_canon_f32(int type, const uint8_t* w, int64_t N, int64_t K,
                     float da = (float)oracle_half_to_double(rd16(arow + b * 34));
                     float dw = (float)r.d[32 * b];
                     p = fmaf((float)I, dw * da, p);
-                    if (type == T_Q4_K) {
+                    if (type == T_Q4_K || has_min(type)) {
                         float dmw = (float)r.dmin[32 * b];
                         p = fmaf(-(float)Q, dmw * da, p);
                     }

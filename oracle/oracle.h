@@ -17,7 +17,8 @@
  * quantisation in f32 (it decides integer codes, so it takes the kernel's
  * precision), integer partials in int64, and results in f64.
  *
- * Type ids are the GGUF ones: Q4_0 = 2, Q5_0 = 6, Q8_0 = 8, Q4_K = 12, Q6_K = 14.
+ * Type ids are the GGUF ones: Q4_0 = 2, Q4_1 = 3, Q5_0 = 6, Q5_1 = 7, Q8_0 = 8,
+ * Q8_1 = 9, Q4_K = 12, Q6_K = 14.
  * All functions return 0 on success and a negative value on a bad argument
  * (-1 unknown type, -2 bad shape, -3 a partial does not fit in int32).
  */
@@ -38,10 +39,13 @@ uint16_t oracle_float_to_half(float f);
 int oracle_quantize_act(const float* x, int64_t rows, int64_t K, uint8_t* out);
 
 /* Field-by-field unpack of an N x K weight blob.  Per element: the stored code
- * q[N*K] (Q8_0 signed, Q4_0/Q4_K 0..15, Q5_0 0..31, Q6_K 0..63), its sub-block scale
- * sub_scale[N*K] (Q4_K sc_j, Q6_K s_j, else 1) and min sub_min[N*K] (Q4_K m_j,
- * else 0).  Per block of QK elements: d[N*K/QK] and dmin[N*K/QK] (Q4_K only,
- * else 0).  Any output pointer may be NULL. */
+ * q[N*K] (Q8_0/Q8_1 signed, Q4_0/Q4_1/Q4_K 0..15, Q5_0/Q5_1 0..31, Q6_K 0..63),
+ * its sub-block scale sub_scale[N*K] (Q4_K sc_j, Q6_K s_j, else 1) and min
+ * sub_min[N*K] (Q4_K m_j, Q4_1/Q5_1 1, else 0).  Per block of QK elements:
+ * d[N*K/QK] and dmin[N*K/QK] (Q4_K dmin, Q4_1/Q5_1 the block's m, else 0).
+ * Values: d*q (Q8_0, Q8_1), d*(q-8) (Q4_0), d*(q-16) (Q5_0), d*q + m
+ * (Q4_1, Q5_1), d*sc_j*q - dmin*m_j (Q4_K), d*s_j*(q-32) (Q6_K).  Any output
+ * pointer may be NULL. */
 int oracle_unpack(int type, const uint8_t* w, int64_t N, int64_t K, int32_t* q,
                   int32_t* sub_scale, int32_t* sub_min, double* d, double* dmin);
 
@@ -52,10 +56,11 @@ int oracle_dequant(int type, const uint8_t* w, int64_t N, int64_t K, double* out
 int oracle_dequant_act(const uint8_t* xq, int64_t rows, int64_t K, double* out);
 
 /* Exact integer partial per (m, n, 32-element block b), layout [B][N][K/32]:
- *   Q8_0: sum w*a     Q4_0: sum (q-8)*a     Q5_0: sum (q-16)*a
+ *   Q8_0, Q8_1: sum w*a     Q4_0: sum (q-8)*a     Q5_0: sum (q-16)*a
  *   Q6_K: sum s_j*(q-32)*a
  *   Q4_K: two integers per block, layout [B][N][K/32][2]:
- *         P = sum sc_j*q*a  and  Q = sum m_j*a                              */
+ *         P = sum sc_j*q*a  and  Q = sum m_j*a
+ *   Q4_1, Q5_1: the same pair with P = sum q*a and Q = sum a               */
 int oracle_partials(int type, const uint8_t* w, int64_t N, int64_t K,
                     const uint8_t* xq, int64_t B, int32_t* P);
 
@@ -72,8 +77,9 @@ int oracle_dense_f64(int type, const uint8_t* w, int64_t N, int64_t K,
  * grouped into chunks of 8 (256 elements; the last chunk may be short); each
  * chunk starts at +0 and adds its block terms in ascending order, each term
  * added with one rounding (fmaf of the exact partial and the exact product of
- * the two fp16 scales; Q4_K adds +P*(d*da) then -Q*(dmin*da)); y is the
- * chunk sums added in ascending order starting from +0. */
+ * the two fp16 scales; Q4_K adds +P*(d*da) then -Q*(dmin*da), Q4_1/Q5_1
+ * +P*(d*da) then +Q*(m*da)); y is the chunk sums added in ascending order
+ * starting from +0. */
 int oracle_matmul_canon_f32(int type, const uint8_t* w, int64_t N, int64_t K,
                             const uint8_t* xq, int64_t B, float* y);
 

@@ -17,6 +17,10 @@ the byte layouts below are the published GGUF ones:
   Q5_0  32 elems, 22 B : d f16 | qh u32 | qs u8[16]       low 4 bits as Q4_0; bit 4 of
                                                           q is bit e of qh (LE u32);
                                                           value d*(q-16)
+  Q4_1  32 elems, 20 B : d f16 | m f16 | qs u8[16]        nibbles as Q4_0; value d*q + m
+  Q5_1  32 elems, 24 B : d f16 | m f16 | qh u32 | qs[16]  codes as Q5_0; value d*q + m
+  Q8_1  32 elems, 36 B : d f16 | s f16 | qs int8[32]      value d*qs[e] (s = d*sum(qs),
+                                                          stored, not part of the value)
   Q4_K 256 elems, 144 B: d f16 | dmin f16 | sc12 u8[12] | qs u8[128]
                          element e: c=e//64, r=e%64, byte qs[32c + r%32],
                          lo nibble if r<32 else hi nibble; sub-block j=e//32;
@@ -32,11 +36,13 @@ from __future__ import annotations
 import numpy as np
 
 # GGUF tensor type ids (public GGUF enumeration).
-Q4_0, Q5_0, Q8_0, Q4_K, Q6_K = 2, 6, 8, 12, 14
-FORMATS = {"Q4_0": Q4_0, "Q5_0": Q5_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
+Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q8_1, Q4_K, Q6_K = 2, 3, 6, 7, 8, 9, 12, 14
+FORMATS = {"Q4_0": Q4_0, "Q4_1": Q4_1, "Q5_0": Q5_0, "Q5_1": Q5_1, "Q8_0": Q8_0, "Q8_1": Q8_1,
+           "Q4_K": Q4_K, "Q6_K": Q6_K}
 NAMES = {v: k for k, v in FORMATS.items()}
 # (elements per block, bytes per block)
-BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_K: (256, 144), Q6_K: (256, 210)}
+BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_1: (32, 20), Q5_1: (32, 24),
+         Q8_1: (32, 36), Q4_K: (256, 144), Q6_K: (256, 210)}
 
 
 def row_bytes(fmt: int, K: int) -> int:
@@ -67,7 +73,7 @@ def draw_fields(fmt: int, N: int, K: int, seed: int, dscale: float = 0.01,
     rng = np.random.Generator(np.random.PCG64(seed))
     nb = K // qk
     f: dict = {"fmt": fmt, "N": N, "K": K}
-    if fmt == Q8_0:
+    if fmt in (Q8_0, Q8_1):
         f["d"] = _f16_scales(rng, (N, nb), dscale)
         f["q"] = rng.integers(-127, 128, size=(N, K), dtype=np.int16).astype(np.int8)
     elif fmt == Q4_0:
@@ -76,6 +82,11 @@ def draw_fields(fmt: int, N: int, K: int, seed: int, dscale: float = 0.01,
     elif fmt == Q5_0:
         f["d"] = _f16_scales(rng, (N, nb), dscale)
         f["q"] = rng.integers(0, 32, size=(N, K), dtype=np.uint8)
+    elif fmt in (Q4_1, Q5_1):
+        # m: the block minimum, negative in practice: -|N(0,1)| * 8 * dscale
+        f["d"] = _f16_scales(rng, (N, nb), dscale)
+        f["m"] = (-_f16_scales(rng, (N, nb), dscale * 8)).astype(np.float16)
+        f["q"] = rng.integers(0, 16 if fmt == Q4_1 else 32, size=(N, K), dtype=np.uint8)
     elif fmt == Q4_K:
         f["d"] = _f16_scales(rng, (N, nb), dscale)
         f["dmin"] = _f16_scales(rng, (N, nb), dscale)
@@ -106,18 +117,33 @@ def encode(f: dict) -> np.ndarray:
     if fmt == Q8_0:
         out[:, :, 0:2] = _f16_bytes(f["d"])
         out[:, :, 2:34] = f["q"].reshape(N, nb, 32).view(np.uint8)
+    elif fmt == Q8_1:
+        q = f["q"].reshape(N, nb, 32)
+        out[:, :, 0:2] = _f16_bytes(f["d"])
+        s = f["d"].astype(np.float32) * q.astype(np.float32).sum(axis=2)
+        out[:, :, 2:4] = _f16_bytes(s.astype(np.float16))
+        out[:, :, 4:36] = q.view(np.uint8)
     elif fmt == Q4_0:
         q = f["q"].reshape(N, nb, 32)
         out[:, :, 0:2] = _f16_bytes(f["d"])
         out[:, :, 2:18] = q[:, :, :16] | (q[:, :, 16:] << 4)
-    elif fmt == Q5_0:
+    elif fmt in (Q5_0, Q5_1):
         q = f["q"].reshape(N, nb, 32)
         out[:, :, 0:2] = _f16_bytes(f["d"])
+        o = 2
+        if fmt == Q5_1:
+            out[:, :, 2:4] = _f16_bytes(f["m"])
+            o = 4
         bits = (q >> 4).astype(np.uint32) << np.arange(32, dtype=np.uint32)
         qh = np.bitwise_or.reduce(bits, axis=2)
-        out[:, :, 2:6] = qh.astype("<u4").view(np.uint8).reshape(N, nb, 4)
+        out[:, :, o:o + 4] = qh.astype("<u4").view(np.uint8).reshape(N, nb, 4)
         lo = q & 15
-        out[:, :, 6:22] = lo[:, :, :16] | (lo[:, :, 16:] << 4)
+        out[:, :, o + 4:o + 20] = lo[:, :, :16] | (lo[:, :, 16:] << 4)
+    elif fmt == Q4_1:
+        q = f["q"].reshape(N, nb, 32)
+        out[:, :, 0:2] = _f16_bytes(f["d"])
+        out[:, :, 2:4] = _f16_bytes(f["m"])
+        out[:, :, 4:20] = q[:, :, :16] | (q[:, :, 16:] << 4)
     elif fmt == Q4_K:
         sc, m = f["sc"], f["m"]
         out[:, :, 0:2] = _f16_bytes(f["d"])

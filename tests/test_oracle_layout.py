@@ -16,14 +16,15 @@ import oracle
 import synth
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden", "weight_blocks.json")
-FMTS = [synth.Q8_0, synth.Q4_0, synth.Q5_0, synth.Q4_K, synth.Q6_K]
+FMTS = [synth.Q8_0, synth.Q4_0, synth.Q5_0, synth.Q4_1, synth.Q5_1, synth.Q8_1, synth.Q4_K,
+        synth.Q6_K]
 
 
 def _golden():
     return json.load(open(GOLD))["blocks"]
 
 
-@pytest.mark.parametrize("name", ["Q8_0", "Q4_0", "Q5_0", "Q4_K", "Q6_K"])
+@pytest.mark.parametrize("name", ["Q8_0", "Q4_0", "Q5_0", "Q4_1", "Q5_1", "Q8_1", "Q4_K", "Q6_K"])
 def test_hand_assembled_block(name):
     g = _golden()[name]
     blk = np.zeros(g["nbytes"], np.uint8)
@@ -47,6 +48,9 @@ def test_hand_assembled_block(name):
     if name == "Q6_K":
         assert np.array_equal(u["sub_scale"][0].reshape(16, 16)[:, 0], g["s"])
         assert u["d"][0, 0] == 0.25
+    if name in ("Q4_1", "Q5_1"):
+        assert u["dmin"][0, 0] == {"Q4_1": -1.0, "Q5_1": 2.0}[name]
+        assert np.all(u["sub_min"][0] == 1)
 
 
 def _expected_fields(f):
@@ -60,6 +64,9 @@ def _expected_fields(f):
         sc = np.repeat(f["sc"].reshape(N, -1), 32, axis=1).astype(np.int32)
         mn = np.repeat(f["m"].reshape(N, -1), 32, axis=1).astype(np.int32)
         dmin = f["dmin"].astype(np.float64)
+    if fmt in (synth.Q4_1, synth.Q5_1):
+        mn = np.ones((N, K), np.int32)
+        dmin = f["m"].astype(np.float64)
     if fmt == synth.Q6_K:
         sc = np.repeat(f["s"].reshape(N, -1), 16, axis=1).astype(np.int32)
     return q, sc, mn, f["d"].astype(np.float64), dmin
@@ -92,14 +99,14 @@ def test_roundtrip_exhaustive_codes_and_subscales(fmt):
     qk = synth.BLOCK[fmt][0]
     K = qk * 2
     f = synth.draw_fields(fmt, 1, K, 0)
-    rng_codes = {synth.Q8_0: 256, synth.Q4_0: 16, synth.Q5_0: 32, synth.Q4_K: 16,
-                 synth.Q6_K: 64}[fmt]
+    rng_codes = {synth.Q8_0: 256, synth.Q4_0: 16, synth.Q5_0: 32, synth.Q4_1: 16, synth.Q5_1: 32,
+                 synth.Q8_1: 256, synth.Q4_K: 16, synth.Q6_K: 64}[fmt]
     N = max(rng_codes, 64 if fmt == synth.Q4_K else 1, 256 if fmt == synth.Q6_K else 1)
     f = synth.draw_fields(fmt, N, K, 3)
     n = np.arange(N)[:, None]
     e = np.arange(K)[None, :]
     codes = (n + e) % rng_codes
-    if fmt == synth.Q8_0:
+    if fmt in (synth.Q8_0, synth.Q8_1):
         f["q"] = (codes - 128).astype(np.int8)
     else:
         f["q"] = codes.astype(np.uint8)
@@ -119,13 +126,15 @@ def test_roundtrip_exhaustive_codes_and_subscales(fmt):
 def test_one_hot_element_position(fmt):
     """A single non-neutral code lands on exactly its own element."""
     qk = synth.BLOCK[fmt][0]
-    neutral = {synth.Q8_0: 0, synth.Q4_0: 8, synth.Q5_0: 16, synth.Q4_K: 0, synth.Q6_K: 32}[fmt]
+    neutral = {synth.Q8_0: 0, synth.Q4_0: 8, synth.Q5_0: 16, synth.Q4_1: 0, synth.Q5_1: 0,
+               synth.Q8_1: 0, synth.Q4_K: 0, synth.Q6_K: 32}[fmt]
     for e in [0, 1, 15, 16, 31, qk - 1] + ([32, 63, 64, 127, 128, 200] if qk == 256 else []):
         f = synth.draw_fields(fmt, 1, qk, 5)
         f["q"][:] = neutral
         f["q"][0, e] = neutral + 3
-        if fmt == synth.Q4_K:
+        if "m" in f:
             f["m"][:] = 0
+        if fmt == synth.Q4_K:
             f["sc"][:] = 1
         if fmt == synth.Q6_K:
             f["s"][:] = 1
@@ -148,6 +157,10 @@ def test_dequant_matches_element_formulas(fmt):
         want = d * (q - 8)
     elif fmt == synth.Q5_0:
         want = d * (q - 16)
+    elif fmt in (synth.Q4_1, synth.Q5_1):
+        want = d * q + np.repeat(f["m"].astype(np.float64), qk, axis=1)
+    elif fmt == synth.Q8_1:
+        want = d * q
     elif fmt == synth.Q4_K:
         sc = np.repeat(f["sc"].reshape(N, -1), 32, axis=1)
         mm = np.repeat(f["m"].reshape(N, -1), 32, axis=1)
@@ -162,6 +175,6 @@ def test_dequant_matches_element_formulas(fmt):
 
 def test_refusals():
     with pytest.raises(ValueError):
-        oracle.dequant(3, np.zeros(64, np.uint8), 1, 32)        # unknown type
+        oracle.dequant(4, np.zeros(64, np.uint8), 1, 32)        # unknown type
     with pytest.raises(ValueError):
         oracle.dequant(synth.Q4_K, np.zeros(144, np.uint8), 1, 128)  # K % 256

@@ -21,7 +21,9 @@ import oracle
 import synth
 from checks import assert_bitwise, assert_tol, tol_violations
 
-FMTS = [synth.Q8_0, synth.Q4_0, synth.Q5_0, synth.Q4_K, synth.Q6_K]
+FMTS = [synth.Q8_0, synth.Q4_0, synth.Q5_0, synth.Q4_1, synth.Q5_1, synth.Q8_1, synth.Q4_K,
+        synth.Q6_K]
+MIN_FMTS = (synth.Q4_K, synth.Q4_1, synth.Q5_1)   # partials come in pairs
 
 
 def _acts(xq, B, K):
@@ -45,8 +47,11 @@ def _wint_mint(f):
     fmt, N, K = f["fmt"], f["N"], f["K"]
     q = f["q"].astype(np.int64)
     mint = np.zeros((N, K), np.int64)
-    if fmt == synth.Q8_0:
+    if fmt in (synth.Q8_0, synth.Q8_1):
         wint = q
+    elif fmt in (synth.Q4_1, synth.Q5_1):
+        wint = q
+        mint = np.ones((N, K), np.int64)
     elif fmt == synth.Q4_0:
         wint = q - 8
     elif fmt == synth.Q5_0:
@@ -71,7 +76,7 @@ def test_partials_brute_force(fmt):
                 sl = slice(32 * b, 32 * b + 32)
                 I = sum(int(w) * int(v) for w, v in zip(wint[n, sl], a[m, sl]))
                 Q = sum(int(w) * int(v) for w, v in zip(mint[n, sl], a[m, sl]))
-                if fmt == synth.Q4_K:
+                if fmt in MIN_FMTS:
                     assert (P[m, n, b, 0], P[m, n, b, 1]) == (I, Q)
                 else:
                     assert P[m, n, b] == I and Q == 0
@@ -95,6 +100,8 @@ def test_partials_reproduce_exact_block_dot(fmt):
                 dmw = Fraction(float(u["dmin"][n, (32 * b) // qk]))
                 if fmt == synth.Q4_K:
                     got = Fraction(float(da[m, b])) * (dw * int(P[m, n, b, 0]) - dmw * int(P[m, n, b, 1]))
+                elif fmt in MIN_FMTS:   # dmin reports the block's m, which is added
+                    got = Fraction(float(da[m, b])) * (dw * int(P[m, n, b, 0]) + dmw * int(P[m, n, b, 1]))
                 else:
                     got = Fraction(float(da[m, b])) * dw * int(P[m, n, b])
                 assert got == exact
@@ -148,6 +155,22 @@ def test_zero_point_rows_give_exact_zero(fmt):
     y, _ = oracle.matmul_f64(fmt, blob, N, K, xq, B)
     assert np.all(y == 0)
     assert np.all(oracle.matmul_canon_f32(fmt, blob, N, K, xq, B) == 0)
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_1, synth.Q5_1])
+def test_zero_codes_leave_the_block_minimum(fmt):
+    """q = 0 everywhere: y = sum_b d_a * m_b * S_b (S_b = sum of activation codes)."""
+    blob, f, x, xq, N, K, B = _case(fmt, N=2, nblk=3, B=2, seed=13)
+    f["q"][:] = 0
+    blob = synth.encode(f)
+    y, _ = oracle.matmul_f64(fmt, blob, N, K, xq, B)
+    da, a = _acts(xq, B, K)
+    S = a.reshape(B, K // 32, 32).sum(axis=2)
+    for m in range(B):
+        for n in range(N):
+            want = sum(Fraction(float(da[m, b])) * Fraction(float(f["m"][n, b])) * int(S[m, b])
+                       for b in range(K // 32))
+            assert abs(Fraction(y[m, n]) - want) <= abs(want) * Fraction(1, 2 ** 50)
 
 
 def test_q4k_scale_zero_leaves_minus_min_term():
@@ -211,10 +234,11 @@ def _canon_exact(fmt, blob, N, K, xq, B):
                 for b in range(c0, min(nb, c0 + 8)):
                     dA = Fraction(float(da[m, b]))
                     dw = Fraction(float(u["d"][n, (32 * b) // qk]))
-                    if fmt == synth.Q4_K:
+                    if fmt in MIN_FMTS:
                         p = _round_f32(p + int(P[m, n, b, 0]) * dw * dA)
                         dmw = Fraction(float(u["dmin"][n, (32 * b) // qk]))
-                        p = _round_f32(p - int(P[m, n, b, 1]) * dmw * dA)
+                        sgn = -1 if fmt == synth.Q4_K else 1   # Q4_K subtracts, Q4_1/Q5_1 add
+                        p = _round_f32(p + sgn * int(P[m, n, b, 1]) * dmw * dA)
                     else:
                         p = _round_f32(p + int(P[m, n, b]) * dw * dA)
                 acc = _round_f32(acc + p)
@@ -223,6 +247,7 @@ def _canon_exact(fmt, blob, N, K, xq, B):
 
 
 @pytest.mark.parametrize("fmt,nblk", [(synth.Q8_0, 20), (synth.Q4_0, 9), (synth.Q5_0, 11),
+                                      (synth.Q4_1, 9), (synth.Q5_1, 10), (synth.Q8_1, 9),
                                       (synth.Q4_K, 2), (synth.Q6_K, 2)])
 def test_canon_f32_against_exact_rational_emulation(fmt, nblk):
     blob, f, x, xq, N, K, B = _case(fmt, N=3, nblk=nblk, B=2, seed=31)
@@ -237,7 +262,7 @@ def test_canon_f32_error_bound(fmt):
     y, A = oracle.matmul_f64(fmt, blob, N, K, xq, B)
     yc = oracle.matmul_canon_f32(fmt, blob, N, K, xq, B).astype(np.float64)
     nb = K // 32
-    rounds = nb * (2 if fmt == synth.Q4_K else 1) + (nb + 7) // 8
+    rounds = nb * (2 if fmt in MIN_FMTS else 1) + (nb + 7) // 8
     assert np.all(np.abs(yc - y) <= rounds * 2.0 ** -24 * A * 1.0001)
 
 
