@@ -14,9 +14,11 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqmv.so")
 
-Q4_0, Q5_0, Q8_0, Q4_K, Q6_K = 2, 6, 8, 12, 14
-TYPES = {"Q4_0": Q4_0, "Q5_0": Q5_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
-BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_K: (256, 144), Q6_K: (256, 210)}
+Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q8_1, Q4_K, Q6_K = 2, 3, 6, 7, 8, 9, 12, 14
+TYPES = {"Q4_0": Q4_0, "Q4_1": Q4_1, "Q5_0": Q5_0, "Q5_1": Q5_1, "Q8_0": Q8_0, "Q8_1": Q8_1,
+         "Q4_K": Q4_K, "Q6_K": Q6_K}
+BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_1: (32, 20), Q5_1: (32, 24),
+         Q8_1: (32, 36), Q4_K: (256, 144), Q6_K: (256, 210)}
 EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
            "qmv_partials_launch", "qmv_strerror")
 MAX_BATCH = 16
@@ -212,9 +214,9 @@ def matmul(type: int, w, N: int, K: int, x=None, xq=None, M=None, y=None, stream
 
 
 def partials(type: int, w, N: int, K: int, xq, B: int, P=None, stream=None):
-    """Test hook: int32 per-block partials [B, N, K/32] (Q4_K [B, N, K/32, 2])."""
+    """Test hook: int32 per-block partials [B, N, K/32] (Q4_K, Q4_1, Q5_1: [B, N, K/32, 2])."""
     import torch
-    shape = (B, N, K // 32, 2) if type == Q4_K else (B, N, K // 32)
+    shape = (B, N, K // 32, 2) if type in (Q4_K, Q4_1, Q5_1) else (B, N, K // 32)
     if P is None:
         P = torch.empty(shape, dtype=torch.int32, device=w.device)
     qmv_partials_launch(type, _dev(w, torch.uint8, "w"), N, K, _dev(xq, torch.uint8, "xq"), B,

@@ -42,7 +42,13 @@
 namespace qmv {
 namespace {
 
-constexpr int T_Q4_0 = 2, T_Q5_0 = 6, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14;
+constexpr int T_Q4_0 = 2, T_Q4_1 = 3, T_Q5_0 = 6, T_Q5_1 = 7, T_Q8_0 = 8, T_Q8_1 = 9,
+              T_Q4_K = 12, T_Q6_K = 14;
+// Formats whose block term has a second part fed by the activation code sums
+// (Q4_K's sub-block mins; the block minimum m of Q4_1 / Q5_1).
+template <int FMT> constexpr bool has_min_term() {
+    return FMT == T_Q4_K || FMT == T_Q4_1 || FMT == T_Q5_1;
+}
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -58,6 +64,9 @@ template <int FMT> struct GFmt;
 template <> struct GFmt<T_Q8_0> { static constexpr int QK = 32, BB = 34; };
 template <> struct GFmt<T_Q4_0> { static constexpr int QK = 32, BB = 18; };
 template <> struct GFmt<T_Q5_0> { static constexpr int QK = 32, BB = 22; };
+template <> struct GFmt<T_Q4_1> { static constexpr int QK = 32, BB = 20; };
+template <> struct GFmt<T_Q5_1> { static constexpr int QK = 32, BB = 24; };
+template <> struct GFmt<T_Q8_1> { static constexpr int QK = 32, BB = 36; };
 template <> struct GFmt<T_Q4_K> { static constexpr int QK = 256, BB = 144; };
 template <> struct GFmt<T_Q6_K> { static constexpr int QK = 256, BB = 210; };
 
@@ -74,13 +83,16 @@ template <int FMT> struct WRaw;
 template <> struct WRaw<T_Q8_0> { uint32_t v[9]; };    // 34 B
 template <> struct WRaw<T_Q4_0> { uint32_t v[5]; };    // 18 B
 template <> struct WRaw<T_Q5_0> { uint32_t v[6]; };    // 22 B
+template <> struct WRaw<T_Q4_1> { uint32_t v[5]; };    // 20 B
+template <> struct WRaw<T_Q5_1> { uint32_t v[6]; };    // 24 B
+template <> struct WRaw<T_Q8_1> { uint32_t v[9]; };    // 36 B
 template <> struct WRaw<T_Q4_K> { uint32_t hdr[4]; uint32_t q[8]; };   // d, dmin, sc12; 32 B of qs
 template <> struct WRaw<T_Q6_K> { uint32_t ql[8]; uint32_t qh[8]; uint32_t sd; };  // s pair | d << 16
 
 // Block b (< nb) of a weight row.
 template <int FMT>
 __device__ __forceinline__ void fetch_w(const uint8_t* row, int b, WRaw<FMT>& r) {
-    if constexpr (FMT == T_Q8_0 || FMT == T_Q4_0 || FMT == T_Q5_0) {
+    if constexpr (GFmt<FMT>::QK == 32) {
         __builtin_memcpy(r.v, row + (int64_t)b * GFmt<FMT>::BB, GFmt<FMT>::BB);
     } else if constexpr (FMT == T_Q4_K) {
         const uint8_t* sb = row + (int64_t)144 * (b >> 3);
@@ -142,13 +154,14 @@ struct WScale {
 // and <= 4096: exact in f16), else leaves q - 32 and returns s0, s1.
 template <int FMT, bool FOLD>
 __device__ __forceinline__ void decode_w(const WRaw<FMT>& r, int b, uint32_t (&o)[16], WScale& s) {
-    if constexpr (FMT == T_Q8_0) {
+    if constexpr (FMT == T_Q8_0 || FMT == T_Q8_1) {
         const uint8_t* blk = reinterpret_cast<const uint8_t*>(r.v);
         s.d = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8);
+        constexpr int QS = FMT == T_Q8_0 ? 2 : 4;  // Q8_1 keeps s = d*sum(q) in bytes 2-3
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             uint32_t q;
-            __builtin_memcpy(&q, blk + 2 + 4 * i, 4);
+            __builtin_memcpy(&q, blk + QS + 4 * i, 4);
             // int8 x -> x ^ 0x80 = x + 128 in [0, 255]; minus 128 after the f16 trick
             bytes_to_f16(q ^ 0x80808080u, 128.0f, o[2 * i], o[2 * i + 1]);
         }
@@ -161,6 +174,28 @@ __device__ __forceinline__ void decode_w(const WRaw<FMT>& r, int b, uint32_t (&o
             __builtin_memcpy(&q, blk + 2 + 4 * i, 4);
             bytes_to_f16(q & 0x0F0F0F0Fu, 8.0f, o[2 * i], o[2 * i + 1]);                // 0..15
             bytes_to_f16((q >> 4) & 0x0F0F0F0Fu, 8.0f, o[8 + 2 * i], o[8 + 2 * i + 1]);  // 16..31
+        }
+    } else if constexpr (FMT == T_Q4_1 || FMT == T_Q5_1) {
+        // codes 0..15 / 0..31 as f16; the block minimum is the second term:
+        // x1 = -m, so that the epilogue's fma(-x1, d_a S, p) adds m d_a S
+        const uint8_t* blk = reinterpret_cast<const uint8_t*>(r.v);
+        s.d = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8);
+        s.x1 = __float_as_uint(-(float)h_of_bits((uint32_t)blk[2] | ((uint32_t)blk[3] << 8)));
+        constexpr int QS = FMT == T_Q4_1 ? 4 : 8;
+        uint32_t h = 0;
+        if constexpr (FMT == T_Q5_1) __builtin_memcpy(&h, blk + 4, 4);
+        auto spread4 = [](uint32_t v) { return (__umul24(v, 0x204081u) & 0x01010101u) << 4; };
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint32_t q;
+            __builtin_memcpy(&q, blk + QS + 4 * i, 4);
+            uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
+            if constexpr (FMT == T_Q5_1) {
+                lo |= spread4((h >> (4 * i)) & 15u);
+                hi |= spread4((h >> (16 + 4 * i)) & 15u);
+            }
+            bytes_to_f16(lo, 0.0f, o[2 * i], o[2 * i + 1]);            // 0..15
+            bytes_to_f16(hi, 0.0f, o[8 + 2 * i], o[8 + 2 * i + 1]);    // 16..31
         }
     } else if constexpr (FMT == T_Q5_0) {
         const uint8_t* blk = reinterpret_cast<const uint8_t*>(r.v);
@@ -346,7 +381,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
         const int bc = r.have ? b : nb - 1;
         fetch_w<FMT>(wrow, bc, r.w);
         r.da = ahda[bc];
-        if (FMT == T_Q4_K) r.ca = arca[bc];
+        if (has_min_term<FMT>()) r.ca = arca[bc];
     };
 
     // accumulators of tile i: chunk sum p and running sum yv
@@ -388,8 +423,8 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
             const uint32_t dd = f.d | (f.d << 16);
             sm->rw[sk][sr] = make_uint4(dd, dd, dd, dd);
             sm->ra[sk][sr] = make_uint4(r.da, 0, 0, 0);
-            if (FMT == T_Q4_K) sm->ca[sk][sr] = r.ca;
-            if (FMT == T_Q4_K || FMT == T_Q6_K) sm->x1[sk][sr] = f.x1;
+            if (has_min_term<FMT>()) sm->ca[sk][sr] = r.ca;
+            if (has_min_term<FMT>() || FMT == T_Q6_K) sm->x1[sk][sr] = f.x1;
         }
         // B2: the W tile is staged; this wave's activation loads of step h
         // completed before its weight loads of step h were consumed above
@@ -425,7 +460,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
                         __builtin_memcpy(&Ra[1], &r1, 16);
                         __builtin_memcpy(&Rw, &rb, 16);
                     }
-                    const uint32_t x1 = (FMT == T_Q4_K || FMT == T_Q6_K) ? sm->x1[bk][brow] : 0u;
+                    const uint32_t x1 = (has_min_term<FMT>() || FMT == T_Q6_K) ? sm->x1[bk][brow] : 0u;
 #pragma unroll
                     for (int i = 0; i < 2; i++) {
                         const v16f S = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ra[i], Rw, zero16, 0, 0, 0);
@@ -443,7 +478,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
                             I = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i][1], Bf[1], I, 0, 0, 0);
 #pragma unroll
                             for (int e = 0; e < 16; e++) p[i][e] = fmaf(I[e], S[e], p[i][e]);
-                            if constexpr (FMT == T_Q4_K) {
+                            if constexpr (has_min_term<FMT>()) {
                                 // element e of the lane is row 8(e/4) + 4kq + e%4 of the tile
                                 const float nX = -__uint_as_float(x1);
                                 const float* cr = &sm->ca[bk][64 * wm + 32 * i + 4 * kq];
@@ -514,6 +549,9 @@ int launch_gemm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t*
     case T_Q8_0: return launch_gemm_t<T_Q8_0>(w, N, K, xq, M, y, s);
     case T_Q4_0: return launch_gemm_t<T_Q4_0>(w, N, K, xq, M, y, s);
     case T_Q5_0: return launch_gemm_t<T_Q5_0>(w, N, K, xq, M, y, s);
+    case T_Q4_1: return launch_gemm_t<T_Q4_1>(w, N, K, xq, M, y, s);
+    case T_Q5_1: return launch_gemm_t<T_Q5_1>(w, N, K, xq, M, y, s);
+    case T_Q8_1: return launch_gemm_t<T_Q8_1>(w, N, K, xq, M, y, s);
     case T_Q4_K: return launch_gemm_t<T_Q4_K>(w, N, K, xq, M, y, s);
     case T_Q6_K: return launch_gemm_t<T_Q6_K>(w, N, K, xq, M, y, s);
     }

@@ -17,7 +17,10 @@ int elems_per_block(int type) {
     switch (type) {
     case QMV_Q8_0:
     case QMV_Q4_0:
-    case QMV_Q5_0: return 32;
+    case QMV_Q5_0:
+    case QMV_Q4_1:
+    case QMV_Q5_1:
+    case QMV_Q8_1: return 32;
     case QMV_Q4_K:
     case QMV_Q6_K: return 256;
     }
@@ -141,8 +144,8 @@ const char* qmv_strerror(int code) {
     switch (code) {
     case QMV_OK: return "ok";
     case QMV_EINVAL_TYPE:
-        return "unsupported weight type: accepted are Q4_0 (2), Q5_0 (6), Q8_0 (8), Q4_K (12), "
-               "Q6_K (14)";
+        return "unsupported weight type: accepted are Q4_0 (2), Q4_1 (3), Q5_0 (6), Q5_1 (7), "
+               "Q8_0 (8), Q8_1 (9), Q4_K (12), Q6_K (14)";
     case QMV_EINVAL_SHAPE:
         return "bad shape: need 1 <= N <= 2^31-1, 32 <= K <= 2^20 with K % 32 == 0 "
                "(K % 256 == 0 for Q4_K/Q6_K), 1 <= B <= 16 for qmv_launch (use qmm_launch "

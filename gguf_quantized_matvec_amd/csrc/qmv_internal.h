@@ -65,7 +65,10 @@ struct GemvDesc {
 inline int64_t row_bytes(int type, int64_t K) {
     switch (type) {
     case 2: return K / 32 * 18;     // Q4_0
+    case 3: return K / 32 * 20;     // Q4_1
     case 6: return K / 32 * 22;     // Q5_0
+    case 7: return K / 32 * 24;     // Q5_1
+    case 9: return K / 32 * 36;     // Q8_1
     case 8: return K / 32 * 34;     // Q8_0
     case 12: return K / 256 * 144;  // Q4_K
     case 14: return K / 256 * 210;  // Q6_K

@@ -31,7 +31,13 @@
 namespace qmv {
 namespace {
 
-constexpr int T_Q4_0 = 2, T_Q5_0 = 6, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14;
+constexpr int T_Q4_0 = 2, T_Q4_1 = 3, T_Q5_0 = 6, T_Q5_1 = 7, T_Q8_0 = 8, T_Q8_1 = 9,
+              T_Q4_K = 12, T_Q6_K = 14;
+// Formats whose block term has a second, minimum part fed by the activation
+// code sums: Q4_K (sub-block mins, subtracted) and Q4_1 / Q5_1 (d*q + m).
+template <int FMT> constexpr bool has_min_term() {
+    return FMT == T_Q4_K || FMT == T_Q4_1 || FMT == T_Q5_1;
+}
 
 // Batch sizes up to this run on the lane-per-chunk v_dot4 kernel, larger ones on MFMA.
 constexpr int DOT_MAX_ROWS = 4;
@@ -208,6 +214,10 @@ template <int FMT> struct Fmt;
 template <> struct Fmt<T_Q8_0> { static constexpr int QK = 32, BB = 34, CB = 272, PPS = 18; };
 template <> struct Fmt<T_Q4_0> { static constexpr int QK = 32, BB = 18, CB = 144, PPS = 10; };
 template <> struct Fmt<T_Q5_0> { static constexpr int QK = 32, BB = 22, CB = 176, PPS = 12; };
+// 20-, 24- and 36-byte blocks keep every span 4-byte aligned
+template <> struct Fmt<T_Q4_1> { static constexpr int QK = 32, BB = 20, CB = 160, PPS = 11; };
+template <> struct Fmt<T_Q5_1> { static constexpr int QK = 32, BB = 24, CB = 192, PPS = 13; };
+template <> struct Fmt<T_Q8_1> { static constexpr int QK = 32, BB = 36, CB = 288, PPS = 19; };
 template <> struct Fmt<T_Q4_K> { static constexpr int QK = 256, BB = 144, CB = 144, PPS = 9; };
 template <> struct Fmt<T_Q6_K> { static constexpr int QK = 256, BB = 210, CB = 210, PPS = 14; };
 
@@ -355,7 +365,7 @@ __device__ __forceinline__ void fetch_act(const ActRef& A, int c, int nbc, int l
     const uint32_t o = (8 * c + sbc) * 16 + 2 * (lane & 7);
     float2 da = *reinterpret_cast<const float2*>(A.da + o);
     float2 ca = make_float2(0.f, 0.f);
-    if (FMT == T_Q4_K) ca = *reinterpret_cast<const float2*>(A.ca + o);
+    if (has_min_term<FMT>()) ca = *reinterpret_cast<const float2*>(A.ca + o);
     const bool ok = sb < nbc;
     r.da = ok ? da : make_float2(0.f, 0.f);
     r.ca = ok ? ca : make_float2(0.f, 0.f);
@@ -386,22 +396,27 @@ __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, c
     uint64_t q[8];       // per block (Q8_0, Q4_0); per 32-byte quarter (Q4_K, Q6_K ql)
     uint16_t dq[8];      // per-block fp16 d (Q8_0, Q4_0)
     uint64_t qh[2];      // Q6_K high bits, per 128-element half
-    uint32_t h5[8];      // Q5_0: the block's fifth bits, the lane's 8 in the low byte
+    uint32_t h5[8];      // Q5_0, Q5_1: the block's fifth bits, the lane's 8 in the low byte
+    uint16_t mq[8];      // Q4_1, Q5_1: per-block fp16 m
     uint4 hdr;           // Q4_K: d, dmin, 12 scale bytes; Q6_K: the 16 sub-scales
     uint16_t d6 = 0;     // Q6_K d
-    if (FMT == T_Q8_0 || FMT == T_Q4_0 || FMT == T_Q5_0) {
+    if (F_QK<FMT>() == 32) {
+        // field offsets: codes, fifth-bit word
+        constexpr int QS = FMT == T_Q8_0 ? 2 : FMT == T_Q8_1 ? 4 : FMT == T_Q4_0 ? 2
+                         : FMT == T_Q4_1 ? 4 : FMT == T_Q5_0 ? 6 : 8;
+        constexpr int QH = FMT == T_Q5_0 ? 2 : 4;
 #pragma unroll
         for (int bb = 0; bb < 8; bb++) {
             const uint8_t* blk = rb + F_BB<FMT>() * bb;
             dq[bb] = ld<uint16_t>(blk);
-            if (FMT == T_Q8_0) {
-                q[bb] = ld<uint64_t>(blk + 2 + 8 * kg);
+            if (FMT == T_Q8_0 || FMT == T_Q8_1) {
+                q[bb] = ld<uint64_t>(blk + QS + 8 * kg);
             } else {
                 // lanes kg = 2, 3 take the high nibbles: one per-lane shift
-                const int qs = FMT == T_Q5_0 ? 6 : 2;
-                q[bb] = ld<uint64_t>(blk + qs + 8 * (kg & 1)) >> (2 * (kg & 2));
+                q[bb] = ld<uint64_t>(blk + QS + 8 * (kg & 1)) >> (2 * (kg & 2));
             }
-            if (FMT == T_Q5_0) h5[bb] = ld<uint32_t>(blk + 2) >> (8 * kg);
+            if (FMT == T_Q5_0 || FMT == T_Q5_1) h5[bb] = ld<uint32_t>(blk + QH) >> (8 * kg);
+            if (FMT == T_Q4_1 || FMT == T_Q5_1) mq[bb] = ld<uint16_t>(blk + 2);
         }
     } else if (FMT == T_Q4_K) {
         hdr = ld<uint4>(rb);
@@ -424,18 +439,18 @@ __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, c
             for (int i = 0; i < 4; i++) dav[bb][i] = cav[bb][i] = 0.0f;
             if (NI == 1) {
                 dav[bb][0] = sp[0];
-                if (FMT == T_Q4_K) cav[bb][0] = sp[128];
+                if (has_min_term<FMT>()) cav[bb][0] = sp[128];
             } else if (NI == 2) {
                 const float2 d2 = *reinterpret_cast<const float2*>(sp);
                 dav[bb][0] = d2.x; dav[bb][1] = d2.y;
-                if (FMT == T_Q4_K) {
+                if (has_min_term<FMT>()) {
                     const float2 c2 = *reinterpret_cast<const float2*>(sp + 128);
                     cav[bb][0] = c2.x; cav[bb][1] = c2.y;
                 }
             } else {
                 const float4 d4 = *reinterpret_cast<const float4*>(sp);
                 dav[bb][0] = d4.x; dav[bb][1] = d4.y; dav[bb][2] = d4.z; dav[bb][3] = d4.w;
-                if (FMT == T_Q4_K) {
+                if (has_min_term<FMT>()) {
                     const float4 c4 = *reinterpret_cast<const float4*>(sp + 128);
                     cav[bb][0] = c4.x; cav[bb][1] = c4.y; cav[bb][2] = c4.z; cav[bb][3] = c4.w;
                 }
@@ -466,9 +481,20 @@ __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, c
         // MFMA sums (|.| < 2^16) and the 6- or 8-bit scales fit its operands.
         v4i I;
         int mn = 0;
-        if (FMT == T_Q8_0) {
+        if (FMT == T_Q8_0 || FMT == T_Q8_1) {
             dw = half_bits_to_float(dq[bb]);
             I = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, (long)q[bb], zero, 0, 0, 0);
+        } else if (FMT == T_Q4_1) {
+            dw = half_bits_to_float(dq[bb]);
+            mn = 1;
+            I = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, (long)(q[bb] & 0x0F0F0F0F0F0F0F0Full), zero,
+                                                     0, 0, 0);
+        } else if (FMT == T_Q5_1) {
+            dw = half_bits_to_float(dq[bb]);
+            mn = 1;
+            const uint64_t b5 = ((uint64_t)spread4((h5[bb] >> 4) & 15u) << 32) | spread4(h5[bb] & 15u);
+            I = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                a, (long)((q[bb] & 0x0F0F0F0F0F0F0F0Full) | b5), zero, 0, 0, 0);
         } else if (FMT == T_Q4_0) {
             dw = half_bits_to_float(dq[bb]);
             const uint64_t wc = bytes_minus(q[bb] & 0x0F0F0F0F0F0F0F0Full, 0x0808080808080808ull);
@@ -516,14 +542,14 @@ __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, c
         if (PARTIALS) {
             const int b = 8 * c + bb;
             int4 S4 = make_int4(0, 0, 0, 0);
-            if (FMT == T_Q4_K) S4 = *reinterpret_cast<const int4*>(po.S + b * 16);
+            if (has_min_term<FMT>()) S4 = *reinterpret_cast<const int4*>(po.S + b * 16);
             const int Sv[4] = {S4.x, S4.y, S4.z, S4.w};
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int m = 4 * kg + i;
                 if (m < po.Bg && po.n < po.nrows) {
                     const int64_t o = ((po.row0 + m) * po.N + po.n) * po.nb + b;
-                    if (FMT == T_Q4_K) {
+                    if (has_min_term<FMT>()) {
                         po.P[2 * o] = I[i];
                         po.P[2 * o + 1] = mn * Sv[i];
                     } else {
@@ -532,11 +558,14 @@ __device__ __forceinline__ void chunk_math(const uint8_t* rb, const float* sl, c
                 }
             }
         } else {
-            const float cw = FMT == T_Q4_K ? dmw * (float)mn : 0.0f;
+            // second term: Q4_K -(dmin m_j)(d_a S); Q4_1 / Q5_1 +m (d_a S)
+            float cw = 0.0f;
+            if (FMT == T_Q4_K) cw = -(dmw * (float)mn);
+            if (FMT == T_Q4_1 || FMT == T_Q5_1) cw = half_bits_to_float(mq[bb]);
 #pragma unroll
             for (int i = 0; i < NI; i++) {
                 p[i] = fmaf((float)I[i], dw * dav[bb][i], p[i]);
-                if (FMT == T_Q4_K) p[i] = fmaf(-cw, cav[bb][i], p[i]);
+                if (has_min_term<FMT>()) p[i] = fmaf(cw, cav[bb][i], p[i]);
             }
         }
     }
@@ -553,7 +582,7 @@ __device__ __forceinline__ void stage_all(uint8_t* wl, float* sl, int lane,
                                           const ActRegs& nxt, long (&acur)[8]) {
     stage_chunk<FMT>(wl, lane, reg);
     *reinterpret_cast<float2*>(sl + 2 * lane) = nxt.da;
-    if (FMT == T_Q4_K) *reinterpret_cast<float2*>(sl + 128 + 2 * lane) = nxt.ca;
+    if (has_min_term<FMT>()) *reinterpret_cast<float2*>(sl + 128 + 2 * lane) = nxt.ca;
 #pragma unroll
     for (int bb = 0; bb < 8; bb++) acur[bb] = nxt.a[bb];
     wave_sync();
@@ -763,12 +792,17 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
 // alignment lose a quarter of the bandwidth, at 4-byte alignment nothing);
 // realign_chunk then shifts them down by 0 or 2 bytes.
 template <int FMT> struct DotFmt;
-// NWD = ceil(CB/4) dwords after the shift, plus the one the shift reads from.
+// NWD = ceil(CB/4) dwords after the shift, plus the one the shift reads from
+// (formats whose chunks are always 4-byte aligned need no shift).
 template <> struct DotFmt<T_Q8_0> { static constexpr int NWD = 69; };  // 272 B: 68 + 1
 template <> struct DotFmt<T_Q4_0> { static constexpr int NWD = 37; };  // 144 B: 36 + 1
 template <> struct DotFmt<T_Q5_0> { static constexpr int NWD = 45; };  // 176 B: 44 + 1
+template <> struct DotFmt<T_Q4_1> { static constexpr int NWD = 40; };  // 160 B, aligned
+template <> struct DotFmt<T_Q5_1> { static constexpr int NWD = 48; };  // 192 B, aligned
+template <> struct DotFmt<T_Q8_1> { static constexpr int NWD = 72; };  // 288 B, aligned
 template <> struct DotFmt<T_Q4_K> { static constexpr int NWD = 36; };  // 144 B, aligned
 template <> struct DotFmt<T_Q6_K> { static constexpr int NWD = 54; };  // 210 B: 53 + 1
+template <int FMT> constexpr bool chunk_aligned4() { return Fmt<FMT>::BB % 4 == 0; }
 
 template <int FMT>
 __device__ __forceinline__ void load_chunk_regs(const uint8_t* w, int64_t off, int64_t wbytes,
@@ -795,7 +829,7 @@ __device__ __forceinline__ void load_chunk_regs(const uint8_t* w, int64_t off, i
 template <int FMT>
 __device__ __forceinline__ void realign_chunk(int64_t off, uint32_t (&r)[DotFmt<FMT>::NWD]) {
     constexpr int NWD = DotFmt<FMT>::NWD;
-    if constexpr (FMT != T_Q4_K) {
+    if constexpr (!chunk_aligned4<FMT>()) {
         const uint32_t sh = (uint32_t)(off & 3);  // 0 or 2
 #pragma unroll
         for (int j = 0; j < NWD - 1; j++) r[j] = __builtin_amdgcn_alignbyte(r[j + 1], r[j], sh);
@@ -882,6 +916,60 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                 const int s16 = A[m].s16[b];
                 const int S = (int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16);
                 const float t = fmaf((float)(D - 8 * S), dw * A[m].da[b], p[m]);
+                p[m] = on ? t : p[m];
+            }
+        });
+    } else if constexpr (FMT == T_Q8_1) {
+        static_for<8>([&](auto BB) {
+            constexpr int bb = BB;
+            const bool on = bb < nbc;
+            const int b = 8 * c + bb;
+            const float dw = half_bits_to_float(half_at<36 * bb>(r));
+            uint32_t w[8];
+            static_for<8>([&](auto I) { w[I] = dw_at<36 * bb + 4 + 4 * I>(r); });
+#pragma unroll
+            for (int m = 0; m < B; m++) {
+                uint32_t a[8];
+                act_block(A[m], b, a);
+                int D = 0;
+#pragma unroll
+                for (int i = 0; i < 8; i++) D = dot4(w[i], a[i], D);
+                const float t = fmaf((float)D, dw * A[m].da[b], p[m]);
+                p[m] = on ? t : p[m];
+            }
+        });
+    } else if constexpr (FMT == T_Q4_1 || FMT == T_Q5_1) {
+        // d, m, [fifth bits,] nibbles; term P (d d_a) then + m (d_a S)
+        constexpr int BBY = Fmt<FMT>::BB, QS = FMT == T_Q4_1 ? 4 : 8;
+        static_for<8>([&](auto BB) {
+            constexpr int bb = BB;
+            const bool on = bb < nbc;
+            const int b = 8 * c + bb;
+            const float dw = half_bits_to_float(half_at<BBY * bb>(r));
+            const float mw = half_bits_to_float(half_at<BBY * bb + 2>(r));
+            uint32_t h = 0;
+            if constexpr (FMT == T_Q5_1) h = dw_at<BBY * bb + 4>(r);
+            uint32_t lo[4], hi[4];
+            static_for<4>([&](auto I) {
+                const uint32_t q = dw_at<BBY * bb + QS + 4 * I>(r);
+                lo[I] = q & 0x0F0F0F0Fu;
+                hi[I] = (q >> 4) & 0x0F0F0F0Fu;
+                if constexpr (FMT == T_Q5_1) {
+                    lo[I] |= spread4((h >> (4 * I)) & 15u);
+                    hi[I] |= spread4((h >> (16 + 4 * I)) & 15u);
+                }
+            });
+#pragma unroll
+            for (int m = 0; m < B; m++) {
+                uint32_t a[8];
+                act_block(A[m], b, a);
+                int D = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) D = dot4(lo[i], a[i], D);
+#pragma unroll
+                for (int i = 0; i < 4; i++) D = dot4(hi[i], a[4 + i], D);
+                float t = fmaf((float)D, dw * A[m].da[b], p[m]);
+                t = fmaf(mw, A[m].ca[b], t);
                 p[m] = on ? t : p[m];
             }
         });
@@ -1348,6 +1436,9 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
     case T_Q8_0: return launch_dot_rows<T_Q8_0>(jobs, rows, fused, blocks, shmem, s);
     case T_Q4_0: return launch_dot_rows<T_Q4_0>(jobs, rows, fused, blocks, shmem, s);
     case T_Q5_0: return launch_dot_rows<T_Q5_0>(jobs, rows, fused, blocks, shmem, s);
+    case T_Q4_1: return launch_dot_rows<T_Q4_1>(jobs, rows, fused, blocks, shmem, s);
+    case T_Q5_1: return launch_dot_rows<T_Q5_1>(jobs, rows, fused, blocks, shmem, s);
+    case T_Q8_1: return launch_dot_rows<T_Q8_1>(jobs, rows, fused, blocks, shmem, s);
     case T_Q4_K: return launch_dot_rows<T_Q4_K>(jobs, rows, fused, blocks, shmem, s);
     case T_Q6_K: return launch_dot_rows<T_Q6_K>(jobs, rows, fused, blocks, shmem, s);
     }
@@ -1456,6 +1547,9 @@ int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
     case T_Q8_0: return launch_qmv_t<T_Q8_0>(w, N, K, xq, rows, y, nullptr, s, false);
     case T_Q4_0: return launch_qmv_t<T_Q4_0>(w, N, K, xq, rows, y, nullptr, s, false);
     case T_Q5_0: return launch_qmv_t<T_Q5_0>(w, N, K, xq, rows, y, nullptr, s, false);
+    case T_Q4_1: return launch_qmv_t<T_Q4_1>(w, N, K, xq, rows, y, nullptr, s, false);
+    case T_Q5_1: return launch_qmv_t<T_Q5_1>(w, N, K, xq, rows, y, nullptr, s, false);
+    case T_Q8_1: return launch_qmv_t<T_Q8_1>(w, N, K, xq, rows, y, nullptr, s, false);
     case T_Q4_K: return launch_qmv_t<T_Q4_K>(w, N, K, xq, rows, y, nullptr, s, false);
     case T_Q6_K: return launch_qmv_t<T_Q6_K>(w, N, K, xq, rows, y, nullptr, s, false);
     }
@@ -1485,6 +1579,9 @@ int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* x
     case T_Q8_0: return launch_qmv_ni<T_Q8_0, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     case T_Q4_0: return launch_qmv_ni<T_Q4_0, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     case T_Q5_0: return launch_qmv_ni<T_Q5_0, 4>(w, N, K, xq, rows, nullptr, P, s, true);
+    case T_Q4_1: return launch_qmv_ni<T_Q4_1, 4>(w, N, K, xq, rows, nullptr, P, s, true);
+    case T_Q5_1: return launch_qmv_ni<T_Q5_1, 4>(w, N, K, xq, rows, nullptr, P, s, true);
+    case T_Q8_1: return launch_qmv_ni<T_Q8_1, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     case T_Q4_K: return launch_qmv_ni<T_Q4_K, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     case T_Q6_K: return launch_qmv_ni<T_Q6_K, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     }

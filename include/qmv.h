@@ -17,7 +17,8 @@
  * with I the exact integer dot product of the block's weight codes and
  * activation codes (Q4_0 codes offset by -8, Q5_0 codes by -16, Q6_K codes by
  * -32 and weighted by the 16-element sub-scale; Q4_K contributes
- * d*sc_j*sum(q*a) - dmin*m_j*sum(a)).
+ * d*sc_j*sum(q*a) - dmin*m_j*sum(a); Q4_1 and Q5_1, whose values are d*q + m,
+ * contribute d*sum(q*a) + m*sum(a); Q8_0 and Q8_1 d*sum(q*a)).
  *
  * Floating-point order (fixed, identical for every entry point, batch size
  * and launch shape, so that every row of a batched or prefill call is
@@ -29,13 +30,16 @@
  *   the last chunk may be shorter).  Each chunk sum starts at +0 and adds its
  *   blocks in ascending order, each block term added with ONE rounding to f32
  *   (an fma of the exact integer partial with the exact product of the two
- *   fp16 scales; Q4_K adds its +d and then its -dmin term).  Y is the chunk
- *   sums added in ascending order starting from +0.
+ *   fp16 scales; Q4_K adds its +d and then its -dmin term, Q4_1 / Q5_1 their
+ *   +d and then their +m term, m times the f32 product d_a * sum(a)).  Y is
+ *   the chunk sums added in ascending order starting from +0.
  *
  * Weight layout.  Row n of W occupies bytes [n*R, (n+1)*R) of w, R =
  * (K/QK)*block_bytes: Q8_0 (type 8) 32 elements / 34 bytes, Q4_0 (type 2)
- * 32 / 18, Q5_0 (type 6) 32 / 22, Q4_K (type 12) 256 / 144, Q6_K (type 14)
- * 256 / 210 — a GGUF 2-D tensor with K (ne0) contiguous.  The formats are
+ * 32 / 18, Q5_0 (type 6) 32 / 22, Q4_1 (type 3) 32 / 20, Q5_1 (type 7)
+ * 32 / 24, Q8_1 (type 9) 32 / 36 (its stored s = d*sum(q) is not read),
+ * Q4_K (type 12) 256 / 144, Q6_K (type 14) 256 / 210 — a GGUF 2-D tensor
+ * with K (ne0) contiguous.  The formats are
  * the ones the pages list ("Models and formats", section "Tensor formats");
  * the byte layouts are the GGUF block structures, which the pages do not
  * print.  Q5_0 is the format of most matrices in the pages' own Qwen2.5-0.5B
@@ -64,11 +68,14 @@ extern "C" {
 #endif
 
 /* GGUF tensor type ids. */
-enum qmv_type { QMV_Q4_0 = 2, QMV_Q5_0 = 6, QMV_Q8_0 = 8, QMV_Q4_K = 12, QMV_Q6_K = 14 };
+enum qmv_type {
+    QMV_Q4_0 = 2, QMV_Q4_1 = 3, QMV_Q5_0 = 6, QMV_Q5_1 = 7, QMV_Q8_0 = 8, QMV_Q8_1 = 9,
+    QMV_Q4_K = 12, QMV_Q6_K = 14
+};
 
 enum qmv_status {
     QMV_OK = 0,
-    QMV_EINVAL_TYPE = -1,        /* type is not Q4_0, Q5_0, Q8_0, Q4_K or Q6_K */
+    QMV_EINVAL_TYPE = -1,        /* type is not one of qmv_type */
     QMV_EINVAL_SHAPE = -2,       /* N, K, rows or batch out of range */
     QMV_EINVAL_PTR = -3,         /* NULL or misaligned pointer */
     QMV_ELAUNCH = -4,            /* the HIP launch failed */
@@ -151,7 +158,8 @@ int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, in
  * (MFMA) path.  xq must hold quantize_act_q8_0's Q8_0 blocks for B rows,
  * 1 <= B <= 16; the hook first rebuilds the private part of xq from them
  * (the Q8_0 blocks are not changed).  P layout [B][N][K/32] int32; for Q4_K
- * [B][N][K/32][2] = (sc_j * sum q*a, m_j * sum a). */
+ * [B][N][K/32][2] = (sc_j * sum q*a, m_j * sum a), for Q4_1 and Q5_1
+ * [B][N][K/32][2] = (sum q*a, sum a). */
 int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                         int64_t B, int32_t* P, void* stream);
 

@@ -204,6 +204,9 @@ WORKLOADS = {
     # attention q/o 896x896, k/v 128x896 (an inference)
     "q5_0_qwen": dict(mats=[(Q5_0, 4864, 896, 0.02), (Q5_0, 896, 896, 0.02),
                             (Q5_0, 128, 896, 0.02)], batches=[1, 16, 512]),
+    # the other 32-element formats the pages list, at the FFN gate shape
+    "fmt32_4864x896": dict(mats=[(Q4_1, 4864, 896, 0.02), (Q5_1, 4864, 896, 0.02),
+                                 (Q8_1, 4864, 896, 0.02)], batches=[1, 16, 512]),
 }
 
 

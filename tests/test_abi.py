@@ -43,10 +43,14 @@ FAKE = 1 << 20  # a 16-byte aligned non-NULL address; never dereferenced
 
 
 @pytest.mark.parametrize("args,code", [
-    ((3, FAKE, 16, 32, FAKE, 1, FAKE, FAKE), -1),            # unknown type
-    ((7, FAKE, 16, 32, FAKE, 1, FAKE, FAKE), -1),            # Q5_1: not (yet) accepted
+    ((4, FAKE, 16, 32, FAKE, 1, FAKE, FAKE), -1),            # unknown type (GGUF 4, 5: retired)
+    ((5, FAKE, 16, 32, FAKE, 1, FAKE, FAKE), -1),
+    ((10, FAKE, 16, 256, FAKE, 1, FAKE, FAKE), -1),          # Q2_K: not accepted
     ((g.Q5_0, FAKE, 16, 48, FAKE, 1, FAKE, FAKE), -2),       # Q5_0 accepted: K % 32
     ((g.Q5_0, FAKE + 8, 16, 32, FAKE, 1, FAKE, FAKE), -3),   # Q5_0 accepted: w misaligned
+    ((g.Q4_1, FAKE + 8, 16, 32, FAKE, 1, FAKE, FAKE), -3),   # Q4_1, Q5_1, Q8_1 accepted
+    ((g.Q5_1, FAKE + 8, 16, 32, FAKE, 1, FAKE, FAKE), -3),
+    ((g.Q8_1, FAKE, 16, 48, FAKE, 1, FAKE, FAKE), -2),
     ((g.Q8_0, FAKE, 16, 48, FAKE, 1, FAKE, FAKE), -2),       # K % 32
     ((g.Q4_K, FAKE, 16, 896, FAKE, 1, FAKE, FAKE), -2),      # K-quant K % 256
     ((g.Q6_K, FAKE, 16, 4864 + 32, FAKE, 1, FAKE, FAKE), -2),
@@ -72,7 +76,7 @@ def test_qmm_and_partials_refusals():
     assert L.qmm_launch(g.Q4_K, FAKE, 16, 512 + 32, FAKE, 4, FAKE, FAKE, None) == -2
     assert L.qmv_partials_launch(g.Q8_0, FAKE, 16, 32, FAKE, 17, FAKE, None) == -2
     assert L.qmv_partials_launch(g.Q8_0, FAKE, 16, 32, None, 1, FAKE, None) == -3
-    assert L.qmv_partials_launch(7, FAKE, 16, 32, FAKE, 1, FAKE, None) == -1
+    assert L.qmv_partials_launch(5, FAKE, 16, 32, FAKE, 1, FAKE, None) == -1
     assert L.quantize_act_q8_0(FAKE, FAKE, 1, 40, None) == -2
     assert L.quantize_act_q8_0(FAKE + 4, FAKE, 1, 32, None) == -3
 
@@ -82,7 +86,7 @@ def test_group_refusals():
     G = g.Gemv
     ok = G(16, 1, 32, 16, None, 16)
     arr = (G * 1)(ok)
-    assert L.qmv_launch_group(3, 1, arr, 1, None) == -1                    # type
+    assert L.qmv_launch_group(4, 1, arr, 1, None) == -1                    # type
     assert L.qmv_launch_group(8, 1, arr, 0, None) == -2                    # count
     assert L.qmv_launch_group(8, 1, arr, 9, None) == -2
     assert L.qmv_launch_group(8, 17, arr, 1, None) == -2                   # batch
@@ -96,10 +100,11 @@ def test_group_refusals():
 
 
 def test_strerror_names_what_works():
-    assert "Q4_0" in g.strerror(-1) and "Q6_K" in g.strerror(-1) and "Q5_0" in g.strerror(-1)
+    assert all(t in g.strerror(-1) for t in ("Q4_0", "Q4_1", "Q5_0", "Q5_1", "Q8_0", "Q8_1",
+                                              "Q4_K", "Q6_K"))
     assert "K % 256" in g.strerror(-2) and "qmm_launch" in g.strerror(-2)
     assert "gfx950" in g.strerror(-5)
     assert g.strerror(0) == "ok" and "unknown" in g.strerror(-99)
     with pytest.raises(g.QmvError) as e:
-        g.qmv_launch(3, FAKE, 16, 32, FAKE, 1, FAKE, FAKE, 0)
+        g.qmv_launch(4, FAKE, 16, 32, FAKE, 1, FAKE, FAKE, 0)
     assert e.value.code == -1

@@ -51,6 +51,8 @@ SMALL = [
     (synth.Q4_K, 45, 1024), (synth.Q4_K, 16, 256), (synth.Q4_K, 7, 4864),
     (synth.Q6_K, 33, 768), (synth.Q6_K, 16, 256), (synth.Q6_K, 19, 1024),
     (synth.Q5_0, 45, 896), (synth.Q5_0, 16, 32), (synth.Q5_0, 33, 4096 + 96),
+    (synth.Q4_1, 45, 896), (synth.Q4_1, 17, 32), (synth.Q5_1, 33, 4096 + 96),
+    (synth.Q5_1, 16, 416), (synth.Q8_1, 40, 896), (synth.Q8_1, 19, 64),
 ]
 
 
@@ -108,7 +110,8 @@ def test_batch_rows_equal_batch1(g, fmt, N, K):
     assert_bitwise(yp, y16[perm], "permuted batch")
 
 
-@pytest.mark.parametrize("fmt,N,K", [SMALL[0], SMALL[4], SMALL[6], SMALL[9], SMALL[12]])
+@pytest.mark.parametrize("fmt,N,K", [SMALL[0], SMALL[4], SMALL[6], SMALL[9], SMALL[12],
+                                     SMALL[15], SMALL[17], SMALL[19]])
 @pytest.mark.parametrize("M", [17, 40])
 def test_qmm_rows_equal_qmv(g, fmt, N, K, M):
     blob, x = _inputs(fmt, N, K, M, 400 + N)
@@ -131,6 +134,8 @@ GEMM = [
     (synth.Q4_K, 200, 1024, 150, None), (synth.Q6_K, 140, 768, 131, (-128, 127)),
     (synth.Q6_K, 140, 768, 131, (-32, 31)), (synth.Q6_K, 260, 1024, 257, "mixed"),
     (synth.Q5_0, 150, 896, 140, None), (synth.Q5_0, 129, 4192, 129, None),
+    (synth.Q4_1, 150, 896, 140, None), (synth.Q5_1, 129, 4192, 129, None),
+    (synth.Q8_1, 131, 416, 150, None),
 ]
 
 
@@ -156,7 +161,8 @@ def test_gemm_tiles_against_oracle(g, fmt, N, K, M, srange):
         assert_bitwise(y[m], y1[0], f"gemm row {m} vs qmv")
 
 
-@pytest.mark.parametrize("fmt,N,K", [SMALL[1], SMALL[5], SMALL[7], SMALL[10], SMALL[13]])
+@pytest.mark.parametrize("fmt,N,K", [SMALL[1], SMALL[5], SMALL[7], SMALL[10], SMALL[13],
+                                     SMALL[16], SMALL[18], SMALL[20]])
 def test_staged_xq_paths(g, fmt, N, K):
     """x = NULL uses xq as staged; quantize with x = NULL re-stages Q8_0 blocks
     written by someone else (here the oracle) over a scribbled staging area."""
@@ -179,7 +185,8 @@ def test_staged_xq_paths(g, fmt, N, K):
     assert_bitwise(host(g.matmul(fmt, w, N, K, xq=xq2, M=B)), y_ref, "qmm x=NULL vs qmv")
 
 
-@pytest.mark.parametrize("fmt,N,K", [SMALL[0], SMALL[4], SMALL[8], SMALL[11], SMALL[14]])
+@pytest.mark.parametrize("fmt,N,K", [SMALL[0], SMALL[4], SMALL[8], SMALL[11], SMALL[14],
+                                     SMALL[15], SMALL[17], SMALL[19]])
 @pytest.mark.parametrize("B", [1, 3, 4, 5])
 def test_fused_quantisation_leaves_xq_as_quantize(g, fmt, N, K, B):
     """qmv with x quantises inside the GEMV for B <= 4: xq must then hold the
@@ -257,14 +264,17 @@ def test_byte_coverage(g):
     assert not unchanged, f"bytes with no effect: {unchanged[:10]}"
 
 
+@pytest.mark.parametrize("fmt", [synth.Q5_0, synth.Q4_1, synth.Q5_1])
 @pytest.mark.parametrize("B", [1, 5])
-def test_byte_coverage_q5_0(g, B):
-    """Q5_0: flipping bit 0 or bit 4 of any byte (scale, fifth-bit word or
+def test_byte_coverage_32(g, fmt, B):
+    """Flipping bit 0 or bit 4 of any byte (scale, minimum, fifth-bit word or
     nibbles; each flip moves exactly one field) changes the output, through
     the lane-per-chunk path (B = 1) and the MFMA path (B = 5)."""
-    fmt, N, K = synth.Q5_0, 2, 64
+    N, K = 2, 64
     f = synth.draw_fields(fmt, N, K, 960)
     f["d"] = np.maximum(f["d"], np.float16(1e-2))
+    if "m" in f:
+        f["m"] = np.minimum(f["m"], np.float16(-1e-2))
     blob = synth.encode(f)
     x = np.abs(synth.activations(B, K, 961)) + np.float32(0.5)   # codes all >= 1
     xd = dev(x)
@@ -285,6 +295,9 @@ def test_byte_coverage_q5_0(g, B):
     (synth.Q6_K, [(33, 768), (19, 1024)]),
     (synth.Q8_0, [(100, 896), (16, 32), (33, 4192), (17, 64), (5, 32), (70, 416), (9, 96), (40, 4096)]),
     (synth.Q5_0, [(4864, 896), (896, 896), (128, 896)]),
+    (synth.Q4_1, [(300, 896), (45, 4864)]),
+    (synth.Q5_1, [(300, 896), (45, 4864)]),
+    (synth.Q8_1, [(100, 896), (33, 4192)]),
 ])
 @pytest.mark.parametrize("B", [1, 3, 5])
 def test_group_equals_single_launches(g, fmt, shapes, B):
@@ -314,7 +327,8 @@ def test_group_equals_single_launches(g, fmt, shapes, B):
         assert_bitwise(host(ys2[k]), ref[k], f"staged group entry {k}")
 
 
-@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0, synth.Q4_K, synth.Q6_K, synth.Q5_0])
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0, synth.Q4_K, synth.Q6_K, synth.Q5_0,
+                                 synth.Q4_1, synth.Q5_1, synth.Q8_1])
 @pytest.mark.parametrize("fused", [False, True])
 def test_large_gemv_persistent(g, fmt, fused):
     """Batch 1 over 24613 rows (more than 6144 work units of 4 rows: the
