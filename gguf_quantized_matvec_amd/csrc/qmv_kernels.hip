@@ -1085,18 +1085,19 @@ constexpr int MAX_JOBS = 8;
 struct DotJobs {
     int first[MAX_JOBS];  // job k owns workgroups [first[k], first[k+1])
     int count;
+    int waves;            // waves per workgroup (4 or 8), as launched
     DotJob j[MAX_JOBS];
 };
 
 // Work units: C <= 64 chunks per row: a unit is G = 64/LPR rows (LPR = lanes
 // per row, a power of two >= C), one chunk per lane; C > 64: a unit is one
 // row, in passes of 64 chunks.  Every wave takes one unit; a workgroup is 4
-// waves sharing the activation rows staged in LDS.  Each lane streams its
+// (or 8) waves sharing the activation rows staged in LDS.  Each lane streams its
 // chunk straight into registers, issued before the activations are staged.
 // Chunk sums are added in chunk order per row through a small LDS buffer,
 // and each row's result is stored once, at the end.
 template <int FMT, int B, bool FUSED, bool SINGLE>
-__global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
+__global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     using F = Fmt<FMT>;
     constexpr int NWD = DotFmt<FMT>::NWD;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -1128,7 +1129,7 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
     const int LPR = 1 << lg, G = 64 >> lg;
     const int PR = (C + 63) >> 6;  // passes (1 unless C > 64)
     const int64_t units = C <= 64 ? (N + G - 1) >> (6 - lg) : N;
-    const int64_t u = (int64_t)((int)blockIdx.x - first_block) * 4 + wv;
+    const int64_t u = (int64_t)((int)blockIdx.x - first_block) * jobs.waves + wv;
     const bool active = u < units;
 
     auto chunk_of = [&](int q, int64_t& row, int& c) {
@@ -1358,17 +1359,19 @@ __global__ __launch_bounds__(256) void k_dot(DotJobs jobs) {
 }
 
 // Workgroups of the dot kernel for one GEMV: one wave per unit, 4 per group.
-inline int64_t dot_blocks(int type, int64_t N, int64_t K) {
+inline int64_t dot_blocks(int type, int64_t N, int64_t K, int waves) {
     const int nb = (int)(K / 32), C = (nb + 7) / 8;
     int LPR = 1;
     while (LPR < C && LPR < 64) LPR <<= 1;
     const int64_t G = 64 / LPR;
     (void)type;
     const int64_t units = C <= 64 ? (N + G - 1) / G : N;
-    return (units + 3) / 4;
+    return (units + waves - 1) / waves;
 }
 
-inline size_t dot_shmem(int B, int64_t K) { return (size_t)B * act_lds_row_bytes(K) + 4 * B * 256; }
+inline size_t dot_shmem(int B, int64_t K, int waves) {
+    return (size_t)B * act_lds_row_bytes(K) + (size_t)waves * B * 256;
+}
 
 template <int FMT, int B, bool FUSED, bool SINGLE>
 int launch_dot_kernel(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
@@ -1378,7 +1381,7 @@ int launch_dot_kernel(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStre
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, SINGLE>), dim3((unsigned)blocks), dim3(256), shmem,
+    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, SINGLE>), dim3((unsigned)blocks), dim3(64 * jobs.waves), shmem,
                        s, jobs);
     return (int)hipGetLastError();
 }
@@ -1412,6 +1415,12 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
     int64_t blocks = 0;
     size_t shmem = 0;
     const bool fused = d[0].x != nullptr;
+    // 4-wave workgroups, unless that grid would just overrun the 256 CUs:
+    // then 8-wave workgroups fit the same waves in one round of workgroups
+    // (one per CU) instead of leaving a second round for a few CUs.
+    int64_t blocks4 = 0;
+    for (int k = 0; k < count; k++) blocks4 += dot_blocks(type, d[k].N, d[k].K, 4);
+    jobs.waves = blocks4 > 256 && blocks4 <= 512 ? 8 : 4;
     for (int k = 0; k < count; k++) {
         const ActLayout L = act_layout(rows, d[k].K);
         DotJob& J = jobs.j[k];
@@ -1427,8 +1436,8 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
         J.rca = L.rca;
         J.rs16 = L.rs16;
         jobs.first[k] = (int)blocks;
-        blocks += dot_blocks(type, d[k].N, d[k].K);
-        const size_t sh = dot_shmem((int)rows, d[k].K);
+        blocks += dot_blocks(type, d[k].N, d[k].K, jobs.waves);
+        const size_t sh = dot_shmem((int)rows, d[k].K, jobs.waves);
         shmem = sh > shmem ? sh : shmem;
     }
     if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
@@ -1497,7 +1506,7 @@ int launch_qmv_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int6
 // The lane-per-chunk kernel takes up to DOT_MAX_ROWS rows whose activations fit
 // in a workgroup's LDS; everything else up to 16 rows runs on MFMA.
 bool use_dot(int64_t rows, int64_t K) {
-    return rows <= DOT_MAX_ROWS && rows * act_lds_row_bytes(K) + 4 * rows * 256 <= DOT_MAX_ACT_LDS;
+    return rows <= DOT_MAX_ROWS && rows * act_lds_row_bytes(K) + 8 * rows * 256 <= DOT_MAX_ACT_LDS;
 }
 
 }  // namespace
@@ -1530,7 +1539,7 @@ int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
         // quantisation fused into the kernel when x is given, unless the
         // workgroups' re-reads of x would exceed the weight bytes: then one
         // quantise launch first
-        if (x && dot_blocks(type, N, K) * rows * K * 4 > N * row_bytes(type, K)) {
+        if (x && dot_blocks(type, N, K, 4) * rows * K * 4 > N * row_bytes(type, K)) {
             const int rc = launch_quantize(x, xq, rows, K, ST_ROW, s);
             if (rc) return rc;
             x = nullptr;
