@@ -330,9 +330,9 @@ def test_group_equals_single_launches(g, fmt, shapes, B):
 @pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0, synth.Q4_K, synth.Q6_K, synth.Q5_0,
                                  synth.Q4_1, synth.Q5_1, synth.Q8_1])
 @pytest.mark.parametrize("fused", [False, True])
-def test_large_gemv_persistent(g, fmt, fused):
-    """Batch 1 over 24613 rows (more than 6144 work units of 4 rows: the
-    persistent, double-buffered schedule), ragged last unit, against the
+def test_large_gemv_many_workgroups(g, fmt, fused):
+    """Batch 1 over 24613 rows: more workgroups than the chip holds at once,
+    a ragged last unit, with the quantisation fused and staged, against the
     documented f32 order."""
     N, K = 24613, 4096
     blob, x = _inputs(fmt, N, K, 1, 950 + fmt)
