@@ -55,7 +55,6 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int TM = 128, TN = 128;   // workgroup tile
 constexpr int SB = 4;               // 32-element blocks per K step
 constexpr int PR = 4 * SB;          // 16-byte pieces per tile row per step
 constexpr int NA = 2;               // activation steps resident in LDS (1 in flight)
@@ -287,36 +286,43 @@ __device__ __forceinline__ void tile_of(int64_t wg, int64_t tilesM, int64_t tile
 // The scale products run as rank-1 MFMAs whose operands are read ready-made:
 // ra[b][r] = (d_a, 0, ..., 0) for activation row r (row TM is all zero, for
 // the lanes that hold k = 8..15), rw[b][r] = d_w in all 8 halves.
-struct Smem {
-    uint4 w[TN * PR];      // decoded weights (f16)
-    uint4 ra[SB][TM + 1];  // rank-1 A operands (fp16 d_a at k = 0)
-    uint4 rw[SB][TN];      // rank-1 B operands (fp16 d_w broadcast)
-    float ca[SB][TM];      // Q4_K: d_a * S (S = the block's code sum)
-    uint32_t x1[SB][TN];   // see WScale::x1
+// T = TM = TN: the workgroup tile.
+template <int T> struct Smem {
+    uint4 w[T * PR];      // decoded weights (f16)
+    uint4 ra[SB][T + 1];  // rank-1 A operands (fp16 d_a at k = 0)
+    uint4 rw[SB][T];      // rank-1 B operands (fp16 d_w broadcast)
+    float ca[SB][T];      // Q4_K: d_a * S (S = the block's code sum)
+    uint32_t x1[SB][T];   // see WScale::x1
 };
 __device__ __forceinline__ int slot(int row, int q) { return row * PR + (q ^ (row & 15)); }
 
-// The activation ring (f16 codes of NA = 2 steps) lives in two separate LDS
-// objects: while the next step is copied into one by global_load_lds, the
-// multiply reads the other, and the compiler, seeing two objects, does not
-// make those reads wait for the copy in flight (with one object it must).
-__shared__ uint4 lds_a0[TM * PR];
-__shared__ uint4 lds_a1[TM * PR];
-__shared__ Smem lds_rest;
-template <int P> __device__ __forceinline__ uint4* a_buf() {
-    if constexpr (P == 0) return lds_a0;
-    else return lds_a1;
-}
 using Even = std::integral_constant<int, 0>;
 using Odd = std::integral_constant<int, 1>;
 
-template <int FMT>
-__global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int64_t N, int64_t K,
-                                              const uint8_t* __restrict__ xq, ActLayout L,
-                                              int64_t M, int64_t tilesM, int64_t tilesN,
-                                              float* __restrict__ y) {
+// NW waves per workgroup: NW = 8 owns 128 x 128 outputs (each wave 64 x 32,
+// two MFMA tiles), NW = 4 owns 64 x 64 (each wave one 32 x 32 tile) for
+// grids that would not fill the chip with the larger tile.
+template <int FMT, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm(const uint8_t* __restrict__ w, int64_t N, int64_t K,
+                                                  const uint8_t* __restrict__ xq, ActLayout L,
+                                                  int64_t M, int64_t tilesM, int64_t tilesN,
+                                                  float* __restrict__ y) {
     using F = GFmt<FMT>;
-    Smem* const sm = &lds_rest;
+    constexpr int TM = 16 * NW, TN = 16 * NW;  // workgroup tile
+    constexpr int WT = NW / 4;                 // 32 x 32 MFMA tiles per wave (along M)
+    // The activation ring (f16 codes of NA = 2 steps) lives in two separate
+    // LDS objects: while the next step is copied into one by global_load_lds,
+    // the multiply reads the other, and the compiler, seeing two objects,
+    // does not make those reads wait for the copy in flight (with one object
+    // it must).
+    __shared__ uint4 lds_a0[TM * PR];
+    __shared__ uint4 lds_a1[TM * PR];
+    __shared__ Smem<TM> lds_rest;
+    Smem<TM>* const sm = &lds_rest;
+    auto a_buf = [&](auto par) -> uint4* {
+        if constexpr (decltype(par)::value == 0) return lds_a0;
+        else return lds_a1;
+    };
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wm = wv & 1, wn = wv >> 1;
     int64_t tm, tn;
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
                 if (blk >= nb) src -= (int64_t)(blk - (nb - 1)) * 64;
             }
             __builtin_amdgcn_global_load_lds(
-                src, (lds_void*)(a_buf<decltype(par)::value>() + (16 * wv + 4 * i) * PR), 16, 0, 0);
+                src, (lds_void*)(a_buf(par) + (16 * wv + 4 * i) * PR), 16, 0, 0);
         }
     };
 
@@ -385,17 +391,17 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
     };
 
     // accumulators of tile i: chunk sum p and running sum yv
-    v16f p[2], yv[2];
+    v16f p[WT], yv[WT];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < WT; i++)
 #pragma unroll
         for (int e = 0; e < 16; e++) p[i][e] = yv[i][e] = 0.0f;
 
     const int lr = lane & 31, kq = lane >> 5;  // MFMA lane roles
     const v16f zero16 = {};
-    // fragment slots: A rows 64wm + 32i + lr, B rows 32wn + lr; piece
+    // fragment slots: A rows 32 WT wm + 32i + lr, B rows 32wn + lr; piece
     // 4*bk + 2hh + kq holds k = 16hh + 8kq .. +8 of block bk
-    const int arow0 = 64 * wm + lr, brow = 32 * wn + lr;
+    const int arow0 = 32 * WT * wm + lr, brow = 32 * wn + lr;
 
     // step h reads activation buffer P = h % 2 and fills the other
     auto step = [&](int h, Raw& r, auto par) {
@@ -433,7 +439,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
             issue_a(h + 1, std::integral_constant<int, 1 - P>{});  // in flight while step h is multiplied
             fetch(h + 1, r);
         }
-        const uint4* A = a_buf<P>();
+        const uint4* A = a_buf(par);
         // the multiply of one step; UNF: Q6_K codes were staged without their
         // sub-scales (a scale that cannot be folded exactly occurs in the step)
         auto multiply = [&](auto unf_tag) {
@@ -441,11 +447,11 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
 #pragma unroll
             for (int bk = 0; bk < SB; bk++) {
                 if (bk < nbh) {
-                    v8h Af[2][2], Bf[2], Ra[2], Rw;
+                    v8h Af[WT][2], Bf[2], Ra[WT], Rw;
 #pragma unroll
                     for (int hh = 0; hh < 2; hh++) {
 #pragma unroll
-                        for (int i = 0; i < 2; i++) {
+                        for (int i = 0; i < WT; i++) {
                             const uint4 va = A[slot(arow0 + 32 * i, 4 * bk + 2 * hh + kq)];
                             __builtin_memcpy(&Af[i][hh], &va, 16);
                         }
@@ -453,16 +459,17 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
                         __builtin_memcpy(&Bf[hh], &vb, 16);
                     }
                     {
-                        const uint4 r0 = sm->ra[bk][kq ? TM : arow0];
-                        const uint4 r1 = sm->ra[bk][kq ? TM : arow0 + 32];
+#pragma unroll
+                        for (int i = 0; i < WT; i++) {
+                            const uint4 ri = sm->ra[bk][kq ? TM : arow0 + 32 * i];
+                            __builtin_memcpy(&Ra[i], &ri, 16);
+                        }
                         const uint4 rb = sm->rw[bk][brow];
-                        __builtin_memcpy(&Ra[0], &r0, 16);
-                        __builtin_memcpy(&Ra[1], &r1, 16);
                         __builtin_memcpy(&Rw, &rb, 16);
                     }
                     const uint32_t x1 = (has_min_term<FMT>() || FMT == T_Q6_K) ? sm->x1[bk][brow] : 0u;
 #pragma unroll
-                    for (int i = 0; i < 2; i++) {
+                    for (int i = 0; i < WT; i++) {
                         const v16f S = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ra[i], Rw, zero16, 0, 0, 0);
                         if constexpr (FMT == T_Q6_K && UNF) {
                             const v16f I0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i][0], Bf[0], zero16, 0, 0, 0);
@@ -481,7 +488,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
                             if constexpr (has_min_term<FMT>()) {
                                 // element e of the lane is row 8(e/4) + 4kq + e%4 of the tile
                                 const float nX = -__uint_as_float(x1);
-                                const float* cr = &sm->ca[bk][64 * wm + 32 * i + 4 * kq];
+                                const float* cr = &sm->ca[bk][32 * WT * wm + 32 * i + 4 * kq];
 #pragma unroll
                                 for (int g = 0; g < 4; g++) {
                                     const float4 c4 = *reinterpret_cast<const float4*>(cr + 8 * g);
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
         // end of a 256-element chunk (two steps) or of K: add it, in chunk order
         if ((h & 1) || h + 1 == H) {
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int i = 0; i < WT; i++)
 #pragma unroll
                 for (int e = 0; e < 16; e++) {
                     yv[i][e] = yv[i][e] + p[i][e];
@@ -523,21 +530,32 @@ __global__ __launch_bounds__(512) void k_gemm(const uint8_t* __restrict__ w, int
     // lane l, element e of tile i: row 8(e/4) + 4kq + e%4, column lr
     const int64_t n = n0 + 32 * wn + lr;
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < WT; i++)
 #pragma unroll
         for (int e = 0; e < 16; e++) {
-            const int64_t m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * kq + (e & 3);
+            const int64_t m = m0 + 32 * WT * wm + 32 * i + 8 * (e >> 2) + 4 * kq + (e & 3);
             if (m < M && n < N) y[m * N + n] = yv[i][e];
         }
 }
 
+// Workgroups of 128 x 128 outputs, unless so few of them cover the output
+// that half the 256 CUs or more would idle: then 64 x 64 tiles (four times
+// the workgroups; measured slower per output than the larger tile, faster
+// when the larger one leaves most of the chip empty).
 template <int FMT>
 int launch_gemm_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
                   float* y, hipStream_t s) {
     const ActLayout L = act_layout(M, K);
-    const int64_t tilesM = (M + TM - 1) / TM, tilesN = (N + TN - 1) / TN;
-    hipLaunchKernelGGL((k_gemm<FMT>), dim3((unsigned)(tilesM * tilesN)), dim3(512), 0,
-                       s, w, N, K, xq, L, M, tilesM, tilesN, y);
+    int64_t tilesM = (M + 127) / 128, tilesN = (N + 127) / 128;
+    if (tilesM * tilesN > 128) {
+        hipLaunchKernelGGL((k_gemm<FMT, 8>), dim3((unsigned)(tilesM * tilesN)), dim3(512), 0,
+                           s, w, N, K, xq, L, M, tilesM, tilesN, y);
+    } else {
+        tilesM = (M + 63) / 64;
+        tilesN = (N + 63) / 64;
+        hipLaunchKernelGGL((k_gemm<FMT, 4>), dim3((unsigned)(tilesM * tilesN)), dim3(256), 0,
+                           s, w, N, K, xq, L, M, tilesM, tilesN, y);
+    }
     return (int)hipGetLastError();
 }
 

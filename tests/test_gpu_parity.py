@@ -124,7 +124,7 @@ def test_qmm_rows_equal_qmv(g, fmt, N, K, M):
         assert_bitwise(y[m], y1[0], f"qmm row {m} vs qmv")
 
 
-# Prefill GEMM over several 128 x 128 workgroup tiles with ragged edges in M
+# Prefill GEMM over several workgroup tiles with ragged edges in M
 # and N, and a ragged last K step (K = 416: 13 blocks).  Q6_K also with the
 # sub-scale range of the workloads ([-32, 31], folded into f16 codes) and with
 # a few rows whose odd sub-scales beyond +-64 force the unfolded path in
@@ -157,6 +157,37 @@ def test_gemm_tiles_against_oracle(g, fmt, N, K, M, srange):
     assert_tol(y, y64, A, what="gemm vs f64")
     assert_bitwise(y, oracle.matmul_canon_f32(fmt, blob, N, K, xq, M), "gemm vs f32 order")
     for m in (0, 127, 128, M - 1):
+        y1 = host(g.matvec(fmt, w, N, K, x=dev(x[m:m + 1])))
+        assert_bitwise(y[m], y1[0], f"gemm row {m} vs qmv")
+
+
+# The shapes above launch at most 128 tiles of 128 x 128 and run the 64 x 64
+# workgroup tile; this grid (17 x 16 tiles of 128, ragged in M, N and K) runs
+# the 128 x 128 one, for every format and for Q6_K steps staged unfolded.  Sampled tokens are checked against the oracle on every row.
+@pytest.mark.parametrize("fmt,srange", [(synth.Q8_0, None), (synth.Q4_0, None), (synth.Q5_0, None),
+                                        (synth.Q4_1, None), (synth.Q5_1, None), (synth.Q8_1, None),
+                                        (synth.Q4_K, None), (synth.Q6_K, None), (synth.Q6_K, "mixed")])
+def test_gemm_large_tile_grid(g, fmt, srange):
+    M, N = 2067, 1921
+    K = 768 if fmt in (synth.Q4_K, synth.Q6_K) else 416
+    seed = 1700 + fmt
+    if srange == "mixed":
+        f = synth.draw_fields(fmt, N, K, seed, s_range=(-32, 31))
+        f["s"][7, 0, 5] = 101      # odd, beyond +-64
+        f["s"][1900, 2, 14] = -77
+        blob = synth.encode(f)
+    else:
+        blob, _ = synth.weights(fmt, N, K, seed)
+    x = synth.activations(M, K, seed + 7)
+    w = dev(blob)
+    y = host(g.matmul(fmt, w, N, K, x=dev(x)))
+    toks = np.array([0, 1, 63, 64, 127, 128, 1000, 2047, 2048, M - 1])
+    xq = oracle.quantize_act(x[toks])
+    y64, A = oracle.matmul_f64(fmt, blob, N, K, xq, len(toks))
+    assert_tol(y[toks], y64, A, what="gemm vs f64")
+    assert_bitwise(y[toks], oracle.matmul_canon_f32(fmt, blob, N, K, xq, len(toks)),
+                   "gemm vs f32 order")
+    for m in (0, 128, M - 1):
         y1 = host(g.matvec(fmt, w, N, K, x=dev(x[m:m + 1])))
         assert_bitwise(y[m], y1[0], f"gemm row {m} vs qmv")
 
