@@ -1078,12 +1078,12 @@ struct DotJob {
     int64_t rcodes, rda, rca, rs16;  // offsets of the row-major staging in xq
 };
 constexpr int MAX_JOBS = 8;
-// The first workgroups of all jobs come first, so that a workgroup of a group
-// finds its job with one scalar load and compares, then loads that job's
-// fields once: every dependent kernel-argument load (about half a
-// microsecond each, measured) sits at the head of every wave's critical path.
+// A grouped launch is a 2-D grid: row y of workgroups is job y (as many
+// workgroups as the largest job needs; the surplus ones of smaller jobs
+// exit at once), so a workgroup loads its job's fields with one dependent
+// kernel-argument load, which sits at the head of every wave's critical
+// path (about half a microsecond each, measured).
 struct DotJobs {
-    int first[MAX_JOBS];  // job k owns workgroups [first[k], first[k+1])
     int count;
     int waves;            // waves per workgroup (4 or 8), as launched
     DotJob j[MAX_JOBS];
@@ -1101,21 +1101,12 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     using F = Fmt<FMT>;
     constexpr int NWD = DotFmt<FMT>::NWD;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    // this workgroup's job: a single GEMV reads its fields directly (one
-    // round trip); a group finds its job in the table head, then loads it
+    // this workgroup's job (one kernel-argument round trip)
     DotJob J;
-    int first_block = 0;
     if constexpr (SINGLE) {
         J = jobs.j[0];
     } else {
-        int job = 0;
-#pragma unroll
-        for (int k = 1; k < MAX_JOBS; k++) {
-            const bool mine = k < jobs.count && (int)blockIdx.x >= jobs.first[k];
-            job = mine ? k : job;
-            first_block = mine ? jobs.first[k] : first_block;
-        }
-        J = jobs.j[job];
+        J = jobs.j[blockIdx.y];
     }
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int64_t N = J.N, K = J.K;
@@ -1129,7 +1120,8 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     const int LPR = 1 << lg, G = 64 >> lg;
     const int PR = (C + 63) >> 6;  // passes (1 unless C > 64)
     const int64_t units = C <= 64 ? (N + G - 1) >> (6 - lg) : N;
-    const int64_t u = (int64_t)((int)blockIdx.x - first_block) * jobs.waves + wv;
+    if ((int64_t)blockIdx.x * jobs.waves >= units) return;  // surplus workgroup of a smaller job
+    const int64_t u = (int64_t)blockIdx.x * jobs.waves + wv;
     const bool active = u < units;
 
     auto chunk_of = [&](int q, int64_t& row, int& c) {
@@ -1198,7 +1190,7 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     if constexpr (FUSED) {
         // four lanes per block, 8 elements each: the block's amax and code
         // sums by lane shuffles, then the same d, id and codes as k_quantize
-        const bool writer = (int)blockIdx.x == first_block && J.xq != nullptr;
+        const bool writer = blockIdx.x == 0 && J.xq != nullptr;
         const float* x = J.x;
         uint8_t* xq = J.xq;
         const int total = 4 * B * nb;  // (block, quarter) tasks; whole blocks stay in one pass
@@ -1381,8 +1373,8 @@ int launch_dot_kernel(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStre
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, SINGLE>), dim3((unsigned)blocks), dim3(64 * jobs.waves), shmem,
-                       s, jobs);
+    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, SINGLE>), dim3((unsigned)blocks, (unsigned)jobs.count),
+                       dim3(64 * jobs.waves), shmem, s, jobs);
     return (int)hipGetLastError();
 }
 
@@ -1435,8 +1427,8 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
         J.rda = L.rda;
         J.rca = L.rca;
         J.rs16 = L.rs16;
-        jobs.first[k] = (int)blocks;
-        blocks += dot_blocks(type, d[k].N, d[k].K, jobs.waves);
+        const int64_t bk = dot_blocks(type, d[k].N, d[k].K, jobs.waves);
+        blocks = bk > blocks ? bk : blocks;  // grid x: the largest job
         const size_t sh = dot_shmem((int)rows, d[k].K, jobs.waves);
         shmem = sh > shmem ? sh : shmem;
     }
