@@ -22,6 +22,7 @@ runs on), the CPU oracle timed on a bounded sample of the same step, and
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--suite]
 
 Counter collection helpers: --profile-steps N (eager steps only),
+--profile-matrix WORKLOAD:INDEX:ROWS (one workload matrix, eagerly),
 --copy-calib (a 256 MiB copy, the counters' byte calibration) and
 --traffic-from DIR (turns their rocprofv3 --pmc output into
 profiles/traffic.json).
@@ -245,6 +246,30 @@ def suite(torch, g, synth, rotate_bytes):
     return res
 
 
+def profile_matrix(torch, g, synth, spec, launches=20):
+    """Launch one workload matrix (the suite's seeded weights, activations
+    staged by quantize_act_q8_0) `launches` times back to back, eagerly."""
+    wl, mi, rows = spec.split(":")
+    mi, rows = int(mi), int(rows)
+    ci = list(synth.WORKLOADS).index(wl)
+    fmt, N, K, ds = synth.WORKLOADS[wl]["mats"][mi]
+    blob, _ = synth.weights(fmt, N, K, synth.seed_for(ci, mi), dscale=ds)
+    w = torch.from_numpy(blob).cuda()
+    x = torch.from_numpy(synth.activations(rows, K, synth.act_seed_for(ci, rows))).cuda()
+    xq = g.quantize(x)
+    y = torch.empty(rows, N, dtype=torch.float32, device="cuda")
+    L = g.lib()
+    fn = L.qmv_launch if rows <= 16 else L.qmm_launch
+    for _ in range(launches):
+        rc = fn(fmt, w.data_ptr(), N, K, None, rows, xq.data_ptr(), y.data_ptr(),
+                torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise g.QmvError(rc, "profile_matrix")
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_matrix": spec, "fmt": synth.NAMES[fmt], "N": N, "K": K,
+                      "rows": rows, "launches": launches}))
+
+
 def traffic_from(pmc_dir):
     """profiles/traffic.json from four rocprofv3 --pmc runs under pmc_dir:
     fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of `bench.py --profile-steps`),
@@ -300,6 +325,9 @@ def main():
                     help="write profiles/traffic.json from rocprofv3 --pmc output under DIR")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 256 MiB device copy 10 times (counter calibration)")
+    ap.add_argument("--profile-matrix", default=None, metavar="WORKLOAD:INDEX:ROWS",
+                    help="only launch one workload matrix (e.g. 8b_class:2:2048) 20 times, "
+                         "eagerly (for counter collection)")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -332,6 +360,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes": a.numel(), "launches": 10}))
+        return
+
+    if args.profile_matrix:
+        profile_matrix(torch, g, synth, args.profile_matrix)
         return
 
     W = ffn_workload(torch, g, synth, args.rotate_mib << 20)
