@@ -329,6 +329,9 @@ def test_byte_coverage_32(g, fmt, B):
     (synth.Q4_1, [(300, 896), (45, 4864)]),
     (synth.Q5_1, [(300, 896), (45, 4864)]),
     (synth.Q8_1, [(100, 896), (33, 4192)]),
+    # one large GEMV between two tiny ones: most workgroup rows of the grid
+    # belong to no work and exit
+    (synth.Q4_0, [(8, 32), (20000, 896), (3, 4864)]),
 ])
 @pytest.mark.parametrize("B", [1, 3, 5])
 def test_group_equals_single_launches(g, fmt, shapes, B):
