@@ -15,9 +15,11 @@ HIP graph (the path is launch-bound at this size).
 
 Prints ONE JSON line: metric/value (weight GB/s of the timed steps, wall
 clock), the roofline of the dominant kernel (the GEMV; execution times from
-HIP events that each kernel records at its own start and end on the stream it
-runs on), the CPU oracle timed on a bounded sample of the same step, and
-(with --suite) per-matrix GEMV/GEMM figures for every workload shape.
+HIP events on the stream it runs on), the CPU oracle timed on a bounded
+sample of the same step, the metric's other halves (prefill GEMM TOPS at the
+512-token Q4_0 FFN and the 8B-class Q4_K 14336x4096 shape, LM-head GEMV
+GB/s; --no-extra leaves them out), and (with --suite) per-matrix GEMV/GEMM
+figures for every workload shape.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--suite]
 
@@ -201,21 +203,25 @@ def cpu_baseline(W, seconds):
                       f"{dt:.1f} s; tok/s {steps / dt:.2f}"}
 
 
-def suite(torch, g, synth, rotate_bytes):
+def suite(torch, g, synth, rotate_bytes, only=None):
     """Per-matrix figures for every workload shape: GEMV at each decode batch
     (weight GB/s) and GEMM at each prefill size (int8-equivalent TOPS), from
-    the time per launch of back-to-back graph launches over rotated copies."""
+    the time per launch of back-to-back graph launches over rotated copies.
+    only: a set of (workload, matrix index, rows) to restrict it to."""
     res = []
     L = g.lib()
     for wl, spec in synth.WORKLOADS.items():
         ci = list(synth.WORKLOADS).index(wl)
         for mi, (fmt, N, K, ds) in enumerate(spec["mats"]):
+            batches = [B for B in spec["batches"] if only is None or (wl, mi, B) in only]
+            if not batches:
+                continue
             blob, _ = synth.weights(fmt, N, K, synth.seed_for(ci, mi), dscale=ds)
             wt = torch.from_numpy(blob).cuda()
             nbytes = int(wt.numel())
             R = max(1, min(64, math.ceil(rotate_bytes / nbytes)))
             copies = [wt] + [wt.clone() for _ in range(R - 1)]
-            for B in spec["batches"]:
+            for B in batches:
                 x = torch.from_numpy(synth.activations(B, K, synth.act_seed_for(ci, B))).cuda()
                 xq = g.quantize(x)
                 y = torch.empty(B, N, dtype=torch.float32, device="cuda")
@@ -244,6 +250,34 @@ def suite(torch, g, synth, rotate_bytes):
             del copies, wt
             torch.cuda.empty_cache()
     return res
+
+
+def other_halves(torch, g, synth):
+    """The metric's other figures beside the headline decode step: the prefill
+    GEMM (int8-equivalent TOPS) at the pages' 512-token prompt (Q4_0 gate/up
+    and down) and at the 8B-class 2048-token shape (Q4_K 14336x4096), and the
+    largest decode GEMV (the Q6_K 151936x1024 LM head, batch 1)."""
+    rows = suite(torch, g, synth, 512 << 20,
+                 only={("q4_0_prefill512", 0, 512), ("q4_0_prefill512", 1, 512),
+                       ("8b_class", 2, 2048), ("kquant_lmhead", 0, 1)})
+    by = {(r["workload"], r["N"], r["K"], r["rows"]): r for r in rows}
+    gate, down = by[("q4_0_prefill512", 4864, 896, 512)], by[("q4_0_prefill512", 896, 4864, 512)]
+    big = by[("8b_class", 14336, 4096, 2048)]
+    lm = by[("kquant_lmhead", 151936, 1024, 1)]
+    ops512 = 2.0 * 512 * 4864 * 896 * 2
+    tops512 = ops512 / ((gate["us"] + down["us"]) * 1e-6) / 1e12
+    return {
+        "prefill": {
+            "unit": "int8-equivalent TOPS", "peak": INT8_PEAK_TOPS,
+            "q4_0_ffn_m512": {"TOPS": round(tops512, 1), "frac": round(tops512 / INT8_PEAK_TOPS, 4),
+                              "us_gate_4864x896": gate["us"], "us_down_896x4864": down["us"]},
+            "q4_k_14336x4096_m2048": {"TOPS": big["int8_TOPS"], "frac": big["mfma_frac"],
+                                      "us": big["us"]},
+            "timing": "HIP events around graph replays of back-to-back launches",
+        },
+        "lm_head": {"matrix": "Q6_K 151936x1024, batch 1", "weight_GBs": lm["weight_GBs"],
+                    "frac": lm["hbm_frac"], "us": lm["us"]},
+    }
 
 
 def profile_matrix(torch, g, synth, spec, launches=20):
@@ -317,6 +351,8 @@ def main():
     ap.add_argument("--rotate-mib", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="leave out the prefill GEMM and LM-head figures")
     ap.add_argument("--suite", action="store_true",
                     help="also report every workload matrix (GEMV and GEMM) separately")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -446,8 +482,14 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
-    if args.suite:
+    if not args.no_extra:
         del graphs
+        W.clear()
+        torch.cuda.empty_cache()
+        graphs = None
+        out.update(other_halves(torch, g, synth))
+    if args.suite:
+        graphs = None
         W.clear()
         torch.cuda.empty_cache()
         out["suite"] = suite(torch, g, synth, 512 << 20)
