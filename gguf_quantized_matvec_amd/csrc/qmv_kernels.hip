@@ -1089,9 +1089,19 @@ struct DotJobs {
     DotJob j[MAX_JOBS];
 };
 
-// Work units: C <= 64 chunks per row: a unit is G = 64/LPR rows (LPR = lanes
-// per row, a power of two >= C), one chunk per lane; C > 64: a unit is one
-// row, in passes of 64 chunks.  Every wave takes one unit; a workgroup is 4
+// floor(a / b) for 0 <= a < 4096 and 1 <= b <= 64, through the f32
+// reciprocal: (a + 1/2) / b lies at least 1/(2b) >= 1/128 from an integer,
+// and the rounding of a + 1/2 (exact), rcp(b) (1 ulp) and the product keeps
+// the result within 4096 * 2^-21 = 1/512 of it.
+__device__ __forceinline__ int small_div(int a, int b) {
+    return (int)(((float)a + 0.5f) * __builtin_amdgcn_rcpf((float)b));
+}
+
+// Work units: C <= 64 chunks per row: a unit is G = floor(64/C) rows, C
+// lanes per row (LPR = C), one chunk per lane; C > 64: a unit is one row,
+// in passes of 64 chunks.  (Waves start at a limited rate per XCD, about
+// one per 25 ns measured, so packing rows tightly into the 64 lanes, rather
+// than into power-of-two lane groups, shortens the launch.)  Every wave takes one unit; a workgroup is 4
 // (or 8) waves sharing the activation rows staged in LDS.  Each lane streams its
 // chunk straight into registers, issued before the activations are staged.
 // Chunk sums are added in chunk order per row through a small LDS buffer,
@@ -1115,18 +1125,18 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     float (*pbuf)[64] = reinterpret_cast<float (*)[64]>(smem + B * rowb + wv * B * 256);
 
     const int64_t R = (K / F::QK) * F::BB;
-    int lg = 0;  // LPR = 2^lg lanes per row, G = 64 / LPR rows per unit
-    while ((1 << lg) < C && lg < 6) lg++;
-    const int LPR = 1 << lg, G = 64 >> lg;
+    const int LPR = C <= 64 ? C : 64, G = 64 / LPR;  // lanes per row, rows per unit
     const int PR = (C + 63) >> 6;  // passes (1 unless C > 64)
-    const int64_t units = C <= 64 ? (N + G - 1) >> (6 - lg) : N;
+    const int64_t units = C <= 64 ? (N + G - 1) / G : N;
+    const int lrow = small_div(lane, LPR), lchunk = lane - lrow * LPR;  // this lane's row in the unit, chunk
     if ((int64_t)blockIdx.x * jobs.waves >= units) return;  // surplus workgroup of a smaller job
     const int64_t u = (int64_t)blockIdx.x * jobs.waves + wv;
     const bool active = u < units;
 
     auto chunk_of = [&](int q, int64_t& row, int& c) {
-        row = C <= 64 ? u * G + (lane >> lg) : u;
-        c = C <= 64 ? (lane & (LPR - 1)) : 64 * q + lane;
+        // lanes past the unit's G rows (64 % C of them) get a row past N: idle
+        row = C <= 64 ? (lrow < G ? u * G + lrow : N) : u;
+        c = C <= 64 ? lchunk : 64 * q + lane;
     };
     auto issue = [&](int q, uint32_t (&r)[NWD]) {
         int64_t row;
@@ -1333,7 +1343,7 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
         for (int j = 0; j < B; j++) {
             const int t = lane + 64 * j;
             if (t < G * B) {
-                const int m = t >> (6 - lg), rl = t & (G - 1);
+                const int m = small_div(t, G), rl = t - m * G;
                 for (int k = 0; k < cnt; k++) yacc[j] = yacc[j] + pbuf[m][rl * LPR + k];
             }
         }
@@ -1343,7 +1353,7 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     for (int j = 0; j < B; j++) {
         const int t = lane + 64 * j;
         if (t < G * B) {
-            const int m = t >> (6 - lg), rl = t & (G - 1);
+            const int m = small_div(t, G), rl = t - m * G;
             const int64_t orow = C <= 64 ? u * G + rl : u;
             if (orow < N) J.y[m * N + orow] = yacc[j];
         }
@@ -1353,9 +1363,7 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
 // Workgroups of the dot kernel for one GEMV: one wave per unit, 4 per group.
 inline int64_t dot_blocks(int type, int64_t N, int64_t K, int waves) {
     const int nb = (int)(K / 32), C = (nb + 7) / 8;
-    int LPR = 1;
-    while (LPR < C && LPR < 64) LPR <<= 1;
-    const int64_t G = 64 / LPR;
+    const int64_t G = 64 / (C <= 64 ? C : 64);  // rows per unit, as k_dot
     (void)type;
     const int64_t units = C <= 64 ? (N + G - 1) / G : N;
     return (units + waves - 1) / waves;
@@ -1413,9 +1421,24 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
     int64_t blocks4 = 0;
     for (int k = 0; k < count; k++) blocks4 += dot_blocks(type, d[k].N, d[k].K, 4);
     jobs.waves = blocks4 > 256 && blocks4 <= 512 ? 8 : 4;
+    // Rows of the grid in decreasing workgroup count: workgroups are
+    // dispatched row after row at a limited rate, so the surplus (exiting)
+    // workgroups of a smaller GEMV delay only the rows after it, and the
+    // last row's delay nothing.
+    int order[MAX_JOBS];
     for (int k = 0; k < count; k++) {
+        int at = k;
+        const int64_t bk = dot_blocks(type, d[k].N, d[k].K, 4);
+        while (at > 0 && dot_blocks(type, d[order[at - 1]].N, d[order[at - 1]].K, 4) < bk) {
+            order[at] = order[at - 1];
+            at--;
+        }
+        order[at] = k;
+    }
+    for (int jk = 0; jk < count; jk++) {
+        const int k = order[jk];
         const ActLayout L = act_layout(rows, d[k].K);
-        DotJob& J = jobs.j[k];
+        DotJob& J = jobs.j[jk];
         J.w = d[k].w;
         J.y = d[k].y;
         J.x = d[k].x;
