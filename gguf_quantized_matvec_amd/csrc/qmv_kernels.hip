@@ -831,8 +831,12 @@ __device__ __forceinline__ void realign_chunk(int64_t off, uint32_t (&r)[DotFmt<
     constexpr int NWD = DotFmt<FMT>::NWD;
     if constexpr (!chunk_aligned4<FMT>()) {
         const uint32_t sh = (uint32_t)(off & 3);  // 0 or 2
+        // skipped when every chunk of the wave is 4-byte aligned (e.g. all
+        // rows of a whole number of 8-byte spans)
+        if (__builtin_amdgcn_ballot_w64(sh != 0) != 0) {
 #pragma unroll
-        for (int j = 0; j < NWD - 1; j++) r[j] = __builtin_amdgcn_alignbyte(r[j + 1], r[j], sh);
+            for (int j = 0; j < NWD - 1; j++) r[j] = __builtin_amdgcn_alignbyte(r[j + 1], r[j], sh);
+        }
     }
 }
 
