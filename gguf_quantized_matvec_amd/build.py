@@ -36,11 +36,13 @@ def _run(cmd: list) -> None:
 
 
 def build() -> str:
-    objs = []
-    for src, extra in SOURCES:
-        obj = os.path.join(CSRC, os.path.basename(src) + ".o")
-        _run([HIPCC, *FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj])
-        objs.append(obj)
+    # the translation units compile in parallel (one hipcc process each)
+    from concurrent.futures import ThreadPoolExecutor
+    objs = [os.path.join(CSRC, os.path.basename(src) + ".o") for src, _ in SOURCES]
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        for f in [ex.submit(_run, [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj])
+                  for (src, extra), obj in zip(SOURCES, objs)]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", *objs, "-o", tmp])
     for obj in objs:

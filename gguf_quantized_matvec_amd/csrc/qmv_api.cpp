@@ -63,7 +63,7 @@ int matmul_common(int type, const void* w, int64_t N, int64_t K, const float* x,
     if (rc) return rc;
     if (rows < 1 || rows > max_rows) return QMV_EINVAL_SHAPE;
     if (!xq || !y || !aligned(xq, 16) || !aligned(y, 4)) return QMV_EINVAL_PTR;
-    if (x && !aligned(x, 16)) return QMV_EINVAL_PTR;
+    if (x && !aligned(x, 4)) return QMV_EINVAL_PTR;
     if ((rc = check_device())) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* q = static_cast<uint8_t*>(xq);
@@ -83,7 +83,7 @@ size_t qmv_act_bytes(int64_t rows, int64_t K) {
 
 int quantize_act_q8_0(const float* x, void* xq, int64_t rows, int64_t K, void* stream) {
     if (rows < 1 || rows > QMV_MAX_M || K < 32 || K > QMV_MAX_K || K % 32) return QMV_EINVAL_SHAPE;
-    if (!xq || !aligned(xq, 16) || (x && !aligned(x, 16))) return QMV_EINVAL_PTR;
+    if (!xq || !aligned(xq, 16) || (x && !aligned(x, 4))) return QMV_EINVAL_PTR;
     const int rc = check_device();
     if (rc) return rc;
     uint8_t* q = static_cast<uint8_t*>(xq);
@@ -108,16 +108,23 @@ int qmv_launch_group(int type, int64_t B, const qmv_gemv* g, int count, void* st
         if (rc) return rc;
         if ((g[k].x != nullptr) != quantise) return QMV_EINVAL_PTR;
         if (!g[k].y || !aligned(g[k].y, 4)) return QMV_EINVAL_PTR;
-        if (g[k].x && !aligned(g[k].x, 16)) return QMV_EINVAL_PTR;
+        if (g[k].x && !aligned(g[k].x, 4)) return QMV_EINVAL_PTR;
         if (!g[k].x && !g[k].xq) return QMV_EINVAL_PTR;
         if (g[k].xq && !aligned(g[k].xq, 16)) return QMV_EINVAL_PTR;
         d[k] = qmv::GemvDesc{static_cast<const uint8_t*>(g[k].w), g[k].N, g[k].K, g[k].x,
                              static_cast<uint8_t*>(g[k].xq), g[k].y};
     }
-    // xq may be left NULL only when the whole group runs as one fused launch;
-    // every other path quantises into xq first
-    for (int k = 0; k < count; k++)
-        if (!g[k].xq && qmv::staging_for(B, g[k].K) != qmv::ST_ROW) return QMV_EINVAL_PTR;
+    // xq may be left NULL only when the whole group (every entry's K and B)
+    // runs as one fused launch and no entry's x needs a quantise launch of
+    // its own (x not 16-byte aligned); every other path quantises into xq
+    // first.  Decided for the whole group before anything is launched.
+    bool any_null = false, any_unaligned = false;
+    for (int k = 0; k < count; k++) {
+        any_null |= g[k].xq == nullptr;
+        any_unaligned |= g[k].x != nullptr && !aligned(g[k].x, 16);
+    }
+    if (any_null && (any_unaligned || !qmv::group_is_one_launch(d, count, B)))
+        return QMV_EINVAL_PTR;
     const int rc = check_device();
     if (rc) return rc;
     return launched(qmv::launch_qmv_group(type, d, count, B, static_cast<hipStream_t>(stream)));
@@ -151,8 +158,9 @@ const char* qmv_strerror(int code) {
                "(K % 256 == 0 for Q4_K/Q6_K), 1 <= B <= 16 for qmv_launch (use qmm_launch "
                "for more rows), 1 <= M <= 2^24 for qmm_launch";
     case QMV_EINVAL_PTR:
-        return "bad pointer: w and xq must be non-NULL, w, x and xq 16-byte aligned (x may "
-               "be NULL to use xq as staged), y and P 4-byte aligned";
+        return "bad pointer: w and xq must be non-NULL, w and xq 16-byte aligned, x, y and P "
+               "4-byte aligned (x may be NULL to use xq as staged; a group entry may leave xq "
+               "NULL only when the group runs as one launch and its x is 16-byte aligned)";
     case QMV_ELAUNCH: return "HIP kernel launch failed";
     case QMV_EUNSUPPORTED_DEVICE: return "current device is not an MI355X (gfx950)";
     }

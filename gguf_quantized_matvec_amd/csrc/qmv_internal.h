@@ -31,6 +31,7 @@ struct ActLayout {
 };
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 inline ActLayout act_layout(int64_t rows, int64_t K) {
     ActLayout L;
@@ -84,6 +85,10 @@ enum Staging : int {
     ST_F16 = 4,   // hcodes, hda and rca (prefill GEMM)
 };
 int staging_for(int64_t rows, int64_t K);
+// Whether launch_qmv_group runs the whole group as one launch of the
+// lane-per-chunk kernel (then an entry with x given may leave xq NULL, as
+// long as its x is 16-byte aligned).
+bool group_is_one_launch(const GemvDesc* d, int count, int64_t rows);
 
 // Kernel launchers (qmv_kernels.hip).  Arguments are already validated.
 // Each returns 0 or a hipError_t value.  x != NULL: the launch quantises x

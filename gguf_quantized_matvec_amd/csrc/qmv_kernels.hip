@@ -9,8 +9,8 @@
 // block per instruction, 16 activation rows x 16 weight rows), and the f32
 // scale-and-accumulate follows one fixed order for every launch shape (see
 // include/qmv.h), so a row's result never depends on the batch around it
-// (llamay docs, "The three claims": same output regardless of batch
-// composition).
+// (llamay docs front page, "The three claims": determinism, claimed for any
+// mix of requests in a batch).
 //
 // Decode is memory-bound ("Architecture", bench transcript), so the weight
 // stream is the thing to get right: each wave owns 16 weight rows and walks
@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <utility>
 
 #include "qmv_internal.h"
@@ -69,15 +70,22 @@ __device__ __forceinline__ T ld(const uint8_t* p) {
 // ------------------------------------------------------------ quantise ----
 // Q8_0 of one 32-element block: amax, d = amax/127 (correctly rounded f32
 // divide), id = 1/d (0 for an all-zero block), codes = round-half-away(x*id),
-// stored scale fp16(d); dval = f32 value of the stored scale.
+// stored scale fp16(d); dval = f32 value of the stored scale.  A16: xb is
+// 16-byte aligned (float4 loads); otherwise only 4-byte alignment is assumed.
+template <bool A16>
 __device__ __forceinline__ void quant_block(const float* __restrict__ xb, uint8_t (&q)[32],
                                             uint16_t& h, float& dval) {
     float v[32];
-    const float4* x4 = reinterpret_cast<const float4*>(xb);
+    if constexpr (A16) {
+        const float4* x4 = reinterpret_cast<const float4*>(xb);
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const float4 f = x4[j];
-        v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+        for (int j = 0; j < 8; j++) {
+            const float4 f = x4[j];
+            v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; i++) v[i] = xb[i];
     }
     float amax = 0.0f;
 #pragma unroll
@@ -129,7 +137,7 @@ __device__ __forceinline__ void store_row_staging(uint8_t* xq, const ActLayout& 
 // in xq) and write the staging copies selected by `staging`.  One thread per
 // (row, block); with ST_MFMA over the 16-row-padded range, whose padding
 // rows get zero codes and scales in that copy.
-template <bool FROM_PUBLIC>
+template <bool FROM_PUBLIC, bool A16>
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x,
                                                   uint8_t* __restrict__ xq, int64_t rows,
                                                   int64_t K, ActLayout L, int staging) {
@@ -144,7 +152,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x,
         uint8_t* pub = xq + (r * nb + b) * 34;
         if (!FROM_PUBLIC) {
             uint16_t h;
-            quant_block(x + r * K + 32 * b, q, h, dval);
+            quant_block<A16>(x + r * K + 32 * b, q, h, dval);
             store_public(pub, q, h);
         } else {
             uint8_t blk[34];
@@ -1377,14 +1385,28 @@ inline size_t dot_shmem(int B, int64_t K, int waves) {
     return (size_t)B * act_lds_row_bytes(K) + (size_t)waves * B * 256;
 }
 
+// Raise a kernel's dynamic-LDS limit to the full 160 KB, once per kernel and
+// device.  The state is atomic, so concurrent first calls from several host
+// threads are safe (both may set the attribute, which is idempotent); a
+// failure is returned to the caller and retried on the next call.
+inline int raise_lds_limit(const void* kernel, std::atomic<int> (&state)[64]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return (int)hipErrorInvalidDevice;
+    std::atomic<int>* st = dev >= 0 && dev < 64 ? &state[dev] : nullptr;
+    if (st && st->load(std::memory_order_acquire) == 1) return 0;
+    const hipError_t rc =
+        hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (rc != hipSuccess) return (int)rc;
+    if (st) st->store(1, std::memory_order_release);
+    return 0;
+}
+
 template <int FMT, int B, bool FUSED, bool SINGLE>
 int launch_dot_kernel(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
-    static bool attr_set = false;  // allow up to the full 160 KB of LDS
-    if (!attr_set) {
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED, SINGLE>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr_set = true;
-    }
+    static std::atomic<int> lds_state[64];
+    const int arc = raise_lds_limit(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED, SINGLE>),
+                                    lds_state);
+    if (arc) return arc;
     hipLaunchKernelGGL((k_dot<FMT, B, FUSED, SINGLE>), dim3((unsigned)blocks, (unsigned)jobs.count),
                        dim3(64 * jobs.waves), shmem, s, jobs);
     return (int)hipGetLastError();
@@ -1530,6 +1552,13 @@ bool use_dot(int64_t rows, int64_t K) {
 
 }  // namespace
 
+bool group_is_one_launch(const GemvDesc* d, int count, int64_t rows) {
+    bool one = count >= 1 && count <= MAX_JOBS;
+    for (int k = 0; k < count && one; k++)
+        one = use_dot(rows, d[k].K) && ((d[k].x != nullptr) == (d[0].x != nullptr));
+    return one;
+}
+
 int staging_for(int64_t rows, int64_t K) {
     if (rows > 16) return ST_F16;
     return use_dot(rows, K) ? ST_ROW : ST_MFMA;
@@ -1539,15 +1568,19 @@ int launch_quantize(const float* x, uint8_t* xq, int64_t rows, int64_t K, int st
                     hipStream_t s) {
     const ActLayout L = act_layout(rows, K);
     const int64_t threads = ((staging & ST_MFMA) ? 16 * L.G : rows) * L.nb;
-    hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       s, x, xq, rows, K, L, staging);
+    if (aligned16(x))
+        hipLaunchKernelGGL((k_quantize<false, true>), dim3((unsigned)((threads + 255) / 256)),
+                           dim3(256), 0, s, x, xq, rows, K, L, staging);
+    else
+        hipLaunchKernelGGL((k_quantize<false, false>), dim3((unsigned)((threads + 255) / 256)),
+                           dim3(256), 0, s, x, xq, rows, K, L, staging);
     return (int)hipGetLastError();
 }
 
 int launch_rebuild(uint8_t* xq, int64_t rows, int64_t K, int staging, hipStream_t s) {
     const ActLayout L = act_layout(rows, K);
     const int64_t threads = ((staging & ST_MFMA) ? 16 * L.G : rows) * L.nb;
-    hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL((k_quantize<true, true>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                        s, nullptr, xq, rows, K, L, staging);
     return (int)hipGetLastError();
 }
@@ -1558,7 +1591,8 @@ int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
         // quantisation fused into the kernel when x is given, unless the
         // workgroups' re-reads of x would exceed the weight bytes: then one
         // quantise launch first
-        if (x && dot_blocks(type, N, K, 4) * rows * K * 4 > N * row_bytes(type, K)) {
+        if (x && (!aligned16(x) ||
+                  dot_blocks(type, N, K, 4) * rows * K * 4 > N * row_bytes(type, K))) {
             const int rc = launch_quantize(x, xq, rows, K, ST_ROW, s);
             if (rc) return rc;
             x = nullptr;
@@ -1585,10 +1619,25 @@ int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
 }
 
 int launch_qmv_group(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s) {
-    bool one = count <= MAX_JOBS;
-    for (int k = 0; k < count && one; k++)
-        one = use_dot(rows, d[k].K) && ((d[k].x != nullptr) == (d[0].x != nullptr));
-    if (one) return launch_dot(type, d, count, rows, s);
+    if (group_is_one_launch(d, count, rows)) {
+        // the fused quantisation reads x with 16-byte loads: an entry whose x
+        // is only 4-byte aligned is quantised by a launch of its own first
+        GemvDesc e[MAX_JOBS];
+        bool restaged = false;
+        for (int k = 0; k < count; k++) {
+            e[k] = d[k];
+            if (d[k].x && !aligned16(d[k].x)) restaged = true;
+        }
+        if (restaged) {
+            for (int k = 0; k < count; k++) {
+                if (!e[k].xq) return (int)hipErrorInvalidValue;
+                const int rc = launch_quantize(e[k].x, e[k].xq, rows, e[k].K, ST_ROW, s);
+                if (rc) return rc;
+                e[k].x = nullptr;
+            }
+        }
+        return launch_dot(type, e, count, rows, s);
+    }
     for (int k = 0; k < count; k++)  // one after another: each needs its xq
         if (!d[k].xq) return (int)hipErrorInvalidValue;
     for (int k = 0; k < count; k++) {

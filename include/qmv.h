@@ -3,10 +3,10 @@
  * for GGUF block-quantised weights (libqmv.so).
  *
  * What it computes.  The llamay pages ("Architecture", section "The package
- * map") place the block layouts, dequantisation and fused W4A8 kernels in
- * pkg/quant and "MatVec for decode, MatMul for prefill" in pkg/tensor; the
- * same page's bench transcript notes that prefill is arithmetic-bound and
- * decode memory-bound.  Here that is, for a weight matrix W (N rows of K
+ * map") put the block layouts, dequantisation and fused W4A8 kernels in
+ * pkg/quant, and in pkg/tensor a matrix-vector product used while decoding
+ * and a matrix-matrix product used for the prompt; the same page's bench
+ * transcript reports prefill limited by arithmetic and decode by memory.  Here that is, for a weight matrix W (N rows of K
  * elements, GGUF block layout) and f32 activations X (rows of K elements):
  *
  *     xq      = Q8_0(X)                           (per 32-element block:
@@ -44,7 +44,8 @@
  * the byte layouts are the GGUF block structures, which the pages do not
  * print.  Q5_0 is the format of most matrices in the pages' own Qwen2.5-0.5B
  * file (the tensor histogram of its info transcript).  Blocks need not be aligned; w itself must
- * be 16-byte aligned.  X and Y are dense row-major f32.
+ * be 16-byte aligned.  X and Y are dense row-major f32, 4-byte aligned (a
+ * 16-byte aligned x lets the quantisation run inside the multiply).
  *
  * Ownership.  The caller owns and allocates every buffer (device memory).
  * The library allocates nothing, keeps no per-call state, never synchronises,
@@ -99,7 +100,7 @@ enum qmv_status {
  * written).  Returns 0 for an invalid shape. */
 size_t qmv_act_bytes(int64_t rows, int64_t K);
 
-/* Quantise x [rows][K] (f32, 16-byte aligned) to Q8_0 into xq (16-byte
+/* Quantise x [rows][K] (f32, 4-byte aligned) to Q8_0 into xq (16-byte
  * aligned, qmv_act_bytes(rows, K) bytes): the Q8_0 blocks and the staging
  * copy.  With x == NULL, the Q8_0 blocks already in xq (first rows*(K/32)*34
  * bytes, e.g. produced elsewhere) are taken as the input and only the staging
@@ -128,8 +129,10 @@ typedef struct qmv_gemv {
     const float* x;  /* [B][K] f32 activations, or NULL for all entries (xq staged) */
     void* xq;        /* qmv_act_bytes(B, K) bytes: receives the quantisation when x is given,
                         or holds it when x is NULL.  May be NULL only with x given and
-                        B <= 4 (the group then runs as one launch that needs no scratch);
-                        otherwise a NULL xq is refused with QMV_EINVAL_PTR */
+                        16-byte aligned, and only when the whole group runs as one launch
+                        that needs no scratch (B <= 4 and every entry's activation rows fit
+                        the kernel's LDS); otherwise a NULL xq is refused with
+                        QMV_EINVAL_PTR, whatever the other entries hold */
     float* y;        /* [B][N] */
 } qmv_gemv;
 

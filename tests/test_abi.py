@@ -60,7 +60,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-NULL address; never dereferenced
     ((g.Q8_0, FAKE, 16, (1 << 20) + 32, FAKE, 1, FAKE, FAKE), -2),
     ((g.Q8_0, None, 16, 32, FAKE, 1, FAKE, FAKE), -3),       # w NULL
     ((g.Q8_0, FAKE + 8, 16, 32, FAKE, 1, FAKE, FAKE), -3),   # w misaligned
-    ((g.Q8_0, FAKE, 16, 32, FAKE + 4, 1, FAKE, FAKE), -3),   # x misaligned
+    ((g.Q8_0, FAKE, 16, 32, FAKE + 2, 1, FAKE, FAKE), -3),   # x not 4-byte aligned
     ((g.Q8_0, FAKE, 16, 32, FAKE, 1, None, FAKE), -3),       # xq NULL
     ((g.Q8_0, FAKE, 16, 32, FAKE, 1, FAKE + 8, FAKE), -3),   # xq misaligned
     ((g.Q8_0, FAKE, 16, 32, FAKE, 1, FAKE, FAKE + 2), -3),   # y misaligned
@@ -78,7 +78,8 @@ def test_qmm_and_partials_refusals():
     assert L.qmv_partials_launch(g.Q8_0, FAKE, 16, 32, None, 1, FAKE, None) == -3
     assert L.qmv_partials_launch(5, FAKE, 16, 32, FAKE, 1, FAKE, None) == -1
     assert L.quantize_act_q8_0(FAKE, FAKE, 1, 40, None) == -2
-    assert L.quantize_act_q8_0(FAKE + 4, FAKE, 1, 32, None) == -3
+    assert L.quantize_act_q8_0(FAKE + 2, FAKE, 1, 32, None) == -3   # x 4-byte aligned at least
+    assert L.quantize_act_q8_0(FAKE, FAKE + 4, 1, 32, None) == -3   # xq 16-byte aligned
 
 
 def test_group_refusals():
@@ -97,6 +98,14 @@ def test_group_refusals():
     assert L.qmv_launch_group(12, 1, (G * 1)(G(16, 1, 96, 16, None, 16)), 1, None) == -2
     # xq may be NULL only for a single fused launch (B <= 4); B = 5 quantises into xq
     assert L.qmv_launch_group(8, 5, (G * 1)(G(16, 1, 32, 16, None, 16)), 1, None) == -3
+    # ... decided for the whole group: an entry whose K is too long for the
+    # one-launch kernel (activation rows beyond its LDS) makes the group run
+    # one GEMV after another, so the small entry's NULL xq is refused too
+    mixed = (G * 2)(G(16, 1, 32, 16, None, 16), G(16, 1, 1 << 17, 16, 16, 16))
+    assert L.qmv_launch_group(8, 1, mixed, 2, None) == -3
+    # an x only 4-byte aligned is quantised by a launch of its own: needs xq
+    assert L.qmv_launch_group(8, 1, (G * 1)(G(16, 1, 32, 20, None, 16)), 1, None) == -3
+    assert L.qmv_launch_group(8, 1, (G * 1)(G(16, 1, 32, 18, 16, 16)), 1, None) == -3
 
 
 def test_strerror_names_what_works():
