@@ -51,9 +51,10 @@ def lib():
         L.oracle_matmul_f64.argtypes = [I, P, I64, I64, P, I64, P, P]
         L.oracle_dense_f64.argtypes = [I, P, I64, I64, P, I64, P]
         L.oracle_matmul_canon_f32.argtypes = [I, P, I64, I64, P, I64, P]
+        L.oracle_swiglu.argtypes = [P, P, I64, P]
         for name in ("oracle_quantize_act", "oracle_unpack", "oracle_dequant",
                      "oracle_dequant_act", "oracle_partials", "oracle_matmul_f64",
-                     "oracle_dense_f64", "oracle_matmul_canon_f32"):
+                     "oracle_dense_f64", "oracle_matmul_canon_f32", "oracle_swiglu"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -151,3 +152,14 @@ def matmul_canon_f32(fmt: int, blob, N: int, K: int, xq, B: int) -> np.ndarray:
     _ok(lib().oracle_matmul_canon_f32(fmt, _p(blob), N, K, _p(xq), B, _p(y)),
         "matmul_canon_f32")
     return y.reshape(B, N)
+
+
+def swiglu(g, u) -> np.ndarray:
+    """h = silu(g) * u element by element (f64 evaluation, one rounding to f32)."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    if g.shape != u.shape:
+        raise ValueError("g and u differ in shape")
+    h = np.zeros(g.shape, np.float32)
+    _ok(lib().oracle_swiglu(_p(g), _p(u), g.size, _p(h)), "swiglu")
+    return h

@@ -448,3 +448,19 @@ int oracle_matmul_canon_f32(int type, const uint8_t* w, int64_t N, int64_t K,
     row_free(&r);
     return 0;
 }
+
+/* SwiGLU gate of a decode FFN (llamay "Models and formats", the architectures
+ * table: SwiGLU feed-forward in the llama / qwen2 family; the pages give no
+ * formula, so the usual one is read): h = silu(g) * u with
+ * silu(g) = g / (1 + e^-g).  Each element is evaluated in f64 in the order
+ * t = exp(-g), s = g / (1 + t), h = s * u, and rounded once to f32. */
+int oracle_swiglu(const float* g, const float* u, int64_t n, float* h) {
+    if (n < 0) return -2;
+    for (int64_t i = 0; i < n; i++) {
+        const double gd = (double)g[i];
+        const double t = exp(-gd);
+        const double s = gd / (1.0 + t);
+        h[i] = (float)(s * (double)u[i]);
+    }
+    return 0;
+}

@@ -83,6 +83,11 @@ int oracle_dense_f64(int type, const uint8_t* w, int64_t N, int64_t K,
 int oracle_matmul_canon_f32(int type, const uint8_t* w, int64_t N, int64_t K,
                             const uint8_t* xq, int64_t B, float* y);
 
+/* SwiGLU of a decode FFN, element by element: h = silu(g) * u with
+ * silu(g) = g / (1 + exp(-g)), evaluated in f64 as t = exp(-g),
+ * s = g / (1 + t), h = s * u and rounded once to f32. */
+int oracle_swiglu(const float* g, const float* u, int64_t n, float* h);
+
 #ifdef __cplusplus
 }
 #endif
