@@ -1,33 +1,39 @@
 #!/usr/bin/env python3
 """Benchmark of the fused dequantise-and-multiply on one MI355X.
 
-One step = one decode token through a Q4_0 SwiGLU FFN at batch 1 (the
-Qwen2.5-0.5B FFN shape of the llamay pages: gate and up 4864x896, down
-896x4864): quantise the 896-wide activation once, GEMV gate and up on it,
-quantise the 4864-wide activation, GEMV down.  The three GEMVs are
-independent here (down takes its own synthetic activation), so a step is one
-grouped launch (qmv_launch_group) in which each GEMV quantises its activation
-inside the kernel.  Inputs are seeded synthetic
-weights/activations already resident in HBM; the weights are rotated over
-copies totalling >= --rotate-mib so every step streams them from HBM rather
-than from the 256 MB last-level cache.  Steps are replayed from a captured
-HIP graph (the path is launch-bound at this size).
+Headline step: one decoder layer of an 8B-class model in decode at batch 1,
+built from the four 8B-class weight shapes (Q4_K 4096x4096, 1024x4096,
+14336x4096, Q6_K 4096x14336) in the order a model runs them:
 
-Prints ONE JSON line: metric/value (weight GB/s of the timed steps, wall
-clock), the roofline of the dominant kernel (the GEMV; execution times from
-HIP events on the stream it runs on), the CPU oracle timed on a bounded
-sample of the same step, the metric's other halves (prefill GEMM TOPS at the
-512-token Q4_0 FFN and the 8B-class Q4_K 14336x4096 shape, LM-head GEMV
-GB/s; --no-extra leaves them out), and (with --suite) per-matrix GEMV/GEMM
-figures for every workload shape.
+  A  q 4096x4096, k and v 1024x4096 on one activation (one grouped launch)
+  B  o 4096x4096 on the attention output (a synthetic activation here)
+  C  gate and up 14336x4096 on one activation, with the SwiGLU
+     h = silu(gate) * up in the same launch (qmv_launch_gateup_swiglu)
+  D  down 4096x14336 (Q6_K) on h
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--suite]
+Each stage quantises its own activation to Q8_0 inside the GEMV where it
+can.  Attention, norms and residuals are not part of the multiply and are
+not run.  A step is replayed from a captured HIP graph; the weights are
+rotated over copies totalling >= --rotate-mib, so every step streams them
+from HBM rather than from the 256 MB last-level cache.  value = weight bytes
+of the step / wall-clock time of the timed steps.
 
-Counter collection helpers: --profile-steps N (eager steps only),
---profile-matrix WORKLOAD:INDEX:ROWS (one workload matrix, eagerly),
---copy-calib (a 256 MiB copy, the counters' byte calibration) and
---traffic-from DIR (turns their rocprofv3 --pmc output into
-profiles/traffic.json).
+The same JSON line also carries: the roofline of the step's dominant kernel
+(HIP-event time per launch on the stream it runs on), the layer step at batch
+16, the prefill GEMMs of the four shapes at 2048 tokens (int8-equivalent
+TOPS), the LM-head GEMV (Q6_K 151936x1024) at batch 1/4/16, the pages' own
+Qwen2.5-0.5B shapes (Q8_0 896x896, the Q4_0 SwiGLU FFN at batch 1, the Q4_0
+prefill at 512 tokens), the measured ceilings of the chip (a streaming read,
+int8 and f16 MFMA loops, the GEMM's f32 epilogue alone) and the CPU oracle
+timed on the host's cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--suite] [--no-cpu]
+
+Counter / trace helpers: --profile-stage NAME (eager launches of one stage),
+--profile-matrix WORKLOAD:INDEX:ROWS, --copy-calib (a 256 MiB copy, the
+counters' byte calibration), --traffic-from DIR (profiles/traffic.json from
+rocprofv3 --pmc output) and --trace-summary DIR (per-kernel, per-grid
+durations from a rocprofv3 kernel trace).
 """
 from __future__ import annotations
 
@@ -45,19 +51,33 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
-KERNEL_SRC = os.path.join(ROOT, "gguf_quantized_matvec_amd", "csrc", "qmv_kernels.hip")
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense f16 MFMA, vendor figure
+CSRC = os.path.join(ROOT, "gguf_quantized_matvec_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+MAX_HOST_THREADS = 16          # the host CPUs the GPU machine allots to one GPU
+
+Q4_0, Q8_0, Q4_K, Q6_K = 2, 8, 12, 14
+# (name, fmt, N, K) of one 8B-class decoder layer's projections
+LAYER = [("q", Q4_K, 4096, 4096), ("k", Q4_K, 1024, 4096), ("v", Q4_K, 1024, 4096),
+         ("o", Q4_K, 4096, 4096), ("gate", Q4_K, 14336, 4096), ("up", Q4_K, 14336, 4096),
+         ("down", Q6_K, 4096, 14336)]
+STAGES = {"A_qkv": ("q", "k", "v"), "B_o": ("o",), "C_gateup_swiglu": ("gate", "up"),
+          "D_down": ("down",)}
+STAGE_KERNEL = {"A_qkv": "k_dot (grouped: q, k, v)", "B_o": "k_dot (single: o)",
+                "C_gateup_swiglu": "k_dot (paired gate/up, SwiGLU epilogue)",
+                "D_down": "k_dot (single: down, Q6_K)"}
 
 
 def kernel_src_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in ("qmv_kernels.hip", "qmm_kernels.hip"):
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
-def gemv_alg_bytes(fmt, N, K, B, g, fused=False) -> int:
-    """Algorithmic bytes of one GEMV launch: weight blob + Q8_0 activation
-    blocks (written, or read) + f32 output; a launch that quantises x itself
-    also reads x (f32)."""
-    return N * g.row_bytes(fmt, K) + B * (K // 32) * 34 + B * N * 4 + (B * K * 4 if fused else 0)
+def row_bytes(fmt, K):
+    qk, nb = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210)}[fmt]
+    return K // qk * nb
 
 
 class GraphSteps:
@@ -70,7 +90,7 @@ class GraphSteps:
         with torch.cuda.stream(s):
             with torch.cuda.graph(self.graph, stream=s):
                 for i in range(nsteps):
-                    step(i, None)
+                    step(i)
         torch.cuda.current_stream().wait_stream(s)
         self.nsteps = nsteps
 
@@ -79,12 +99,12 @@ class GraphSteps:
 
 
 def graph_launch_us(torch, launch, n, reps=3):
-    """Average time per launch of `n` back-to-back launches of one kernel
-    (launch(i) enqueues launch i), captured into a HIP graph and replayed
-    between two HIP events on the stream the kernels run on.  The figure is
-    the kernel's execution time plus the short dispatch gap between
-    consecutive graph nodes; the median over `reps` replays is returned."""
-    G = GraphSteps(torch, lambda i, _: launch(i), n)
+    """Average time per launch of `n` back-to-back launches (launch(i)
+    enqueues launch i), captured into a HIP graph and replayed between two
+    HIP events on the stream the kernels run on.  The figure is the kernel's
+    execution time plus the short dispatch gap between consecutive graph
+    nodes; the median over `reps` replays is returned."""
+    G = GraphSteps(torch, launch, n)
     G.replay()                               # warm
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
@@ -111,173 +131,405 @@ def run_steps(graphs, make, n):
         graphs[r].replay()
 
 
-def ffn_workload(torch, g, synth, rotate_bytes):
-    """The headline step's buffers: rotated weight copies, activations, outputs."""
-    fmt = synth.Q4_0
-    shapes = [("gate", 4864, 896), ("up", 4864, 896), ("down", 896, 4864)]
-    blobs = {}
-    for i, (name, N, K) in enumerate(shapes):
-        blob, _ = synth.weights(fmt, N, K, synth.seed_for(1, i), dscale=0.02)
-        blobs[name] = torch.from_numpy(blob).cuda()
-    step_bytes = sum(int(b.numel()) for b in blobs.values())
-    R = max(1, math.ceil(rotate_bytes / step_bytes))
-    copies = {k: [v] + [v.clone() for _ in range(R - 1)] for k, v in blobs.items()}
-    x1 = torch.from_numpy(synth.activations(1, 896, synth.act_seed_for(1, 1))).cuda()
-    x2 = torch.from_numpy(synth.activations(1, 4864, synth.act_seed_for(1, 1) + 1)).cuda()
-    xq1, xq2 = g.act_buffer(1, 896), g.act_buffer(1, 4864)
-    ys = {n: torch.empty(1, N, dtype=torch.float32, device="cuda") for n, N, _ in shapes}
-    return dict(fmt=fmt, shapes=shapes, copies=copies, R=R, x1=x1, x2=x2, xq1=xq1, xq2=xq2,
-                ys=ys, step_bytes=step_bytes)
+_WEIGHTS = {}
 
 
-def make_ffn_step(torch, g, W):
-    """One decode step = one grouped launch (qmv_launch_group) of the three
-    GEMVs, each quantising its own activation inside the kernel; gate's and
-    down's Q8_0 blocks are also written to their xq buffers."""
+def weights(synth, fmt, N, K, seed, ds):
+    """Seeded weight blob (generated once per process)."""
+    key = (fmt, N, K, seed, ds)
+    if key not in _WEIGHTS:
+        _WEIGHTS[key] = synth.weights(fmt, N, K, seed, dscale=ds)[0]
+    return _WEIGHTS[key]
+
+
+def _check(g, rc, what):
+    if rc:
+        raise g.QmvError(rc, what)
+
+
+# ------------------------------------------------------------ layer step --
+
+class Layer:
+    """Buffers of the 8B-class layer step at batch B: rotated weight copies,
+    the stage activations, scratch and outputs."""
+
+    def __init__(self, torch, g, synth, B, rotate_bytes):
+        self.B = B
+        self.torch, self.g = torch, g
+        blobs = {}
+        for i, (name, fmt, N, K) in enumerate(LAYER):
+            blob = weights(synth, fmt, N, K, synth.seed_for(4, 10 + i), 0.02)
+            blobs[name] = torch.from_numpy(blob).cuda()
+        self.step_bytes = sum(int(b.numel()) for b in blobs.values())
+        self.R = max(1, math.ceil(rotate_bytes / self.step_bytes))
+        self.w = {k: [v] + [v.clone() for _ in range(self.R - 1)] for k, v in blobs.items()}
+        act = lambda K, j: torch.from_numpy(synth.activations(B, K, synth.act_seed_for(4, B) + j)).cuda()
+        self.xa, self.xo, self.xc = act(4096, 0), act(4096, 1), act(4096, 2)
+        self.xq_a = g.act_buffer(B, 4096)
+        self.xq_o = g.act_buffer(B, 4096)
+        self.xq_c = torch.empty(g.qmv_gateup_act_bytes(B, 14336, 4096), dtype=torch.uint8,
+                                device="cuda")
+        self.xq_d = g.act_buffer(B, 14336)
+        self.h = torch.empty(B, 14336, dtype=torch.float32, device="cuda")
+        self.y = {n: torch.empty(B, N, dtype=torch.float32, device="cuda")
+                  for n, _, N, _ in LAYER if n not in ("gate", "up")}
+        self._groups = []
+        for c in range(self.R):
+            P = lambda n: self.w[n][c].data_ptr()
+            fused = B <= 4
+            xa = self.xa.data_ptr() if fused else None
+            xq_k = None if fused else self.xq_a.data_ptr()
+            self._groups.append((g.Gemv * 3)(
+                g.Gemv(P("q"), 4096, 4096, xa, self.xq_a.data_ptr(), self.y["q"].data_ptr()),
+                g.Gemv(P("k"), 1024, 4096, xa, xq_k, self.y["k"].data_ptr()),
+                g.Gemv(P("v"), 1024, 4096, xa, xq_k, self.y["v"].data_ptr())))
+
+    def stage(self, name, c):
+        """Enqueue stage `name` with weight copy c on the current stream."""
+        torch, g, B = self.torch, self.g, self.B
+        L = g.lib()
+        s = torch.cuda.current_stream().cuda_stream
+        W = lambda n: self.w[n][c].data_ptr()
+        if name == "A_qkv":
+            if B > 4:   # the group runs its GEMVs one after another: quantise once
+                _check(g, L.quantize_act_q8_0(self.xa.data_ptr(), self.xq_a.data_ptr(), B, 4096, s),
+                       "quantize")
+            _check(g, L.qmv_launch_group(Q4_K, B, self._groups[c], 3, s), "qkv")
+        elif name == "B_o":
+            _check(g, L.qmv_launch(Q4_K, W("o"), 4096, 4096, self.xo.data_ptr(), B,
+                                   self.xq_o.data_ptr(), self.y["o"].data_ptr(), s), "o")
+        elif name == "C_gateup_swiglu":
+            _check(g, L.qmv_launch_gateup_swiglu(Q4_K, W("gate"), W("up"), 14336, 4096,
+                                                 self.xc.data_ptr(), B, self.xq_c.data_ptr(),
+                                                 self.h.data_ptr(), s), "gate/up")
+        else:
+            _check(g, L.qmv_launch(Q6_K, W("down"), 4096, 14336, self.h.data_ptr(), B,
+                                   self.xq_d.data_ptr(), self.y["down"].data_ptr(), s), "down")
+
+    def step(self, i):
+        c = i % self.R
+        for name in STAGES:
+            self.stage(name, c)
+
+    def stage_alg_bytes(self, name):
+        """Algorithmic bytes of one launch of a stage: weight blobs, the f32
+        activation read, its Q8_0 blocks written, the f32 outputs."""
+        B = self.B
+        wb = {n: row_bytes(f, K) * N for n, f, N, K in LAYER}
+        Kd = {n: K for n, _, _, K in LAYER}
+        Nd = {n: N for n, _, N, _ in LAYER}
+        mats = STAGES[name]
+        K = Kd[mats[0]]
+        w = sum(wb[n] for n in mats)
+        outs = B * Nd["gate"] * 4 if name == "C_gateup_swiglu" else sum(B * Nd[n] * 4 for n in mats)
+        return w + B * K * 4 + B * (K // 32) * 34 + outs
+
+
+def time_layer(torch, g, synth, B, steps, warmup, rotate_bytes):
+    Lw = Layer(torch, g, synth, B, rotate_bytes)
+    Lw.step(0)
+    torch.cuda.synchronize()
+    graphs = {}
+
+    def make(n):
+        return GraphSteps(torch, Lw.step, n)
+
+    graphs["full"] = make(Lw.R)
+    for n in (warmup, steps):
+        r = n % Lw.R
+        if r and r not in graphs:
+            graphs[r] = make(r)
+    run_steps(graphs, make, warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(graphs, make, steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # each stage alone, back to back over every rotated copy
+    stage_us = {name: graph_launch_us(torch, lambda i, name=name: Lw.stage(name, i % Lw.R), Lw.R)
+                for name in STAGES}
+    res = {"wall_s": wall, "step_bytes": Lw.step_bytes, "R": Lw.R, "stage_us": stage_us,
+           "stage_alg_bytes": {n: Lw.stage_alg_bytes(n) for n in STAGES}}
+    del graphs, Lw
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------- per-matrix rows --
+
+def matrix_us(torch, g, synth, fmt, N, K, rows, seed, ds, rotate_bytes, n_min=20):
+    """Time per launch of qmv_launch (rows <= 16) or qmm_launch on one
+    seeded matrix, activations staged in xq, weights rotated."""
+    blob = weights(synth, fmt, N, K, seed, ds)
+    wt = torch.from_numpy(blob).cuda()
+    nbytes = int(wt.numel())
+    R = max(1, math.ceil(rotate_bytes / nbytes))
+    copies = [wt] + [wt.clone() for _ in range(R - 1)]
+    x = torch.from_numpy(synth.activations(rows, K, seed + 1)).cuda()
+    xq = g.quantize(x)
+    y = torch.empty(rows, N, dtype=torch.float32, device="cuda")
     L = g.lib()
-    fmt = W["fmt"]
-    R = W["R"]
-    x1, x2 = W["x1"].data_ptr(), W["x2"].data_ptr()
-    q1, q2 = W["xq1"].data_ptr(), W["xq2"].data_ptr()
-    y = {k: v.data_ptr() for k, v in W["ys"].items()}
-    groups = []
-    for c in range(R):
-        wp = {k: v[c].data_ptr() for k, v in W["copies"].items()}
-        groups.append((g.Gemv * 3)(g.Gemv(wp["gate"], 4864, 896, x1, q1, y["gate"]),
-                                   g.Gemv(wp["up"], 4864, 896, x1, None, y["up"]),
-                                   g.Gemv(wp["down"], 896, 4864, x2, q2, y["down"])))
+    fn = L.qmv_launch if rows <= 16 else L.qmm_launch
 
-    def step(i, _unused=None):
-        rc = L.qmv_launch_group(fmt, 1, groups[i % R], 3, torch.cuda.current_stream().cuda_stream)
-        if rc:
-            raise g.QmvError(rc, "qmv_launch_group")
-    return step
+    def launch(i):
+        _check(g, fn(fmt, copies[i % R].data_ptr(), N, K, None, rows, xq.data_ptr(),
+                     y.data_ptr(), torch.cuda.current_stream().cuda_stream), "matrix")
+    launch(0)
+    n = max(R, n_min) if rows <= 16 else max(min(R, 10), 5)
+    us = graph_launch_us(torch, launch, n)
+    del copies, wt, x, xq, y
+    torch.cuda.empty_cache()
+    return us, nbytes, R
 
 
-def cpu_baseline(W, seconds):
-    """The CPU oracle on the same step (both quantisations and the three
-    products in f64), rows split over host threads, for ~`seconds`."""
+def gemv_row(us, nbytes, B):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "weight_MB": round(nbytes / 1e6, 2), "weight_GBs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tok_s": round(B / (us * 1e-6), 1)}
+
+
+def gemm_row(us, M, N, K):
+    tops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    return {"us": round(us, 2), "TOPS": round(tops, 1), "frac": round(tops / INT8_PEAK_TOPS, 4)}
+
+
+def prefill_8b(torch, g, synth, M=2048):
+    """GEMMs of the four 8B-class shapes at M tokens, and the layer's seven."""
+    shapes = [("q,o", Q4_K, 4096, 4096, 2), ("k,v", Q4_K, 1024, 4096, 2),
+              ("gate,up", Q4_K, 14336, 4096, 2), ("down", Q6_K, 4096, 14336, 1)]
+    out, tot_ops, tot_us = {}, 0.0, 0.0
+    for i, (name, fmt, N, K, cnt) in enumerate(shapes):
+        us, _, _ = matrix_us(torch, g, synth, fmt, N, K, M, synth.seed_for(4, i), 0.02, 512 << 20)
+        out[f"{name} {N}x{K}"] = gemm_row(us, M, N, K)
+        tot_ops += cnt * 2.0 * M * N * K
+        tot_us += cnt * us
+    tops = tot_ops / (tot_us * 1e-6) / 1e12
+    out["layer (7 GEMMs)"] = {"us": round(tot_us, 1), "TOPS": round(tops, 1),
+                              "frac": round(tops / INT8_PEAK_TOPS, 4)}
+    return out
+
+
+def lm_head(torch, g, synth):
+    res = {}
+    for B in (1, 4, 16):
+        us, nb, R = matrix_us(torch, g, synth, Q6_K, 151936, 1024, B, synth.seed_for(2, 0), 0.01,
+                              1 << 30)
+        res[f"B{B}"] = gemv_row(us, nb, B)
+    return res
+
+
+def qwen_ffn(torch, g, synth, rotate_bytes):
+    """The pages' Qwen2.5-0.5B FFN at batch 1 (Q4_0 gate/up 4864x896, down
+    896x4864) as a model runs it: gate/up with the SwiGLU, then down on h."""
+    L = g.lib()
+    ws = {}
+    for i, (n, N, K) in enumerate([("gate", 4864, 896), ("up", 4864, 896), ("down", 896, 4864)]):
+        blob, _ = synth.weights(Q4_0, N, K, synth.seed_for(1, i), dscale=0.02)
+        ws[n] = torch.from_numpy(blob).cuda()
+    step_bytes = sum(int(v.numel()) for v in ws.values())
+    R = max(1, math.ceil(rotate_bytes / step_bytes))
+    cp = {k: [v] + [v.clone() for _ in range(R - 1)] for k, v in ws.items()}
+    x = torch.from_numpy(synth.activations(1, 896, synth.act_seed_for(1, 1))).cuda()
+    xq = torch.empty(g.qmv_gateup_act_bytes(1, 4864, 896), dtype=torch.uint8, device="cuda")
+    xq2 = g.act_buffer(1, 4864)
+    h = torch.empty(1, 4864, dtype=torch.float32, device="cuda")
+    y = torch.empty(1, 896, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        c = i % R
+        s = torch.cuda.current_stream().cuda_stream
+        _check(g, L.qmv_launch_gateup_swiglu(Q4_0, cp["gate"][c].data_ptr(), cp["up"][c].data_ptr(),
+                                             4864, 896, x.data_ptr(), 1, xq.data_ptr(),
+                                             h.data_ptr(), s), "qwen gate/up")
+        _check(g, L.qmv_launch(Q4_0, cp["down"][c].data_ptr(), 896, 4864, h.data_ptr(), 1,
+                               xq2.data_ptr(), y.data_ptr(), s), "qwen down")
+    step(0)
+    us = graph_launch_us(torch, step, R)
+    del cp, ws
+    torch.cuda.empty_cache()
+    gbs = step_bytes / (us * 1e-6) / 1e9
+    return {"us_per_step": round(us, 2), "weight_MB": round(step_bytes / 1e6, 2),
+            "weight_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "tok_s": round(1e6 / us, 1), "launches_per_step": 2,
+            "note": "latency-bound: 7.35 MB of weights per step"}
+
+
+def qwen_small(torch, g, synth):
+    us, nb, _ = matrix_us(torch, g, synth, Q8_0, 896, 896, 1, synth.seed_for(0, 0), 0.01, 1 << 30)
+    q8 = gemv_row(us, nb, 1)
+    q8["note"] = "latency-bound: 0.85 MB of weights"
+    pre = {}
+    tot_us = 0.0
+    for i, (N, K) in enumerate([(4864, 896), (896, 4864)]):
+        us, _, _ = matrix_us(torch, g, synth, Q4_0, N, K, 512, synth.seed_for(3, i), 0.02, 512 << 20)
+        pre[f"{N}x{K}"] = gemm_row(us, 512, N, K)
+        tot_us += us * (2 if N == 4864 else 1)
+    tops = 3 * 2.0 * 512 * 4864 * 896 / (tot_us * 1e-6) / 1e12
+    pre["ffn (gate, up, down)"] = {"us": round(tot_us, 1), "TOPS": round(tops, 1),
+                                   "frac": round(tops / INT8_PEAK_TOPS, 4)}
+    return {"q8_0_896x896_b1": q8, "q4_0_prefill_m512": pre}
+
+
+# --------------------------------------------------------------- ceilings --
+
+def ceilings(torch):
+    """Measured ceilings of this chip (libqmv_ceilings.so)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "gguf_quantized_matvec_amd", "libqmv_ceilings.so"))
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.qmv_ceil_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+    for f in ("qmv_ceil_mfma_i8", "qmv_ceil_mfma_f16", "qmv_ceil_epilogue"):
+        getattr(lib, f).argtypes = [P, I, I, P]
+    s = lambda: torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            best = t if best is None else min(best, t)
+        return best
+
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(nbytes // 16 // 16, dtype=torch.int32, device="cuda")
+    t = timed(lambda: lib.qmv_ceil_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), s()))
+    out = {"stream_read_GBs": round(nbytes / t / 1e9, 1)}
+    del buf, sink
+    blocks, iters = 256 * 8, 2000
+    o = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    t = timed(lambda: lib.qmv_ceil_mfma_i8(o.data_ptr(), blocks, iters, s()))
+    out["mfma_i8_TOPS"] = round(blocks * 4 * 4 * iters * 65536 / t / 1e12, 1)
+    t = timed(lambda: lib.qmv_ceil_mfma_f16(o.data_ptr(), blocks, iters, s()))
+    out["mfma_f16_TFLOPS"] = round(blocks * 4 * 4 * iters * 32768 / t / 1e12, 1)
+    t = timed(lambda: lib.qmv_ceil_epilogue(o.data_ptr(), blocks, iters, s()))
+    fma_s = blocks * 256 * 16 * iters / t
+    out["epilogue_Tfma_s"] = round(fma_s / 1e12, 2)
+    # one fma per output and 32-element block = 32 int8 MACs = 64 int8 ops
+    out["epilogue_bound_int8_TOPS"] = round(fma_s * 64 / 1e12, 1)
+    out["how"] = ("libqmv_ceilings.so (qmv_ceilings.hip): a 1 GiB read with 16-byte loads, 16 "
+                  "in flight per thread; 2048 workgroups x 4 waves of 4 independent MFMA chains; "
+                  "16 f32 fma chains per thread; best of 5 launches by HIP events")
+    return out
+
+
+# ----------------------------------------------------------- CPU baseline --
+
+def host_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    return {"nproc": os.cpu_count(), "affinity": aff, "model": model}
+
+
+def cpu_baseline(synth, seconds):
+    """The CPU oracle (plain C, f64 products, f32 quantisation) on the
+    headline step (the 8B-class layer at batch 1: quantise, seven products,
+    SwiGLU), rows split over the host threads this process may use (at most
+    16: the machine's host CPUs per GPU), for about `seconds`; plus single-thread
+    figures for the pages' own shapes."""
     import concurrent.futures as cf
 
     import numpy as np
 
     import oracle
-    import synth
-    blobs = {k: v[0].cpu().numpy() for k, v in W["copies"].items()}
-    x1, x2 = W["x1"].cpu().numpy(), W["x2"].cpu().numpy()
-    fmt = W["fmt"]
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
-    rb = {n: synth.row_bytes(fmt, K) for n, _, K in W["shapes"]}
-
-    def rows_job(name, N, K, xq, r0, r1):
-        b = blobs[name][r0 * rb[name]: r1 * rb[name]]
-        oracle.matmul_f64(fmt, b, r1 - r0, K, xq, 1, want_abs=False)
-
+    info = host_info()
+    threads = max(1, min(info["affinity"], MAX_HOST_THREADS))
     oracle.lib()
+    blobs = {}
+    for i, (name, fmt, N, K) in enumerate(LAYER):
+        blobs[name] = weights(synth, fmt, N, K, synth.seed_for(4, 10 + i), 0.02)
+    rb = {n: row_bytes(f, K) for n, f, _, K in LAYER}
+    spec = {n: (f, N, K) for n, f, N, K in LAYER}
+    xs = [synth.activations(1, 4096, synth.act_seed_for(4, 1) + j) for j in range(3)]
+    step_bytes = sum(int(b.size) for b in blobs.values())
+
+    def rows_job(name, xq, r0, r1):
+        f, _, K = spec[name]
+        y, _ = oracle.matmul_f64(f, blobs[name][r0 * rb[name]: r1 * rb[name]], r1 - r0, K, xq, 1,
+                                 want_abs=False)
+        return r0, y
+
+    def product(ex, name, xq):
+        N = spec[name][1]
+        per = math.ceil(N / threads)
+        y = np.zeros(N)
+        for f in [ex.submit(rows_job, name, xq, r0, min(N, r0 + per)) for r0 in range(0, N, per)]:
+            r0, part = f.result()
+            y[r0: r0 + part.shape[1]] = part[0]
+        return y
+
     steps = 0
     t0 = time.perf_counter()
-    with cf.ThreadPoolExecutor(cores) as ex:
+    with cf.ThreadPoolExecutor(threads) as ex:
         while True:
-            xq1 = oracle.quantize_act(x1)
-            xq2 = oracle.quantize_act(x2)
-            futs = []
-            for name, N, K in W["shapes"]:
-                xq = xq1 if K == 896 else xq2
-                per = math.ceil(N / cores)
-                for r0 in range(0, N, per):
-                    futs.append(ex.submit(rows_job, name, N, K, xq, r0, min(N, r0 + per)))
-            for f in futs:
-                f.result()
+            xa = oracle.quantize_act(xs[0])
+            for n in ("q", "k", "v"):
+                product(ex, n, xa)
+            product(ex, "o", oracle.quantize_act(xs[1]))
+            xc = oracle.quantize_act(xs[2])
+            gt = product(ex, "gate", xc).astype(np.float32)
+            up = product(ex, "up", xc).astype(np.float32)
+            h = oracle.swiglu(gt, up).reshape(1, -1)
+            product(ex, "down", oracle.quantize_act(h))
             steps += 1
             if time.perf_counter() - t0 >= seconds:
                 break
     dt = time.perf_counter() - t0
-    return {"value": round(W["step_bytes"] * steps / dt / 1e9, 4), "unit": "GB/s",
-            "cores": cores, "kind": "oracle",
-            "sample": f"{steps} steps of the Q4_0 FFN decode step (quantise both activations, "
-                      f"gate/up/down products in f64), rows split over {cores} threads, "
-                      f"{dt:.1f} s; tok/s {steps / dt:.2f}"}
+
+    # single thread, the pages' shapes at batch 1 (configs 1-3)
+    single = {}
+
+    def one(tag, fmt, N, K, seed, ds, rows=None):
+        blob = weights(synth, fmt, N, K, seed, ds)
+        xq = oracle.quantize_act(synth.activations(1, K, seed + 1))
+        n = rows or N
+        part = blob[: n * row_bytes(fmt, K)]
+        t = time.perf_counter()
+        oracle.matmul_f64(fmt, part, n, K, xq, 1, want_abs=False)
+        el = (time.perf_counter() - t) * N / n
+        single[tag] = {"s_per_call": round(el, 4), "weight_GBs": round(blob.size / el / 1e9, 3)}
+        if rows:
+            single[tag]["sample"] = f"first {n} of {N} rows, scaled to all rows"
+
+    one("q8_0_896x896", Q8_0, 896, 896, synth.seed_for(0, 0), 0.01)
+    one("q4_0_4864x896", Q4_0, 4864, 896, synth.seed_for(1, 0), 0.02)
+    one("q4_0_896x4864", Q4_0, 896, 4864, synth.seed_for(1, 2), 0.02)
+    one("q6_k_151936x1024", Q6_K, 151936, 1024, synth.seed_for(2, 0), 0.01, rows=16384)
+    one("q4_k_4864x1024", Q4_K, 4864, 1024, synth.seed_for(2, 1), 0.01)
+    return {"value": round(step_bytes * steps / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{steps} headline steps (8B-class layer, batch 1: 3 activation "
+                       f"quantisations, 7 products in f64, SwiGLU) in {dt:.1f} s with rows split "
+                       f"over {threads} threads; tok/s {steps / dt:.3f}"),
+            "host": {**info, "threads_used": threads,
+                     "why_threads": "at most 16: the host CPUs a GPU box allots to one GPU"},
+            "single_thread_b1": single}
 
 
-def suite(torch, g, synth, rotate_bytes, only=None):
-    """Per-matrix figures for every workload shape: GEMV at each decode batch
-    (weight GB/s) and GEMM at each prefill size (int8-equivalent TOPS), from
-    the time per launch of back-to-back graph launches over rotated copies.
-    only: a set of (workload, matrix index, rows) to restrict it to."""
-    res = []
-    L = g.lib()
-    for wl, spec in synth.WORKLOADS.items():
-        ci = list(synth.WORKLOADS).index(wl)
-        for mi, (fmt, N, K, ds) in enumerate(spec["mats"]):
-            batches = [B for B in spec["batches"] if only is None or (wl, mi, B) in only]
-            if not batches:
-                continue
-            blob, _ = synth.weights(fmt, N, K, synth.seed_for(ci, mi), dscale=ds)
-            wt = torch.from_numpy(blob).cuda()
-            nbytes = int(wt.numel())
-            R = max(1, min(64, math.ceil(rotate_bytes / nbytes)))
-            copies = [wt] + [wt.clone() for _ in range(R - 1)]
-            for B in batches:
-                x = torch.from_numpy(synth.activations(B, K, synth.act_seed_for(ci, B))).cuda()
-                xq = g.quantize(x)
-                y = torch.empty(B, N, dtype=torch.float32, device="cuda")
-                fn = L.qmv_launch if B <= 16 else L.qmm_launch
+# --------------------------------------------------------- profile helpers --
 
-                def launch(i, fn=fn, B=B, xq=xq, y=y):
-                    rc = fn(fmt, copies[i % R].data_ptr(), N, K, None, B, xq.data_ptr(),
-                            y.data_ptr(), torch.cuda.current_stream().cuda_stream)
-                    if rc:
-                        raise g.QmvError(rc, "suite")
-                launch(0)
-                n = max(R, 20) if B <= 16 else max(min(R, 10), 5)
-                med = graph_launch_us(torch, launch, n) * 1e-6
-                row = {"workload": wl, "fmt": synth.NAMES[fmt], "N": N, "K": K, "rows": B,
-                       "us": round(med * 1e6, 2), "weight_MB": round(nbytes / 1e6, 2)}
-                if B <= 16:
-                    gbs = nbytes / med / 1e9
-                    row.update(weight_GBs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
-                               tok_s=round(B / med, 1))
-                else:
-                    tops = 2.0 * B * N * K / med / 1e12
-                    row.update(int8_TOPS=round(tops, 1), mfma_frac=round(tops / INT8_PEAK_TOPS, 4))
-                res.append(row)
-                print(json.dumps({"suite_row": row}), file=sys.stderr, flush=True)
-                del x, xq, y
-            del copies, wt
-            torch.cuda.empty_cache()
-    return res
-
-
-def other_halves(torch, g, synth):
-    """The metric's other figures beside the headline decode step: the prefill
-    GEMM (int8-equivalent TOPS) at the pages' 512-token prompt (Q4_0 gate/up
-    and down) and at the 8B-class 2048-token shape (Q4_K 14336x4096), and the
-    largest decode GEMV (the Q6_K 151936x1024 LM head, batch 1)."""
-    rows = suite(torch, g, synth, 512 << 20,
-                 only={("q4_0_prefill512", 0, 512), ("q4_0_prefill512", 1, 512),
-                       ("8b_class", 2, 2048), ("kquant_lmhead", 0, 1)})
-    by = {(r["workload"], r["N"], r["K"], r["rows"]): r for r in rows}
-    gate, down = by[("q4_0_prefill512", 4864, 896, 512)], by[("q4_0_prefill512", 896, 4864, 512)]
-    big = by[("8b_class", 14336, 4096, 2048)]
-    lm = by[("kquant_lmhead", 151936, 1024, 1)]
-    ops512 = 2.0 * 512 * 4864 * 896 * 2
-    tops512 = ops512 / ((gate["us"] + down["us"]) * 1e-6) / 1e12
-    return {
-        "prefill": {
-            "unit": "int8-equivalent TOPS", "peak": INT8_PEAK_TOPS,
-            "q4_0_ffn_m512": {"TOPS": round(tops512, 1), "frac": round(tops512 / INT8_PEAK_TOPS, 4),
-                              "us_gate_4864x896": gate["us"], "us_down_896x4864": down["us"]},
-            "q4_k_14336x4096_m2048": {"TOPS": big["int8_TOPS"], "frac": big["mfma_frac"],
-                                      "us": big["us"]},
-            "timing": "HIP events around graph replays of back-to-back launches",
-        },
-        "lm_head": {"matrix": "Q6_K 151936x1024, batch 1", "weight_GBs": lm["weight_GBs"],
-                    "frac": lm["hbm_frac"], "us": lm["us"]},
-    }
+def profile_stage(torch, g, synth, name, launches=20):
+    Lw = Layer(torch, g, synth, 1, 1 << 30)
+    for i in range(launches):
+        Lw.stage(name, i % Lw.R)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_stage": name, "launches": launches}))
 
 
 def profile_matrix(torch, g, synth, spec, launches=20):
@@ -295,18 +547,34 @@ def profile_matrix(torch, g, synth, spec, launches=20):
     L = g.lib()
     fn = L.qmv_launch if rows <= 16 else L.qmm_launch
     for _ in range(launches):
-        rc = fn(fmt, w.data_ptr(), N, K, None, rows, xq.data_ptr(), y.data_ptr(),
-                torch.cuda.current_stream().cuda_stream)
-        if rc:
-            raise g.QmvError(rc, "profile_matrix")
+        _check(g, fn(fmt, w.data_ptr(), N, K, None, rows, xq.data_ptr(), y.data_ptr(),
+                     torch.cuda.current_stream().cuda_stream), "profile_matrix")
     torch.cuda.synchronize()
     print(json.dumps({"profile_matrix": spec, "fmt": synth.NAMES[fmt], "N": N, "K": K,
                       "rows": rows, "launches": launches}))
 
 
-def traffic_from(pmc_dir):
+def suite(torch, g, synth, rotate_bytes):
+    """Every workload matrix at each of its batch sizes: GEMV weight GB/s and
+    GEMM int8-equivalent TOPS, weights rotated over >= rotate_bytes."""
+    res = []
+    for wl, spec in synth.WORKLOADS.items():
+        ci = list(synth.WORKLOADS).index(wl)
+        for mi, (fmt, N, K, ds) in enumerate(spec["mats"]):
+            for B in spec["batches"]:
+                us, nb, R = matrix_us(torch, g, synth, fmt, N, K, B, synth.seed_for(ci, mi), ds,
+                                      rotate_bytes)
+                row = {"workload": wl, "fmt": synth.NAMES[fmt], "N": N, "K": K, "rows": B,
+                       "rotated_copies": R}
+                row.update(gemv_row(us, nb, B) if B <= 16 else gemm_row(us, B, N, K))
+                res.append(row)
+                print(json.dumps({"suite_row": row}), file=sys.stderr, flush=True)
+    return res
+
+
+def traffic_from(pmc_dir, kernel_filter):
     """profiles/traffic.json from four rocprofv3 --pmc runs under pmc_dir:
-    fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of `bench.py --profile-steps`),
+    fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of `bench.py --profile-stage`),
     calib_fetch/ and calib_write/ (the same counters of `bench.py --copy-calib`).
     Each counter is scaled by true bytes / counted bytes of the plain copy."""
     import csv
@@ -323,18 +591,14 @@ def traffic_from(pmc_dir):
             raise SystemExit(f"no {counter} rows under {os.path.join(pmc_dir, sub)}")
         return out
 
-    def copy_kib(sub, counter):
-        # the largest dispatch of the calibration run is the 256 MiB copy
-        return max(v for _, v in rows(sub, counter))
-
     copy_bytes = 256 << 20
-    f_scale = copy_bytes / (copy_kib("calib_fetch", "FETCH_SIZE") * 1024)
-    w_scale = copy_bytes / (copy_kib("calib_write", "WRITE_SIZE") * 1024)
-    fk = [v for k, v in rows("fetch", "FETCH_SIZE") if "k_dot" in k]
-    wk = [v for k, v in rows("write", "WRITE_SIZE") if "k_dot" in k]
+    f_scale = copy_bytes / (max(v for _, v in rows("calib_fetch", "FETCH_SIZE")) * 1024)
+    w_scale = copy_bytes / (max(v for _, v in rows("calib_write", "WRITE_SIZE")) * 1024)
+    fk = [v for k, v in rows("fetch", "FETCH_SIZE") if kernel_filter in k]
+    wk = [v for k, v in rows("write", "WRITE_SIZE") if kernel_filter in k]
     fetch = sum(fk) / len(fk) * 1024 * f_scale
     write = sum(wk) / len(wk) * 1024 * w_scale
-    out = {"kernel": "k_dot (grouped GEMV gate+up+down, Q4_0, batch 1)", "kernel_src_sha": kernel_src_sha(),
+    out = {"kernel_filter": kernel_filter, "kernel_src_sha": kernel_src_sha(),
            "dispatches": [len(fk), len(wk)],
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
@@ -343,31 +607,56 @@ def traffic_from(pmc_dir):
     print(json.dumps(out))
 
 
+def trace_summary(trace_dir):
+    """Per (kernel, grid) launch counts and durations from a rocprofv3
+    --kernel-trace run (its *kernel_trace.csv files)."""
+    import csv
+    import glob
+    import statistics
+    groups = {}
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"][:90], r.get("Grid_Size_X", r.get("Grid_Size", "")),
+                   r.get("Grid_Size_Y", ""), r.get("Workgroup_Size_X", r.get("Workgroup_Size", "")))
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups.setdefault(key, []).append(dur)
+    print("| kernel | grid x | grid y | workgroup | launches | mean us | median us | min us |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|")
+    for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{key[0]}` | {key[1]} | {key[2]} | {key[3]} | {len(d)} | "
+              f"{statistics.mean(d):.2f} | {statistics.median(d):.2f} | {min(d):.2f} |")
+
+
+# ------------------------------------------------------------------- main --
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--rotate-mib", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="leave out the prefill GEMM and LM-head figures")
+                    help="only the headline step (no batch-16 step, prefill, LM head, ceilings)")
     ap.add_argument("--suite", action="store_true",
                     help="also report every workload matrix (GEMV and GEMM) separately")
-    ap.add_argument("--profile-steps", type=int, default=0,
-                    help="only run this many eager steps (for counter collection)")
-    ap.add_argument("--traffic-from", default=None,
-                    help="write profiles/traffic.json from rocprofv3 --pmc output under DIR")
+    ap.add_argument("--profile-stage", default=None, choices=list(STAGES),
+                    help="only launch one stage of the layer step 20 times, eagerly")
+    ap.add_argument("--profile-matrix", default=None, metavar="WORKLOAD:INDEX:ROWS",
+                    help="only launch one workload matrix 20 times, eagerly")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 256 MiB device copy 10 times (counter calibration)")
-    ap.add_argument("--profile-matrix", default=None, metavar="WORKLOAD:INDEX:ROWS",
-                    help="only launch one workload matrix (e.g. 8b_class:2:2048) 20 times, "
-                         "eagerly (for counter collection)")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR")
+    ap.add_argument("--traffic-kernel", default="k_dot")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR")
     args = ap.parse_args()
 
     if args.traffic_from:
-        traffic_from(args.traffic_from)
+        traffic_from(args.traffic_from, args.traffic_kernel)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -397,59 +686,28 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes": a.numel(), "launches": 10}))
         return
-
+    if args.profile_stage:
+        profile_stage(torch, g, synth, args.profile_stage)
+        return
     if args.profile_matrix:
         profile_matrix(torch, g, synth, args.profile_matrix)
         return
 
-    W = ffn_workload(torch, g, synth, args.rotate_mib << 20)
-    step = make_ffn_step(torch, g, W)
-    step(0, None)                       # eager run: device check, lazy init
-    torch.cuda.synchronize()
-    if args.profile_steps:
-        for i in range(args.profile_steps):
-            step(i, None)
-        torch.cuda.synchronize()
-        print(json.dumps({"profile_steps": args.profile_steps}))
-        return
-
-    graphs = {}
-
-    def make(n):
-        return GraphSteps(torch, step, n)
-
-    graphs["full"] = make(W["R"])
-    # capture the partial-replay graphs too before anything is timed
-    for n in (args.warmup, args.steps):
-        r = n % W["R"]
-        if r and r not in graphs:
-            graphs[r] = make(r)
-    run_steps(graphs, make, args.warmup)
-    torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    run_steps(graphs, make, args.steps)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-
-    # the dominant (only) kernel: time per launch of the grouped GEMV, back to
-    # back over every rotated copy
-    per_launch_us = graph_launch_us(torch, lambda i: step(i), W["R"])
-    # every GEMV reads its x; gate and down write their Q8_0 blocks, up does not
-    alg = {"gate": gemv_alg_bytes(W["fmt"], 4864, 896, 1, g, fused=True),
-           "up": gemv_alg_bytes(W["fmt"], 4864, 896, 1, g, fused=True) - (896 // 32) * 34,
-           "down": gemv_alg_bytes(W["fmt"], 896, 4864, 1, g, fused=True)}
-    alg_per_launch = alg["gate"] + alg["up"] + alg["down"]
-    achieved = alg_per_launch / (per_launch_us * 1e-6) / 1e9
+    rot = args.rotate_mib << 20
+    print("step: headline layer, batch 1", file=sys.stderr, flush=True)
+    r1 = time_layer(torch, g, synth, 1, args.steps, args.warmup, rot)
+    wall = r1["wall_s"]
+    value = r1["step_bytes"] * args.steps / wall / 1e9
+    dom = max(r1["stage_us"], key=r1["stage_us"].get)
+    dom_us = r1["stage_us"][dom]
+    achieved = r1["stage_alg_bytes"][dom] / (dom_us * 1e-6) / 1e9
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tf = json.load(open(TRAFFIC_FILE))
-        if tf.get("kernel_src_sha") == kernel_src_sha():
+        if tf.get("kernel_src_sha") == kernel_src_sha() and tf.get("stage") == dom:
             traffic = tf.get("bytes_per_launch")
 
-    value = W["step_bytes"] * args.steps / wall / 1e9
     out = {
         "metric": "decode GEMV weight-GB/s (% HBM peak); prefill int8 GEMM TOPS (% MFMA peak)",
         "value": round(value, 2),
@@ -462,37 +720,50 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "i8",
-        "data": "synthetic (seeded GGUF Q4_0 blocks and N(0,1) activations)",
-        "config": {"workload": "Q4_0 SwiGLU FFN decode, batch 1: gate+up 4864x896, down 896x4864 "
-                               "(llamay Qwen2.5-0.5B shapes)",
-                   "global_batch": 1, "weights_per_step_bytes": W["step_bytes"],
-                   "rotated_copies": W["R"], "graph_replay": True,
-                   "tok_s": round(args.steps / wall, 1),
-                   "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4)},
+        "data": "synthetic (seeded GGUF Q4_K / Q6_K blocks, N(0,1) activations)",
+        "config": {
+            "workload": ("8B-class decoder layer, decode batch 1: [q 4096x4096, k/v 1024x4096] "
+                         "-> o 4096x4096 -> [gate, up 14336x4096 + SwiGLU] -> down 4096x14336; "
+                         "Q4_K, down Q6_K; 5 launches per step in dependency order"),
+            "global_batch": 1, "weights_per_step_bytes": r1["step_bytes"],
+            "rotated_copies": r1["R"], "graph_replay": True,
+            "tok_s": round(args.steps / wall, 1),
+            "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4),
+            "stage_us": {k: round(v, 2) for k, v in r1["stage_us"].items()},
+        },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": "k_dot<Q4_0, 1, fused> (grouped GEMV: gate, up, down)",
-                     "avg_launch_us": round(per_launch_us, 3),
-                     "launches_timed": W["R"],
+                     "traffic": traffic, "stage": dom, "kernel": STAGE_KERNEL[dom],
+                     "avg_launch_us": round(dom_us, 3), "launches_timed": r1["R"],
+                     "alg_bytes_per_launch": r1["stage_alg_bytes"][dom],
                      "timing": "HIP events on the launch stream around a graph replay of the "
-                               "step's grouped launch back to back over every rotated copy; "
-                               "time per launch includes the inter-node dispatch gap",
-                     "alg_bytes_per_launch": alg},
+                               "stage's launches back to back over every rotated copy; time per "
+                               "launch includes the dispatch gap between graph nodes"},
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
+        print("step: cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(synth, args.cpu_seconds)
     if not args.no_extra:
-        del graphs
-        W.clear()
-        torch.cuda.empty_cache()
-        graphs = None
-        out.update(other_halves(torch, g, synth))
+        print("step: layer batch 16", file=sys.stderr, flush=True)
+        n16 = max(20, args.steps // 4)
+        r16 = time_layer(torch, g, synth, 16, n16, max(2, args.warmup // 4), rot)
+        v16 = r16["step_bytes"] * n16 / r16["wall_s"] / 1e9
+        out["decode_b16"] = {"value_GBs": round(v16, 1), "hbm_frac": round(v16 / HBM_PEAK_GBS, 4),
+                             "ms_per_step": round(r16["wall_s"] / n16 * 1e3, 5),
+                             "tok_s": round(16 * n16 / r16["wall_s"], 1), "steps": n16,
+                             "stage_us": {k: round(v, 2) for k, v in r16["stage_us"].items()}}
+        print("step: prefill M=2048", file=sys.stderr, flush=True)
+        out["prefill_m2048"] = {"unit": "int8-equivalent TOPS", "peak": INT8_PEAK_TOPS,
+                                **prefill_8b(torch, g, synth)}
+        print("step: lm head", file=sys.stderr, flush=True)
+        out["lm_head_q6_k_151936x1024"] = lm_head(torch, g, synth)
+        print("step: qwen shapes", file=sys.stderr, flush=True)
+        out["qwen_ffn_b1"] = qwen_ffn(torch, g, synth, rot)
+        out.update(qwen_small(torch, g, synth))
+        print("step: ceilings", file=sys.stderr, flush=True)
+        out["ceilings"] = ceilings(torch)
     if args.suite:
-        graphs = None
-        W.clear()
-        torch.cuda.empty_cache()
-        out["suite"] = suite(torch, g, synth, 512 << 20)
+        out["suite"] = suite(torch, g, synth, rot)
     print(json.dumps(out))
 
 

@@ -20,7 +20,8 @@ TYPES = {"Q4_0": Q4_0, "Q4_1": Q4_1, "Q5_0": Q5_0, "Q5_1": Q5_1, "Q8_0": Q8_0, "
 BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_1: (32, 20), Q5_1: (32, 24),
          Q8_1: (32, 36), Q4_K: (256, 144), Q6_K: (256, 210)}
 EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
-           "qmv_partials_launch", "qmv_strerror")
+           "qmv_partials_launch", "qmv_gateup_act_bytes",
+           "qmv_launch_gateup_swiglu", "qmv_strerror")
 MAX_BATCH = 16
 MAX_GROUP = 8
 
@@ -55,8 +56,11 @@ def lib() -> ctypes.CDLL:
         L.qmm_launch.argtypes = [I, P, I64, I64, P, I64, P, P, P]
         L.qmv_launch_group.argtypes = [I, I64, ctypes.POINTER(Gemv), I, P]
         L.qmv_partials_launch.argtypes = [I, P, I64, I64, P, I64, P, P]
+        L.qmv_gateup_act_bytes.argtypes = [I64, I64, I64]
+        L.qmv_gateup_act_bytes.restype = ctypes.c_size_t
+        L.qmv_launch_gateup_swiglu.argtypes = [I, P, P, I64, I64, P, I64, P, P, P]
         for f in ("quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
-                  "qmv_partials_launch"):
+                  "qmv_partials_launch", "qmv_launch_gateup_swiglu"):
             getattr(L, f).restype = I
         L.qmv_strerror.argtypes = [I]
         L.qmv_strerror.restype = ctypes.c_char_p
@@ -102,6 +106,16 @@ def qmm_launch(type: int, w: int, N: int, K: int, x, M: int, xq: int, y: int,
 def qmv_partials_launch(type: int, w: int, N: int, K: int, xq: int, B: int, P: int,
                         stream: int = 0) -> None:
     _check(lib().qmv_partials_launch(type, w, N, K, xq, B, P, stream), "qmv_partials_launch")
+
+
+def qmv_gateup_act_bytes(B: int, N: int, K: int) -> int:
+    return int(lib().qmv_gateup_act_bytes(B, N, K))
+
+
+def qmv_launch_gateup_swiglu(type: int, w_gate: int, w_up: int, N: int, K: int, x, B: int,
+                             xq: int, h: int, stream: int = 0) -> None:
+    _check(lib().qmv_launch_gateup_swiglu(type, w_gate, w_up, N, K, x, B, xq, h, stream),
+           "qmv_launch_gateup_swiglu")
 
 
 def qmv_strerror(code: int) -> str:
@@ -196,6 +210,27 @@ def matvec_group(type: int, items, stream=None):
         ys.append(y)
     qmv_launch_group(type, B, descs, _stream(stream))
     return ys
+
+
+def gateup_swiglu(type: int, w_gate, w_up, N: int, K: int, x=None, xq=None, B=None, h=None,
+                  stream=None):
+    """h [B, N] f32 = silu(x @ Wg^T) * (x @ Wu^T) (x None: use the staged xq)."""
+    import torch
+    if x is not None:
+        B = x.shape[0]
+    if xq is None:
+        n = qmv_gateup_act_bytes(B, N, K)
+        if n == 0:
+            raise ValueError(f"bad shape B={B} N={N} K={K}")
+        xq = torch.empty(n, dtype=torch.uint8, device=w_gate.device)
+    if h is None:
+        h = torch.empty(B, N, dtype=torch.float32, device=w_gate.device)
+    xp = _dev(x, torch.float32, "x") if x is not None else None
+    qmv_launch_gateup_swiglu(type, _dev(w_gate, torch.uint8, "w_gate"),
+                             _dev(w_up, torch.uint8, "w_up"), N, K, xp, B,
+                             _dev(xq, torch.uint8, "xq"), _dev(h, torch.float32, "h"),
+                             _stream(stream))
+    return h
 
 
 def matmul(type: int, w, N: int, K: int, x=None, xq=None, M=None, y=None, stream=None):

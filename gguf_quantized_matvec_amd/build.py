@@ -1,4 +1,5 @@
-"""Build libqmv.so in-tree with hipcc for gfx950.
+"""Build libqmv.so (the product library) and libqmv_ceilings.so (the
+benchmark's measurement kernels) in-tree with hipcc for gfx950.
 
     python -m gguf_quantized_matvec_amd.build
 """
@@ -11,6 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmv.so")
+CEIL_LIB = os.path.join(HERE, "libqmv_ceilings.so")
+CEIL_SRC = os.path.join(CSRC, "qmv_ceilings.hip")
 # (source, extra flags): the GEMV kernels take MFMA results straight into
 # VGPRs (no accumulation-register copies); the GEMM keeps the default choice
 SOURCES = [(os.path.join(CSRC, "qmv_kernels.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
@@ -38,16 +41,18 @@ def _run(cmd: list) -> None:
 def build() -> str:
     # the translation units compile in parallel (one hipcc process each)
     from concurrent.futures import ThreadPoolExecutor
-    objs = [os.path.join(CSRC, os.path.basename(src) + ".o") for src, _ in SOURCES]
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
+    srcs = SOURCES + [(CEIL_SRC, [])]
+    objs = [os.path.join(CSRC, os.path.basename(src) + ".o") for src, _ in srcs]
+    with ThreadPoolExecutor(len(srcs)) as ex:
         for f in [ex.submit(_run, [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj])
-                  for (src, extra), obj in zip(SOURCES, objs)]:
+                  for (src, extra), obj in zip(srcs, objs)]:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", *objs, "-o", tmp])
+    for lib, parts in ((LIB, objs[:-1]), (CEIL_LIB, objs[-1:])):
+        tmp = lib + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", *parts, "-o", tmp])
+        os.replace(tmp, lib)
     for obj in objs:
         os.remove(obj)
-    os.replace(tmp, LIB)
     return LIB
 
 

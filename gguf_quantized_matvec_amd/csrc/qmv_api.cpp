@@ -130,6 +130,29 @@ int qmv_launch_group(int type, int64_t B, const qmv_gemv* g, int count, void* st
     return launched(qmv::launch_qmv_group(type, d, count, B, static_cast<hipStream_t>(stream)));
 }
 
+size_t qmv_gateup_act_bytes(int64_t B, int64_t N, int64_t K) {
+    if (B < 1 || B > QMV_MAX_BATCH || N < 1 || N > INT32_MAX || K < 32 || K > QMV_MAX_K ||
+        K % 32)
+        return 0;
+    return (size_t)qmv::gateup_act_bytes(B, N, K);
+}
+
+int qmv_launch_gateup_swiglu(int type, const void* w_gate, const void* w_up, int64_t N,
+                             int64_t K, const float* x, int64_t B, void* xq, float* h,
+                             void* stream) {
+    int rc = check_weights(type, w_gate, N, K);
+    if (rc) return rc;
+    if ((rc = check_weights(type, w_up, N, K))) return rc;
+    if (B < 1 || B > QMV_MAX_BATCH) return QMV_EINVAL_SHAPE;
+    if (!xq || !h || !aligned(xq, 16) || !aligned(h, 4)) return QMV_EINVAL_PTR;
+    if (x && !aligned(x, 4)) return QMV_EINVAL_PTR;
+    if ((rc = check_device())) return rc;
+    return launched(qmv::launch_gateup(type, static_cast<const uint8_t*>(w_gate),
+                                       static_cast<const uint8_t*>(w_up), N, K, x,
+                                       static_cast<uint8_t*>(xq), B, h,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t M,
                void* xq, float* y, void* stream) {
     return matmul_common(type, w, N, K, x, M, QMV_MAX_M, xq, y, stream, true);

@@ -101,6 +101,14 @@ int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
 // count GEMVs of one type and row count: one launch if the lane-per-chunk
 // kernel takes them all (and all or none quantise x), else one after another.
 int launch_qmv_group(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s);
+// Gate/up pair of a SwiGLU FFN: h[rows][N] = silu(x Wg^T) * (x Wu^T).  xq
+// holds gateup_act_bytes(rows, N, K) bytes.
+bool gateup_is_one_launch(int64_t rows, int64_t K);
+inline int64_t gateup_act_bytes(int64_t rows, int64_t N, int64_t K) {
+    return align256(act_layout(rows, K).total) + 2 * align256(rows * N * 4);
+}
+int launch_gateup(int type, const uint8_t* wg, const uint8_t* wu, int64_t N, int64_t K,
+                  const float* x, uint8_t* xq, int64_t rows, float* h, hipStream_t s);
 int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* xq,
                     int64_t rows, int32_t* P, hipStream_t s);
 int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,

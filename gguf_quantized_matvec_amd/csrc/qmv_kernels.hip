@@ -1083,6 +1083,7 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
 // in the kernel (FUSED), or the staged quantisation in xq.
 struct DotJob {
     const uint8_t* w;
+    const uint8_t* w2;  // paired launch (gate/up + SwiGLU): the up blob; w is the gate blob
     float* y;
     const float* x;   // FUSED: f32 activations [B][K]
     uint8_t* xq;      // staged quantisation; FUSED: written by the job's first workgroup (may be NULL)
@@ -1118,14 +1119,30 @@ __device__ __forceinline__ int small_div(int a, int b) {
 // chunk straight into registers, issued before the activations are staged.
 // Chunk sums are added in chunk order per row through a small LDS buffer,
 // and each row's result is stored once, at the end.
-template <int FMT, int B, bool FUSED, bool SINGLE>
+// SwiGLU of one output element: silu(g) * u with silu(g) = g / (1 + e^-g),
+// evaluated in f64 as t = exp(-g), s = g / (1 + t), h = s * u and rounded
+// once to f32 (the llama-family feed-forward gate; llamay "Models and
+// formats", architectures table).
+__device__ __forceinline__ float swiglu(float g, float u) {
+    const double gd = (double)g;
+    const double t = exp(-gd);
+    const double s = gd / (1.0 + t);
+    return (float)(s * (double)u);
+}
+
+// Launch modes of the dot kernel: a group of GEMVs (job = blockIdx.y), one
+// GEMV, or one gate/up pair whose rows are computed side by side and leave
+// h = silu(gate) * up instead of two outputs.
+constexpr int MODE_GROUP = 0, MODE_SINGLE = 1, MODE_PAIRED = 2;
+
+template <int FMT, int B, bool FUSED, int MODE>
 __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     using F = Fmt<FMT>;
     constexpr int NWD = DotFmt<FMT>::NWD;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // this workgroup's job (one kernel-argument round trip)
     DotJob J;
-    if constexpr (SINGLE) {
+    if constexpr (MODE != MODE_GROUP) {
         J = jobs.j[0];
     } else {
         J = jobs.j[blockIdx.y];
@@ -1139,7 +1156,10 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     const int64_t R = (K / F::QK) * F::BB;
     const int LPR = C <= 64 ? C : 64, G = 64 / LPR;  // lanes per row, rows per unit
     const int PR = (C + 63) >> 6;  // passes (1 unless C > 64)
-    const int64_t units = C <= 64 ? (N + G - 1) / G : N;
+    // output rows per unit: G, or G/2 gate/up pairs (lane rows 0..GP-1 take
+    // gate rows, GP..2GP-1 the same up rows; the launcher ensures C <= 32)
+    const int GP = MODE == MODE_PAIRED ? G >> 1 : G;
+    const int64_t units = C <= 64 ? (N + GP - 1) / GP : N;
     const int lrow = small_div(lane, LPR), lchunk = lane - lrow * LPR;  // this lane's row in the unit, chunk
     if ((int64_t)blockIdx.x * jobs.waves >= units) return;  // surplus workgroup of a smaller job
     const int64_t u = (int64_t)blockIdx.x * jobs.waves + wv;
@@ -1147,9 +1167,13 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
 
     auto chunk_of = [&](int q, int64_t& row, int& c) {
         // lanes past the unit's G rows (64 % C of them) get a row past N: idle
-        row = C <= 64 ? (lrow < G ? u * G + lrow : N) : u;
+        if constexpr (MODE == MODE_PAIRED)
+            row = lrow < 2 * GP ? u * GP + (lrow < GP ? lrow : lrow - GP) : N;
+        else
+            row = C <= 64 ? (lrow < G ? u * G + lrow : N) : u;
         c = C <= 64 ? lchunk : 64 * q + lane;
     };
+    const uint8_t* wsrc = MODE == MODE_PAIRED && lrow >= GP ? J.w2 : J.w;
     auto issue = [&](int q, uint32_t (&r)[NWD]) {
         int64_t row;
         int c;
@@ -1158,7 +1182,7 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
         const int64_t off = row * R + (int64_t)c * F::CB;
         const bool near_end = valid && off + 4 * NWD > J.wbytes;
         if (valid) {
-            load_chunk_regs<FMT>(J.w, off, J.wbytes, __builtin_amdgcn_ballot_w64(near_end) != 0, r);
+            load_chunk_regs<FMT>(wsrc, off, J.wbytes, __builtin_amdgcn_ballot_w64(near_end) != 0, r);
         } else {
 #pragma unroll
             for (int i = 0; i < NWD; i++) r[i] = 0;
@@ -1361,6 +1385,29 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
         }
         wave_sync();
     }
+    if constexpr (MODE == MODE_PAIRED) {
+        // the gate and up sums of each output row meet in LDS; the gate
+        // lane writes h = silu(gate) * up
+#pragma unroll
+        for (int j = 0; j < B; j++) {
+            const int t = lane + 64 * j;
+            if (t < G * B) {
+                const int m = small_div(t, G), rl = t - m * G;
+                pbuf[m][rl] = yacc[j];
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int j = 0; j < B; j++) {
+            const int t = lane + 64 * j;
+            if (t < G * B) {
+                const int m = small_div(t, G), rl = t - m * G;
+                const int64_t orow = u * GP + rl;
+                if (rl < GP && orow < N) J.y[m * N + orow] = swiglu(yacc[j], pbuf[m][GP + rl]);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < B; j++) {
         const int t = lane + 64 * j;
@@ -1372,10 +1419,20 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     }
 }
 
+// h = silu(g) * u element by element (the gate/up pair's fallback path).
+__global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ g,
+                                                const float* __restrict__ u,
+                                                float* __restrict__ h, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) h[i] = swiglu(g[i], u[i]);
+}
+
 // Workgroups of the dot kernel for one GEMV: one wave per unit, 4 per group.
-inline int64_t dot_blocks(int type, int64_t N, int64_t K, int waves) {
+// paired: a gate/up pair (a unit holds G/2 rows of each).
+inline int64_t dot_blocks(int type, int64_t N, int64_t K, int waves, bool paired = false) {
     const int nb = (int)(K / 32), C = (nb + 7) / 8;
-    const int64_t G = 64 / (C <= 64 ? C : 64);  // rows per unit, as k_dot
+    int64_t G = 64 / (C <= 64 ? C : 64);  // rows per unit, as k_dot
+    if (paired) G >>= 1;
     (void)type;
     const int64_t units = C <= 64 ? (N + G - 1) / G : N;
     return (units + waves - 1) / waves;
@@ -1401,41 +1458,48 @@ inline int raise_lds_limit(const void* kernel, std::atomic<int> (&state)[64]) {
     return 0;
 }
 
-template <int FMT, int B, bool FUSED, bool SINGLE>
+template <int FMT, int B, bool FUSED, int MODE>
 int launch_dot_kernel(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
     static std::atomic<int> lds_state[64];
-    const int arc = raise_lds_limit(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED, SINGLE>),
+    const int arc = raise_lds_limit(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED, MODE>),
                                     lds_state);
     if (arc) return arc;
-    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, SINGLE>), dim3((unsigned)blocks, (unsigned)jobs.count),
+    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, MODE>), dim3((unsigned)blocks, (unsigned)jobs.count),
                        dim3(64 * jobs.waves), shmem, s, jobs);
     return (int)hipGetLastError();
 }
 
 template <int FMT, int B, bool FUSED>
-int launch_dot_jobs(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
-    return jobs.count == 1 ? launch_dot_kernel<FMT, B, FUSED, true>(jobs, blocks, shmem, s)
-                           : launch_dot_kernel<FMT, B, FUSED, false>(jobs, blocks, shmem, s);
+int launch_dot_jobs(const DotJobs& jobs, bool paired, int64_t blocks, size_t shmem,
+                    hipStream_t s) {
+    if (paired) return launch_dot_kernel<FMT, B, FUSED, MODE_PAIRED>(jobs, blocks, shmem, s);
+    return jobs.count == 1 ? launch_dot_kernel<FMT, B, FUSED, MODE_SINGLE>(jobs, blocks, shmem, s)
+                           : launch_dot_kernel<FMT, B, FUSED, MODE_GROUP>(jobs, blocks, shmem, s);
 }
 
 template <int FMT>
-int launch_dot_rows(const DotJobs& jobs, int64_t rows, bool fused, int64_t blocks, size_t shmem,
-                    hipStream_t s) {
+int launch_dot_rows(const DotJobs& jobs, int64_t rows, bool fused, bool paired, int64_t blocks,
+                    size_t shmem, hipStream_t s) {
     switch (rows) {
-    case 1: return fused ? launch_dot_jobs<FMT, 1, true>(jobs, blocks, shmem, s)
-                         : launch_dot_jobs<FMT, 1, false>(jobs, blocks, shmem, s);
-    case 2: return fused ? launch_dot_jobs<FMT, 2, true>(jobs, blocks, shmem, s)
-                         : launch_dot_jobs<FMT, 2, false>(jobs, blocks, shmem, s);
-    case 3: return fused ? launch_dot_jobs<FMT, 3, true>(jobs, blocks, shmem, s)
-                         : launch_dot_jobs<FMT, 3, false>(jobs, blocks, shmem, s);
-    default: return fused ? launch_dot_jobs<FMT, 4, true>(jobs, blocks, shmem, s)
-                          : launch_dot_jobs<FMT, 4, false>(jobs, blocks, shmem, s);
+    case 1: return fused ? launch_dot_jobs<FMT, 1, true>(jobs, paired, blocks, shmem, s)
+                         : launch_dot_jobs<FMT, 1, false>(jobs, paired, blocks, shmem, s);
+    case 2: return fused ? launch_dot_jobs<FMT, 2, true>(jobs, paired, blocks, shmem, s)
+                         : launch_dot_jobs<FMT, 2, false>(jobs, paired, blocks, shmem, s);
+    case 3: return fused ? launch_dot_jobs<FMT, 3, true>(jobs, paired, blocks, shmem, s)
+                         : launch_dot_jobs<FMT, 3, false>(jobs, paired, blocks, shmem, s);
+    default: return fused ? launch_dot_jobs<FMT, 4, true>(jobs, paired, blocks, shmem, s)
+                          : launch_dot_jobs<FMT, 4, false>(jobs, paired, blocks, shmem, s);
     }
 }
 
 // One launch of the dot kernel over `count` GEMVs of one type and row count.
-int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s) {
+// up != NULL: one gate/up pair (d[0].w the gate blob, up the up blob, count
+// 1) whose output d[0].y receives h = silu(gate) * up.
+int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s,
+               const uint8_t* up = nullptr) {
     if (count < 1 || count > MAX_JOBS) return (int)hipErrorInvalidValue;
+    const bool paired = up != nullptr;
+    if (paired && count != 1) return (int)hipErrorInvalidValue;
     DotJobs jobs{};
     jobs.count = count;
     int64_t blocks = 0;
@@ -1445,7 +1509,7 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
     // then 8-wave workgroups fit the same waves in one round of workgroups
     // (one per CU) instead of leaving a second round for a few CUs.
     int64_t blocks4 = 0;
-    for (int k = 0; k < count; k++) blocks4 += dot_blocks(type, d[k].N, d[k].K, 4);
+    for (int k = 0; k < count; k++) blocks4 += dot_blocks(type, d[k].N, d[k].K, 4, paired);
     jobs.waves = blocks4 > 256 && blocks4 <= 512 ? 8 : 4;
     // Rows of the grid in decreasing workgroup count: workgroups are
     // dispatched row after row at a limited rate, so the surplus (exiting)
@@ -1466,6 +1530,7 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
         const ActLayout L = act_layout(rows, d[k].K);
         DotJob& J = jobs.j[jk];
         J.w = d[k].w;
+        J.w2 = up;
         J.y = d[k].y;
         J.x = d[k].x;
         J.xq = d[k].xq;
@@ -1476,21 +1541,21 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
         J.rda = L.rda;
         J.rca = L.rca;
         J.rs16 = L.rs16;
-        const int64_t bk = dot_blocks(type, d[k].N, d[k].K, jobs.waves);
+        const int64_t bk = dot_blocks(type, d[k].N, d[k].K, jobs.waves, paired);
         blocks = bk > blocks ? bk : blocks;  // grid x: the largest job
         const size_t sh = dot_shmem((int)rows, d[k].K, jobs.waves);
         shmem = sh > shmem ? sh : shmem;
     }
     if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
     switch (type) {
-    case T_Q8_0: return launch_dot_rows<T_Q8_0>(jobs, rows, fused, blocks, shmem, s);
-    case T_Q4_0: return launch_dot_rows<T_Q4_0>(jobs, rows, fused, blocks, shmem, s);
-    case T_Q5_0: return launch_dot_rows<T_Q5_0>(jobs, rows, fused, blocks, shmem, s);
-    case T_Q4_1: return launch_dot_rows<T_Q4_1>(jobs, rows, fused, blocks, shmem, s);
-    case T_Q5_1: return launch_dot_rows<T_Q5_1>(jobs, rows, fused, blocks, shmem, s);
-    case T_Q8_1: return launch_dot_rows<T_Q8_1>(jobs, rows, fused, blocks, shmem, s);
-    case T_Q4_K: return launch_dot_rows<T_Q4_K>(jobs, rows, fused, blocks, shmem, s);
-    case T_Q6_K: return launch_dot_rows<T_Q6_K>(jobs, rows, fused, blocks, shmem, s);
+    case T_Q8_0: return launch_dot_rows<T_Q8_0>(jobs, rows, fused, paired, blocks, shmem, s);
+    case T_Q4_0: return launch_dot_rows<T_Q4_0>(jobs, rows, fused, paired, blocks, shmem, s);
+    case T_Q5_0: return launch_dot_rows<T_Q5_0>(jobs, rows, fused, paired, blocks, shmem, s);
+    case T_Q4_1: return launch_dot_rows<T_Q4_1>(jobs, rows, fused, paired, blocks, shmem, s);
+    case T_Q5_1: return launch_dot_rows<T_Q5_1>(jobs, rows, fused, paired, blocks, shmem, s);
+    case T_Q8_1: return launch_dot_rows<T_Q8_1>(jobs, rows, fused, paired, blocks, shmem, s);
+    case T_Q4_K: return launch_dot_rows<T_Q4_K>(jobs, rows, fused, paired, blocks, shmem, s);
+    case T_Q6_K: return launch_dot_rows<T_Q6_K>(jobs, rows, fused, paired, blocks, shmem, s);
     }
     return (int)hipErrorInvalidValue;
 }
@@ -1663,6 +1728,40 @@ int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* x
     case T_Q6_K: return launch_qmv_ni<T_Q6_K, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     }
     return (int)hipErrorInvalidValue;
+}
+
+bool gateup_is_one_launch(int64_t rows, int64_t K) {
+    const int64_t C = (K / 32 + 7) / 8;
+    return use_dot(rows, K) && C <= 32;  // at least one gate/up row pair per wave
+}
+
+int launch_gateup(int type, const uint8_t* wg, const uint8_t* wu, int64_t N, int64_t K,
+                  const float* x, uint8_t* xq, int64_t rows, float* h, hipStream_t s) {
+    if (gateup_is_one_launch(rows, K)) {
+        // one launch: each wave takes matching gate and up rows (the
+        // quantisation fused as in qmv_launch, with the same rule for when
+        // the workgroups' re-reads of x call for a launch of its own)
+        if (x && (!aligned16(x) ||
+                  dot_blocks(type, N, K, 4, true) * rows * K * 4 > 2 * N * row_bytes(type, K))) {
+            const int rc = launch_quantize(x, xq, rows, K, ST_ROW, s);
+            if (rc) return rc;
+            x = nullptr;
+        }
+        const GemvDesc d{wg, N, K, x, xq, h};
+        return launch_dot(type, &d, 1, rows, s, wu);
+    }
+    // otherwise: quantise once, gate and up into the scratch after the
+    // activation copy, then the SwiGLU
+    const int64_t act = align256(act_layout(rows, K).total);
+    float* gt = reinterpret_cast<float*>(xq + act);
+    float* ut = reinterpret_cast<float*>(xq + act + align256(rows * N * 4));
+    int rc = 0;
+    if (x && (rc = launch_quantize(x, xq, rows, K, staging_for(rows, K), s))) return rc;
+    if ((rc = launch_qmv(type, wg, N, K, nullptr, xq, rows, gt, s))) return rc;
+    if ((rc = launch_qmv(type, wu, N, K, nullptr, xq, rows, ut, s))) return rc;
+    const int64_t n = rows * N;
+    hipLaunchKernelGGL(k_swiglu, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gt, ut, h, n);
+    return (int)hipGetLastError();
 }
 
 int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,

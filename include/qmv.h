@@ -147,6 +147,32 @@ typedef struct qmv_gemv {
  * another entry reads or writes. */
 int qmv_launch_group(int type, int64_t B, const qmv_gemv* g, int count, void* stream);
 
+/* Bytes of scratch `xq` for qmv_launch_gateup_swiglu with B rows, N
+ * outputs and K inputs: the activation quantisation as for qmv_launch
+ * (qmv_act_bytes(B, K) laid out the same way, first), then room for the two
+ * intermediate products when the pair does not run as one launch.  Returns 0
+ * for an invalid shape. */
+size_t qmv_gateup_act_bytes(int64_t B, int64_t N, int64_t K);
+
+/* Gate and up projections of a SwiGLU feed-forward block in decode, fused:
+ * h[B][N] = silu(x * Wg^T) * (x * Wu^T), with silu(g) = g / (1 + e^-g) — the
+ * feed-forward gate of the llama family ("Models and formats", architectures
+ * table).  Each product is bit-identical to qmv_launch on its own weights;
+ * each element of h is then evaluated in f64 as t = exp(-g), s = g / (1 + t),
+ * s * u and rounded once to f32.  w_gate and w_up are two N x K blobs of one
+ * type (as for qmv_launch); 1 <= B <= 16.  x: [B][K] f32 (4-byte aligned),
+ * quantised into xq as qmv_launch does, or NULL to use the quantisation
+ * already staged at the start of xq (as quantize_act_q8_0 leaves it).  xq:
+ * qmv_gateup_act_bytes(B, N, K) bytes, 16-byte aligned.  h: [B][N] f32,
+ * 4-byte aligned; feed it to qmv_launch as the down projection's x.  For
+ * B <= 4 and K <= 8192 (and activation rows that fit the kernel's LDS) the
+ * pair is one launch in which each wave multiplies matching rows of both
+ * matrices and writes h; otherwise the two GEMVs run one after another and a
+ * third launch forms h.  h must not overlap x, xq or the weights. */
+int qmv_launch_gateup_swiglu(int type, const void* w_gate, const void* w_up, int64_t N,
+                             int64_t K, const float* x, int64_t B, void* xq, float* h,
+                             void* stream);
+
 /* Prefill GEMM (MatMul): y[M][N] = x[M][K] * W^T for any M >= 1.  Prefill
  * is the arithmetic-bound phase ("Architecture", bench transcript): for
  * M > 16 the integer block dots run on the matrix cores (f16 MFMA, which is

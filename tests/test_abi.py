@@ -108,6 +108,23 @@ def test_group_refusals():
     assert L.qmv_launch_group(8, 1, (G * 1)(G(16, 1, 32, 18, 16, 16)), 1, None) == -3
 
 
+def test_gateup_refusals_and_scratch_size():
+    L = g.lib()
+    # the activation scratch of qmv_launch (24576 B at 1 x 896), then two
+    # 256-aligned [B][N] f32 products: 4864 * 4 = 19456 B each
+    assert g.qmv_gateup_act_bytes(1, 4864, 896) == 24576 + 2 * 19456
+    assert g.qmv_gateup_act_bytes(17, 16, 32) == 0 and g.qmv_gateup_act_bytes(1, 0, 32) == 0
+    f = L.qmv_launch_gateup_swiglu
+    assert f(4, FAKE, FAKE, 16, 32, FAKE, 1, FAKE, FAKE, None) == -1
+    assert f(g.Q4_K, FAKE, FAKE, 16, 896, FAKE, 1, FAKE, FAKE, None) == -2
+    assert f(g.Q4_0, FAKE, None, 16, 32, FAKE, 1, FAKE, FAKE, None) == -3   # up blob NULL
+    assert f(g.Q4_0, FAKE, FAKE + 8, 16, 32, FAKE, 1, FAKE, FAKE, None) == -3
+    assert f(g.Q4_0, FAKE, FAKE, 16, 32, FAKE, 17, FAKE, FAKE, None) == -2
+    assert f(g.Q4_0, FAKE, FAKE, 16, 32, FAKE, 1, None, FAKE, None) == -3
+    assert f(g.Q4_0, FAKE, FAKE, 16, 32, FAKE, 1, FAKE, FAKE + 2, None) == -3
+    assert f(g.Q4_0, FAKE, FAKE, 16, 32, FAKE + 2, 1, FAKE, FAKE, None) == -3
+
+
 def test_strerror_names_what_works():
     assert all(t in g.strerror(-1) for t in ("Q4_0", "Q4_1", "Q5_0", "Q5_1", "Q8_0", "Q8_1",
                                               "Q4_K", "Q6_K"))
@@ -117,3 +134,23 @@ def test_strerror_names_what_works():
     with pytest.raises(g.QmvError) as e:
         g.qmv_launch(4, FAKE, 16, 32, FAKE, 1, FAKE, FAKE, 0)
     assert e.value.code == -1
+
+
+def test_ceilings_library_exports_its_header():
+    import ctypes
+    lib_path = os.path.join(ROOT, "gguf_quantized_matvec_amd", "libqmv_ceilings.so")
+    if not os.path.exists(lib_path):
+        pytest.skip("libqmv_ceilings.so not built")
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qmv_ceilings.h")).read(),
+                 flags=re.S)
+    names = set(re.findall(r"^\s*int\s+([a-z_0-9]+)\s*\(", src, re.M))
+    assert names == {"qmv_ceil_stream_read", "qmv_ceil_mfma_i8", "qmv_ceil_mfma_f16",
+                     "qmv_ceil_epilogue"}
+    L = ctypes.CDLL(lib_path)
+    for n in names:
+        assert hasattr(L, n), n
+    # host-side refusals (nothing is launched): sizes that are not whole slices
+    L.qmv_ceil_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    assert L.qmv_ceil_stream_read(FAKE, 1000, FAKE, None) == -2
+    assert L.qmv_ceil_stream_read(None, 65536, FAKE, None) == -2

@@ -1,0 +1,121 @@
+"""GPU parity of the fused decode FFN: qmv_launch_gateup_swiglu (gate and up
+GEMVs with the SwiGLU h = silu(g) * u in their epilogue) and the down GEMV
+fed with h, against the CPU oracle chain: canonical-f32 gate and up ->
+oracle SwiGLU -> Q8_0 of h -> down.
+
+* h: bit-identical to oracle.swiglu of the oracle's canonical-f32 gate and up
+  (every product bit-identical to qmv_launch; the SwiGLU evaluated in f64 on
+  both sides and rounded once);
+* the quantisation of h (xq of the down GEMV): bit-exact;
+* y: within 1e-4 * sum|w^ x^| of the f64 result and bit-identical to the
+  canonical f32 order.
+Covers the one-launch path (B <= 4, K <= 8192; shapes with an odd number of
+rows per wave and a ragged last unit), the fallback (B > 4; K > 8192),
+staged and 4-byte-aligned activations."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from checks import assert_bitwise, assert_tol
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gguf_quantized_matvec_amd as g
+    g.lib()
+    return g
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _pair(fmt, N, K, seed):
+    wg, _ = synth.weights(fmt, N, K, seed, dscale=0.02)
+    wu, _ = synth.weights(fmt, N, K, seed + 1, dscale=0.02)
+    return wg, wu
+
+
+def _oracle_h(fmt, wg, wu, N, K, x):
+    xq = oracle.quantize_act(x)
+    gate = oracle.matmul_canon_f32(fmt, wg, N, K, xq, x.shape[0])
+    up = oracle.matmul_canon_f32(fmt, wu, N, K, xq, x.shape[0])
+    return oracle.swiglu(gate, up)
+
+
+# (fmt, N, K, B): K = 896 -> 4 chunks, 8 pairs per wave; K = 4864 -> 19 chunks,
+# 3 rows per wave -> 1 pair (one lane row idle); K = 4096 -> 2 pairs;
+# K = 32 single block; N not a multiple of the pairs per wave.
+ONE_LAUNCH = [
+    (synth.Q4_0, 4864, 896, 1), (synth.Q4_0, 333, 896, 3), (synth.Q4_K, 1000, 4096, 1),
+    (synth.Q4_K, 77, 4096, 4), (synth.Q6_K, 90, 1024, 2), (synth.Q8_0, 129, 4864, 1),
+    (synth.Q5_0, 40, 896, 4), (synth.Q4_1, 31, 32, 1), (synth.Q5_1, 45, 416, 2),
+    (synth.Q8_1, 64, 896, 3),
+]
+FALLBACK = [
+    (synth.Q4_0, 200, 896, 5), (synth.Q4_K, 130, 4096, 16), (synth.Q6_K, 50, 9216, 1),
+    (synth.Q8_0, 70, 8192 + 32, 2),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,B", ONE_LAUNCH + FALLBACK)
+def test_gateup_swiglu_h_bit_exact(g, fmt, N, K, B):
+    wg, wu = _pair(fmt, N, K, 300 + N)
+    x = synth.activations(B, K, 301 + K)
+    print(f"gateup fmt={fmt} N={N} K={K} B={B}", flush=True)
+    h = g.gateup_swiglu(fmt, dev(wg), dev(wu), N, K, x=dev(x))
+    torch.cuda.synchronize()
+    assert_bitwise(h.cpu().numpy(), _oracle_h(fmt, wg, wu, N, K, x), "h")
+
+
+@pytest.mark.parametrize("fmt,N,K,B", [ONE_LAUNCH[2], FALLBACK[1]])
+def test_gateup_swiglu_staged_and_unaligned_x(g, fmt, N, K, B):
+    wg, wu = _pair(fmt, N, K, 400 + N)
+    x = synth.activations(B, K, 401)
+    want = _oracle_h(fmt, wg, wu, N, K, x)
+    wgd, wud = dev(wg), dev(wu)
+    # staged: quantise first, then x NULL
+    xq = torch.zeros(g.qmv_gateup_act_bytes(B, N, K), dtype=torch.uint8, device="cuda")
+    g.quantize(dev(x), xq=xq)
+    h = g.gateup_swiglu(fmt, wgd, wud, N, K, xq=xq, B=B)
+    torch.cuda.synchronize()
+    assert_bitwise(h.cpu().numpy(), want, "h from staged xq")
+    # x 4-byte aligned only (one float into a buffer)
+    buf = torch.zeros(B * K + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = dev(x).reshape(-1)
+    xv = buf[1:].view(B, K)
+    assert xv.data_ptr() % 16 == 4
+    h2 = g.gateup_swiglu(fmt, wgd, wud, N, K, x=xv)
+    torch.cuda.synchronize()
+    assert_bitwise(h2.cpu().numpy(), want, "h from 4-byte aligned x")
+
+
+@pytest.mark.parametrize("fmt,N,K,B", [
+    (synth.Q4_0, 4864, 896, 1),    # the pages' Qwen2.5-0.5B FFN (down 896 x 4864)
+    (synth.Q4_K, 1536, 4096, 2),   # 8B-class gate/up rows (a slice), down Q6_K
+    (synth.Q4_K, 512, 4096, 8),
+])
+def test_ffn_chain(g, fmt, N, K, B):
+    """gate/up + SwiGLU, then down on h: y against the oracle chain."""
+    fdown = synth.Q6_K if fmt == synth.Q4_K else fmt
+    wg, wu = _pair(fmt, N, K, 500 + N)
+    wd, _ = synth.weights(fdown, K, N, 502 + N, dscale=0.02)
+    x = synth.activations(B, K, 503)
+    h = g.gateup_swiglu(fmt, dev(wg), dev(wu), N, K, x=dev(x))
+    xq_d = g.act_buffer(B, N)
+    y = g.matvec(fdown, dev(wd), K, N, x=h, xq=xq_d)
+    torch.cuda.synchronize()
+    h_o = _oracle_h(fmt, wg, wu, N, K, x)
+    assert_bitwise(h.cpu().numpy(), h_o, "h")
+    xq_o = oracle.quantize_act(h_o)
+    assert_bitwise(xq_d.cpu().numpy()[: xq_o.size], xq_o, "Q8_0 of h")
+    y64, A = oracle.matmul_f64(fdown, wd, K, N, xq_o, B)
+    assert_tol(y.cpu().numpy(), y64, A, what="ffn down")
+    assert_bitwise(y.cpu().numpy(), oracle.matmul_canon_f32(fdown, wd, K, N, xq_o, B), "ffn f32")
