@@ -170,6 +170,21 @@ int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                                          static_cast<hipStream_t>(stream)));
 }
 
+int qmv_launch_noalloc(int type, const void* w, int64_t N, int64_t K, const float* x,
+                       int64_t B, float* y, void* stream) {
+    int rc = check_weights(type, w, N, K);
+    if (rc) return rc;
+    if (B < 1 || B > QMV_MAX_BATCH) return QMV_EINVAL_SHAPE;
+    if (!x || !y || !aligned(x, 4) || !aligned(y, 4)) return QMV_EINVAL_PTR;
+    if ((size_t)qmv::act_layout(B, K).total > QMV_NOALLOC_MAX_ACT_BYTES) return QMV_ETOO_LARGE;
+    if ((rc = check_device())) return rc;
+    int err = 0;
+    uint8_t* xq = qmv::noalloc_scratch(&err);
+    if (!xq) return QMV_ELAUNCH;
+    return launched(qmv::launch_qmv(type, static_cast<const uint8_t*>(w), N, K, x, xq, B, y,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 const char* qmv_strerror(int code) {
     switch (code) {
     case QMV_OK: return "ok";
@@ -186,6 +201,10 @@ const char* qmv_strerror(int code) {
                "NULL only when the group runs as one launch and its x is 16-byte aligned)";
     case QMV_ELAUNCH: return "HIP kernel launch failed";
     case QMV_EUNSUPPORTED_DEVICE: return "current device is not an MI355X (gfx950)";
+    case QMV_ETOO_LARGE:
+        return "too large for qmv_launch_noalloc: qmv_act_bytes(B, K) must be at most "
+               "QMV_NOALLOC_MAX_ACT_BYTES (8 MiB; every K <= 65536 at B <= 16); use qmv_launch "
+               "with a caller-supplied xq for larger shapes";
     }
     return "unknown status code";
 }

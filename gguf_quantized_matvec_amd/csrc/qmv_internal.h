@@ -113,6 +113,9 @@ int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* x
                     int64_t rows, int32_t* P, hipStream_t s);
 int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                int64_t rows, float* y, hipStream_t s);
+// Device address of the current device's fixed activation scratch for
+// qmv_launch_noalloc (qmv_noalloc.hip), or NULL with *err set.
+uint8_t* noalloc_scratch(int* err);
 // Prefill GEMM on f16 MFMA (qmm_kernels.hip), for rows > 16.
 int launch_gemm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
                 float* y, hipStream_t s);

@@ -80,7 +80,9 @@ enum qmv_status {
     QMV_EINVAL_SHAPE = -2,       /* N, K, rows or batch out of range */
     QMV_EINVAL_PTR = -3,         /* NULL or misaligned pointer */
     QMV_ELAUNCH = -4,            /* the HIP launch failed */
-    QMV_EUNSUPPORTED_DEVICE = -5 /* the current device is not gfx950 */
+    QMV_EUNSUPPORTED_DEVICE = -5, /* the current device is not gfx950 */
+    QMV_ETOO_LARGE = -6          /* qmv_launch_noalloc: the activation scratch for B rows of
+                                    K elements exceeds QMV_NOALLOC_MAX_ACT_BYTES */
 };
 
 /* Limits: 1 <= N <= 2^31-1; 32 <= K <= 2^20, K % 32 == 0 (K % 256 == 0 for
@@ -191,6 +193,24 @@ int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, in
  * [B][N][K/32][2] = (sum q*a, sum a). */
 int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                         int64_t B, int32_t* P, void* stream);
+
+/* Decode GEMV for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops or harnesses that forbid hipMalloc): the
+ * same multiply and result as qmv_launch(type, w, N, K, x, B, xq, y, stream)
+ * with x given, bit for bit, but the activation scratch is a fixed array
+ * inside the library (one per GPU, QMV_NOALLOC_MAX_ACT_BYTES bytes, held
+ * until the process ends) instead of a caller-supplied xq.  The call
+ * allocates nothing.  x [B][K] f32 must be non-NULL (4-byte aligned); y
+ * [B][N] f32.  Shapes as qmv_launch; in addition qmv_act_bytes(B, K) must not
+ * exceed QMV_NOALLOC_MAX_ACT_BYTES, else QMV_ETOO_LARGE (this admits every
+ * K <= 65536 at B = 16).  Every call on one GPU uses that GPU's one scratch
+ * array: calls that may overlap in time on one GPU (other streams, other
+ * host threads without ordering) race on it and must be serialised by the
+ * caller; calls in one stream are ordered and safe.  Nothing in the scratch
+ * needs to start at zero: each call writes every byte it reads. */
+#define QMV_NOALLOC_MAX_ACT_BYTES ((size_t)8 << 20)
+int qmv_launch_noalloc(int type, const void* w, int64_t N, int64_t K, const float* x,
+                       int64_t B, float* y, void* stream);
 
 /* Static text for a status code. */
 const char* qmv_strerror(int code);

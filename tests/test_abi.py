@@ -108,6 +108,23 @@ def test_group_refusals():
     assert L.qmv_launch_group(8, 1, (G * 1)(G(16, 1, 32, 18, 16, 16)), 1, None) == -3
 
 
+def test_noalloc_refusals():
+    L = g.lib()
+    # the fixed scratch admits every K <= 65536 at B = 16 (and no more at K = 2^17)
+    assert g.qmv_act_bytes(16, 65536) <= 8 << 20 < g.qmv_act_bytes(16, 1 << 17)
+    assert L.qmv_launch_noalloc(g.Q8_0, FAKE, 16, 1 << 17, FAKE, 16, FAKE, None) == -6
+    assert L.qmv_launch_noalloc(g.Q8_0, FAKE, 16, 1 << 19, FAKE, 1, FAKE, None) == -6
+    assert L.qmv_launch_noalloc(4, FAKE, 16, 32, FAKE, 1, FAKE, None) == -1
+    assert L.qmv_launch_noalloc(g.Q4_K, FAKE, 16, 896, FAKE, 1, FAKE, None) == -2
+    assert L.qmv_launch_noalloc(g.Q8_0, FAKE, 16, 32, FAKE, 0, FAKE, None) == -2
+    assert L.qmv_launch_noalloc(g.Q8_0, FAKE, 16, 32, FAKE, 17, FAKE, None) == -2
+    assert L.qmv_launch_noalloc(g.Q8_0, FAKE, 16, 32, None, 1, FAKE, None) == -3   # x required
+    assert L.qmv_launch_noalloc(g.Q8_0, FAKE, 16, 32, FAKE + 2, 1, FAKE, None) == -3
+    assert L.qmv_launch_noalloc(g.Q8_0, FAKE, 16, 32, FAKE, 1, None, None) == -3
+    assert L.qmv_launch_noalloc(g.Q8_0, FAKE + 8, 16, 32, FAKE, 1, FAKE, None) == -3
+    assert "QMV_NOALLOC_MAX_ACT_BYTES" in g.strerror(-6)
+
+
 def test_gateup_refusals_and_scratch_size():
     L = g.lib()
     # the activation scratch of qmv_launch (24576 B at 1 x 896), then two
