@@ -572,10 +572,10 @@ def suite(torch, g, synth, rotate_bytes):
     return res
 
 
-def traffic_from(pmc_dir, kernel_filter):
+def traffic_from(pmc_dir, kernel_filter, stage):
     """profiles/traffic.json from four rocprofv3 --pmc runs under pmc_dir:
-    fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of `bench.py --profile-stage`),
-    calib_fetch/ and calib_write/ (the same counters of `bench.py --copy-calib`).
+    stage_FETCH_SIZE/ and stage_WRITE_SIZE/ (`bench.py --profile-stage S`),
+    calib_FETCH_SIZE/ and calib_WRITE_SIZE/ (`bench.py --copy-calib`).
     Each counter is scaled by true bytes / counted bytes of the plain copy."""
     import csv
     import glob
@@ -592,13 +592,13 @@ def traffic_from(pmc_dir, kernel_filter):
         return out
 
     copy_bytes = 256 << 20
-    f_scale = copy_bytes / (max(v for _, v in rows("calib_fetch", "FETCH_SIZE")) * 1024)
-    w_scale = copy_bytes / (max(v for _, v in rows("calib_write", "WRITE_SIZE")) * 1024)
-    fk = [v for k, v in rows("fetch", "FETCH_SIZE") if kernel_filter in k]
-    wk = [v for k, v in rows("write", "WRITE_SIZE") if kernel_filter in k]
+    f_scale = copy_bytes / (max(v for _, v in rows("calib_FETCH_SIZE", "FETCH_SIZE")) * 1024)
+    w_scale = copy_bytes / (max(v for _, v in rows("calib_WRITE_SIZE", "WRITE_SIZE")) * 1024)
+    fk = [v for k, v in rows("stage_FETCH_SIZE", "FETCH_SIZE") if kernel_filter in k]
+    wk = [v for k, v in rows("stage_WRITE_SIZE", "WRITE_SIZE") if kernel_filter in k]
     fetch = sum(fk) / len(fk) * 1024 * f_scale
     write = sum(wk) / len(wk) * 1024 * w_scale
-    out = {"kernel_filter": kernel_filter, "kernel_src_sha": kernel_src_sha(),
+    out = {"stage": stage, "kernel_filter": kernel_filter, "kernel_src_sha": kernel_src_sha(),
            "dispatches": [len(fk), len(wk)],
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
@@ -649,11 +649,12 @@ def main():
                     help="only run a 256 MiB device copy 10 times (counter calibration)")
     ap.add_argument("--traffic-from", default=None, metavar="DIR")
     ap.add_argument("--traffic-kernel", default="k_dot")
+    ap.add_argument("--traffic-stage", default="C_gateup_swiglu", choices=list(STAGES))
     ap.add_argument("--trace-summary", default=None, metavar="DIR")
     args = ap.parse_args()
 
     if args.traffic_from:
-        traffic_from(args.traffic_from, args.traffic_kernel)
+        traffic_from(args.traffic_from, args.traffic_kernel, args.traffic_stage)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)

@@ -20,7 +20,7 @@ TYPES = {"Q4_0": Q4_0, "Q4_1": Q4_1, "Q5_0": Q5_0, "Q5_1": Q5_1, "Q8_0": Q8_0, "
 BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_1: (32, 20), Q5_1: (32, 24),
          Q8_1: (32, 36), Q4_K: (256, 144), Q6_K: (256, 210)}
 EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
-           "qmv_partials_launch", "qmv_launch_noalloc", "qmv_gateup_act_bytes",
+           "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc", "qmv_gateup_act_bytes",
            "qmv_launch_gateup_swiglu", "qmv_strerror")
 MAX_BATCH = 16
 MAX_GROUP = 8
@@ -57,11 +57,12 @@ def lib() -> ctypes.CDLL:
         L.qmv_launch_group.argtypes = [I, I64, ctypes.POINTER(Gemv), I, P]
         L.qmv_partials_launch.argtypes = [I, P, I64, I64, P, I64, P, P]
         L.qmv_launch_noalloc.argtypes = [I, P, I64, I64, P, I64, P, P]
+        L.qmm_partials_launch.argtypes = [I, P, I64, I64, P, I64, P, P]
         L.qmv_gateup_act_bytes.argtypes = [I64, I64, I64]
         L.qmv_gateup_act_bytes.restype = ctypes.c_size_t
         L.qmv_launch_gateup_swiglu.argtypes = [I, P, P, I64, I64, P, I64, P, P, P]
         for f in ("quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
-                  "qmv_partials_launch", "qmv_launch_noalloc", "qmv_launch_gateup_swiglu"):
+                  "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc", "qmv_launch_gateup_swiglu"):
             getattr(L, f).restype = I
         L.qmv_strerror.argtypes = [I]
         L.qmv_strerror.restype = ctypes.c_char_p
@@ -107,6 +108,11 @@ def qmm_launch(type: int, w: int, N: int, K: int, x, M: int, xq: int, y: int,
 def qmv_partials_launch(type: int, w: int, N: int, K: int, xq: int, B: int, P: int,
                         stream: int = 0) -> None:
     _check(lib().qmv_partials_launch(type, w, N, K, xq, B, P, stream), "qmv_partials_launch")
+
+
+def qmm_partials_launch(type: int, w: int, N: int, K: int, xq: int, M: int, P: int,
+                        stream: int = 0) -> None:
+    _check(lib().qmm_partials_launch(type, w, N, K, xq, M, P, stream), "qmm_partials_launch")
 
 
 def qmv_launch_noalloc(type: int, w: int, N: int, K: int, x: int, B: int, y: int,
@@ -254,12 +260,14 @@ def matmul(type: int, w, N: int, K: int, x=None, xq=None, M=None, y=None, stream
     return y
 
 
-def partials(type: int, w, N: int, K: int, xq, B: int, P=None, stream=None):
-    """Test hook: int32 per-block partials [B, N, K/32] (Q4_K, Q4_1, Q5_1: [B, N, K/32, 2])."""
+def partials(type: int, w, N: int, K: int, xq, B: int, P=None, stream=None, gemm=False):
+    """Test hook: int32 per-block partials [B, N, K/32] (Q4_K, Q4_1, Q5_1: [B, N, K/32, 2])
+    of the kernel that qmv_launch (gemm: qmm_launch) runs for B rows."""
     import torch
     shape = (B, N, K // 32, 2) if type in (Q4_K, Q4_1, Q5_1) else (B, N, K // 32)
     if P is None:
         P = torch.empty(shape, dtype=torch.int32, device=w.device)
-    qmv_partials_launch(type, _dev(w, torch.uint8, "w"), N, K, _dev(xq, torch.uint8, "xq"), B,
-                        _dev(P, torch.int32, "P"), _stream(stream))
+    fn = qmm_partials_launch if gemm else qmv_partials_launch
+    fn(type, _dev(w, torch.uint8, "w"), N, K, _dev(xq, torch.uint8, "xq"), B,
+       _dev(P, torch.int32, "P"), _stream(stream))
     return P

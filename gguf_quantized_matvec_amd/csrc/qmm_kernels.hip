@@ -145,6 +145,7 @@ __device__ __forceinline__ uint32_t pk_mul(uint32_t a, _Float16 s) {
 struct WScale {
     uint32_t d;    // fp16 bits of the block / superblock d
     uint32_t x1;   // Q4_K: f32 bits of dmin * m_j;  Q6_K (unscaled codes): s0 | s1 << 16
+    int mn;        // Q4_K: the 6-bit min m_j (the partials hook reports m_j * S)
 };
 
 // Decode block b of the fetched bytes into 32 f16 values (16 dwords, element
@@ -230,6 +231,7 @@ __device__ __forceinline__ void decode_w(const WRaw<FMT>& r, int b, uint32_t (&o
         }
         const float dmin = (float)h_of_bits(r.hdr[0] >> 16);
         s.x1 = __float_as_uint(dmin * (float)mn);  // exact: 11-bit x 6-bit
+        s.mn = mn;
         const _Float16 sch = (_Float16)(float)sc;
         const int sh = 4 * (j & 1);
 #pragma unroll
@@ -294,6 +296,12 @@ template <int T> struct Smem {
     float ca[SB][T];      // Q4_K: d_a * S (S = the block's code sum)
     uint32_t x1[SB][T];   // see WScale::x1
 };
+// The partials hook's extra staging: per step, the code sum S of each
+// activation row's block and the Q4_K min m_j of each weight row's block.
+template <int T> struct SmemPart {
+    int S[SB][T];
+    int mn[SB][T];
+};
 __device__ __forceinline__ int slot(int row, int q) { return row * PR + (q ^ (row & 15)); }
 
 using Even = std::integral_constant<int, 0>;
@@ -302,11 +310,14 @@ using Odd = std::integral_constant<int, 1>;
 // NW waves per workgroup: NW = 8 owns 128 x 128 outputs (each wave 64 x 32,
 // two MFMA tiles), NW = 4 owns 64 x 64 (each wave one 32 x 32 tile) for
 // grids that would not fill the chip with the larger tile.
-template <int FMT, int NW>
+// PART: the test hook; instead of scaling and accumulating, each block's
+// exact integer partial(s) go to P[m][n][b] (two per block for the formats
+// with a minimum term), y unused.
+template <int FMT, int NW, bool PART = false>
 __global__ __launch_bounds__(64 * NW) void k_gemm(const uint8_t* __restrict__ w, int64_t N, int64_t K,
                                                   const uint8_t* __restrict__ xq, ActLayout L,
                                                   int64_t M, int64_t tilesM, int64_t tilesN,
-                                                  float* __restrict__ y) {
+                                                  float* __restrict__ y, int32_t* __restrict__ P) {
     using F = GFmt<FMT>;
     constexpr int TM = 16 * NW, TN = 16 * NW;  // workgroup tile
     constexpr int WT = NW / 4;                 // 32 x 32 MFMA tiles per wave (along M)
@@ -319,6 +330,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const uint8_t* __restrict__ w,
     __shared__ uint4 lds_a1[TM * PR];
     __shared__ Smem<TM> lds_rest;
     Smem<TM>* const sm = &lds_rest;
+    __shared__ SmemPart<PART ? TM : 1> lds_part;
     auto a_buf = [&](auto par) -> uint4* {
         if constexpr (decltype(par)::value == 0) return lds_a0;
         else return lds_a1;
@@ -405,7 +417,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const uint8_t* __restrict__ w,
 
     // step h reads activation buffer P = h % 2 and fills the other
     auto step = [&](int h, Raw& r, auto par) {
-        constexpr int P = decltype(par)::value;
+        constexpr int PB = decltype(par)::value;
         const int nbh = min(SB, nb - SB * h);
         bool odd_big = false;
         if constexpr (FMT == T_Q6_K) {
@@ -431,12 +443,25 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const uint8_t* __restrict__ w,
             sm->ra[sk][sr] = make_uint4(r.da, 0, 0, 0);
             if (has_min_term<FMT>()) sm->ca[sk][sr] = r.ca;
             if (has_min_term<FMT>() || FMT == T_Q6_K) sm->x1[sk][sr] = f.x1;
+            if constexpr (PART) {
+                // S: the sum of the staged activation codes of the block (the
+                // f16 values the matrix cores multiply), exact in int
+                int S = 0;
+                if (has_min_term<FMT>() && r.have) {
+                    const _Float16* hc = reinterpret_cast<const _Float16*>(xq + L.hcodes) +
+                                         am * K + 32 * (int64_t)(SB * h + sk);
+#pragma unroll
+                    for (int i = 0; i < 32; i++) S += (int)(float)hc[i];
+                }
+                lds_part.S[sk][sr] = S;
+                lds_part.mn[sk][sr] = f.mn;
+            }
         }
         // B2: the W tile is staged; this wave's activation loads of step h
         // completed before its weight loads of step h were consumed above
         __syncthreads();
         if (h + 1 < H) {
-            issue_a(h + 1, std::integral_constant<int, 1 - P>{});  // in flight while step h is multiplied
+            issue_a(h + 1, std::integral_constant<int, 1 - PB>{});  // in flight while step h is multiplied
             fetch(h + 1, r);
         }
         const uint4* A = a_buf(par);
@@ -468,6 +493,39 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const uint8_t* __restrict__ w,
                         __builtin_memcpy(&Rw, &rb, 16);
                     }
                     const uint32_t x1 = (has_min_term<FMT>() || FMT == T_Q6_K) ? sm->x1[bk][brow] : 0u;
+                    if constexpr (PART) {
+                        // the exact integers of the block, as the MFMAs form them
+                        constexpr int per = has_min_term<FMT>() ? 2 : 1;
+                        const int64_t n = n0 + brow, b = (int64_t)SB * h + bk;
+#pragma unroll
+                        for (int i = 0; i < WT; i++) {
+                            v16f I;
+                            if constexpr (FMT == T_Q6_K && UNF) {
+                                const v16f I0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i][0], Bf[0], zero16, 0, 0, 0);
+                                const v16f I1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i][1], Bf[1], zero16, 0, 0, 0);
+                                const float s0 = (float)(int16_t)(x1 & 0xFFFF), s1 = (float)((int)x1 >> 16);
+#pragma unroll
+                                for (int e = 0; e < 16; e++) I[e] = fmaf(s0, I0[e], s1 * I1[e]);
+                            } else {
+                                I = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i][0], Bf[0], zero16, 0, 0, 0);
+                                I = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i][1], Bf[1], I, 0, 0, 0);
+                            }
+#pragma unroll
+                            for (int e = 0; e < 16; e++) {
+                                const int rl = 32 * WT * wm + 32 * i + 8 * (e >> 2) + 4 * kq + (e & 3);
+                                const int64_t m = m0 + rl;
+                                if (m < M && n < N) {
+                                    int32_t* o = P + ((m * N + n) * nb + b) * per;
+                                    o[0] = (int32_t)I[e];
+                                    if constexpr (per == 2) {
+                                        const int S = lds_part.S[bk][rl];
+                                        o[1] = FMT == T_Q4_K ? lds_part.mn[bk][brow] * S : S;
+                                    }
+                                }
+                            }
+                        }
+                        continue;
+                    }
 #pragma unroll
                     for (int i = 0; i < WT; i++) {
                         const v16f S = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ra[i], Rw, zero16, 0, 0, 0);
@@ -527,6 +585,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const uint8_t* __restrict__ w,
         if (h + 1 < H) step(h + 1, r, Odd{});
     }
 
+    if constexpr (PART) return;
     // lane l, element e of tile i: row 8(e/4) + 4kq + e%4, column lr
     const int64_t n = n0 + 32 * wn + lr;
 #pragma unroll
@@ -544,17 +603,25 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const uint8_t* __restrict__ w,
 // when the larger one leaves most of the chip empty).
 template <int FMT>
 int launch_gemm_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
-                  float* y, hipStream_t s) {
+                  float* y, int32_t* P, hipStream_t s) {
     const ActLayout L = act_layout(M, K);
     int64_t tilesM = (M + 127) / 128, tilesN = (N + 127) / 128;
     if (tilesM * tilesN > 128) {
-        hipLaunchKernelGGL((k_gemm<FMT, 8>), dim3((unsigned)(tilesM * tilesN)), dim3(512), 0,
-                           s, w, N, K, xq, L, M, tilesM, tilesN, y);
+        if (P)
+            hipLaunchKernelGGL((k_gemm<FMT, 8, true>), dim3((unsigned)(tilesM * tilesN)), dim3(512),
+                               0, s, w, N, K, xq, L, M, tilesM, tilesN, y, P);
+        else
+            hipLaunchKernelGGL((k_gemm<FMT, 8>), dim3((unsigned)(tilesM * tilesN)), dim3(512), 0,
+                               s, w, N, K, xq, L, M, tilesM, tilesN, y, P);
     } else {
         tilesM = (M + 63) / 64;
         tilesN = (N + 63) / 64;
-        hipLaunchKernelGGL((k_gemm<FMT, 4>), dim3((unsigned)(tilesM * tilesN)), dim3(256), 0,
-                           s, w, N, K, xq, L, M, tilesM, tilesN, y);
+        if (P)
+            hipLaunchKernelGGL((k_gemm<FMT, 4, true>), dim3((unsigned)(tilesM * tilesN)), dim3(256),
+                               0, s, w, N, K, xq, L, M, tilesM, tilesN, y, P);
+        else
+            hipLaunchKernelGGL((k_gemm<FMT, 4>), dim3((unsigned)(tilesM * tilesN)), dim3(256), 0,
+                               s, w, N, K, xq, L, M, tilesM, tilesN, y, P);
     }
     return (int)hipGetLastError();
 }
@@ -562,16 +629,16 @@ int launch_gemm_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int
 }  // namespace
 
 int launch_gemm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
-                float* y, hipStream_t s) {
+                float* y, hipStream_t s, int32_t* P) {
     switch (type) {
-    case T_Q8_0: return launch_gemm_t<T_Q8_0>(w, N, K, xq, M, y, s);
-    case T_Q4_0: return launch_gemm_t<T_Q4_0>(w, N, K, xq, M, y, s);
-    case T_Q5_0: return launch_gemm_t<T_Q5_0>(w, N, K, xq, M, y, s);
-    case T_Q4_1: return launch_gemm_t<T_Q4_1>(w, N, K, xq, M, y, s);
-    case T_Q5_1: return launch_gemm_t<T_Q5_1>(w, N, K, xq, M, y, s);
-    case T_Q8_1: return launch_gemm_t<T_Q8_1>(w, N, K, xq, M, y, s);
-    case T_Q4_K: return launch_gemm_t<T_Q4_K>(w, N, K, xq, M, y, s);
-    case T_Q6_K: return launch_gemm_t<T_Q6_K>(w, N, K, xq, M, y, s);
+    case T_Q8_0: return launch_gemm_t<T_Q8_0>(w, N, K, xq, M, y, P, s);
+    case T_Q4_0: return launch_gemm_t<T_Q4_0>(w, N, K, xq, M, y, P, s);
+    case T_Q5_0: return launch_gemm_t<T_Q5_0>(w, N, K, xq, M, y, P, s);
+    case T_Q4_1: return launch_gemm_t<T_Q4_1>(w, N, K, xq, M, y, P, s);
+    case T_Q5_1: return launch_gemm_t<T_Q5_1>(w, N, K, xq, M, y, P, s);
+    case T_Q8_1: return launch_gemm_t<T_Q8_1>(w, N, K, xq, M, y, P, s);
+    case T_Q4_K: return launch_gemm_t<T_Q4_K>(w, N, K, xq, M, y, P, s);
+    case T_Q6_K: return launch_gemm_t<T_Q6_K>(w, N, K, xq, M, y, P, s);
     }
     return (int)hipErrorInvalidValue;
 }

@@ -170,6 +170,18 @@ int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                                          static_cast<hipStream_t>(stream)));
 }
 
+int qmm_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
+                        int64_t M, int32_t* P, void* stream) {
+    int rc = check_weights(type, w, N, K);
+    if (rc) return rc;
+    if (M < 1 || M > QMV_MAX_M) return QMV_EINVAL_SHAPE;
+    if (!xq || !P || !aligned(xq, 16) || !aligned(P, 4)) return QMV_EINVAL_PTR;
+    if ((rc = check_device())) return rc;
+    return launched(qmv::launch_qmm_partials(type, static_cast<const uint8_t*>(w), N, K,
+                                             static_cast<uint8_t*>(xq), M, P,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int qmv_launch_noalloc(int type, const void* w, int64_t N, int64_t K, const float* x,
                        int64_t B, float* y, void* stream) {
     int rc = check_weights(type, w, N, K);

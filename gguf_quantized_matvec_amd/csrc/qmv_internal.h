@@ -117,7 +117,11 @@ int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
 // qmv_launch_noalloc (qmv_noalloc.hip), or NULL with *err set.
 uint8_t* noalloc_scratch(int* err);
 // Prefill GEMM on f16 MFMA (qmm_kernels.hip), for rows > 16.
+// P != NULL: the test hook; the exact block partials go to P instead of y.
 int launch_gemm(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
-                float* y, hipStream_t s);
+                float* y, hipStream_t s, int32_t* P = nullptr);
+// Partials of the kernel qmm_launch runs at M rows (the GEMM for M > 16).
+int launch_qmm_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* xq,
+                        int64_t M, int32_t* P, hipStream_t s);
 
 }  // namespace qmv

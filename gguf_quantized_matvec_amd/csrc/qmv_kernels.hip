@@ -875,9 +875,30 @@ __host__ __device__ inline int act_lds_row_bytes(int64_t K) {
 }
 
 // p[m] = sum over the chunk's blocks in order (documented f32 order).
-template <int FMT, int B>
+// Where a partials launch writes the exact integers of the lane's row:
+// P[m][row][b] (two per block, [..][b][2], for the formats with a minimum term).
+struct PartOut {
+    int32_t* row;     // P + row * nb * per
+    int64_t mstride;  // N * nb * per: from activation row m to m + 1
+};
+
+// PART: instead of scaling and accumulating, store each block's exact
+// integer partial(s) (the ones the documented f32 order scales) to po.
+template <int FMT, int B, bool PART = false>
 __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
-                                          const ActRow (&A)[B], int c, int nbc, float (&p)[B]) {
+                                          const ActRow (&A)[B], int c, int nbc, float (&p)[B],
+                                          PartOut po = PartOut{}) {
+    constexpr int per = has_min_term<FMT>() ? 2 : 1;
+    // the integer(s) of block b, activation row m (only when PART)
+    auto emit = [&](int m, int b, bool on, int I, int Q) {
+        if constexpr (PART) {
+            if (on) {
+                int32_t* o = po.row + m * po.mstride + (int64_t)b * per;
+                o[0] = I;
+                if constexpr (per == 2) o[1] = Q;
+            }
+        }
+    };
 #pragma unroll
     for (int m = 0; m < B; m++) p[m] = 0.0f;
     // 32-element formats: the blocks of a short last chunk (bb >= nbc) are
@@ -900,6 +921,7 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                 int D = 0;
 #pragma unroll
                 for (int i = 0; i < 8; i++) D = dot4(w[i], a[i], D);
+                emit(m, b, on, D, 0);
                 const float t = fmaf((float)D, dw * A[m].da[b], p[m]);
                 p[m] = on ? t : p[m];
             }
@@ -927,6 +949,7 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                 for (int i = 0; i < 4; i++) D = dot4(hi[i], a[4 + i], D);
                 const int s16 = A[m].s16[b];
                 const int S = (int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16);
+                emit(m, b, on, D - 8 * S, 0);
                 const float t = fmaf((float)(D - 8 * S), dw * A[m].da[b], p[m]);
                 p[m] = on ? t : p[m];
             }
@@ -946,6 +969,7 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                 int D = 0;
 #pragma unroll
                 for (int i = 0; i < 8; i++) D = dot4(w[i], a[i], D);
+                emit(m, b, on, D, 0);
                 const float t = fmaf((float)D, dw * A[m].da[b], p[m]);
                 p[m] = on ? t : p[m];
             }
@@ -980,6 +1004,10 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                 for (int i = 0; i < 4; i++) D = dot4(lo[i], a[i], D);
 #pragma unroll
                 for (int i = 0; i < 4; i++) D = dot4(hi[i], a[4 + i], D);
+                if constexpr (PART) {
+                    const int s16 = A[m].s16[b];
+                    emit(m, b, on, D, (int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16));
+                }
                 float t = fmaf((float)D, dw * A[m].da[b], p[m]);
                 t = fmaf(mw, A[m].ca[b], t);
                 p[m] = on ? t : p[m];
@@ -1009,6 +1037,7 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                 for (int i = 0; i < 4; i++) D = dot4(hi[i], a[4 + i], D);
                 const int s16 = A[m].s16[b];
                 const int S = (int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16);
+                emit(m, b, on, D - 16 * S, 0);
                 const float t = fmaf((float)(D - 16 * S), dw * A[m].da[b], p[m]);
                 p[m] = on ? t : p[m];
             }
@@ -1043,6 +1072,10 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                 int D = 0;
 #pragma unroll
                 for (int i = 0; i < 8; i++) D = dot4(q[i], a[i], D);
+                if constexpr (PART) {
+                    const int s16 = A[m].s16[b];
+                    emit(m, b, true, sc * D, mn * ((int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16)));
+                }
                 p[m] = fmaf((float)(sc * D), d * A[m].da[b], p[m]);
                 p[m] = fmaf(-cw, A[m].ca[b], p[m]);
             }
@@ -1072,6 +1105,7 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
                 const int s16 = A[m].s16[b];
                 const int S0 = (int)(int16_t)(s16 & 0xFFFF), S1 = s16 >> 16;
                 const int I = s0 * (D0 - 32 * S0) + s1 * (D1 - 32 * S1);
+                emit(m, b, true, I, 0);
                 p[m] = fmaf((float)I, d * A[m].da[b], p[m]);
             }
         });
@@ -1133,7 +1167,9 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 // Launch modes of the dot kernel: a group of GEMVs (job = blockIdx.y), one
 // GEMV, or one gate/up pair whose rows are computed side by side and leave
 // h = silu(gate) * up instead of two outputs.
-constexpr int MODE_GROUP = 0, MODE_SINGLE = 1, MODE_PAIRED = 2;
+// MODE_PARTIALS: one GEMV on staged activations whose y is an int32 buffer
+// receiving the exact block partials instead (the test hook).
+constexpr int MODE_GROUP = 0, MODE_SINGLE = 1, MODE_PAIRED = 2, MODE_PARTIALS = 3;
 
 template <int FMT, int B, bool FUSED, int MODE>
 __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
@@ -1362,6 +1398,17 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
         const bool valid = row < N && c < C;
         const int nbc = F::QK == 32 ? min(8, nb - 8 * c) : 8;
         float p[B];
+        if constexpr (MODE == MODE_PARTIALS) {
+            if (valid) {
+                constexpr int per = has_min_term<FMT>() ? 2 : 1;
+                realign_chunk<FMT>(row * R + (int64_t)c * F::CB, r);
+                const PartOut po{reinterpret_cast<int32_t*>(J.y) + row * nb * per,
+                                 N * nb * per};
+                dot_chunk<FMT, B, true>(r, A, c, nbc, p, po);
+            }
+            if (q + 1 < PR) issue(q + 1, r);
+            continue;
+        }
         if (valid) {
             realign_chunk<FMT>(row * R + (int64_t)c * F::CB, r);
             dot_chunk<FMT, B>(r, A, c, nbc, p);
@@ -1385,6 +1432,7 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
         }
         wave_sync();
     }
+    if constexpr (MODE == MODE_PARTIALS) return;
     if constexpr (MODE == MODE_PAIRED) {
         // the gate and up sums of each output row meet in LDS; the gate
         // lane writes h = silu(gate) * up
@@ -1712,9 +1760,56 @@ int launch_qmv_group(int type, const GemvDesc* d, int count, int64_t rows, hipSt
     return 0;
 }
 
+template <int FMT>
+int launch_dot_partials_t(const DotJobs& jobs, int64_t rows, int64_t blocks, size_t shmem,
+                          hipStream_t s) {
+    switch (rows) {
+    case 1: return launch_dot_kernel<FMT, 1, false, MODE_PARTIALS>(jobs, blocks, shmem, s);
+    case 2: return launch_dot_kernel<FMT, 2, false, MODE_PARTIALS>(jobs, blocks, shmem, s);
+    case 3: return launch_dot_kernel<FMT, 3, false, MODE_PARTIALS>(jobs, blocks, shmem, s);
+    default: return launch_dot_kernel<FMT, 4, false, MODE_PARTIALS>(jobs, blocks, shmem, s);
+    }
+}
+
 int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* xq,
                     int64_t rows, int32_t* P, hipStream_t s) {
-    // the partials come from the MFMA path: stage its copy from the Q8_0 blocks
+    if (use_dot(rows, K)) {
+        // the lane-per-chunk kernel, which qmv_launch runs at this many rows:
+        // stage its copy from the Q8_0 blocks, then the kernel writes P
+        int rc = launch_rebuild(xq, rows, K, ST_ROW, s);
+        if (rc) return rc;
+        const ActLayout L = act_layout(rows, K);
+        DotJobs jobs{};
+        jobs.count = 1;
+        jobs.waves = 4;
+        DotJob& J = jobs.j[0];
+        J.w = w;
+        J.w2 = nullptr;
+        J.y = reinterpret_cast<float*>(P);
+        J.x = nullptr;
+        J.xq = xq;
+        J.N = N;
+        J.K = K;
+        J.wbytes = N * row_bytes(type, K);
+        J.rcodes = L.rcodes;
+        J.rda = L.rda;
+        J.rca = L.rca;
+        J.rs16 = L.rs16;
+        const int64_t blocks = dot_blocks(type, N, K, 4);
+        const size_t shmem = dot_shmem((int)rows, K, 4);
+        switch (type) {
+        case T_Q8_0: return launch_dot_partials_t<T_Q8_0>(jobs, rows, blocks, shmem, s);
+        case T_Q4_0: return launch_dot_partials_t<T_Q4_0>(jobs, rows, blocks, shmem, s);
+        case T_Q5_0: return launch_dot_partials_t<T_Q5_0>(jobs, rows, blocks, shmem, s);
+        case T_Q4_1: return launch_dot_partials_t<T_Q4_1>(jobs, rows, blocks, shmem, s);
+        case T_Q5_1: return launch_dot_partials_t<T_Q5_1>(jobs, rows, blocks, shmem, s);
+        case T_Q8_1: return launch_dot_partials_t<T_Q8_1>(jobs, rows, blocks, shmem, s);
+        case T_Q4_K: return launch_dot_partials_t<T_Q4_K>(jobs, rows, blocks, shmem, s);
+        case T_Q6_K: return launch_dot_partials_t<T_Q6_K>(jobs, rows, blocks, shmem, s);
+        }
+        return (int)hipErrorInvalidValue;
+    }
+    // otherwise the MFMA path: stage its copy from the Q8_0 blocks
     const int rc = launch_rebuild(xq, rows, K, ST_MFMA, s);
     if (rc) return rc;
     switch (type) {
@@ -1728,6 +1823,14 @@ int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* x
     case T_Q6_K: return launch_qmv_ni<T_Q6_K, 4>(w, N, K, xq, rows, nullptr, P, s, true);
     }
     return (int)hipErrorInvalidValue;
+}
+
+int launch_qmm_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* xq,
+                        int64_t M, int32_t* P, hipStream_t s) {
+    if (M <= 16) return launch_partials(type, w, N, K, xq, M, P, s);
+    const int rc = launch_rebuild(xq, M, K, ST_F16, s);
+    if (rc) return rc;
+    return launch_gemm(type, w, N, K, xq, M, nullptr, s, P);
 }
 
 bool gateup_is_one_launch(int64_t rows, int64_t K) {

@@ -185,14 +185,25 @@ int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, in
                void* xq, float* y, void* stream);
 
 /* Test hook: the exact int32 per-block partials that the kernels scale and
- * accumulate, from the weight decode and integer dot of the batched-decode
- * (MFMA) path.  xq must hold quantize_act_q8_0's Q8_0 blocks for B rows,
- * 1 <= B <= 16; the hook first rebuilds the private part of xq from them
- * (the Q8_0 blocks are not changed).  P layout [B][N][K/32] int32; for Q4_K
- * [B][N][K/32][2] = (sc_j * sum q*a, m_j * sum a), for Q4_1 and Q5_1
- * [B][N][K/32][2] = (sum q*a, sum a). */
+ * accumulate, produced by the weight decode and integer dot of the same
+ * kernel that qmv_launch runs for these B rows (the lane-per-chunk kernel
+ * for B <= 4, the MFMA kernel otherwise).  xq must hold quantize_act_q8_0's
+ * Q8_0 blocks for B rows, 1 <= B <= 16; the hook first rebuilds the private
+ * part of xq from them (the Q8_0 blocks are not changed).  P layout
+ * [B][N][K/32] int32; for Q4_K [B][N][K/32][2] = (sc_j * sum q*a,
+ * m_j * sum a), for Q4_1 and Q5_1 [B][N][K/32][2] = (sum q*a, sum a). */
 int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                         int64_t B, int32_t* P, void* stream);
+
+/* Test hook for prefill: as qmv_partials_launch, from the kernel that
+ * qmm_launch runs for M rows (the prefill GEMM for M > 16), 1 <= M <= 2^24;
+ * P holds M rows in the same layout.  For Q4_K / Q4_1 / Q5_1 the GEMM forms
+ * only the first integer on the matrix cores (its min term multiplies the
+ * exact f32 product d_a * S); the second is reported as m_j (Q4_K, decoded
+ * by the GEMM) times S, the sum of the staged activation codes it
+ * multiplies. */
+int qmm_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
+                        int64_t M, int32_t* P, void* stream);
 
 /* Decode GEMV for callers that cannot allocate device memory (code under
  * HIP graph capture, serving loops or harnesses that forbid hipMalloc): the
