@@ -244,7 +244,8 @@ int oracle_dequant(int type, const uint8_t* w, int64_t N, int64_t K, double* out
 /* ------------------------------------------- activation quantisation --- */
 
 /* Q8_0 per 32-element block: amax = max|x|, d = amax/127 (f32, correctly
- * rounded), id = 1/d (0 when d == 0), code = round-half-away-from-zero(x*id)
+ * rounded), id = 1/d (0 when 1/d is not finite, i.e. d == 0 or d below about
+ * 2^-128: such a block's fp16 scale is 0), code = round-half-away-from-zero(x*id)
  * with the product in f32; the stored scale is fp16(d). */
 int oracle_quantize_act(const float* x, int64_t rows, int64_t K, uint8_t* out) {
     if (rows < 0 || K <= 0 || K % 32) return -2;
@@ -256,7 +257,10 @@ int oracle_quantize_act(const float* x, int64_t rows, int64_t K, uint8_t* out) {
             float amax = 0.0f;
             for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(xb[i]));
             float d = amax / 127.0f;
-            float id = d != 0.0f ? 1.0f / d : 0.0f;
+            /* a block too small for 1/d to be finite in f32 (d < ~2^-128,
+             * d == 0 included) gets all-zero codes: its fp16 scale is 0 */
+            float r = 1.0f / d;
+            float id = isinf(r) ? 0.0f : r;
             uint16_t dh = oracle_float_to_half(d);
             o[0] = (uint8_t)(dh & 255);
             o[1] = (uint8_t)(dh >> 8);

@@ -94,3 +94,30 @@ def test_zero_rows_and_blocks():
     assert d[1, 0] == 0 and np.all(q[1, 0] == 0)
     assert q[1, 1, 8] == 127 and np.count_nonzero(q[1, 1]) == 1
     assert oracle.quantize_act(np.zeros((0, 32), np.float32)).size == 0
+
+
+def test_blocks_too_small_for_a_finite_reciprocal_scale():
+    """A block whose d = amax/127 is so small that 1/d overflows f32 (d below
+    about 2^-128; subnormal amax, as a SwiGLU gate far below zero yields) is
+    quantised like an all-zero block: codes 0 (its fp16 scale is 0 anyway).
+    One just above that edge is quantised normally: its amax element maps
+    to +-127."""
+    x = np.zeros((1, 96), np.float32)
+    x[0, 0:32] = np.linspace(-1e-40, 7e-41, 32, dtype=np.float32)     # subnormal amax
+    x[0, 32:64] = np.linspace(2.0e-37, -2.5e-37, 32, dtype=np.float32)  # d ~ 2e-39: 1/d = inf
+    x[0, 64:96] = np.linspace(-1e-36, 4e-37, 32, dtype=np.float32)     # d ~ 7.9e-39: 1/d finite
+    q = oracle.quantize_act(x).reshape(3, 34)
+    assert np.all(q[0] == 0) and np.all(q[1] == 0)
+    assert q[2, 0] == 0 and q[2, 1] == 0                  # fp16(d) underflows to 0
+    codes = q[2, 2:].view(np.int8)
+    assert codes[0] == -127 and codes[-1] == 51           # -1e-36 -> -127, 4e-37 -> 50.8 -> 51
+    # the edge itself: 1/d is finite exactly when d >= 1/FLT_MAX (to rounding)
+    fmax = np.finfo(np.float32).max
+    for amax in (np.float32(127.0) / fmax * np.float32(0.999), np.float32(127.0) / fmax * np.float32(1.001)):
+        xb = np.zeros((1, 32), np.float32)
+        xb[0, 0] = amax
+        d = np.float32(amax) / np.float32(127.0)
+        with np.errstate(over="ignore", divide="ignore"):
+            finite = np.isfinite(np.float32(1.0) / d)
+        c = oracle.quantize_act(xb)[2:].view(np.int8)
+        assert c[0] == (127 if finite else 0)
