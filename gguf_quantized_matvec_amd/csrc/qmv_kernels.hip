@@ -68,8 +68,17 @@ __device__ __forceinline__ T ld(const uint8_t* p) {
 }
 
 // ------------------------------------------------------------ quantise ----
+// id = 1/d, or 0 when 1/d is not finite in f32 (d == 0, or d below about
+// 2^-128, a subnormal amax): such a block gets all-zero codes, like an
+// all-zero block (its fp16 scale is 0 anyway), instead of the undefined
+// integer conversion of an infinite x * id.
+__device__ __forceinline__ float inv_scale(float d) {
+    const float r = 1.0f / d;
+    return __builtin_isinf(r) ? 0.0f : r;
+}
+
 // Q8_0 of one 32-element block: amax, d = amax/127 (correctly rounded f32
-// divide), id = 1/d (0 for an all-zero block), codes = round-half-away(x*id),
+// divide), id = inv_scale(d), codes = round-half-away(x*id),
 // stored scale fp16(d); dval = f32 value of the stored scale.  A16: xb is
 // 16-byte aligned (float4 loads); otherwise only 4-byte alignment is assumed.
 template <bool A16>
@@ -91,7 +100,7 @@ __device__ __forceinline__ void quant_block(const float* __restrict__ xb, uint8_
 #pragma unroll
     for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
     const float d = amax / 127.0f;
-    const float id = d != 0.0f ? 1.0f / d : 0.0f;
+    const float id = inv_scale(d);
 #pragma unroll
     for (int i = 0; i < 32; i++) q[i] = (uint8_t)(int8_t)(int)roundf(v[i] * id);
     h = float_to_half_bits(d);
@@ -1312,7 +1321,7 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
             amax = fmaxf(amax, __shfl_xor(amax, 1));
             amax = fmaxf(amax, __shfl_xor(amax, 2));
             const float d = amax / 127.0f;
-            const float id = d != 0.0f ? 1.0f / d : 0.0f;
+            const float id = inv_scale(d);
             uint32_t c2[2] = {0u, 0u};
             int sp = 0;
 #pragma unroll
@@ -1542,9 +1551,10 @@ int launch_dot_rows(const DotJobs& jobs, int64_t rows, bool fused, bool paired, 
 
 // One launch of the dot kernel over `count` GEMVs of one type and row count.
 // up != NULL: one gate/up pair (d[0].w the gate blob, up the up blob, count
-// 1) whose output d[0].y receives h = silu(gate) * up.
+// 1) whose output d[0].y receives h = silu(gate) * up.  waves: 4 or 8 waves
+// per workgroup, or 0 to choose by the grid size.
 int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s,
-               const uint8_t* up = nullptr) {
+               const uint8_t* up = nullptr, int waves = 0) {
     if (count < 1 || count > MAX_JOBS) return (int)hipErrorInvalidValue;
     const bool paired = up != nullptr;
     if (paired && count != 1) return (int)hipErrorInvalidValue;
@@ -1558,7 +1568,7 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
     // (one per CU) instead of leaving a second round for a few CUs.
     int64_t blocks4 = 0;
     for (int k = 0; k < count; k++) blocks4 += dot_blocks(type, d[k].N, d[k].K, 4, paired);
-    jobs.waves = blocks4 > 256 && blocks4 <= 512 ? 8 : 4;
+    jobs.waves = waves ? waves : blocks4 > 256 && blocks4 <= 512 ? 8 : 4;
     // Rows of the grid in decreasing workgroup count: workgroups are
     // dispatched row after row at a limited rate, so the surplus (exiting)
     // workgroups of a smaller GEMV delay only the rows after it, and the
@@ -1704,8 +1714,11 @@ int launch_qmv(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
         // quantisation fused into the kernel when x is given, unless the
         // workgroups' re-reads of x would exceed the weight bytes: then one
         // quantise launch first
-        if (x && (!aligned16(x) ||
-                  dot_blocks(type, N, K, 4) * rows * K * 4 > N * row_bytes(type, K))) {
+        // (measured on the 8B-class down projection, 4096 x 14336 Q6_K: the
+        // separate quantise launch plus the staged GEMV, 18.7 us, beats the
+        // fused GEMV in 8-wave workgroups, which halve the re-reads, 20.7 us)
+        const int64_t wbytes = N * row_bytes(type, K);
+        if (x && (!aligned16(x) || dot_blocks(type, N, K, 4) * rows * K * 4 > wbytes)) {
             const int rc = launch_quantize(x, xq, rows, K, ST_ROW, s);
             if (rc) return rc;
             x = nullptr;

@@ -10,8 +10,8 @@
  * elements, GGUF block layout) and f32 activations X (rows of K elements):
  *
  *     xq      = Q8_0(X)                           (per 32-element block:
- *               d = amax/127 in f32, codes = round-half-away(x * (1/d)),
- *               stored scale fp16(d))
+ *               d = amax/127 in f32, codes = round-half-away(x * (1/d))
+ *               (0 when 1/d is not finite), stored scale fp16(d))
  *     Y[m][n] = sum over 32-blocks b of  d_w(n,b) * d_a(m,b) * I(m,n,b)
  *
  * with I the exact integer dot product of the block's weight codes and
@@ -58,7 +58,9 @@
  * launch returns QMV_ELAUNCH.  qmv_strerror() names what is accepted.
  *
  * Preconditions not checked (data lives on the device): activations finite,
- * and each 32-block's amax either 0 or in [127 * 2^-126, 127 * 65504].
+ * and each 32-block's amax at most 127 * 65504.  A block whose d = amax/127
+ * is too small for 1/d to be finite in f32 (d below about 2^-128) is
+ * quantised like an all-zero block (codes 0; its fp16 scale is 0 anyway).
  */
 #ifndef QMV_H
 #define QMV_H

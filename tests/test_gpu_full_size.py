@@ -1,10 +1,10 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times.
 
-* The decode step of the benchmark: one grouped launch of the Q4_0 SwiGLU FFN
-  GEMVs (gate and up 4864x896, down 896x4864, batch 1), each quantising its
-  own activation inside the kernel; every output against the oracle (all
-  rows), the written Q8_0 blocks bit-exact.
+* The benchmark's headline step (one 8B-class decoder layer at batch 1 and
+  16: q/k/v grouped, o, gate/up with the SwiGLU, down on h) and the pages'
+  Qwen2.5-0.5B FFN step, in the launch configuration the benchmark times;
+  outputs against the oracle chain, h and the Q8_0 blocks bit-exact.
 * Every GEMV of the per-matrix suite (B <= 16, activations staged by
   quantize_act_q8_0): all outputs of matrices up to 8192 rows, and a seeded
   sample of rows (plus the first and last rows and rows on 16-row tile
@@ -98,27 +98,77 @@ def _cases(small):
     return out
 
 
-def test_headline_ffn_step(g):
-    """The benchmark's step: gate, up and down as one grouped launch with the
-    quantisation fused; gate and down also write their Q8_0 blocks."""
+# The benchmark's headline step: one 8B-class decoder layer's projections.
+LAYER = [("q", synth.Q4_K, 4096, 4096), ("k", synth.Q4_K, 1024, 4096),
+         ("v", synth.Q4_K, 1024, 4096), ("o", synth.Q4_K, 4096, 4096),
+         ("gate", synth.Q4_K, 14336, 4096), ("up", synth.Q4_K, 14336, 4096),
+         ("down", synth.Q6_K, 4096, 14336)]
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_headline_layer_step(g, B):
+    """The benchmark's step, in its launch configuration: q/k/v as one grouped
+    launch (x fused at B <= 4, quantised once otherwise), o, gate/up with the
+    SwiGLU, down on h; every stage's outputs on sampled rows against the
+    oracle chain (canonical-f32 gate and up -> SwiGLU -> Q8_0 of h -> down),
+    h and the down GEMV's Q8_0 blocks bit-exact."""
+    blobs = {n: synth.weights(f, N, K, synth.seed_for(4, 10 + i), dscale=0.02)[0]
+             for i, (n, f, N, K) in enumerate(LAYER)}
+    w = {n: dev(b) for n, b in blobs.items()}
+    xs = [synth.activations(B, 4096, synth.act_seed_for(4, B) + j) for j in range(3)]
+    xa, xo, xc = (dev(x) for x in xs)
+    print(f"layer step B={B}", flush=True)
+    qa = g.act_buffer(B, 4096)
+    if B <= 4:
+        items = [dict(w=w["q"], N=4096, K=4096, x=xa, xq=qa), dict(w=w["k"], N=1024, K=4096, x=xa),
+                 dict(w=w["v"], N=1024, K=4096, x=xa)]
+    else:
+        g.quantize(xa, xq=qa)
+        items = [dict(w=w[n], N=N, K=4096, xq=qa, B=B) for n, N in (("q", 4096), ("k", 1024),
+                                                                      ("v", 1024))]
+    yq, yk, yv = g.matvec_group(synth.Q4_K, items)
+    yo = g.matvec(synth.Q4_K, w["o"], 4096, 4096, x=xo)
+    h = g.gateup_swiglu(synth.Q4_K, w["gate"], w["up"], 14336, 4096, x=xc)
+    qd = g.act_buffer(B, 14336)
+    yd = g.matvec(synth.Q6_K, w["down"], 4096, 14336, x=h, xq=qd)
+    xq = [oracle.quantize_act(x) for x in xs]
+    for n, y, xqi in (("q", yq, xq[0]), ("k", yk, xq[0]), ("v", yv, xq[0]), ("o", yo, xq[1])):
+        f, N, K = next((f, N, K) for m, f, N, K in LAYER if m == n)
+        check_against_oracle(f, blobs[n], N, K, xqi, B, host(y), sample_rows(N, 50 + N), n)
+    # h on sampled rows: oracle SwiGLU of the oracle's gate and up rows
+    rows = sample_rows(14336, 61)
+    gt = oracle.matmul_canon_f32(synth.Q4_K, rows_of(synth.Q4_K, blobs["gate"], 14336, 4096, rows),
+                                 len(rows), 4096, xq[2], B)
+    up = oracle.matmul_canon_f32(synth.Q4_K, rows_of(synth.Q4_K, blobs["up"], 14336, 4096, rows),
+                                 len(rows), 4096, xq[2], B)
+    hh = host(h)
+    assert_bitwise(np.ascontiguousarray(hh[:, rows]), oracle.swiglu(gt, up), "h")
+    # down: its Q8_0 blocks of the GPU's h bit-exact, outputs against the oracle
+    xq_h = oracle.quantize_act(hh)
+    assert_bitwise(host(qd)[: xq_h.size], xq_h, "Q8_0 of h")
+    check_against_oracle(synth.Q6_K, blobs["down"], 4096, 14336, xq_h, B, host(yd),
+                         sample_rows(4096, 62), "down")
+
+
+def test_qwen_ffn_step(g):
+    """The pages' Qwen2.5-0.5B FFN at batch 1 as the benchmark runs it:
+    gate/up (Q4_0 4864x896) with the SwiGLU, then down (896x4864) on h."""
     fmt = synth.Q4_0
     shapes = [("gate", 4864, 896), ("up", 4864, 896), ("down", 896, 4864)]
     blobs = {n: synth.weights(fmt, N, K, synth.seed_for(1, i), dscale=0.02)[0]
              for i, (n, N, K) in enumerate(shapes)}
     x1 = synth.activations(1, 896, synth.act_seed_for(1, 1))
-    x2 = synth.activations(1, 4864, synth.act_seed_for(1, 1) + 1)
     w = {n: dev(b) for n, b in blobs.items()}
-    X1, X2 = dev(x1), dev(x2)
-    q1, q2 = g.act_buffer(1, 896), g.act_buffer(1, 4864)
-    ys = g.matvec_group(fmt, [dict(w=w["gate"], N=4864, K=896, x=X1, xq=q1),
-                              dict(w=w["up"], N=4864, K=896, x=X1),
-                              dict(w=w["down"], N=896, K=4864, x=X2, xq=q2)])
-    xq1, xq2 = oracle.quantize_act(x1), oracle.quantize_act(x2)
-    assert_bitwise(host(q1)[:xq1.size], xq1, "gate Q8_0 blocks")
-    assert_bitwise(host(q2)[:xq2.size], xq2, "down Q8_0 blocks")
-    for (n, N, K), y in zip(shapes, ys):
-        xq = xq1 if K == 896 else xq2
-        check_against_oracle(fmt, blobs[n], N, K, xq, 1, host(y), np.arange(N), n)
+    h = g.gateup_swiglu(fmt, w["gate"], w["up"], 4864, 896, x=dev(x1))
+    q2 = g.act_buffer(1, 4864)
+    y = g.matvec(fmt, w["down"], 896, 4864, x=h, xq=q2)
+    xq1 = oracle.quantize_act(x1)
+    h_o = oracle.swiglu(oracle.matmul_canon_f32(fmt, blobs["gate"], 4864, 896, xq1, 1),
+                        oracle.matmul_canon_f32(fmt, blobs["up"], 4864, 896, xq1, 1))
+    assert_bitwise(host(h), h_o, "h")
+    xq2 = oracle.quantize_act(h_o)
+    assert_bitwise(host(q2)[: xq2.size], xq2, "Q8_0 of h")
+    check_against_oracle(fmt, blobs["down"], 896, 4864, xq2, 1, host(y), np.arange(896), "down")
 
 
 @pytest.mark.parametrize("wl,mi,B", _cases(small=True))

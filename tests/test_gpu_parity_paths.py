@@ -171,3 +171,35 @@ def test_multipass_rows(g, fmt, K, B, fused):
     y64, A = oracle.matmul_f64(fmt, blob, N, K, xq_o, B)
     assert_tol(y, y64, A, what="multipass")
     assert_bitwise(y, oracle.matmul_canon_f32(fmt, blob, N, K, xq_o, B), "multipass f32 order")
+
+
+@pytest.mark.parametrize("rows,K", [(1, 1024), (3, 896), (16, 4096), (40, 512)])
+def test_blocks_too_small_for_a_finite_reciprocal_scale(g, rows, K):
+    """Subnormal-amax blocks (1/d overflows f32) quantise to all-zero codes on
+    every quantiser: the standalone launch, the GEMV-fused one and the
+    gate/up pair's; the multiply then adds nothing for them."""
+    x = synth.activations(rows, K, 1200 + K)
+    x[:, 32:64] *= np.float32(1e-40)     # subnormal amax
+    x[:, 64:96] *= np.float32(5e-38)     # d ~ 1.6e-39: 1/d = inf
+    x[:, 128:160] *= np.float32(3e-36)   # 1/d finite, fp16(d) = 0
+    xq_o = oracle.quantize_act(x)
+    blk = xq_o.reshape(rows, K // 32, 34)
+    assert np.all(blk[:, 1:3] == 0) and np.any(blk[:, 4, 2:] != 0)
+    xd = dev(x)
+    print(f"tiny scales rows={rows} K={K}", flush=True)
+    assert_bitwise(host(g.quantize(xd))[: xq_o.size], xq_o, "standalone quantiser")
+    fmt, N = synth.Q4_0, 48
+    blob, _ = synth.weights(fmt, N, K, 1201)
+    xq = g.act_buffer(rows, K) if rows <= 16 else None
+    if rows <= 16:
+        y = host(g.matvec(fmt, dev(blob), N, K, x=xd, xq=xq))
+        assert_bitwise(host(xq)[: xq_o.size], xq_o, "GEMV quantiser")
+    else:
+        y = host(g.matmul(fmt, dev(blob), N, K, x=xd))
+    assert_bitwise(y, oracle.matmul_canon_f32(fmt, blob, N, K, xq_o, rows), "y")
+    if rows <= 16:
+        wu, _ = synth.weights(fmt, N, K, 1202)
+        h = host(g.gateup_swiglu(fmt, dev(blob), dev(wu), N, K, x=xd))
+        want = oracle.swiglu(oracle.matmul_canon_f32(fmt, blob, N, K, xq_o, rows),
+                             oracle.matmul_canon_f32(fmt, wu, N, K, xq_o, rows))
+        assert_bitwise(h, want, "h")
