@@ -52,9 +52,16 @@ def lib():
         L.oracle_dense_f64.argtypes = [I, P, I64, I64, P, I64, P]
         L.oracle_matmul_canon_f32.argtypes = [I, P, I64, I64, P, I64, P]
         L.oracle_swiglu.argtypes = [P, P, I64, P]
+        L.oracle_quantize_act_q8k.argtypes = [P, I64, I64, P]
+        L.oracle_dequant_act_q8k.argtypes = [P, I64, I64, P]
+        L.oracle_partials_q8k.argtypes = [I, P, I64, I64, P, I64, P]
+        L.oracle_matmul_q8k_f64.argtypes = [I, P, I64, I64, P, I64, P, P]
+        L.oracle_matmul_q8k_canon_f32.argtypes = [I, P, I64, I64, P, I64, P]
         for name in ("oracle_quantize_act", "oracle_unpack", "oracle_dequant",
                      "oracle_dequant_act", "oracle_partials", "oracle_matmul_f64",
-                     "oracle_dense_f64", "oracle_matmul_canon_f32", "oracle_swiglu"):
+                     "oracle_dense_f64", "oracle_matmul_canon_f32", "oracle_swiglu",
+                     "oracle_quantize_act_q8k", "oracle_dequant_act_q8k", "oracle_partials_q8k",
+                     "oracle_matmul_q8k_f64", "oracle_matmul_q8k_canon_f32"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -163,3 +170,53 @@ def swiglu(g, u) -> np.ndarray:
     h = np.zeros(g.shape, np.float32)
     _ok(lib().oracle_swiglu(_p(g), _p(u), g.size, _p(h)), "swiglu")
     return h
+
+
+# ------------------------------------------ K-quants x Q8_K activations --
+
+Q8K_BYTES = 292
+
+
+def quantize_act_q8k(x: np.ndarray) -> np.ndarray:
+    """f32 [rows, K] (K % 256 == 0) -> Q8_K blocks uint8 [rows * K/256 * 292]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, K = x.shape
+    out = np.zeros(rows * (K // 256) * Q8K_BYTES, dtype=np.uint8)
+    _ok(lib().oracle_quantize_act_q8k(_p(x), rows, K, _p(out)), "quantize_act_q8k")
+    return out
+
+
+def dequant_act_q8k(xq, rows: int, K: int) -> np.ndarray:
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    out = np.zeros(rows * K, np.float64)
+    _ok(lib().oracle_dequant_act_q8k(_p(xq), rows, K, _p(out)), "dequant_act_q8k")
+    return out.reshape(rows, K)
+
+
+def partials_q8k(fmt: int, blob, N: int, K: int, xq, B: int) -> np.ndarray:
+    """Q4_K [B, N, K/256, 2] (P, Q); Q6_K [B, N, K/256]."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    per = 2 if fmt == Q4_K else 1
+    P = np.zeros(B * N * (K // 256) * per, np.int32)
+    _ok(lib().oracle_partials_q8k(fmt, _p(blob), N, K, _p(xq), B, _p(P)), "partials_q8k")
+    return P.reshape((B, N, K // 256, 2) if per == 2 else (B, N, K // 256))
+
+
+def matmul_q8k_f64(fmt: int, blob, N: int, K: int, xq, B: int, want_abs: bool = True):
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    y = np.zeros(B * N, np.float64)
+    A = np.zeros(B * N, np.float64) if want_abs else None
+    _ok(lib().oracle_matmul_q8k_f64(fmt, _p(blob), N, K, _p(xq), B, _p(y), _p(A)),
+        "matmul_q8k_f64")
+    return y.reshape(B, N), (A.reshape(B, N) if want_abs else None)
+
+
+def matmul_q8k_canon_f32(fmt: int, blob, N: int, K: int, xq, B: int) -> np.ndarray:
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    y = np.zeros(B * N, np.float32)
+    _ok(lib().oracle_matmul_q8k_canon_f32(fmt, _p(blob), N, K, _p(xq), B, _p(y)),
+        "matmul_q8k_canon_f32")
+    return y.reshape(B, N)

@@ -468,3 +468,184 @@ int oracle_swiglu(const float* g, const float* u, int64_t n, float* h) {
     }
     return 0;
 }
+
+/* ------------------------------------- K-quants x Q8_K activations ----- */
+/*
+ * Q8_K: the 8-bit format of the K-quant family ("Models and formats", the
+ * list of tensor formats, which names it next to Q2_K..Q6_K).  The pages do
+ * not describe it; taken here: one block per 256 elements, 292 bytes: the
+ * scale d as an f32 (LE), 256 int8 codes, then 16 int16 (LE) sums of the
+ * codes of each 16-element group (stored for the kernels; the oracle
+ * recomputes every sum it needs from the codes).  The quantisation rule is
+ * the Q8_0 rule over 256 elements, with the f32 d kept as is: amax, d =
+ * amax/127, id = 1/d (0 when 1/d is not finite), code = round-half-away(x*id).
+ *
+ * The multiply pairs it with Q4_K and Q6_K weights, whose sub-block scales
+ * are integers, so one superblock's partial is one integer (two for Q4_K):
+ *   Q4_K: P = sum_j sc_j sum_{k in j} q_k a_k,   Q = sum_j m_j sum_{k in j} a_k
+ *   Q6_K: I = sum_j s_j sum_{k in j} (q_k - 32) a_k
+ * and the superblock adds d_a (d P - dmin Q), or d_a d I.
+ */
+
+enum { Q8K_BYTES = 292 };
+
+static float rdf32(const uint8_t* p) {
+    uint32_t u = rd32(p);
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+int oracle_quantize_act_q8k(const float* x, int64_t rows, int64_t K, uint8_t* out) {
+    if (rows < 0 || K <= 0 || K % 256) return -2;
+    int64_t nsb = K / 256;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t s = 0; s < nsb; s++) {
+            const float* xb = x + r * K + 256 * s;
+            uint8_t* o = out + (r * nsb + s) * Q8K_BYTES;
+            float amax = 0.0f;
+            for (int i = 0; i < 256; i++) amax = fmaxf(amax, fabsf(xb[i]));
+            float d = amax / 127.0f;
+            float rcp = 1.0f / d;
+            float id = isinf(rcp) ? 0.0f : rcp;
+            uint32_t du;
+            memcpy(&du, &d, 4);
+            for (int i = 0; i < 4; i++) o[i] = (uint8_t)(du >> (8 * i));
+            int8_t q[256];
+            for (int i = 0; i < 256; i++) q[i] = (int8_t)(int)roundf(xb[i] * id);
+            for (int i = 0; i < 256; i++) o[4 + i] = (uint8_t)q[i];
+            for (int g = 0; g < 16; g++) {
+                int sum = 0;
+                for (int i = 0; i < 16; i++) sum += q[16 * g + i];
+                o[260 + 2 * g] = (uint8_t)(sum & 255);
+                o[261 + 2 * g] = (uint8_t)((sum >> 8) & 255);
+            }
+        }
+    return 0;
+}
+
+int oracle_dequant_act_q8k(const uint8_t* xq, int64_t rows, int64_t K, double* out) {
+    if (rows < 0 || K <= 0 || K % 256) return -2;
+    int64_t nsb = K / 256;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t s = 0; s < nsb; s++) {
+            const uint8_t* blk = xq + (r * nsb + s) * Q8K_BYTES;
+            double d = (double)rdf32(blk);
+            for (int i = 0; i < 256; i++) out[r * K + 256 * s + i] = d * (int8_t)blk[4 + i];
+        }
+    return 0;
+}
+
+static int check_q8k(int type, int64_t N, int64_t K, int64_t B, int* qk, int* nbytes) {
+    if (type != T_Q4_K && type != T_Q6_K) return -1;
+    int rc = check(type, N, K, qk, nbytes);
+    if (rc) return rc;
+    return B < 0 ? -2 : 0;
+}
+
+/* Integer partial(s) of superblock s of one Q8_K activation row. */
+static void superblock_ints(const row_t* r, const uint8_t* arow, int64_t s, int64_t* I, int64_t* Q) {
+    const uint8_t* ablk = arow + s * Q8K_BYTES;
+    *I = 0;
+    *Q = 0;
+    for (int i = 0; i < 256; i++) {
+        int64_t a = (int8_t)ablk[4 + i];
+        *I += r->wint[256 * s + i] * a;
+        *Q += r->mint[256 * s + i] * a;
+    }
+}
+
+int oracle_partials_q8k(int type, const uint8_t* w, int64_t N, int64_t K,
+                        const uint8_t* xq, int64_t B, int32_t* P) {
+    int qk, nbytes, rc = check_q8k(type, N, K, B, &qk, &nbytes);
+    if (rc) return rc;
+    int64_t nsb = K / 256, rb = nsb * nbytes;
+    int per = type == T_Q4_K ? 2 : 1;
+    row_t r;
+    if (row_alloc(&r, K)) { row_free(&r); return -4; }
+    for (int64_t n = 0; n < N; n++) {
+        row_decode(type, w + n * rb, K, qk, nbytes, &r);
+        for (int64_t m = 0; m < B; m++)
+            for (int64_t s = 0; s < nsb; s++) {
+                int64_t I, Q;
+                superblock_ints(&r, xq + m * nsb * Q8K_BYTES, s, &I, &Q);
+                if (!fits32(I) || !fits32(Q)) { row_free(&r); return -3; }
+                int32_t* o = P + ((m * N + n) * nsb + s) * per;
+                o[0] = (int32_t)I;
+                if (per == 2) o[1] = (int32_t)Q;
+            }
+    }
+    row_free(&r);
+    return 0;
+}
+
+int oracle_matmul_q8k_f64(int type, const uint8_t* w, int64_t N, int64_t K,
+                          const uint8_t* xq, int64_t B, double* y, double* A) {
+    int qk, nbytes, rc = check_q8k(type, N, K, B, &qk, &nbytes);
+    if (rc) return rc;
+    int64_t nsb = K / 256, rb = nsb * nbytes;
+    row_t r;
+    if (row_alloc(&r, K)) { row_free(&r); return -4; }
+    for (int64_t n = 0; n < N; n++) {
+        row_decode(type, w + n * rb, K, qk, nbytes, &r);
+        for (int64_t m = 0; m < B; m++) {
+            const uint8_t* arow = xq + m * nsb * Q8K_BYTES;
+            double acc = 0.0, absacc = 0.0;
+            for (int64_t s = 0; s < nsb; s++) {
+                int64_t I, Q;
+                superblock_ints(&r, arow, s, &I, &Q);
+                double da = (double)rdf32(arow + s * Q8K_BYTES);
+                double dw = r.d[256 * s], dmw = r.dmin[256 * s];
+                acc += da * (dw * (double)I - dmw * (double)Q);
+                if (A)
+                    for (int i = 0; i < 256; i++) {
+                        int64_t k = 256 * s + i;
+                        double wv = dw * (double)r.wint[k] - dmw * (double)r.mint[k];
+                        double xv = da * (double)(int8_t)arow[s * Q8K_BYTES + 4 + i];
+                        absacc += fabs(wv * xv);
+                    }
+            }
+            if (y) y[m * N + n] = acc;
+            if (A) A[m * N + n] = absacc;
+        }
+    }
+    row_free(&r);
+    return 0;
+}
+
+/* The f32 order of the Q8_K path: per superblock s (in ascending order),
+ *   Q4_K: p = fmaf((float)P, fl(d * d_a), +0); p = fmaf(-(float)Q, fl(dmin * d_a), p)
+ *   Q6_K: p = fmaf((float)I, fl(d * d_a), +0)
+ * where fl(d * d_a) is the f32 product of the fp16 weight scale and the f32
+ * activation scale, rounded once, and (float)P rounds to nearest even when
+ * |P| > 2^24; then y = ((+0 + p_0) + p_1) + ... */
+int oracle_matmul_q8k_canon_f32(int type, const uint8_t* w, int64_t N, int64_t K,
+                                const uint8_t* xq, int64_t B, float* y) {
+    int qk, nbytes, rc = check_q8k(type, N, K, B, &qk, &nbytes);
+    if (rc) return rc;
+    int64_t nsb = K / 256, rb = nsb * nbytes;
+    row_t r;
+    if (row_alloc(&r, K)) { row_free(&r); return -4; }
+    for (int64_t n = 0; n < N; n++) {
+        row_decode(type, w + n * rb, K, qk, nbytes, &r);
+        for (int64_t m = 0; m < B; m++) {
+            const uint8_t* arow = xq + m * nsb * Q8K_BYTES;
+            float acc = 0.0f;
+            for (int64_t s = 0; s < nsb; s++) {
+                int64_t I, Q;
+                superblock_ints(&r, arow, s, &I, &Q);
+                float da = rdf32(arow + s * Q8K_BYTES);
+                float sd = (float)r.d[256 * s] * da;
+                float p = fmaf((float)I, sd, 0.0f);
+                if (type == T_Q4_K) {
+                    float sm = (float)r.dmin[256 * s] * da;
+                    p = fmaf(-(float)Q, sm, p);
+                }
+                acc = acc + p;
+            }
+            y[m * N + n] = acc;
+        }
+    }
+    row_free(&r);
+    return 0;
+}

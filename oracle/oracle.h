@@ -88,6 +88,25 @@ int oracle_matmul_canon_f32(int type, const uint8_t* w, int64_t N, int64_t K,
  * s = g / (1 + t), h = s * u and rounded once to f32. */
 int oracle_swiglu(const float* g, const float* u, int64_t n, float* h);
 
+/* ---- K-quant weights (Q4_K = 12, Q6_K = 14) x Q8_K activations ----
+ * Q8_K block: 256 elements in 292 bytes: f32 d (LE), int8 codes[256], int16
+ * sums of each 16-element group of codes (LE).  Quantisation as Q8_0 over
+ * 256 elements with d kept in f32.  K % 256 == 0. */
+int oracle_quantize_act_q8k(const float* x, int64_t rows, int64_t K, uint8_t* out);
+int oracle_dequant_act_q8k(const uint8_t* xq, int64_t rows, int64_t K, double* out);
+/* Per superblock s: Q4_K [B][N][K/256][2] = (sum_j sc_j sum q a, sum_j m_j sum a);
+ * Q6_K [B][N][K/256] = sum_j s_j sum (q-32) a.  Other types: -1. */
+int oracle_partials_q8k(int type, const uint8_t* w, int64_t N, int64_t K,
+                        const uint8_t* xq, int64_t B, int32_t* P);
+/* y = sum_s d_a (d P - dmin Q) (Q4_K) or d_a d I (Q6_K) in f64; A = sum |w^ x^|. */
+int oracle_matmul_q8k_f64(int type, const uint8_t* w, int64_t N, int64_t K,
+                          const uint8_t* xq, int64_t B, double* y, double* A);
+/* The f32 order of the Q8_K path: per superblock in order,
+ * p = fmaf((float)P, fl(d*d_a), +0) then (Q4_K) p = fmaf(-(float)Q,
+ * fl(dmin*d_a), p); y = ((+0 + p_0) + p_1) + ... */
+int oracle_matmul_q8k_canon_f32(int type, const uint8_t* w, int64_t N, int64_t K,
+                                const uint8_t* xq, int64_t B, float* y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,19 @@ static int run(int type, int64_t N, int64_t K, int64_t B, int qk, int bb) {
         if (!(fabs(y[i] - yd[i]) <= 1e-9 * A[i] + 1e-300)) bad = 1;
         if (!(fabs((double)yc[i] - y[i]) <= 1e-4 * A[i])) bad = 1;
     }
+    if (qk == 256) {  /* the Q8_K path of the K-quants */
+        uint8_t* xk = malloc((size_t)(B * (K / 256) * 292));
+        int32_t* Pk = malloc(sizeof(int32_t) * (size_t)(B * N * (K / 256) * 2));
+        float* yk = malloc(sizeof(float) * (size_t)(B * N));
+        bad |= oracle_quantize_act_q8k(x, B, K, xk) != 0;
+        bad |= oracle_dequant_act_q8k(xk, B, K, xa) != 0;
+        bad |= oracle_partials_q8k(type, w, N, K, xk, B, Pk) != 0;
+        bad |= oracle_matmul_q8k_f64(type, w, N, K, xk, B, y, A) != 0;
+        bad |= oracle_matmul_q8k_canon_f32(type, w, N, K, xk, B, yk) != 0;
+        for (int64_t i = 0; i < B * N; i++)
+            if (!(fabs((double)yk[i] - y[i]) <= 1e-4 * A[i])) bad = 1;
+        free(xk); free(Pk); free(yk);
+    }
     float h[64], gg[64], uu[64];
     for (int i = 0; i < 64; i++) {
         gg[i] = (float)((int)(next() % 4001) - 2000) / 20.0f;
