@@ -21,7 +21,8 @@ BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_1: (32, 20), Q5_1: (
          Q8_1: (32, 36), Q4_K: (256, 144), Q6_K: (256, 210)}
 EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
            "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc", "qmv_gateup_act_bytes",
-           "qmv_launch_gateup_swiglu", "qmv_strerror")
+           "qmv_launch_gateup_swiglu", "qmv_act_bytes_q8k", "quantize_act_q8_k", "qmv_launch_q8k",
+           "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_strerror")
 MAX_BATCH = 16
 MAX_GROUP = 8
 
@@ -58,11 +59,19 @@ def lib() -> ctypes.CDLL:
         L.qmv_partials_launch.argtypes = [I, P, I64, I64, P, I64, P, P]
         L.qmv_launch_noalloc.argtypes = [I, P, I64, I64, P, I64, P, P]
         L.qmm_partials_launch.argtypes = [I, P, I64, I64, P, I64, P, P]
+        L.qmv_act_bytes_q8k.argtypes = [I64, I64]
+        L.qmv_act_bytes_q8k.restype = ctypes.c_size_t
+        L.quantize_act_q8_k.argtypes = [P, P, I64, I64, P]
+        L.qmv_launch_q8k.argtypes = [I, P, I64, I64, P, I64, P, P, P]
+        L.qmm_launch_q8k.argtypes = [I, P, I64, I64, P, I64, P, P, P]
+        L.qmv_partials_q8k_launch.argtypes = [I, P, I64, I64, P, I64, P, P]
         L.qmv_gateup_act_bytes.argtypes = [I64, I64, I64]
         L.qmv_gateup_act_bytes.restype = ctypes.c_size_t
         L.qmv_launch_gateup_swiglu.argtypes = [I, P, P, I64, I64, P, I64, P, P, P]
         for f in ("quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
-                  "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc", "qmv_launch_gateup_swiglu"):
+                  "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc",
+                  "qmv_launch_gateup_swiglu", "quantize_act_q8_k", "qmv_launch_q8k",
+                  "qmm_launch_q8k", "qmv_partials_q8k_launch"):
             getattr(L, f).restype = I
         L.qmv_strerror.argtypes = [I]
         L.qmv_strerror.restype = ctypes.c_char_p
@@ -128,6 +137,30 @@ def qmv_launch_gateup_swiglu(type: int, w_gate: int, w_up: int, N: int, K: int, 
                              xq: int, h: int, stream: int = 0) -> None:
     _check(lib().qmv_launch_gateup_swiglu(type, w_gate, w_up, N, K, x, B, xq, h, stream),
            "qmv_launch_gateup_swiglu")
+
+
+def qmv_act_bytes_q8k(rows: int, K: int) -> int:
+    return int(lib().qmv_act_bytes_q8k(rows, K))
+
+
+def quantize_act_q8_k(x, xq: int, rows: int, K: int, stream: int = 0) -> None:
+    _check(lib().quantize_act_q8_k(x, xq, rows, K, stream), "quantize_act_q8_k")
+
+
+def qmv_launch_q8k(type: int, w: int, N: int, K: int, x, B: int, xq: int, y: int,
+                   stream: int = 0) -> None:
+    _check(lib().qmv_launch_q8k(type, w, N, K, x, B, xq, y, stream), "qmv_launch_q8k")
+
+
+def qmm_launch_q8k(type: int, w: int, N: int, K: int, x, M: int, xq: int, y: int,
+                   stream: int = 0) -> None:
+    _check(lib().qmm_launch_q8k(type, w, N, K, x, M, xq, y, stream), "qmm_launch_q8k")
+
+
+def qmv_partials_q8k_launch(type: int, w: int, N: int, K: int, xq: int, M: int, P: int,
+                            stream: int = 0) -> None:
+    _check(lib().qmv_partials_q8k_launch(type, w, N, K, xq, M, P, stream),
+           "qmv_partials_q8k_launch")
 
 
 def qmv_strerror(code: int) -> str:
@@ -270,4 +303,48 @@ def partials(type: int, w, N: int, K: int, xq, B: int, P=None, stream=None, gemm
     fn = qmm_partials_launch if gemm else qmv_partials_launch
     fn(type, _dev(w, torch.uint8, "w"), N, K, _dev(xq, torch.uint8, "xq"), B,
        _dev(P, torch.int32, "P"), _stream(stream))
+    return P
+
+
+# ------------------------------------------- K-quants x Q8_K activations --
+
+def quantize_q8k(x, xq=None, stream=None, rows=None, K=None):
+    """x: f32 [rows, K] (K % 256 == 0) -> Q8_K scratch (blocks first); x None:
+    rebuild the staging from the Q8_K blocks already in xq."""
+    import torch
+    if x is not None:
+        rows, K = x.shape
+    if xq is None:
+        n = qmv_act_bytes_q8k(rows, K)
+        if n == 0:
+            raise ValueError(f"bad shape rows={rows} K={K}")
+        xq = torch.empty(n, dtype=torch.uint8, device=x.device)
+    xp = _dev(x, torch.float32, "x") if x is not None else None
+    quantize_act_q8_k(xp, _dev(xq, torch.uint8, "xq"), rows, K, _stream(stream))
+    return xq
+
+
+def matmul_q8k(type: int, w, N: int, K: int, x=None, xq=None, M=None, y=None, stream=None):
+    """y [M, N] f32 = x [M, K] @ W^T on the Q8_K path (any M; x None: staged xq)."""
+    import torch
+    if x is not None:
+        M = x.shape[0]
+    if xq is None:
+        xq = torch.empty(qmv_act_bytes_q8k(M, K), dtype=torch.uint8, device=w.device)
+    if y is None:
+        y = torch.empty(M, N, dtype=torch.float32, device=w.device)
+    xp = _dev(x, torch.float32, "x") if x is not None else None
+    qmm_launch_q8k(type, _dev(w, torch.uint8, "w"), N, K, xp, M, _dev(xq, torch.uint8, "xq"),
+                   _dev(y, torch.float32, "y"), _stream(stream))
+    return y
+
+
+def partials_q8k(type: int, w, N: int, K: int, xq, M: int, P=None, stream=None):
+    """Superblock partials of the Q8_K path: Q4_K [M, N, K/256, 2], Q6_K [M, N, K/256]."""
+    import torch
+    shape = (M, N, K // 256, 2) if type == Q4_K else (M, N, K // 256)
+    if P is None:
+        P = torch.empty(shape, dtype=torch.int32, device=w.device)
+    qmv_partials_q8k_launch(type, _dev(w, torch.uint8, "w"), N, K, _dev(xq, torch.uint8, "xq"), M,
+                            _dev(P, torch.int32, "P"), _stream(stream))
     return P

@@ -18,6 +18,7 @@ CEIL_SRC = os.path.join(CSRC, "qmv_ceilings.hip")
 # VGPRs (no accumulation-register copies); the GEMM keeps the default choice
 SOURCES = [(os.path.join(CSRC, "qmv_kernels.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
            (os.path.join(CSRC, "qmm_kernels.hip"), []),
+           (os.path.join(CSRC, "qmm8k_kernels.hip"), []),
            (os.path.join(CSRC, "qmv_noalloc.hip"), []),
            (os.path.join(CSRC, "qmv_api.cpp"), [])]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

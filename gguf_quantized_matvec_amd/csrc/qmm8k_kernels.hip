@@ -1,0 +1,472 @@
+// K-quant weights (Q4_K, Q6_K) x Q8_K activations on gfx950: the Q8_K
+// quantiser and the prefill GEMM on int8 MFMA.
+//
+// Q8_K is the 8-bit format of the K-quant family ("Models and formats", the
+// list of tensor formats): one f32 scale per 256 activations.  Against it,
+// the integer sub-block scales of Q4_K / Q6_K fold into the integer partial
+// of a whole superblock, so the f32 scaling runs once per 256 elements
+// instead of once per 32 (include/qmv.h states the f32 order):
+//   Q4_K: P = sum_j sc_j sum_k q a,  Q = sum_j m_j sum_k a
+//   Q6_K: I = sum_j s_j sum_k (q - 32) a
+//
+// The GEMM keeps the whole superblock on the int8 matrix cores
+// (v_mfma_i32_32x32x32_i8), exactly: each weight element's value sc*q
+// (Q4_K, 0..945) or s*(q-32) (Q6_K, -4096..4064) is split into two int8
+// digits, v = 64*hi + lo with lo in 0..63, and the superblock partial is
+// ACC_lo + 64*ACC_hi of two int32 accumulators.  Q4_K's min term Q runs on
+// the matrix cores too: the eight 32-code sums S_j of an activation row, split
+// the same way, against the row's eight m_j, in one otherwise-zero MFMA per
+// digit.  The VALU then does per superblock and output: P, (float)P, the
+// scale product, one or two fma and the add in superblock order.
+//
+// Tiling: a workgroup of 4 waves owns 128 weight rows (32 per wave: lane l
+// decodes row l%32's codes for its half of each 32-element block straight
+// from the GGUF bytes into MFMA B operands) x 32*WM activation rows, staged
+// per superblock in LDS (double buffered, one barrier per superblock); the
+// next superblock's weight bytes and activation rows are loaded into
+// registers while the current one is multiplied.
+//
+// Built with -ffp-contract=off: every float operation is the one written.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmv_internal.h"
+
+namespace qmv {
+namespace {
+
+constexpr int T_Q4_K = 12, T_Q6_K = 14;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef short s2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    const uint16_t u = (uint16_t)h;
+    _Float16 f;
+    __builtin_memcpy(&f, &u, 2);
+    return (float)f;
+}
+
+// id = 1/d, or 0 when 1/d is not finite (the block quantises to zero codes)
+__device__ __forceinline__ float inv_scale(float d) {
+    const float r = 1.0f / d;
+    return __builtin_isinf(r) ? 0.0f : r;
+}
+
+// ------------------------------------------------------------ quantise ----
+// One wave per (row, superblock), 4 elements per lane: amax over the wave,
+// d = amax/127, codes = round-half-away(x * id); the public Q8_K block and
+// the row-major staging (codes, d per 32 codes, the two 16-code sums of each
+// 32 codes).  FROM_PUBLIC: take codes and d from the Q8_K block in xq.
+template <bool FROM_PUBLIC, bool A16>
+__global__ __launch_bounds__(256) void k_quantize_q8k(const float* __restrict__ x,
+                                                      uint8_t* __restrict__ xq, int64_t rows,
+                                                      int64_t K, ActLayoutK L) {
+    const int lane = threadIdx.x & 63;
+    const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (task >= rows * L.nsb) return;  // uniform per wave
+    const int64_t r = task / L.nsb, sb = task - r * L.nsb;
+    uint8_t* pub = xq + task * 292;
+    uint32_t c4 = 0;
+    float d;
+    if constexpr (!FROM_PUBLIC) {
+        const float* xb = x + r * K + 256 * sb + 4 * lane;
+        float v[4];
+        if constexpr (A16) {
+            const float4 f = *reinterpret_cast<const float4*>(xb);
+            v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) v[i] = xb[i];
+        }
+        float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        d = amax / 127.0f;
+        const float id = inv_scale(d);
+#pragma unroll
+        for (int i = 0; i < 4; i++) c4 |= ((uint32_t)(int)roundf(v[i] * id) & 0xFFu) << (8 * i);
+        if (lane == 0) *reinterpret_cast<float*>(pub) = d;
+        *reinterpret_cast<uint32_t*>(pub + 4 + 4 * lane) = c4;
+    } else {
+        d = *reinterpret_cast<const float*>(pub);
+        c4 = *reinterpret_cast<const uint32_t*>(pub + 4 + 4 * lane);
+    }
+    int s4 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) s4 += (int)(int8_t)(c4 >> (8 * i));
+    int s16 = s4 + __shfl_xor(s4, 1);
+    s16 += __shfl_xor(s16, 2);                   // sum of the lane's 16-code group
+    const int s16b = __shfl_xor(s16, 4);         // the other group of its 32 codes
+    if (!FROM_PUBLIC && (lane & 3) == 0)
+        *reinterpret_cast<int16_t*>(pub + 260 + 2 * (lane >> 2)) = (int16_t)s16;
+    *reinterpret_cast<uint32_t*>(xq + L.rcodes + r * K + 256 * sb + 4 * lane) = c4;
+    if ((lane & 7) == 0) {
+        const int64_t b = r * L.nb + 8 * sb + (lane >> 3);
+        reinterpret_cast<float*>(xq + L.rda)[b] = d;
+        reinterpret_cast<int32_t*>(xq + L.rs16)[b] =
+            (int32_t)(((uint32_t)s16 & 0xFFFFu) | ((uint32_t)s16b << 16));
+    }
+}
+
+// ---------------------------------------------------------------- GEMM ----
+// 16 bytes at a 2-byte aligned address (Q6_K superblocks are 210 bytes):
+// five dwords from the 4-byte aligned address below it, shifted down.
+// The fifth dword is read only when p is not 4-byte aligned, so that no byte
+// past p + 16 is touched (the last field of the blob's last superblock).
+__device__ __forceinline__ uint4 ld16_a2(const uint8_t* p) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
+    const uint32_t sh = (uint32_t)(a & 3);
+    uint32_t v[5];
+    __builtin_memcpy(v, q, 16);
+    v[4] = sh ? q[4] : 0u;
+    return make_uint4(__builtin_amdgcn_alignbyte(v[1], v[0], sh),
+                      __builtin_amdgcn_alignbyte(v[2], v[1], sh),
+                      __builtin_amdgcn_alignbyte(v[3], v[2], sh),
+                      __builtin_amdgcn_alignbyte(v[4], v[3], sh));
+}
+
+// The bytes of one superblock that one lane (weight row, half h of every
+// 32-element block: elements 16h..16h+15) needs.
+template <int FMT> struct WRawK;
+template <> struct WRawK<T_Q4_K> {
+    uint4 hdr;    // d, dmin, 12 scale bytes
+    uint4 qs[4];  // qs[32c + 16h .. +16], c = 0..3 (blocks 2c, 2c+1: low, high nibbles)
+};
+template <> struct WRawK<T_Q6_K> {
+    uint4 ql[4];  // ql[64hh + 32kk + 16h .. +16], index 2hh + kk
+    uint4 qh[2];  // qh[32hh + 16h .. +16]
+    uint4 sc;     // bytes 192..207: the 16 sub-scales
+    uint32_t d;   // bytes 208, 209: fp16 d
+};
+
+template <int FMT>
+__device__ __forceinline__ void fetch_wk(const uint8_t* sbp, int h, WRawK<FMT>& r) {
+    if constexpr (FMT == T_Q4_K) {
+        const uint4* p = reinterpret_cast<const uint4*>(sbp);  // 144-byte superblocks, 16-aligned
+        r.hdr = p[0];
+#pragma unroll
+        for (int c = 0; c < 4; c++) r.qs[c] = p[1 + 2 * c + h];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) r.ql[i] = ld16_a2(sbp + 64 * (i >> 1) + 32 * (i & 1) + 16 * h);
+#pragma unroll
+        for (int i = 0; i < 2; i++) r.qh[i] = ld16_a2(sbp + 128 + 32 * i + 16 * h);
+        r.sc = ld16_a2(sbp + 192);
+        r.d = (uint32_t)sbp[208] | ((uint32_t)sbp[209] << 8);
+    }
+}
+
+__device__ __forceinline__ uint32_t u4_at(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Q4_K: 6-bit scale and min of sub-block j from the 12 scale bytes.
+__device__ __forceinline__ void q4k_sc_m(const uint4& hdr, int j, int& sc, int& mn) {
+    auto byte = [&](int i) -> int { return (int)((u4_at(hdr, 1 + (i >> 2)) >> (8 * (i & 3))) & 0xFFu); };
+    if (j < 4) {
+        sc = byte(j) & 63;
+        mn = byte(j + 4) & 63;
+    } else {
+        sc = (byte(j + 4) & 15) | ((byte(j - 4) >> 6) << 4);
+        mn = (byte(j + 4) >> 4) | ((byte(j) >> 6) << 4);
+    }
+}
+
+// Two int8 digits of 4 values v = f * c (c: 4 codes, one per byte, offset
+// already applied for Q6_K; f the sub-block's integer scale): v = 64 hi + lo,
+// lo in 0..63.  Computed in 16-bit lanes (|v| <= 8064).
+__device__ __forceinline__ void digits4(uint32_t codes, int off, int f, uint32_t& lo, uint32_t& hi) {
+    const s2 vo = {(short)off, (short)off}, vf = {(short)f, (short)f};
+    const s2 a = __builtin_bit_cast(s2, codes & 0x00FF00FFu) - vo;          // codes 0, 2
+    const s2 b = __builtin_bit_cast(s2, (codes >> 8) & 0x00FF00FFu) - vo;   // codes 1, 3
+    const s2 va = a * vf, vb = b * vf;
+    const s2 m63 = {63, 63}, six = {6, 6};
+    const uint32_t la = __builtin_bit_cast(uint32_t, (s2)(va & m63));
+    const uint32_t lb = __builtin_bit_cast(uint32_t, (s2)(vb & m63));
+    const uint32_t ha = __builtin_bit_cast(uint32_t, (s2)(va >> six)) & 0x00FF00FFu;
+    const uint32_t hb = __builtin_bit_cast(uint32_t, (s2)(vb >> six)) & 0x00FF00FFu;
+    lo = la | (lb << 8);
+    hi = ha | (hb << 8);
+}
+
+// Digits of the lane's 16 weight values of block j (elements 16h..16h+15).
+template <int FMT>
+__device__ __forceinline__ void decode_block(const WRawK<FMT>& r, int j, int h, v4i& wlo, v4i& whi) {
+    uint32_t codes[4];
+    int f, off;
+    if constexpr (FMT == T_Q4_K) {
+        int mn;
+        q4k_sc_m(r.hdr, j, f, mn);
+        off = 0;
+        const uint4 q = r.qs[j >> 1];
+        const int sh = 4 * (j & 1);
+#pragma unroll
+        for (int i = 0; i < 4; i++) codes[i] = (u4_at(q, i) >> sh) & 0x0F0F0F0Fu;
+    } else {
+        const int hh = j >> 2, k = j & 3;
+        const uint4 ql = r.ql[2 * hh + (k & 1)], qh = r.qh[hh];
+        const int lsh = 4 * (k >> 1), hsh = 2 * k;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            codes[i] = ((u4_at(ql, i) >> lsh) & 0x0F0F0F0Fu) | (((u4_at(qh, i) >> hsh) & 0x03030303u) << 4);
+        f = (int)(int8_t)((u4_at(r.sc, (2 * j + h) >> 2) >> (8 * ((2 * j + h) & 3))) & 0xFFu);
+        off = 32;
+    }
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) digits4(codes[i], off, f, lo[i], hi[i]);
+    wlo = (v4i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
+    whi = (v4i){(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+constexpr int ROWB = 256 + 16;  // LDS bytes per staged activation row (16 of padding)
+
+// WM: 32-row MFMA tiles per wave along M (the workgroup's 32*WM activation
+// rows).  PART: write the exact superblock partials to P instead of y.
+template <int FMT, int WM, bool PART>
+__global__ __launch_bounds__(256, 2) void k_gemm8k(const uint8_t* __restrict__ w, int64_t N,
+                                                   int64_t K, const uint8_t* __restrict__ xq,
+                                                   ActLayoutK L, int64_t M, int64_t tilesM,
+                                                   int64_t tilesN, float* __restrict__ y,
+                                                   int32_t* __restrict__ P) {
+    constexpr int TM = 32 * WM;
+    constexpr int NPC = TM * 16 / 256;  // 16-byte activation pieces per thread and superblock
+    __shared__ __attribute__((aligned(16))) uint8_t act[2][TM * ROWB];
+    __shared__ __attribute__((aligned(16))) float dal[2][TM];
+    __shared__ __attribute__((aligned(16))) int32_t s16l[2][TM * 8];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lr = lane & 31, h = lane >> 5;
+    // workgroup -> tile: XCD x (= blockIdx % 8) takes a contiguous range of
+    // tiles, M fastest, so that the workgroups resident on one XCD share
+    // weight rows and activation rows through its L2
+    int64_t tm, tn;
+    {
+        const int64_t nt = tilesM * tilesN, per = (nt + 7) >> 3;
+        const int64_t x8 = blockIdx.x & 7, k8 = blockIdx.x >> 3;
+        int64_t t = x8 * per + k8;
+        if (x8 >= (nt & 7) && (nt & 7)) {  // ranges of per-1 after the first nt%8 XCDs
+            t = (nt & 7) * per + (x8 - (nt & 7)) * (per - 1) + k8;
+        }
+        tm = t % tilesM;
+        tn = t / tilesM;
+    }
+    const int64_t m0 = tm * TM, n0 = tn * 128;
+    const int nsb = (int)(K >> 8), nb = (int)(K >> 5);
+    const int64_t R = (int64_t)nsb * (FMT == T_Q4_K ? 144 : 210);
+    const int64_t n = n0 + 32 * wv + lr;
+    const uint8_t* wrow = w + (n < N ? n : N - 1) * R;
+    constexpr int SBB = FMT == T_Q4_K ? 144 : 210;
+
+    // activation staging: piece q = tid + 256 p is row q/16, bytes 16 (q%16)
+    const uint8_t* asrc[NPC];
+#pragma unroll
+    for (int p = 0; p < NPC; p++) {
+        const int q = tid + 256 * p, row = q >> 4;
+        const int64_t m = m0 + row < M ? m0 + row : M - 1;
+        asrc[p] = xq + L.rcodes + m * K + 16 * (q & 15);
+    }
+    const float* dsrc = reinterpret_cast<const float*>(xq + L.rda);
+    const int32_t* ssrc = reinterpret_cast<const int32_t*>(xq + L.rs16);
+    auto arow = [&](int row) -> int64_t { return m0 + row < M ? m0 + row : M - 1; };
+
+    uint4 apre[NPC];
+    float dpre = 0.0f;
+    int32_t spre[2] = {0, 0};
+    auto load_act = [&](int s) {
+#pragma unroll
+        for (int p = 0; p < NPC; p++) apre[p] = *reinterpret_cast<const uint4*>(asrc[p] + 256 * s);
+        if (tid < TM) dpre = dsrc[arow(tid) * nb + 8 * s];
+        if constexpr (FMT == T_Q4_K) {
+#pragma unroll
+            for (int p = 0; p < 2; p++) {
+                const int q = tid + 256 * p;  // TM * 8 words
+                if (q < TM * 8) spre[p] = ssrc[arow(q >> 3) * nb + 8 * s + (q & 7)];
+            }
+        }
+    };
+    auto store_act = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < NPC; p++) {
+            const int q = tid + 256 * p;
+            *reinterpret_cast<uint4*>(&act[buf][(q >> 4) * ROWB + 16 * (q & 15)]) = apre[p];
+        }
+        if (tid < TM) dal[buf][tid] = dpre;
+        if constexpr (FMT == T_Q4_K) {
+#pragma unroll
+            for (int p = 0; p < 2; p++) {
+                const int q = tid + 256 * p;
+                if (q < TM * 8) s16l[buf][q] = spre[p];
+            }
+        }
+    };
+
+    WRawK<FMT> wcur, wnext;
+    load_act(0);
+    fetch_wk<FMT>(wrow, h, wcur);
+    store_act(0);
+    __syncthreads();
+
+    float yacc[WM][16];
+#pragma unroll
+    for (int t = 0; t < WM; t++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) yacc[t][e] = 0.0f;
+    const v16i zero16 = {};
+
+    for (int s = 0; s < nsb; s++) {
+        const int buf = s & 1;
+        if (s + 1 < nsb) {
+            load_act(s + 1);
+            fetch_wk<FMT>(wrow + (int64_t)(s + 1) * SBB, h, wnext);
+        }
+        v16i alo[WM], ahi[WM];
+#pragma unroll
+        for (int t = 0; t < WM; t++) alo[t] = ahi[t] = zero16;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            v4i wlo, whi;
+            decode_block<FMT>(wcur, j, h, wlo, whi);
+#pragma unroll
+            for (int t = 0; t < WM; t++) {
+                const uint4 av = *reinterpret_cast<const uint4*>(&act[buf][(32 * t + lr) * ROWB + 32 * j + 16 * h]);
+                const v4i a = (v4i){(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+                alo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, wlo, alo[t], 0, 0, 0);
+                ahi[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, whi, ahi[t], 0, 0, 0);
+            }
+        }
+        // Q4_K min term: S_j (activation row) against m_j (weight row) for
+        // j = 4h..4h+3 in bytes 0..3 of the lane's operands, the rest zero
+        v16i qlo[WM], qhi[WM];
+        if constexpr (FMT == T_Q4_K) {
+            uint32_t mb = 0;
+#pragma unroll
+            for (int t2 = 0; t2 < 4; t2++) {
+                int sc, mn;
+                q4k_sc_m(wcur.hdr, 4 * h + t2, sc, mn);
+                mb |= (uint32_t)mn << (8 * t2);
+            }
+            const v4i bm = (v4i){(int)mb, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < WM; t++) {
+                const int32_t* sp = &s16l[buf][(32 * t + lr) * 8 + 4 * h];
+                uint32_t slo = 0, shi = 0;
+#pragma unroll
+                for (int t2 = 0; t2 < 4; t2++) {
+                    const int32_t v = sp[t2];
+                    const int S = (int)(int16_t)(v & 0xFFFF) + (v >> 16);  // -4064..4064
+                    slo |= (uint32_t)(S & 63) << (8 * t2);
+                    shi |= (uint32_t)((S >> 6) & 0xFF) << (8 * t2);
+                }
+                qlo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i){(int)slo, 0, 0, 0}, bm, zero16, 0, 0, 0);
+                qhi[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i){(int)shi, 0, 0, 0}, bm, zero16, 0, 0, 0);
+            }
+        }
+        // lane l, element e of tile t: activation row 32t + 8(e/4) + 4h + e%4,
+        // weight row n (column lr)
+        if constexpr (PART) {
+            constexpr int per = FMT == T_Q4_K ? 2 : 1;
+#pragma unroll
+            for (int t = 0; t < WM; t++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int64_t m = m0 + 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+                    if (m < M && n < N) {
+                        int32_t* o = P + ((m * N + n) * nsb + s) * per;
+                        o[0] = alo[t][e] + 64 * ahi[t][e];
+                        if constexpr (per == 2) o[1] = qlo[t][e] + 64 * qhi[t][e];
+                    }
+                }
+        } else {
+            float dw, dmw = 0.0f;
+            if constexpr (FMT == T_Q4_K) {
+                dw = half_bits_to_float(wcur.hdr.x & 0xFFFFu);
+                dmw = half_bits_to_float(wcur.hdr.x >> 16);
+            } else {
+                dw = half_bits_to_float(wcur.d);
+            }
+#pragma unroll
+            for (int t = 0; t < WM; t++)
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const float4 d4 = *reinterpret_cast<const float4*>(&dal[buf][32 * t + 8 * g + 4 * h]);
+                    const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int e = 4 * g + i;
+                        const int Pv = alo[t][e] + 64 * ahi[t][e];
+                        float p = fmaf((float)Pv, dw * da[i], 0.0f);
+                        if constexpr (FMT == T_Q4_K) {
+                            const int Qv = qlo[t][e] + 64 * qhi[t][e];
+                            p = fmaf(-(float)Qv, dmw * da[i], p);
+                        }
+                        yacc[t][e] = yacc[t][e] + p;
+                    }
+                }
+        }
+        if (s + 1 < nsb) {
+            store_act(buf ^ 1);
+            wcur = wnext;
+        }
+        __syncthreads();
+    }
+    if constexpr (PART) return;
+#pragma unroll
+    for (int t = 0; t < WM; t++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            const int64_t m = m0 + 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (m < M && n < N) y[m * N + n] = yacc[t][e];
+        }
+}
+
+template <int FMT, int WM>
+int launch_gemm8k_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
+                    float* y, int32_t* P, hipStream_t s) {
+    const ActLayoutK L = act_layout_q8k(M, K);
+    const int64_t tilesM = (M + 32 * WM - 1) / (32 * WM), tilesN = (N + 127) / 128;
+    const int64_t grid = tilesM * tilesN;
+    if (grid > INT32_MAX) return (int)hipErrorInvalidValue;
+    if (P)
+        hipLaunchKernelGGL((k_gemm8k<FMT, WM, true>), dim3((unsigned)grid), dim3(256), 0, s, w, N,
+                           K, xq, L, M, tilesM, tilesN, y, P);
+    else
+        hipLaunchKernelGGL((k_gemm8k<FMT, WM, false>), dim3((unsigned)grid), dim3(256), 0, s, w, N,
+                           K, xq, L, M, tilesM, tilesN, y, P);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_quantize_q8k(const float* x, uint8_t* xq, int64_t rows, int64_t K, hipStream_t s) {
+    const ActLayoutK L = act_layout_q8k(rows, K);
+    const int64_t tasks = rows * L.nsb;
+    const unsigned blocks = (unsigned)((tasks + 3) / 4);
+    if (!x)
+        hipLaunchKernelGGL((k_quantize_q8k<true, true>), dim3(blocks), dim3(256), 0, s, x, xq, rows,
+                           K, L);
+    else if (aligned16(x))
+        hipLaunchKernelGGL((k_quantize_q8k<false, true>), dim3(blocks), dim3(256), 0, s, x, xq,
+                           rows, K, L);
+    else
+        hipLaunchKernelGGL((k_quantize_q8k<false, false>), dim3(blocks), dim3(256), 0, s, x, xq,
+                           rows, K, L);
+    return (int)hipGetLastError();
+}
+
+int launch_gemm_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
+                    int64_t M, float* y, int32_t* P, hipStream_t s) {
+    const bool big = M > 32;
+    switch (type) {
+    case T_Q4_K: return big ? launch_gemm8k_t<T_Q4_K, 2>(w, N, K, xq, M, y, P, s)
+                            : launch_gemm8k_t<T_Q4_K, 1>(w, N, K, xq, M, y, P, s);
+    case T_Q6_K: return big ? launch_gemm8k_t<T_Q6_K, 2>(w, N, K, xq, M, y, P, s)
+                            : launch_gemm8k_t<T_Q6_K, 1>(w, N, K, xq, M, y, P, s);
+    }
+    return (int)hipErrorInvalidValue;
+}
+
+}  // namespace qmv

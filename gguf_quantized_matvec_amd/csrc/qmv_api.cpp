@@ -182,6 +182,53 @@ int qmm_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                                              static_cast<hipStream_t>(stream)));
 }
 
+size_t qmv_act_bytes_q8k(int64_t rows, int64_t K) {
+    if (rows < 1 || rows > QMV_MAX_M || K < 256 || K > QMV_MAX_K || K % 256) return 0;
+    return (size_t)qmv::act_layout_q8k(rows, K).total;
+}
+
+int quantize_act_q8_k(const float* x, void* xq, int64_t rows, int64_t K, void* stream) {
+    if (rows < 1 || rows > QMV_MAX_M || K < 256 || K > QMV_MAX_K || K % 256) return QMV_EINVAL_SHAPE;
+    if (!xq || !aligned(xq, 16) || (x && !aligned(x, 4))) return QMV_EINVAL_PTR;
+    const int rc = check_device();
+    if (rc) return rc;
+    return launched(qmv::launch_quantize_q8k(x, static_cast<uint8_t*>(xq), rows, K,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+int q8k_common(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t rows,
+               int64_t max_rows, void* xq, float* y, int32_t* P, void* stream) {
+    if (type != QMV_Q4_K && type != QMV_Q6_K) return QMV_EINVAL_TYPE;
+    int rc = check_weights(type, w, N, K);
+    if (rc) return rc;
+    if (rows < 1 || rows > max_rows) return QMV_EINVAL_SHAPE;
+    if (!xq || !aligned(xq, 16)) return QMV_EINVAL_PTR;
+    if (P ? !aligned(P, 4) : (!y || !aligned(y, 4))) return QMV_EINVAL_PTR;
+    if (x && !aligned(x, 4)) return QMV_EINVAL_PTR;
+    if ((rc = check_device())) return rc;
+    return launched(qmv::launch_qmv_q8k(type, static_cast<const uint8_t*>(w), N, K, x,
+                                        static_cast<uint8_t*>(xq), rows, y, P,
+                                        static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int qmv_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
+                   void* xq, float* y, void* stream) {
+    return q8k_common(type, w, N, K, x, B, QMV_MAX_BATCH, xq, y, nullptr, stream);
+}
+
+int qmm_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t M,
+                   void* xq, float* y, void* stream) {
+    return q8k_common(type, w, N, K, x, M, QMV_MAX_M, xq, y, nullptr, stream);
+}
+
+int qmv_partials_q8k_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
+                            int64_t M, int32_t* P, void* stream) {
+    if (!P) return QMV_EINVAL_PTR;
+    return q8k_common(type, w, N, K, nullptr, M, QMV_MAX_M, xq, nullptr, P, stream);
+}
+
 int qmv_launch_noalloc(int type, const void* w, int64_t N, int64_t K, const float* x,
                        int64_t B, float* y, void* stream) {
     int rc = check_weights(type, w, N, K);

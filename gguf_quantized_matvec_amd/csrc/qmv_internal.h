@@ -53,6 +53,32 @@ inline ActLayout act_layout(int64_t rows, int64_t K) {
     return L;
 }
 
+// Activation scratch for the K-quant x Q8_K path, rows of K elements
+// (K % 256 == 0):
+//   [0, pub)           Q8_K blocks, row-major: f32 d (LE), 32 x 8 int8
+//                      codes, 16 int16 sums of 16-code groups (292 bytes)
+//   then (256-aligned) the row-major staging that the kernels read:
+//     rcodes [rows][K] int8    codes in element order
+//     rda    [rows][K/32] f32  d of the element's superblock, per 32 codes
+//     rs16   [rows][K/32] i32  sums of the two 16-code halves of each 32
+//                              codes, as two int16 (low half = first)
+// (the layout of the lane-per-chunk GEMV's Q8_0 staging, so that kernel
+// stages either; rca is not used on this path and aliases rda).
+struct ActLayoutK {
+    int64_t nb, nsb, pub, rcodes, rda, rs16, total;
+};
+inline ActLayoutK act_layout_q8k(int64_t rows, int64_t K) {
+    ActLayoutK L;
+    L.nb = K / 32;
+    L.nsb = K / 256;
+    L.pub = rows * L.nsb * 292;
+    L.rcodes = (L.pub + 255) & ~int64_t(255);
+    L.rda = (L.rcodes + rows * K + 255) & ~int64_t(255);
+    L.rs16 = (L.rda + rows * L.nb * 4 + 255) & ~int64_t(255);
+    L.total = (L.rs16 + rows * L.nb * 4 + 255) & ~int64_t(255);
+    return L;
+}
+
 // One GEMV of a (possibly grouped) decode launch.
 struct GemvDesc {
     const uint8_t* w;
@@ -113,6 +139,15 @@ int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* x
                     int64_t rows, int32_t* P, hipStream_t s);
 int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                int64_t rows, float* y, hipStream_t s);
+// K-quant (Q4_K, Q6_K) x Q8_K path.  x given: quantise it into xq first
+// (x == NULL for launch_quantize_q8k: rebuild the staging from the Q8_K
+// blocks already in xq).  P != NULL: the exact superblock partials go to P.
+int launch_quantize_q8k(const float* x, uint8_t* xq, int64_t rows, int64_t K, hipStream_t s);
+int launch_qmv_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
+                   int64_t rows, float* y, int32_t* P, hipStream_t s);
+// The int8-MFMA GEMM of the Q8_K path (qmm8k_kernels.hip), any rows >= 1.
+int launch_gemm_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
+                    int64_t M, float* y, int32_t* P, hipStream_t s);
 // Device address of the current device's fixed activation scratch for
 // qmv_launch_noalloc (qmv_noalloc.hip), or NULL with *err set.
 uint8_t* noalloc_scratch(int* err);

@@ -1121,6 +1121,101 @@ __device__ __forceinline__ void dot_chunk(const uint32_t (&r)[DotFmt<FMT>::NWD],
     }
 }
 
+// The same chunk (one K-quant superblock c) against Q8_K activations: the
+// integer sub-block scales fold into one superblock partial (Q4_K: P and Q,
+// Q6_K: I), scaled once: p = fma((float)P, fl(d d_a), +0) [then
+// fma(-(float)Q, fl(dmin d_a), p)], d_a the activation superblock's f32
+// scale (staged per 32 codes; [8c] is the superblock's).  PART: store the
+// superblock partials instead, at po.row[m * po.mstride + c * per].
+template <int FMT, int B, bool PART = false>
+__device__ __forceinline__ void dot_chunk_q8k(const uint32_t (&r)[DotFmt<FMT>::NWD],
+                                              const ActRow (&A)[B], int c, float (&p)[B],
+                                              PartOut po = PartOut{}) {
+    if constexpr (FMT == T_Q4_K) {
+        const float d = half_bits_to_float(half_at<0>(r));
+        const float dmin = half_bits_to_float(half_at<2>(r));
+        int Pv[B], Qv[B];
+#pragma unroll
+        for (int m = 0; m < B; m++) Pv[m] = Qv[m] = 0;
+        static_for<8>([&](auto BB) {
+            constexpr int j = BB;
+            const int b = 8 * c + j;
+            int sc, mn;
+            if constexpr (j < 4) {
+                sc = (int)((dw_at<4 + (j & ~3)>(r) >> (8 * (j & 3))) & 63);
+                mn = (int)((dw_at<8>(r) >> (8 * j)) & 63);
+            } else {
+                const uint32_t s_hi = dw_at<12>(r) >> (8 * (j - 4));
+                const uint32_t s_lo = dw_at<4>(r) >> (8 * (j - 4));
+                const uint32_t s_mid = dw_at<8>(r) >> (8 * (j - 4));
+                sc = (int)((s_hi & 15) | (((s_lo >> 6) & 3) << 4));
+                mn = (int)(((s_hi >> 4) & 15) | (((s_mid >> 6) & 3) << 4));
+            }
+            uint32_t q[8];
+            static_for<8>([&](auto I) {
+                q[I] = (dw_at<16 + 32 * (j >> 1) + 4 * I>(r) >> (4 * (j & 1))) & 0x0F0F0F0Fu;
+            });
+#pragma unroll
+            for (int m = 0; m < B; m++) {
+                uint32_t a[8];
+                act_block(A[m], b, a);
+                int D = 0;
+#pragma unroll
+                for (int i = 0; i < 8; i++) D = dot4(q[i], a[i], D);
+                const int s16 = A[m].s16[b];
+                Pv[m] += sc * D;
+                Qv[m] += mn * ((int)(int16_t)(s16 & 0xFFFF) + (s16 >> 16));
+            }
+        });
+#pragma unroll
+        for (int m = 0; m < B; m++) {
+            if constexpr (PART) {
+                int32_t* o = po.row + m * po.mstride + (int64_t)c * 2;
+                o[0] = Pv[m];
+                o[1] = Qv[m];
+            }
+            const float da = A[m].da[8 * c];
+            const float t = fmaf((float)Pv[m], d * da, 0.0f);
+            p[m] = fmaf(-(float)Qv[m], dmin * da, t);
+        }
+    } else {  // Q6_K
+        const float d = half_bits_to_float(half_at<208>(r));
+        int Iv[B];
+#pragma unroll
+        for (int m = 0; m < B; m++) Iv[m] = 0;
+        static_for<8>([&](auto BB) {
+            constexpr int bb = BB, h = bb >> 2, kq = bb & 3;
+            const int b = 8 * c + bb;
+            const int s0 = sbyte_at<192 + 2 * bb>(r), s1 = sbyte_at<193 + 2 * bb>(r);
+            uint32_t q[8];
+            static_for<8>([&](auto I) {
+                const uint32_t ql = dw_at<64 * h + 32 * (kq & 1) + 4 * I>(r);
+                const uint32_t qh = dw_at<128 + 32 * h + 4 * I>(r);
+                q[I] = ((ql >> (4 * (kq >> 1))) & 0x0F0F0F0Fu) |
+                       (((qh >> (2 * kq)) & 0x03030303u) << 4);
+            });
+#pragma unroll
+            for (int m = 0; m < B; m++) {
+                uint32_t a[8];
+                act_block(A[m], b, a);
+                int D0 = 0, D1 = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) D0 = dot4(q[i], a[i], D0);
+#pragma unroll
+                for (int i = 4; i < 8; i++) D1 = dot4(q[i], a[i], D1);
+                const int s16 = A[m].s16[b];
+                const int S0 = (int)(int16_t)(s16 & 0xFFFF), S1 = s16 >> 16;
+                Iv[m] += s0 * (D0 - 32 * S0) + s1 * (D1 - 32 * S1);
+            }
+        });
+#pragma unroll
+        for (int m = 0; m < B; m++) {
+            if constexpr (PART) po.row[m * po.mstride + c] = Iv[m];
+            p[m] = fmaf((float)Iv[m], d * A[m].da[8 * c], 0.0f);
+        }
+    }
+}
+
 // One GEMV of a launch (a launch may carry several, of one format and one
 // row count B): weights, shape, output, and the activations: x to quantise
 // in the kernel (FUSED), or the staged quantisation in xq.
@@ -1180,7 +1275,9 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 // receiving the exact block partials instead (the test hook).
 constexpr int MODE_GROUP = 0, MODE_SINGLE = 1, MODE_PAIRED = 2, MODE_PARTIALS = 3;
 
-template <int FMT, int B, bool FUSED, int MODE>
+// Q8K: the activations are staged Q8_K (K-quant formats only, not FUSED):
+// each chunk is scaled once per superblock (dot_chunk_q8k).
+template <int FMT, int B, bool FUSED, int MODE, bool Q8K = false>
 __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     using F = Fmt<FMT>;
     constexpr int NWD = DotFmt<FMT>::NWD;
@@ -1411,16 +1508,24 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
             if (valid) {
                 constexpr int per = has_min_term<FMT>() ? 2 : 1;
                 realign_chunk<FMT>(row * R + (int64_t)c * F::CB, r);
-                const PartOut po{reinterpret_cast<int32_t*>(J.y) + row * nb * per,
-                                 N * nb * per};
-                dot_chunk<FMT, B, true>(r, A, c, nbc, p, po);
+                if constexpr (Q8K) {
+                    const PartOut po{reinterpret_cast<int32_t*>(J.y) + row * C * per, N * C * per};
+                    dot_chunk_q8k<FMT, B, true>(r, A, c, p, po);
+                } else {
+                    const PartOut po{reinterpret_cast<int32_t*>(J.y) + row * nb * per,
+                                     N * nb * per};
+                    dot_chunk<FMT, B, true>(r, A, c, nbc, p, po);
+                }
             }
             if (q + 1 < PR) issue(q + 1, r);
             continue;
         }
         if (valid) {
             realign_chunk<FMT>(row * R + (int64_t)c * F::CB, r);
-            dot_chunk<FMT, B>(r, A, c, nbc, p);
+            if constexpr (Q8K)
+                dot_chunk_q8k<FMT, B>(r, A, c, p);
+            else
+                dot_chunk<FMT, B>(r, A, c, nbc, p);
         } else {
 #pragma unroll
             for (int m = 0; m < B; m++) p[m] = 0.0f;
@@ -1515,13 +1620,13 @@ inline int raise_lds_limit(const void* kernel, std::atomic<int> (&state)[64]) {
     return 0;
 }
 
-template <int FMT, int B, bool FUSED, int MODE>
+template <int FMT, int B, bool FUSED, int MODE, bool Q8K = false>
 int launch_dot_kernel(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
     static std::atomic<int> lds_state[64];
-    const int arc = raise_lds_limit(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED, MODE>),
+    const int arc = raise_lds_limit(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED, MODE, Q8K>),
                                     lds_state);
     if (arc) return arc;
-    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, MODE>), dim3((unsigned)blocks, (unsigned)jobs.count),
+    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, MODE, Q8K>), dim3((unsigned)blocks, (unsigned)jobs.count),
                        dim3(64 * jobs.waves), shmem, s, jobs);
     return (int)hipGetLastError();
 }
@@ -1844,6 +1949,60 @@ int launch_qmm_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_
     const int rc = launch_rebuild(xq, M, K, ST_F16, s);
     if (rc) return rc;
     return launch_gemm(type, w, N, K, xq, M, nullptr, s, P);
+}
+
+namespace {
+template <int FMT, int MODE>
+int launch_dot_q8k_t(const DotJobs& jobs, int64_t rows, int64_t blocks, size_t shmem,
+                     hipStream_t s) {
+    switch (rows) {
+    case 1: return launch_dot_kernel<FMT, 1, false, MODE, true>(jobs, blocks, shmem, s);
+    case 2: return launch_dot_kernel<FMT, 2, false, MODE, true>(jobs, blocks, shmem, s);
+    case 3: return launch_dot_kernel<FMT, 3, false, MODE, true>(jobs, blocks, shmem, s);
+    default: return launch_dot_kernel<FMT, 4, false, MODE, true>(jobs, blocks, shmem, s);
+    }
+}
+}  // namespace
+
+int launch_qmv_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
+                   int64_t rows, float* y, int32_t* P, hipStream_t s) {
+    // x given: quantise it; the partials hook rebuilds the staging from the
+    // Q8_K blocks; otherwise xq is used as staged
+    if (x || P) {
+        const int rc = launch_quantize_q8k(x, xq, rows, K, s);
+        if (rc) return rc;
+    }
+    if (!use_dot(rows, K)) return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, s);
+    // the lane-per-chunk kernel on the staged Q8_K rows (same staging layout)
+    const ActLayoutK L = act_layout_q8k(rows, K);
+    DotJobs jobs{};
+    jobs.count = 1;
+    jobs.waves = 4;
+    DotJob& J = jobs.j[0];
+    J.w = w;
+    J.w2 = nullptr;
+    J.y = P ? reinterpret_cast<float*>(P) : y;
+    J.x = nullptr;
+    J.xq = xq;
+    J.N = N;
+    J.K = K;
+    J.wbytes = N * row_bytes(type, K);
+    J.rcodes = L.rcodes;
+    J.rda = L.rda;
+    J.rca = L.rda;  // not read on this path
+    J.rs16 = L.rs16;
+    int64_t blocks4 = dot_blocks(type, N, K, 4);
+    if (blocks4 > 256 && blocks4 <= 512) jobs.waves = 8;
+    const int64_t blocks = dot_blocks(type, N, K, jobs.waves);
+    const size_t shmem = dot_shmem((int)rows, K, jobs.waves);
+    if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
+    switch (type) {
+    case T_Q4_K: return P ? launch_dot_q8k_t<T_Q4_K, MODE_PARTIALS>(jobs, rows, blocks, shmem, s)
+                          : launch_dot_q8k_t<T_Q4_K, MODE_SINGLE>(jobs, rows, blocks, shmem, s);
+    case T_Q6_K: return P ? launch_dot_q8k_t<T_Q6_K, MODE_PARTIALS>(jobs, rows, blocks, shmem, s)
+                          : launch_dot_q8k_t<T_Q6_K, MODE_SINGLE>(jobs, rows, blocks, shmem, s);
+    }
+    return (int)hipErrorInvalidValue;
 }
 
 bool gateup_is_one_launch(int64_t rows, int64_t K) {

@@ -207,6 +207,56 @@ int qmv_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
 int qmm_partials_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                         int64_t M, int32_t* P, void* stream);
 
+/* ---- K-quant weights x Q8_K activations ----
+ * Q8_K is the 8-bit activation format of the K-quant family (listed with the
+ * tensor formats, "Models and formats"; its layout is not on the pages): one
+ * block per 256 elements, 292 bytes: f32 d (LE), 256 int8 codes, then 16
+ * int16 sums of each 16-code group (LE).  Quantised as Q8_0 is, over 256
+ * elements, with d kept in f32: amax, d = amax/127, codes =
+ * round-half-away(x * (1/d)) (0 when 1/d is not finite).  Against Q4_K and
+ * Q6_K weights (the only types these calls accept; others return
+ * QMV_EINVAL_TYPE; K % 256 == 0) a whole superblock reduces to integers
+ * (Q4_K: P = sum_j sc_j sum q*a and Q = sum_j m_j sum a; Q6_K:
+ * I = sum_j s_j sum (q-32)*a), scaled once per superblock in this f32 order:
+ *   p = fma((float)P, fl(d * d_a), +0), then for Q4_K
+ *   p = fma(-(float)Q, fl(dmin * d_a), p); y = ((+0 + p_0) + p_1) + ...
+ * over the superblocks in ascending order, fl() one f32 rounding of the
+ * product of the fp16 weight scale and the f32 activation scale, (float)P
+ * rounded to nearest even.  Every row of qmm_launch_q8k and of
+ * qmv_launch_q8k with B > 1 is bit-identical to qmv_launch_q8k with B = 1 on
+ * that row.  Results differ from the Q8_0 path (a different quantisation of
+ * x). */
+
+/* Bytes of activation scratch for `rows` rows of K elements on the Q8_K
+ * path: the Q8_K blocks (rows * K/256 * 292 bytes, row-major) first, then
+ * private staging.  Returns 0 for an invalid shape (K % 256 != 0 included). */
+size_t qmv_act_bytes_q8k(int64_t rows, int64_t K);
+
+/* Quantise x [rows][K] (f32, 4-byte aligned) to Q8_K into xq
+ * (qmv_act_bytes_q8k(rows, K) bytes, 16-byte aligned), or with x == NULL
+ * rebuild the private staging from Q8_K blocks already at the start of xq. */
+int quantize_act_q8_k(const float* x, void* xq, int64_t rows, int64_t K, void* stream);
+
+/* Decode GEMV on the Q8_K path: y[B][N] = x[B][K] * W^T, 1 <= B <= 16, W
+ * Q4_K or Q6_K.  x given: quantised into xq first; x NULL: xq holds a
+ * complete quantize_act_q8_k result for these B rows.  B <= 4 runs the
+ * lane-per-chunk kernel, B = 5..16 the int8-MFMA GEMM. */
+int qmv_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
+                   void* xq, float* y, void* stream);
+
+/* Prefill GEMM on the Q8_K path: y[M][N] = x[M][K] * W^T for any M >= 1
+ * (M <= 16 runs as qmv_launch_q8k).  The integer superblock partials run on
+ * the int8 matrix cores (v_mfma_i32_32x32x32_i8). */
+int qmm_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t M,
+                   void* xq, float* y, void* stream);
+
+/* Test hook: the exact int32 superblock partials of the kernel that
+ * qmv_launch_q8k / qmm_launch_q8k runs for M rows (1 <= M <= 2^24), from the
+ * Q8_K blocks in xq (the private staging is rebuilt from them first).  P
+ * layout: Q4_K [M][N][K/256][2] = (P, Q); Q6_K [M][N][K/256] = I. */
+int qmv_partials_q8k_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
+                            int64_t M, int32_t* P, void* stream);
+
 /* Decode GEMV for callers that cannot allocate device memory (code under
  * HIP graph capture, serving loops or harnesses that forbid hipMalloc): the
  * same multiply and result as qmv_launch(type, w, N, K, x, B, xq, y, stream)

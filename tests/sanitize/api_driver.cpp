@@ -56,6 +56,14 @@ int main() {
         gv[1].K = 1 << 17;
         CHECK(qmv_launch_group(QMV_Q8_0, 1, gv, 2, nullptr) == QMV_EINVAL_PTR);
     }
+    CHECK(qmv_launch_q8k(QMV_Q4_0, W, 16, 256, X, 1, XQ, Y, nullptr) == QMV_EINVAL_TYPE);
+    CHECK(qmv_launch_q8k(QMV_Q4_K, W, 16, 512 + 32, X, 1, XQ, Y, nullptr) == QMV_EINVAL_SHAPE);
+    CHECK(qmv_launch_q8k(QMV_Q6_K, W, 16, 256, X, 17, XQ, Y, nullptr) == QMV_EINVAL_SHAPE);
+    CHECK(qmm_launch_q8k(QMV_Q6_K, W, 16, 256, X, 0, XQ, Y, nullptr) == QMV_EINVAL_SHAPE);
+    CHECK(qmm_launch_q8k(QMV_Q6_K, W, 16, 256, X, 40, XQ + 4, Y, nullptr) == QMV_EINVAL_PTR);
+    CHECK(qmv_partials_q8k_launch(QMV_Q4_K, W, 16, 256, XQ, 3, nullptr, nullptr) == QMV_EINVAL_PTR);
+    CHECK(quantize_act_q8_k(X, XQ, 1, 128, nullptr) == QMV_EINVAL_SHAPE);
+    CHECK(qmv_act_bytes_q8k(1, 128) == 0 && qmv_act_bytes_q8k(0, 256) == 0);
     CHECK(g_last.calls == calls0);
 
     // accepted calls reach the launcher with the caller's arguments
@@ -81,6 +89,11 @@ int main() {
         CHECK(qmv_launch_group(QMV_Q8_0, 2, gv, 3, nullptr) == QMV_OK &&
               !strcmp(g_last.what, "group") && g_last.group_count == 3);
     }
+    CHECK(qmm_launch_q8k(QMV_Q4_K, W, 48, 4096, X, 2048, XQ, Y, nullptr) == QMV_OK &&
+          !strcmp(g_last.what, "qmv_q8k") && g_last.rows == 2048 && g_last.x == X);
+    CHECK(qmv_partials_q8k_launch(QMV_Q6_K, W, 48, 512, XQ, 7, (int32_t*)Y, nullptr) == QMV_OK &&
+          !strcmp(g_last.what, "partials_q8k") && g_last.x == nullptr);
+    CHECK(quantize_act_q8_k(X, XQ, 3, 512, nullptr) == QMV_OK && !strcmp(g_last.what, "quantize_q8k"));
     // sizes
     CHECK(qmv_act_bytes(1, 896) == 24576);
     CHECK(qmv_act_bytes(0, 32) == 0 && qmv_act_bytes(1, 48) == 0);

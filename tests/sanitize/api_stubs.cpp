@@ -81,4 +81,11 @@ int launch_gateup(int type, const uint8_t*, const uint8_t*, int64_t N, int64_t K
                   uint8_t* xq, int64_t rows, float* h, hipStream_t) {
     return record("gateup", type, N, K, rows, x, xq, h);
 }
+int launch_quantize_q8k(const float* x, uint8_t* xq, int64_t rows, int64_t K, hipStream_t) {
+    return record("quantize_q8k", 0, 0, K, rows, x, xq, nullptr);
+}
+int launch_qmv_q8k(int type, const uint8_t*, int64_t N, int64_t K, const float* x, uint8_t* xq,
+                   int64_t rows, float* y, int32_t* P, hipStream_t) {
+    return record(P ? "partials_q8k" : "qmv_q8k", type, N, K, rows, x, xq, P ? (void*)P : (void*)y);
+}
 }  // namespace qmv

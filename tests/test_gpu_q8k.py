@@ -1,0 +1,158 @@
+"""GPU parity of the K-quant x Q8_K path (Q4_K / Q6_K weights, activations
+quantised per 256 elements with an f32 scale) against the CPU oracle:
+
+* the Q8_K blocks of the quantiser: bit-exact (zero, tiny and normal blocks,
+  16- and 4-byte aligned x);
+* the superblock partials of every kernel path (the lane-per-chunk GEMV for
+  B <= 4, the int8-MFMA GEMM with 32- and 64-row tiles for more rows):
+  bit-exact, including superblock partials above 2^24;
+* y: bit-identical to the oracle's replay of the Q8_K f32 order and within
+  1e-4 * sum|w^ x^| of its f64 result; GEMM rows bit-identical to the
+  batch-1 GEMV; at the 8B-class sizes (M = 2048) on sampled tokens and rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from checks import assert_bitwise, assert_tol
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gguf_quantized_matvec_amd as g
+    g.lib()
+    return g
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def pubk(xq, rows, K):
+    return host(xq)[: rows * (K // 256) * 292]
+
+
+@pytest.mark.parametrize("rows,K", [(1, 256), (3, 1024), (16, 4096), (40, 512), (7, 14336)])
+def test_quantize_q8k_bit_exact(g, rows, K):
+    x = synth.activations(rows, K, 2000 + K) * np.float32(3.0)
+    x[0, :256] = 0.0                        # an all-zero block
+    if K >= 768:
+        x[-1, 256:512] *= np.float32(1e-40)  # 1/d not finite: zero codes
+        x[-1, 512:768] *= np.float32(1e-30)  # tiny but quantised normally
+    want = oracle.quantize_act_q8k(x)
+    print(f"quantize q8k rows={rows} K={K}", flush=True)
+    assert_bitwise(pubk(g.quantize_q8k(dev(x)), rows, K), want, "Q8_K blocks")
+    # only 4-byte aligned x
+    buf = torch.zeros(rows * K + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = dev(x).reshape(-1)
+    assert_bitwise(pubk(g.quantize_q8k(buf[1:].view(rows, K)), rows, K), want, "Q8_K, x unaligned")
+
+
+FMTS = [synth.Q4_K, synth.Q6_K]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", [(37, 256), (130, 1024), (300, 4096 + 256)])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 16, 33, 70])
+def test_partials_q8k_every_path(g, fmt, N, K, M):
+    blob, _ = synth.weights(fmt, N, K, 2100 + N + M, s_range=(-128, 127))
+    x = synth.activations(M, K, 2101 + K)
+    print(f"partials q8k fmt={fmt} N={N} K={K} M={M}", flush=True)
+    xq = g.quantize_q8k(dev(x))
+    P = host(g.partials_q8k(fmt, dev(blob), N, K, xq, M))
+    assert_bitwise(P, oracle.partials_q8k(fmt, blob, N, K, oracle.quantize_act_q8k(x), M),
+                   "q8k partials")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [1, 3, 40])
+def test_partials_q8k_above_2_24(g, fmt, M):
+    """Large scales, codes and activations: superblock partials beyond 2^24
+    (Q4_K's P up to 8*63*15*32*127), where (float)P rounds."""
+    N, K = 64, 1024
+    f = synth.draw_fields(fmt, N, K, 2200, s_range=(-128, 127))
+    if fmt == synth.Q4_K:
+        f["sc"] = np.maximum(f["sc"], 56)
+        f["q"] = np.maximum(f["q"], 12)
+    else:
+        f["s"] = np.where(np.abs(f["s"]) < 100, np.int8(-128), f["s"]).astype(np.int8)
+        f["q"] = np.minimum(f["q"], 3)
+    blob = synth.encode(f)
+    x = (np.abs(synth.activations(M, K, 2201)) * 0.2 + 4).astype(np.float32)
+    xq_o = oracle.quantize_act_q8k(x)
+    P_o = oracle.partials_q8k(fmt, blob, N, K, xq_o, M)
+    assert np.abs(P_o[..., 0] if fmt == synth.Q4_K else P_o).max() > 2 ** 24
+    print(f"q8k large partials fmt={fmt} M={M}", flush=True)
+    xd = dev(x)
+    P = host(g.partials_q8k(fmt, dev(blob), N, K, g.quantize_q8k(xd), M))
+    assert_bitwise(P, P_o, "q8k partials > 2^24")
+    y = host(g.matmul_q8k(fmt, dev(blob), N, K, x=xd))
+    assert_bitwise(y, oracle.matmul_q8k_canon_f32(fmt, blob, N, K, xq_o, M), "y, (float)P rounding")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K,M", [(45, 1024, 1), (96, 4352, 3), (33, 768, 4), (129, 1024, 7),
+                                   (250, 2048, 16), (130, 512, 65), (70, 4096, 200)])
+def test_q8k_against_oracle(g, fmt, N, K, M):
+    blob, _ = synth.weights(fmt, N, K, 2300 + N, s_range=(-128, 127))
+    x = synth.activations(M, K, 2301 + M)
+    print(f"q8k y fmt={fmt} N={N} K={K} M={M}", flush=True)
+    y = host(g.matmul_q8k(fmt, dev(blob), N, K, x=dev(x)))
+    xq = oracle.quantize_act_q8k(x)
+    y64, A = oracle.matmul_q8k_f64(fmt, blob, N, K, xq, M)
+    assert_tol(y, y64, A, what="q8k vs f64")
+    assert_bitwise(y, oracle.matmul_q8k_canon_f32(fmt, blob, N, K, xq, M), "q8k f32 order")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [5, 16, 64, 130])
+def test_q8k_rows_equal_batch1(g, fmt, M):
+    N, K = 200, 2048
+    blob, _ = synth.weights(fmt, N, K, 2400, s_range=(-128, 127))
+    x = synth.activations(M, K, 2401)
+    w = dev(blob)
+    y = host(g.matmul_q8k(fmt, w, N, K, x=dev(x)))
+    for t in sorted({0, 1, M // 2, M - 1}):
+        y1 = host(g.matmul_q8k(fmt, w, N, K, x=dev(x[t:t + 1])))
+        assert_bitwise(y[t:t + 1], y1, f"row {t} of M={M} vs batch 1")
+
+
+@pytest.mark.parametrize("fmt,N,K", [(synth.Q4_K, 14336, 4096), (synth.Q6_K, 4096, 14336),
+                                     (synth.Q4_K, 1024, 4096)])
+def test_q8k_gemm_8b_class_full_size(g, fmt, N, K):
+    """The 8B-class shapes at 2048 tokens, in the benchmark's launch
+    configuration: sampled tokens x rows against the oracle, sampled tokens'
+    full rows against the batch-1 GEMV."""
+    M = 2048
+    blob, _ = synth.weights(fmt, N, K, synth.seed_for(4, {4096: 0, 1024: 1, 14336: 2}[N]
+                                                      if fmt == synth.Q4_K else 3), dscale=0.02)
+    x = synth.activations(M, K, synth.act_seed_for(4, M))
+    w, xd = dev(blob), dev(x)
+    print(f"q8k full size fmt={fmt} N={N} K={K}", flush=True)
+    y = host(g.matmul_q8k(fmt, w, N, K, x=xd))
+    rng = np.random.Generator(np.random.PCG64(2500 + N))
+    toks = np.unique(np.concatenate([[0, 63, 64, M - 1], rng.choice(M, 8, replace=False)]))
+    rows = np.unique(np.concatenate([[0, 127, 128, N - 1], rng.choice(N, 200, replace=False)]))
+    R = synth.row_bytes(fmt, K)
+    sub = np.ascontiguousarray(blob.reshape(N, R)[rows]).reshape(-1)
+    xq = oracle.quantize_act_q8k(x[toks])
+    got = np.ascontiguousarray(y[toks][:, rows])
+    y64, A = oracle.matmul_q8k_f64(fmt, sub, len(rows), K, xq, len(toks))
+    assert_tol(got, y64, A, what="q8k full size")
+    assert_bitwise(got, oracle.matmul_q8k_canon_f32(fmt, sub, len(rows), K, xq, len(toks)),
+                   "q8k full size f32 order")
+    for t in toks[:4]:
+        y1 = host(g.matmul_q8k(fmt, w, N, K, x=dev(x[t:t + 1])))
+        assert_bitwise(y[t:t + 1], y1, f"token {t} vs batch-1 GEMV")
