@@ -111,14 +111,15 @@ __global__ __launch_bounds__(256) void k_quantize_q8k(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------- GEMM ----
+typedef __attribute__((address_space(3))) void lds_void;
+
 // 16 bytes at a 2-byte aligned address (Q6_K superblocks are 210 bytes):
-// five dwords from the 4-byte aligned address below it, shifted down.
-// The fifth dword is read only when p is not 4-byte aligned, so that no byte
-// past p + 16 is touched (the last field of the blob's last superblock).
+// the dwords from the 4-byte aligned address below it, shifted down.  The
+// fifth dword is read only when p is not 4-byte aligned, so that no byte past
+// p + 16 is touched (the last field of the blob's last superblock).
 __device__ __forceinline__ uint4 ld16_a2(const uint8_t* p) {
-    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
-    const uint32_t sh = (uint32_t)(a & 3);
+    const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(p) & 3);
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p - sh);
     uint32_t v[5];
     __builtin_memcpy(v, q, 16);
     v[4] = sh ? q[4] : 0u;
@@ -155,7 +156,9 @@ __device__ __forceinline__ void fetch_wk(const uint8_t* sbp, int h, WRawK<FMT>& 
 #pragma unroll
         for (int i = 0; i < 2; i++) r.qh[i] = ld16_a2(sbp + 128 + 32 * i + 16 * h);
         r.sc = ld16_a2(sbp + 192);
-        r.d = (uint32_t)sbp[208] | ((uint32_t)sbp[209] << 8);
+        uint16_t d16;
+        __builtin_memcpy(&d16, sbp + 208, 2);
+        r.d = d16;
     }
 }
 
@@ -175,9 +178,9 @@ __device__ __forceinline__ void q4k_sc_m(const uint4& hdr, int j, int& sc, int& 
     }
 }
 
-// Two int8 digits of 4 values v = f * c (c: 4 codes, one per byte, offset
-// already applied for Q6_K; f the sub-block's integer scale): v = 64 hi + lo,
-// lo in 0..63.  Computed in 16-bit lanes (|v| <= 8064).
+// Two int8 digits of 4 values v = f * c (c: 4 codes, one per byte, minus
+// `off`; f the sub-block's integer scale): v = 64 hi + lo, lo in 0..63.
+// Computed in 16-bit lanes (|v| <= 4096).
 __device__ __forceinline__ void digits4(uint32_t codes, int off, int f, uint32_t& lo, uint32_t& hi) {
     const s2 vo = {(short)off, (short)off}, vf = {(short)f, (short)f};
     const s2 a = __builtin_bit_cast(s2, codes & 0x00FF00FFu) - vo;          // codes 0, 2
@@ -222,21 +225,28 @@ __device__ __forceinline__ void decode_block(const WRawK<FMT>& r, int j, int h, 
     whi = (v4i){(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-constexpr int ROWB = 256 + 16;  // LDS bytes per staged activation row (16 of padding)
+// LDS of one superblock step: the activation tile (TM rows x 256 code bytes
+// as 16 pieces of 16 bytes; piece q of row r in slot 16 r + (q ^ (r & 15)),
+// so that the lanes of one ds_read_b128 pass hit different banks), the rows'
+// f32 scales and (Q4_K) their 32-code sums as pairs of int16.
+template <int TM> struct StageK {
+    uint4 a[TM * 16];
+    float d[TM];
+    int32_t s16[TM * 8];
+};
 
 // WM: 32-row MFMA tiles per wave along M (the workgroup's 32*WM activation
 // rows).  PART: write the exact superblock partials to P instead of y.
 template <int FMT, int WM, bool PART>
-__global__ __launch_bounds__(256, 2) void k_gemm8k(const uint8_t* __restrict__ w, int64_t N,
+__global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* __restrict__ w, int64_t N,
                                                    int64_t K, const uint8_t* __restrict__ xq,
                                                    ActLayoutK L, int64_t M, int64_t tilesM,
                                                    int64_t tilesN, float* __restrict__ y,
                                                    int32_t* __restrict__ P) {
     constexpr int TM = 32 * WM;
-    constexpr int NPC = TM * 16 / 256;  // 16-byte activation pieces per thread and superblock
-    __shared__ __attribute__((aligned(16))) uint8_t act[2][TM * ROWB];
-    __shared__ __attribute__((aligned(16))) float dal[2][TM];
-    __shared__ __attribute__((aligned(16))) int32_t s16l[2][TM * 8];
+    // the two stages are separate LDS objects, so that reads of one are not
+    // ordered behind the asynchronous copies into the other
+    __shared__ StageK<TM> st0, st1;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int lr = lane & 31, h = lane >> 5;
@@ -245,70 +255,55 @@ __global__ __launch_bounds__(256, 2) void k_gemm8k(const uint8_t* __restrict__ w
     // weight rows and activation rows through its L2
     int64_t tm, tn;
     {
-        const int64_t nt = tilesM * tilesN, per = (nt + 7) >> 3;
+        const int64_t nt = tilesM * tilesN, per = (nt + 7) >> 3, rem = nt & 7;
         const int64_t x8 = blockIdx.x & 7, k8 = blockIdx.x >> 3;
-        int64_t t = x8 * per + k8;
-        if (x8 >= (nt & 7) && (nt & 7)) {  // ranges of per-1 after the first nt%8 XCDs
-            t = (nt & 7) * per + (x8 - (nt & 7)) * (per - 1) + k8;
-        }
+        const int64_t t = (rem == 0 || x8 < rem) ? x8 * per + k8
+                                                 : rem * per + (x8 - rem) * (per - 1) + k8;
         tm = t % tilesM;
         tn = t / tilesM;
     }
     const int64_t m0 = tm * TM, n0 = tn * 128;
     const int nsb = (int)(K >> 8), nb = (int)(K >> 5);
-    const int64_t R = (int64_t)nsb * (FMT == T_Q4_K ? 144 : 210);
+    constexpr int SBB = FMT == T_Q4_K ? 144 : 210;
+    const int64_t R = (int64_t)nsb * SBB;
     const int64_t n = n0 + 32 * wv + lr;
     const uint8_t* wrow = w + (n < N ? n : N - 1) * R;
-    constexpr int SBB = FMT == T_Q4_K ? 144 : 210;
-
-    // activation staging: piece q = tid + 256 p is row q/16, bytes 16 (q%16)
-    const uint8_t* asrc[NPC];
-#pragma unroll
-    for (int p = 0; p < NPC; p++) {
-        const int q = tid + 256 * p, row = q >> 4;
-        const int64_t m = m0 + row < M ? m0 + row : M - 1;
-        asrc[p] = xq + L.rcodes + m * K + 16 * (q & 15);
-    }
-    const float* dsrc = reinterpret_cast<const float*>(xq + L.rda);
-    const int32_t* ssrc = reinterpret_cast<const int32_t*>(xq + L.rs16);
     auto arow = [&](int row) -> int64_t { return m0 + row < M ? m0 + row : M - 1; };
 
-    uint4 apre[NPC];
-    float dpre = 0.0f;
-    int32_t spre[2] = {0, 0};
-    auto load_act = [&](int s) {
+    // asynchronous global -> LDS copy of superblock s into stage `dst`: each
+    // wave instruction fills 64 consecutive 16-byte slots (4 tile rows); wave
+    // wv fills rows [TM/4 wv, TM/4 (wv+1)); lane l of instruction i: slot
+    // 16 r + u with r = TM/4 wv + 4i + l/16, u = l % 16, i.e. piece u ^ (r & 15)
+    constexpr int RPW = TM / 4;  // tile rows per wave
+    const uint8_t* asrc[RPW / 4];
 #pragma unroll
-        for (int p = 0; p < NPC; p++) apre[p] = *reinterpret_cast<const uint4*>(asrc[p] + 256 * s);
-        if (tid < TM) dpre = dsrc[arow(tid) * nb + 8 * s];
+    for (int i = 0; i < RPW / 4; i++) {
+        const int r = RPW * wv + 4 * i + (lane >> 4);
+        asrc[i] = xq + L.rcodes + arow(r) * K + 16 * ((lane & 15) ^ (r & 15));
+    }
+    const int drow = 64 * wv + lane;  // the row whose f32 scale this lane stages
+    const float* dsrc = reinterpret_cast<const float*>(xq + L.rda) + arow(drow < TM ? drow : 0) * nb;
+    const int32_t* ssrc = reinterpret_cast<const int32_t*>(xq + L.rs16) +
+                          arow((64 * wv + lane) >> 1 < TM ? (64 * wv + lane) >> 1 : 0) * nb +
+                          4 * (lane & 1);
+    // (the global operands are passed as plain void pointers: given as typed
+    // pointer arithmetic, the host pass of this compiler drops the kernel)
+    auto issue = [&](int s, StageK<TM>& dst) {
+#pragma unroll
+        for (int i = 0; i < RPW / 4; i++)
+            __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + 256 * s),
+                                             (lds_void*)&dst.a[16 * (RPW * wv + 4 * i)], 16, 0, 0);
+        if (drow < TM)  // the rows' f32 scales, one dword per lane (row 64 wv + lane)
+            __builtin_amdgcn_global_load_lds((const void*)(dsrc + 8 * s), (lds_void*)&dst.d[64 * wv],
+                                             4, 0, 0);
         if constexpr (FMT == T_Q4_K) {
-#pragma unroll
-            for (int p = 0; p < 2; p++) {
-                const int q = tid + 256 * p;  // TM * 8 words
-                if (q < TM * 8) spre[p] = ssrc[arow(q >> 3) * nb + 8 * s + (q & 7)];
-            }
+            // each row's 8 sums (32 bytes): two 16-byte pieces, global lanes
+            // 2r, 2r+1 (64 wv + lane); a wave's 64 pieces fill 256 ints
+            if (64 * wv < 2 * TM)
+                __builtin_amdgcn_global_load_lds((const void*)(ssrc + 8 * s),
+                                                 (lds_void*)&dst.s16[256 * wv], 16, 0, 0);
         }
     };
-    auto store_act = [&](int buf) {
-#pragma unroll
-        for (int p = 0; p < NPC; p++) {
-            const int q = tid + 256 * p;
-            *reinterpret_cast<uint4*>(&act[buf][(q >> 4) * ROWB + 16 * (q & 15)]) = apre[p];
-        }
-        if (tid < TM) dal[buf][tid] = dpre;
-        if constexpr (FMT == T_Q4_K) {
-#pragma unroll
-            for (int p = 0; p < 2; p++) {
-                const int q = tid + 256 * p;
-                if (q < TM * 8) s16l[buf][q] = spre[p];
-            }
-        }
-    };
-
-    WRawK<FMT> wcur, wnext;
-    load_act(0);
-    fetch_wk<FMT>(wrow, h, wcur);
-    store_act(0);
-    __syncthreads();
 
     float yacc[WM][16];
 #pragma unroll
@@ -317,10 +312,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm8k(const uint8_t* __restrict__ w
         for (int e = 0; e < 16; e++) yacc[t][e] = 0.0f;
     const v16i zero16 = {};
 
-    for (int s = 0; s < nsb; s++) {
-        const int buf = s & 1;
+    WRawK<FMT> wcur, wnext;
+    issue(0, st0);
+    fetch_wk<FMT>(wrow, h, wcur);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // one superblock on stage `cur` (the next one is copied into `nxt`)
+    auto step = [&](int s, StageK<TM>& cur, StageK<TM>& nxt) {
         if (s + 1 < nsb) {
-            load_act(s + 1);
+            issue(s + 1, nxt);
             fetch_wk<FMT>(wrow + (int64_t)(s + 1) * SBB, h, wnext);
         }
         v16i alo[WM], ahi[WM];
@@ -332,16 +333,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm8k(const uint8_t* __restrict__ w
             decode_block<FMT>(wcur, j, h, wlo, whi);
 #pragma unroll
             for (int t = 0; t < WM; t++) {
-                const uint4 av = *reinterpret_cast<const uint4*>(&act[buf][(32 * t + lr) * ROWB + 32 * j + 16 * h]);
-                const v4i a = (v4i){(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+                const int r = 32 * t + lr;
+                const v4i a = __builtin_bit_cast(v4i, cur.a[16 * r + ((2 * j + h) ^ (r & 15))]);
                 alo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, wlo, alo[t], 0, 0, 0);
                 ahi[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, whi, ahi[t], 0, 0, 0);
             }
         }
-        // Q4_K min term: S_j (activation row) against m_j (weight row) for
-        // j = 4h..4h+3 in bytes 0..3 of the lane's operands, the rest zero
-        v16i qlo[WM], qhi[WM];
+        float dw, dmw = 0.0f;
+        v4i bm = {0, 0, 0, 0};
         if constexpr (FMT == T_Q4_K) {
+            dw = half_bits_to_float(wcur.hdr.x & 0xFFFFu);
+            dmw = half_bits_to_float(wcur.hdr.x >> 16);
+            // Q4_K min term operands: m_j, j = 4h..4h+3, in bytes 0..3
             uint32_t mb = 0;
 #pragma unroll
             for (int t2 = 0; t2 < 4; t2++) {
@@ -349,69 +352,70 @@ __global__ __launch_bounds__(256, 2) void k_gemm8k(const uint8_t* __restrict__ w
                 q4k_sc_m(wcur.hdr, 4 * h + t2, sc, mn);
                 mb |= (uint32_t)mn << (8 * t2);
             }
-            const v4i bm = (v4i){(int)mb, 0, 0, 0};
+            bm = (v4i){(int)mb, 0, 0, 0};
+        } else {
+            dw = half_bits_to_float(wcur.d);
+        }
+        // per tile: lane l, element e = activation row 32t + 8(e/4) + 4h +
+        // e%4, weight row n (column lr)
 #pragma unroll
-            for (int t = 0; t < WM; t++) {
-                const int32_t* sp = &s16l[buf][(32 * t + lr) * 8 + 4 * h];
+        for (int t = 0; t < WM; t++) {
+            int Qv[16];
+            if constexpr (FMT == T_Q4_K) {
+                // the row's 32-code sums S_j (j = 4h..4h+3) as two int8 digits
+                // against m_j, in an otherwise-zero MFMA per digit
+                const int4 s4 = *reinterpret_cast<const int4*>(&cur.s16[(32 * t + lr) * 8 + 4 * h]);
+                const int sv[4] = {s4.x, s4.y, s4.z, s4.w};
                 uint32_t slo = 0, shi = 0;
 #pragma unroll
                 for (int t2 = 0; t2 < 4; t2++) {
-                    const int32_t v = sp[t2];
-                    const int S = (int)(int16_t)(v & 0xFFFF) + (v >> 16);  // -4064..4064
+                    const int S = (int)(int16_t)(sv[t2] & 0xFFFF) + (sv[t2] >> 16);  // |S| <= 4064
                     slo |= (uint32_t)(S & 63) << (8 * t2);
                     shi |= (uint32_t)((S >> 6) & 0xFF) << (8 * t2);
                 }
-                qlo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i){(int)slo, 0, 0, 0}, bm, zero16, 0, 0, 0);
-                qhi[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i){(int)shi, 0, 0, 0}, bm, zero16, 0, 0, 0);
-            }
-        }
-        // lane l, element e of tile t: activation row 32t + 8(e/4) + 4h + e%4,
-        // weight row n (column lr)
-        if constexpr (PART) {
-            constexpr int per = FMT == T_Q4_K ? 2 : 1;
+                const v16i ql = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i){(int)slo, 0, 0, 0}, bm, zero16, 0, 0, 0);
+                const v16i qh = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i){(int)shi, 0, 0, 0}, bm, zero16, 0, 0, 0);
 #pragma unroll
-            for (int t = 0; t < WM; t++)
+                for (int e = 0; e < 16; e++) Qv[e] = ql[e] + 64 * qh[e];
+            }
+            if constexpr (PART) {
+                constexpr int per = FMT == T_Q4_K ? 2 : 1;
 #pragma unroll
                 for (int e = 0; e < 16; e++) {
                     const int64_t m = m0 + 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
                     if (m < M && n < N) {
                         int32_t* o = P + ((m * N + n) * nsb + s) * per;
                         o[0] = alo[t][e] + 64 * ahi[t][e];
-                        if constexpr (per == 2) o[1] = qlo[t][e] + 64 * qhi[t][e];
+                        if constexpr (per == 2) o[1] = Qv[e];
                     }
                 }
-        } else {
-            float dw, dmw = 0.0f;
-            if constexpr (FMT == T_Q4_K) {
-                dw = half_bits_to_float(wcur.hdr.x & 0xFFFFu);
-                dmw = half_bits_to_float(wcur.hdr.x >> 16);
             } else {
-                dw = half_bits_to_float(wcur.d);
-            }
-#pragma unroll
-            for (int t = 0; t < WM; t++)
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
-                    const float4 d4 = *reinterpret_cast<const float4*>(&dal[buf][32 * t + 8 * g + 4 * h]);
+                    const float4 d4 = *reinterpret_cast<const float4*>(&cur.d[32 * t + 8 * g + 4 * h]);
                     const float da[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
                         const int e = 4 * g + i;
                         const int Pv = alo[t][e] + 64 * ahi[t][e];
                         float p = fmaf((float)Pv, dw * da[i], 0.0f);
-                        if constexpr (FMT == T_Q4_K) {
-                            const int Qv = qlo[t][e] + 64 * qhi[t][e];
-                            p = fmaf(-(float)Qv, dmw * da[i], p);
-                        }
+                        if constexpr (FMT == T_Q4_K) p = fmaf(-(float)Qv[e], dmw * da[i], p);
                         yacc[t][e] = yacc[t][e] + p;
                     }
                 }
+            }
+            // one tile's epilogue at a time: keeps the min-term MFMA results
+            // of the other tiles from being held live at once
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (s + 1 < nsb) {
-            store_act(buf ^ 1);
-            wcur = wnext;
-        }
+        if (s + 1 < nsb) wcur = wnext;
+        // this wave's copies into `nxt` are complete, then every wave's
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    for (int s = 0; s < nsb; s += 2) {
+        step(s, st0, st1);
+        if (s + 1 < nsb) step(s + 1, st1, st0);
     }
     if constexpr (PART) return;
 #pragma unroll
@@ -457,14 +461,20 @@ int launch_quantize_q8k(const float* x, uint8_t* xq, int64_t rows, int64_t K, hi
     return (int)hipGetLastError();
 }
 
+// Q6_K: 128 activation rows per workgroup (4 MFMA tiles per wave: each
+// decoded weight value feeds 4 MFMAs, one wave per SIMD) when that still
+// gives the chip a few rounds of workgroups; else 64 or 32.  Q4_K: at most
+// 64 (its min-term MFMAs do not fit the registers of 4 tiles).
 int launch_gemm_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
                     int64_t M, float* y, int32_t* P, hipStream_t s) {
-    const bool big = M > 32;
+    const int64_t tn = (N + 127) / 128;
+    const int wm = M <= 32 ? 1 : ((M + 127) / 128) * tn >= 512 ? 4 : 2;
     switch (type) {
-    case T_Q4_K: return big ? launch_gemm8k_t<T_Q4_K, 2>(w, N, K, xq, M, y, P, s)
-                            : launch_gemm8k_t<T_Q4_K, 1>(w, N, K, xq, M, y, P, s);
-    case T_Q6_K: return big ? launch_gemm8k_t<T_Q6_K, 2>(w, N, K, xq, M, y, P, s)
-                            : launch_gemm8k_t<T_Q6_K, 1>(w, N, K, xq, M, y, P, s);
+    case T_Q4_K: return wm >= 2 ? launch_gemm8k_t<T_Q4_K, 2>(w, N, K, xq, M, y, P, s)
+                                : launch_gemm8k_t<T_Q4_K, 1>(w, N, K, xq, M, y, P, s);
+    case T_Q6_K: return wm == 4 ? launch_gemm8k_t<T_Q6_K, 4>(w, N, K, xq, M, y, P, s)
+                      : wm == 2 ? launch_gemm8k_t<T_Q6_K, 2>(w, N, K, xq, M, y, P, s)
+                                : launch_gemm8k_t<T_Q6_K, 1>(w, N, K, xq, M, y, P, s);
     }
     return (int)hipErrorInvalidValue;
 }

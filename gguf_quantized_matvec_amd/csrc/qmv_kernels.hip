@@ -1972,37 +1972,48 @@ int launch_qmv_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const float
         const int rc = launch_quantize_q8k(x, xq, rows, K, s);
         if (rc) return rc;
     }
-    if (!use_dot(rows, K)) return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, s);
-    // the lane-per-chunk kernel on the staged Q8_K rows (same staging layout)
+    // decode batches run the lane-per-chunk kernel, in launches of up to 4
+    // activation rows (each reads the weights once); prefill the int8-MFMA GEMM
+    if (rows > 16 || !use_dot(rows < 4 ? rows : 4, K))
+        return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, s);
     const ActLayoutK L = act_layout_q8k(rows, K);
-    DotJobs jobs{};
-    jobs.count = 1;
-    jobs.waves = 4;
-    DotJob& J = jobs.j[0];
-    J.w = w;
-    J.w2 = nullptr;
-    J.y = P ? reinterpret_cast<float*>(P) : y;
-    J.x = nullptr;
-    J.xq = xq;
-    J.N = N;
-    J.K = K;
-    J.wbytes = N * row_bytes(type, K);
-    J.rcodes = L.rcodes;
-    J.rda = L.rda;
-    J.rca = L.rda;  // not read on this path
-    J.rs16 = L.rs16;
-    int64_t blocks4 = dot_blocks(type, N, K, 4);
-    if (blocks4 > 256 && blocks4 <= 512) jobs.waves = 8;
-    const int64_t blocks = dot_blocks(type, N, K, jobs.waves);
-    const size_t shmem = dot_shmem((int)rows, K, jobs.waves);
-    if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
-    switch (type) {
-    case T_Q4_K: return P ? launch_dot_q8k_t<T_Q4_K, MODE_PARTIALS>(jobs, rows, blocks, shmem, s)
-                          : launch_dot_q8k_t<T_Q4_K, MODE_SINGLE>(jobs, rows, blocks, shmem, s);
-    case T_Q6_K: return P ? launch_dot_q8k_t<T_Q6_K, MODE_PARTIALS>(jobs, rows, blocks, shmem, s)
-                          : launch_dot_q8k_t<T_Q6_K, MODE_SINGLE>(jobs, rows, blocks, shmem, s);
+    const int per = type == T_Q4_K ? 2 : 1;
+    for (int64_t r0 = 0; r0 < rows; r0 += 4) {
+        const int64_t rg = rows - r0 < 4 ? rows - r0 : 4;
+        DotJobs jobs{};
+        jobs.count = 1;
+        jobs.waves = 4;
+        DotJob& J = jobs.j[0];
+        J.w = w;
+        J.w2 = nullptr;
+        // rows r0.. of the output (or of the partials) and of the staging
+        J.y = P ? reinterpret_cast<float*>(P + r0 * N * (K / 256) * per) : y + r0 * N;
+        J.x = nullptr;
+        J.xq = xq;
+        J.N = N;
+        J.K = K;
+        J.wbytes = N * row_bytes(type, K);
+        J.rcodes = L.rcodes + r0 * K;
+        J.rda = L.rda + r0 * L.nb * 4;
+        J.rca = J.rda;  // not read on this path
+        J.rs16 = L.rs16 + r0 * L.nb * 4;
+        const int64_t blocks4 = dot_blocks(type, N, K, 4);
+        if (blocks4 > 256 && blocks4 <= 512) jobs.waves = 8;
+        const int64_t blocks = dot_blocks(type, N, K, jobs.waves);
+        const size_t shmem = dot_shmem((int)rg, K, jobs.waves);
+        if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
+        int rc = (int)hipErrorInvalidValue;
+        switch (type) {
+        case T_Q4_K: rc = P ? launch_dot_q8k_t<T_Q4_K, MODE_PARTIALS>(jobs, rg, blocks, shmem, s)
+                            : launch_dot_q8k_t<T_Q4_K, MODE_SINGLE>(jobs, rg, blocks, shmem, s);
+            break;
+        case T_Q6_K: rc = P ? launch_dot_q8k_t<T_Q6_K, MODE_PARTIALS>(jobs, rg, blocks, shmem, s)
+                            : launch_dot_q8k_t<T_Q6_K, MODE_SINGLE>(jobs, rg, blocks, shmem, s);
+            break;
+        }
+        if (rc) return rc;
     }
-    return (int)hipErrorInvalidValue;
+    return 0;
 }
 
 bool gateup_is_one_launch(int64_t rows, int64_t K) {
