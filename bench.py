@@ -21,7 +21,8 @@ of the step / wall-clock time of the timed steps.
 The same JSON line also carries: the roofline of the step's dominant kernel
 (HIP-event time per launch on the stream it runs on), the layer step at batch
 16, the prefill GEMMs of the four shapes at 2048 tokens (int8-equivalent
-TOPS), the LM-head GEMV (Q6_K 151936x1024) at batch 1/4/16, the pages' own
+TOPS; Q8_0 activations on f16 MFMA, and Q8_K activations on int8 MFMA), the
+four matrices as Q8_K-path GEMVs at batch 1 and 16, the LM-head GEMV (Q6_K 151936x1024) at batch 1/4/16, the pages' own
 Qwen2.5-0.5B shapes (Q8_0 896x896, the Q4_0 SwiGLU FFN at batch 1, the Q4_0
 prefill at 512 tokens), the measured ceilings of the chip (a streaming read,
 int8 and f16 MFMA loops, the GEMM's f32 epilogue alone) and the CPU oracle
@@ -257,19 +258,23 @@ def time_layer(torch, g, synth, B, steps, warmup, rotate_bytes):
 
 # ------------------------------------------------------- per-matrix rows --
 
-def matrix_us(torch, g, synth, fmt, N, K, rows, seed, ds, rotate_bytes, n_min=20):
+def matrix_us(torch, g, synth, fmt, N, K, rows, seed, ds, rotate_bytes, n_min=20, q8k=False):
     """Time per launch of qmv_launch (rows <= 16) or qmm_launch on one
-    seeded matrix, activations staged in xq, weights rotated."""
+    seeded matrix, activations staged in xq, weights rotated; q8k: the same
+    on the Q8_K path (qmv_launch_q8k / qmm_launch_q8k)."""
     blob = weights(synth, fmt, N, K, seed, ds)
     wt = torch.from_numpy(blob).cuda()
     nbytes = int(wt.numel())
     R = max(1, math.ceil(rotate_bytes / nbytes))
     copies = [wt] + [wt.clone() for _ in range(R - 1)]
     x = torch.from_numpy(synth.activations(rows, K, seed + 1)).cuda()
-    xq = g.quantize(x)
+    xq = g.quantize_q8k(x) if q8k else g.quantize(x)
     y = torch.empty(rows, N, dtype=torch.float32, device="cuda")
     L = g.lib()
-    fn = L.qmv_launch if rows <= 16 else L.qmm_launch
+    if q8k:
+        fn = L.qmv_launch_q8k if rows <= 16 else L.qmm_launch_q8k
+    else:
+        fn = L.qmv_launch if rows <= 16 else L.qmm_launch
 
     def launch(i):
         _check(g, fn(fmt, copies[i % R].data_ptr(), N, K, None, rows, xq.data_ptr(),
@@ -293,13 +298,17 @@ def gemm_row(us, M, N, K):
     return {"us": round(us, 2), "TOPS": round(tops, 1), "frac": round(tops / INT8_PEAK_TOPS, 4)}
 
 
-def prefill_8b(torch, g, synth, M=2048):
-    """GEMMs of the four 8B-class shapes at M tokens, and the layer's seven."""
-    shapes = [("q,o", Q4_K, 4096, 4096, 2), ("k,v", Q4_K, 1024, 4096, 2),
-              ("gate,up", Q4_K, 14336, 4096, 2), ("down", Q6_K, 4096, 14336, 1)]
+SHAPES_8B = [("q,o", Q4_K, 4096, 4096, 2), ("k,v", Q4_K, 1024, 4096, 2),
+             ("gate,up", Q4_K, 14336, 4096, 2), ("down", Q6_K, 4096, 14336, 1)]
+
+
+def prefill_8b(torch, g, synth, M=2048, q8k=False):
+    """GEMMs of the four 8B-class shapes at M tokens, and the layer's seven
+    (Q8_0 activations: f16 MFMA; Q8_K: int8 MFMA)."""
     out, tot_ops, tot_us = {}, 0.0, 0.0
-    for i, (name, fmt, N, K, cnt) in enumerate(shapes):
-        us, _, _ = matrix_us(torch, g, synth, fmt, N, K, M, synth.seed_for(4, i), 0.02, 512 << 20)
+    for i, (name, fmt, N, K, cnt) in enumerate(SHAPES_8B):
+        us, _, _ = matrix_us(torch, g, synth, fmt, N, K, M, synth.seed_for(4, i), 0.02, 512 << 20,
+                             q8k=q8k)
         out[f"{name} {N}x{K}"] = gemm_row(us, M, N, K)
         tot_ops += cnt * 2.0 * M * N * K
         tot_us += cnt * us
@@ -307,6 +316,18 @@ def prefill_8b(torch, g, synth, M=2048):
     out["layer (7 GEMMs)"] = {"us": round(tot_us, 1), "TOPS": round(tops, 1),
                               "frac": round(tops / INT8_PEAK_TOPS, 4)}
     return out
+
+
+def decode_8b_q8k(torch, g, synth):
+    """The four 8B-class matrices as single GEMVs on the Q8_K path, batch 1 and
+    16, activations staged, weights rotated over >= 1 GiB."""
+    res = {}
+    for B in (1, 16):
+        for i, (name, fmt, N, K, _) in enumerate(SHAPES_8B):
+            us, nb, _ = matrix_us(torch, g, synth, fmt, N, K, B, synth.seed_for(4, i), 0.02, 1 << 30,
+                                  q8k=True)
+            res[f"B{B} {name} {N}x{K}"] = gemv_row(us, nb, B)
+    return res
 
 
 def lm_head(torch, g, synth):
@@ -534,18 +555,24 @@ def profile_stage(torch, g, synth, name, launches=20):
 
 def profile_matrix(torch, g, synth, spec, launches=20):
     """Launch one workload matrix (the suite's seeded weights, activations
-    staged by quantize_act_q8_0) `launches` times back to back, eagerly."""
-    wl, mi, rows = spec.split(":")
+    staged) `launches` times back to back, eagerly.  spec WORKLOAD:INDEX:ROWS
+    (Q8_0 activations) or WORKLOAD:INDEX:ROWS:q8k (the Q8_K path)."""
+    parts = spec.split(":")
+    wl, mi, rows = parts[:3]
+    q8k = parts[3:] == ["q8k"]
     mi, rows = int(mi), int(rows)
     ci = list(synth.WORKLOADS).index(wl)
     fmt, N, K, ds = synth.WORKLOADS[wl]["mats"][mi]
     blob, _ = synth.weights(fmt, N, K, synth.seed_for(ci, mi), dscale=ds)
     w = torch.from_numpy(blob).cuda()
     x = torch.from_numpy(synth.activations(rows, K, synth.act_seed_for(ci, rows))).cuda()
-    xq = g.quantize(x)
+    xq = g.quantize_q8k(x) if q8k else g.quantize(x)
     y = torch.empty(rows, N, dtype=torch.float32, device="cuda")
     L = g.lib()
-    fn = L.qmv_launch if rows <= 16 else L.qmm_launch
+    if q8k:
+        fn = L.qmv_launch_q8k if rows <= 16 else L.qmm_launch_q8k
+    else:
+        fn = L.qmv_launch if rows <= 16 else L.qmm_launch
     for _ in range(launches):
         _check(g, fn(fmt, w.data_ptr(), N, K, None, rows, xq.data_ptr(), y.data_ptr(),
                      torch.cuda.current_stream().cuda_stream), "profile_matrix")
@@ -756,6 +783,11 @@ def main():
         print("step: prefill M=2048", file=sys.stderr, flush=True)
         out["prefill_m2048"] = {"unit": "int8-equivalent TOPS", "peak": INT8_PEAK_TOPS,
                                 **prefill_8b(torch, g, synth)}
+        print("step: prefill M=2048, Q8_K activations", file=sys.stderr, flush=True)
+        out["prefill_m2048_q8k"] = {"unit": "int8-equivalent TOPS", "peak": INT8_PEAK_TOPS,
+                                    **prefill_8b(torch, g, synth, q8k=True)}
+        print("step: decode GEMVs, Q8_K activations", file=sys.stderr, flush=True)
+        out["decode_8b_q8k"] = decode_8b_q8k(torch, g, synth)
         print("step: lm head", file=sys.stderr, flush=True)
         out["lm_head_q6_k_151936x1024"] = lm_head(torch, g, synth)
         print("step: qwen shapes", file=sys.stderr, flush=True)

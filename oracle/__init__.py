@@ -57,11 +57,15 @@ def lib():
         L.oracle_partials_q8k.argtypes = [I, P, I64, I64, P, I64, P]
         L.oracle_matmul_q8k_f64.argtypes = [I, P, I64, I64, P, I64, P, P]
         L.oracle_matmul_q8k_canon_f32.argtypes = [I, P, I64, I64, P, I64, P]
+        L.oracle_prepared_bytes.argtypes = [I, I64, I64]
+        L.oracle_prepared_bytes.restype = I64
+        L.oracle_prepare_q8k.argtypes = [I, P, I64, I64, P]
         for name in ("oracle_quantize_act", "oracle_unpack", "oracle_dequant",
                      "oracle_dequant_act", "oracle_partials", "oracle_matmul_f64",
                      "oracle_dense_f64", "oracle_matmul_canon_f32", "oracle_swiglu",
                      "oracle_quantize_act_q8k", "oracle_dequant_act_q8k", "oracle_partials_q8k",
-                     "oracle_matmul_q8k_f64", "oracle_matmul_q8k_canon_f32"):
+                     "oracle_matmul_q8k_f64", "oracle_matmul_q8k_canon_f32",
+                     "oracle_prepare_q8k"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -220,3 +224,18 @@ def matmul_q8k_canon_f32(fmt: int, blob, N: int, K: int, xq, B: int) -> np.ndarr
     _ok(lib().oracle_matmul_q8k_canon_f32(fmt, _p(blob), N, K, _p(xq), B, _p(y)),
         "matmul_q8k_canon_f32")
     return y.reshape(B, N)
+
+
+def prepared_bytes(fmt: int, N: int, K: int) -> int:
+    return int(lib().oracle_prepared_bytes(fmt, N, K))
+
+
+def prepare_q8k(fmt: int, blob, N: int, K: int) -> np.ndarray:
+    """The load-time repack of a Q4_K / Q6_K blob (uint8 [prepared_bytes])."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    n = prepared_bytes(fmt, N, K)
+    if n < 0:
+        raise ValueError(f"oracle prepare: type {fmt} N={N} K={K} refused ({n})")
+    out = np.zeros(n, np.uint8)
+    _ok(lib().oracle_prepare_q8k(fmt, _p(blob), N, K, _p(out)), "prepare_q8k")
+    return out

@@ -649,3 +649,76 @@ int oracle_matmul_q8k_canon_f32(int type, const uint8_t* w, int64_t N, int64_t K
     row_free(&r);
     return 0;
 }
+
+/* ------------------------------------------ load-time repack (Q8_K path) -- */
+/*
+ * The pages' own benchmark runs with the weights repacked when the file is
+ * loaded ("Architecture", bench transcript header: repack on) and do not say
+ * into what.  The repack here serves the prefill multiply against Q8_K
+ * activations: each element's integer weight factor wint (Q4_K: sc_j * q;
+ * Q6_K: s_j * (q - 32)) stored as two int8 digits, wint = 64 * hi + lo with
+ * lo = wint mod 64 in 0..63, so that one superblock's integer partial is
+ * 64 * sum(hi * a) + sum(lo * a), sums of int8 products.  Layout, for N rows
+ * in tiles of 32 (row n in tile n / 32, position r = n % 32) and superblocks
+ * s = 0..K/256-1: region (t * (K/256) + s) of 16896 bytes holds
+ *   bytes 1024 * (2j + g) + 16 * (32 h + r) + i, for element e = 32 j + 16 h + i
+ *     of superblock s: digit g (0: lo, 1: hi, as int8) of row n's element e;
+ *   bytes 16384 + 16 r .. + 15: row n's f32 d (the fp16 d, widened), f32
+ *     dmin (Q4_K; 0 for Q6_K), then the eight 6-bit mins m_0..m_7 (Q4_K; 0
+ *     for Q6_K), all little-endian;
+ * rows n >= N of the last tile are all zero.
+ */
+enum { PREP_REGION = 16896, PREP_REC = 16384 };
+
+int64_t oracle_prepared_bytes(int type, int64_t N, int64_t K) {
+    int qk, nbytes;
+    if (type != T_Q4_K && type != T_Q6_K) return -1;
+    if (check(type, N, K, &qk, &nbytes)) return -2;
+    return (N + 31) / 32 * (K / 256) * PREP_REGION;
+}
+
+static void wr32(uint8_t* p, uint32_t v) {
+    for (int i = 0; i < 4; i++) p[i] = (uint8_t)(v >> (8 * i));
+}
+
+int oracle_prepare_q8k(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* out) {
+    int64_t bytes = oracle_prepared_bytes(type, N, K);
+    if (bytes < 0) return (int)bytes;
+    memset(out, 0, (size_t)bytes);
+    int qk, nbytes;
+    check(type, N, K, &qk, &nbytes);
+    int64_t nsb = K / 256;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t s = 0; s < nsb; s++) {
+            const uint8_t* blk = w + (n * nsb + s) * nbytes;
+            uint8_t* reg = out + ((n / 32) * nsb + s) * PREP_REGION;
+            int r = (int)(n % 32);
+            for (int e = 0; e < 256; e++) {
+                int q, sc, mn;
+                int64_t wint, mint;
+                decode_elem(type, blk, e, &q, &sc, &mn);
+                elem_ints(type, q, sc, mn, &wint, &mint);
+                int64_t lo = ((wint % 64) + 64) % 64;
+                int64_t hi = (wint - lo) / 64;
+                int j = e / 32, h = (e % 32) / 16, i = e % 16;
+                reg[1024 * (2 * j) + 16 * (32 * h + r) + i] = (uint8_t)lo;
+                reg[1024 * (2 * j + 1) + 16 * (32 * h + r) + i] = (uint8_t)(int8_t)hi;
+            }
+            double d, dmin;
+            block_scales(type, blk, &d, &dmin);
+            float fd = (float)d, fdmin = (float)dmin;
+            uint32_t ud, udmin;
+            memcpy(&ud, &fd, 4);
+            memcpy(&udmin, &fdmin, 4);
+            uint8_t* rec = reg + PREP_REC + 16 * r;
+            wr32(rec, ud);
+            wr32(rec + 4, udmin);
+            if (type == T_Q4_K)
+                for (int j = 0; j < 8; j++) {
+                    int sc, mn;
+                    q4k_scale_min(blk + 4, j, &sc, &mn);
+                    rec[8 + j] = (uint8_t)mn;
+                }
+        }
+    return 0;
+}

@@ -107,6 +107,15 @@ int oracle_matmul_q8k_f64(int type, const uint8_t* w, int64_t N, int64_t K,
 int oracle_matmul_q8k_canon_f32(int type, const uint8_t* w, int64_t N, int64_t K,
                                 const uint8_t* xq, int64_t B, float* y);
 
+/* ---- Load-time repack of Q4_K / Q6_K weights for the Q8_K path ----
+ * Each element's integer weight factor as two int8 digits (wint = 64 hi + lo,
+ * lo in 0..63) in 32-row tiles, one 16896-byte region per (tile, superblock):
+ * digit g of row 32t + r, element 32j + 16h + i at byte 1024(2j + g) +
+ * 16(32h + r) + i; at 16384 + 16r the row's f32 d, f32 dmin and (Q4_K) its
+ * eight 6-bit mins; rows past N zero.  Other types: -1. */
+int64_t oracle_prepared_bytes(int type, int64_t N, int64_t K);
+int oracle_prepare_q8k(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -156,3 +156,29 @@ def test_q8k_gemm_8b_class_full_size(g, fmt, N, K):
     for t in toks[:4]:
         y1 = host(g.matmul_q8k(fmt, w, N, K, x=dev(x[t:t + 1])))
         assert_bitwise(y[t:t + 1], y1, f"token {t} vs batch-1 GEMV")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_q8k_gemm_wide_grid_ragged(g, fmt):
+    """A grid of more than 512 tiles of 128 x 128 with ragged M and N (130 tokens,
+    32805 rows): the launch shape with 128 activation rows per workgroup, on
+    sampled rows against the oracle and on sampled tokens against batch 1."""
+    N, K, M = 32805, 512, 130
+    blob, _ = synth.weights(fmt, N, K, 2600 + fmt, s_range=(-128, 127))
+    x = synth.activations(M, K, 2601)
+    w, xd = dev(blob), dev(x)
+    print(f"q8k wide ragged fmt={fmt}", flush=True)
+    y = host(g.matmul_q8k(fmt, w, N, K, x=xd))
+    rng = np.random.Generator(np.random.PCG64(2602))
+    rows = np.unique(np.concatenate([[0, 127, 128, N - 38, N - 1], rng.choice(N, 300, replace=False)]))
+    R = synth.row_bytes(fmt, K)
+    sub = np.ascontiguousarray(blob.reshape(N, R)[rows]).reshape(-1)
+    xq = oracle.quantize_act_q8k(x)
+    assert_bitwise(np.ascontiguousarray(y[:, rows]),
+                   oracle.matmul_q8k_canon_f32(fmt, sub, len(rows), K, xq, M), "wide grid f32 order")
+    for t in (0, 127, 128, 129):
+        y1 = host(g.matmul_q8k(fmt, w, N, K, x=dev(x[t:t + 1])))
+        assert_bitwise(y[t:t + 1], y1, f"token {t} vs batch 1")
+    P = host(g.partials_q8k(fmt, w, N, K, g.quantize_q8k(xd), M))
+    assert_bitwise(np.ascontiguousarray(P[:, rows]),
+                   oracle.partials_q8k(fmt, sub, len(rows), K, xq, M), "wide grid partials")
