@@ -258,20 +258,27 @@ def time_layer(torch, g, synth, B, steps, warmup, rotate_bytes):
 
 # ------------------------------------------------------- per-matrix rows --
 
-def matrix_us(torch, g, synth, fmt, N, K, rows, seed, ds, rotate_bytes, n_min=20, q8k=False):
+def matrix_us(torch, g, synth, fmt, N, K, rows, seed, ds, rotate_bytes, n_min=20, q8k=False,
+              prepared=False):
     """Time per launch of qmv_launch (rows <= 16) or qmm_launch on one
     seeded matrix, activations staged in xq, weights rotated; q8k: the same
-    on the Q8_K path (qmv_launch_q8k / qmm_launch_q8k)."""
+    on the Q8_K path (qmv_launch_q8k / qmm_launch_q8k); prepared: the Q8_K
+    GEMM on weights repacked by qmv_prepare beforehand (untimed, as at load).
+    Returns (us, GGUF weight bytes, copies)."""
     blob = weights(synth, fmt, N, K, seed, ds)
     wt = torch.from_numpy(blob).cuda()
     nbytes = int(wt.numel())
-    R = max(1, math.ceil(rotate_bytes / nbytes))
+    if prepared:
+        wt = g.prepare(fmt, wt, N, K)
+    R = max(1, math.ceil(rotate_bytes / int(wt.numel())))
     copies = [wt] + [wt.clone() for _ in range(R - 1)]
     x = torch.from_numpy(synth.activations(rows, K, seed + 1)).cuda()
-    xq = g.quantize_q8k(x) if q8k else g.quantize(x)
+    xq = g.quantize_q8k(x) if (q8k or prepared) else g.quantize(x)
     y = torch.empty(rows, N, dtype=torch.float32, device="cuda")
     L = g.lib()
-    if q8k:
+    if prepared:
+        fn = L.qmm_launch_q8k_prepared
+    elif q8k:
         fn = L.qmv_launch_q8k if rows <= 16 else L.qmm_launch_q8k
     else:
         fn = L.qmv_launch if rows <= 16 else L.qmm_launch
@@ -302,13 +309,14 @@ SHAPES_8B = [("q,o", Q4_K, 4096, 4096, 2), ("k,v", Q4_K, 1024, 4096, 2),
              ("gate,up", Q4_K, 14336, 4096, 2), ("down", Q6_K, 4096, 14336, 1)]
 
 
-def prefill_8b(torch, g, synth, M=2048, q8k=False):
+def prefill_8b(torch, g, synth, M=2048, q8k=False, prepared=False):
     """GEMMs of the four 8B-class shapes at M tokens, and the layer's seven
-    (Q8_0 activations: f16 MFMA; Q8_K: int8 MFMA)."""
+    (Q8_0 activations: f16 MFMA; Q8_K: int8 MFMA, on the GGUF blob or on the
+    load-time repacked weights)."""
     out, tot_ops, tot_us = {}, 0.0, 0.0
     for i, (name, fmt, N, K, cnt) in enumerate(SHAPES_8B):
         us, _, _ = matrix_us(torch, g, synth, fmt, N, K, M, synth.seed_for(4, i), 0.02, 512 << 20,
-                             q8k=q8k)
+                             q8k=q8k, prepared=prepared)
         out[f"{name} {N}x{K}"] = gemm_row(us, M, N, K)
         tot_ops += cnt * 2.0 * M * N * K
         tot_us += cnt * us
@@ -556,20 +564,26 @@ def profile_stage(torch, g, synth, name, launches=20):
 def profile_matrix(torch, g, synth, spec, launches=20):
     """Launch one workload matrix (the suite's seeded weights, activations
     staged) `launches` times back to back, eagerly.  spec WORKLOAD:INDEX:ROWS
-    (Q8_0 activations) or WORKLOAD:INDEX:ROWS:q8k (the Q8_K path)."""
+    (Q8_0 activations), WORKLOAD:INDEX:ROWS:q8k (the Q8_K path) or
+    WORKLOAD:INDEX:ROWS:q8kp (the Q8_K GEMM on repacked weights)."""
     parts = spec.split(":")
     wl, mi, rows = parts[:3]
-    q8k = parts[3:] == ["q8k"]
+    q8k = parts[3:] in (["q8k"], ["q8kp"])
+    prepared = parts[3:] == ["q8kp"]
     mi, rows = int(mi), int(rows)
     ci = list(synth.WORKLOADS).index(wl)
     fmt, N, K, ds = synth.WORKLOADS[wl]["mats"][mi]
     blob, _ = synth.weights(fmt, N, K, synth.seed_for(ci, mi), dscale=ds)
     w = torch.from_numpy(blob).cuda()
+    if prepared:
+        w = g.prepare(fmt, w, N, K)
     x = torch.from_numpy(synth.activations(rows, K, synth.act_seed_for(ci, rows))).cuda()
     xq = g.quantize_q8k(x) if q8k else g.quantize(x)
     y = torch.empty(rows, N, dtype=torch.float32, device="cuda")
     L = g.lib()
-    if q8k:
+    if prepared:
+        fn = L.qmm_launch_q8k_prepared
+    elif q8k:
         fn = L.qmv_launch_q8k if rows <= 16 else L.qmm_launch_q8k
     else:
         fn = L.qmv_launch if rows <= 16 else L.qmm_launch
@@ -786,6 +800,12 @@ def main():
         print("step: prefill M=2048, Q8_K activations", file=sys.stderr, flush=True)
         out["prefill_m2048_q8k"] = {"unit": "int8-equivalent TOPS", "peak": INT8_PEAK_TOPS,
                                     **prefill_8b(torch, g, synth, q8k=True)}
+        print("step: prefill M=2048, Q8_K activations, repacked weights", file=sys.stderr,
+              flush=True)
+        out["prefill_m2048_q8k_repacked"] = {
+            "unit": "int8-equivalent TOPS", "peak": INT8_PEAK_TOPS,
+            "repack": "qmv_prepare at load (untimed): int8 digit pairs, 3.7x Q4_K / 2.5x Q6_K bytes",
+            **prefill_8b(torch, g, synth, q8k=True, prepared=True)}
         print("step: decode GEMVs, Q8_K activations", file=sys.stderr, flush=True)
         out["decode_8b_q8k"] = decode_8b_q8k(torch, g, synth)
         print("step: lm head", file=sys.stderr, flush=True)

@@ -22,7 +22,8 @@ BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_1: (32, 20), Q5_1: (
 EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
            "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc", "qmv_gateup_act_bytes",
            "qmv_launch_gateup_swiglu", "qmv_act_bytes_q8k", "quantize_act_q8_k", "qmv_launch_q8k",
-           "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_strerror")
+           "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepared_bytes", "qmv_prepare",
+           "qmm_launch_q8k_prepared", "qmm_partials_q8k_prepared_launch", "qmv_strerror")
 MAX_BATCH = 16
 MAX_GROUP = 8
 
@@ -65,13 +66,19 @@ def lib() -> ctypes.CDLL:
         L.qmv_launch_q8k.argtypes = [I, P, I64, I64, P, I64, P, P, P]
         L.qmm_launch_q8k.argtypes = [I, P, I64, I64, P, I64, P, P, P]
         L.qmv_partials_q8k_launch.argtypes = [I, P, I64, I64, P, I64, P, P]
+        L.qmv_prepared_bytes.argtypes = [I, I64, I64]
+        L.qmv_prepared_bytes.restype = ctypes.c_size_t
+        L.qmv_prepare.argtypes = [I, P, I64, I64, P, P]
+        L.qmm_launch_q8k_prepared.argtypes = [I, P, I64, I64, P, I64, P, P, P]
+        L.qmm_partials_q8k_prepared_launch.argtypes = [I, P, I64, I64, P, I64, P, P]
         L.qmv_gateup_act_bytes.argtypes = [I64, I64, I64]
         L.qmv_gateup_act_bytes.restype = ctypes.c_size_t
         L.qmv_launch_gateup_swiglu.argtypes = [I, P, P, I64, I64, P, I64, P, P, P]
         for f in ("quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
                   "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc",
                   "qmv_launch_gateup_swiglu", "quantize_act_q8_k", "qmv_launch_q8k",
-                  "qmm_launch_q8k", "qmv_partials_q8k_launch"):
+                  "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepare",
+                  "qmm_launch_q8k_prepared", "qmm_partials_q8k_prepared_launch"):
             getattr(L, f).restype = I
         L.qmv_strerror.argtypes = [I]
         L.qmv_strerror.restype = ctypes.c_char_p
@@ -161,6 +168,26 @@ def qmv_partials_q8k_launch(type: int, w: int, N: int, K: int, xq: int, M: int, 
                             stream: int = 0) -> None:
     _check(lib().qmv_partials_q8k_launch(type, w, N, K, xq, M, P, stream),
            "qmv_partials_q8k_launch")
+
+
+def qmv_prepared_bytes(type: int, N: int, K: int) -> int:
+    return int(lib().qmv_prepared_bytes(type, N, K))
+
+
+def qmv_prepare(type: int, w: int, N: int, K: int, wp: int, stream: int = 0) -> None:
+    _check(lib().qmv_prepare(type, w, N, K, wp, stream), "qmv_prepare")
+
+
+def qmm_launch_q8k_prepared(type: int, wp: int, N: int, K: int, x, M: int, xq: int, y: int,
+                            stream: int = 0) -> None:
+    _check(lib().qmm_launch_q8k_prepared(type, wp, N, K, x, M, xq, y, stream),
+           "qmm_launch_q8k_prepared")
+
+
+def qmm_partials_q8k_prepared_launch(type: int, wp: int, N: int, K: int, xq: int, M: int,
+                                     P: int, stream: int = 0) -> None:
+    _check(lib().qmm_partials_q8k_prepared_launch(type, wp, N, K, xq, M, P, stream),
+           "qmm_partials_q8k_prepared_launch")
 
 
 def qmv_strerror(code: int) -> str:
@@ -347,4 +374,44 @@ def partials_q8k(type: int, w, N: int, K: int, xq, M: int, P=None, stream=None):
         P = torch.empty(shape, dtype=torch.int32, device=w.device)
     qmv_partials_q8k_launch(type, _dev(w, torch.uint8, "w"), N, K, _dev(xq, torch.uint8, "xq"), M,
                             _dev(P, torch.int32, "P"), _stream(stream))
+    return P
+
+
+def prepare(type: int, w, N: int, K: int, wp=None, stream=None):
+    """The load-time repack of a Q4_K / Q6_K blob for the Q8_K prefill GEMM."""
+    import torch
+    n = qmv_prepared_bytes(type, N, K)
+    if n == 0:
+        raise ValueError(f"no repacked layout for type {type} N={N} K={K}")
+    if wp is None:
+        wp = torch.empty(n, dtype=torch.uint8, device=w.device)
+    qmv_prepare(type, _dev(w, torch.uint8, "w"), N, K, _dev(wp, torch.uint8, "wp"), _stream(stream))
+    return wp
+
+
+def matmul_q8k_prepared(type: int, wp, N: int, K: int, x=None, xq=None, M=None, y=None,
+                        stream=None):
+    """y [M, N] f32 = x [M, K] @ W^T from repacked weights (x None: staged xq)."""
+    import torch
+    if x is not None:
+        M = x.shape[0]
+    if xq is None:
+        xq = torch.empty(qmv_act_bytes_q8k(M, K), dtype=torch.uint8, device=wp.device)
+    if y is None:
+        y = torch.empty(M, N, dtype=torch.float32, device=wp.device)
+    xp = _dev(x, torch.float32, "x") if x is not None else None
+    qmm_launch_q8k_prepared(type, _dev(wp, torch.uint8, "wp"), N, K, xp, M,
+                            _dev(xq, torch.uint8, "xq"), _dev(y, torch.float32, "y"),
+                            _stream(stream))
+    return y
+
+
+def partials_q8k_prepared(type: int, wp, N: int, K: int, xq, M: int, P=None, stream=None):
+    import torch
+    shape = (M, N, K // 256, 2) if type == Q4_K else (M, N, K // 256)
+    if P is None:
+        P = torch.empty(shape, dtype=torch.int32, device=wp.device)
+    qmm_partials_q8k_prepared_launch(type, _dev(wp, torch.uint8, "wp"), N, K,
+                                     _dev(xq, torch.uint8, "xq"), M, _dev(P, torch.int32, "P"),
+                                     _stream(stream))
     return P

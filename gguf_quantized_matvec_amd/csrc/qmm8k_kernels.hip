@@ -229,15 +229,29 @@ __device__ __forceinline__ void decode_block(const WRawK<FMT>& r, int j, int h, 
 // as 16 pieces of 16 bytes; piece q of row r in slot 16 r + (q ^ (r & 15)),
 // so that the lanes of one ds_read_b128 pass hit different banks), the rows'
 // f32 scales and (Q4_K) their 32-code sums as pairs of int16.
+// (d and s16 are sized for every wave's copy instruction, whatever TM, so
+// that each wave issues the same number of copies; slots past the tile's
+// rows hold duplicates that are not read)
 template <int TM> struct StageK {
     uint4 a[TM * 16];
-    float d[TM];
-    int32_t s16[TM * 8];
+    float d[256];
+    int32_t s16[1024];
 };
+
+// Load-time repacked weights (qmv_prepare): per 32-row tile and superblock a
+// region of 16 digit slabs of 1 KB (slab 2j + g: digit g of block j; lane l's
+// 16 bytes at 16 l, l = 32 h + row, i.e. exactly its MFMA B operand), then
+// the 32 rows' 16-byte scale records (f32 d, f32 dmin, Q4_K's eight mins).
+constexpr int PREP_REGION = 16896, PREP_REC = 16384;
+
+// s_waitcnt with vmcnt = 17 (the repacked kernel's weight loads of one
+// superblock: 16 digit slabs and a scale record), expcnt and lgkmcnt 0
+constexpr int WAIT_VM17 = (1 << 14) | 1;
 
 // WM: 32-row MFMA tiles per wave along M (the workgroup's 32*WM activation
 // rows).  PART: write the exact superblock partials to P instead of y.
-template <int FMT, int WM, bool PART>
+// PREP: w holds the repacked layout instead of the GGUF blob.
+template <int FMT, int WM, bool PART, bool PREP>
 __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* __restrict__ w, int64_t N,
                                                    int64_t K, const uint8_t* __restrict__ xq,
                                                    ActLayoutK L, int64_t M, int64_t tilesM,
@@ -265,9 +279,16 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
     const int64_t m0 = tm * TM, n0 = tn * 128;
     const int nsb = (int)(K >> 8), nb = (int)(K >> 5);
     constexpr int SBB = FMT == T_Q4_K ? 144 : 210;
-    const int64_t R = (int64_t)nsb * SBB;
     const int64_t n = n0 + 32 * wv + lr;
-    const uint8_t* wrow = w + (n < N ? n : N - 1) * R;
+    // direct: the lane's GGUF row; repacked: the wave's 32-row tile (the
+    // last one for a wave wholly past N, whose outputs are not stored)
+    const uint8_t* wrow;
+    if constexpr (PREP) {
+        const int64_t T = (N + 31) >> 5, tile = (n0 >> 5) + wv;
+        wrow = w + (tile < T ? tile : T - 1) * nsb * PREP_REGION;
+    } else {
+        wrow = w + (n < N ? n : N - 1) * ((int64_t)nsb * SBB);
+    }
     auto arow = [&](int row) -> int64_t { return m0 + row < M ? m0 + row : M - 1; };
 
     // asynchronous global -> LDS copy of superblock s into stage `dst`: each
@@ -288,22 +309,25 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
                           4 * (lane & 1);
     // (the global operands are passed as plain void pointers: given as typed
     // pointer arithmetic, the host pass of this compiler drops the kernel)
-    auto issue = [&](int s, StageK<TM>& dst) {
+    auto issue = [&](int s, StageK<TM>* __restrict__ dst) {
 #pragma unroll
         for (int i = 0; i < RPW / 4; i++)
             __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + 256 * s),
-                                             (lds_void*)&dst.a[16 * (RPW * wv + 4 * i)], 16, 0, 0);
-        if (drow < TM)  // the rows' f32 scales, one dword per lane (row 64 wv + lane)
-            __builtin_amdgcn_global_load_lds((const void*)(dsrc + 8 * s), (lds_void*)&dst.d[64 * wv],
-                                             4, 0, 0);
+                                             (lds_void*)&dst->a[16 * (RPW * wv + 4 * i)], 16, 0, 0);
+        // the rows' f32 scales, one dword per lane (row 64 wv + lane)
+        __builtin_amdgcn_global_load_lds((const void*)(dsrc + 8 * s), (lds_void*)&dst->d[64 * wv],
+                                         4, 0, 0);
         if constexpr (FMT == T_Q4_K) {
             // each row's 8 sums (32 bytes): two 16-byte pieces, global lanes
             // 2r, 2r+1 (64 wv + lane); a wave's 64 pieces fill 256 ints
-            if (64 * wv < 2 * TM)
-                __builtin_amdgcn_global_load_lds((const void*)(ssrc + 8 * s),
-                                                 (lds_void*)&dst.s16[256 * wv], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(ssrc + 8 * s),
+                                             (lds_void*)&dst->s16[256 * wv], 16, 0, 0);
         }
     };
+    // the copies one issue() makes per wave, and an s_waitcnt that lets
+    // exactly those stay in flight (expcnt and lgkmcnt not waited for)
+    constexpr int NCOPY = RPW / 4 + 1 + (FMT == T_Q4_K ? 1 : 0);
+    constexpr int WAIT_COPIES = NCOPY | (7 << 4) | (15 << 8);
 
     float yacc[WM][16];
 #pragma unroll
@@ -312,36 +336,90 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
         for (int e = 0; e < 16; e++) yacc[t][e] = 0.0f;
     const v16i zero16 = {};
 
-    WRawK<FMT> wcur, wnext;
-    issue(0, st0);
-    fetch_wk<FMT>(wrow, h, wcur);
+    WRawK<FMT> wcur, wnext;   // direct: the raw bytes of this and the next superblock
+    v4i wd[16];               // repacked: this superblock's digit slabs (refilled
+    uint4 rec, recn;          // with the next one's as they are used), scale records
+    auto slab = [&](int s, int i) -> v4i {
+        return *reinterpret_cast<const v4i*>(wrow + (int64_t)s * PREP_REGION + 1024 * i + 16 * lane);
+    };
+    auto record = [&](int s) -> uint4 {
+        return *reinterpret_cast<const uint4*>(wrow + (int64_t)s * PREP_REGION + PREP_REC + 16 * lr);
+    };
+    issue(0, &st0);
+    if constexpr (PREP) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) wd[i] = slab(0, i);
+        rec = record(0);
+    } else {
+        fetch_wk<FMT>(wrow, h, wcur);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // one superblock on stage `cur` (the next one is copied into `nxt`)
-    auto step = [&](int s, StageK<TM>& cur, StageK<TM>& nxt) {
-        if (s + 1 < nsb) {
-            issue(s + 1, nxt);
+    // (the stages as restrict pointers: once inlined, the LDS reads of `cur`
+    // carry alias scopes that tell the wait-count pass they do not depend on
+    // the asynchronous copies into `nxt`)
+    auto step = [&](int s, StageK<TM>* __restrict__ cur, StageK<TM>* __restrict__ nxt) {
+        // the next superblock (repacked: the last step copies and loads its
+        // own again, into a stage that is not read any more: no branch, so
+        // that the wait counts below stay exact)
+        const int sn = s + 1 < nsb ? s + 1 : s;
+        if (PREP || s + 1 < nsb) issue(sn, nxt);
+        if constexpr (PREP) {
+            // this superblock's weights (loaded during the previous step,
+            // before these copies) have arrived; the copies stay in flight
+            __builtin_amdgcn_s_waitcnt(WAIT_COPIES);
+            // the 17 weight loads below are the wave's last vector-memory
+            // operations of the step, after the copies
+            __builtin_amdgcn_sched_barrier(0);
+            recn = record(sn);
+        } else if (s + 1 < nsb) {
             fetch_wk<FMT>(wrow + (int64_t)(s + 1) * SBB, h, wnext);
         }
         v16i alo[WM], ahi[WM];
 #pragma unroll
         for (int t = 0; t < WM; t++) alo[t] = ahi[t] = zero16;
+        // the activation operands of block j (tile t: rows 32 t + lr), read
+        // from LDS one block ahead of their MFMAs (repacked: nothing else
+        // hides the LDS latency)
+        auto a_op = [&](int j, int t) -> v4i {
+            const int r = 32 * t + lr;
+            return __builtin_bit_cast(v4i, cur->a[16 * r + ((2 * j + h) ^ (r & 15))]);
+        };
+        v4i acur[WM];
+#pragma unroll
+        for (int t = 0; t < WM; t++) acur[t] = a_op(0, t);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             v4i wlo, whi;
-            decode_block<FMT>(wcur, j, h, wlo, whi);
+            if constexpr (PREP) {
+                wlo = wd[2 * j];
+                whi = wd[2 * j + 1];
+            } else {
+                decode_block<FMT>(wcur, j, h, wlo, whi);
+            }
+            v4i anxt[WM];
+#pragma unroll
+            for (int t = 0; t < WM; t++) anxt[t] = a_op(j < 7 ? j + 1 : 7, t);
 #pragma unroll
             for (int t = 0; t < WM; t++) {
-                const int r = 32 * t + lr;
-                const v4i a = __builtin_bit_cast(v4i, cur.a[16 * r + ((2 * j + h) ^ (r & 15))]);
-                alo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, wlo, alo[t], 0, 0, 0);
-                ahi[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, whi, ahi[t], 0, 0, 0);
+                alo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(acur[t], wlo, alo[t], 0, 0, 0);
+                ahi[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(acur[t], whi, ahi[t], 0, 0, 0);
+                acur[t] = anxt[t];
+            }
+            if constexpr (PREP) {
+                wd[2 * j] = slab(sn, 2 * j);
+                wd[2 * j + 1] = slab(sn, 2 * j + 1);
             }
         }
         float dw, dmw = 0.0f;
         v4i bm = {0, 0, 0, 0};
-        if constexpr (FMT == T_Q4_K) {
+        if constexpr (PREP) {
+            dw = __builtin_bit_cast(float, rec.x);
+            dmw = __builtin_bit_cast(float, rec.y);
+            bm = (v4i){(int)(h ? rec.w : rec.z), 0, 0, 0};
+        } else if constexpr (FMT == T_Q4_K) {
             dw = half_bits_to_float(wcur.hdr.x & 0xFFFFu);
             dmw = half_bits_to_float(wcur.hdr.x >> 16);
             // Q4_K min term operands: m_j, j = 4h..4h+3, in bytes 0..3
@@ -364,7 +442,7 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
             if constexpr (FMT == T_Q4_K) {
                 // the row's 32-code sums S_j (j = 4h..4h+3) as two int8 digits
                 // against m_j, in an otherwise-zero MFMA per digit
-                const int4 s4 = *reinterpret_cast<const int4*>(&cur.s16[(32 * t + lr) * 8 + 4 * h]);
+                const int4 s4 = *reinterpret_cast<const int4*>(&cur->s16[(32 * t + lr) * 8 + 4 * h]);
                 const int sv[4] = {s4.x, s4.y, s4.z, s4.w};
                 uint32_t slo = 0, shi = 0;
 #pragma unroll
@@ -392,7 +470,7 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
             } else {
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
-                    const float4 d4 = *reinterpret_cast<const float4*>(&cur.d[32 * t + 8 * g + 4 * h]);
+                    const float4 d4 = *reinterpret_cast<const float4*>(&cur->d[32 * t + 8 * g + 4 * h]);
                     const float da[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
@@ -408,14 +486,36 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
             // of the other tiles from being held live at once
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (s + 1 < nsb) wcur = wnext;
-        // this wave's copies into `nxt` are complete, then every wave's
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        if constexpr (PREP) {
+            rec = recn;
+            // this wave's copies into `nxt` are complete (they precede the
+            // 17 weight loads, which stay in flight), then every wave's; the
+            // barrier is a plain s_barrier so that no wait for the weight
+            // loads is added before it
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(WAIT_VM17);
+            asm volatile("s_barrier" ::: "memory");
+        } else {
+            if (s + 1 < nsb) wcur = wnext;
+            // this wave's copies into `nxt` are complete, then every wave's
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
     };
-    for (int s = 0; s < nsb; s += 2) {
-        step(s, st0, st1);
-        if (s + 1 < nsb) step(s + 1, st1, st0);
+    if constexpr (PREP) {
+        // two straight-line steps per iteration, the odd one after the loop
+        int s = 0;
+        for (; s + 1 < nsb; s += 2) {
+            step(s, &st0, &st1);
+            step(s + 1, &st1, &st0);
+        }
+        if (s < nsb) step(s, &st0, &st1);
+        __builtin_amdgcn_s_waitcnt(0);  // the last step's repeated copies and loads
+    } else {
+        for (int s = 0; s < nsb; s += 2) {
+            step(s, &st0, &st1);
+            if (s + 1 < nsb) step(s + 1, &st1, &st0);
+        }
     }
     if constexpr (PART) return;
 #pragma unroll
@@ -427,7 +527,7 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
         }
 }
 
-template <int FMT, int WM>
+template <int FMT, int WM, bool PREP>
 int launch_gemm8k_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
                     float* y, int32_t* P, hipStream_t s) {
     const ActLayoutK L = act_layout_q8k(M, K);
@@ -435,12 +535,57 @@ int launch_gemm8k_t(const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq, i
     const int64_t grid = tilesM * tilesN;
     if (grid > INT32_MAX) return (int)hipErrorInvalidValue;
     if (P)
-        hipLaunchKernelGGL((k_gemm8k<FMT, WM, true>), dim3((unsigned)grid), dim3(256), 0, s, w, N,
-                           K, xq, L, M, tilesM, tilesN, y, P);
+        hipLaunchKernelGGL((k_gemm8k<FMT, WM, true, PREP>), dim3((unsigned)grid), dim3(256), 0, s,
+                           w, N, K, xq, L, M, tilesM, tilesN, y, P);
     else
-        hipLaunchKernelGGL((k_gemm8k<FMT, WM, false>), dim3((unsigned)grid), dim3(256), 0, s, w, N,
-                           K, xq, L, M, tilesM, tilesN, y, P);
+        hipLaunchKernelGGL((k_gemm8k<FMT, WM, false, PREP>), dim3((unsigned)grid), dim3(256), 0, s,
+                           w, N, K, xq, L, M, tilesM, tilesN, y, P);
     return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------- repack ----
+// One thread per (tile, superblock, block j, lane l = 32 h + row): the two
+// digit slabs' 16 bytes of that lane, from the same decode as the direct
+// GEMM; lanes j = 0 also write their row's scale record.  Rows past N: zero.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_prepare_q8k(const uint8_t* __restrict__ w, int64_t N,
+                                                     int64_t K, uint8_t* __restrict__ out,
+                                                     int64_t total) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int l = (int)(idx & 63), j = (int)((idx >> 6) & 7);
+    const int64_t ts = idx >> 9, nsb = K >> 8;
+    const int64_t t = ts / nsb, s = ts - t * nsb;
+    const int r = l & 31, h = l >> 5;
+    const int64_t n = 32 * t + r;
+    uint8_t* reg = out + ts * PREP_REGION;
+    v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+    uint4 rc = make_uint4(0u, 0u, 0u, 0u);
+    if (n < N) {
+        constexpr int SBB = FMT == T_Q4_K ? 144 : 210;
+        const uint8_t* sbp = w + (n * nsb + s) * SBB;
+        WRawK<FMT> raw;
+        fetch_wk<FMT>(sbp, h, raw);
+        decode_block<FMT>(raw, j, h, lo, hi);
+        if constexpr (FMT == T_Q4_K) {
+            rc.x = __builtin_bit_cast(uint32_t, half_bits_to_float(raw.hdr.x & 0xFFFFu));
+            rc.y = __builtin_bit_cast(uint32_t, half_bits_to_float(raw.hdr.x >> 16));
+            uint32_t m[2] = {0u, 0u};
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                int sc, mn;
+                q4k_sc_m(raw.hdr, k, sc, mn);
+                m[k >> 2] |= (uint32_t)mn << (8 * (k & 3));
+            }
+            rc.z = m[0];
+            rc.w = m[1];
+        } else {
+            rc.x = __builtin_bit_cast(uint32_t, half_bits_to_float(raw.d));
+        }
+    }
+    *reinterpret_cast<v4i*>(reg + 1024 * (2 * j) + 16 * l) = lo;
+    *reinterpret_cast<v4i*>(reg + 1024 * (2 * j + 1) + 16 * l) = hi;
+    if (j == 0 && h == 0) *reinterpret_cast<uint4*>(reg + PREP_REC + 16 * r) = rc;
 }
 
 }  // namespace
@@ -461,22 +606,63 @@ int launch_quantize_q8k(const float* x, uint8_t* xq, int64_t rows, int64_t K, hi
     return (int)hipGetLastError();
 }
 
-// Q6_K: 128 activation rows per workgroup (4 MFMA tiles per wave: each
-// decoded weight value feeds 4 MFMAs, one wave per SIMD) when that still
-// gives the chip a few rounds of workgroups; else 64 or 32.  Q4_K: at most
-// 64 (its min-term MFMAs do not fit the registers of 4 tiles).
+// Direct: Q6_K takes 128 activation rows per workgroup (4 MFMA tiles per
+// wave: each decoded weight value feeds 4 MFMAs, one wave per SIMD) when that
+// still gives the chip a few rounds of workgroups, else 64 or 32; Q4_K at most
+// 64 (its decode and min-term MFMAs do not fit the registers of 4 tiles).
+// Repacked (no decode to amortise): 64 rows, two waves per SIMD so that one
+// wave's f32 epilogue overlaps the other's MFMAs, when that gives at least
+// 256 workgroups; else 32.  (Measured on the 8B-class shapes at M = 512 and
+// 2048: 128-row tiles were 10-45 % slower than 64 on every repacked shape.)
 int launch_gemm_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
-                    int64_t M, float* y, int32_t* P, hipStream_t s) {
+                    int64_t M, float* y, int32_t* P, bool prepared, hipStream_t s) {
     const int64_t tn = (N + 127) / 128;
+    if (prepared) {
+        const bool w2 = M > 32 && ((M + 63) / 64) * tn >= 256;
+        switch (type) {
+        case T_Q4_K: return w2 ? launch_gemm8k_t<T_Q4_K, 2, true>(w, N, K, xq, M, y, P, s)
+                               : launch_gemm8k_t<T_Q4_K, 1, true>(w, N, K, xq, M, y, P, s);
+        case T_Q6_K: return w2 ? launch_gemm8k_t<T_Q6_K, 2, true>(w, N, K, xq, M, y, P, s)
+                               : launch_gemm8k_t<T_Q6_K, 1, true>(w, N, K, xq, M, y, P, s);
+        }
+        return (int)hipErrorInvalidValue;
+    }
     const int wm = M <= 32 ? 1 : ((M + 127) / 128) * tn >= 512 ? 4 : 2;
     switch (type) {
-    case T_Q4_K: return wm >= 2 ? launch_gemm8k_t<T_Q4_K, 2>(w, N, K, xq, M, y, P, s)
-                                : launch_gemm8k_t<T_Q4_K, 1>(w, N, K, xq, M, y, P, s);
-    case T_Q6_K: return wm == 4 ? launch_gemm8k_t<T_Q6_K, 4>(w, N, K, xq, M, y, P, s)
-                      : wm == 2 ? launch_gemm8k_t<T_Q6_K, 2>(w, N, K, xq, M, y, P, s)
-                                : launch_gemm8k_t<T_Q6_K, 1>(w, N, K, xq, M, y, P, s);
+    case T_Q4_K: return wm >= 2 ? launch_gemm8k_t<T_Q4_K, 2, false>(w, N, K, xq, M, y, P, s)
+                                : launch_gemm8k_t<T_Q4_K, 1, false>(w, N, K, xq, M, y, P, s);
+    case T_Q6_K: return wm == 4 ? launch_gemm8k_t<T_Q6_K, 4, false>(w, N, K, xq, M, y, P, s)
+                      : wm == 2 ? launch_gemm8k_t<T_Q6_K, 2, false>(w, N, K, xq, M, y, P, s)
+                                : launch_gemm8k_t<T_Q6_K, 1, false>(w, N, K, xq, M, y, P, s);
     }
     return (int)hipErrorInvalidValue;
+}
+
+int launch_qmm_q8k_prepared(int type, const uint8_t* wp, int64_t N, int64_t K, const float* x,
+                            uint8_t* xq, int64_t rows, float* y, int32_t* P, hipStream_t s) {
+    if (x || P) {
+        const int rc = launch_quantize_q8k(x, xq, rows, K, s);
+        if (rc) return rc;
+    }
+    return launch_gemm_q8k(type, wp, N, K, xq, rows, y, P, true, s);
+}
+
+int64_t prepared_bytes_q8k(int type, int64_t N, int64_t K) {
+    return (N + 31) / 32 * (K / 256) * PREP_REGION;
+}
+
+int launch_prepare_q8k(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* out,
+                       hipStream_t s) {
+    const int64_t total = (N + 31) / 32 * (K / 256) * 512;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
+    if (type == T_Q4_K)
+        hipLaunchKernelGGL(k_prepare_q8k<T_Q4_K>, dim3((unsigned)blocks), dim3(256), 0, s, w, N, K,
+                           out, total);
+    else
+        hipLaunchKernelGGL(k_prepare_q8k<T_Q6_K>, dim3((unsigned)blocks), dim3(256), 0, s, w, N, K,
+                           out, total);
+    return (int)hipGetLastError();
 }
 
 }  // namespace qmv

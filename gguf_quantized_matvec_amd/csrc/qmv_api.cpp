@@ -197,8 +197,11 @@ int quantize_act_q8_k(const float* x, void* xq, int64_t rows, int64_t K, void* s
 }
 
 namespace {
+// prepared: w is the repacked layout of qmv_prepare (checked like a blob:
+// the type, the shape, a 16-byte aligned pointer).
 int q8k_common(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t rows,
-               int64_t max_rows, void* xq, float* y, int32_t* P, void* stream) {
+               int64_t max_rows, void* xq, float* y, int32_t* P, void* stream,
+               bool prepared = false) {
     if (type != QMV_Q4_K && type != QMV_Q6_K) return QMV_EINVAL_TYPE;
     int rc = check_weights(type, w, N, K);
     if (rc) return rc;
@@ -207,11 +210,41 @@ int q8k_common(int type, const void* w, int64_t N, int64_t K, const float* x, in
     if (P ? !aligned(P, 4) : (!y || !aligned(y, 4))) return QMV_EINVAL_PTR;
     if (x && !aligned(x, 4)) return QMV_EINVAL_PTR;
     if ((rc = check_device())) return rc;
-    return launched(qmv::launch_qmv_q8k(type, static_cast<const uint8_t*>(w), N, K, x,
-                                        static_cast<uint8_t*>(xq), rows, y, P,
-                                        static_cast<hipStream_t>(stream)));
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    uint8_t* xb = static_cast<uint8_t*>(xq);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (prepared) return launched(qmv::launch_qmm_q8k_prepared(type, wb, N, K, x, xb, rows, y, P, s));
+    return launched(qmv::launch_qmv_q8k(type, wb, N, K, x, xb, rows, y, P, s));
 }
 }  // namespace
+
+size_t qmv_prepared_bytes(int type, int64_t N, int64_t K) {
+    if (type != QMV_Q4_K && type != QMV_Q6_K) return 0;
+    if (N < 1 || N > INT32_MAX || K < 256 || K > QMV_MAX_K || K % 256) return 0;
+    return (size_t)qmv::prepared_bytes_q8k(type, N, K);
+}
+
+int qmv_prepare(int type, const void* w, int64_t N, int64_t K, void* wp, void* stream) {
+    if (type != QMV_Q4_K && type != QMV_Q6_K) return QMV_EINVAL_TYPE;
+    int rc = check_weights(type, w, N, K);
+    if (rc) return rc;
+    if (!wp || !aligned(wp, 16)) return QMV_EINVAL_PTR;
+    if ((rc = check_device())) return rc;
+    return launched(qmv::launch_prepare_q8k(type, static_cast<const uint8_t*>(w), N, K,
+                                            static_cast<uint8_t*>(wp),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int qmm_launch_q8k_prepared(int type, const void* wp, int64_t N, int64_t K, const float* x,
+                            int64_t M, void* xq, float* y, void* stream) {
+    return q8k_common(type, wp, N, K, x, M, QMV_MAX_M, xq, y, nullptr, stream, true);
+}
+
+int qmm_partials_q8k_prepared_launch(int type, const void* wp, int64_t N, int64_t K, void* xq,
+                                     int64_t M, int32_t* P, void* stream) {
+    if (!P) return QMV_EINVAL_PTR;
+    return q8k_common(type, wp, N, K, nullptr, M, QMV_MAX_M, xq, nullptr, P, stream, true);
+}
 
 int qmv_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
                    void* xq, float* y, void* stream) {

@@ -145,9 +145,17 @@ int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
 int launch_quantize_q8k(const float* x, uint8_t* xq, int64_t rows, int64_t K, hipStream_t s);
 int launch_qmv_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                    int64_t rows, float* y, int32_t* P, hipStream_t s);
-// The int8-MFMA GEMM of the Q8_K path (qmm8k_kernels.hip), any rows >= 1.
+// The int8-MFMA GEMM of the Q8_K path (qmm8k_kernels.hip), any rows >= 1;
+// prepared: w is the load-time repacked layout (launch_prepare_q8k).
 int launch_gemm_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
-                    int64_t M, float* y, int32_t* P, hipStream_t s);
+                    int64_t M, float* y, int32_t* P, bool prepared, hipStream_t s);
+// Load-time repack of a Q4_K / Q6_K blob for the Q8_K GEMM: its size in
+// bytes, the repack, and the GEMM on it (x given or P: quantise first).
+int64_t prepared_bytes_q8k(int type, int64_t N, int64_t K);
+int launch_prepare_q8k(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* out,
+                       hipStream_t s);
+int launch_qmm_q8k_prepared(int type, const uint8_t* wp, int64_t N, int64_t K, const float* x,
+                            uint8_t* xq, int64_t rows, float* y, int32_t* P, hipStream_t s);
 // Device address of the current device's fixed activation scratch for
 // qmv_launch_noalloc (qmv_noalloc.hip), or NULL with *err set.
 uint8_t* noalloc_scratch(int* err);

@@ -1975,7 +1975,7 @@ int launch_qmv_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const float
     // decode batches run the lane-per-chunk kernel, in launches of up to 4
     // activation rows (each reads the weights once); prefill the int8-MFMA GEMM
     if (rows > 16 || !use_dot(rows < 4 ? rows : 4, K))
-        return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, s);
+        return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, false, s);
     const ActLayoutK L = act_layout_q8k(rows, K);
     const int per = type == T_Q4_K ? 2 : 1;
     for (int64_t r0 = 0; r0 < rows; r0 += 4) {

@@ -257,6 +257,44 @@ int qmm_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x
 int qmv_partials_q8k_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                             int64_t M, int32_t* P, void* stream);
 
+/* ---- Load-time repack for the Q8_K prefill GEMM (opt-in) ----
+ * The pages' benchmark runs with the weights repacked at load ("Architecture",
+ * bench transcript header) without saying into what.  Here the repack serves
+ * the arithmetic-bound prefill: it stores each Q4_K / Q6_K element's integer
+ * weight factor (Q4_K: sc_j * q; Q6_K: s_j * (q - 32)) as the two int8 digits
+ * the int8 matrix cores take (v = 64 * hi + lo, lo in 0..63), in the order
+ * one MFMA operand load reads them, with the scales split out, so that the
+ * GEMM does no unpacking.  Layout (N rows in tiles of 32, t = n / 32,
+ * r = n % 32; superblocks s = 0..K/256-1): region t * (K/256) + s of 16896
+ * bytes holds at byte 1024 * (2j + g) + 16 * (32h + r) + i digit g (0: lo,
+ * 1: hi, int8) of row n's element 32j + 16h + i of superblock s, and at byte
+ * 16384 + 16r row n's f32 d (its fp16 d widened), f32 dmin (Q4_K, else 0)
+ * and eight 6-bit mins (Q4_K, else 0), little-endian; rows n >= N are zero.
+ * It takes 16896 / (32 * 144) = 3.7x the Q4_K bytes and 2.5x the Q6_K bytes:
+ * the decode GEMVs, which are bound by weight bytes, keep reading the GGUF
+ * blob; the repacked copy is for prefill only.  Results are bit-identical to
+ * qmm_launch_q8k on the blob it was made from. */
+
+/* Bytes of the repacked layout of an N x K Q4_K / Q6_K matrix; 0 for another
+ * type or an invalid shape (K % 256 != 0 included). */
+size_t qmv_prepared_bytes(int type, int64_t N, int64_t K);
+
+/* Repack the GGUF blob w (as for qmv_launch) into wp (qmv_prepared_bytes
+ * bytes, 16-byte aligned, caller-owned, not overlapping w), asynchronously on
+ * `stream`.  Q4_K and Q6_K only (else QMV_EINVAL_TYPE). */
+int qmv_prepare(int type, const void* w, int64_t N, int64_t K, void* wp, void* stream);
+
+/* qmm_launch_q8k on repacked weights: y[M][N] = x[M][K] * W^T for any
+ * M >= 1, on the int8-MFMA GEMM for every M (no GEMV on this layout).  wp:
+ * qmv_prepare's output for this type, N and K; x / xq / y as qmm_launch_q8k. */
+int qmm_launch_q8k_prepared(int type, const void* wp, int64_t N, int64_t K, const float* x,
+                            int64_t M, void* xq, float* y, void* stream);
+
+/* Test hook: the exact superblock partials of qmm_launch_q8k_prepared's
+ * kernel for M rows, in qmv_partials_q8k_launch's layout. */
+int qmm_partials_q8k_prepared_launch(int type, const void* wp, int64_t N, int64_t K, void* xq,
+                                     int64_t M, int32_t* P, void* stream);
+
 /* Decode GEMV for callers that cannot allocate device memory (code under
  * HIP graph capture, serving loops or harnesses that forbid hipMalloc): the
  * same multiply and result as qmv_launch(type, w, N, K, x, B, xq, y, stream)

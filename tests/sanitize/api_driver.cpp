@@ -94,6 +94,17 @@ int main() {
     CHECK(qmv_partials_q8k_launch(QMV_Q6_K, W, 48, 512, XQ, 7, (int32_t*)Y, nullptr) == QMV_OK &&
           !strcmp(g_last.what, "partials_q8k") && g_last.x == nullptr);
     CHECK(quantize_act_q8_k(X, XQ, 3, 512, nullptr) == QMV_OK && !strcmp(g_last.what, "quantize_q8k"));
+    CHECK(qmv_prepare(QMV_Q4_K, W, 33, 512, XQ, nullptr) == QMV_OK && !strcmp(g_last.what, "prepare") &&
+          g_last.N == 33);
+    CHECK(qmv_prepare(QMV_Q4_0, W, 33, 512, XQ, nullptr) == QMV_EINVAL_TYPE);
+    CHECK(qmv_prepare(QMV_Q6_K, W, 33, 512, XQ + 8, nullptr) == QMV_EINVAL_PTR);
+    CHECK(qmm_launch_q8k_prepared(QMV_Q6_K, W, 48, 512, X, 5, XQ, Y, nullptr) == QMV_OK &&
+          !strcmp(g_last.what, "qmm_q8k_prepared") && g_last.rows == 5);
+    CHECK(qmm_launch_q8k_prepared(QMV_Q6_K, W, 48, 500, X, 5, XQ, Y, nullptr) == QMV_EINVAL_SHAPE);
+    CHECK(qmm_partials_q8k_prepared_launch(QMV_Q4_K, W, 48, 512, XQ, 9, (int32_t*)Y, nullptr) ==
+              QMV_OK && !strcmp(g_last.what, "partials_q8k_prepared") && g_last.x == nullptr);
+    CHECK(qmv_prepared_bytes(QMV_Q4_K, 33, 512) == 2 * 2 * 16896);
+    CHECK(qmv_prepared_bytes(QMV_Q8_0, 33, 512) == 0 && qmv_prepared_bytes(QMV_Q6_K, 33, 500) == 0);
     // sizes
     CHECK(qmv_act_bytes(1, 896) == 24576);
     CHECK(qmv_act_bytes(0, 32) == 0 && qmv_act_bytes(1, 48) == 0);

@@ -88,4 +88,13 @@ int launch_qmv_q8k(int type, const uint8_t*, int64_t N, int64_t K, const float* 
                    int64_t rows, float* y, int32_t* P, hipStream_t) {
     return record(P ? "partials_q8k" : "qmv_q8k", type, N, K, rows, x, xq, P ? (void*)P : (void*)y);
 }
+int launch_qmm_q8k_prepared(int type, const uint8_t*, int64_t N, int64_t K, const float* x,
+                            uint8_t* xq, int64_t rows, float* y, int32_t* P, hipStream_t) {
+    return record(P ? "partials_q8k_prepared" : "qmm_q8k_prepared", type, N, K, rows, x, xq,
+                  P ? (void*)P : (void*)y);
+}
+int64_t prepared_bytes_q8k(int, int64_t N, int64_t K) { return (N + 31) / 32 * (K / 256) * 16896; }
+int launch_prepare_q8k(int type, const uint8_t*, int64_t N, int64_t K, uint8_t* out, hipStream_t) {
+    return record("prepare", type, N, K, 0, nullptr, out, nullptr);
+}
 }  // namespace qmv

@@ -108,6 +108,55 @@ def test_group_refusals():
     assert L.qmv_launch_group(8, 1, (G * 1)(G(16, 1, 32, 18, 16, 16)), 1, None) == -3
 
 
+def test_q8k_refusals_and_scratch_size():
+    L = g.lib()
+    # Q8_K blocks 292 B per 256 elements come first in the scratch
+    assert g.qmv_act_bytes_q8k(3, 1024) >= 3 * 4 * 292
+    for rows, K in [(0, 256), (1, 128), (1, 896), (1, (1 << 20) + 256), ((1 << 24) + 1, 256)]:
+        assert g.qmv_act_bytes_q8k(rows, K) == 0
+    assert L.quantize_act_q8_k(FAKE, FAKE, 1, 896, None) == -2
+    assert L.quantize_act_q8_k(FAKE + 2, FAKE, 1, 256, None) == -3
+    assert L.quantize_act_q8_k(FAKE, FAKE + 4, 1, 256, None) == -3
+    for f, cap in ((L.qmv_launch_q8k, 16), (L.qmm_launch_q8k, 1 << 24)):
+        assert f(g.Q4_0, FAKE, 16, 256, FAKE, 1, FAKE, FAKE, None) == -1   # K-quants only
+        assert f(g.Q8_0, FAKE, 16, 256, FAKE, 1, FAKE, FAKE, None) == -1
+        assert f(g.Q4_K, FAKE, 16, 896, FAKE, 1, FAKE, FAKE, None) == -2
+        assert f(g.Q6_K, FAKE, 16, 256, FAKE, 0, FAKE, FAKE, None) == -2
+        assert f(g.Q6_K, FAKE, 16, 256, FAKE, cap + 1, FAKE, FAKE, None) == -2
+        assert f(g.Q6_K, FAKE + 8, 16, 256, FAKE, 1, FAKE, FAKE, None) == -3
+        assert f(g.Q6_K, FAKE, 16, 256, FAKE + 2, 1, FAKE, FAKE, None) == -3
+        assert f(g.Q6_K, FAKE, 16, 256, FAKE, 1, FAKE + 8, FAKE, None) == -3
+        assert f(g.Q6_K, FAKE, 16, 256, FAKE, 1, FAKE, None, None) == -3
+    assert L.qmv_partials_q8k_launch(g.Q4_K, FAKE, 16, 256, FAKE, 1, None, None) == -3
+    assert L.qmv_partials_q8k_launch(g.Q4_0, FAKE, 16, 256, FAKE, 1, FAKE, None) == -1
+
+
+def test_prepare_refusals_and_size():
+    L = g.lib()
+    # 16896-byte regions per 32-row tile and superblock
+    assert g.qmv_prepared_bytes(g.Q4_K, 33, 512) == 2 * 2 * 16896
+    assert g.qmv_prepared_bytes(g.Q6_K, 32, 256) == 16896
+    for t, N, K in [(g.Q4_0, 32, 256), (g.Q8_0, 32, 256), (g.Q4_K, 32, 896), (g.Q6_K, 0, 256),
+                    (g.Q6_K, 32, (1 << 20) + 256)]:
+        assert g.qmv_prepared_bytes(t, N, K) == 0
+    assert L.qmv_prepare(g.Q4_0, FAKE, 16, 256, FAKE, None) == -1
+    assert L.qmv_prepare(g.Q4_K, FAKE, 16, 896, FAKE, None) == -2
+    assert L.qmv_prepare(g.Q4_K, FAKE, 16, 256, None, None) == -3
+    assert L.qmv_prepare(g.Q4_K, FAKE, 16, 256, FAKE + 8, None) == -3
+    assert L.qmv_prepare(g.Q4_K, FAKE + 8, 16, 256, FAKE, None) == -3
+    f = L.qmm_launch_q8k_prepared
+    assert f(g.Q4_0, FAKE, 16, 256, FAKE, 1, FAKE, FAKE, None) == -1
+    assert f(g.Q6_K, FAKE, 16, 4096 + 32, FAKE, 1, FAKE, FAKE, None) == -2
+    assert f(g.Q6_K, FAKE, 16, 256, FAKE, 0, FAKE, FAKE, None) == -2
+    assert f(g.Q6_K, FAKE, 16, 256, FAKE, (1 << 24) + 1, FAKE, FAKE, None) == -2
+    assert f(g.Q6_K, FAKE + 8, 16, 256, FAKE, 1, FAKE, FAKE, None) == -3
+    assert f(g.Q6_K, FAKE, 16, 256, FAKE, 1, None, FAKE, None) == -3
+    assert f(g.Q6_K, FAKE, 16, 256, FAKE, 1, FAKE, FAKE + 2, None) == -3
+    p = L.qmm_partials_q8k_prepared_launch
+    assert p(g.Q4_K, FAKE, 16, 256, FAKE, 1, None, None) == -3
+    assert p(g.Q4_1, FAKE, 16, 256, FAKE, 1, FAKE, None) == -1
+
+
 def test_noalloc_refusals():
     L = g.lib()
     # the fixed scratch admits every K <= 65536 at B = 16 (and no more at K = 2^17)
