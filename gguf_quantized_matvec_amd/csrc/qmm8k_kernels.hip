@@ -296,31 +296,36 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
     // wv fills rows [TM/4 wv, TM/4 (wv+1)); lane l of instruction i: slot
     // 16 r + u with r = TM/4 wv + 4i + l/16, u = l % 16, i.e. piece u ^ (r & 15)
     constexpr int RPW = TM / 4;  // tile rows per wave
-    const uint8_t* asrc[RPW / 4];
+    // copy sources: a base uniform over the workgroup (the tile's first
+    // row) and 32-bit per-lane offsets (a tile's rows span < 2^27 bytes in
+    // each staging array), which keeps one register per address
+    const uint8_t* abase = xq + L.rcodes + m0 * K;
+    const uint8_t* dbase = xq + L.rda + m0 * nb * 4;
+    const uint8_t* sbase = xq + L.rs16 + m0 * nb * 4;
+    uint32_t aoff[RPW / 4];
 #pragma unroll
     for (int i = 0; i < RPW / 4; i++) {
         const int r = RPW * wv + 4 * i + (lane >> 4);
-        asrc[i] = xq + L.rcodes + arow(r) * K + 16 * ((lane & 15) ^ (r & 15));
+        aoff[i] = (uint32_t)((arow(r) - m0) * K + 16 * ((lane & 15) ^ (r & 15)));
     }
     const int drow = 64 * wv + lane;  // the row whose f32 scale this lane stages
-    const float* dsrc = reinterpret_cast<const float*>(xq + L.rda) + arow(drow < TM ? drow : 0) * nb;
-    const int32_t* ssrc = reinterpret_cast<const int32_t*>(xq + L.rs16) +
-                          arow((64 * wv + lane) >> 1 < TM ? (64 * wv + lane) >> 1 : 0) * nb +
-                          4 * (lane & 1);
+    const uint32_t doff = (uint32_t)((arow(drow < TM ? drow : 0) - m0) * nb * 4);
+    const uint32_t soff = (uint32_t)(
+        (arow((64 * wv + lane) >> 1 < TM ? (64 * wv + lane) >> 1 : 0) - m0) * nb * 4 + 16 * (lane & 1));
     // (the global operands are passed as plain void pointers: given as typed
     // pointer arithmetic, the host pass of this compiler drops the kernel)
     auto issue = [&](int s, StageK<TM>* __restrict__ dst) {
 #pragma unroll
         for (int i = 0; i < RPW / 4; i++)
-            __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + 256 * s),
+            __builtin_amdgcn_global_load_lds((const void*)(abase + (aoff[i] + 256u * s)),
                                              (lds_void*)&dst->a[16 * (RPW * wv + 4 * i)], 16, 0, 0);
         // the rows' f32 scales, one dword per lane (row 64 wv + lane)
-        __builtin_amdgcn_global_load_lds((const void*)(dsrc + 8 * s), (lds_void*)&dst->d[64 * wv],
+        __builtin_amdgcn_global_load_lds((const void*)(dbase + (doff + 32u * s)), (lds_void*)&dst->d[64 * wv],
                                          4, 0, 0);
         if constexpr (FMT == T_Q4_K) {
             // each row's 8 sums (32 bytes): two 16-byte pieces, global lanes
             // 2r, 2r+1 (64 wv + lane); a wave's 64 pieces fill 256 ints
-            __builtin_amdgcn_global_load_lds((const void*)(ssrc + 8 * s),
+            __builtin_amdgcn_global_load_lds((const void*)(sbase + (soff + 32u * s)),
                                              (lds_void*)&dst->s16[256 * wv], 16, 0, 0);
         }
     };
