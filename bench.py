@@ -64,9 +64,15 @@ LAYER = [("q", Q4_K, 4096, 4096), ("k", Q4_K, 1024, 4096), ("v", Q4_K, 1024, 409
          ("down", Q6_K, 4096, 14336)]
 STAGES = {"A_qkv": ("q", "k", "v"), "B_o": ("o",), "C_gateup_swiglu": ("gate", "up"),
           "D_down": ("down",)}
-STAGE_KERNEL = {"A_qkv": "k_dot (grouped: q, k, v)", "B_o": "k_dot (single: o)",
-                "C_gateup_swiglu": "k_dot (paired gate/up, SwiGLU epilogue)",
-                "D_down": "k_dot (single: down, Q6_K)"}
+# the multiply kernel of each stage as the batch-1 step runs it (rocprofv3
+# name prefix: format, rows, fused quantisation, mode): A, B and C quantise
+# their activation inside the kernel (the stage is that one kernel); D's
+# activation h is quantised by a launch of its own before the GEMV
+STAGE_KERNEL = {"A_qkv": "k_dot<12, 1, true, 0>", "B_o": "k_dot<12, 1, true, 1>",
+                "C_gateup_swiglu": "k_dot<12, 1, true, 2>", "D_down": "k_dot<14, 1, false, 1>"}
+STAGE_KERNEL_WHAT = {"A_qkv": "grouped GEMV q, k, v (Q4_K)", "B_o": "GEMV o (Q4_K)",
+                     "C_gateup_swiglu": "paired GEMV gate/up with the SwiGLU epilogue (Q4_K)",
+                     "D_down": "GEMV down (Q6_K 4096x14336)"}
 
 
 def kernel_src_sha() -> str:
@@ -185,6 +191,32 @@ class Layer:
                 g.Gemv(P("k"), 1024, 4096, xa, xq_k, self.y["k"].data_ptr()),
                 g.Gemv(P("v"), 1024, 4096, xa, xq_k, self.y["v"].data_ptr())))
 
+    def stage_inputs(self):
+        """Quantise h into D's xq, as the step's quantisation launch does
+        (for kernel("D_down"))."""
+        self.g.quantize(self.h, xq=self.xq_d)
+
+    def kernel(self, name, c):
+        """Enqueue the multiply kernel of stage `name` as the batch-1 step runs
+        it: stages A, B, C are one kernel each (quantisation fused); for D the
+        down GEMV alone, on the h quantised by stage_inputs()."""
+        if name != "D_down":
+            self.stage(name, c)
+            return
+        torch, g, B = self.torch, self.g, self.B
+        s = torch.cuda.current_stream().cuda_stream
+        _check(g, g.lib().qmv_launch(Q6_K, self.w["down"][c].data_ptr(), 4096, 14336, None, B,
+                                     self.xq_d.data_ptr(), self.y["down"].data_ptr(), s),
+               "down staged")
+
+    def kernel_alg_bytes(self, name):
+        """Algorithmic bytes of one kernel(): as stage_alg_bytes for the fused
+        stages; for D the weights, the Q8_0 blocks of h read and y written."""
+        if name != "D_down":
+            return self.stage_alg_bytes(name)
+        B = self.B
+        return row_bytes(Q6_K, 14336) * 4096 + B * (14336 // 32) * 34 + B * 4096 * 4
+
     def stage(self, name, c):
         """Enqueue stage `name` with weight copy c on the current stream."""
         torch, g, B = self.torch, self.g, self.B
@@ -247,10 +279,19 @@ def time_layer(torch, g, synth, B, steps, warmup, rotate_bytes):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # each stage alone, back to back over every rotated copy
-    stage_us = {name: graph_launch_us(torch, lambda i, name=name: Lw.stage(name, i % Lw.R), Lw.R)
+    n = max(Lw.R, 32)
+    stage_us = {name: graph_launch_us(torch, lambda i, name=name: Lw.stage(name, i % Lw.R), n)
                 for name in STAGES}
     res = {"wall_s": wall, "step_bytes": Lw.step_bytes, "R": Lw.R, "stage_us": stage_us,
-           "stage_alg_bytes": {n: Lw.stage_alg_bytes(n) for n in STAGES}}
+           "stage_alg_bytes": {n_: Lw.stage_alg_bytes(n_) for n_ in STAGES}}
+    if B <= 4:
+        # each stage's multiply kernel as one kernel per launch
+        Lw.stage_inputs()
+        res["kernel_us"] = {
+            name: graph_launch_us(torch, lambda i, name=name: Lw.kernel(name, i % Lw.R), n)
+            for name in STAGES}
+        res["kernel_alg_bytes"] = {n_: Lw.kernel_alg_bytes(n_) for n_ in STAGES}
+        res["kernel_launches"] = n
     del graphs, Lw
     torch.cuda.empty_cache()
     return res
@@ -561,6 +602,18 @@ def profile_stage(torch, g, synth, name, launches=20):
     print(json.dumps({"profile_stage": name, "launches": launches}))
 
 
+def profile_kernel(torch, g, synth, name, launches=20):
+    """Launch one stage's multiply kernel (Layer.kernel) `launches` times,
+    eagerly, over the rotated weight copies."""
+    Lw = Layer(torch, g, synth, 1, 1 << 30)
+    Lw.stage_inputs()
+    torch.cuda.synchronize()
+    for i in range(launches):
+        Lw.kernel(name, i % Lw.R)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_kernel": name, "kernel": STAGE_KERNEL[name], "launches": launches}))
+
+
 def profile_matrix(torch, g, synth, spec, launches=20):
     """Launch one workload matrix (the suite's seeded weights, activations
     staged) `launches` times back to back, eagerly.  spec WORKLOAD:INDEX:ROWS
@@ -684,18 +737,21 @@ def main():
                     help="also report every workload matrix (GEMV and GEMM) separately")
     ap.add_argument("--profile-stage", default=None, choices=list(STAGES),
                     help="only launch one stage of the layer step 20 times, eagerly")
+    ap.add_argument("--profile-kernel", default=None, choices=list(STAGES),
+                    help="only launch one stage's multiply kernel 20 times, eagerly")
     ap.add_argument("--profile-matrix", default=None, metavar="WORKLOAD:INDEX:ROWS",
                     help="only launch one workload matrix 20 times, eagerly")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 256 MiB device copy 10 times (counter calibration)")
     ap.add_argument("--traffic-from", default=None, metavar="DIR")
-    ap.add_argument("--traffic-kernel", default="k_dot")
-    ap.add_argument("--traffic-stage", default="C_gateup_swiglu", choices=list(STAGES))
+    ap.add_argument("--traffic-stage", default="D_down", choices=list(STAGES),
+                    help="the stage whose kernel (--profile-kernel) the counters under "
+                         "--traffic-from were taken on")
     ap.add_argument("--trace-summary", default=None, metavar="DIR")
     args = ap.parse_args()
 
     if args.traffic_from:
-        traffic_from(args.traffic_from, args.traffic_kernel, args.traffic_stage)
+        traffic_from(args.traffic_from, STAGE_KERNEL[args.traffic_stage], args.traffic_stage)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
@@ -731,6 +787,9 @@ def main():
     if args.profile_stage:
         profile_stage(torch, g, synth, args.profile_stage)
         return
+    if args.profile_kernel:
+        profile_kernel(torch, g, synth, args.profile_kernel)
+        return
     if args.profile_matrix:
         profile_matrix(torch, g, synth, args.profile_matrix)
         return
@@ -740,9 +799,11 @@ def main():
     r1 = time_layer(torch, g, synth, 1, args.steps, args.warmup, rot)
     wall = r1["wall_s"]
     value = r1["step_bytes"] * args.steps / wall / 1e9
-    dom = max(r1["stage_us"], key=r1["stage_us"].get)
-    dom_us = r1["stage_us"][dom]
-    achieved = r1["stage_alg_bytes"][dom] / (dom_us * 1e-6) / 1e9
+    # roofline: the step's slowest multiply kernel, each timed as one kernel
+    # (as a kernel trace sees it)
+    dom = max(r1["kernel_us"], key=r1["kernel_us"].get)
+    dom_us = r1["kernel_us"][dom]
+    achieved = r1["kernel_alg_bytes"][dom] / (dom_us * 1e-6) / 1e9
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -772,15 +833,17 @@ def main():
             "tok_s": round(args.steps / wall, 1),
             "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4),
             "stage_us": {k: round(v, 2) for k, v in r1["stage_us"].items()},
+            "kernel_us": {k: round(v, 2) for k, v in r1["kernel_us"].items()},
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "stage": dom, "kernel": STAGE_KERNEL[dom],
-                     "avg_launch_us": round(dom_us, 3), "launches_timed": r1["R"],
-                     "alg_bytes_per_launch": r1["stage_alg_bytes"][dom],
-                     "timing": "HIP events on the launch stream around a graph replay of the "
-                               "stage's launches back to back over every rotated copy; time per "
-                               "launch includes the dispatch gap between graph nodes"},
+                     "kernel_does": STAGE_KERNEL_WHAT[dom],
+                     "avg_launch_us": round(dom_us, 3), "launches_timed": r1["kernel_launches"],
+                     "alg_bytes_per_launch": r1["kernel_alg_bytes"][dom],
+                     "timing": "HIP events on the launch stream around graph replays of the "
+                               "kernel's launches back to back over the rotated weight copies; "
+                               "time per launch includes the dispatch gap between graph nodes"},
     }
     if not args.no_cpu:
         print("step: cpu baseline", file=sys.stderr, flush=True)

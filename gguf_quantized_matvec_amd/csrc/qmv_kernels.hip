@@ -1778,6 +1778,65 @@ bool use_dot(int64_t rows, int64_t K) {
     return rows <= DOT_MAX_ROWS && rows * act_lds_row_bytes(K) + 8 * rows * 256 <= DOT_MAX_ACT_LDS;
 }
 
+// The same quantisation for the row staging alone (the decode GEMV's, B <= 4),
+// 8 lanes per 32-block, 4 elements per lane: coalesced loads, the amax and
+// the code sums by lane shuffles, every lane writing its own 4 codes.  The
+// arithmetic per element is quant_block's, so the bytes are the same.
+template <bool A16>
+__global__ __launch_bounds__(256) void k_quantize_row(const float* __restrict__ x,
+                                                      uint8_t* __restrict__ xq, int64_t rows,
+                                                      int64_t K, ActLayout L) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nb = L.nb;
+    const int64_t blk = t >> 3;               // uniform over each group of 8 lanes
+    const bool live = blk < rows * nb;        // (the shuffles below take every lane)
+    const int sub = (int)(t & 7);
+    const int64_t r = live ? blk / nb : 0, b = live ? blk - r * nb : 0;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (live) {
+        const float* xb = x + r * K + 32 * b + 4 * sub;
+        if constexpr (A16) {
+            const float4 f = *reinterpret_cast<const float4*>(xb);
+            v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) v[i] = xb[i];
+        }
+    }
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float d = amax / 127.0f;
+    const float id = inv_scale(d);
+    uint32_t c4 = 0;
+    int s4 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int c = (int)roundf(v[i] * id);
+        c4 |= ((uint32_t)c & 0xFFu) << (8 * i);
+        s4 += c;
+    }
+    int s16 = s4 + __shfl_xor(s4, 1);
+    s16 += __shfl_xor(s16, 2);               // the sum of this lane's 16-code half
+    const int s16o = __shfl_xor(s16, 4);     // the other half's
+    if (!live) return;
+    const uint16_t h = float_to_half_bits(d);
+    const float dval = half_bits_to_float(h);
+    uint8_t* pub = xq + (r * nb + b) * 34;   // 2-byte aligned
+    uint16_t* pc = reinterpret_cast<uint16_t*>(pub + 2 + 4 * sub);
+    pc[0] = (uint16_t)(c4 & 0xFFFFu);
+    pc[1] = (uint16_t)(c4 >> 16);
+    *reinterpret_cast<uint32_t*>(xq + L.rcodes + r * K + 32 * b + 4 * sub) = c4;
+    if (sub == 0) {
+        *reinterpret_cast<uint16_t*>(pub) = h;
+        const int S = s16 + s16o;
+        reinterpret_cast<float*>(xq + L.rda)[r * nb + b] = dval;
+        reinterpret_cast<float*>(xq + L.rca)[r * nb + b] = dval * (float)S;
+        reinterpret_cast<int32_t*>(xq + L.rs16)[r * nb + b] =
+            (int32_t)(((uint32_t)s16 & 0xFFFFu) | ((uint32_t)s16o << 16));
+    }
+}
+
 }  // namespace
 
 bool group_is_one_launch(const GemvDesc* d, int count, int64_t rows) {
@@ -1795,6 +1854,14 @@ int staging_for(int64_t rows, int64_t K) {
 int launch_quantize(const float* x, uint8_t* xq, int64_t rows, int64_t K, int staging,
                     hipStream_t s) {
     const ActLayout L = act_layout(rows, K);
+    if (staging == ST_ROW) {
+        const unsigned grid = (unsigned)((rows * L.nb * 8 + 255) / 256);
+        if (aligned16(x))
+            hipLaunchKernelGGL((k_quantize_row<true>), dim3(grid), dim3(256), 0, s, x, xq, rows, K, L);
+        else
+            hipLaunchKernelGGL((k_quantize_row<false>), dim3(grid), dim3(256), 0, s, x, xq, rows, K, L);
+        return (int)hipGetLastError();
+    }
     const int64_t threads = ((staging & ST_MFMA) ? 16 * L.G : rows) * L.nb;
     if (aligned16(x))
         hipLaunchKernelGGL((k_quantize<false, true>), dim3((unsigned)((threads + 255) / 256)),
