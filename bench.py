@@ -8,11 +8,13 @@ built from the four 8B-class weight shapes (Q4_K 4096x4096, 1024x4096,
   A  q 4096x4096, k and v 1024x4096 on one activation (one grouped launch)
   B  o 4096x4096 on the attention output (a synthetic activation here)
   C  gate and up 14336x4096 on one activation, with the SwiGLU
-     h = silu(gate) * up in the same launch (qmv_launch_gateup_swiglu)
-  D  down 4096x14336 (Q6_K) on h
+     h = silu(gate) * up and the Q8_0 quantisation of h in the same launch
+     (qmv_launch_gateup_swiglu_q8)
+  D  down 4096x14336 (Q6_K) on the quantised h
 
-Each stage quantises its own activation to Q8_0 inside the GEMV where it
-can.  Attention, norms and residuals are not part of the multiply and are
+A, B and C quantise their own activation to Q8_0 inside the GEMV; the
+quantisation of h follows C's kernel as a launch of its own (at K = 4096 the
+paired launch does not take it in: see qmv_launch_gateup_swiglu_q8).  Attention, norms and residuals are not part of the multiply and are
 not run.  A step is replayed from a captured HIP graph; the weights are
 rotated over copies totalling >= --rotate-mib, so every step streams them
 from HBM rather than from the 256 MB last-level cache.  value = weight bytes
@@ -64,12 +66,13 @@ LAYER = [("q", Q4_K, 4096, 4096), ("k", Q4_K, 1024, 4096), ("v", Q4_K, 1024, 409
          ("down", Q6_K, 4096, 14336)]
 STAGES = {"A_qkv": ("q", "k", "v"), "B_o": ("o",), "C_gateup_swiglu": ("gate", "up"),
           "D_down": ("down",)}
-# the multiply kernel of each stage as the batch-1 step runs it (rocprofv3
-# name prefix: format, rows, fused quantisation, mode): A, B and C quantise
-# their activation inside the kernel (the stage is that one kernel); D's
-# activation h is quantised by a launch of its own before the GEMV
-STAGE_KERNEL = {"A_qkv": "k_dot<12, 1, true, 0>", "B_o": "k_dot<12, 1, true, 1>",
-                "C_gateup_swiglu": "k_dot<12, 1, true, 2>", "D_down": "k_dot<14, 1, false, 1>"}
+# the multiply kernel of each stage at batch 1 (its rocprofv3 name: format,
+# rows, fused quantisation, mode, Q8_K activations): A, B and C quantise their
+# activation inside the kernel; at K = 4096 the quantisation of h for D is a
+# launch of its own after C's kernel; D reads it
+STAGE_KERNEL = {"A_qkv": "k_dot<12, 1, true, 0, false>", "B_o": "k_dot<12, 1, true, 1, false>",
+                "C_gateup_swiglu": "k_dot<12, 1, true, 2, false>",
+                "D_down": "k_dot<14, 1, false, 1, false>"}
 STAGE_KERNEL_WHAT = {"A_qkv": "grouped GEMV q, k, v (Q4_K)", "B_o": "GEMV o (Q4_K)",
                      "C_gateup_swiglu": "paired GEMV gate/up with the SwiGLU epilogue (Q4_K)",
                      "D_down": "GEMV down (Q6_K 4096x14336)"}
@@ -191,31 +194,26 @@ class Layer:
                 g.Gemv(P("k"), 1024, 4096, xa, xq_k, self.y["k"].data_ptr()),
                 g.Gemv(P("v"), 1024, 4096, xa, xq_k, self.y["v"].data_ptr())))
 
-    def stage_inputs(self):
-        """Quantise h into D's xq, as the step's quantisation launch does
-        (for kernel("D_down"))."""
-        self.g.quantize(self.h, xq=self.xq_d)
-
     def kernel(self, name, c):
-        """Enqueue the multiply kernel of stage `name` as the batch-1 step runs
-        it: stages A, B, C are one kernel each (quantisation fused); for D the
-        down GEMV alone, on the h quantised by stage_inputs()."""
-        if name != "D_down":
+        """Enqueue the multiply kernel of stage `name` alone: the stage itself
+        for A, B and D (one kernel each at batch <= 4); for C the paired
+        gate/up GEMV without the quantisation of h that follows it."""
+        if name != "C_gateup_swiglu":
             self.stage(name, c)
             return
-        torch, g, B = self.torch, self.g, self.B
-        s = torch.cuda.current_stream().cuda_stream
-        _check(g, g.lib().qmv_launch(Q6_K, self.w["down"][c].data_ptr(), 4096, 14336, None, B,
-                                     self.xq_d.data_ptr(), self.y["down"].data_ptr(), s),
-               "down staged")
+        g = self.g
+        s = self.torch.cuda.current_stream().cuda_stream
+        _check(g, g.lib().qmv_launch_gateup_swiglu(
+            Q4_K, self.w["gate"][c].data_ptr(), self.w["up"][c].data_ptr(), 14336, 4096,
+            self.xc.data_ptr(), self.B, self.xq_c.data_ptr(), self.h.data_ptr(), s), "gate/up")
 
     def kernel_alg_bytes(self, name):
-        """Algorithmic bytes of one kernel(): as stage_alg_bytes for the fused
-        stages; for D the weights, the Q8_0 blocks of h read and y written."""
-        if name != "D_down":
-            return self.stage_alg_bytes(name)
-        B = self.B
-        return row_bytes(Q6_K, 14336) * 4096 + B * (14336 // 32) * 34 + B * 4096 * 4
+        """Algorithmic bytes of one kernel(): as stage_alg_bytes, without the
+        quantisation of h for C."""
+        b = self.stage_alg_bytes(name)
+        if name == "C_gateup_swiglu":
+            b -= self.B * (14336 // 32) * 34
+        return b
 
     def stage(self, name, c):
         """Enqueue stage `name` with weight copy c on the current stream."""
@@ -232,12 +230,14 @@ class Layer:
             _check(g, L.qmv_launch(Q4_K, W("o"), 4096, 4096, self.xo.data_ptr(), B,
                                    self.xq_o.data_ptr(), self.y["o"].data_ptr(), s), "o")
         elif name == "C_gateup_swiglu":
-            _check(g, L.qmv_launch_gateup_swiglu(Q4_K, W("gate"), W("up"), 14336, 4096,
-                                                 self.xc.data_ptr(), B, self.xq_c.data_ptr(),
-                                                 self.h.data_ptr(), s), "gate/up")
+            # h = silu(gate) * up, and its Q8_0 quantisation into D's scratch
+            _check(g, L.qmv_launch_gateup_swiglu_q8(Q4_K, W("gate"), W("up"), 14336, 4096,
+                                                    self.xc.data_ptr(), B, self.xq_c.data_ptr(),
+                                                    self.h.data_ptr(), self.xq_d.data_ptr(), s),
+                   "gate/up")
         else:
-            _check(g, L.qmv_launch(Q6_K, W("down"), 4096, 14336, self.h.data_ptr(), B,
-                                   self.xq_d.data_ptr(), self.y["down"].data_ptr(), s), "down")
+            _check(g, L.qmv_launch(Q6_K, W("down"), 4096, 14336, None, B, self.xq_d.data_ptr(),
+                                   self.y["down"].data_ptr(), s), "down")
 
     def step(self, i):
         c = i % self.R
@@ -245,8 +245,9 @@ class Layer:
             self.stage(name, c)
 
     def stage_alg_bytes(self, name):
-        """Algorithmic bytes of one launch of a stage: weight blobs, the f32
-        activation read, its Q8_0 blocks written, the f32 outputs."""
+        """Algorithmic bytes of one launch of a stage: weight blobs; A, B, C:
+        the f32 activation read and its Q8_0 blocks written; D: the Q8_0
+        blocks of h read; the f32 outputs (C: h, and its Q8_0 blocks)."""
         B = self.B
         wb = {n: row_bytes(f, K) * N for n, f, N, K in LAYER}
         Kd = {n: K for n, _, _, K in LAYER}
@@ -254,8 +255,13 @@ class Layer:
         mats = STAGES[name]
         K = Kd[mats[0]]
         w = sum(wb[n] for n in mats)
-        outs = B * Nd["gate"] * 4 if name == "C_gateup_swiglu" else sum(B * Nd[n] * 4 for n in mats)
-        return w + B * K * 4 + B * (K // 32) * 34 + outs
+        if name == "D_down":
+            return w + B * (K // 32) * 34 + B * Nd["down"] * 4
+        act = B * K * 4 + B * (K // 32) * 34
+        if name == "C_gateup_swiglu":
+            Nh = Nd["gate"]
+            return w + act + B * Nh * 4 + B * (Nh // 32) * 34
+        return w + act + sum(B * Nd[n] * 4 for n in mats)
 
 
 def time_layer(torch, g, synth, B, steps, warmup, rotate_bytes):
@@ -285,8 +291,7 @@ def time_layer(torch, g, synth, B, steps, warmup, rotate_bytes):
     res = {"wall_s": wall, "step_bytes": Lw.step_bytes, "R": Lw.R, "stage_us": stage_us,
            "stage_alg_bytes": {n_: Lw.stage_alg_bytes(n_) for n_ in STAGES}}
     if B <= 4:
-        # each stage's multiply kernel as one kernel per launch
-        Lw.stage_inputs()
+        # each stage's multiply kernel alone
         res["kernel_us"] = {
             name: graph_launch_us(torch, lambda i, name=name: Lw.kernel(name, i % Lw.R), n)
             for name in STAGES}
@@ -406,12 +411,14 @@ def qwen_ffn(torch, g, synth, rotate_bytes):
     y = torch.empty(1, 896, dtype=torch.float32, device="cuda")
 
     def step(i):
+        # gate/up + SwiGLU + the quantisation of h in one launch, then down
         c = i % R
         s = torch.cuda.current_stream().cuda_stream
-        _check(g, L.qmv_launch_gateup_swiglu(Q4_0, cp["gate"][c].data_ptr(), cp["up"][c].data_ptr(),
-                                             4864, 896, x.data_ptr(), 1, xq.data_ptr(),
-                                             h.data_ptr(), s), "qwen gate/up")
-        _check(g, L.qmv_launch(Q4_0, cp["down"][c].data_ptr(), 896, 4864, h.data_ptr(), 1,
+        _check(g, L.qmv_launch_gateup_swiglu_q8(Q4_0, cp["gate"][c].data_ptr(),
+                                                cp["up"][c].data_ptr(), 4864, 896, x.data_ptr(), 1,
+                                                xq.data_ptr(), h.data_ptr(), xq2.data_ptr(), s),
+               "qwen gate/up")
+        _check(g, L.qmv_launch(Q4_0, cp["down"][c].data_ptr(), 896, 4864, None, 1,
                                xq2.data_ptr(), y.data_ptr(), s), "qwen down")
     step(0)
     us = graph_launch_us(torch, step, R)
@@ -606,7 +613,7 @@ def profile_kernel(torch, g, synth, name, launches=20):
     """Launch one stage's multiply kernel (Layer.kernel) `launches` times,
     eagerly, over the rotated weight copies."""
     Lw = Layer(torch, g, synth, 1, 1 << 30)
-    Lw.stage_inputs()
+    Lw.step(0)   # (D reads the h quantised by C)
     torch.cuda.synchronize()
     for i in range(launches):
         Lw.kernel(name, i % Lw.R)
@@ -737,6 +744,9 @@ def main():
                     help="also report every workload matrix (GEMV and GEMM) separately")
     ap.add_argument("--profile-stage", default=None, choices=list(STAGES),
                     help="only launch one stage of the layer step 20 times, eagerly")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the M = 2048 GEMMs of the four 8B-class shapes (Q8_0 activations, "
+                         "Q8_K, Q8_K on repacked weights)")
     ap.add_argument("--profile-kernel", default=None, choices=list(STAGES),
                     help="only launch one stage's multiply kernel 20 times, eagerly")
     ap.add_argument("--profile-matrix", default=None, metavar="WORKLOAD:INDEX:ROWS",
@@ -787,6 +797,12 @@ def main():
     if args.profile_stage:
         profile_stage(torch, g, synth, args.profile_stage)
         return
+    if args.prefill_only:
+        print(json.dumps({"prefill_m2048": prefill_8b(torch, g, synth),
+                          "prefill_m2048_q8k": prefill_8b(torch, g, synth, q8k=True),
+                          "prefill_m2048_q8k_repacked": prefill_8b(torch, g, synth, q8k=True,
+                                                                   prepared=True)}))
+        return
     if args.profile_kernel:
         profile_kernel(torch, g, synth, args.profile_kernel)
         return
@@ -799,8 +815,8 @@ def main():
     r1 = time_layer(torch, g, synth, 1, args.steps, args.warmup, rot)
     wall = r1["wall_s"]
     value = r1["step_bytes"] * args.steps / wall / 1e9
-    # roofline: the step's slowest multiply kernel, each timed as one kernel
-    # (as a kernel trace sees it)
+    # roofline: the step's slowest multiply kernel, timed alone (as a kernel
+    # trace sees it)
     dom = max(r1["kernel_us"], key=r1["kernel_us"].get)
     dom_us = r1["kernel_us"][dom]
     achieved = r1["kernel_alg_bytes"][dom] / (dom_us * 1e-6) / 1e9

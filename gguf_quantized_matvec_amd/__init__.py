@@ -21,7 +21,7 @@ BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_1: (32, 20), Q5_1: (
          Q8_1: (32, 36), Q4_K: (256, 144), Q6_K: (256, 210)}
 EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
            "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc", "qmv_gateup_act_bytes",
-           "qmv_launch_gateup_swiglu", "qmv_act_bytes_q8k", "quantize_act_q8_k", "qmv_launch_q8k",
+           "qmv_launch_gateup_swiglu", "qmv_launch_gateup_swiglu_q8", "qmv_act_bytes_q8k", "quantize_act_q8_k", "qmv_launch_q8k",
            "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepared_bytes", "qmv_prepare",
            "qmm_launch_q8k_prepared", "qmm_partials_q8k_prepared_launch", "qmv_strerror")
 MAX_BATCH = 16
@@ -74,9 +74,10 @@ def lib() -> ctypes.CDLL:
         L.qmv_gateup_act_bytes.argtypes = [I64, I64, I64]
         L.qmv_gateup_act_bytes.restype = ctypes.c_size_t
         L.qmv_launch_gateup_swiglu.argtypes = [I, P, P, I64, I64, P, I64, P, P, P]
+        L.qmv_launch_gateup_swiglu_q8.argtypes = [I, P, P, I64, I64, P, I64, P, P, P, P]
         for f in ("quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
                   "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc",
-                  "qmv_launch_gateup_swiglu", "quantize_act_q8_k", "qmv_launch_q8k",
+                  "qmv_launch_gateup_swiglu", "qmv_launch_gateup_swiglu_q8", "quantize_act_q8_k", "qmv_launch_q8k",
                   "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepare",
                   "qmm_launch_q8k_prepared", "qmm_partials_q8k_prepared_launch"):
             getattr(L, f).restype = I
@@ -144,6 +145,12 @@ def qmv_launch_gateup_swiglu(type: int, w_gate: int, w_up: int, N: int, K: int, 
                              xq: int, h: int, stream: int = 0) -> None:
     _check(lib().qmv_launch_gateup_swiglu(type, w_gate, w_up, N, K, x, B, xq, h, stream),
            "qmv_launch_gateup_swiglu")
+
+
+def qmv_launch_gateup_swiglu_q8(type: int, w_gate: int, w_up: int, N: int, K: int, x, B: int,
+                                xq: int, h: int, hq: int, stream: int = 0) -> None:
+    _check(lib().qmv_launch_gateup_swiglu_q8(type, w_gate, w_up, N, K, x, B, xq, h, hq, stream),
+           "qmv_launch_gateup_swiglu_q8")
 
 
 def qmv_act_bytes_q8k(rows: int, K: int) -> int:
@@ -303,6 +310,29 @@ def gateup_swiglu(type: int, w_gate, w_up, N: int, K: int, x=None, xq=None, B=No
                              _dev(xq, torch.uint8, "xq"), _dev(h, torch.float32, "h"),
                              _stream(stream))
     return h
+
+
+def gateup_swiglu_q8(type: int, w_gate, w_up, N: int, K: int, x=None, xq=None, B=None, h=None,
+                     hq=None, stream=None):
+    """(h [B, N] f32, hq) with hq the Q8_0 scratch of h for the down GEMV."""
+    import torch
+    if x is not None:
+        B = x.shape[0]
+    if xq is None:
+        n = qmv_gateup_act_bytes(B, N, K)
+        if n == 0:
+            raise ValueError(f"bad shape B={B} N={N} K={K}")
+        xq = torch.empty(n, dtype=torch.uint8, device=w_gate.device)
+    if h is None:
+        h = torch.empty(B, N, dtype=torch.float32, device=w_gate.device)
+    if hq is None:
+        hq = act_buffer(B, N, w_gate.device)
+    xp = _dev(x, torch.float32, "x") if x is not None else None
+    qmv_launch_gateup_swiglu_q8(type, _dev(w_gate, torch.uint8, "w_gate"),
+                                _dev(w_up, torch.uint8, "w_up"), N, K, xp, B,
+                                _dev(xq, torch.uint8, "xq"), _dev(h, torch.float32, "h"),
+                                _dev(hq, torch.uint8, "hq"), _stream(stream))
+    return h, hq
 
 
 def matmul(type: int, w, N: int, K: int, x=None, xq=None, M=None, y=None, stream=None):

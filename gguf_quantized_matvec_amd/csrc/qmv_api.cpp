@@ -153,6 +153,26 @@ int qmv_launch_gateup_swiglu(int type, const void* w_gate, const void* w_up, int
                                        static_cast<hipStream_t>(stream)));
 }
 
+int qmv_launch_gateup_swiglu_q8(int type, const void* w_gate, const void* w_up, int64_t N,
+                                int64_t K, const float* x, int64_t B, void* xq, float* h,
+                                void* hq, void* stream) {
+    int rc = check_weights(type, w_gate, N, K);
+    if (rc) return rc;
+    if ((rc = check_weights(type, w_up, N, K))) return rc;
+    if (B < 1 || B > QMV_MAX_BATCH) return QMV_EINVAL_SHAPE;
+    // h is the next projection's activation: whole 32-element blocks
+    if (N < 32 || N > QMV_MAX_K || N % 32) return QMV_EINVAL_SHAPE;
+    if (!xq || !h || !hq || !aligned(xq, 16) || !aligned(h, 4) || !aligned(hq, 16))
+        return QMV_EINVAL_PTR;
+    if (x && !aligned(x, 4)) return QMV_EINVAL_PTR;
+    if ((rc = check_device())) return rc;
+    return launched(qmv::launch_gateup(type, static_cast<const uint8_t*>(w_gate),
+                                       static_cast<const uint8_t*>(w_up), N, K, x,
+                                       static_cast<uint8_t*>(xq), B, h,
+                                       static_cast<hipStream_t>(stream),
+                                       static_cast<uint8_t*>(hq)));
+}
+
 int qmm_launch(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t M,
                void* xq, float* y, void* stream) {
     return matmul_common(type, w, N, K, x, M, QMV_MAX_M, xq, y, stream, true);

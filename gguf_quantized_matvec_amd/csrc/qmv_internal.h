@@ -133,8 +133,12 @@ bool gateup_is_one_launch(int64_t rows, int64_t K);
 inline int64_t gateup_act_bytes(int64_t rows, int64_t N, int64_t K) {
     return align256(act_layout(rows, K).total) + 2 * align256(rows * N * 4);
 }
+// hq != NULL: h quantised to Q8_0 into hq as quantize_act_q8_0(h, hq, rows,
+// N) leaves it, inside the paired launch when gateup_quantises_h().
 int launch_gateup(int type, const uint8_t* wg, const uint8_t* wu, int64_t N, int64_t K,
-                  const float* x, uint8_t* xq, int64_t rows, float* h, hipStream_t s);
+                  const float* x, uint8_t* xq, int64_t rows, float* h, hipStream_t s,
+                  uint8_t* hq = nullptr);
+bool gateup_quantises_h(int type, int64_t rows, int64_t N, int64_t K);
 int launch_partials(int type, const uint8_t* w, int64_t N, int64_t K, uint8_t* xq,
                     int64_t rows, int32_t* P, hipStream_t s);
 int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,

@@ -146,6 +146,47 @@ __device__ __forceinline__ void store_row_staging(uint8_t* xq, const ActLayout& 
 // in xq) and write the staging copies selected by `staging`.  One thread per
 // (row, block); with ST_MFMA over the 16-row-padded range, whose padding
 // rows get zero codes and scales in that copy.
+// One 32-block quantised by an aligned group of 8 lanes, 4 elements each
+// (lane sub = lane & 7 holds elements 4 sub .. 4 sub + 3): the amax and the
+// code sums by lane shuffles (every lane of the wave takes part), then each
+// live lane writes its 4 codes into the public block at pub and into the row
+// staging at rc, and lane 0 of the group the scale and sums at index bi of
+// rda / rca / rs16.  The arithmetic per element is quant_block's, so the
+// bytes are the same as k_quantize's.
+__device__ __forceinline__ void quant_block8(const float (&v)[4], int sub, bool live, uint8_t* pub,
+                                             uint8_t* rc, float* rda, float* rca, int32_t* rs16,
+                                             int64_t bi) {
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float d = amax / 127.0f;
+    const float id = inv_scale(d);
+    uint32_t c4 = 0;
+    int s4 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int c = (int)roundf(v[i] * id);
+        c4 |= ((uint32_t)c & 0xFFu) << (8 * i);
+        s4 += c;
+    }
+    int s16 = s4 + __shfl_xor(s4, 1);
+    s16 += __shfl_xor(s16, 2);               // the sum of this lane's 16-code half
+    const int s16o = __shfl_xor(s16, 4);     // the other half's
+    if (!live) return;
+    const uint16_t h = float_to_half_bits(d);
+    const float dval = half_bits_to_float(h);
+    uint16_t* pc = reinterpret_cast<uint16_t*>(pub + 2 + 4 * sub);  // 2-byte aligned
+    pc[0] = (uint16_t)(c4 & 0xFFFFu);
+    pc[1] = (uint16_t)(c4 >> 16);
+    *reinterpret_cast<uint32_t*>(rc + 4 * sub) = c4;
+    if (sub == 0) {
+        *reinterpret_cast<uint16_t*>(pub) = h;
+        rda[bi] = dval;
+        rca[bi] = dval * (float)(s16 + s16o);
+        rs16[bi] = (int32_t)(((uint32_t)s16 & 0xFFFFu) | ((uint32_t)s16o << 16));
+    }
+}
+
 template <bool FROM_PUBLIC, bool A16>
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x,
                                                   uint8_t* __restrict__ xq, int64_t rows,
@@ -1227,6 +1268,10 @@ struct DotJob {
     uint8_t* xq;      // staged quantisation; FUSED: written by the job's first workgroup (may be NULL)
     int64_t N, K, wbytes;
     int64_t rcodes, rda, rca, rs16;  // offsets of the row-major staging in xq
+    // paired launch with the quantisation of h (MODE_PAIRED_Q): the Q8_0
+    // blocks and row staging of h go to hq (layout act_layout(B, N))
+    uint8_t* hq;
+    int64_t hnb, hrcodes, hrda, hrca, hrs16;
 };
 constexpr int MAX_JOBS = 8;
 // A grouped launch is a 2-D grid: row y of workgroups is job y (as many
@@ -1273,12 +1318,17 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 // h = silu(gate) * up instead of two outputs.
 // MODE_PARTIALS: one GEMV on staged activations whose y is an int32 buffer
 // receiving the exact block partials instead (the test hook).
-constexpr int MODE_GROUP = 0, MODE_SINGLE = 1, MODE_PAIRED = 2, MODE_PARTIALS = 3;
+// MODE_PAIRED_Q: MODE_PAIRED whose workgroups (of 32/GP waves, up to 8)
+// each own one 32-element block of h per activation row and also write its
+// Q8_0 quantisation (public block and row staging) for the down projection
+constexpr int MODE_GROUP = 0, MODE_SINGLE = 1, MODE_PAIRED = 2, MODE_PARTIALS = 3,
+              MODE_PAIRED_Q = 4;
 
 // Q8K: the activations are staged Q8_K (K-quant formats only, not FUSED):
 // each chunk is scaled once per superblock (dot_chunk_q8k).
 template <int FMT, int B, bool FUSED, int MODE, bool Q8K = false>
 __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
+    constexpr bool PAIRED = MODE == MODE_PAIRED || MODE == MODE_PAIRED_Q;
     using F = Fmt<FMT>;
     constexpr int NWD = DotFmt<FMT>::NWD;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -1300,7 +1350,7 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     const int PR = (C + 63) >> 6;  // passes (1 unless C > 64)
     // output rows per unit: G, or G/2 gate/up pairs (lane rows 0..GP-1 take
     // gate rows, GP..2GP-1 the same up rows; the launcher ensures C <= 32)
-    const int GP = MODE == MODE_PAIRED ? G >> 1 : G;
+    const int GP = PAIRED ? G >> 1 : G;
     const int64_t units = C <= 64 ? (N + GP - 1) / GP : N;
     const int lrow = small_div(lane, LPR), lchunk = lane - lrow * LPR;  // this lane's row in the unit, chunk
     if ((int64_t)blockIdx.x * jobs.waves >= units) return;  // surplus workgroup of a smaller job
@@ -1309,13 +1359,13 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
 
     auto chunk_of = [&](int q, int64_t& row, int& c) {
         // lanes past the unit's G rows (64 % C of them) get a row past N: idle
-        if constexpr (MODE == MODE_PAIRED)
+        if constexpr (PAIRED)
             row = lrow < 2 * GP ? u * GP + (lrow < GP ? lrow : lrow - GP) : N;
         else
             row = C <= 64 ? (lrow < G ? u * G + lrow : N) : u;
         c = C <= 64 ? lchunk : 64 * q + lane;
     };
-    const uint8_t* wsrc = MODE == MODE_PAIRED && lrow >= GP ? J.w2 : J.w;
+    const uint8_t* wsrc = PAIRED && lrow >= GP ? J.w2 : J.w;
     auto issue = [&](int q, uint32_t (&r)[NWD]) {
         int64_t row;
         int c;
@@ -1547,7 +1597,7 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
         wave_sync();
     }
     if constexpr (MODE == MODE_PARTIALS) return;
-    if constexpr (MODE == MODE_PAIRED) {
+    if constexpr (PAIRED) {
         // the gate and up sums of each output row meet in LDS; the gate
         // lane writes h = silu(gate) * up
 #pragma unroll
@@ -1559,13 +1609,40 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
             }
         }
         wave_sync();
+        // MODE_PAIRED_Q: this workgroup's 32 rows of h (row 32 blockIdx.x + i
+        // at hb[m][i]) for the quantisation below
+        float* hb = reinterpret_cast<float*>(smem + B * rowb + jobs.waves * B * 256);
 #pragma unroll
         for (int j = 0; j < B; j++) {
             const int t = lane + 64 * j;
             if (t < G * B) {
                 const int m = small_div(t, G), rl = t - m * G;
                 const int64_t orow = u * GP + rl;
-                if (rl < GP && orow < N) J.y[m * N + orow] = swiglu(yacc[j], pbuf[m][GP + rl]);
+                if (rl < GP && orow < N) {
+                    const float hv = swiglu(yacc[j], pbuf[m][GP + rl]);
+                    J.y[m * N + orow] = hv;
+                    if constexpr (MODE == MODE_PAIRED_Q) hb[m * 32 + (int)(orow & 31)] = hv;
+                }
+            }
+        }
+        if constexpr (MODE == MODE_PAIRED_Q) {
+            // every wave of the workgroup is active (N % 32 == 0, 32/GP waves)
+            __syncthreads();
+            if (wv == 0) {
+                // lanes 8 m .. 8 m + 7 quantise row m's block (block index
+                // blockIdx.x of the N/32 blocks of h)
+                const int m = lane >> 3, sub = lane & 7;
+                const bool live = m < B;
+                float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (live) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) v[i] = hb[m * 32 + 4 * sub + i];
+                }
+                const int64_t b = blockIdx.x, hnb = J.hnb, mm = live ? m : 0;
+                uint8_t* hq = J.hq;
+                quant_block8(v, sub, live, hq + (mm * hnb + b) * 34, hq + J.hrcodes + mm * N + 32 * b,
+                             reinterpret_cast<float*>(hq + J.hrda), reinterpret_cast<float*>(hq + J.hrca),
+                             reinterpret_cast<int32_t*>(hq + J.hrs16), mm * hnb + b);
             }
         }
         return;
@@ -1631,9 +1708,20 @@ int launch_dot_kernel(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStre
     return (int)hipGetLastError();
 }
 
+// The formats whose paired launch can also quantise h (the others run the
+// quantisation as a launch of its own)
+constexpr bool pairedq_format(int fmt) {
+    return fmt == T_Q4_0 || fmt == T_Q5_0 || fmt == T_Q8_0 || fmt == T_Q4_K || fmt == T_Q6_K;
+}
+
 template <int FMT, int B, bool FUSED>
 int launch_dot_jobs(const DotJobs& jobs, bool paired, int64_t blocks, size_t shmem,
                     hipStream_t s) {
+    if (paired && jobs.j[0].hq) {
+        if constexpr (pairedq_format(FMT))
+            return launch_dot_kernel<FMT, B, FUSED, MODE_PAIRED_Q>(jobs, blocks, shmem, s);
+        return (int)hipErrorInvalidValue;
+    }
     if (paired) return launch_dot_kernel<FMT, B, FUSED, MODE_PAIRED>(jobs, blocks, shmem, s);
     return jobs.count == 1 ? launch_dot_kernel<FMT, B, FUSED, MODE_SINGLE>(jobs, blocks, shmem, s)
                            : launch_dot_kernel<FMT, B, FUSED, MODE_GROUP>(jobs, blocks, shmem, s);
@@ -1659,7 +1747,7 @@ int launch_dot_rows(const DotJobs& jobs, int64_t rows, bool fused, bool paired, 
 // 1) whose output d[0].y receives h = silu(gate) * up.  waves: 4 or 8 waves
 // per workgroup, or 0 to choose by the grid size.
 int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s,
-               const uint8_t* up = nullptr, int waves = 0) {
+               const uint8_t* up = nullptr, int waves = 0, uint8_t* hq = nullptr) {
     if (count < 1 || count > MAX_JOBS) return (int)hipErrorInvalidValue;
     const bool paired = up != nullptr;
     if (paired && count != 1) return (int)hipErrorInvalidValue;
@@ -1704,9 +1792,18 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
         J.rda = L.rda;
         J.rca = L.rca;
         J.rs16 = L.rs16;
+        J.hq = hq;
+        if (hq) {
+            const ActLayout H = act_layout(rows, d[k].N);
+            J.hnb = H.nb;
+            J.hrcodes = H.rcodes;
+            J.hrda = H.rda;
+            J.hrca = H.rca;
+            J.hrs16 = H.rs16;
+        }
         const int64_t bk = dot_blocks(type, d[k].N, d[k].K, jobs.waves, paired);
         blocks = bk > blocks ? bk : blocks;  // grid x: the largest job
-        const size_t sh = dot_shmem((int)rows, d[k].K, jobs.waves);
+        const size_t sh = dot_shmem((int)rows, d[k].K, jobs.waves) + (hq ? rows * 32 * 4 : 0);
         shmem = sh > shmem ? sh : shmem;
     }
     if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
@@ -1779,9 +1876,8 @@ bool use_dot(int64_t rows, int64_t K) {
 }
 
 // The same quantisation for the row staging alone (the decode GEMV's, B <= 4),
-// 8 lanes per 32-block, 4 elements per lane: coalesced loads, the amax and
-// the code sums by lane shuffles, every lane writing its own 4 codes.  The
-// arithmetic per element is quant_block's, so the bytes are the same.
+// 8 lanes per 32-block, 4 elements per lane: coalesced loads, every lane
+// writing its own 4 codes.
 template <bool A16>
 __global__ __launch_bounds__(256) void k_quantize_row(const float* __restrict__ x,
                                                       uint8_t* __restrict__ xq, int64_t rows,
@@ -1803,38 +1899,9 @@ __global__ __launch_bounds__(256) void k_quantize_row(const float* __restrict__ 
             for (int i = 0; i < 4; i++) v[i] = xb[i];
         }
     }
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    const float d = amax / 127.0f;
-    const float id = inv_scale(d);
-    uint32_t c4 = 0;
-    int s4 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int c = (int)roundf(v[i] * id);
-        c4 |= ((uint32_t)c & 0xFFu) << (8 * i);
-        s4 += c;
-    }
-    int s16 = s4 + __shfl_xor(s4, 1);
-    s16 += __shfl_xor(s16, 2);               // the sum of this lane's 16-code half
-    const int s16o = __shfl_xor(s16, 4);     // the other half's
-    if (!live) return;
-    const uint16_t h = float_to_half_bits(d);
-    const float dval = half_bits_to_float(h);
-    uint8_t* pub = xq + (r * nb + b) * 34;   // 2-byte aligned
-    uint16_t* pc = reinterpret_cast<uint16_t*>(pub + 2 + 4 * sub);
-    pc[0] = (uint16_t)(c4 & 0xFFFFu);
-    pc[1] = (uint16_t)(c4 >> 16);
-    *reinterpret_cast<uint32_t*>(xq + L.rcodes + r * K + 32 * b + 4 * sub) = c4;
-    if (sub == 0) {
-        *reinterpret_cast<uint16_t*>(pub) = h;
-        const int S = s16 + s16o;
-        reinterpret_cast<float*>(xq + L.rda)[r * nb + b] = dval;
-        reinterpret_cast<float*>(xq + L.rca)[r * nb + b] = dval * (float)S;
-        reinterpret_cast<int32_t*>(xq + L.rs16)[r * nb + b] =
-            (int32_t)(((uint32_t)s16 & 0xFFFFu) | ((uint32_t)s16o << 16));
-    }
+    quant_block8(v, sub, live, xq + (r * nb + b) * 34, xq + L.rcodes + r * K + 32 * b,
+                 reinterpret_cast<float*>(xq + L.rda), reinterpret_cast<float*>(xq + L.rca),
+                 reinterpret_cast<int32_t*>(xq + L.rs16), r * nb + b);
 }
 
 }  // namespace
@@ -2088,8 +2155,23 @@ bool gateup_is_one_launch(int64_t rows, int64_t K) {
     return use_dot(rows, K) && C <= 32;  // at least one gate/up row pair per wave
 }
 
+// The paired launch also quantises h when its workgroups, of 32/GP waves,
+// cover whole 32-element blocks of h: GP (gate/up row pairs per wave)
+// divides 32 and is at least 4 (workgroups of up to 8 waves: with 16, at
+// K = 4096, one workgroup fits a CU and the launch took 22.0 us against 18.5
+// for the plain pair plus about 3 for the quantisation launch), N is whole
+// blocks, and the down projection reads the row staging.
+bool gateup_quantises_h(int type, int64_t rows, int64_t N, int64_t K) {
+    if (!gateup_is_one_launch(rows, K) || N % 32 || staging_for(rows, N) != ST_ROW) return false;
+    if (!(type == T_Q4_0 || type == T_Q5_0 || type == T_Q8_0 || type == T_Q4_K || type == T_Q6_K))
+        return false;
+    const int C = (int)((K / 32 + 7) / 8), GP = (64 / C) >> 1;
+    return GP >= 4 && 32 % GP == 0;
+}
+
 int launch_gateup(int type, const uint8_t* wg, const uint8_t* wu, int64_t N, int64_t K,
-                  const float* x, uint8_t* xq, int64_t rows, float* h, hipStream_t s) {
+                  const float* x, uint8_t* xq, int64_t rows, float* h, hipStream_t s,
+                  uint8_t* hq) {
     if (gateup_is_one_launch(rows, K)) {
         // one launch: each wave takes matching gate and up rows (the
         // quantisation fused as in qmv_launch, with the same rule for when
@@ -2101,7 +2183,13 @@ int launch_gateup(int type, const uint8_t* wg, const uint8_t* wu, int64_t N, int
             x = nullptr;
         }
         const GemvDesc d{wg, N, K, x, xq, h};
-        return launch_dot(type, &d, 1, rows, s, wu);
+        if (hq && gateup_quantises_h(type, rows, N, K)) {
+            const int C = (int)((K / 32 + 7) / 8), GP = (64 / C) >> 1;
+            return launch_dot(type, &d, 1, rows, s, wu, 32 / GP, hq);
+        }
+        const int rc = launch_dot(type, &d, 1, rows, s, wu);
+        if (rc || !hq) return rc;
+        return launch_quantize(h, hq, rows, N, staging_for(rows, N), s);
     }
     // otherwise: quantise once, gate and up into the scratch after the
     // activation copy, then the SwiGLU
@@ -2114,7 +2202,8 @@ int launch_gateup(int type, const uint8_t* wg, const uint8_t* wu, int64_t N, int
     if ((rc = launch_qmv(type, wu, N, K, nullptr, xq, rows, ut, s))) return rc;
     const int64_t n = rows * N;
     hipLaunchKernelGGL(k_swiglu, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gt, ut, h, n);
-    return (int)hipGetLastError();
+    if ((rc = (int)hipGetLastError()) || !hq) return rc;
+    return launch_quantize(h, hq, rows, N, staging_for(rows, N), s);
 }
 
 int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,

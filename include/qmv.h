@@ -177,6 +177,23 @@ int qmv_launch_gateup_swiglu(int type, const void* w_gate, const void* w_up, int
                              int64_t K, const float* x, int64_t B, void* xq, float* h,
                              void* stream);
 
+/* qmv_launch_gateup_swiglu that also leaves h quantised for the down
+ * projection: hq (qmv_act_bytes(B, N) bytes, 16-byte aligned, not
+ * overlapping the other buffers) receives exactly what quantize_act_q8_0(h,
+ * hq, B, N) would write, so that qmv_launch(type_down, w_down, N_down, N,
+ * NULL, B, hq, y, stream) can follow with no quantisation launch of its own.
+ * h is still written.  N must be whole 32-element blocks (32 <= N <= 2^20,
+ * N % 32 == 0; else QMV_EINVAL_SHAPE).  When each workgroup of the paired
+ * launch can own whole 32-row blocks of h (B <= 4, Q4_0 / Q5_0 / Q8_0 / Q4_K
+ * / Q6_K weights, K such that a wave takes 4, 8 or 16 gate/up row pairs,
+ * e.g. K = 256 .. 2048 or the 896 of the pages' Qwen2.5-0.5B) the
+ * quantisation runs in that same launch: the workgroup gathers its 32 values
+ * of h in LDS and quantises them; otherwise a quantisation launch follows.  The SwiGLU chain of a decode step in the
+ * pages' architecture table ("Models and formats") then takes two launches. */
+int qmv_launch_gateup_swiglu_q8(int type, const void* w_gate, const void* w_up, int64_t N,
+                                int64_t K, const float* x, int64_t B, void* xq, float* h,
+                                void* hq, void* stream);
+
 /* Prefill GEMM (MatMul): y[M][N] = x[M][K] * W^T for any M >= 1.  Prefill
  * is the arithmetic-bound phase ("Architecture", bench transcript): for
  * M > 16 the integer block dots run on the matrix cores (f16 MFMA, which is

@@ -84,6 +84,13 @@ int main() {
           !strcmp(g_last.what, "qmv") && g_last.xq != nullptr && g_last.xq != XQ);
     CHECK(qmv_launch_gateup_swiglu(QMV_Q4_0, W, W + 256, 48, 896, X, 2, XQ, Y, nullptr) == QMV_OK &&
           !strcmp(g_last.what, "gateup") && g_last.N == 48 && g_last.rows == 2);
+    CHECK(qmv_launch_gateup_swiglu_q8(QMV_Q4_K, W, W + 256, 64, 4096, X, 1, XQ, Y, XQ + 4096,
+                                      nullptr) == QMV_OK &&
+          !strcmp(g_last.what, "gateup_q8") && g_last.hq == XQ + 4096);
+    CHECK(qmv_launch_gateup_swiglu_q8(QMV_Q4_K, W, W + 256, 48 + 8, 4096, X, 1, XQ, Y, XQ + 4096,
+                                      nullptr) == QMV_EINVAL_SHAPE);
+    CHECK(qmv_launch_gateup_swiglu_q8(QMV_Q4_K, W, W + 256, 64, 4096, X, 1, XQ, Y, nullptr,
+                                      nullptr) == QMV_EINVAL_PTR);
     {
         qmv_gemv gv[3] = {{W, 16, 32, X, XQ, Y}, {W, 24, 64, X, nullptr, Y}, {W, 8, 96, X, nullptr, Y}};
         CHECK(qmv_launch_group(QMV_Q8_0, 2, gv, 3, nullptr) == QMV_OK &&

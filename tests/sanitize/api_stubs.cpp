@@ -78,8 +78,9 @@ int launch_qmm(int type, const uint8_t*, int64_t N, int64_t K, const float* x, u
     return record("qmm", type, N, K, rows, x, xq, y);
 }
 int launch_gateup(int type, const uint8_t*, const uint8_t*, int64_t N, int64_t K, const float* x,
-                  uint8_t* xq, int64_t rows, float* h, hipStream_t) {
-    return record("gateup", type, N, K, rows, x, xq, h);
+                  uint8_t* xq, int64_t rows, float* h, hipStream_t, uint8_t* hq) {
+    g_last.hq = hq;
+    return record(hq ? "gateup_q8" : "gateup", type, N, K, rows, x, xq, h);
 }
 int launch_quantize_q8k(const float* x, uint8_t* xq, int64_t rows, int64_t K, hipStream_t) {
     return record("quantize_q8k", 0, 0, K, rows, x, xq, nullptr);

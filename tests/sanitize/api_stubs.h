@@ -13,5 +13,6 @@ struct LastCall {
     const void* xq = nullptr;
     const void* y = nullptr;
     int group_count = 0;
+    const void* hq = nullptr;
 };
 extern LastCall g_last;

@@ -157,6 +157,17 @@ def test_prepare_refusals_and_size():
     assert p(g.Q4_1, FAKE, 16, 256, FAKE, 1, FAKE, None) == -1
 
 
+def test_gateup_q8_refusals():
+    f = g.lib().qmv_launch_gateup_swiglu_q8
+    assert f(4, FAKE, FAKE, 64, 4096, FAKE, 1, FAKE, FAKE, FAKE, None) == -1
+    assert f(g.Q4_K, FAKE, FAKE, 64 + 16, 4096, FAKE, 1, FAKE, FAKE, FAKE, None) == -2  # N % 32
+    assert f(g.Q4_K, FAKE, FAKE, 16, 4096, FAKE, 1, FAKE, FAKE, FAKE, None) == -2       # N < 32
+    assert f(g.Q4_K, FAKE, FAKE, 64, 4096, FAKE, 17, FAKE, FAKE, FAKE, None) == -2
+    assert f(g.Q4_K, FAKE, FAKE, 64, 4096, FAKE, 1, FAKE, FAKE, None, None) == -3       # hq NULL
+    assert f(g.Q4_K, FAKE, FAKE, 64, 4096, FAKE, 1, FAKE, FAKE, FAKE + 4, None) == -3   # hq align
+    assert f(g.Q4_K, FAKE, FAKE + 8, 64, 4096, FAKE, 1, FAKE, FAKE, FAKE, None) == -3
+
+
 def test_noalloc_refusals():
     L = g.lib()
     # the fixed scratch admits every K <= 65536 at B = 16 (and no more at K = 2^17)

@@ -119,3 +119,45 @@ def test_ffn_chain(g, fmt, N, K, B):
     y64, A = oracle.matmul_f64(fdown, wd, K, N, xq_o, B)
     assert_tol(y.cpu().numpy(), y64, A, what="ffn down")
     assert_bitwise(y.cpu().numpy(), oracle.matmul_canon_f32(fdown, wd, K, N, xq_o, B), "ffn f32")
+
+
+# (fmt, N, K, B): the paired launch quantises h itself for K = 2048 (8-wave
+# workgroups), 896 and 1024 (4 waves), B <= 4; it falls back to a
+# quantisation launch for K = 4096 (2 pairs per wave would need 16 waves),
+# Q4_1 (format), K = 8192 (1 pair per wave), K = 4864 (3 rows per wave) and
+# B > 4.
+Q8_CASES = [
+    (synth.Q4_K, 14336, 4096, 1), (synth.Q4_K, 96, 4096, 4), (synth.Q6_K, 64, 2048, 2),
+    (synth.Q4_K, 4864, 2048, 1), (synth.Q4_K, 256, 512, 4),
+    (synth.Q4_0, 4864, 896, 1), (synth.Q8_0, 160, 1024, 3), (synth.Q5_0, 32, 896, 4),
+    (synth.Q4_1, 64, 896, 1), (synth.Q4_K, 64, 8192, 1), (synth.Q8_0, 96, 4864, 2),
+    (synth.Q4_0, 128, 896, 5), (synth.Q4_K, 256, 4096, 16),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,B", Q8_CASES)
+def test_gateup_swiglu_q8_leaves_h_quantised(g, fmt, N, K, B):
+    """h bit-identical to qmv_launch_gateup_swiglu; hq holds exactly what
+    quantize_act_q8_0(h) writes (the public blocks against the oracle, the
+    staging through the down GEMV: y from hq equals y from h)."""
+    wg, wu = _pair(fmt, N, K, 600 + N + K)
+    fdown = synth.Q6_K if N % 256 == 0 else synth.Q4_0   # down: K outputs of N inputs
+    wd, _ = synth.weights(fdown, K, N, 602, dscale=0.02)
+    x = synth.activations(B, K, 603 + B)
+    xd, wgd, wud = dev(x), dev(wg), dev(wu)
+    print(f"gateup q8 fmt={fmt} N={N} K={K} B={B}", flush=True)
+    h, hq = g.gateup_swiglu_q8(fmt, wgd, wud, N, K, x=xd)
+    h1 = g.gateup_swiglu(fmt, wgd, wud, N, K, x=xd)
+    torch.cuda.synchronize()
+    h_o = _oracle_h(fmt, wg, wu, N, K, x)
+    assert_bitwise(h.cpu().numpy(), h_o, "h")
+    assert_bitwise(h1.cpu().numpy(), h_o, "h without hq")
+    xq_o = oracle.quantize_act(h_o)
+    assert_bitwise(hq.cpu().numpy()[: xq_o.size], xq_o, "Q8_0 blocks of h")
+    wdd = dev(wd)
+    y_q = g.matvec(fdown, wdd, K, N, xq=hq, B=B)
+    y_h = g.matvec(fdown, wdd, K, N, x=h)
+    torch.cuda.synchronize()
+    assert_bitwise(y_q.cpu().numpy(), y_h.cpu().numpy(), "down from hq vs from h")
+    assert_bitwise(y_q.cpu().numpy(), oracle.matmul_canon_f32(fdown, wd, K, N, xq_o, B),
+                   "down f32 order")
