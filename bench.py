@@ -57,7 +57,7 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 F16_PEAK_TFLOPS = 2500.0       # MI355X dense f16 MFMA, vendor figure
 CSRC = os.path.join(ROOT, "gguf_quantized_matvec_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-MAX_HOST_THREADS = 16          # the host CPUs the GPU machine allots to one GPU
+MAX_HOST_THREADS = 16          # one GPU's share of the host CPUs (16 per GPU)
 
 Q4_0, Q8_0, Q4_K, Q6_K = 2, 8, 12, 14
 # (name, fmt, N, K) of one 8B-class decoder layer's projections
@@ -80,7 +80,7 @@ STAGE_KERNEL_WHAT = {"A_qkv": "grouped GEMV q, k, v (Q4_K)", "B_o": "GEMV o (Q4_
 
 def kernel_src_sha() -> str:
     h = hashlib.sha256()
-    for f in ("qmv_kernels.hip", "qmm_kernels.hip"):
+    for f in ("qmv_kernels.hip", "qmm_kernels.hip", "qmv_internal.h"):
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -333,11 +333,12 @@ def matrix_us(torch, g, synth, fmt, N, K, rows, seed, ds, rotate_bytes, n_min=20
         _check(g, fn(fmt, copies[i % R].data_ptr(), N, K, None, rows, xq.data_ptr(),
                      y.data_ptr(), torch.cuda.current_stream().cuda_stream), "matrix")
     launch(0)
-    n = max(R, n_min) if rows <= 16 else max(min(R, 10), 5)
+    n = max(R, n_min) if rows <= 16 else max(R, 5)
     us = graph_launch_us(torch, launch, n)
+    touched = min(n, R) * int(wt.numel())
     del copies, wt, x, xq, y
     torch.cuda.empty_cache()
-    return us, nbytes, R
+    return us, nbytes, (R, touched)
 
 
 def gemv_row(us, nbytes, B):
@@ -595,7 +596,7 @@ def cpu_baseline(synth, seconds):
                        f"quantisations, 7 products in f64, SwiGLU) in {dt:.1f} s with rows split "
                        f"over {threads} threads; tok/s {steps / dt:.3f}"),
             "host": {**info, "threads_used": threads,
-                     "why_threads": "at most 16: the host CPUs a GPU box allots to one GPU"},
+                     "why_threads": "at most 16: one GPU's share of the host CPUs"},
             "single_thread_b1": single}
 
 
@@ -663,10 +664,13 @@ def suite(torch, g, synth, rotate_bytes):
         ci = list(synth.WORKLOADS).index(wl)
         for mi, (fmt, N, K, ds) in enumerate(spec["mats"]):
             for B in spec["batches"]:
-                us, nb, R = matrix_us(torch, g, synth, fmt, N, K, B, synth.seed_for(ci, mi), ds,
-                                      rotate_bytes)
+                us, nb, (R, touched) = matrix_us(torch, g, synth, fmt, N, K, B,
+                                                 synth.seed_for(ci, mi), ds, rotate_bytes)
+                # weights the timed launches read: past the 256 MB last-level
+                # cache they stream from HBM, else they may be served from it
                 row = {"workload": wl, "fmt": synth.NAMES[fmt], "N": N, "K": K, "rows": B,
-                       "rotated_copies": R}
+                       "rotated_copies": R, "weights_read_MB": round(touched / 1e6, 1),
+                       "weights_from": "HBM" if touched > 512e6 else "last-level cache"}
                 row.update(gemv_row(us, nb, B) if B <= 16 else gemm_row(us, B, N, K))
                 res.append(row)
                 print(json.dumps({"suite_row": row}), file=sys.stderr, flush=True)
