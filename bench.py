@@ -115,8 +115,14 @@ def graph_launch_us(torch, launch, n, reps=3):
     execution time plus the short dispatch gap between consecutive graph
     nodes; the median over `reps` replays is returned."""
     G = GraphSteps(torch, launch, n)
-    G.replay()                               # warm
-    torch.cuda.synchronize()
+    # warm: replays for at least 30 ms (the first milliseconds of a long
+    # run are measurably slower than the rest)
+    t0 = time.perf_counter()
+    while True:
+        G.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= 0.03:
+            break
     s = torch.cuda.current_stream()
     out = []
     for _ in range(reps):
