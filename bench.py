@@ -462,6 +462,7 @@ def ceilings(torch):
     lib = ctypes.CDLL(os.path.join(ROOT, "gguf_quantized_matvec_amd", "libqmv_ceilings.so"))
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.qmv_ceil_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.qmv_ceil_stream_read_nt.argtypes = [P, ctypes.c_size_t, P, P]
     for f in ("qmv_ceil_mfma_i8", "qmv_ceil_mfma_f16", "qmv_ceil_epilogue"):
         getattr(lib, f).argtypes = [P, I, I, P]
     s = lambda: torch.cuda.current_stream().cuda_stream
@@ -482,9 +483,23 @@ def ceilings(torch):
 
     nbytes = 1 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
-    sink = torch.empty(nbytes // 16 // 16, dtype=torch.int32, device="cuda")
+    sink = torch.empty(nbytes // 128, dtype=torch.int32, device="cuda")  # the larger of the two sinks
     t = timed(lambda: lib.qmv_ceil_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), s()))
     out = {"stream_read_GBs": round(nbytes / t / 1e9, 1)}
+    t = timed(lambda: lib.qmv_ceil_stream_read_nt(buf.data_ptr(), nbytes, sink.data_ptr(), s()))
+    out["stream_read_nt_GBs"] = round(nbytes / t / 1e9, 1)
+    # the nontemporal read at the size of the headline's dominant launch
+    # (66.1 MB), rotated over the 16 slices of the buffer so none is cached
+    part = (66138368 // 32768) * 32768
+    copies = nbytes // part
+
+    def rotated():
+        for i in range(32):
+            lib.qmv_ceil_stream_read_nt(buf.data_ptr() + (i % copies) * part, part,
+                                        sink.data_ptr(), s())
+    t = timed(rotated) / 32
+    out["stream_read_nt_66MB_us"] = round(t * 1e6, 2)
+    out["stream_read_nt_66MB_GBs"] = round(part / t / 1e9, 1)
     del buf, sink
     blocks, iters = 256 * 8, 2000
     o = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
@@ -498,7 +513,8 @@ def ceilings(torch):
     # one fma per output and 32-element block = 32 int8 MACs = 64 int8 ops
     out["epilogue_bound_int8_TOPS"] = round(fma_s * 64 / 1e12, 1)
     out["how"] = ("libqmv_ceilings.so (qmv_ceilings.hip): a 1 GiB read with 16-byte loads, 16 "
-                  "in flight per thread; 2048 workgroups x 4 waves of 4 independent MFMA chains; "
+                  "in flight per thread, and with the nontemporal hint, 8 in flight per thread "
+                  "(also 32 back-to-back 66.1 MB reads over rotated slices, time per read); 2048 workgroups x 4 waves of 4 independent MFMA chains; "
                   "16 f32 fma chains per thread; best of 5 launches by HIP events")
     return out
 

@@ -4,7 +4,8 @@
 // measured ceilings too.  Not part of the product path.
 //
 //   * a streaming read of HBM (16-byte loads, every load of a wave issued
-//     before any is used, the same way the decode GEMV loads its weights);
+//     before any is used), plain and with the nontemporal hint that the
+//     decode GEMVs put on their weight loads;
 //   * loops of independent int8 and f16 MFMAs with operands in registers
 //     (v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_f16);
 //   * the prefill GEMM's scale epilogue alone: chains of f32 fma, one per
@@ -24,21 +25,38 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int READ_LOADS = 16;  // 16-byte loads per thread, all in flight together
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-// Workgroup b reads bytes [b*64K, (b+1)*64K): thread t loads the 16-byte
-// pieces t, t+256, ..., t+15*256 (each load instruction of a wave covers
-// 1 KB contiguously), then xors them into one word.
+// Workgroup b reads bytes [b*256*L*16, (b+1)*256*L*16): thread t loads the
+// 16-byte pieces t, t+256, ..., t+(L-1)*256 (each load instruction of a wave
+// covers 1 KB contiguously), all in flight together, then xors them into one
+// word.  NT: the loads carry the nontemporal hint, as the weight loads of
+// the decode GEMVs do.
+template <int L, bool NT>
 __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ buf,
                                                      uint32_t* __restrict__ sink) {
-    const uint4* p = buf + (size_t)blockIdx.x * 256 * READ_LOADS + threadIdx.x;
-    uint4 v[READ_LOADS];
+    const uint4* p = buf + (size_t)blockIdx.x * 256 * L + threadIdx.x;
+    v4u v[L];
 #pragma unroll
-    for (int i = 0; i < READ_LOADS; i++) v[i] = p[256 * i];
+    for (int i = 0; i < L; i++) {
+        const v4u* q = reinterpret_cast<const v4u*>(p + 256 * i);
+        v[i] = NT ? __builtin_nontemporal_load(q) : *q;
+    }
     uint32_t acc = 0;
 #pragma unroll
-    for (int i = 0; i < READ_LOADS; i++) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    for (int i = 0; i < L; i++) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
     sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+template <int L, bool NT>
+int stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+    const size_t per_block = 256 * L * 16;
+    if (!buf || !sink || bytes < per_block || bytes % per_block ||
+        (reinterpret_cast<uintptr_t>(buf) & 15) || bytes / per_block > 0x7fffffff)
+        return -2;
+    hipLaunchKernelGGL((k_stream_read<L, NT>), dim3((unsigned)(bytes / per_block)), dim3(256), 0,
+                       stream, static_cast<const uint4*>(buf), sink);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 // Four independent accumulator chains per wave, so that issue, not the
@@ -107,13 +125,10 @@ int launched() { return hipGetLastError() == hipSuccess ? 0 : -4; }
 extern "C" {
 
 int qmv_ceil_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
-    const size_t per_block = 256 * READ_LOADS * 16;
-    if (!buf || !sink || bytes < per_block || bytes % per_block ||
-        (reinterpret_cast<uintptr_t>(buf) & 15) || bytes / per_block > 0x7fffffff)
-        return -2;
-    hipLaunchKernelGGL(k_stream_read, dim3((unsigned)(bytes / per_block)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf), sink);
-    return launched();
+    return stream_read<16, false>(buf, bytes, sink, static_cast<hipStream_t>(stream));
+}
+int qmv_ceil_stream_read_nt(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    return stream_read<8, true>(buf, bytes, sink, static_cast<hipStream_t>(stream));
 }
 
 int qmv_ceil_mfma_i8(int32_t* out, int blocks, int iters, void* stream) {

@@ -44,6 +44,9 @@ template <int FMT> constexpr bool has_min_term() {
 constexpr int DOT_MAX_ROWS = 4;
 // ... as long as their activation rows fit in a workgroup's LDS.
 constexpr int DOT_MAX_ACT_LDS = 96 * 1024;
+// On the Q8_K path, batches from this size up to 16 rows run the batched
+// MFMA kernel (k_bdot8k), smaller ones the lane-per-chunk kernel.
+constexpr int BDOT_MIN_ROWS = 5;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -799,6 +802,218 @@ __global__ __launch_bounds__(512) void k_qmv_split(const uint8_t* __restrict__ w
     if (!PARTIALS && threadIdx.x < 16 * Bg) {
         const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
         if (n < t.nrows) y[(16 * g + m) * N + n0 + n] = yacc;
+    }
+}
+
+// ------------------------------------- batched decode on the Q8_K path ----
+// 5..16 activation rows against Q4_K / Q6_K weights with Q8_K activations
+// (one f32 scale per 256 activations): a workgroup owns a tile of 16 weight
+// rows, and its KS waves take the tile's superblocks round-robin.  A wave
+// streams the 16 rows' bytes of its superblock as 16-byte pieces into its LDS
+// slice (as k_qmv_split does), then lane (nn = l%16, kg = l/16) takes weight
+// row nn's codes 8kg..8kg+7 of each 32-element block and activation row
+// l%16's, one v_mfma_i32_16x16x32_i8 per block (Q6_K: two, one per 16-element
+// sub-block, the other half's codes zeroed); result element i is activation
+// row 4kg+i.  The sub-block scales multiply the exact int32 block sums, so a
+// superblock reduces to the integers of the Q8_K order and is scaled in f32
+// once, not once per 32 elements as on the Q8_0 path.  Q4_K's min term
+// Q = sum_j m_j S_j runs as two more MFMAs: the row's eight 32-code sums S_j
+// as two int8 digits (S = 64 hi + lo, lo in 0..63) against the eight 6-bit
+// mins, in k-group 0 only.  After each round of KS superblocks their results
+// are added to y in ascending superblock order through LDS.  PART: the
+// integer partials are written instead (test hook).
+struct ActRegsK {
+    uint64_t a[8];  // activation row l%16: codes 8kg..8kg+7 of each 32-element block
+    float da[4];    // Q8_K d of activation rows 4kg+i (0 past the batch)
+    uint4 s16[2];   // Q4_K, k-group 0: row l%16's eight pairs of 16-code sums
+};
+
+template <int FMT>
+__device__ __forceinline__ void fetch_act_k(const uint8_t* xq, const ActLayoutK& L, int64_t K,
+                                            int64_t row0, int Bg, int c, int lane, ActRegsK& r) {
+    const int m = lane & 15, kg = lane >> 4;
+    const bool live = m < Bg;
+    const uint8_t* ar = xq + L.rcodes + (row0 + (live ? m : 0)) * K + 256 * c + 8 * kg;
+#pragma unroll
+    for (int j = 0; j < 8; j++) r.a[j] = live ? ld<uint64_t>(ar + 32 * j) : 0ull;
+    const float* rda = reinterpret_cast<const float*>(xq + L.rda);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int mr = 4 * kg + i;
+        r.da[i] = mr < Bg ? rda[(row0 + mr) * L.nb + 8 * c] : 0.0f;
+    }
+    if constexpr (FMT == T_Q4_K) {
+        r.s16[0] = r.s16[1] = make_uint4(0, 0, 0, 0);
+        if (kg == 0 && live) {
+            const uint4* sp = reinterpret_cast<const uint4*>(xq + L.rs16) + ((row0 + m) * L.nb + 8 * c) / 4;
+            r.s16[0] = sp[0];
+            r.s16[1] = sp[1];
+        }
+    }
+}
+
+// The integer partials of one superblock (rb: weight row nn's bytes of it in
+// LDS) for activation rows 4kg+i: Q4_K Pi = sum_j sc_j sum q a and
+// Qi = sum_j m_j S_j; Q6_K Pi = sum_j s_j sum (q - 32) a.  dw, dmw: the
+// superblock's fp16 d and dmin, widened.
+template <int FMT>
+__device__ __forceinline__ void superblock_k(const uint8_t* rb, const ActRegsK& A, int kg,
+                                             int (&Pi)[4], int (&Qi)[4], float& dw, float& dmw) {
+    const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; i++) Pi[i] = Qi[i] = 0;
+    if constexpr (FMT == T_Q4_K) {
+        const uint4 hdr = ld<uint4>(rb);
+        uint64_t q[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) q[j] = ld<uint64_t>(rb + 16 + 32 * j + 8 * kg);
+        dw = half_bits_to_float((uint16_t)(hdr.x & 0xFFFF));
+        dmw = half_bits_to_float((uint16_t)(hdr.x >> 16));
+        const uint32_t s12[3] = {hdr.y, hdr.z, hdr.w};
+        const uint8_t* sb = reinterpret_cast<const uint8_t*>(s12);
+        uint64_t mins = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            int sc, mn;
+            if (j < 4) {
+                sc = sb[j] & 63;
+                mn = sb[j + 4] & 63;
+            } else {
+                sc = (sb[j + 4] & 15) | ((sb[j - 4] >> 6) << 4);
+                mn = (sb[j + 4] >> 4) | ((sb[j] >> 6) << 4);
+            }
+            mins |= (uint64_t)mn << (8 * j);
+            uint64_t raw = q[j >> 1];
+            if (j & 1) raw >>= 4;
+            const v4i acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                (long)A.a[j], (long)(raw & 0x0F0F0F0F0F0F0F0Full), zero, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; i++) Pi[i] = __mul24(sc, acc[i]) + Pi[i];
+        }
+        // min term: k-group 0 carries S_j (two digits) against m_j, j = 0..7
+        uint64_t slo = 0, shi = 0;
+        const uint32_t sv[8] = {A.s16[0].x, A.s16[0].y, A.s16[0].z, A.s16[0].w,
+                                A.s16[1].x, A.s16[1].y, A.s16[1].z, A.s16[1].w};
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int S = (int)(int16_t)(sv[j] & 0xFFFFu) + ((int)sv[j] >> 16);  // |S| <= 4096
+            slo |= (uint64_t)(uint32_t)(S & 63) << (8 * j);
+            shi |= (uint64_t)(uint32_t)((S >> 6) & 0xFF) << (8 * j);
+        }
+        const long bm = kg == 0 ? (long)mins : 0;
+        const v4i ql = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)slo, bm, zero, 0, 0, 0);
+        const v4i qh = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)shi, bm, zero, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; i++) Qi[i] = ql[i] + 64 * qh[i];
+    } else {
+        uint64_t q[4], qh[2];
+#pragma unroll
+        for (int j = 0; j < 4; j++) q[j] = ld<uint64_t>(rb + 32 * j + 8 * kg);
+        qh[0] = ld<uint64_t>(rb + 128 + 8 * kg);
+        qh[1] = ld<uint64_t>(rb + 160 + 8 * kg);
+        const uint4 scv = ld<uint4>(rb + 192);
+        dw = half_bits_to_float(ld<uint16_t>(rb + 208));
+        dmw = 0.0f;
+        const uint32_t sc6[4] = {scv.x, scv.y, scv.z, scv.w};
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int h = j >> 2, kq = j & 3;
+            uint64_t ql = q[2 * h + (kq & 1)];
+            if (kq & 2) ql >>= 4;
+            const uint64_t q6 = (ql & 0x0F0F0F0F0F0F0F0Full) |
+                                (((qh[h] >> (2 * kq)) & 0x0303030303030303ull) << 4);
+            const uint64_t wc = bytes_minus(q6, 0x2020202020202020ull);
+            const uint32_t sw = sc6[j >> 1] >> (16 * (j & 1));
+            const int s0 = (int8_t)(sw & 0xFF), s1 = (int8_t)((sw >> 8) & 0xFF);
+            const long lo = kg < 2 ? (long)wc : 0, hi = kg < 2 ? 0 : (long)wc;
+            const v4i acc0 = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)A.a[j], lo, zero, 0, 0, 0);
+            const v4i acc1 = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)A.a[j], hi, zero, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; i++) Pi[i] = __mul24(s0, acc0[i]) + __mul24(s1, acc1[i]) + Pi[i];
+        }
+    }
+}
+
+template <int FMT, bool PART>
+__global__ __launch_bounds__(512) void k_bdot8k(const uint8_t* __restrict__ w, int64_t wbytes,
+                                                int64_t N, int64_t K,
+                                                const uint8_t* __restrict__ xq, ActLayoutK L,
+                                                int64_t rows, float* __restrict__ y,
+                                                int32_t* __restrict__ P) {
+    using F = Fmt<FMT>;
+    constexpr int NP = pieces_per_lane<FMT>();
+    constexpr int SL = 16 * span_stride<FMT>();  // a wave's weight slice
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6), KS = blockDim.x >> 6;
+    uint8_t* wl = smem + wv * SL;
+    float* pbuf = reinterpret_cast<float*>(smem + KS * SL);
+    const int64_t tile = blockIdx.x, n0 = tile * 16;
+    const int Bg = (int)(rows < 16 ? rows : 16);
+    const int C = (int)(K >> 8);
+    const int64_t Rl = (int64_t)C * F::BB;
+    const uint32_t R = (uint32_t)Rl;
+    const int nn = lane & 15, kg = lane >> 4;
+    const TileRef t = make_tile(w, wbytes, N, Rl, tile);
+
+    float yacc = 0.0f;
+    uint4 reg[NP];
+    ActRegsK nxt;
+    if (wv < C) {
+        fetch_chunk<FMT>(t, R, wv, 8, lane, reg);
+        fetch_act_k<FMT>(xq, L, K, 0, Bg, wv, lane, nxt);
+    }
+    for (int r0 = 0; r0 < C; r0 += KS) {
+        const int c = r0 + wv;
+        if (c < C) {
+            stage_chunk<FMT>(wl, lane, reg);
+            const ActRegsK cur = nxt;
+            wave_sync();
+            const int cn = c + KS;
+            if (cn < C) {
+                fetch_chunk<FMT>(t, R, cn, 8, lane, reg);
+                fetch_act_k<FMT>(xq, L, K, 0, Bg, cn, lane, nxt);
+            }
+            const uint8_t* rb = wl + nn * span_stride<FMT>() + ((nn * R + c * F::CB) & 15);
+            int Pi[4], Qi[4];
+            float dw, dmw;
+            superblock_k<FMT>(rb, cur, kg, Pi, Qi, dw, dmw);
+            wave_sync();  // the slice is read: the next round may overwrite it
+            const int64_t n = n0 + nn;
+            if constexpr (PART) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int m = 4 * kg + i;
+                    if (m < Bg && n < N) {
+                        const int64_t o = ((int64_t)m * N + n) * C + c;
+                        if constexpr (FMT == T_Q4_K) {
+                            P[2 * o] = Pi[i];
+                            P[2 * o + 1] = Qi[i];
+                        } else {
+                            P[o] = Pi[i];
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int m = 4 * kg + i;
+                    float p = fmaf((float)Pi[i], dw * cur.da[i], 0.0f);
+                    if constexpr (FMT == T_Q4_K) p = fmaf(-(float)Qi[i], dmw * cur.da[i], p);
+                    if (m < Bg) pbuf[wv * 256 + m * 16 + nn] = p;
+                }
+            }
+        }
+        if constexpr (!PART) {
+            __syncthreads();
+            const int nact = C - r0 < KS ? C - r0 : KS;
+            if (threadIdx.x < 16 * Bg)
+                for (int w2 = 0; w2 < nact; w2++) yacc = yacc + pbuf[w2 * 256 + threadIdx.x];
+            __syncthreads();
+        }
+    }
+    if (!PART && threadIdx.x < 16 * Bg) {
+        const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
+        if (n < t.nrows) y[(int64_t)m * N + n0 + n] = yacc;
     }
 }
 
@@ -2098,6 +2313,42 @@ int launch_dot_q8k_t(const DotJobs& jobs, int64_t rows, int64_t blocks, size_t s
 }
 }  // namespace
 
+// The batched Q8_K kernel for BDOT_MIN_ROWS..16 activation rows: one
+// workgroup per 16-row weight tile, KS waves sharing its superblocks (more
+// waves when the tiles alone would leave the chip short of work; at least
+// enough threads for the in-order combine of 16 x rows outputs).
+int launch_bdot_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
+                    int64_t rows, float* y, int32_t* P, hipStream_t s) {
+    const int64_t tiles = (N + 15) / 16;
+    const int C = (int)(K / 256);
+    if (tiles > INT32_MAX || rows < 1 || rows > 16) return (int)hipErrorInvalidValue;
+    int KS = 1;
+    while (KS < 8 && tiles * KS < 4096 && KS * 2 <= C) KS *= 2;
+    const int need = (int)((16 * rows + 63) / 64);
+    if (!P && KS < need) KS = need;
+    const ActLayoutK L = act_layout_q8k(rows, K);
+    const int64_t wbytes = N * row_bytes(type, K);
+    const size_t pb = P ? 0 : (size_t)KS * 1024;
+    if (type == T_Q4_K) {
+        const size_t sh = (size_t)KS * 16 * span_stride<T_Q4_K>() + pb;
+        if (P)
+            hipLaunchKernelGGL((k_bdot8k<T_Q4_K, true>), dim3((unsigned)tiles), dim3(64 * KS), sh,
+                               s, w, wbytes, N, K, xq, L, rows, y, P);
+        else
+            hipLaunchKernelGGL((k_bdot8k<T_Q4_K, false>), dim3((unsigned)tiles), dim3(64 * KS), sh,
+                               s, w, wbytes, N, K, xq, L, rows, y, P);
+    } else {
+        const size_t sh = (size_t)KS * 16 * span_stride<T_Q6_K>() + pb;
+        if (P)
+            hipLaunchKernelGGL((k_bdot8k<T_Q6_K, true>), dim3((unsigned)tiles), dim3(64 * KS), sh,
+                               s, w, wbytes, N, K, xq, L, rows, y, P);
+        else
+            hipLaunchKernelGGL((k_bdot8k<T_Q6_K, false>), dim3((unsigned)tiles), dim3(64 * KS), sh,
+                               s, w, wbytes, N, K, xq, L, rows, y, P);
+    }
+    return (int)hipGetLastError();
+}
+
 int launch_qmv_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
                    int64_t rows, float* y, int32_t* P, hipStream_t s) {
     // x given: quantise it; the partials hook rebuilds the staging from the
@@ -2106,10 +2357,12 @@ int launch_qmv_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const float
         const int rc = launch_quantize_q8k(x, xq, rows, K, s);
         if (rc) return rc;
     }
-    // decode batches run the lane-per-chunk kernel, in launches of up to 4
-    // activation rows (each reads the weights once); prefill the int8-MFMA GEMM
-    if (rows > 16 || !use_dot(rows < 4 ? rows : 4, K))
-        return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, false, s);
+    // BDOT_MIN_ROWS..16 rows: the batched MFMA kernel; prefill: the GEMM
+    if (rows > 16) return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, false, s);
+    if (rows >= BDOT_MIN_ROWS) return launch_bdot_q8k(type, w, N, K, xq, rows, y, P, s);
+    // fewer rows run the lane-per-chunk kernel, in launches of up to 4
+    // activation rows (each reads the weights once)
+    if (!use_dot(rows, K)) return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, false, s);
     const ActLayoutK L = act_layout_q8k(rows, K);
     const int per = type == T_Q4_K ? 2 : 1;
     for (int64_t r0 = 0; r0 < rows; r0 += 4) {

@@ -24,6 +24,12 @@ extern "C" {
  * a thread in flight together; sink receives bytes/16/16 uint32 words. */
 int qmv_ceil_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* As qmv_ceil_stream_read with the nontemporal hint on every load (the
+ * cache policy of the decode GEMVs' weight loads) and 8 loads per thread:
+ * one 32 KB slice per workgroup, bytes a multiple of 32768; sink receives
+ * bytes/128 uint32 words. */
+int qmv_ceil_stream_read_nt(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* `blocks` workgroups of 4 waves, each wave issuing 4*iters
  * v_mfma_i32_32x32x32_i8 (65536 int8 operations each) in four independent
  * chains; out receives blocks*256 int32 words. */

@@ -221,8 +221,8 @@ def test_ceilings_library_exports_its_header():
     src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qmv_ceilings.h")).read(),
                  flags=re.S)
     names = set(re.findall(r"^\s*int\s+([a-z_0-9]+)\s*\(", src, re.M))
-    assert names == {"qmv_ceil_stream_read", "qmv_ceil_mfma_i8", "qmv_ceil_mfma_f16",
-                     "qmv_ceil_epilogue"}
+    assert names == {"qmv_ceil_stream_read", "qmv_ceil_stream_read_nt", "qmv_ceil_mfma_i8",
+                     "qmv_ceil_mfma_f16", "qmv_ceil_epilogue"}
     L = ctypes.CDLL(lib_path)
     for n in names:
         assert hasattr(L, n), n
@@ -231,3 +231,6 @@ def test_ceilings_library_exports_its_header():
                                        ctypes.c_void_p]
     assert L.qmv_ceil_stream_read(FAKE, 1000, FAKE, None) == -2
     assert L.qmv_ceil_stream_read(None, 65536, FAKE, None) == -2
+    L.qmv_ceil_stream_read_nt.argtypes = L.qmv_ceil_stream_read.argtypes
+    assert L.qmv_ceil_stream_read_nt(FAKE, 32768 + 16384, FAKE, None) == -2
+    assert L.qmv_ceil_stream_read_nt(FAKE + 4, 32768, FAKE, None) == -2

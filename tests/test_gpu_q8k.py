@@ -4,8 +4,9 @@ quantised per 256 elements with an f32 scale) against the CPU oracle:
 * the Q8_K blocks of the quantiser: bit-exact (zero, tiny and normal blocks,
   16- and 4-byte aligned x);
 * the superblock partials of every kernel path (the lane-per-chunk GEMV for
-  B <= 4, the int8-MFMA GEMM with 32- and 64-row tiles for more rows):
-  bit-exact, including superblock partials above 2^24;
+  B <= 4, the batched int8-MFMA kernel for B = 5..16, the int8-MFMA GEMM
+  with 32- and 64-row tiles for more rows): bit-exact, including superblock
+  partials above 2^24;
 * y: bit-identical to the oracle's replay of the Q8_K f32 order and within
   1e-4 * sum|w^ x^| of its f64 result; GEMM rows bit-identical to the
   batch-1 GEMV; at the 8B-class sizes (M = 2048) on sampled tokens and rows.
@@ -77,7 +78,7 @@ def test_partials_q8k_every_path(g, fmt, N, K, M):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [1, 3, 40])
+@pytest.mark.parametrize("M", [1, 3, 9, 40])
 def test_partials_q8k_above_2_24(g, fmt, M):
     """Large scales, codes and activations: superblock partials beyond 2^24
     (Q4_K's P up to 8*63*15*32*127), where (float)P rounds."""
@@ -182,3 +183,53 @@ def test_q8k_gemm_wide_grid_ragged(g, fmt):
     P = host(g.partials_q8k(fmt, w, N, K, g.quantize_q8k(xd), M))
     assert_bitwise(np.ascontiguousarray(P[:, rows]),
                    oracle.partials_q8k(fmt, sub, len(rows), K, xq, M), "wide grid partials")
+
+
+@pytest.mark.parametrize("fmt,N,K,M", [(synth.Q6_K, 151936, 1024, 16), (synth.Q6_K, 151936, 1024, 5),
+                                       (synth.Q4_K, 14336, 4096, 16), (synth.Q6_K, 4096, 14336, 16),
+                                       (synth.Q4_K, 1024, 4096, 11)])
+def test_q8k_batched_decode_full_size(g, fmt, N, K, M):
+    """Batched decode (5..16 rows) at the LM-head and 8B-class shapes: sampled
+    weight rows of every token against the oracle, bitwise in the Q8_K f32
+    order and within tolerance of f64; a few tokens' full rows against the
+    batch-1 GEMV; the partials on the sampled rows."""
+    blob, _ = synth.weights(fmt, N, K, 2700 + N % 97, dscale=0.02)
+    x = synth.activations(M, K, 2701 + M)
+    w, xd = dev(blob), dev(x)
+    print(f"q8k batched full size fmt={fmt} N={N} K={K} M={M}", flush=True)
+    y = host(g.matmul_q8k(fmt, w, N, K, x=xd))
+    rng = np.random.Generator(np.random.PCG64(2702 + N))
+    rows = np.unique(np.concatenate([[0, 15, 16, N - 1], rng.choice(N, 200, replace=False)]))
+    R = synth.row_bytes(fmt, K)
+    sub = np.ascontiguousarray(blob.reshape(N, R)[rows]).reshape(-1)
+    xq = oracle.quantize_act_q8k(x)
+    got = np.ascontiguousarray(y[:, rows])
+    y64, A = oracle.matmul_q8k_f64(fmt, sub, len(rows), K, xq, M)
+    assert_tol(got, y64, A, what="batched q8k full size")
+    assert_bitwise(got, oracle.matmul_q8k_canon_f32(fmt, sub, len(rows), K, xq, M),
+                   "batched q8k f32 order")
+    for t in sorted({0, M // 2, M - 1}):
+        y1 = host(g.matmul_q8k(fmt, w, N, K, x=dev(x[t:t + 1])))
+        assert_bitwise(y[t:t + 1], y1, f"token {t} vs batch-1 GEMV")
+    P = host(g.partials_q8k(fmt, w, N, K, g.quantize_q8k(xd), M))
+    assert_bitwise(np.ascontiguousarray(P[:, rows]),
+                   oracle.partials_q8k(fmt, sub, len(rows), K, xq, M), "batched partials")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_q8k_batched_long_rows(g, fmt):
+    """Rows of 65536 elements (256 superblocks, 32 rounds of the workgroup's
+    waves; too long for the lane-per-chunk kernel's LDS staging) at 8 tokens,
+    with a ragged last tile (N = 37)."""
+    N, K, M = 37, 65536, 8
+    blob, _ = synth.weights(fmt, N, K, 2800 + fmt, s_range=(-128, 127))
+    x = synth.activations(M, K, 2801)
+    xd = dev(x)
+    print(f"q8k batched long rows fmt={fmt}", flush=True)
+    y = host(g.matmul_q8k(fmt, dev(blob), N, K, x=xd))
+    xq = oracle.quantize_act_q8k(x)
+    y64, A = oracle.matmul_q8k_f64(fmt, blob, N, K, xq, M)
+    assert_tol(y, y64, A, what="long rows vs f64")
+    assert_bitwise(y, oracle.matmul_q8k_canon_f32(fmt, blob, N, K, xq, M), "long rows f32 order")
+    P = host(g.partials_q8k(fmt, dev(blob), N, K, g.quantize_q8k(xd), M))
+    assert_bitwise(P, oracle.partials_q8k(fmt, blob, N, K, xq, M), "long rows partials")
