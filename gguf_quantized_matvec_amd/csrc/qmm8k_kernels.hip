@@ -58,7 +58,8 @@ __device__ __forceinline__ float inv_scale(float d) {
 // One wave per (row, superblock), 4 elements per lane: amax over the wave,
 // d = amax/127, codes = round-half-away(x * id); the public Q8_K block and
 // the row-major staging (codes, d per 32 codes, the two 16-code sums of each
-// 32 codes).  FROM_PUBLIC: take codes and d from the Q8_K block in xq.
+// 32 codes), and for at most 16 rows the MFMA-order copy of the batched
+// decode kernel.  FROM_PUBLIC: take codes and d from the Q8_K block in xq.
 template <bool FROM_PUBLIC, bool A16>
 __global__ __launch_bounds__(256) void k_quantize_q8k(const float* __restrict__ x,
                                                       uint8_t* __restrict__ xq, int64_t rows,
@@ -107,6 +108,21 @@ __global__ __launch_bounds__(256) void k_quantize_q8k(const float* __restrict__ 
         reinterpret_cast<float*>(xq + L.rda)[b] = d;
         reinterpret_cast<int32_t*>(xq + L.rs16)[b] =
             (int32_t)(((uint32_t)s16 & 0xFFFFu) | ((uint32_t)s16b << 16));
+    }
+    if (L.gcodes) {
+        // element 4 lane + t is byte 8 kg + 4 (lane & 1) + t of block j:
+        // j = lane / 8, kg = (lane % 8) / 2
+        const int j = lane >> 3, kg = (lane & 7) >> 1;
+        uint8_t* gb = xq + L.gcodes + sb * 4096;
+        *reinterpret_cast<uint32_t*>(gb + (j >> 1) * 1024 + (r + 16 * kg) * 16 + (j & 1) * 8 +
+                                     4 * (lane & 1)) = c4;
+        if (lane == 0) reinterpret_cast<float*>(xq + L.gda)[sb * 16 + r] = d;
+        if ((lane & 7) == 0) {
+            const int S = s16 + s16b;  // the block's 32-code sum, |S| <= 4064
+            uint8_t* sd = xq + L.gsd + sb * 256 + r * 16;
+            sd[j] = (uint8_t)(S & 63);
+            sd[8 + j] = (uint8_t)((S >> 6) & 0xFF);
+        }
     }
 }
 

@@ -64,8 +64,19 @@ inline ActLayout act_layout(int64_t rows, int64_t K) {
 //                              codes, as two int16 (low half = first)
 // (the layout of the lane-per-chunk GEMV's Q8_0 staging, so that kernel
 // stages either; rca is not used on this path and aliases rda).
+//   For rows <= 16 (gcodes != 0) also the copy the batched decode kernel
+//   reads, in the operand order of v_mfma_i32_16x16x32_i8, per superblock c:
+//     gcodes [c][p = 0..3][lane 0..63][16]  lane l = m + 16 kg: row m's codes
+//                                           8kg..8kg+7 of block 2p, then of
+//                                           block 2p+1
+//     gda    [c][16] f32                    row m's Q8_K d
+//     gsd    [c][16][16] int8               row m's eight 32-code sums S_j as
+//                                           digits, S & 63 at [j], S >> 6 at
+//                                           [8 + j] (S = 64 hi + lo)
+//   (entries of rows m >= rows are not written: they only ever feed outputs
+//   of rows that are not stored).
 struct ActLayoutK {
-    int64_t nb, nsb, pub, rcodes, rda, rs16, total;
+    int64_t nb, nsb, pub, rcodes, rda, rs16, gcodes, gda, gsd, total;
 };
 inline ActLayoutK act_layout_q8k(int64_t rows, int64_t K) {
     ActLayoutK L;
@@ -76,6 +87,13 @@ inline ActLayoutK act_layout_q8k(int64_t rows, int64_t K) {
     L.rda = (L.rcodes + rows * K + 255) & ~int64_t(255);
     L.rs16 = (L.rda + rows * L.nb * 4 + 255) & ~int64_t(255);
     L.total = (L.rs16 + rows * L.nb * 4 + 255) & ~int64_t(255);
+    L.gcodes = L.gda = L.gsd = 0;
+    if (rows <= 16) {
+        L.gcodes = L.total;
+        L.gda = L.gcodes + L.nsb * 4096;
+        L.gsd = (L.gda + L.nsb * 64 + 255) & ~int64_t(255);
+        L.total = (L.gsd + L.nsb * 256 + 255) & ~int64_t(255);
+    }
     return L;
 }
 

@@ -811,45 +811,38 @@ __global__ __launch_bounds__(512) void k_qmv_split(const uint8_t* __restrict__ w
 // rows, and its KS waves take the tile's superblocks round-robin.  A wave
 // streams the 16 rows' bytes of its superblock as 16-byte pieces into its LDS
 // slice (as k_qmv_split does), then lane (nn = l%16, kg = l/16) takes weight
-// row nn's codes 8kg..8kg+7 of each 32-element block and activation row
-// l%16's, one v_mfma_i32_16x16x32_i8 per block (Q6_K: two, one per 16-element
-// sub-block, the other half's codes zeroed); result element i is activation
-// row 4kg+i.  The sub-block scales multiply the exact int32 block sums, so a
-// superblock reduces to the integers of the Q8_K order and is scaled in f32
-// once, not once per 32 elements as on the Q8_0 path.  Q4_K's min term
-// Q = sum_j m_j S_j runs as two more MFMAs: the row's eight 32-code sums S_j
-// as two int8 digits (S = 64 hi + lo, lo in 0..63) against the eight 6-bit
-// mins, in k-group 0 only.  After each round of KS superblocks their results
-// are added to y in ascending superblock order through LDS.  PART: the
-// integer partials are written instead (test hook).
+// row nn's codes 8kg..8kg+7 of each 32-element block, one
+// v_mfma_i32_16x16x32_i8 per block (Q6_K: two, one per 16-element sub-block,
+// the other half's codes zeroed); result element i is activation row 4kg+i.
+// The activation operands come from the quantiser's copy in operand order
+// (four 16-byte loads per lane and superblock, each wave instruction reading
+// 1 KB contiguously; the rows' scales in one more).  The sub-block scales
+// multiply the exact int32 block sums, so a superblock reduces to the
+// integers of the Q8_K order and is scaled in f32 once, not once per 32
+// elements as on the Q8_0 path.  Q4_K's min term Q = sum_j m_j S_j runs as
+// two more MFMAs: the rows' eight 32-code sums as two int8 digits (from the
+// quantiser) against the eight 6-bit mins, in k-group 0 only.  Every
+// superblock's f32 results wait in LDS until a window of BDOT_WINDOW
+// superblocks is done; then they are added to y in ascending superblock
+// order.  PART: the integer partials are written instead (test hook).
+constexpr int BDOT_WINDOW = 32;
+
 struct ActRegsK {
-    uint64_t a[8];  // activation row l%16: codes 8kg..8kg+7 of each 32-element block
-    float da[4];    // Q8_K d of activation rows 4kg+i (0 past the batch)
-    uint4 s16[2];   // Q4_K, k-group 0: row l%16's eight pairs of 16-code sums
+    uint4 a[4];   // blocks 2p, 2p+1: activation row l%16, codes 8kg..8kg+7 of each
+    float4 da;    // Q8_K d of activation rows 4kg..4kg+3
+    uint4 sd;     // Q4_K, k-group 0: row l%16's digits of S_0..S_7 (lo, then hi)
 };
 
 template <int FMT>
-__device__ __forceinline__ void fetch_act_k(const uint8_t* xq, const ActLayoutK& L, int64_t K,
-                                            int64_t row0, int Bg, int c, int lane, ActRegsK& r) {
-    const int m = lane & 15, kg = lane >> 4;
-    const bool live = m < Bg;
-    const uint8_t* ar = xq + L.rcodes + (row0 + (live ? m : 0)) * K + 256 * c + 8 * kg;
+__device__ __forceinline__ void fetch_act_k(const uint8_t* xq, const ActLayoutK& L, int c, int lane,
+                                            ActRegsK& r) {
+    const uint8_t* cb = xq + L.gcodes + (int64_t)c * 4096 + lane * 16;
 #pragma unroll
-    for (int j = 0; j < 8; j++) r.a[j] = live ? ld<uint64_t>(ar + 32 * j) : 0ull;
-    const float* rda = reinterpret_cast<const float*>(xq + L.rda);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int mr = 4 * kg + i;
-        r.da[i] = mr < Bg ? rda[(row0 + mr) * L.nb + 8 * c] : 0.0f;
-    }
-    if constexpr (FMT == T_Q4_K) {
-        r.s16[0] = r.s16[1] = make_uint4(0, 0, 0, 0);
-        if (kg == 0 && live) {
-            const uint4* sp = reinterpret_cast<const uint4*>(xq + L.rs16) + ((row0 + m) * L.nb + 8 * c) / 4;
-            r.s16[0] = sp[0];
-            r.s16[1] = sp[1];
-        }
-    }
+    for (int p = 0; p < 4; p++) r.a[p] = *reinterpret_cast<const uint4*>(cb + 1024 * p);
+    r.da = *reinterpret_cast<const float4*>(xq + L.gda + (int64_t)c * 64 + 16 * (lane >> 4));
+    if constexpr (FMT == T_Q4_K)
+        r.sd = lane < 16 ? *reinterpret_cast<const uint4*>(xq + L.gsd + (int64_t)c * 256 + 16 * lane)
+                         : make_uint4(0, 0, 0, 0);
 }
 
 // The integer partials of one superblock (rb: weight row nn's bytes of it in
@@ -860,6 +853,10 @@ template <int FMT>
 __device__ __forceinline__ void superblock_k(const uint8_t* rb, const ActRegsK& A, int kg,
                                              int (&Pi)[4], int (&Qi)[4], float& dw, float& dmw) {
     const v4i zero = {0, 0, 0, 0};
+    auto act = [&](int j) -> long {
+        const uint4 v = A.a[j >> 1];
+        return (j & 1) ? (long)(((uint64_t)v.w << 32) | v.z) : (long)(((uint64_t)v.y << 32) | v.x);
+    };
 #pragma unroll
     for (int i = 0; i < 4; i++) Pi[i] = Qi[i] = 0;
     if constexpr (FMT == T_Q4_K) {
@@ -886,23 +883,16 @@ __device__ __forceinline__ void superblock_k(const uint8_t* rb, const ActRegsK& 
             uint64_t raw = q[j >> 1];
             if (j & 1) raw >>= 4;
             const v4i acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                (long)A.a[j], (long)(raw & 0x0F0F0F0F0F0F0F0Full), zero, 0, 0, 0);
+                act(j), (long)(raw & 0x0F0F0F0F0F0F0F0Full), zero, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; i++) Pi[i] = __mul24(sc, acc[i]) + Pi[i];
         }
-        // min term: k-group 0 carries S_j (two digits) against m_j, j = 0..7
-        uint64_t slo = 0, shi = 0;
-        const uint32_t sv[8] = {A.s16[0].x, A.s16[0].y, A.s16[0].z, A.s16[0].w,
-                                A.s16[1].x, A.s16[1].y, A.s16[1].z, A.s16[1].w};
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int S = (int)(int16_t)(sv[j] & 0xFFFFu) + ((int)sv[j] >> 16);  // |S| <= 4096
-            slo |= (uint64_t)(uint32_t)(S & 63) << (8 * j);
-            shi |= (uint64_t)(uint32_t)((S >> 6) & 0xFF) << (8 * j);
-        }
+        // min term: k-group 0 carries the S_j digits against m_j, j = 0..7
         const long bm = kg == 0 ? (long)mins : 0;
-        const v4i ql = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)slo, bm, zero, 0, 0, 0);
-        const v4i qh = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)shi, bm, zero, 0, 0, 0);
+        const long slo = (long)(((uint64_t)A.sd.y << 32) | A.sd.x);
+        const long shi = (long)(((uint64_t)A.sd.w << 32) | A.sd.z);
+        const v4i ql = __builtin_amdgcn_mfma_i32_16x16x32_i8(slo, bm, zero, 0, 0, 0);
+        const v4i qh = __builtin_amdgcn_mfma_i32_16x16x32_i8(shi, bm, zero, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; i++) Qi[i] = ql[i] + 64 * qh[i];
     } else {
@@ -926,16 +916,18 @@ __device__ __forceinline__ void superblock_k(const uint8_t* rb, const ActRegsK& 
             const uint32_t sw = sc6[j >> 1] >> (16 * (j & 1));
             const int s0 = (int8_t)(sw & 0xFF), s1 = (int8_t)((sw >> 8) & 0xFF);
             const long lo = kg < 2 ? (long)wc : 0, hi = kg < 2 ? 0 : (long)wc;
-            const v4i acc0 = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)A.a[j], lo, zero, 0, 0, 0);
-            const v4i acc1 = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)A.a[j], hi, zero, 0, 0, 0);
+            const v4i acc0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(act(j), lo, zero, 0, 0, 0);
+            const v4i acc1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(act(j), hi, zero, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; i++) Pi[i] = __mul24(s0, acc0[i]) + __mul24(s1, acc1[i]) + Pi[i];
         }
     }
 }
 
+// (Q4_K: at most 128 VGPRs, i.e. 4 waves per SIMD; with one register more,
+// 3 waves, the 14336 x 4096 GEMV at 16 rows took 16.5 us against 13.0)
 template <int FMT, bool PART>
-__global__ __launch_bounds__(512) void k_bdot8k(const uint8_t* __restrict__ w, int64_t wbytes,
+__global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(const uint8_t* __restrict__ w, int64_t wbytes,
                                                 int64_t N, int64_t K,
                                                 const uint8_t* __restrict__ xq, ActLayoutK L,
                                                 int64_t rows, float* __restrict__ y,
@@ -946,7 +938,7 @@ __global__ __launch_bounds__(512) void k_bdot8k(const uint8_t* __restrict__ w, i
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6), KS = blockDim.x >> 6;
     uint8_t* wl = smem + wv * SL;
-    float* pbuf = reinterpret_cast<float*>(smem + KS * SL);
+    float* pbuf = reinterpret_cast<float*>(smem + KS * SL);  // [window][256]
     const int64_t tile = blockIdx.x, n0 = tile * 16;
     const int Bg = (int)(rows < 16 ? rows : 16);
     const int C = (int)(K >> 8);
@@ -955,29 +947,32 @@ __global__ __launch_bounds__(512) void k_bdot8k(const uint8_t* __restrict__ w, i
     const int nn = lane & 15, kg = lane >> 4;
     const TileRef t = make_tile(w, wbytes, N, Rl, tile);
 
-    float yacc = 0.0f;
     uint4 reg[NP];
     ActRegsK nxt;
     if (wv < C) {
         fetch_chunk<FMT>(t, R, wv, 8, lane, reg);
-        fetch_act_k<FMT>(xq, L, K, 0, Bg, wv, lane, nxt);
+        fetch_act_k<FMT>(xq, L, wv, lane, nxt);
     }
-    for (int r0 = 0; r0 < C; r0 += KS) {
-        const int c = r0 + wv;
-        if (c < C) {
+    float yacc = 0.0f;
+    // the wave's superblocks are c = wv (mod KS), in ascending order across
+    // the windows: the one in flight at a window's end is its first of the next
+    int c = wv;
+    for (int w0 = 0; w0 < C; w0 += BDOT_WINDOW) {
+        const int w1 = C - w0 < BDOT_WINDOW ? C : w0 + BDOT_WINDOW;
+        for (; c < w1; c += KS) {
             stage_chunk<FMT>(wl, lane, reg);
             const ActRegsK cur = nxt;
             wave_sync();
             const int cn = c + KS;
             if (cn < C) {
                 fetch_chunk<FMT>(t, R, cn, 8, lane, reg);
-                fetch_act_k<FMT>(xq, L, K, 0, Bg, cn, lane, nxt);
+                fetch_act_k<FMT>(xq, L, cn, lane, nxt);
             }
             const uint8_t* rb = wl + nn * span_stride<FMT>() + ((nn * R + c * F::CB) & 15);
             int Pi[4], Qi[4];
             float dw, dmw;
             superblock_k<FMT>(rb, cur, kg, Pi, Qi, dw, dmw);
-            wave_sync();  // the slice is read: the next round may overwrite it
+            wave_sync();  // the slice is read: the next superblock may overwrite it
             const int64_t n = n0 + nn;
             if constexpr (PART) {
 #pragma unroll
@@ -994,20 +989,20 @@ __global__ __launch_bounds__(512) void k_bdot8k(const uint8_t* __restrict__ w, i
                     }
                 }
             } else {
+                const float da[4] = {cur.da.x, cur.da.y, cur.da.z, cur.da.w};
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     const int m = 4 * kg + i;
-                    float p = fmaf((float)Pi[i], dw * cur.da[i], 0.0f);
-                    if constexpr (FMT == T_Q4_K) p = fmaf(-(float)Qi[i], dmw * cur.da[i], p);
-                    if (m < Bg) pbuf[wv * 256 + m * 16 + nn] = p;
+                    float p = fmaf((float)Pi[i], dw * da[i], 0.0f);
+                    if constexpr (FMT == T_Q4_K) p = fmaf(-(float)Qi[i], dmw * da[i], p);
+                    if (m < Bg) pbuf[(c - w0) * 256 + m * 16 + nn] = p;
                 }
             }
         }
         if constexpr (!PART) {
             __syncthreads();
-            const int nact = C - r0 < KS ? C - r0 : KS;
             if (threadIdx.x < 16 * Bg)
-                for (int w2 = 0; w2 < nact; w2++) yacc = yacc + pbuf[w2 * 256 + threadIdx.x];
+                for (int cc = 0; cc < w1 - w0; cc++) yacc = yacc + pbuf[cc * 256 + threadIdx.x];
             __syncthreads();
         }
     }
@@ -2321,14 +2316,16 @@ int launch_bdot_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const uint
                     int64_t rows, float* y, int32_t* P, hipStream_t s) {
     const int64_t tiles = (N + 15) / 16;
     const int C = (int)(K / 256);
-    if (tiles > INT32_MAX || rows < 1 || rows > 16) return (int)hipErrorInvalidValue;
+    const ActLayoutK L = act_layout_q8k(rows, K);
+    if (tiles > INT32_MAX || rows < 1 || rows > 16 || !L.gcodes) return (int)hipErrorInvalidValue;
+    // 8 waves per tile (measured best at 8 wherever a tile has 8 superblocks),
+    // fewer when it has fewer; at least one thread per output for the combine
     int KS = 1;
-    while (KS < 8 && tiles * KS < 4096 && KS * 2 <= C) KS *= 2;
+    while (KS < 8 && KS * 2 <= C) KS *= 2;
     const int need = (int)((16 * rows + 63) / 64);
     if (!P && KS < need) KS = need;
-    const ActLayoutK L = act_layout_q8k(rows, K);
     const int64_t wbytes = N * row_bytes(type, K);
-    const size_t pb = P ? 0 : (size_t)KS * 1024;
+    const size_t pb = P ? 0 : (size_t)(C < BDOT_WINDOW ? C : BDOT_WINDOW) * 1024;
     if (type == T_Q4_K) {
         const size_t sh = (size_t)KS * 16 * span_stride<T_Q4_K>() + pb;
         if (P)
