@@ -169,8 +169,9 @@ class Layer:
     """Buffers of the 8B-class layer step at batch B: rotated weight copies,
     the stage activations, scratch and outputs."""
 
-    def __init__(self, torch, g, synth, B, rotate_bytes):
+    def __init__(self, torch, g, synth, B, rotate_bytes, q8k=False):
         self.B = B
+        self.q8k = q8k
         self.torch, self.g = torch, g
         blobs = {}
         for i, (name, fmt, N, K) in enumerate(LAYER):
@@ -181,11 +182,15 @@ class Layer:
         self.w = {k: [v] + [v.clone() for _ in range(self.R - 1)] for k, v in blobs.items()}
         act = lambda K, j: torch.from_numpy(synth.activations(B, K, synth.act_seed_for(4, B) + j)).cuda()
         self.xa, self.xo, self.xc = act(4096, 0), act(4096, 1), act(4096, 2)
-        self.xq_a = g.act_buffer(B, 4096)
-        self.xq_o = g.act_buffer(B, 4096)
-        self.xq_c = torch.empty(g.qmv_gateup_act_bytes(B, 14336, 4096), dtype=torch.uint8,
-                                device="cuda")
-        self.xq_d = g.act_buffer(B, 14336)
+        if q8k:
+            qb = lambda K: torch.empty(g.qmv_act_bytes_q8k(B, K), dtype=torch.uint8, device="cuda")
+            self.xq_a, self.xq_o, self.xq_c, self.xq_d = qb(4096), qb(4096), qb(4096), qb(14336)
+        else:
+            self.xq_a = g.act_buffer(B, 4096)
+            self.xq_o = g.act_buffer(B, 4096)
+            self.xq_c = torch.empty(g.qmv_gateup_act_bytes(B, 14336, 4096), dtype=torch.uint8,
+                                    device="cuda")
+            self.xq_d = g.act_buffer(B, 14336)
         self.h = torch.empty(B, 14336, dtype=torch.float32, device="cuda")
         self.y = {n: torch.empty(B, N, dtype=torch.float32, device="cuda")
                   for n, _, N, _ in LAYER if n not in ("gate", "up")}
@@ -227,6 +232,9 @@ class Layer:
         L = g.lib()
         s = torch.cuda.current_stream().cuda_stream
         W = lambda n: self.w[n][c].data_ptr()
+        if self.q8k:
+            self._stage_q8k(name, W, s)
+            return
         if name == "A_qkv":
             if B > 4:   # the group runs its GEMVs one after another: quantise once
                 _check(g, L.quantize_act_q8_0(self.xa.data_ptr(), self.xq_a.data_ptr(), B, 4096, s),
@@ -244,6 +252,27 @@ class Layer:
         else:
             _check(g, L.qmv_launch(Q6_K, W("down"), 4096, 14336, None, B, self.xq_d.data_ptr(),
                                    self.y["down"].data_ptr(), s), "down")
+
+    def _stage_q8k(self, name, W, s):
+        """The stage on the Q8_K path: A quantises x once for q, k, v; C is
+        the paired gate/up launch with the SwiGLU; B and D quantise their x."""
+        g, B, L = self.g, self.B, self.g.lib()
+        if name == "A_qkv":
+            _check(g, L.quantize_act_q8_k(self.xa.data_ptr(), self.xq_a.data_ptr(), B, 4096, s),
+                   "quantize q8k")
+            for n, N in (("q", 4096), ("k", 1024), ("v", 1024)):
+                _check(g, L.qmv_launch_q8k(Q4_K, W(n), N, 4096, None, B, self.xq_a.data_ptr(),
+                                           self.y[n].data_ptr(), s), n)
+        elif name == "B_o":
+            _check(g, L.qmv_launch_q8k(Q4_K, W("o"), 4096, 4096, self.xo.data_ptr(), B,
+                                       self.xq_o.data_ptr(), self.y["o"].data_ptr(), s), "o")
+        elif name == "C_gateup_swiglu":
+            _check(g, L.qmv_launch_gateup_swiglu_q8k(Q4_K, W("gate"), W("up"), 14336, 4096,
+                                                     self.xc.data_ptr(), B, self.xq_c.data_ptr(),
+                                                     self.h.data_ptr(), s), "gate/up")
+        else:
+            _check(g, L.qmv_launch_q8k(Q6_K, W("down"), 4096, 14336, self.h.data_ptr(), B,
+                                       self.xq_d.data_ptr(), self.y["down"].data_ptr(), s), "down")
 
     def step(self, i):
         c = i % self.R
@@ -270,8 +299,8 @@ class Layer:
         return w + act + sum(B * Nd[n] * 4 for n in mats)
 
 
-def time_layer(torch, g, synth, B, steps, warmup, rotate_bytes):
-    Lw = Layer(torch, g, synth, B, rotate_bytes)
+def time_layer(torch, g, synth, B, steps, warmup, rotate_bytes, q8k=False):
+    Lw = Layer(torch, g, synth, B, rotate_bytes, q8k)
     Lw.step(0)
     torch.cuda.synchronize()
     graphs = {}
@@ -484,9 +513,14 @@ def ceilings(torch):
     nbytes = 1 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     sink = torch.empty(nbytes // 128, dtype=torch.int32, device="cuda")  # the larger of the two sinks
-    t = timed(lambda: lib.qmv_ceil_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), s()))
+    # 4 reads of the 1 GiB back to back per timing (a lone launch also pays
+    # its dispatch and ramp-up, some 20 % of it here)
+    def reads(fn):
+        for _ in range(4):
+            fn(buf.data_ptr(), nbytes, sink.data_ptr(), s())
+    t = timed(lambda: reads(lib.qmv_ceil_stream_read)) / 4
     out = {"stream_read_GBs": round(nbytes / t / 1e9, 1)}
-    t = timed(lambda: lib.qmv_ceil_stream_read_nt(buf.data_ptr(), nbytes, sink.data_ptr(), s()))
+    t = timed(lambda: reads(lib.qmv_ceil_stream_read_nt)) / 4
     out["stream_read_nt_GBs"] = round(nbytes / t / 1e9, 1)
     # the nontemporal read at the size of the headline's dominant launch
     # (66.1 MB), rotated over the 16 slices of the buffer so none is cached
@@ -512,9 +546,10 @@ def ceilings(torch):
     out["epilogue_Tfma_s"] = round(fma_s / 1e12, 2)
     # one fma per output and 32-element block = 32 int8 MACs = 64 int8 ops
     out["epilogue_bound_int8_TOPS"] = round(fma_s * 64 / 1e12, 1)
-    out["how"] = ("libqmv_ceilings.so (qmv_ceilings.hip): a 1 GiB read with 16-byte loads, 16 "
-                  "in flight per thread, and with the nontemporal hint, 8 in flight per thread "
-                  "(also 32 back-to-back 66.1 MB reads over rotated slices, time per read); 2048 workgroups x 4 waves of 4 independent MFMA chains; "
+    out["how"] = ("libqmv_ceilings.so (qmv_ceilings.hip): 4 back-to-back reads of 1 GiB with "
+                  "16-byte loads, 16 in flight per thread, and with the nontemporal hint, 8 in "
+                  "flight per thread (also 32 back-to-back 66.1 MB reads over rotated slices), "
+                  "time per read; 2048 workgroups x 4 waves of 4 independent MFMA chains; "
                   "16 f32 fma chains per thread; best of 5 launches by HIP events")
     return out
 
@@ -899,6 +934,17 @@ def main():
                              "ms_per_step": round(r16["wall_s"] / n16 * 1e3, 5),
                              "tok_s": round(16 * n16 / r16["wall_s"], 1), "steps": n16,
                              "stage_us": {k: round(v, 2) for k, v in r16["stage_us"].items()}}
+        print("step: layer batch 16, Q8_K activations", file=sys.stderr, flush=True)
+        r16k = time_layer(torch, g, synth, 16, n16, max(2, args.warmup // 4), rot, q8k=True)
+        v16k = r16k["step_bytes"] * n16 / r16k["wall_s"] / 1e9
+        out["decode_b16_q8k"] = {
+            "value_GBs": round(v16k, 1), "hbm_frac": round(v16k / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(r16k["wall_s"] / n16 * 1e3, 5),
+            "tok_s": round(16 * n16 / r16k["wall_s"], 1), "steps": n16,
+            "stage_us": {k: round(v, 2) for k, v in r16k["stage_us"].items()},
+            "path": "the same step with Q8_K activations: A quantises once, then q, k, v "
+                    "(qmv_launch_q8k); B, D qmv_launch_q8k; C qmv_launch_gateup_swiglu_q8k; "
+                    "the batched int8-MFMA kernel, one f32 term per superblock"}
         print("step: prefill M=2048", file=sys.stderr, flush=True)
         out["prefill_m2048"] = {"unit": "int8-equivalent TOPS", "peak": INT8_PEAK_TOPS,
                                 **prefill_8b(torch, g, synth)}

@@ -22,7 +22,7 @@ BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_1: (32, 20), Q5_1: (
 EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
            "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc", "qmv_gateup_act_bytes",
            "qmv_launch_gateup_swiglu", "qmv_launch_gateup_swiglu_q8", "qmv_act_bytes_q8k", "quantize_act_q8_k", "qmv_launch_q8k",
-           "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepared_bytes", "qmv_prepare",
+           "qmv_launch_gateup_swiglu_q8k", "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepared_bytes", "qmv_prepare",
            "qmm_launch_q8k_prepared", "qmm_partials_q8k_prepared_launch", "qmv_strerror")
 MAX_BATCH = 16
 MAX_GROUP = 8
@@ -75,10 +75,11 @@ def lib() -> ctypes.CDLL:
         L.qmv_gateup_act_bytes.restype = ctypes.c_size_t
         L.qmv_launch_gateup_swiglu.argtypes = [I, P, P, I64, I64, P, I64, P, P, P]
         L.qmv_launch_gateup_swiglu_q8.argtypes = [I, P, P, I64, I64, P, I64, P, P, P, P]
+        L.qmv_launch_gateup_swiglu_q8k.argtypes = [I, P, P, I64, I64, P, I64, P, P, P]
         for f in ("quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
                   "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc",
                   "qmv_launch_gateup_swiglu", "qmv_launch_gateup_swiglu_q8", "quantize_act_q8_k", "qmv_launch_q8k",
-                  "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepare",
+                  "qmv_launch_gateup_swiglu_q8k", "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepare",
                   "qmm_launch_q8k_prepared", "qmm_partials_q8k_prepared_launch"):
             getattr(L, f).restype = I
         L.qmv_strerror.argtypes = [I]
@@ -151,6 +152,12 @@ def qmv_launch_gateup_swiglu_q8(type: int, w_gate: int, w_up: int, N: int, K: in
                                 xq: int, h: int, hq: int, stream: int = 0) -> None:
     _check(lib().qmv_launch_gateup_swiglu_q8(type, w_gate, w_up, N, K, x, B, xq, h, hq, stream),
            "qmv_launch_gateup_swiglu_q8")
+
+
+def qmv_launch_gateup_swiglu_q8k(type: int, w_gate: int, w_up: int, N: int, K: int, x, B: int,
+                                 xq: int, h: int, stream: int = 0) -> None:
+    _check(lib().qmv_launch_gateup_swiglu_q8k(type, w_gate, w_up, N, K, x, B, xq, h, stream),
+           "qmv_launch_gateup_swiglu_q8k")
 
 
 def qmv_act_bytes_q8k(rows: int, K: int) -> int:
@@ -394,6 +401,24 @@ def matmul_q8k(type: int, w, N: int, K: int, x=None, xq=None, M=None, y=None, st
     qmm_launch_q8k(type, _dev(w, torch.uint8, "w"), N, K, xp, M, _dev(xq, torch.uint8, "xq"),
                    _dev(y, torch.float32, "y"), _stream(stream))
     return y
+
+
+def gateup_swiglu_q8k(type: int, w_gate, w_up, N: int, K: int, x=None, xq=None, B=None, h=None,
+                      stream=None):
+    """h [B, N] f32 = silu(x Wg^T) * (x Wu^T) on the Q8_K path (x None: staged xq)."""
+    import torch
+    if x is not None:
+        B = x.shape[0]
+    if xq is None:
+        xq = torch.empty(qmv_act_bytes_q8k(B, K), dtype=torch.uint8, device=w_gate.device)
+    if h is None:
+        h = torch.empty(B, N, dtype=torch.float32, device=w_gate.device)
+    xp = _dev(x, torch.float32, "x") if x is not None else None
+    qmv_launch_gateup_swiglu_q8k(type, _dev(w_gate, torch.uint8, "w_gate"),
+                                 _dev(w_up, torch.uint8, "w_up"), N, K, xp, B,
+                                 _dev(xq, torch.uint8, "xq"), _dev(h, torch.float32, "h"),
+                                 _stream(stream))
+    return h
 
 
 def partials_q8k(type: int, w, N: int, K: int, xq, M: int, P=None, stream=None):

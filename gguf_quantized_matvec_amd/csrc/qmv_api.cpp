@@ -276,6 +276,23 @@ int qmm_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x
     return q8k_common(type, w, N, K, x, M, QMV_MAX_M, xq, y, nullptr, stream);
 }
 
+int qmv_launch_gateup_swiglu_q8k(int type, const void* w_gate, const void* w_up, int64_t N,
+                                 int64_t K, const float* x, int64_t B, void* xq, float* h,
+                                 void* stream) {
+    if (type != QMV_Q4_K && type != QMV_Q6_K) return QMV_EINVAL_TYPE;
+    int rc = check_weights(type, w_gate, N, K);
+    if (rc) return rc;
+    if ((rc = check_weights(type, w_up, N, K))) return rc;
+    if (B < 1 || B > QMV_MAX_BATCH) return QMV_EINVAL_SHAPE;
+    if (!xq || !h || !aligned(xq, 16) || !aligned(h, 4)) return QMV_EINVAL_PTR;
+    if (x && !aligned(x, 4)) return QMV_EINVAL_PTR;
+    if ((rc = check_device())) return rc;
+    return launched(qmv::launch_gateup_q8k(type, static_cast<const uint8_t*>(w_gate),
+                                           static_cast<const uint8_t*>(w_up), N, K, x,
+                                           static_cast<uint8_t*>(xq), B, h,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int qmv_partials_q8k_launch(int type, const void* w, int64_t N, int64_t K, void* xq,
                             int64_t M, int32_t* P, void* stream) {
     if (!P) return QMV_EINVAL_PTR;

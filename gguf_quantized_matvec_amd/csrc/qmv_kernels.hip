@@ -805,6 +805,17 @@ __global__ __launch_bounds__(512) void k_qmv_split(const uint8_t* __restrict__ w
     }
 }
 
+// SwiGLU of one output element: silu(g) * u with silu(g) = g / (1 + e^-g),
+// evaluated in f64 as t = exp(-g), s = g / (1 + t), h = s * u and rounded
+// once to f32 (the llama-family feed-forward gate; llamay "Models and
+// formats", architectures table).
+__device__ __forceinline__ float swiglu(float g, float u) {
+    const double gd = (double)g;
+    const double t = exp(-gd);
+    const double s = gd / (1.0 + t);
+    return (float)(s * (double)u);
+}
+
 // ------------------------------------- batched decode on the Q8_K path ----
 // 5..16 activation rows against Q4_K / Q6_K weights with Q8_K activations
 // (one f32 scale per 256 activations): a workgroup owns a tile of 16 weight
@@ -825,6 +836,9 @@ __global__ __launch_bounds__(512) void k_qmv_split(const uint8_t* __restrict__ w
 // superblock's f32 results wait in LDS until a window of BDOT_WINDOW
 // superblocks is done; then they are added to y in ascending superblock
 // order.  PART: the integer partials are written instead (test hook).
+// PAIR: the workgroup takes tile t of two matrices of one shape (the gate
+// and up projections), walks the first one's superblocks and then the
+// second's, sums each in its own order and writes h = silu(g) * u.
 constexpr int BDOT_WINDOW = 32;
 
 struct ActRegsK {
@@ -926,12 +940,11 @@ __device__ __forceinline__ void superblock_k(const uint8_t* rb, const ActRegsK& 
 
 // (Q4_K: at most 128 VGPRs, i.e. 4 waves per SIMD; with one register more,
 // 3 waves, the 14336 x 4096 GEMV at 16 rows took 16.5 us against 13.0)
-template <int FMT, bool PART>
-__global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(const uint8_t* __restrict__ w, int64_t wbytes,
-                                                int64_t N, int64_t K,
-                                                const uint8_t* __restrict__ xq, ActLayoutK L,
-                                                int64_t rows, float* __restrict__ y,
-                                                int32_t* __restrict__ P) {
+template <int FMT, bool PART, bool PAIR = false>
+__global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ w2, int64_t wbytes, int64_t N,
+    int64_t K, const uint8_t* __restrict__ xq, ActLayoutK L, int64_t rows, float* __restrict__ y,
+    int32_t* __restrict__ P) {
     using F = Fmt<FMT>;
     constexpr int NP = pieces_per_lane<FMT>();
     constexpr int SL = 16 * span_stride<FMT>();  // a wave's weight slice
@@ -946,29 +959,32 @@ __global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(const uin
     const uint32_t R = (uint32_t)Rl;
     const int nn = lane & 15, kg = lane >> 4;
     const TileRef t = make_tile(w, wbytes, N, Rl, tile);
+    const TileRef t2 = PAIR ? make_tile(w2, wbytes, N, Rl, tile) : t;
+    const int CT = PAIR ? 2 * C : C;  // superblocks walked: the first matrix's, then the second's
+    auto fetch = [&](int cc, uint4 (&rg)[NP], ActRegsK& a) {
+        const bool second = PAIR && cc >= C;
+        const int c1 = second ? cc - C : cc;
+        fetch_chunk<FMT>(second ? t2 : t, R, c1, 8, lane, rg);
+        fetch_act_k<FMT>(xq, L, c1, lane, a);
+    };
 
     uint4 reg[NP];
     ActRegsK nxt;
-    if (wv < C) {
-        fetch_chunk<FMT>(t, R, wv, 8, lane, reg);
-        fetch_act_k<FMT>(xq, L, wv, lane, nxt);
-    }
-    float yacc = 0.0f;
+    if (wv < CT) fetch(wv, reg, nxt);
+    float yacc = 0.0f, yacc2 = 0.0f;
     // the wave's superblocks are c = wv (mod KS), in ascending order across
     // the windows: the one in flight at a window's end is its first of the next
     int c = wv;
-    for (int w0 = 0; w0 < C; w0 += BDOT_WINDOW) {
-        const int w1 = C - w0 < BDOT_WINDOW ? C : w0 + BDOT_WINDOW;
+    for (int w0 = 0; w0 < CT; w0 += BDOT_WINDOW) {
+        const int w1 = CT - w0 < BDOT_WINDOW ? CT : w0 + BDOT_WINDOW;
         for (; c < w1; c += KS) {
             stage_chunk<FMT>(wl, lane, reg);
             const ActRegsK cur = nxt;
             wave_sync();
             const int cn = c + KS;
-            if (cn < C) {
-                fetch_chunk<FMT>(t, R, cn, 8, lane, reg);
-                fetch_act_k<FMT>(xq, L, cn, lane, nxt);
-            }
-            const uint8_t* rb = wl + nn * span_stride<FMT>() + ((nn * R + c * F::CB) & 15);
+            if (cn < CT) fetch(cn, reg, nxt);
+            const int c1 = PAIR && c >= C ? c - C : c;  // superblock within its matrix
+            const uint8_t* rb = wl + nn * span_stride<FMT>() + ((nn * R + c1 * F::CB) & 15);
             int Pi[4], Qi[4];
             float dw, dmw;
             superblock_k<FMT>(rb, cur, kg, Pi, Qi, dw, dmw);
@@ -979,7 +995,7 @@ __global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(const uin
                 for (int i = 0; i < 4; i++) {
                     const int m = 4 * kg + i;
                     if (m < Bg && n < N) {
-                        const int64_t o = ((int64_t)m * N + n) * C + c;
+                        const int64_t o = ((int64_t)m * N + n) * C + c1;
                         if constexpr (FMT == T_Q4_K) {
                             P[2 * o] = Pi[i];
                             P[2 * o + 1] = Qi[i];
@@ -1001,14 +1017,21 @@ __global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(const uin
         }
         if constexpr (!PART) {
             __syncthreads();
-            if (threadIdx.x < 16 * Bg)
-                for (int cc = 0; cc < w1 - w0; cc++) yacc = yacc + pbuf[cc * 256 + threadIdx.x];
+            if (threadIdx.x < 16 * Bg) {
+                for (int cc = 0; cc < w1 - w0; cc++) {
+                    const float v = pbuf[cc * 256 + threadIdx.x];
+                    if (!PAIR || w0 + cc < C)
+                        yacc = yacc + v;
+                    else
+                        yacc2 = yacc2 + v;
+                }
+            }
             __syncthreads();
         }
     }
     if (!PART && threadIdx.x < 16 * Bg) {
         const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
-        if (n < t.nrows) y[(int64_t)m * N + n0 + n] = yacc;
+        if (n < t.nrows) y[(int64_t)m * N + n0 + n] = PAIR ? swiglu(yacc, yacc2) : yacc;
     }
 }
 
@@ -1512,16 +1535,6 @@ __device__ __forceinline__ int small_div(int a, int b) {
 // chunk straight into registers, issued before the activations are staged.
 // Chunk sums are added in chunk order per row through a small LDS buffer,
 // and each row's result is stored once, at the end.
-// SwiGLU of one output element: silu(g) * u with silu(g) = g / (1 + e^-g),
-// evaluated in f64 as t = exp(-g), s = g / (1 + t), h = s * u and rounded
-// once to f32 (the llama-family feed-forward gate; llamay "Models and
-// formats", architectures table).
-__device__ __forceinline__ float swiglu(float g, float u) {
-    const double gd = (double)g;
-    const double t = exp(-gd);
-    const double s = gd / (1.0 + t);
-    return (float)(s * (double)u);
-}
 
 // Launch modes of the dot kernel: a group of GEMVs (job = blockIdx.y), one
 // GEMV, or one gate/up pair whose rows are computed side by side and leave
@@ -2312,38 +2325,55 @@ int launch_dot_q8k_t(const DotJobs& jobs, int64_t rows, int64_t blocks, size_t s
 // workgroup per 16-row weight tile, KS waves sharing its superblocks (more
 // waves when the tiles alone would leave the chip short of work; at least
 // enough threads for the in-order combine of 16 x rows outputs).
-int launch_bdot_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const uint8_t* xq,
-                    int64_t rows, float* y, int32_t* P, hipStream_t s) {
+int launch_bdot_q8k(int type, const uint8_t* w, const uint8_t* w2, int64_t N, int64_t K,
+                    const uint8_t* xq, int64_t rows, float* y, int32_t* P, hipStream_t s) {
     const int64_t tiles = (N + 15) / 16;
-    const int C = (int)(K / 256);
+    const int C = (int)(K / 256), CT = w2 ? 2 * C : C;
     const ActLayoutK L = act_layout_q8k(rows, K);
-    if (tiles > INT32_MAX || rows < 1 || rows > 16 || !L.gcodes) return (int)hipErrorInvalidValue;
+    if (tiles > INT32_MAX || rows < 1 || rows > 16 || !L.gcodes || (w2 && P))
+        return (int)hipErrorInvalidValue;
     // 8 waves per tile (measured best at 8 wherever a tile has 8 superblocks),
     // fewer when it has fewer; at least one thread per output for the combine
     int KS = 1;
-    while (KS < 8 && KS * 2 <= C) KS *= 2;
+    while (KS < 8 && KS * 2 <= CT) KS *= 2;
     const int need = (int)((16 * rows + 63) / 64);
     if (!P && KS < need) KS = need;
     const int64_t wbytes = N * row_bytes(type, K);
-    const size_t pb = P ? 0 : (size_t)(C < BDOT_WINDOW ? C : BDOT_WINDOW) * 1024;
+    const size_t pb = P ? 0 : (size_t)(CT < BDOT_WINDOW ? CT : BDOT_WINDOW) * 1024;
+    const dim3 grid((unsigned)tiles), block(64 * KS);
     if (type == T_Q4_K) {
         const size_t sh = (size_t)KS * 16 * span_stride<T_Q4_K>() + pb;
         if (P)
-            hipLaunchKernelGGL((k_bdot8k<T_Q4_K, true>), dim3((unsigned)tiles), dim3(64 * KS), sh,
-                               s, w, wbytes, N, K, xq, L, rows, y, P);
+            hipLaunchKernelGGL((k_bdot8k<T_Q4_K, true>), grid, block, sh, s, w, w, wbytes, N, K,
+                               xq, L, rows, y, P);
+        else if (w2)
+            hipLaunchKernelGGL((k_bdot8k<T_Q4_K, false, true>), grid, block, sh, s, w, w2, wbytes,
+                               N, K, xq, L, rows, y, P);
         else
-            hipLaunchKernelGGL((k_bdot8k<T_Q4_K, false>), dim3((unsigned)tiles), dim3(64 * KS), sh,
-                               s, w, wbytes, N, K, xq, L, rows, y, P);
+            hipLaunchKernelGGL((k_bdot8k<T_Q4_K, false>), grid, block, sh, s, w, w, wbytes, N, K,
+                               xq, L, rows, y, P);
     } else {
         const size_t sh = (size_t)KS * 16 * span_stride<T_Q6_K>() + pb;
         if (P)
-            hipLaunchKernelGGL((k_bdot8k<T_Q6_K, true>), dim3((unsigned)tiles), dim3(64 * KS), sh,
-                               s, w, wbytes, N, K, xq, L, rows, y, P);
+            hipLaunchKernelGGL((k_bdot8k<T_Q6_K, true>), grid, block, sh, s, w, w, wbytes, N, K,
+                               xq, L, rows, y, P);
+        else if (w2)
+            hipLaunchKernelGGL((k_bdot8k<T_Q6_K, false, true>), grid, block, sh, s, w, w2, wbytes,
+                               N, K, xq, L, rows, y, P);
         else
-            hipLaunchKernelGGL((k_bdot8k<T_Q6_K, false>), dim3((unsigned)tiles), dim3(64 * KS), sh,
-                               s, w, wbytes, N, K, xq, L, rows, y, P);
+            hipLaunchKernelGGL((k_bdot8k<T_Q6_K, false>), grid, block, sh, s, w, w, wbytes, N, K,
+                               xq, L, rows, y, P);
     }
     return (int)hipGetLastError();
+}
+
+int launch_gateup_q8k(int type, const uint8_t* wg, const uint8_t* wu, int64_t N, int64_t K,
+                      const float* x, uint8_t* xq, int64_t rows, float* h, hipStream_t s) {
+    if (x) {
+        const int rc = launch_quantize_q8k(x, xq, rows, K, s);
+        if (rc) return rc;
+    }
+    return launch_bdot_q8k(type, wg, wu, N, K, xq, rows, h, nullptr, s);
 }
 
 int launch_qmv_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const float* x, uint8_t* xq,
@@ -2356,7 +2386,7 @@ int launch_qmv_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const float
     }
     // BDOT_MIN_ROWS..16 rows: the batched MFMA kernel; prefill: the GEMM
     if (rows > 16) return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, false, s);
-    if (rows >= BDOT_MIN_ROWS) return launch_bdot_q8k(type, w, N, K, xq, rows, y, P, s);
+    if (rows >= BDOT_MIN_ROWS) return launch_bdot_q8k(type, w, nullptr, N, K, xq, rows, y, P, s);
     // fewer rows run the lane-per-chunk kernel, in launches of up to 4
     // activation rows (each reads the weights once)
     if (!use_dot(rows, K)) return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, false, s);

@@ -264,6 +264,22 @@ int quantize_act_q8_k(const float* x, void* xq, int64_t rows, int64_t K, void* s
 int qmv_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
                    void* xq, float* y, void* stream);
 
+/* The gate and up projections of a SwiGLU feed-forward block in decode on
+ * the Q8_K path (as qmv_launch_gateup_swiglu on the Q8_0 path): h[B][N] =
+ * silu(x * Wg^T) * (x * Wu^T), w_gate and w_up two N x K blobs of one type,
+ * Q4_K or Q6_K (else QMV_EINVAL_TYPE), K % 256 == 0, 1 <= B <= 16.  Each
+ * product is bit-identical to qmv_launch_q8k on its own weights; each
+ * element of h is then evaluated in f64 as t = exp(-g), s = g / (1 + t),
+ * s * u and rounded once to f32.  x: [B][K] f32 (4-byte aligned), quantised
+ * into xq first (one launch), or NULL to use the quantize_act_q8_k result
+ * already in xq (qmv_act_bytes_q8k(B, K) bytes, 16-byte aligned).  One
+ * launch of the batched int8-MFMA kernel multiplies matching 16-row tiles of
+ * both matrices and writes h (4-byte aligned, not overlapping x, xq or the
+ * weights). */
+int qmv_launch_gateup_swiglu_q8k(int type, const void* w_gate, const void* w_up, int64_t N,
+                                 int64_t K, const float* x, int64_t B, void* xq, float* h,
+                                 void* stream);
+
 /* Prefill GEMM on the Q8_K path: y[M][N] = x[M][K] * W^T for any M >= 1
  * (M <= 16 runs as qmv_launch_q8k).  The integer superblock partials run on
  * the int8 matrix cores (v_mfma_i32_32x32x32_i8). */

@@ -91,6 +91,13 @@ int main() {
                                       nullptr) == QMV_EINVAL_SHAPE);
     CHECK(qmv_launch_gateup_swiglu_q8(QMV_Q4_K, W, W + 256, 64, 4096, X, 1, XQ, Y, nullptr,
                                       nullptr) == QMV_EINVAL_PTR);
+    CHECK(qmv_launch_gateup_swiglu_q8k(QMV_Q6_K, W, W + 256, 40, 1024, X, 16, XQ, Y, nullptr) ==
+              QMV_OK &&
+          !strcmp(g_last.what, "gateup_q8k") && g_last.N == 40 && g_last.rows == 16 && g_last.y == Y);
+    CHECK(qmv_launch_gateup_swiglu_q8k(QMV_Q4_0, W, W + 256, 40, 1024, X, 1, XQ, Y, nullptr) ==
+          QMV_EINVAL_TYPE);
+    CHECK(qmv_launch_gateup_swiglu_q8k(QMV_Q4_K, W, W + 256, 40, 1024 + 32, X, 1, XQ, Y, nullptr) ==
+          QMV_EINVAL_SHAPE);
     {
         qmv_gemv gv[3] = {{W, 16, 32, X, XQ, Y}, {W, 24, 64, X, nullptr, Y}, {W, 8, 96, X, nullptr, Y}};
         CHECK(qmv_launch_group(QMV_Q8_0, 2, gv, 3, nullptr) == QMV_OK &&

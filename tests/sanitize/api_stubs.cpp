@@ -82,6 +82,10 @@ int launch_gateup(int type, const uint8_t*, const uint8_t*, int64_t N, int64_t K
     g_last.hq = hq;
     return record(hq ? "gateup_q8" : "gateup", type, N, K, rows, x, xq, h);
 }
+int launch_gateup_q8k(int type, const uint8_t*, const uint8_t*, int64_t N, int64_t K,
+                      const float* x, uint8_t* xq, int64_t rows, float* h, hipStream_t) {
+    return record("gateup_q8k", type, N, K, rows, x, xq, h);
+}
 int launch_quantize_q8k(const float* x, uint8_t* xq, int64_t rows, int64_t K, hipStream_t) {
     return record("quantize_q8k", 0, 0, K, rows, x, xq, nullptr);
 }

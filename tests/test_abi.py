@@ -168,6 +168,20 @@ def test_gateup_q8_refusals():
     assert f(g.Q4_K, FAKE, FAKE + 8, 64, 4096, FAKE, 1, FAKE, FAKE, FAKE, None) == -3
 
 
+def test_gateup_q8k_refusals():
+    f = g.lib().qmv_launch_gateup_swiglu_q8k
+    assert f(g.Q8_0, FAKE, FAKE, 64, 4096, FAKE, 1, FAKE, FAKE, None) == -1       # not a K-quant
+    assert f(4, FAKE, FAKE, 64, 4096, FAKE, 1, FAKE, FAKE, None) == -1
+    assert f(g.Q4_K, FAKE, FAKE, 64, 4096 + 32, FAKE, 1, FAKE, FAKE, None) == -2  # K % 256
+    assert f(g.Q4_K, FAKE, FAKE, 0, 4096, FAKE, 1, FAKE, FAKE, None) == -2
+    assert f(g.Q6_K, FAKE, FAKE, 64, 4096, FAKE, 0, FAKE, FAKE, None) == -2
+    assert f(g.Q6_K, FAKE, FAKE, 64, 4096, FAKE, 17, FAKE, FAKE, None) == -2
+    assert f(g.Q4_K, FAKE, FAKE + 8, 64, 4096, FAKE, 1, FAKE, FAKE, None) == -3   # w_up align
+    assert f(g.Q4_K, FAKE, FAKE, 64, 4096, FAKE + 2, 1, FAKE, FAKE, None) == -3   # x align
+    assert f(g.Q4_K, FAKE, FAKE, 64, 4096, FAKE, 1, FAKE + 4, FAKE, None) == -3   # xq align
+    assert f(g.Q4_K, FAKE, FAKE, 64, 4096, FAKE, 1, FAKE, None, None) == -3       # h NULL
+
+
 def test_noalloc_refusals():
     L = g.lib()
     # the fixed scratch admits every K <= 65536 at B = 16 (and no more at K = 2^17)

@@ -233,3 +233,31 @@ def test_q8k_batched_long_rows(g, fmt):
     assert_bitwise(y, oracle.matmul_q8k_canon_f32(fmt, blob, N, K, xq, M), "long rows f32 order")
     P = host(g.partials_q8k(fmt, dev(blob), N, K, g.quantize_q8k(xd), M))
     assert_bitwise(P, oracle.partials_q8k(fmt, blob, N, K, xq, M), "long rows partials")
+
+
+@pytest.mark.parametrize("fmt,N,K,B", [(synth.Q4_K, 14336, 4096, 16), (synth.Q4_K, 333, 1024, 5),
+                                       (synth.Q6_K, 90, 1024, 1), (synth.Q6_K, 77, 4352, 11),
+                                       (synth.Q4_K, 40, 65536, 8), (synth.Q6_K, 16, 256, 16)])
+def test_gateup_swiglu_q8k(g, fmt, N, K, B):
+    """qmv_launch_gateup_swiglu_q8k: h bit-identical to the oracle's SwiGLU of
+    the oracle's gate and up products in the Q8_K f32 order (sampled rows at
+    the 8B-class shape), with x quantised by the launch and staged."""
+    wg, _ = synth.weights(fmt, N, K, 2900 + N, dscale=0.02)
+    wu, _ = synth.weights(fmt, N, K, 2901 + N, dscale=0.02)
+    x = synth.activations(B, K, 2902 + B)
+    xd = dev(x)
+    print(f"gate/up swiglu q8k fmt={fmt} N={N} K={K} B={B}", flush=True)
+    h = host(g.gateup_swiglu_q8k(fmt, dev(wg), dev(wu), N, K, x=xd))
+    xq = g.quantize_q8k(xd)
+    h2 = host(g.gateup_swiglu_q8k(fmt, dev(wg), dev(wu), N, K, xq=xq, B=B))
+    assert_bitwise(h2, h, "staged x")
+    rows = np.arange(N)
+    if N > 400:
+        rng = np.random.Generator(np.random.PCG64(2903))
+        rows = np.unique(np.concatenate([[0, 15, 16, N - 1], rng.choice(N, 200, replace=False)]))
+    R = synth.row_bytes(fmt, K)
+    sub = lambda blob: np.ascontiguousarray(blob.reshape(N, R)[rows]).reshape(-1)
+    xo = oracle.quantize_act_q8k(x)
+    gate = oracle.matmul_q8k_canon_f32(fmt, sub(wg), len(rows), K, xo, B)
+    up = oracle.matmul_q8k_canon_f32(fmt, sub(wu), len(rows), K, xo, B)
+    assert_bitwise(np.ascontiguousarray(h[:, rows]), oracle.swiglu(gate, up), "h = silu(g) u")
