@@ -58,8 +58,9 @@ __device__ __forceinline__ float inv_scale(float d) {
 // One wave per (row, superblock), 4 elements per lane: amax over the wave,
 // d = amax/127, codes = round-half-away(x * id); the public Q8_K block and
 // the row-major staging (codes, d per 32 codes, the two 16-code sums of each
-// 32 codes), and for at most 16 rows the MFMA-order copy of the batched
-// decode kernel.  FROM_PUBLIC: take codes and d from the Q8_K block in xq.
+// 32 codes, the digits of each 32-code sum), and for at most 16 rows the
+// MFMA-order copy of the batched decode kernel.  FROM_PUBLIC: take codes and
+// d from the Q8_K block in xq.
 template <bool FROM_PUBLIC, bool A16>
 __global__ __launch_bounds__(256) void k_quantize_q8k(const float* __restrict__ x,
                                                       uint8_t* __restrict__ xq, int64_t rows,
@@ -109,6 +110,21 @@ __global__ __launch_bounds__(256) void k_quantize_q8k(const float* __restrict__ 
         reinterpret_cast<int32_t*>(xq + L.rs16)[b] =
             (int32_t)(((uint32_t)s16 & 0xFFFFu) | ((uint32_t)s16b << 16));
     }
+    if ((lane & 7) == 0) {
+        // the block's 32-code sum (|S| <= 4064) as two digits: block j's lo
+        // at byte 8 (j / 4) + j % 4, its hi 4 bytes later
+        const int j = lane >> 3, S = s16 + s16b;
+        const uint8_t lo = (uint8_t)(S & 63), hi = (uint8_t)((S >> 6) & 0xFF);
+        const int at = 8 * (j >> 2) + (j & 3);
+        uint8_t* sd = xq + L.rsd + task * 16 + at;
+        sd[0] = lo;
+        sd[4] = hi;
+        if (L.gsd) {
+            uint8_t* gs = xq + L.gsd + sb * 256 + r * 16 + at;
+            gs[0] = lo;
+            gs[4] = hi;
+        }
+    }
     if (L.gcodes) {
         // element 4 lane + t is byte 8 kg + 4 (lane & 1) + t of block j:
         // j = lane / 8, kg = (lane % 8) / 2
@@ -117,12 +133,6 @@ __global__ __launch_bounds__(256) void k_quantize_q8k(const float* __restrict__ 
         *reinterpret_cast<uint32_t*>(gb + (j >> 1) * 1024 + (r + 16 * kg) * 16 + (j & 1) * 8 +
                                      4 * (lane & 1)) = c4;
         if (lane == 0) reinterpret_cast<float*>(xq + L.gda)[sb * 16 + r] = d;
-        if ((lane & 7) == 0) {
-            const int S = s16 + s16b;  // the block's 32-code sum, |S| <= 4064
-            uint8_t* sd = xq + L.gsd + sb * 256 + r * 16;
-            sd[j] = (uint8_t)(S & 63);
-            sd[8 + j] = (uint8_t)((S >> 6) & 0xFF);
-        }
     }
 }
 
@@ -244,14 +254,15 @@ __device__ __forceinline__ void decode_block(const WRawK<FMT>& r, int j, int h, 
 // LDS of one superblock step: the activation tile (TM rows x 256 code bytes
 // as 16 pieces of 16 bytes; piece q of row r in slot 16 r + (q ^ (r & 15)),
 // so that the lanes of one ds_read_b128 pass hit different banks), the rows'
-// f32 scales and (Q4_K) their 32-code sums as pairs of int16.
-// (d and s16 are sized for every wave's copy instruction, whatever TM, so
+// f32 scales and (Q4_K) the digits of their eight 32-code sums (16 bytes a
+// row, as the quantiser leaves them).
+// (d and sd are sized for every wave's copy instruction, whatever TM, so
 // that each wave issues the same number of copies; slots past the tile's
 // rows hold duplicates that are not read)
 template <int TM> struct StageK {
     uint4 a[TM * 16];
     float d[256];
-    int32_t s16[1024];
+    uint4 sd[256];
 };
 
 // Load-time repacked weights (qmv_prepare): per 32-row tile and superblock a
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
     // each staging array), which keeps one register per address
     const uint8_t* abase = xq + L.rcodes + m0 * K;
     const uint8_t* dbase = xq + L.rda + m0 * nb * 4;
-    const uint8_t* sbase = xq + L.rs16 + m0 * nb * 4;
+    const uint8_t* sbase = xq + L.rsd + m0 * nsb * 16;
     uint32_t aoff[RPW / 4];
 #pragma unroll
     for (int i = 0; i < RPW / 4; i++) {
@@ -332,8 +343,7 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
     }
     const int drow = 64 * wv + lane;  // the row whose f32 scale this lane stages
     const uint32_t doff = (uint32_t)((arow(drow < TM ? drow : 0) - m0) * nb * 4);
-    const uint32_t soff = (uint32_t)(
-        (arow((64 * wv + lane) >> 1 < TM ? (64 * wv + lane) >> 1 : 0) - m0) * nb * 4 + 16 * (lane & 1));
+    const uint32_t soff = (uint32_t)((arow(drow < TM ? drow : 0) - m0) * nsb * 16);
     // (the global operands are passed as plain void pointers: given as typed
     // pointer arithmetic, the host pass of this compiler drops the kernel)
     auto issue = [&](int s, StageK<TM>* __restrict__ dst) {
@@ -345,10 +355,9 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
         __builtin_amdgcn_global_load_lds((const void*)(dbase + (doff + 32u * s)), (lds_void*)&dst->d[64 * wv],
                                          4, 0, 0);
         if constexpr (FMT == T_Q4_K) {
-            // each row's 8 sums (32 bytes): two 16-byte pieces, global lanes
-            // 2r, 2r+1 (64 wv + lane); a wave's 64 pieces fill 256 ints
-            __builtin_amdgcn_global_load_lds((const void*)(sbase + (soff + 32u * s)),
-                                             (lds_void*)&dst->s16[256 * wv], 16, 0, 0);
+            // the rows' sum digits, 16 bytes per row (row 64 wv + lane)
+            __builtin_amdgcn_global_load_lds((const void*)(sbase + (soff + 16u * s)),
+                                             (lds_void*)&dst->sd[64 * wv], 16, 0, 0);
         }
     };
     // the copies one issue() makes per wave, and an s_waitcnt that lets
@@ -468,16 +477,11 @@ __global__ __launch_bounds__(256, WM >= 4 ? 1 : 2) void k_gemm8k(const uint8_t* 
             int Qv[16];
             if constexpr (FMT == T_Q4_K) {
                 // the row's 32-code sums S_j (j = 4h..4h+3) as two int8 digits
-                // against m_j, in an otherwise-zero MFMA per digit
-                const int4 s4 = *reinterpret_cast<const int4*>(&cur->s16[(32 * t + lr) * 8 + 4 * h]);
-                const int sv[4] = {s4.x, s4.y, s4.z, s4.w};
-                uint32_t slo = 0, shi = 0;
-#pragma unroll
-                for (int t2 = 0; t2 < 4; t2++) {
-                    const int S = (int)(int16_t)(sv[t2] & 0xFFFF) + (sv[t2] >> 16);  // |S| <= 4064
-                    slo |= (uint32_t)(S & 63) << (8 * t2);
-                    shi |= (uint32_t)((S >> 6) & 0xFF) << (8 * t2);
-                }
+                // (from the quantiser) against m_j, in an otherwise-zero MFMA
+                // per digit
+                const uint2 sd2 = *reinterpret_cast<const uint2*>(
+                    reinterpret_cast<const uint8_t*>(&cur->sd[32 * t + lr]) + 8 * h);
+                const uint32_t slo = sd2.x, shi = sd2.y;
                 const v16i ql = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i){(int)slo, 0, 0, 0}, bm, zero16, 0, 0, 0);
                 const v16i qh = __builtin_amdgcn_mfma_i32_32x32x32_i8((v4i){(int)shi, 0, 0, 0}, bm, zero16, 0, 0, 0);
 #pragma unroll

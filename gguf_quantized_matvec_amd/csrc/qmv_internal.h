@@ -62,21 +62,25 @@ inline ActLayout act_layout(int64_t rows, int64_t K) {
 //     rda    [rows][K/32] f32  d of the element's superblock, per 32 codes
 //     rs16   [rows][K/32] i32  sums of the two 16-code halves of each 32
 //                              codes, as two int16 (low half = first)
-// (the layout of the lane-per-chunk GEMV's Q8_0 staging, so that kernel
-// stages either; rca is not used on this path and aliases rda).
+//     rsd    [rows][K/256][16] int8  the superblock's eight 32-code sums S_j
+//                              as two digits, S = 64 hi + lo, lo = S & 63:
+//                              lo of S_0..S_3, hi of S_0..S_3, lo of
+//                              S_4..S_7, hi of S_4..S_7 (the operands of the
+//                              Q4_K min-term MFMAs)
+// (rcodes, rda, rs16: the layout of the lane-per-chunk GEMV's Q8_0 staging,
+// so that kernel stages either; rca is not used on this path and aliases
+// rda).
 //   For rows <= 16 (gcodes != 0) also the copy the batched decode kernel
 //   reads, in the operand order of v_mfma_i32_16x16x32_i8, per superblock c:
 //     gcodes [c][p = 0..3][lane 0..63][16]  lane l = m + 16 kg: row m's codes
 //                                           8kg..8kg+7 of block 2p, then of
 //                                           block 2p+1
 //     gda    [c][16] f32                    row m's Q8_K d
-//     gsd    [c][16][16] int8               row m's eight 32-code sums S_j as
-//                                           digits, S & 63 at [j], S >> 6 at
-//                                           [8 + j] (S = 64 hi + lo)
+//     gsd    [c][16][16] int8               row m's sum digits, as in rsd
 //   (entries of rows m >= rows are not written: they only ever feed outputs
 //   of rows that are not stored).
 struct ActLayoutK {
-    int64_t nb, nsb, pub, rcodes, rda, rs16, gcodes, gda, gsd, total;
+    int64_t nb, nsb, pub, rcodes, rda, rs16, rsd, gcodes, gda, gsd, total;
 };
 inline ActLayoutK act_layout_q8k(int64_t rows, int64_t K) {
     ActLayoutK L;
@@ -86,7 +90,8 @@ inline ActLayoutK act_layout_q8k(int64_t rows, int64_t K) {
     L.rcodes = (L.pub + 255) & ~int64_t(255);
     L.rda = (L.rcodes + rows * K + 255) & ~int64_t(255);
     L.rs16 = (L.rda + rows * L.nb * 4 + 255) & ~int64_t(255);
-    L.total = (L.rs16 + rows * L.nb * 4 + 255) & ~int64_t(255);
+    L.rsd = (L.rs16 + rows * L.nb * 4 + 255) & ~int64_t(255);
+    L.total = (L.rsd + rows * L.nsb * 16 + 255) & ~int64_t(255);
     L.gcodes = L.gda = L.gsd = 0;
     if (rows <= 16) {
         L.gcodes = L.total;

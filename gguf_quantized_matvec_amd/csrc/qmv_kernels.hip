@@ -844,18 +844,23 @@ constexpr int BDOT_WINDOW = 32;
 struct ActRegsK {
     uint4 a[4];   // blocks 2p, 2p+1: activation row l%16, codes 8kg..8kg+7 of each
     float4 da;    // Q8_K d of activation rows 4kg..4kg+3
-    uint4 sd;     // Q4_K, k-group 0: row l%16's digits of S_0..S_7 (lo, then hi)
+    uint4 sd;     // Q4_K, k-group 0: row l%16's digits of S_0..S_7 (lo 0-3, hi 0-3, lo 4-7, hi 4-7)
 };
 
+// The activation side of superblock c from the quantiser's operand-order
+// copy (gc, gd, gs: its uniform starts; 32-bit offsets on uniform bases keep
+// one register per address).
 template <int FMT>
-__device__ __forceinline__ void fetch_act_k(const uint8_t* xq, const ActLayoutK& L, int c, int lane,
+__device__ __forceinline__ void fetch_act_k(const uint8_t* __restrict__ gc,
+                                            const uint8_t* __restrict__ gd,
+                                            const uint8_t* __restrict__ gs, int c, int lane,
                                             ActRegsK& r) {
-    const uint8_t* cb = xq + L.gcodes + (int64_t)c * 4096 + lane * 16;
+    const uint32_t co = (uint32_t)c * 4096u + (uint32_t)lane * 16u;
 #pragma unroll
-    for (int p = 0; p < 4; p++) r.a[p] = *reinterpret_cast<const uint4*>(cb + 1024 * p);
-    r.da = *reinterpret_cast<const float4*>(xq + L.gda + (int64_t)c * 64 + 16 * (lane >> 4));
+    for (int p = 0; p < 4; p++) r.a[p] = *reinterpret_cast<const uint4*>(gc + (co + 1024u * p));
+    r.da = *reinterpret_cast<const float4*>(gd + ((uint32_t)c * 64u + 16u * (uint32_t)(lane >> 4)));
     if constexpr (FMT == T_Q4_K)
-        r.sd = lane < 16 ? *reinterpret_cast<const uint4*>(xq + L.gsd + (int64_t)c * 256 + 16 * lane)
+        r.sd = lane < 16 ? *reinterpret_cast<const uint4*>(gs + ((uint32_t)c * 256u + 16u * (uint32_t)lane))
                          : make_uint4(0, 0, 0, 0);
 }
 
@@ -903,8 +908,8 @@ __device__ __forceinline__ void superblock_k(const uint8_t* rb, const ActRegsK& 
         }
         // min term: k-group 0 carries the S_j digits against m_j, j = 0..7
         const long bm = kg == 0 ? (long)mins : 0;
-        const long slo = (long)(((uint64_t)A.sd.y << 32) | A.sd.x);
-        const long shi = (long)(((uint64_t)A.sd.w << 32) | A.sd.z);
+        const long slo = (long)(((uint64_t)A.sd.z << 32) | A.sd.x);
+        const long shi = (long)(((uint64_t)A.sd.w << 32) | A.sd.y);
         const v4i ql = __builtin_amdgcn_mfma_i32_16x16x32_i8(slo, bm, zero, 0, 0, 0);
         const v4i qh = __builtin_amdgcn_mfma_i32_16x16x32_i8(shi, bm, zero, 0, 0, 0);
 #pragma unroll
@@ -961,11 +966,14 @@ __global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(
     const TileRef t = make_tile(w, wbytes, N, Rl, tile);
     const TileRef t2 = PAIR ? make_tile(w2, wbytes, N, Rl, tile) : t;
     const int CT = PAIR ? 2 * C : C;  // superblocks walked: the first matrix's, then the second's
+    const uint8_t* gc = xq + L.gcodes;
+    const uint8_t* gd = xq + L.gda;
+    const uint8_t* gs = xq + L.gsd;
     auto fetch = [&](int cc, uint4 (&rg)[NP], ActRegsK& a) {
         const bool second = PAIR && cc >= C;
         const int c1 = second ? cc - C : cc;
         fetch_chunk<FMT>(second ? t2 : t, R, c1, 8, lane, rg);
-        fetch_act_k<FMT>(xq, L, c1, lane, a);
+        fetch_act_k<FMT>(gc, gd, gs, c1, lane, a);
     };
 
     uint4 reg[NP];
