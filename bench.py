@@ -421,11 +421,17 @@ def decode_8b_q8k(torch, g, synth):
 
 
 def lm_head(torch, g, synth):
+    """The LM head at batch 1, 4, 16 (Q8_0 activations) and on the Q8_K path
+    at 4 and 16."""
     res = {}
     for B in (1, 4, 16):
         us, nb, R = matrix_us(torch, g, synth, Q6_K, 151936, 1024, B, synth.seed_for(2, 0), 0.01,
                               1 << 30)
         res[f"B{B}"] = gemv_row(us, nb, B)
+    for B in (4, 16):
+        us, nb, R = matrix_us(torch, g, synth, Q6_K, 151936, 1024, B, synth.seed_for(2, 0), 0.01,
+                              1 << 30, q8k=True)
+        res[f"B{B}_q8k"] = gemv_row(us, nb, B)
     return res
 
 
