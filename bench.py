@@ -195,8 +195,12 @@ class Layer:
         self.y = {n: torch.empty(B, N, dtype=torch.float32, device="cuda")
                   for n, _, N, _ in LAYER if n not in ("gate", "up")}
         self._groups = []
+        self._groups_k = []  # the Q8_K path's q, k, v on one staged xq
         for c in range(self.R):
             P = lambda n: self.w[n][c].data_ptr()
+            self._groups_k.append((g.Gemv * 3)(
+                *[g.Gemv(P(n), N, 4096, None, self.xq_a.data_ptr(), self.y[n].data_ptr())
+                  for n, N in (("q", 4096), ("k", 1024), ("v", 1024))]))
             fused = B <= 4
             xa = self.xa.data_ptr() if fused else None
             xq_k = None if fused else self.xq_a.data_ptr()
@@ -233,7 +237,7 @@ class Layer:
         s = torch.cuda.current_stream().cuda_stream
         W = lambda n: self.w[n][c].data_ptr()
         if self.q8k:
-            self._stage_q8k(name, W, s)
+            self._stage_q8k(name, W, s, c)
             return
         if name == "A_qkv":
             if B > 4:   # the group runs its GEMVs one after another: quantise once
@@ -253,16 +257,15 @@ class Layer:
             _check(g, L.qmv_launch(Q6_K, W("down"), 4096, 14336, None, B, self.xq_d.data_ptr(),
                                    self.y["down"].data_ptr(), s), "down")
 
-    def _stage_q8k(self, name, W, s):
-        """The stage on the Q8_K path: A quantises x once for q, k, v; C is
-        the paired gate/up launch with the SwiGLU; B and D quantise their x."""
+    def _stage_q8k(self, name, W, s, c):
+        """The stage on the Q8_K path: A quantises x once for q, k, v, one
+        grouped launch; C is the paired gate/up launch with the SwiGLU; B and
+        D quantise their x."""
         g, B, L = self.g, self.B, self.g.lib()
         if name == "A_qkv":
             _check(g, L.quantize_act_q8_k(self.xa.data_ptr(), self.xq_a.data_ptr(), B, 4096, s),
                    "quantize q8k")
-            for n, N in (("q", 4096), ("k", 1024), ("v", 1024)):
-                _check(g, L.qmv_launch_q8k(Q4_K, W(n), N, 4096, None, B, self.xq_a.data_ptr(),
-                                           self.y[n].data_ptr(), s), n)
+            _check(g, L.qmv_launch_group_q8k(Q4_K, B, self._groups_k[c], 3, s), "qkv q8k")
         elif name == "B_o":
             _check(g, L.qmv_launch_q8k(Q4_K, W("o"), 4096, 4096, self.xo.data_ptr(), B,
                                        self.xq_o.data_ptr(), self.y["o"].data_ptr(), s), "o")
@@ -948,9 +951,10 @@ def main():
             "ms_per_step": round(r16k["wall_s"] / n16 * 1e3, 5),
             "tok_s": round(16 * n16 / r16k["wall_s"], 1), "steps": n16,
             "stage_us": {k: round(v, 2) for k, v in r16k["stage_us"].items()},
-            "path": "the same step with Q8_K activations: A quantises once, then q, k, v "
-                    "(qmv_launch_q8k); B, D qmv_launch_q8k; C qmv_launch_gateup_swiglu_q8k; "
-                    "the batched int8-MFMA kernel, one f32 term per superblock"}
+            "path": "the same step with Q8_K activations: A quantises once, then q, k, v in "
+                    "one qmv_launch_group_q8k; B, D qmv_launch_q8k; C "
+                    "qmv_launch_gateup_swiglu_q8k; the batched int8-MFMA kernel, one f32 term "
+                    "per superblock"}
         print("step: prefill M=2048", file=sys.stderr, flush=True)
         out["prefill_m2048"] = {"unit": "int8-equivalent TOPS", "peak": INT8_PEAK_TOPS,
                                 **prefill_8b(torch, g, synth)}

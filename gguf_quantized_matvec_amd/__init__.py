@@ -22,7 +22,7 @@ BLOCK = {Q8_0: (32, 34), Q4_0: (32, 18), Q5_0: (32, 22), Q4_1: (32, 20), Q5_1: (
 EXPORTS = ("qmv_act_bytes", "quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
            "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc", "qmv_gateup_act_bytes",
            "qmv_launch_gateup_swiglu", "qmv_launch_gateup_swiglu_q8", "qmv_act_bytes_q8k", "quantize_act_q8_k", "qmv_launch_q8k",
-           "qmv_launch_gateup_swiglu_q8k", "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepared_bytes", "qmv_prepare",
+           "qmv_launch_gateup_swiglu_q8k", "qmv_launch_group_q8k", "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepared_bytes", "qmv_prepare",
            "qmm_launch_q8k_prepared", "qmm_partials_q8k_prepared_launch", "qmv_strerror")
 MAX_BATCH = 16
 MAX_GROUP = 8
@@ -76,10 +76,11 @@ def lib() -> ctypes.CDLL:
         L.qmv_launch_gateup_swiglu.argtypes = [I, P, P, I64, I64, P, I64, P, P, P]
         L.qmv_launch_gateup_swiglu_q8.argtypes = [I, P, P, I64, I64, P, I64, P, P, P, P]
         L.qmv_launch_gateup_swiglu_q8k.argtypes = [I, P, P, I64, I64, P, I64, P, P, P]
+        L.qmv_launch_group_q8k.argtypes = [I, I64, ctypes.POINTER(Gemv), I, P]
         for f in ("quantize_act_q8_0", "qmv_launch", "qmv_launch_group", "qmm_launch",
                   "qmv_partials_launch", "qmm_partials_launch", "qmv_launch_noalloc",
                   "qmv_launch_gateup_swiglu", "qmv_launch_gateup_swiglu_q8", "quantize_act_q8_k", "qmv_launch_q8k",
-                  "qmv_launch_gateup_swiglu_q8k", "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepare",
+                  "qmv_launch_gateup_swiglu_q8k", "qmv_launch_group_q8k", "qmm_launch_q8k", "qmv_partials_q8k_launch", "qmv_prepare",
                   "qmm_launch_q8k_prepared", "qmm_partials_q8k_prepared_launch"):
             getattr(L, f).restype = I
         L.qmv_strerror.argtypes = [I]
@@ -116,6 +117,12 @@ def qmv_launch_group(type: int, B: int, gemvs, stream: int = 0) -> None:
     """gemvs: a sequence of Gemv (or of (w, N, K, x, xq, y) tuples)."""
     arr = (Gemv * len(gemvs))(*[gv if isinstance(gv, Gemv) else Gemv(*gv) for gv in gemvs])
     _check(lib().qmv_launch_group(type, B, arr, len(gemvs), stream), "qmv_launch_group")
+
+
+def qmv_launch_group_q8k(type: int, B: int, gemvs, stream: int = 0) -> None:
+    """gemvs: a sequence of Gemv (or of (w, N, K, x, xq, y) tuples), Q8_K path."""
+    arr = (Gemv * len(gemvs))(*[gv if isinstance(gv, Gemv) else Gemv(*gv) for gv in gemvs])
+    _check(lib().qmv_launch_group_q8k(type, B, arr, len(gemvs), stream), "qmv_launch_group_q8k")
 
 
 def qmm_launch(type: int, w: int, N: int, K: int, x, M: int, xq: int, y: int,

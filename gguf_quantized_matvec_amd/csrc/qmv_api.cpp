@@ -276,6 +276,27 @@ int qmm_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x
     return q8k_common(type, w, N, K, x, M, QMV_MAX_M, xq, y, nullptr, stream);
 }
 
+int qmv_launch_group_q8k(int type, int64_t B, const qmv_gemv* g, int count, void* stream) {
+    if (type != QMV_Q4_K && type != QMV_Q6_K) return QMV_EINVAL_TYPE;
+    if (!g) return QMV_EINVAL_PTR;
+    if (count < 1 || count > QMV_MAX_GROUP || B < 1 || B > QMV_MAX_BATCH) return QMV_EINVAL_SHAPE;
+    const bool quantise = g[0].x != nullptr;
+    qmv::GemvDesc d[QMV_MAX_GROUP];
+    for (int k = 0; k < count; k++) {
+        const int rc = check_weights(type, g[k].w, g[k].N, g[k].K);
+        if (rc) return rc;
+        if ((g[k].x != nullptr) != quantise) return QMV_EINVAL_PTR;
+        if (!g[k].y || !aligned(g[k].y, 4)) return QMV_EINVAL_PTR;
+        if (g[k].x && !aligned(g[k].x, 4)) return QMV_EINVAL_PTR;
+        if (!g[k].xq || !aligned(g[k].xq, 16)) return QMV_EINVAL_PTR;
+        d[k] = qmv::GemvDesc{static_cast<const uint8_t*>(g[k].w), g[k].N, g[k].K, g[k].x,
+                             static_cast<uint8_t*>(g[k].xq), g[k].y};
+    }
+    const int rc = check_device();
+    if (rc) return rc;
+    return launched(qmv::launch_group_q8k(type, d, count, B, static_cast<hipStream_t>(stream)));
+}
+
 int qmv_launch_gateup_swiglu_q8k(int type, const void* w_gate, const void* w_up, int64_t N,
                                  int64_t K, const float* x, int64_t B, void* xq, float* h,
                                  void* stream) {

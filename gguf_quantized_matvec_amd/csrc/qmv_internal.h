@@ -170,6 +170,10 @@ int launch_qmm(int type, const uint8_t* w, int64_t N, int64_t K, const float* x,
 // (x == NULL for launch_quantize_q8k: rebuild the staging from the Q8_K
 // blocks already in xq).  P != NULL: the exact superblock partials go to P.
 int launch_quantize_q8k(const float* x, uint8_t* xq, int64_t rows, int64_t K, hipStream_t s);
+// Several GEMVs on the Q8_K path (1..16 rows; x of every entry, if given,
+// quantised into its xq first): one launch of the batched kernel when the
+// rows take it and every entry has the same K, else one after another.
+int launch_group_q8k(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s);
 // Gate/up pair with the SwiGLU on the Q8_K path (1..16 rows): x (if given)
 // quantised into xq, then one launch of the batched kernel writing h.
 int launch_gateup_q8k(int type, const uint8_t* wg, const uint8_t* wu, int64_t N, int64_t K,

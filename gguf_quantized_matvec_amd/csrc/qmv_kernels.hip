@@ -945,11 +945,14 @@ __device__ __forceinline__ void superblock_k(const uint8_t* rb, const ActRegsK& 
 
 // (Q4_K: at most 128 VGPRs, i.e. 4 waves per SIMD; with one register more,
 // 3 waves, the 14336 x 4096 GEMV at 16 rows took 16.5 us against 13.0)
-template <int FMT, bool PART, bool PAIR = false>
-__global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(
-    const uint8_t* __restrict__ w, const uint8_t* __restrict__ w2, int64_t wbytes, int64_t N,
-    int64_t K, const uint8_t* __restrict__ xq, ActLayoutK L, int64_t rows, float* __restrict__ y,
-    int32_t* __restrict__ P) {
+// The work of one workgroup on weight tile `tile` (the kernels below).
+template <int FMT, bool PART, bool PAIR>
+__device__ __forceinline__ void bdot_tile(const uint8_t* __restrict__ w,
+                                          const uint8_t* __restrict__ w2, int64_t wbytes,
+                                          int64_t N, int64_t K, const uint8_t* __restrict__ xq,
+                                          const ActLayoutK& L, int64_t rows,
+                                          float* __restrict__ y, int32_t* __restrict__ P,
+                                          int64_t tile) {
     using F = Fmt<FMT>;
     constexpr int NP = pieces_per_lane<FMT>();
     constexpr int SL = 16 * span_stride<FMT>();  // a wave's weight slice
@@ -957,7 +960,7 @@ __global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6), KS = blockDim.x >> 6;
     uint8_t* wl = smem + wv * SL;
     float* pbuf = reinterpret_cast<float*>(smem + KS * SL);  // [window][256]
-    const int64_t tile = blockIdx.x, n0 = tile * 16;
+    const int64_t n0 = tile * 16;
     const int Bg = (int)(rows < 16 ? rows : 16);
     const int C = (int)(K >> 8);
     const int64_t Rl = (int64_t)C * F::BB;
@@ -1041,6 +1044,36 @@ __global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(
         const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
         if (n < t.nrows) y[(int64_t)m * N + n0 + n] = PAIR ? swiglu(yacc, yacc2) : yacc;
     }
+}
+
+template <int FMT, bool PART, bool PAIR = false>
+__global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k(
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ w2, int64_t wbytes, int64_t N,
+    int64_t K, const uint8_t* __restrict__ xq, ActLayoutK L, int64_t rows, float* __restrict__ y,
+    int32_t* __restrict__ P) {
+    bdot_tile<FMT, PART, PAIR>(w, w2, wbytes, N, K, xq, L, rows, y, P, blockIdx.x);
+}
+
+// Several GEMVs of one K in one launch: job blockIdx.y, its tile blockIdx.x
+// (workgroups past a job's tiles exit at once).
+struct BdotJob {
+    const uint8_t* w;
+    const uint8_t* xq;
+    float* y;
+    int64_t N;
+};
+struct BdotJobs {
+    BdotJob j[8];
+};
+
+template <int FMT>
+__global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k_group(
+    BdotJobs jobs, int64_t K, ActLayoutK L, int64_t rows) {
+    const BdotJob& J = jobs.j[blockIdx.y];
+    const int64_t tiles = (J.N + 15) / 16;
+    if ((int64_t)blockIdx.x >= tiles) return;  // uniform over the workgroup
+    const int64_t wbytes = J.N * (K / 256) * Fmt<FMT>::BB;
+    bdot_tile<FMT, false, false>(J.w, J.w, wbytes, J.N, K, J.xq, L, rows, J.y, nullptr, blockIdx.x);
 }
 
 // ------------------------------------------------- lane-per-chunk GEMV ----
@@ -2372,6 +2405,52 @@ int launch_bdot_q8k(int type, const uint8_t* w, const uint8_t* w2, int64_t N, in
             hipLaunchKernelGGL((k_bdot8k<T_Q6_K, false>), grid, block, sh, s, w, w, wbytes, N, K,
                                xq, L, rows, y, P);
     }
+    return (int)hipGetLastError();
+}
+
+int launch_group_q8k(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t s) {
+    if (count < 1 || count > 8) return (int)hipErrorInvalidValue;
+    const int64_t K = d[0].K;
+    bool one = rows >= BDOT_MIN_ROWS && rows <= 16;
+    for (int k = 0; k < count; k++) one = one && d[k].K == K;
+    for (int k = 0; k < count; k++) {
+        if (d[k].x) {
+            const int rc = launch_quantize_q8k(d[k].x, d[k].xq, rows, d[k].K, s);
+            if (rc) return rc;
+        }
+    }
+    if (!one) {
+        // one after another, each as qmv_launch_q8k on its staged xq
+        for (int k = 0; k < count; k++) {
+            const int rc = launch_qmv_q8k(type, d[k].w, d[k].N, d[k].K, nullptr, d[k].xq, rows,
+                                          d[k].y, nullptr, s);
+            if (rc) return rc;
+        }
+        return 0;
+    }
+    const int C = (int)(K / 256);
+    const ActLayoutK L = act_layout_q8k(rows, K);
+    BdotJobs jobs{};
+    int64_t tmax = 0;
+    for (int k = 0; k < count; k++) {
+        jobs.j[k] = BdotJob{d[k].w, d[k].xq, d[k].y, d[k].N};
+        const int64_t t = (d[k].N + 15) / 16;
+        tmax = t > tmax ? t : tmax;
+    }
+    if (tmax > INT32_MAX || !L.gcodes) return (int)hipErrorInvalidValue;
+    // the single launch's wave count and LDS (one K, so one choice)
+    int KS = 1;
+    while (KS < 8 && KS * 2 <= C) KS *= 2;
+    const int need = (int)((16 * rows + 63) / 64);
+    if (KS < need) KS = need;
+    const size_t pb = (size_t)(C < BDOT_WINDOW ? C : BDOT_WINDOW) * 1024;
+    const dim3 grid((unsigned)tmax, (unsigned)count), block(64 * KS);
+    if (type == T_Q4_K)
+        hipLaunchKernelGGL(k_bdot8k_group<T_Q4_K>, grid, block,
+                           (size_t)KS * 16 * span_stride<T_Q4_K>() + pb, s, jobs, K, L, rows);
+    else
+        hipLaunchKernelGGL(k_bdot8k_group<T_Q6_K>, grid, block,
+                           (size_t)KS * 16 * span_stride<T_Q6_K>() + pb, s, jobs, K, L, rows);
     return (int)hipGetLastError();
 }
 

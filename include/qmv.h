@@ -264,6 +264,19 @@ int quantize_act_q8_k(const float* x, void* xq, int64_t rows, int64_t K, void* s
 int qmv_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
                    void* xq, float* y, void* stream);
 
+/* Several independent decode GEMVs of one K-quant type (Q4_K or Q6_K, else
+ * QMV_EINVAL_TYPE) and one batch B on the Q8_K path, such as the q, k and v
+ * projections of a decode step: entry k gives bit-identical y (and xq, when
+ * written) to qmv_launch_q8k(type, w, N, K, x, B, xq, y) on its own.  Every
+ * entry needs its xq (qmv_act_bytes_q8k(B, K) bytes, 16-byte aligned; NULL:
+ * QMV_EINVAL_PTR); either every entry quantises its x into it (one launch
+ * each) or every entry reads it staged (x NULL; entries may share one xq).
+ * For B = 5..16 with every entry of one K, the products are one launch of
+ * the batched int8-MFMA kernel (a grid row per entry); otherwise they run
+ * one after another.  1 <= count <= QMV_MAX_GROUP.  Entries must not write
+ * to memory that another entry reads or writes. */
+int qmv_launch_group_q8k(int type, int64_t B, const qmv_gemv* g, int count, void* stream);
+
 /* The gate and up projections of a SwiGLU feed-forward block in decode on
  * the Q8_K path (as qmv_launch_gateup_swiglu on the Q8_0 path): h[B][N] =
  * silu(x * Wg^T) * (x * Wu^T), w_gate and w_up two N x K blobs of one type,

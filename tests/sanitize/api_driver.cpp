@@ -99,6 +99,14 @@ int main() {
     CHECK(qmv_launch_gateup_swiglu_q8k(QMV_Q4_K, W, W + 256, 40, 1024 + 32, X, 1, XQ, Y, nullptr) ==
           QMV_EINVAL_SHAPE);
     {
+        qmv_gemv gk[3] = {{W, 16, 1024, nullptr, XQ, Y}, {W, 24, 1024, nullptr, XQ, Y},
+                          {W, 8, 1024, nullptr, XQ, Y}};
+        CHECK(qmv_launch_group_q8k(QMV_Q4_K, 16, gk, 3, nullptr) == QMV_OK &&
+              !strcmp(g_last.what, "group_q8k") && g_last.group_count == 3 && g_last.rows == 16);
+        gk[1].xq = nullptr;
+        CHECK(qmv_launch_group_q8k(QMV_Q4_K, 16, gk, 3, nullptr) == QMV_EINVAL_PTR);
+    }
+    {
         qmv_gemv gv[3] = {{W, 16, 32, X, XQ, Y}, {W, 24, 64, X, nullptr, Y}, {W, 8, 96, X, nullptr, Y}};
         CHECK(qmv_launch_group(QMV_Q8_0, 2, gv, 3, nullptr) == QMV_OK &&
               !strcmp(g_last.what, "group") && g_last.group_count == 3);

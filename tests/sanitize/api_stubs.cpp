@@ -82,6 +82,10 @@ int launch_gateup(int type, const uint8_t*, const uint8_t*, int64_t N, int64_t K
     g_last.hq = hq;
     return record(hq ? "gateup_q8" : "gateup", type, N, K, rows, x, xq, h);
 }
+int launch_group_q8k(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t) {
+    g_last.group_count = count;
+    return record("group_q8k", type, d[0].N, d[0].K, rows, d[0].x, d[0].xq, d[0].y);
+}
 int launch_gateup_q8k(int type, const uint8_t*, const uint8_t*, int64_t N, int64_t K,
                       const float* x, uint8_t* xq, int64_t rows, float* h, hipStream_t) {
     return record("gateup_q8k", type, N, K, rows, x, xq, h);

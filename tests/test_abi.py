@@ -182,6 +182,24 @@ def test_gateup_q8k_refusals():
     assert f(g.Q4_K, FAKE, FAKE, 64, 4096, FAKE, 1, FAKE, None, None) == -3       # h NULL
 
 
+def test_group_q8k_refusals():
+    L, G = g.lib(), g.Gemv
+    ok = (G * 2)(G(FAKE, 16, 1024, None, FAKE, FAKE), G(FAKE, 32, 1024, None, FAKE, FAKE))
+    assert L.qmv_launch_group_q8k(g.Q8_0, 16, ok, 2, None) == -1             # not a K-quant
+    assert L.qmv_launch_group_q8k(g.Q4_K, 16, None, 2, None) == -3
+    assert L.qmv_launch_group_q8k(g.Q4_K, 17, ok, 2, None) == -2
+    assert L.qmv_launch_group_q8k(g.Q4_K, 16, ok, 0, None) == -2
+    assert L.qmv_launch_group_q8k(g.Q4_K, 16, ok, 9, None) == -2
+    bad_k = (G * 1)(G(FAKE, 16, 1024 + 32, None, FAKE, FAKE))
+    assert L.qmv_launch_group_q8k(g.Q6_K, 16, bad_k, 1, None) == -2          # K % 256
+    no_xq = (G * 1)(G(FAKE, 16, 1024, FAKE, None, FAKE))
+    assert L.qmv_launch_group_q8k(g.Q4_K, 16, no_xq, 1, None) == -3          # xq required
+    mixed = (G * 2)(G(FAKE, 16, 1024, FAKE, FAKE, FAKE), G(FAKE, 16, 1024, None, FAKE, FAKE))
+    assert L.qmv_launch_group_q8k(g.Q4_K, 16, mixed, 2, None) == -3          # x all or none
+    unal = (G * 1)(G(FAKE, 16, 1024, None, FAKE + 8, FAKE))
+    assert L.qmv_launch_group_q8k(g.Q4_K, 16, unal, 1, None) == -3
+
+
 def test_noalloc_refusals():
     L = g.lib()
     # the fixed scratch admits every K <= 65536 at B = 16 (and no more at K = 2^17)

@@ -261,3 +261,39 @@ def test_gateup_swiglu_q8k(g, fmt, N, K, B):
     gate = oracle.matmul_q8k_canon_f32(fmt, sub(wg), len(rows), K, xo, B)
     up = oracle.matmul_q8k_canon_f32(fmt, sub(wu), len(rows), K, xo, B)
     assert_bitwise(np.ascontiguousarray(h[:, rows]), oracle.swiglu(gate, up), "h = silu(g) u")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("B,Ks", [(16, (1024, 1024, 1024)), (5, (512, 512)), (3, (1024, 1024, 1024)),
+                                  (16, (1024, 2048))])
+def test_group_q8k_equals_single(g, fmt, B, Ks):
+    """qmv_launch_group_q8k: every entry bit-identical to qmv_launch_q8k on
+    its own (one launch of the batched kernel for B = 5..16 and one K, ragged
+    N; the sequential path for B <= 4 or mixed K), with x quantised by the
+    launch and staged in one shared xq; one entry also against the oracle."""
+    Ns = (520, 130, 37)[:len(Ks)]
+    blobs = [synth.weights(fmt, N, K, 3000 + i, s_range=(-128, 127))[0] for i, (N, K) in enumerate(zip(Ns, Ks))]
+    xs = [synth.activations(B, K, 3010 + i) for i, K in enumerate(Ks)]
+    ws = [dev(b) for b in blobs]
+    print(f"group q8k fmt={fmt} B={B} Ks={Ks}", flush=True)
+    want = [host(g.matmul_q8k(fmt, w, N, K, x=dev(x))) for w, N, K, x in zip(ws, Ns, Ks, xs)]
+    # x given: each entry quantises its own x
+    xds = [dev(x) for x in xs]
+    xqs = [torch.empty(g.qmv_act_bytes_q8k(B, K), dtype=torch.uint8, device="cuda") for K in Ks]
+    ys = [torch.full((B, N), float("nan"), device="cuda") for N in Ns]
+    g.qmv_launch_group_q8k(fmt, B, [(w.data_ptr(), N, K, xd.data_ptr(), xq.data_ptr(), y.data_ptr())
+                                    for w, N, K, xd, xq, y in zip(ws, Ns, Ks, xds, xqs, ys)])
+    for i in range(len(Ns)):
+        assert_bitwise(host(ys[i]), want[i], f"entry {i}, x given")
+    # staged: one x for the entries of the first K, one shared xq
+    if len(set(Ks)) == 1:
+        xq = g.quantize_q8k(xds[0])
+        ys2 = [torch.full((B, N), float("nan"), device="cuda") for N in Ns]
+        g.qmv_launch_group_q8k(fmt, B, [(w.data_ptr(), N, Ks[0], None, xq.data_ptr(), y.data_ptr())
+                                        for w, N, y in zip(ws, Ns, ys2)])
+        for i, (w, N) in enumerate(zip(ws, Ns)):
+            assert_bitwise(host(ys2[i]), host(g.matmul_q8k(fmt, w, N, Ks[0], x=xds[0])),
+                           f"entry {i}, staged")
+    xo = oracle.quantize_act_q8k(xs[1])
+    assert_bitwise(host(ys[1]), oracle.matmul_q8k_canon_f32(fmt, blobs[1], Ns[1], Ks[1], xo, B),
+                   "entry 1 vs oracle")
