@@ -2474,9 +2474,9 @@ int launch_qmv_q8k(int type, const uint8_t* w, int64_t N, int64_t K, const float
     // BDOT_MIN_ROWS..16 rows: the batched MFMA kernel; prefill: the GEMM
     if (rows > 16) return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, false, s);
     if (rows >= BDOT_MIN_ROWS) return launch_bdot_q8k(type, w, nullptr, N, K, xq, rows, y, P, s);
-    // fewer rows run the lane-per-chunk kernel, in launches of up to 4
-    // activation rows (each reads the weights once)
-    if (!use_dot(rows, K)) return launch_gemm_q8k(type, w, N, K, xq, rows, y, P, false, s);
+    // fewer rows run the lane-per-chunk kernel (one launch), unless their
+    // activation rows do not fit its LDS: then the batched kernel too
+    if (!use_dot(rows, K)) return launch_bdot_q8k(type, w, nullptr, N, K, xq, rows, y, P, s);
     const ActLayoutK L = act_layout_q8k(rows, K);
     const int per = type == T_Q4_K ? 2 : 1;
     for (int64_t r0 = 0; r0 < rows; r0 += 4) {

@@ -257,9 +257,10 @@ int quantize_act_q8_k(const float* x, void* xq, int64_t rows, int64_t K, void* s
 /* Decode GEMV on the Q8_K path: y[B][N] = x[B][K] * W^T, 1 <= B <= 16, W
  * Q4_K or Q6_K.  x given: quantised into xq first; x NULL: xq holds a
  * complete quantize_act_q8_k result for these B rows.  B <= 4 runs the
- * lane-per-chunk kernel (one launch), B = 5..16 the batched int8-MFMA
- * kernel (v_mfma_i32_16x16x32_i8, sub-block scales applied to the exact
- * int32 block sums, f32 scaling once per superblock); both read the weights
+ * lane-per-chunk kernel (one launch), B = 5..16 (and B <= 4 with rows too
+ * long for that kernel's LDS staging) the batched int8-MFMA kernel
+ * (v_mfma_i32_16x16x32_i8, sub-block scales applied to the exact int32
+ * block sums, f32 scaling once per superblock); both read the weights
  * once. */
 int qmv_launch_q8k(int type, const void* w, int64_t N, int64_t K, const float* x, int64_t B,
                    void* xq, float* y, void* stream);

@@ -217,15 +217,16 @@ def test_q8k_batched_decode_full_size(g, fmt, N, K, M):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_q8k_batched_long_rows(g, fmt):
+@pytest.mark.parametrize("M", [2, 8])
+def test_q8k_batched_long_rows(g, fmt, M):
     """Rows of 65536 elements (256 superblocks, 32 rounds of the workgroup's
-    waves; too long for the lane-per-chunk kernel's LDS staging) at 8 tokens,
-    with a ragged last tile (N = 37)."""
-    N, K, M = 37, 65536, 8
+    waves; too long for the lane-per-chunk kernel's LDS staging, so at 2
+    tokens too the batched kernel runs) with a ragged last tile (N = 37)."""
+    N, K = 37, 65536
     blob, _ = synth.weights(fmt, N, K, 2800 + fmt, s_range=(-128, 127))
     x = synth.activations(M, K, 2801)
     xd = dev(x)
-    print(f"q8k batched long rows fmt={fmt}", flush=True)
+    print(f"q8k batched long rows fmt={fmt} M={M}", flush=True)
     y = host(g.matmul_q8k(fmt, dev(blob), N, K, x=xd))
     xq = oracle.quantize_act_q8k(x)
     y64, A = oracle.matmul_q8k_f64(fmt, blob, N, K, xq, M)
