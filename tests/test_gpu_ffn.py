@@ -161,3 +161,64 @@ def test_gateup_swiglu_q8_leaves_h_quantised(g, fmt, N, K, B):
     assert_bitwise(y_q.cpu().numpy(), y_h.cpu().numpy(), "down from hq vs from h")
     assert_bitwise(y_q.cpu().numpy(), oracle.matmul_canon_f32(fdown, wd, K, N, xq_o, B),
                    "down f32 order")
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_ffn_chain_8b_full_size(g, B):
+    """The 8B-class FFN at full size as the benchmark runs it: Q4_K gate/up
+    14336x4096 with the SwiGLU and the Q8_0 quantisation of h
+    (qmv_launch_gateup_swiglu_q8), then the Q6_K down 4096x14336 on that
+    quantisation.  h and its Q8_0 blocks bit-exact against the oracle chain
+    (all 14336 rows of gate and up); down on 200 sampled rows bitwise in the
+    f32 order and within tolerance of f64."""
+    N, K = 14336, 4096
+    wg, wu = _pair(synth.Q4_K, N, K, 700 + B)
+    wd, _ = synth.weights(synth.Q6_K, K, N, 702 + B, dscale=0.02)
+    x = synth.activations(B, K, 703 + B)
+    print(f"ffn chain 8b full size B={B}", flush=True)
+    h, hq = g.gateup_swiglu_q8(synth.Q4_K, dev(wg), dev(wu), N, K, x=dev(x))
+    y = g.matvec(synth.Q6_K, dev(wd), K, N, xq=hq, B=B)
+    torch.cuda.synchronize()
+    h_o = _oracle_h(synth.Q4_K, wg, wu, N, K, x)
+    assert_bitwise(h.cpu().numpy(), h_o, "h")
+    xq_o = oracle.quantize_act(h_o)
+    assert_bitwise(hq.cpu().numpy()[: xq_o.size], xq_o, "Q8_0 of h")
+    rng = np.random.Generator(np.random.PCG64(704))
+    rows = np.unique(np.concatenate([[0, K - 1], rng.choice(K, 200, replace=False)]))
+    R = synth.row_bytes(synth.Q6_K, N)
+    sub = np.ascontiguousarray(wd.reshape(K, R)[rows]).reshape(-1)
+    got = np.ascontiguousarray(y.cpu().numpy()[:, rows])
+    y64, A = oracle.matmul_f64(synth.Q6_K, sub, len(rows), N, xq_o, B)
+    assert_tol(got, y64, A, what="down, full size")
+    assert_bitwise(got, oracle.matmul_canon_f32(synth.Q6_K, sub, len(rows), N, xq_o, B), "down f32")
+
+
+def test_ffn_chain_8b_full_size_q8k(g):
+    """The same FFN at 16 rows on the Q8_K path as the benchmark runs it:
+    qmv_launch_gateup_swiglu_q8k, then qmv_launch_q8k on h (quantised by
+    the launch).  h bit-exact against the oracle's SwiGLU of its Q8_K-order
+    gate and up (all rows); down on sampled rows bitwise in the Q8_K f32
+    order and within tolerance of f64."""
+    N, K, B = 14336, 4096, 16
+    wg, wu = _pair(synth.Q4_K, N, K, 710)
+    wd, _ = synth.weights(synth.Q6_K, K, N, 712, dscale=0.02)
+    x = synth.activations(B, K, 713)
+    print("ffn chain 8b full size q8k", flush=True)
+    h = g.gateup_swiglu_q8k(synth.Q4_K, dev(wg), dev(wu), N, K, x=dev(x))
+    y = g.matmul_q8k(synth.Q6_K, dev(wd), K, N, x=h)
+    torch.cuda.synchronize()
+    xq = oracle.quantize_act_q8k(x)
+    gate = oracle.matmul_q8k_canon_f32(synth.Q4_K, wg, N, K, xq, B)
+    up = oracle.matmul_q8k_canon_f32(synth.Q4_K, wu, N, K, xq, B)
+    h_o = oracle.swiglu(gate, up)
+    assert_bitwise(h.cpu().numpy(), h_o, "h")
+    xq_h = oracle.quantize_act_q8k(h_o)
+    rng = np.random.Generator(np.random.PCG64(714))
+    rows = np.unique(np.concatenate([[0, K - 1], rng.choice(K, 200, replace=False)]))
+    R = synth.row_bytes(synth.Q6_K, N)
+    sub = np.ascontiguousarray(wd.reshape(K, R)[rows]).reshape(-1)
+    got = np.ascontiguousarray(y.cpu().numpy()[:, rows])
+    y64, A = oracle.matmul_q8k_f64(synth.Q6_K, sub, len(rows), N, xq_h, B)
+    assert_tol(got, y64, A, what="down q8k, full size")
+    assert_bitwise(got, oracle.matmul_q8k_canon_f32(synth.Q6_K, sub, len(rows), N, xq_h, B),
+                   "down q8k f32")
