@@ -67,12 +67,13 @@ LAYER = [("q", Q4_K, 4096, 4096), ("k", Q4_K, 1024, 4096), ("v", Q4_K, 1024, 409
 STAGES = {"A_qkv": ("q", "k", "v"), "B_o": ("o",), "C_gateup_swiglu": ("gate", "up"),
           "D_down": ("down",)}
 # the multiply kernel of each stage at batch 1 (its rocprofv3 name: format,
-# rows, fused quantisation, mode, Q8_K activations): A, B and C quantise their
-# activation inside the kernel; at K = 4096 the quantisation of h for D is a
-# launch of its own after C's kernel; D reads it
-STAGE_KERNEL = {"A_qkv": "k_dot<12, 1, true, 0, false>", "B_o": "k_dot<12, 1, true, 1, false>",
-                "C_gateup_swiglu": "k_dot<12, 1, true, 2, false>",
-                "D_down": "k_dot<14, 1, false, 1, false>"}
+# rows, fused quantisation, mode, Q8_K activations, lean loads): A, B and C
+# quantise their activation inside the kernel; at K = 4096 the quantisation of
+# h for D is a launch of its own after C's kernel; D reads it
+STAGE_KERNEL = {"A_qkv": "k_dot<12, 1, true, 0, false, true>",
+                "B_o": "k_dot<12, 1, true, 1, false, true>",
+                "C_gateup_swiglu": "k_dot<12, 1, true, 2, false, true>",
+                "D_down": "k_dot<14, 1, false, 1, false, false>"}
 STAGE_KERNEL_WHAT = {"A_qkv": "grouped GEMV q, k, v (Q4_K)", "B_o": "GEMV o (Q4_K)",
                      "C_gateup_swiglu": "paired GEMV gate/up with the SwiGLU epilogue (Q4_K)",
                      "D_down": "GEMV down (Q6_K 4096x14336)"}

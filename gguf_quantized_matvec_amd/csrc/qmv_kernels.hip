@@ -1590,11 +1590,20 @@ constexpr int MODE_GROUP = 0, MODE_SINGLE = 1, MODE_PAIRED = 2, MODE_PARTIALS = 
 
 // Q8K: the activations are staged Q8_K (K-quant formats only, not FUSED):
 // each chunk is scaled once per superblock (dot_chunk_q8k).
-template <int FMT, int B, bool FUSED, int MODE, bool Q8K = false>
+// Loads whose count the compiler can see (LEAN): with every chunk of the
+// launch whole (K a multiple of 256), each lane loads a full window from
+// inside the blob with no branch around the loads, so that the waits for the
+// activation loads issued before them count past the weight loads instead of
+// draining every load (a path that skips its loads at a join forces that).
+// Q6_K keeps the guarded loads, which measured faster for it.
+template <int FMT> constexpr bool lean_loads() { return FMT != T_Q6_K; }
+
+template <int FMT, int B, bool FUSED, int MODE, bool Q8K = false, bool WHOLE = false>
 __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     constexpr bool PAIRED = MODE == MODE_PAIRED || MODE == MODE_PAIRED_Q;
     using F = Fmt<FMT>;
     constexpr int NWD = DotFmt<FMT>::NWD;
+    constexpr bool LEAN = WHOLE && lean_loads<FMT>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // this workgroup's job (one kernel-argument round trip)
     DotJob J;
@@ -1635,13 +1644,25 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
         int c;
         chunk_of(q, row, c);
         const bool valid = active && row < N && c < C;
-        const int64_t off = row * R + (int64_t)c * F::CB;
-        const bool near_end = valid && off + 4 * NWD > J.wbytes;
-        if (valid) {
-            load_chunk_regs<FMT>(wsrc, off, J.wbytes, __builtin_amdgcn_ballot_w64(near_end) != 0, r);
-        } else {
+        if constexpr (LEAN) {
+            // whole chunks: a row is C chunks of CB bytes, a multiple of 4,
+            // so every chunk starts 4-byte aligned (the blob is 16-byte
+            // aligned) and is exactly its CB / 4 dwords; lanes past the rows
+            // read chunk 0 (their sums are dropped)
+            static_assert(F::CB % 4 == 0, "lean loads need 4-byte chunks");
+            const int64_t off = valid ? row * R + (int64_t)c * F::CB : 0;
+            __builtin_memcpy(r, reinterpret_cast<const uint32_t*>(wsrc + off), F::CB);
 #pragma unroll
-            for (int i = 0; i < NWD; i++) r[i] = 0;
+            for (int i = F::CB / 4; i < NWD; i++) r[i] = 0;
+        } else {
+            const int64_t off = row * R + (int64_t)c * F::CB;
+            const bool near_end = valid && off + 4 * NWD > J.wbytes;
+            if (valid) {
+                load_chunk_regs<FMT>(wsrc, off, J.wbytes, __builtin_amdgcn_ballot_w64(near_end) != 0, r);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NWD; i++) r[i] = 0;
+            }
         }
     };
 
@@ -1656,7 +1677,30 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     uint32_t pw[SW][3];
     const int npc = B * nb * 2, nwd = B * nb;
     const bool copy_first = npc >= 256;
-    if constexpr (!FUSED) {
+    if constexpr (!FUSED && LEAN) {
+        // LEAN: the copy always goes first; every thread of a pass that has
+        // work loads (a clamped index), so the loads are not behind branches
+        const uint8_t* xq = J.xq;
+        const int bd = blockDim.x;
+#pragma unroll
+        for (int uu = 0; uu < SP; uu++) {
+            if (uu * bd < npc) {
+                const int i = min((int)threadIdx.x + uu * bd, npc - 1);
+                const int m = i / (2 * nb), k = i - m * 2 * nb;
+                pc[uu] = reinterpret_cast<const uint4*>(xq + J.rcodes + (int64_t)m * K)[k];
+            }
+        }
+#pragma unroll
+        for (int uu = 0; uu < SW; uu++) {
+            if (uu * bd < nwd) {
+                const int i = min((int)threadIdx.x + uu * bd, nwd - 1);
+                pw[uu][0] = reinterpret_cast<const uint32_t*>(xq + J.rda)[i];
+                pw[uu][1] = reinterpret_cast<const uint32_t*>(xq + J.rca)[i];
+                pw[uu][2] = reinterpret_cast<const uint32_t*>(xq + J.rs16)[i];
+            }
+        }
+        issue(0, r);
+    } else if constexpr (!FUSED) {
         const uint8_t* xq = J.xq;
         if (!copy_first) issue(0, r);
 #pragma unroll
@@ -1701,15 +1745,18 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
         // issue order), a short one behind them; formats with long chunks
         // (Q8_0, Q6_K) always load the weights first, which keeps the chunk
         // registers free during the quantisation
-        const bool x_first = NWD <= 40 && total > 256;
-        if (!x_first) issue(0, r);
-        for (int pass = 0; pass == 0 || (int)threadIdx.x + pass * UNR * (int)blockDim.x < total; pass++) {
-          const int i0 = threadIdx.x + pass * UNR * blockDim.x;
-          float4 xf[UNR][2];
+        // LEAN: x goes first for the short-chunk formats whatever its
+        // length, and every thread of a pass that has work loads (a clamped
+        // index), so the loads are not behind branches
+        const bool x_first = NWD <= 40 && (LEAN || total > 256);
+        const int bd = blockDim.x;
+        float4 xf[UNR][2];
+        auto load_x = [&](int pass) {
 #pragma unroll
           for (int uu = 0; uu < UNR; uu++) {
-            const int i = i0 + uu * blockDim.x;
-            if (i < total) {
+            const int i0 = (pass * UNR + uu) * bd;
+            if (LEAN ? i0 < total : i0 + (int)threadIdx.x < total) {
+              const int i = min((int)threadIdx.x + i0, total - 1);
               const int blk = i >> 2, part = i & 3;
               const int m = blk / nb, b = blk - m * nb;
               const float4* xb = reinterpret_cast<const float4*>(x + (int64_t)m * K + 32 * b + 8 * part);
@@ -1717,7 +1764,23 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
               xf[uu][1] = xb[1];
             }
           }
-          if (pass == 0 && x_first) issue(0, r);  // every lane takes pass 0
+        };
+        if constexpr (LEAN) {
+            if constexpr (NWD <= 40) {
+                load_x(0);
+                issue(0, r);
+            } else {
+                issue(0, r);
+                load_x(0);
+            }
+        } else {
+            if (!x_first) issue(0, r);
+            load_x(0);
+            if (x_first) issue(0, r);  // every lane takes pass 0
+        }
+        for (int pass = 0; pass == 0 || pass * UNR * bd < total; pass++) {
+          if (pass > 0) load_x(pass);
+          const int i0 = threadIdx.x + pass * UNR * blockDim.x;
 #pragma unroll
           for (int uu = 0; uu < UNR; uu++) {
             const int i = i0 + uu * blockDim.x;
@@ -1961,15 +2024,31 @@ inline int raise_lds_limit(const void* kernel, std::atomic<int> (&state)[64]) {
     return 0;
 }
 
+template <int FMT, int B, bool FUSED, int MODE, bool Q8K, bool WHOLE>
+int launch_dot_variant(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
+    static std::atomic<int> lds_state[64];
+    const int arc = raise_lds_limit(
+        reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED, MODE, Q8K, WHOLE>), lds_state);
+    if (arc) return arc;
+    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, MODE, Q8K, WHOLE>),
+                       dim3((unsigned)blocks, (unsigned)jobs.count), dim3(64 * jobs.waves), shmem, s,
+                       jobs);
+    return (int)hipGetLastError();
+}
+
+// WHOLE: every job's rows are whole 256-element chunks (always for the
+// 256-element formats), which the lean loads need.
 template <int FMT, int B, bool FUSED, int MODE, bool Q8K = false>
 int launch_dot_kernel(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStream_t s) {
-    static std::atomic<int> lds_state[64];
-    const int arc = raise_lds_limit(reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED, MODE, Q8K>),
-                                    lds_state);
-    if (arc) return arc;
-    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, MODE, Q8K>), dim3((unsigned)blocks, (unsigned)jobs.count),
-                       dim3(64 * jobs.waves), shmem, s, jobs);
-    return (int)hipGetLastError();
+    if constexpr (Fmt<FMT>::QK == 256 || !lean_loads<FMT>()) {
+        return launch_dot_variant<FMT, B, FUSED, MODE, Q8K, lean_loads<FMT>()>(jobs, blocks, shmem,
+                                                                                 s);
+    } else {
+        bool whole = true;
+        for (int k = 0; k < jobs.count; k++) whole = whole && jobs.j[k].K % 256 == 0;
+        return whole ? launch_dot_variant<FMT, B, FUSED, MODE, Q8K, true>(jobs, blocks, shmem, s)
+                     : launch_dot_variant<FMT, B, FUSED, MODE, Q8K, false>(jobs, blocks, shmem, s);
+    }
 }
 
 // The formats whose paired launch can also quantise h (the others run the
