@@ -53,6 +53,10 @@ SMALL = [
     (synth.Q5_0, 45, 896), (synth.Q5_0, 16, 32), (synth.Q5_0, 33, 4096 + 96),
     (synth.Q4_1, 45, 896), (synth.Q4_1, 17, 32), (synth.Q5_1, 33, 4096 + 96),
     (synth.Q5_1, 16, 416), (synth.Q8_1, 40, 896), (synth.Q8_1, 19, 64),
+    # whole 256-element chunks (the branch-free weight loads) with rows past
+    # the last full unit of a wave: 64 / C rows per wave for C chunks a row
+    (synth.Q8_0, 37, 512), (synth.Q4_0, 129, 256), (synth.Q5_0, 29, 1024),
+    (synth.Q4_1, 21, 768), (synth.Q5_1, 13, 2048), (synth.Q8_1, 11, 4096),
 ]
 
 
@@ -329,6 +333,10 @@ def test_byte_coverage_32(g, fmt, B):
     (synth.Q4_1, [(300, 896), (45, 4864)]),
     (synth.Q5_1, [(300, 896), (45, 4864)]),
     (synth.Q8_1, [(100, 896), (33, 4192)]),
+    # every entry of whole chunks (the branch-free loads), rows past the
+    # last full unit of a wave in each
+    (synth.Q8_0, [(37, 512), (129, 256), (5, 4096)]),
+    (synth.Q5_0, [(29, 1024), (3, 4864)]),
     # one large GEMV between two tiny ones: most workgroup rows of the grid
     # belong to no work and exit
     (synth.Q4_0, [(8, 32), (20000, 896), (3, 4864)]),
