@@ -544,6 +544,21 @@ def ceilings(torch):
     t = timed(rotated) / 32
     out["stream_read_nt_66MB_us"] = round(t * 1e6, 2)
     out["stream_read_nt_66MB_GBs"] = round(part / t / 1e9, 1)
+    # the decode GEMV's own load pattern over the same bytes as the headline's
+    # dominant launch (gate + up: 28672 Q4_K rows of 16 chunks of 144 bytes),
+    # every lane one chunk, nothing else
+    lib.qmv_ceil_chunk_read.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P]
+    crows, cpart = 28672, 28672 * 16 * 144
+    ccopies = nbytes // cpart
+
+    def chunk_launch(i):
+        rc = lib.qmv_ceil_chunk_read(buf.data_ptr() + (i % ccopies) * cpart, crows, 16, 144,
+                                     sink.data_ptr(), s())
+        assert rc == 0, rc
+    # timed as the GEMVs are: graph replays of back-to-back launches
+    t = graph_launch_us(torch, chunk_launch, 32) * 1e-6
+    out["chunk_read_66MB_us"] = round(t * 1e6, 2)
+    out["chunk_read_66MB_GBs"] = round(cpart / t / 1e9, 1)
     del buf, sink
     blocks, iters = 256 * 8, 2000
     o = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
@@ -559,7 +574,10 @@ def ceilings(torch):
     out["how"] = ("libqmv_ceilings.so (qmv_ceilings.hip): 4 back-to-back reads of 1 GiB with "
                   "16-byte loads, 16 in flight per thread, and with the nontemporal hint, 8 in "
                   "flight per thread (also 32 back-to-back 66.1 MB reads over rotated slices), "
-                  "time per read; 2048 workgroups x 4 waves of 4 independent MFMA chains; "
+                  "time per read; the decode GEMV's load pattern alone over the same 66.1 MB "
+                  "(28672 Q4_K rows, each lane one 144-byte chunk), rotated likewise and timed "
+                  "by graph replays as the GEMVs are; "
+                  "2048 workgroups x 4 waves of 4 independent MFMA chains; "
                   "16 f32 fma chains per thread; best of 5 launches by HIP events")
     return out
 

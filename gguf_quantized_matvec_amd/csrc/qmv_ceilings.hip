@@ -118,6 +118,28 @@ __global__ __launch_bounds__(256) void k_epilogue(float* __restrict__ out, int i
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = r;
 }
 
+// The decode GEMV's weight-load pattern alone: C lanes per row (one
+// 16*NP-byte chunk each), floor(64/C) rows per wave, every chunk's 16-byte
+// loads in flight together; each lane xors its words and stores only when the
+// result is zero, so that the loads stay but hardly any bytes are written.
+template <int NP>
+__global__ __launch_bounds__(256) void k_chunk_read(const uint4* __restrict__ w, int64_t rows, int C,
+                                                    uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int G = 64 / C, lrow = lane / C, c = lane - lrow * C;
+    const int64_t row = wave * G + lrow;
+    if (lrow >= G || row >= rows) return;
+    const uint4* p = w + (row * C + c) * NP;
+    v4u v[NP];
+#pragma unroll
+    for (int i = 0; i < NP; i++) v[i] = *reinterpret_cast<const v4u*>(p + i);
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < NP; i++) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    if (acc == 0) sink[wave * 64 + lane] = 1u;
+}
+
 int launched() { return hipGetLastError() == hipSuccess ? 0 : -4; }
 
 }  // namespace
@@ -129,6 +151,24 @@ int qmv_ceil_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* st
 }
 int qmv_ceil_stream_read_nt(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
     return stream_read<8, true>(buf, bytes, sink, static_cast<hipStream_t>(stream));
+}
+
+int qmv_ceil_chunk_read(const void* w, int64_t rows, int64_t chunks, int64_t chunk_bytes,
+                        uint32_t* sink, void* stream) {
+    if (!w || !sink || (reinterpret_cast<uintptr_t>(w) & 15) || rows < 1 || chunks < 1 ||
+        chunks > 64 || (chunk_bytes != 144 && chunk_bytes != 272))
+        return -2;
+    const int64_t G = 64 / chunks, waves = (rows + G - 1) / G, blocks = (waves + 3) / 4;
+    if (blocks > 0x7fffffff) return -2;
+    const uint4* p = static_cast<const uint4*>(w);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (chunk_bytes == 144)
+        hipLaunchKernelGGL(k_chunk_read<9>, dim3((unsigned)blocks), dim3(256), 0, s, p, rows,
+                           (int)chunks, sink);
+    else
+        hipLaunchKernelGGL(k_chunk_read<17>, dim3((unsigned)blocks), dim3(256), 0, s, p, rows,
+                           (int)chunks, sink);
+    return launched();
 }
 
 int qmv_ceil_mfma_i8(int32_t* out, int blocks, int iters, void* stream) {

@@ -30,6 +30,16 @@ int qmv_ceil_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* st
  * bytes/128 uint32 words. */
 int qmv_ceil_stream_read_nt(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* The decode GEMV's weight-load pattern with nothing else: a blob of `rows`
+ * rows of `chunks` chunks (1..64) of `chunk_bytes` bytes (144 or 272, the
+ * 256-element chunks of Q4_K / Q4_0 and of Q8_0), w 16-byte aligned; each
+ * lane loads one chunk whole (chunks lanes per row, 64 / chunks rows per
+ * wave, workgroups of 4 waves).  sink receives at most 64 uint32 words per
+ * wave (ceil(rows / (64 / chunks)) waves), and in practice none: a lane
+ * stores only when the xor of its chunk's words is zero. */
+int qmv_ceil_chunk_read(const void* w, int64_t rows, int64_t chunks, int64_t chunk_bytes,
+                        uint32_t* sink, void* stream);
+
 /* `blocks` workgroups of 4 waves, each wave issuing 4*iters
  * v_mfma_i32_32x32x32_i8 (65536 int8 operations each) in four independent
  * chains; out receives blocks*256 int32 words. */

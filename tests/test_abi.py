@@ -254,7 +254,7 @@ def test_ceilings_library_exports_its_header():
                  flags=re.S)
     names = set(re.findall(r"^\s*int\s+([a-z_0-9]+)\s*\(", src, re.M))
     assert names == {"qmv_ceil_stream_read", "qmv_ceil_stream_read_nt", "qmv_ceil_mfma_i8",
-                     "qmv_ceil_mfma_f16", "qmv_ceil_epilogue"}
+                     "qmv_ceil_mfma_f16", "qmv_ceil_epilogue", "qmv_ceil_chunk_read"}
     L = ctypes.CDLL(lib_path)
     for n in names:
         assert hasattr(L, n), n
@@ -266,3 +266,11 @@ def test_ceilings_library_exports_its_header():
     L.qmv_ceil_stream_read_nt.argtypes = L.qmv_ceil_stream_read.argtypes
     assert L.qmv_ceil_stream_read_nt(FAKE, 32768 + 16384, FAKE, None) == -2
     assert L.qmv_ceil_stream_read_nt(FAKE + 4, 32768, FAKE, None) == -2
+    I64 = ctypes.c_int64
+    L.qmv_ceil_chunk_read.argtypes = [ctypes.c_void_p, I64, I64, I64, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    assert L.qmv_ceil_chunk_read(FAKE, 16, 16, 160, FAKE, None) == -2   # chunk size
+    assert L.qmv_ceil_chunk_read(FAKE, 16, 65, 144, FAKE, None) == -2   # > 64 chunks a row
+    assert L.qmv_ceil_chunk_read(FAKE, 0, 16, 144, FAKE, None) == -2    # no rows
+    assert L.qmv_ceil_chunk_read(FAKE + 8, 16, 16, 144, FAKE, None) == -2
+    assert L.qmv_ceil_chunk_read(FAKE, 16, 16, 272, None, None) == -2
