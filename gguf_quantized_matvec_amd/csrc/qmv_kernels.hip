@@ -1062,18 +1062,23 @@ struct BdotJob {
     float* y;
     int64_t N;
 };
+// A grouped launch's grid is flat: entry k owns workgroups
+// [start[k], start[k+1]), one per 16-row tile, so no workgroup is surplus.
 struct BdotJobs {
     BdotJob j[8];
+    int start[9];
+    int count;
 };
 
 template <int FMT>
 __global__ __launch_bounds__(512, FMT == T_Q4_K ? 4 : 1) void k_bdot8k_group(
     BdotJobs jobs, int64_t K, ActLayoutK L, int64_t rows) {
-    const BdotJob& J = jobs.j[blockIdx.y];
-    const int64_t tiles = (J.N + 15) / 16;
-    if ((int64_t)blockIdx.x >= tiles) return;  // uniform over the workgroup
+    int k = 0;
+    while (k + 1 < jobs.count && (int)blockIdx.x >= jobs.start[k + 1]) k++;
+    const BdotJob& J = jobs.j[k];
+    const int64_t tile = (int64_t)blockIdx.x - jobs.start[k];
     const int64_t wbytes = J.N * (K / 256) * Fmt<FMT>::BB;
-    bdot_tile<FMT, false, false>(J.w, J.w, wbytes, J.N, K, J.xq, L, rows, J.y, nullptr, blockIdx.x);
+    bdot_tile<FMT, false, false>(J.w, J.w, wbytes, J.N, K, J.xq, L, rows, J.y, nullptr, tile);
 }
 
 // ------------------------------------------------- lane-per-chunk GEMV ----
@@ -1548,15 +1553,17 @@ struct DotJob {
     int64_t hnb, hrcodes, hrda, hrca, hrs16;
 };
 constexpr int MAX_JOBS = 8;
-// A grouped launch is a 2-D grid: row y of workgroups is job y (as many
-// workgroups as the largest job needs; the surplus ones of smaller jobs
-// exit at once), so a workgroup loads its job's fields with one dependent
-// kernel-argument load, which sits at the head of every wave's critical
-// path (about half a microsecond each, measured).
+// A grouped launch's grid is flat: job k owns workgroups [start[k],
+// start[k+1]), so no workgroup is surplus (a 2-D grid with a row per job,
+// each as wide as the largest, measured 8.8 against 7.5 us for an 8B-class
+// q/k/v group: the exiting workgroups of the smaller jobs still take their
+// turn at dispatch).  A workgroup finds its job with a few scalar compares
+// and loads the job's fields with one dependent kernel-argument load.
 struct DotJobs {
     int count;
     int waves;            // waves per workgroup (4 or 8), as launched
     DotJob j[MAX_JOBS];
+    int start[MAX_JOBS + 1];
 };
 
 // floor(a / b) for 0 <= a < 4096 and 1 <= b <= 64, through the f32
@@ -1607,10 +1614,14 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // this workgroup's job (one kernel-argument round trip)
     DotJob J;
+    int64_t bx = blockIdx.x;  // the workgroup's index within its job
     if constexpr (MODE != MODE_GROUP) {
         J = jobs.j[0];
     } else {
-        J = jobs.j[blockIdx.y];
+        int k = 0;
+        while (k + 1 < jobs.count && (int)blockIdx.x >= jobs.start[k + 1]) k++;
+        J = jobs.j[k];
+        bx = (int64_t)blockIdx.x - jobs.start[k];
     }
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int64_t N = J.N, K = J.K;
@@ -1626,8 +1637,8 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     const int GP = PAIRED ? G >> 1 : G;
     const int64_t units = C <= 64 ? (N + GP - 1) / GP : N;
     const int lrow = small_div(lane, LPR), lchunk = lane - lrow * LPR;  // this lane's row in the unit, chunk
-    if ((int64_t)blockIdx.x * jobs.waves >= units) return;  // surplus workgroup of a smaller job
-    const int64_t u = (int64_t)blockIdx.x * jobs.waves + wv;
+    if (bx * jobs.waves >= units) return;  // past the job's units (its last workgroup's idle waves)
+    const int64_t u = bx * jobs.waves + wv;
     const bool active = u < units;
 
     auto chunk_of = [&](int q, int64_t& row, int& c) {
@@ -1736,7 +1747,7 @@ __global__ __launch_bounds__(512) void k_dot(DotJobs jobs) {
     if constexpr (FUSED) {
         // four lanes per block, 8 elements each: the block's amax and code
         // sums by lane shuffles, then the same d, id and codes as k_quantize
-        const bool writer = blockIdx.x == 0 && J.xq != nullptr;
+        const bool writer = bx == 0 && J.xq != nullptr;
         const float* x = J.x;
         uint8_t* xq = J.xq;
         const int total = 4 * B * nb;  // (block, quarter) tasks; whole blocks stay in one pass
@@ -2030,9 +2041,8 @@ int launch_dot_variant(const DotJobs& jobs, int64_t blocks, size_t shmem, hipStr
     const int arc = raise_lds_limit(
         reinterpret_cast<const void*>(&k_dot<FMT, B, FUSED, MODE, Q8K, WHOLE>), lds_state);
     if (arc) return arc;
-    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, MODE, Q8K, WHOLE>),
-                       dim3((unsigned)blocks, (unsigned)jobs.count), dim3(64 * jobs.waves), shmem, s,
-                       jobs);
+    hipLaunchKernelGGL((k_dot<FMT, B, FUSED, MODE, Q8K, WHOLE>), dim3((unsigned)blocks),
+                       dim3(64 * jobs.waves), shmem, s, jobs);
     return (int)hipGetLastError();
 }
 
@@ -2105,10 +2115,8 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
     int64_t blocks4 = 0;
     for (int k = 0; k < count; k++) blocks4 += dot_blocks(type, d[k].N, d[k].K, 4, paired);
     jobs.waves = waves ? waves : blocks4 > 256 && blocks4 <= 512 ? 8 : 4;
-    // Rows of the grid in decreasing workgroup count: workgroups are
-    // dispatched row after row at a limited rate, so the surplus (exiting)
-    // workgroups of a smaller GEMV delay only the rows after it, and the
-    // last row's delay nothing.
+    // Jobs in decreasing workgroup count along the flat grid (the largest
+    // GEMV's workgroups are dispatched first).
     int order[MAX_JOBS];
     for (int k = 0; k < count; k++) {
         int at = k;
@@ -2145,7 +2153,9 @@ int launch_dot(int type, const GemvDesc* d, int count, int64_t rows, hipStream_t
             J.hrs16 = H.rs16;
         }
         const int64_t bk = dot_blocks(type, d[k].N, d[k].K, jobs.waves, paired);
-        blocks = bk > blocks ? bk : blocks;  // grid x: the largest job
+        if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
+        jobs.start[jk] = (int)blocks;
+        blocks += bk;  // the flat grid: every job's workgroups in turn
         const size_t sh = dot_shmem((int)rows, d[k].K, jobs.waves) + (hq ? rows * 32 * 4 : 0);
         shmem = sh > shmem ? sh : shmem;
     }
@@ -2510,20 +2520,23 @@ int launch_group_q8k(int type, const GemvDesc* d, int count, int64_t rows, hipSt
     const int C = (int)(K / 256);
     const ActLayoutK L = act_layout_q8k(rows, K);
     BdotJobs jobs{};
-    int64_t tmax = 0;
+    jobs.count = count;
+    int64_t tiles = 0;
     for (int k = 0; k < count; k++) {
         jobs.j[k] = BdotJob{d[k].w, d[k].xq, d[k].y, d[k].N};
-        const int64_t t = (d[k].N + 15) / 16;
-        tmax = t > tmax ? t : tmax;
+        if (tiles > INT32_MAX) return (int)hipErrorInvalidValue;
+        jobs.start[k] = (int)tiles;
+        tiles += (d[k].N + 15) / 16;
     }
-    if (tmax > INT32_MAX || !L.gcodes) return (int)hipErrorInvalidValue;
+    if (tiles > INT32_MAX || !L.gcodes) return (int)hipErrorInvalidValue;
+    jobs.start[count] = (int)tiles;
     // the single launch's wave count and LDS (one K, so one choice)
     int KS = 1;
     while (KS < 8 && KS * 2 <= C) KS *= 2;
     const int need = (int)((16 * rows + 63) / 64);
     if (KS < need) KS = need;
     const size_t pb = (size_t)(C < BDOT_WINDOW ? C : BDOT_WINDOW) * 1024;
-    const dim3 grid((unsigned)tmax, (unsigned)count), block(64 * KS);
+    const dim3 grid((unsigned)tiles), block(64 * KS);
     if (type == T_Q4_K)
         hipLaunchKernelGGL(k_bdot8k_group<T_Q4_K>, grid, block,
                            (size_t)KS * 16 * span_stride<T_Q4_K>() + pb, s, jobs, K, L, rows);
